@@ -1,0 +1,122 @@
+"""fp64 CPU oracle for the gated delta-rule (KDA / Gated DeltaNet) state layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product (the HIP
+library and its Python binding) never imports, links or calls anything here,
+and this package shares no code with it.
+
+The arithmetic lives in ``kda_oracle.c``: a token-by-token recurrence in double
+precision that follows the KDA / Gated DeltaNet / delta-rule rows of the table
+"Everything, in one table" on the page "The argument, in one page".  This module
+only marshals arrays into it (upcasting every input exactly to float64) and
+builds it with the system C compiler.
+
+Pinned by ``tests/test_oracle.py`` (worked example, closed forms, brute-force
+matrix products, exact rational arithmetic, orthonormal recall, reductions to
+linear attention and to a scalar first-order recurrence, linearity, continuation)
+and ``tests/test_oracle_mutants.py`` (planted mistakes must fail a pin).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math: IEEE double semantics)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", "-pthread", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load_library(path: str | None = None):
+    """Load (building first if absent) an oracle shared library."""
+    global _lib
+    if path is not None:
+        lib = ctypes.CDLL(path)
+        _declare(lib)
+        return lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build()
+            _lib = ctypes.CDLL(_LIB)
+            _declare(_lib)
+        return _lib
+
+
+def _declare(lib) -> None:
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.kda_oracle_fwd.restype = ctypes.c_int
+    lib.kda_oracle_fwd.argtypes = [I64, P, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P,
+                                   ctypes.c_int, P, P, ctypes.c_int]
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast to a contiguous float64 array (bf16/fp32 -> fp64 is exact)."""
+    if hasattr(x, "detach"):  # torch tensor (possibly bf16, possibly on a device)
+        x = x.detach().to("cpu")
+        import torch
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def kda_oracle(q, k, v, log_a, beta, S0=None, cu_seqlens=None, order: int = 0,
+               threads: int | None = None, lib=None):
+    """Run the fp64 recurrence.
+
+    q, k: [T, H, dk]; v: [T, H, dv]; log_a: [T, H, dk] (per channel) or [T, H]
+    (scalar decay); beta: [T, H]; S0: [N, H, dk, dv] or None (zeros);
+    cu_seqlens: [N+1] int offsets, or None for a single sequence of length T.
+    order 0 is the table's KDA row (erase, decay, write); 1 is decay-first.
+
+    Returns (o [T, H, dv], S_T [N, H, dk, dv]) as float64 arrays.
+    """
+    q, k, v, log_a, beta = (_f64(x) for x in (q, k, v, log_a, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if k.shape != (T, H, dk) or v.shape[:2] != (T, H) or beta.shape != (T, H):
+        raise ValueError("inconsistent shapes")
+    if log_a.shape == (T, H, dk):
+        scalar = 0
+    elif log_a.shape == (T, H):
+        scalar = 1
+    else:
+        raise ValueError("log_a must be [T,H,dk] or [T,H]")
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64))
+    N = cu.shape[0] - 1
+    if cu[-1] != T:
+        raise ValueError("cu_seqlens[-1] must equal T")
+    s0 = None
+    if S0 is not None:
+        s0 = _f64(S0)
+        if s0.shape != (N, H, dk, dv):
+            raise ValueError("S0 must be [N,H,dk,dv]")
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    ST = np.zeros((N, H, dk, dv), dtype=np.float64)
+    nt = threads if threads is not None else (os.cpu_count() or 1)
+    L = lib if lib is not None else load_library()
+    ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    rc = L.kda_oracle_fwd(N, ptr(cu), H, dk, dv, ptr(q), ptr(k), ptr(v), ptr(log_a), scalar,
+                          ptr(beta), ptr(s0), int(order), ptr(o), ptr(ST), int(nt))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_fwd failed with code %d" % rc)
+    return o, ST
