@@ -1,0 +1,138 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) gated delta-rule state layer.
+ *
+ * The layer keeps, per (sequence, head), a fixed-size state S of shape dk x dv
+ * (page "The argument, in one page", section "Everything, in one table", row
+ * "Linear attention": the state replaces the growing cache and never grows).
+ * Every token updates it with the KDA rule of the same table (row "KDA"):
+ *
+ *     S <- Diag(a_t) (I - beta_t k_t^T k_t) S + beta_t k_t^T v_t,   a_t = exp(log_a_t)
+ *
+ * i.e. erase what S holds along the key k_t, decay every key row c of S by its
+ * own a_t[c], then write beta_t k_t^T v_t; the output is the read after the
+ * update, o_t = q_t S.  With one log_a value per (token, head) this is the
+ * "Gated DeltaNet" row; with log_a = 0 it is the "Delta rule" row.
+ *
+ * Two entry points compute it:
+ *   kda_chunk_fwd    -- prefill over packed variable-length sequences by the
+ *                       chunkwise (WY) form (row "Chunkwise / WY" of the same
+ *                       table: the same map, one C x C triangular solve per
+ *                       chunk plus dense products on the matrix cores);
+ *   kda_decode_step  -- one token per sequence, updating S in place.
+ * Both take the initial state in and give the final state out, since the
+ * state cannot be rebuilt from nearby tokens and reuse needs it exported
+ * (glossary page "Linear attention", section "Why it matters").
+ *
+ * Conventions (both entry points)
+ *   - Every pointer is DEVICE memory owned by the caller (e.g. allocated by
+ *     PyTorch).  The library allocates nothing and keeps no global state.
+ *   - Layouts are contiguous, row-major, with the last index fastest.
+ *     Tokens of all sequences are packed along one axis of length T.
+ *   - The call validates its arguments on the host, enqueues its kernels on
+ *     `stream` (a hipStream_t; NULL = the null stream) and returns without
+ *     waiting.  On a non-OK status nothing was enqueued and outputs are
+ *     untouched; kda_last_error() then describes the reason (thread-local).
+ *     Faults during execution surface at the caller's next synchronisation.
+ *   - No scaling of q and no normalisation of k happen inside: callers fold
+ *     any 1/sqrt(dk) into q and normalise k themselves.
+ *   - log_a must be finite and <= 0 (0 < a <= 1); beta is unrestricted.
+ *     Chunked prefill splits decay factors around 16-token references, which
+ *     stays in floating-point range while every log_a >= -10; below that,
+ *     results are accurate only where the decayed terms are negligible.
+ *   - Alignment: q, k, v, o and the fp32 states must be 16-byte aligned, as
+ *     must a per-channel log_a in prefill; beta, a scalar log_a, any decode
+ *     log_a, and cu_seqlens need 4-byte alignment.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef KDA_API
+#define KDA_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, inconsistent dims */
+    KDA_ERR_UNSUPPORTED = 2,      /* a (dk, dv, dtype, chunk) combination not compiled */
+    KDA_ERR_MISALIGNED = 3,       /* a pointer not 16-byte aligned */
+    KDA_ERR_HIP = 4               /* the HIP runtime rejected a launch */
+} kda_status_t;
+
+typedef enum {
+    KDA_F32 = 0,  /* q, k, v, o in float32: products on fp32 matrix cores */
+    KDA_BF16 = 1  /* q, k, v, o in bfloat16: products on bf16 matrix cores, fp32 state */
+} kda_dtype_t;
+
+typedef struct {
+    int32_t num_seqs;     /* N: sequences (prefill) or sequences of one token (decode) */
+    int32_t num_heads;    /* H */
+    int64_t total_tokens; /* T: packed tokens over all sequences (decode: T == N) */
+    int32_t dk;           /* key width: 16, 32, 64 or 128 (bf16 prefill: 32, 64 or 128;
+                             fp32 prefill: 16, 32 or 64) */
+    int32_t dv;           /* value width: 16, 32, 64 or 128 */
+    int32_t qkv_dtype;    /* kda_dtype_t of q, k, v and o */
+    int32_t scalar_decay; /* 0: log_a is [T, H, dk] (KDA); 1: log_a is [T, H] (Gated DeltaNet) */
+    int32_t chunk_size;   /* prefill chunk C: 0 = default (32), else 32 or 64; 64 is
+                             compiled only where its LDS image fits (small dk, dv) */
+    int32_t dv_split;     /* prefill: workgroups per (sequence, head) along dv;
+                             0 = choose from the problem size, else 1, 2, 4 or 8
+                             (each slice dv / split must be 16, 32 or 64) */
+} kda_dims_t;
+
+/*
+ * Chunked prefill.
+ *   q, k      [T, H, dk]   qkv_dtype
+ *   v         [T, H, dv]   qkv_dtype
+ *   log_a     [T, H, dk] float32 (scalar_decay = 0) or [T, H] float32 (= 1)
+ *   beta      [T, H]       float32
+ *   S0        [N, H, dk, dv] float32 initial states, or NULL for zeros
+ *   cu_seqlens[N + 1]      int32 token offsets (device): sequence n is tokens
+ *                          [cu_seqlens[n], cu_seqlens[n+1]); cu_seqlens[0] = 0,
+ *                          non-decreasing, cu_seqlens[N] = T.  Empty sequences
+ *                          are allowed (their S_T equals S0).  NULL means N
+ *                          sequences of equal length T / N (T % N must be 0).
+ *   o         [T, H, dv]   qkv_dtype output, o_t = q_t S_t
+ *   S_T       [N, H, dk, dv] float32 final states, or NULL to skip.  May alias
+ *             S0 (every workgroup reads its part of S0 before it writes S_T).
+ * Results do not depend on chunk_size or dv_split beyond rounding order.
+ * Returns a kda_status_t.
+ */
+KDA_API int kda_chunk_fwd(const kda_dims_t* dims, const void* q, const void* k, const void* v,
+                  const float* log_a, const float* beta, const float* S0,
+                  const int32_t* cu_seqlens, void* o, float* S_T, void* stream);
+
+/*
+ * One decode step: one token per sequence (T == N).
+ *   q, k      [N, H, dk]   qkv_dtype
+ *   v         [N, H, dv]   qkv_dtype
+ *   log_a     [N, H, dk] or [N, H] float32, beta [N, H] float32
+ *   S_in      [N, H, dk, dv] float32 state before the token
+ *   S_out     [N, H, dk, dv] float32 state after the token; may equal S_in
+ *             (in-place update).  Each state is read once and written once.
+ *   o         [N, H, dv]   qkv_dtype output, o = q S_out
+ * Returns a kda_status_t.
+ */
+KDA_API int kda_decode_step(const kda_dims_t* dims, const void* q, const void* k, const void* v,
+                    const float* log_a, const float* beta, const float* S_in, float* S_out,
+                    void* o, void* stream);
+
+/* Static text for a status code. */
+KDA_API const char* kda_status_string(int status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+KDA_API const char* kda_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+KDA_API int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

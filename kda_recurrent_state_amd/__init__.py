@@ -1,1 +1,191 @@
-"""MI355X-native gated delta-rule (KDA / Gated DeltaNet) state layer."""
+"""MI355X-native gated delta-rule (KDA / Gated DeltaNet) state layer.
+
+Thin Python binding over the C ABI in ``include/kda.h`` (``libkda.so``, built
+for gfx950 from ``csrc/``).  This module only marshals arguments: PyTorch
+provides device memory and the current HIP stream; every step of the layer
+runs in the library's HIP kernels.  There is no CPU or PyTorch fallback: if
+the library or a GPU is missing, calls raise.
+
+    o, S_T = chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None)
+    o, S   = decode_step(q, k, v, log_a, beta, S)        # S updated in place
+
+Shapes (tokens of all sequences packed along the first axis):
+    q, k [T, H, dk]; v [T, H, dv]; log_a [T, H, dk] (KDA) or [T, H] (Gated
+    DeltaNet); beta [T, H]; states [N, H, dk, dv] float32.  q/k/v are bf16 or
+    fp32 (o has the same dtype); log_a, beta and states are fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # loads the HIP runtime the library then shares
+
+__all__ = ["chunk_fwd", "decode_step", "KdaError", "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+_lock = threading.Lock()
+_lib = None
+
+KDA_F32, KDA_BF16 = 0, 1
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int64), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("qkv_dtype", ctypes.c_int32), ("scalar_decay", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("dv_split", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(build_if_missing: bool = True):
+    """Load libkda.so (building it with hipcc first if it is absent)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                if not build_if_missing:
+                    raise RuntimeError(f"{_LIB_PATH} is not built")
+                from . import _build
+                _build.build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            lib.kda_chunk_fwd.restype = ctypes.c_int
+            lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P]
+            lib.kda_decode_step.restype = ctypes.c_int
+            lib.kda_decode_step.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P]
+            lib.kda_status_string.restype = ctypes.c_char_p
+            lib.kda_status_string.argtypes = [ctypes.c_int]
+            lib.kda_last_error.restype = ctypes.c_char_p
+            lib.kda_last_error.argtypes = []
+            lib.kda_version.restype = ctypes.c_int
+            _lib = lib
+        return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise RuntimeError(f"{name} must be on a HIP device (got {t.device}); there is no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got {tuple(t.shape)})")
+
+
+def _check(lib, status):
+    if status != 0:
+        msg = lib.kda_last_error().decode() or lib.kda_status_string(status).decode()
+        raise KdaError(status, msg)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32 (got {t.dtype})")
+
+
+def _stream_handle(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, chunk_size: int = 0,
+              dv_split: int = 0, out=None, final_state=True, num_seqs: int | None = None):
+    """Chunked prefill over packed sequences; returns (o, S_T or None).
+
+    cu_seqlens: int32 device tensor [N+1], or None for num_seqs (default 1)
+    sequences of equal length.  final_state=False skips S_T; passing a tensor
+    writes S_T into it (it may be S0 itself)."""
+    lib = load_library()
+    _need(q, "q", ndim=3)
+    T, H, dk = q.shape
+    _need(k, "k", q.dtype, 3)
+    _need(v, "v", q.dtype, 3)
+    dv = v.shape[2]
+    if k.shape != q.shape or v.shape[:2] != (T, H):
+        raise ValueError("q, k, v shapes disagree")
+    _need(log_a, "log_a", torch.float32)
+    if log_a.shape == (T, H, dk):
+        scalar = 0
+    elif log_a.shape == (T, H):
+        scalar = 1
+    else:
+        raise ValueError(f"log_a must be [T,H,dk] or [T,H] (got {tuple(log_a.shape)})")
+    _need(beta, "beta", torch.float32)
+    if beta.shape != (T, H):
+        raise ValueError("beta must be [T,H]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32)
+        if S0.shape != (N, H, dk, dv):
+            raise ValueError(f"S0 must be [{N},{H},{dk},{dv}] (got {tuple(S0.shape)})")
+    o = out if out is not None else torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    _need(o, "out", q.dtype)
+    if isinstance(final_state, torch.Tensor):
+        ST = final_state
+        _need(ST, "final_state", torch.float32)
+    elif final_state:
+        ST = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    else:
+        ST = None
+    d = _Dims(N, H, T, dk, dv, _dtype_code(q), scalar, int(chunk_size), int(dv_split))
+    st = lib.kda_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
+                           _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(ST), _stream_handle(q.device))
+    _check(lib, st)
+    return o, ST
+
+
+def decode_step(q, k, v, log_a, beta, S, *, out=None, S_out=None):
+    """One token per sequence: q, k [N,H,dk], v [N,H,dv], log_a [N,H,dk] or
+    [N,H], beta [N,H], S [N,H,dk,dv].  Updates S in place unless S_out is
+    given; returns (o, state_after)."""
+    lib = load_library()
+    _need(q, "q", ndim=3)
+    N, H, dk = q.shape
+    _need(k, "k", q.dtype, 3)
+    _need(v, "v", q.dtype, 3)
+    dv = v.shape[2]
+    _need(log_a, "log_a", torch.float32)
+    if log_a.shape == (N, H, dk):
+        scalar = 0
+    elif log_a.shape == (N, H):
+        scalar = 1
+    else:
+        raise ValueError("log_a must be [N,H,dk] or [N,H]")
+    _need(beta, "beta", torch.float32)
+    _need(S, "S", torch.float32)
+    if S.shape != (N, H, dk, dv) or k.shape != q.shape or v.shape[:2] != (N, H) or beta.shape != (N, H):
+        raise ValueError("decode shapes disagree")
+    So = S if S_out is None else S_out
+    _need(So, "S_out", torch.float32)
+    o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    _need(o, "out", q.dtype)
+    d = _Dims(N, H, N, dk, dv, _dtype_code(q), scalar, 0, 0)
+    st = lib.kda_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
+                             _ptr(S), _ptr(So), _ptr(o), _stream_handle(q.device))
+    _check(lib, st)
+    return o, So

@@ -1,0 +1,177 @@
+// kda_api.cpp -- the extern "C" entry points declared in include/kda.h.
+//
+// Host-side argument validation, choice of kernel configuration, launch on the
+// caller's stream.  Nothing here allocates device memory or keeps state other
+// than the thread-local text of the last error.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return KDA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool width_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Common checks of the dims structure.
+int check_dims(const kda_dims_t* d) {
+    if (!d) return fail(KDA_ERR_INVALID_ARGUMENT, "dims is NULL");
+    if (d->num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs = %d < 0", d->num_seqs);
+    if (d->num_heads <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_heads = %d <= 0", d->num_heads);
+    if (d->total_tokens < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "total_tokens = %lld < 0", (long long)d->total_tokens);
+    if (d->qkv_dtype != KDA_F32 && d->qkv_dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "qkv_dtype = %d is not KDA_F32 or KDA_BF16", d->qkv_dtype);
+    if (d->scalar_decay != 0 && d->scalar_decay != 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "scalar_decay = %d is not 0 or 1", d->scalar_decay);
+    if (!width_ok(d->dk) || !width_ok(d->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "dk = %d, dv = %d: each must be 16, 32, 64 or 128", d->dk, d->dv);
+    return KDA_OK;
+}
+
+// Non-null pointers with the alignment the kernels' vector accesses need.
+int check_ptrs(const void* const* ptrs, const char* const* names, const int* align, int count) {
+    for (int i = 0; i < count; ++i) {
+        if (!ptrs[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+        if ((uintptr_t)ptrs[i] % (uintptr_t)align[i])
+            return fail(KDA_ERR_MISALIGNED, "%s is not %d-byte aligned", names[i], align[i]);
+    }
+    return KDA_OK;
+}
+
+// Smallest dv split that gives at least 256 workgroups (one per compute unit),
+// among the splits compiled for this shape.
+int choose_split(const kda_dims_t* d, int chunk) {
+    const int64_t units = (int64_t)d->num_seqs * d->num_heads;
+    int best = 0;
+    for (int split = 1; split <= 8; split *= 2) {
+        if (d->dv % split) break;
+        if (!kda::chunk_supported(d->qkv_dtype, d->dk, d->dv / split, chunk, d->scalar_decay)) continue;
+        best = split;
+        if (units * split >= 256) break;
+    }
+    return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return 10000; }
+
+const char* kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+        default: return "KDA_ERR_UNKNOWN";
+    }
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+int kda_chunk_fwd(const kda_dims_t* d, const void* q, const void* k, const void* v,
+                  const float* log_a, const float* beta, const float* S0,
+                  const int32_t* cu_seqlens, void* o, float* S_T, void* stream) {
+    int st = check_dims(d);
+    if (st) return st;
+    const int chunk = d->chunk_size == 0 ? 32 : d->chunk_size;
+    if (chunk != 32 && chunk != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size = %d: must be 0, 32 or 64", d->chunk_size);
+    if (d->num_seqs == 0) {
+        if (d->total_tokens != 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs = 0 but total_tokens = %lld",
+                        (long long)d->total_tokens);
+        return ok();
+    }
+    if (!cu_seqlens && d->total_tokens % d->num_seqs != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "cu_seqlens is NULL but total_tokens = %lld is not a multiple of num_seqs = %d",
+                    (long long)d->total_tokens, d->num_seqs);
+    if (d->total_tokens > 0) {
+        const void* ptrs[] = {q, k, v, log_a, beta, o};
+        const char* names[] = {"q", "k", "v", "log_a", "beta", "o"};
+        const int align[] = {16, 16, 16, d->scalar_decay ? 4 : 16, 4, 16};
+        if ((st = check_ptrs(ptrs, names, align, 6))) return st;
+    }
+    if (S0 && !aligned16(S0)) return fail(KDA_ERR_MISALIGNED, "S0 is not 16-byte aligned");
+    if (S_T && !aligned16(S_T)) return fail(KDA_ERR_MISALIGNED, "S_T is not 16-byte aligned");
+    if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u))
+        return fail(KDA_ERR_MISALIGNED, "cu_seqlens is not 4-byte aligned");
+
+    int split = d->dv_split;
+    if (split == 0) {
+        split = choose_split(d, chunk);
+        if (split == 0)
+            return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, dk %d, dv %d, chunk %d",
+                        d->qkv_dtype, d->dk, d->dv, chunk);
+    } else {
+        if (split != 1 && split != 2 && split != 4 && split != 8)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "dv_split = %d: must be 0, 1, 2, 4 or 8", split);
+        if (d->dv % split || !kda::chunk_supported(d->qkv_dtype, d->dk, d->dv / split, chunk, d->scalar_decay))
+            return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, dk %d, dv %d / split %d, chunk %d",
+                        d->qkv_dtype, d->dk, d->dv, split, chunk);
+    }
+    const int64_t blocks = (int64_t)d->num_seqs * d->num_heads * split;
+    if (blocks > 0x7fffffff)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "too many (sequence, head, slice) units: %lld", (long long)blocks);
+
+    kda::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.beta = beta; a.S0 = S0;
+    a.cu_seqlens = cu_seqlens; a.o = o; a.S_T = S_T;
+    a.num_seqs = d->num_seqs; a.num_heads = d->num_heads; a.total_tokens = d->total_tokens;
+    a.dk = d->dk; a.dv = d->dv; a.dtype = d->qkv_dtype; a.scalar_decay = d->scalar_decay;
+    a.chunk = chunk; a.split = split;
+    hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int kda_decode_step(const kda_dims_t* d, const void* q, const void* k, const void* v,
+                    const float* log_a, const float* beta, const float* S_in, float* S_out,
+                    void* o, void* stream) {
+    int st = check_dims(d);
+    if (st) return st;
+    if (d->total_tokens != d->num_seqs)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "decode needs total_tokens (%lld) == num_seqs (%d)",
+                    (long long)d->total_tokens, d->num_seqs);
+    if (d->num_seqs == 0) return ok();
+    const void* ptrs[] = {q, k, v, log_a, beta, S_in, S_out, o};
+    const char* names[] = {"q", "k", "v", "log_a", "beta", "S_in", "S_out", "o"};
+    const int align[] = {16, 16, 16, 4, 4, 16, 16, 16};
+    if ((st = check_ptrs(ptrs, names, align, 8))) return st;
+    if (!kda::decode_supported(d->qkv_dtype, d->dk, d->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "no decode kernel for dtype %d, dk %d, dv %d", d->qkv_dtype, d->dk, d->dv);
+    const int64_t heads = (int64_t)d->num_seqs * d->num_heads;
+    if (heads > 0x7fffffff) return fail(KDA_ERR_INVALID_ARGUMENT, "too many states: %lld", (long long)heads);
+    hipError_t e = kda::launch_decode(d->qkv_dtype, d->dk, d->dv, d->scalar_decay, heads, q, k, v, log_a,
+                                      beta, S_in, S_out, o, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// kda_launch.hpp -- host-side launchers shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_a;
+    const float* beta;
+    const float* S0;
+    const int32_t* cu_seqlens;  // device; may be null (equal lengths)
+    void* o;
+    float* S_T;                 // may be null
+    int32_t num_seqs;
+    int32_t num_heads;
+    int64_t total_tokens;
+    int32_t dk, dv;
+    int32_t dtype;              // 0 fp32, 1 bf16
+    int32_t scalar_decay;
+    int32_t chunk;              // 32 or 64
+    int32_t split;              // workgroups per (sequence, head) along dv
+};
+
+bool decode_supported(int dtype, int dk, int dv);
+hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int64_t heads, const void* q,
+                         const void* k, const void* v, const float* log_a, const float* beta,
+                         const float* S_in, float* S_out, void* o, hipStream_t stream);
+
+// true if a chunk kernel exists for (dtype, dk, dv / split, chunk)
+bool chunk_supported(int dtype, int dk, int dvs, int chunk, int scalar);
+hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream);
+
+}  // namespace kda

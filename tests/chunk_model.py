@@ -1,0 +1,148 @@
+"""fp64 numpy model of the chunkwise (WY) algorithm that the HIP prefill runs.
+
+Test infrastructure: it documents and checks the derivation of the chunk form
+(page "The argument, in one page", table row "Chunkwise / WY": the same update,
+reorganised so each chunk of C tokens needs one C x C triangular solve plus dense
+products) against the token-by-token oracle.  It is neither the oracle nor the
+GPU path, and the GPU path does not use it.
+
+Derivation, per (sequence, head) and chunk, local tokens t = 0..C-1, state S0 at
+the chunk start, g_t = sum_{j<=t} log a_j (per key channel), with X_t = Diag(e^-g_t) S_t:
+
+  X_t = X_{t-1} + kc_t^T e_t + kt_t^T (b_t v_t),   e_t = -b_t kb_t X_{t-1}
+  kb_t = k_t e^{g_{t-1}}, kc_t = k_t e^{-g_{t-1}}, kt_t = k_t e^{-g_t}, qb_t = q_t e^{g_t}
+
+Solving the recurrence for the rows e_t of E gives (I + A) E = -diag(b) Kb S0 - diag(b) L diag(b) V:
+
+  A  = strict_lower(diag(b) Kb Kc^T)      L  = strict_lower(Kb Kt^T)
+  P1 = lower(Qb Kc^T)                      P2 = lower(Qb Kt^T)
+  T = (I + A)^-1,  W = T diag(b) Kb,  U = T diag(b) L diag(b) V,  E = -(W S0 + U)
+  O   = Qb S0 + P1 E + P2 diag(b) V
+  S_C = Diag(e^{g_C}) S0 + (Kc Diag(e^{g_C}))^T E + (Kt Diag(e^{g_C}))^T diag(b) V
+
+Every exponent kept by the masks is <= 0.  For the products on matrix cores the
+decay factors are split into a row factor and a column factor around a
+reference per 16-token sub-block: the mid-block value of g for blocks on the
+diagonal (both factors stay within e^{+-8*8.5} for |log a| <= 8), and for a
+block pair (bt > bi) the row factor is additionally scaled by e^{mu_bt - mu_bi}
+<= 1; that product can only underflow where the true term is below ~1e-8 of
+the largest factor product, so dropping it is harmless.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SUB = 16  # sub-block length for the decay references
+
+
+def _bf16(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def _unit_lower_inverse(A):
+    """(I + A)^-1 for strictly lower A by 16x16 blocks: diagonal blocks by
+    forward substitution, off-diagonal blocks by T_ij = -T_ii sum_k A_ik T_kj."""
+    C = A.shape[0]
+    nb = (C + SUB - 1) // SUB
+    T = np.zeros_like(A)
+    for b in range(nb):
+        s = slice(b * SUB, min(C, (b + 1) * SUB))
+        Ab = A[s, s]
+        n = Ab.shape[0]
+        Tb = np.eye(n)
+        for r in range(n):
+            for j in range(r):
+                Tb[r, j] = -Ab[r, j:r] @ Tb[j:r, j]
+        T[s, s] = Tb
+    for bi in range(nb):
+        for bj in range(bi):
+            si = slice(bi * SUB, min(C, (bi + 1) * SUB))
+            acc = np.zeros((si.stop - si.start, min(C, (bj + 1) * SUB) - bj * SUB))
+            for bk in range(bj, bi):
+                sk = slice(bk * SUB, min(C, (bk + 1) * SUB))
+                acc += A[si, sk] @ T[sk, bj * SUB:min(C, (bj + 1) * SUB)]
+            T[si, bj * SUB:min(C, (bj + 1) * SUB)] = -T[si, si] @ acc
+    return T
+
+
+def chunk_step(q, k, v, la, beta, S, bf16=False):
+    """One chunk (C tokens, C a multiple of 16) of one (sequence, head).
+    q, k [C, dk]; v [C, dv]; la [C, dk]; beta [C]; S [dk, dv].  Returns (O, S_C).
+    bf16=True rounds every matrix-core operand to bf16 as the GPU path does."""
+    C, dk = q.shape
+    rnd = _bf16 if bf16 else (lambda x: x)
+    nb = C // SUB
+    # cumulative log-decay, local to each sub-block, and block offsets
+    lam = np.zeros((C, dk))
+    Lam = np.zeros((nb, dk))
+    for b in range(nb):
+        lam[b * SUB:(b + 1) * SUB] = np.cumsum(la[b * SUB:(b + 1) * SUB], axis=0)
+        Lam[b] = lam[(b + 1) * SUB - 1]
+    rho = np.concatenate([np.zeros((1, dk)), np.cumsum(Lam, axis=0)])  # [nb+1, dk]
+    gC = rho[nb]
+    mid = np.array([lam[b * SUB + SUB // 2 - 1] for b in range(nb)])  # local g at mid
+    mu = rho[:nb] + mid  # absolute g at mid
+    rin = np.zeros((C, dk))
+    rex = np.zeros((C, dk))
+    for t in range(C):
+        b = t // SUB
+        rin[t] = np.exp(lam[t] - mid[b])
+        prev = lam[t - 1] if t % SUB else np.zeros(dk)
+        rex[t] = np.exp(prev - mid[b])
+    cin, cex = 1.0 / rin, 1.0 / rex
+    blk = np.arange(C) // SUB
+    emu = np.exp(mu)[blk]  # e^{mu_b} per token row
+    ecmu = np.exp(gC[None, :] - mu)[blk]
+    Kr, Qr, Kce, Kci = rnd(k * rex), rnd(q * rin), rnd(k * cex), rnd(k * cin)
+    Kbar = rnd(k * rex * emu)
+    Qbar = rnd(q * rin * emu)
+    Kcc = rnd(k * cex * ecmu)
+    Ktc = rnd(k * cin * ecmu)
+    A = np.zeros((C, C)); L = np.zeros((C, C)); P1 = np.zeros((C, C)); P2 = np.zeros((C, C))
+    for bt in range(nb):
+        st = slice(bt * SUB, (bt + 1) * SUB)
+        for bi in range(bt + 1):
+            si = slice(bi * SUB, (bi + 1) * SUB)
+            if bt == bi:
+                kr, qr = Kr[st], Qr[st]
+            else:
+                F = np.exp(mu[bt] - mu[bi])
+                kr, qr = rnd(Kr[st] * F), rnd(Qr[st] * F)
+            A[st, si] = kr @ Kce[si].T
+            L[st, si] = kr @ Kci[si].T
+            P1[st, si] = qr @ Kce[si].T
+            P2[st, si] = qr @ Kci[si].T
+    A = np.tril(A, -1) * beta[:, None]
+    L = np.tril(L, -1)
+    P1 = np.tril(P1)
+    P2 = np.tril(P2)
+    T = _unit_lower_inverse(A)
+    bV = rnd(beta[:, None] * v)
+    Tb = rnd(T * beta[None, :])  # T diag(b), shared by W and U
+    W = rnd(Tb @ Kbar)
+    U = Tb @ rnd(rnd(L) @ bV)
+    E = -(W @ rnd(S) + U)
+    Er = rnd(E)
+    O = Qbar @ rnd(S) + rnd(P1) @ Er + rnd(P2) @ bV
+    S_new = np.exp(gC)[:, None] * S + Kcc.T @ Er + Ktc.T @ bV
+    return O, S_new
+
+
+def chunk_forward(q, k, v, la, beta, S0=None, C=64, bf16=False):
+    """Whole sequence of one head: q, k [T, dk], v [T, dv], la [T, dk] or [T],
+    beta [T].  Partial last chunk padded with k=q=v=0, beta=0, log a=0."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    if la.ndim == 1:
+        la = np.repeat(la[:, None], dk, axis=1)
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    O = np.zeros((T, dv))
+    for s in range(0, T, C):
+        e = min(T, s + C)
+        n = e - s
+        pad = lambda x, w: np.concatenate([x[s:e], np.zeros((C - n,) + x.shape[1:])]) if n < C else x[s:e]
+        Oc, S = chunk_step(pad(q, 0), pad(k, 0), pad(v, 0), pad(la, 0), pad(beta, 0), S, bf16=bf16)
+        O[s:e] = Oc[:n]
+    return O, S

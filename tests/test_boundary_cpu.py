@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments with the documented status codes before touching a GPU (CPU only).
+
+Fake device addresses are used: every case below is refused by host-side
+validation, so nothing is dereferenced or launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kda_recurrent_state_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED = 0, 1, 2, 3
+GOOD = 0x7F0000000000  # 16-byte aligned fake device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"KDA_API\s+[\w\s\*]+?\b(kda_\w+)\s*\(", text)
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert {"kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_last_error",
+            "kda_version"} <= set(names)
+
+
+def test_every_declared_symbol_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported by {kda.library_path()}"
+
+
+def dims(**kw):
+    base = dict(num_seqs=2, num_heads=4, total_tokens=128, dk=128, dv=128, qkv_dtype=1,
+                scalar_decay=0, chunk_size=0, dv_split=0)
+    base.update(kw)
+    return kda._Dims(**base)
+
+
+def prefill(lib, d, q=GOOD, k=GOOD, v=GOOD, la=GOOD, beta=GOOD, S0=None, cu=GOOD, o=GOOD, ST=GOOD):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    dp = None if d is None else ctypes.byref(d)
+    return lib.kda_chunk_fwd(dp, P(q), P(k), P(v), P(la), P(beta), P(S0), P(cu), P(o), P(ST), None)
+
+
+def decode(lib, d, q=GOOD, k=GOOD, v=GOOD, la=GOOD, beta=GOOD, Si=GOOD, So=GOOD, o=GOOD):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_decode_step(ctypes.byref(d), P(q), P(k), P(v), P(la), P(beta), P(Si), P(So), P(o), None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(d=None), INVALID),
+    (dict(d=dims(num_heads=0)), INVALID),
+    (dict(d=dims(num_seqs=-1)), INVALID),
+    (dict(d=dims(total_tokens=-5)), INVALID),
+    (dict(d=dims(qkv_dtype=7)), INVALID),
+    (dict(d=dims(scalar_decay=2)), INVALID),
+    (dict(d=dims(dk=48)), UNSUPPORTED),
+    (dict(d=dims(dv=256)), UNSUPPORTED),
+    (dict(d=dims(chunk_size=48)), UNSUPPORTED),
+    (dict(d=dims(dv_split=3)), INVALID),
+    (dict(d=dims(qkv_dtype=1, dk=16, dv=16)), UNSUPPORTED),  # no bf16 kernel below dk=32
+    (dict(d=dims(), q=None), INVALID),
+    (dict(d=dims(), beta=None), INVALID),
+    (dict(d=dims(), o=None), INVALID),
+    (dict(d=dims(), q=GOOD + 2), MISALIGNED),
+    (dict(d=dims(), la=GOOD + 4), MISALIGNED),
+    (dict(d=dims(), S0=GOOD + 8), MISALIGNED),
+    (dict(d=dims(), cu=GOOD + 2), MISALIGNED),
+    (dict(d=dims(total_tokens=127), cu=None), INVALID),
+    (dict(d=dims(num_seqs=0, total_tokens=5)), INVALID),
+    (dict(d=dims(num_seqs=0, total_tokens=0), q=None, cu=None), OK),  # nothing to do
+])
+def test_prefill_validation(lib, case, expect):
+    st = prefill(lib, **case)
+    assert st == expect, (st, lib.kda_last_error())
+    if expect != OK:
+        assert lib.kda_last_error().decode() != ""
+    else:
+        assert lib.kda_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(d=dims(total_tokens=3)), INVALID),
+    (dict(d=dims(total_tokens=2), Si=None), INVALID),
+    (dict(d=dims(total_tokens=2), So=GOOD + 4), MISALIGNED),
+    (dict(d=dims(total_tokens=2, dk=24)), UNSUPPORTED),
+    (dict(d=dims(num_seqs=0, total_tokens=0), q=None), OK),
+])
+def test_decode_validation(lib, case, expect):
+    assert decode(lib, **case) == expect
+
+
+def test_scalar_arrays_need_only_4_byte_alignment(lib):
+    """beta and a scalar log_a pass with 4-byte alignment; the call then stops
+    at the misaligned output, so nothing is launched."""
+    st = prefill(lib, dims(scalar_decay=1), la=GOOD + 4, beta=GOOD + 4, o=GOOD + 2)
+    assert st == MISALIGNED and lib.kda_last_error().decode().startswith("o is not")
+    st = decode(lib, dims(total_tokens=2), la=GOOD + 4, beta=GOOD + 4, o=GOOD + 2)
+    assert st == MISALIGNED and lib.kda_last_error().decode().startswith("o is not")
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(3) == b"KDA_ERR_MISALIGNED"
+    assert lib.kda_status_string(99) == b"KDA_ERR_UNKNOWN"
+    assert lib.kda_version() >= 10000
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 1, 32)
+    with pytest.raises(RuntimeError, match="HIP device"):
+        kda.chunk_fwd(x, x, x, torch.zeros(4, 1, 32), torch.zeros(4, 1))

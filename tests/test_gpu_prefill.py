@@ -1,0 +1,179 @@
+"""Chunked prefill on the GPU against the fp64 oracle, plus self-consistency."""
+import numpy as np
+import pytest
+import torch
+
+import kda_recurrent_state_amd as kda
+from kda_recurrent_state_amd.workloads import WORKLOADS, generate, scaled
+from tests.parity import TOL, log, max_rel_err, np64, oracle_all, oracle_unit
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def gpu_prefill(inp, **kw):
+    o, ST = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], S0=inp["S0"],
+                          cu_seqlens=inp["cu_seqlens"], **kw)
+    torch.cuda.synchronize()
+    return o, ST
+
+
+def check_all(inp, o, ST, tol, what=""):
+    ro, rS = oracle_all({k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()})
+    eo, es = max_rel_err(o, ro), max_rel_err(ST, rS)
+    log(f"  {what} err o {eo:.2e} S {es:.2e}")
+    assert eo <= tol, f"o error {eo}"
+    assert es <= tol, f"S_T error {es}"
+    return eo, es
+
+
+def test_prefill_kda_t64_d16_fp32():
+    """B=1, H=1, T=64, dk=dv=16, fp32 inputs, zero initial state: 1e-4."""
+    log("prefill C1: KDA T=64 d=16 fp32")
+    inp = generate(WORKLOADS["kda_t64_d16_fp32"], seed=0, device=DEV)
+    o, ST = gpu_prefill(inp)
+    check_all(inp, o, ST, 1e-4, "C1")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (64, 64), (32, 16), (64, 32)])
+@pytest.mark.parametrize("scalar", [False, True])
+def test_prefill_fp32_varlen(dk, dv, scalar):
+    log(f"prefill fp32 varlen dk={dk} dv={dv} scalar={scalar}")
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=4, heads=2, dk=dk, dv=dv, dtype=torch.float32,
+               scalar_decay=scalar)
+    inp = generate(w, seed=dk * 3 + dv + scalar, device=DEV, lengths=[37, 0, 96, 5])
+    o, ST = gpu_prefill(inp)
+    check_all(inp, o, ST, 1e-4)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (32, 32), (128, 64), (64, 128), (128, 32)])
+@pytest.mark.parametrize("scalar", [False, True])
+def test_prefill_bf16_varlen(dk, dv, scalar):
+    log(f"prefill bf16 varlen dk={dk} dv={dv} scalar={scalar}")
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=4, heads=3, dk=dk, dv=dv, scalar_decay=scalar)
+    inp = generate(w, seed=dk + dv + scalar, device=DEV, lengths=[45, 0, 170, 96])
+    o, ST = gpu_prefill(inp)
+    check_all(inp, o, ST, 2e-2)
+
+
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
+def test_prefill_dv_split_invariance(split):
+    """Splitting dv over workgroups changes nothing beyond rounding."""
+    log(f"prefill dv_split={split}")
+    w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seqlen=200, heads=2, dk=64, dv=64)
+    inp = generate(w, seed=5, device=DEV)
+    try:
+        o, ST = gpu_prefill(inp, dv_split=split)
+    except kda.KdaError as e:
+        assert e.status == 2  # configuration not compiled
+        pytest.skip(f"dv_split={split} not compiled for dk=dv=64")
+    check_all(inp, o, ST, 2e-2, f"split {split}")
+
+
+def test_prefill_chunk64_matches_chunk32():
+    log("prefill chunk 64 vs 32")
+    w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seqlen=300, heads=2, dk=32, dv=32)
+    inp = generate(w, seed=6, device=DEV)
+    o32, S32 = gpu_prefill(inp, chunk_size=32)
+    o64, S64 = gpu_prefill(inp, chunk_size=64)
+    check_all(inp, o64, S64, 2e-2, "C=64")
+    assert max_rel_err(o64, o32) <= 2e-2 and max_rel_err(S64, S32) <= 2e-2
+
+
+def test_prefill_continuation_and_alias():
+    """Split a sequence at a point that is not a chunk multiple, feed S_T back as
+    S0 (written in place over S0), compare with one pass."""
+    log("prefill continuation")
+    w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], n_seqs=1, seqlen=333, heads=2)
+    inp = generate(w, seed=7, device=DEV)
+    o, ST = gpu_prefill(inp)
+    cut = 77
+    part = lambda t, a, b: t[a:b].contiguous()
+    S = inp["S0"].clone()
+    o1, _ = kda.chunk_fwd(part(inp["q"], 0, cut), part(inp["k"], 0, cut), part(inp["v"], 0, cut),
+                          part(inp["log_a"], 0, cut), part(inp["beta"], 0, cut), S0=S, final_state=S)
+    o2, _ = kda.chunk_fwd(part(inp["q"], cut, 333), part(inp["k"], cut, 333), part(inp["v"], cut, 333),
+                          part(inp["log_a"], cut, 333), part(inp["beta"], cut, 333), S0=S, final_state=S)
+    torch.cuda.synchronize()
+    assert max_rel_err(torch.cat([o1, o2]), o) <= 2e-2
+    assert max_rel_err(S, ST) <= 2e-2
+    check_all(inp, o, ST, 2e-2, "one pass")
+
+
+def test_prefill_deterministic():
+    log("prefill determinism")
+    w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seqlen=256, heads=4)
+    inp = generate(w, seed=8, device=DEV)
+    a = gpu_prefill(inp)
+    b = gpu_prefill(inp)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_prefill_empty_and_no_state():
+    """All sequences empty: S_T = S0; S0 = None means zeros."""
+    log("prefill empty sequences")
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=3, heads=2)
+    inp = generate(w, seed=9, device=DEV, lengths=[0, 0, 0])
+    o, ST = gpu_prefill(inp)
+    assert torch.equal(ST, inp["S0"])
+    inp2 = generate(w, seed=10, device=DEV, lengths=[20, 0, 64])
+    inp2["S0"] = None
+    o2, ST2 = gpu_prefill(inp2)
+    check_all(inp2, o2, ST2, 2e-2, "S0=None")
+
+
+def test_chunked_matches_recurrent():
+    """Prefill and a chain of single-token decode steps agree on the GPU."""
+    log("chunked vs recurrent")
+    w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], n_seqs=1, seqlen=70, heads=3)
+    inp = generate(w, seed=11, device=DEV)
+    o, ST = gpu_prefill(inp)
+    S = inp["S0"].clone()
+    outs = []
+    for t in range(70):
+        ot, S = kda.decode_step(inp["q"][t:t + 1], inp["k"][t:t + 1], inp["v"][t:t + 1],
+                                inp["log_a"][t:t + 1], inp["beta"][t:t + 1], S)
+        outs.append(ot)
+    torch.cuda.synchronize()
+    assert max_rel_err(torch.cat(outs), o) <= 2e-2
+    assert max_rel_err(S, ST) <= 2e-2
+
+
+# ---- full sizes, in the launch configuration the benchmark times ------------------------
+def test_prefill_gdn_h16_t4096_full():
+    """Gated DeltaNet, H=16, T=4096, dk=dv=128: every head checked."""
+    log("prefill C2 full: GDN H=16 T=4096")
+    inp = generate(WORKLOADS["gdn_h16_t4096_d128_bf16"], seed=2, device=DEV)
+    o, ST = gpu_prefill(inp)
+    check_all(inp, o, ST, 2e-2, "C2")
+
+
+def _sampled(inp, o, ST, units, tol):
+    worst_o = worst_s = 0.0
+    for n, h in units:
+        ro, rS = oracle_unit({k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}, n, h)
+        cu = inp["cu_seqlens"].cpu().numpy()
+        eo = max_rel_err(o[cu[n]:cu[n + 1], h], ro)
+        es = max_rel_err(ST[n, h], rS)
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+    log(f"  sampled {len(units)} units: worst err o {worst_o:.2e} S {worst_s:.2e}")
+    assert worst_o <= tol and worst_s <= tol
+
+
+def test_prefill_kda_b2_h32_t32768_sampled():
+    """B=2, H=32, T=32768, log_a clipped at -8: whole batch on the GPU, 4 units
+    checked against the oracle."""
+    log("prefill C3 full: KDA B=2 H=32 T=32768")
+    inp = generate(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seed=3, device=DEV)
+    o, ST = gpu_prefill(inp)
+    _sampled(inp, o, ST, [(0, 0), (0, 31), (1, 7), (1, 20)], 2e-2)
+
+
+def test_prefill_varlen_64seq_sampled():
+    """64 packed sequences, lengths U[512, 16384], H=32: 6 units checked."""
+    log("prefill C5 full: varlen 64 sequences")
+    inp = generate(WORKLOADS["kda_varlen_64seq_h32_d128"], seed=5, device=DEV)
+    o, ST = gpu_prefill(inp)
+    L = inp["lengths"]
+    units = [(int(np.argmax(L)), 3), (int(np.argmin(L)), 30), (0, 0), (17, 11), (40, 5), (63, 31)]
+    _sampled(inp, o, ST, units, 2e-2)
