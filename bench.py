@@ -1,0 +1,309 @@
+"""Benchmark of the KDA state layer on one MI355X.
+
+Prints ONE JSON line.  The timed step is one chunked prefill over the KDA
+batch B=2, H=32, T=32768, dk=dv=128 (bf16 q/k/v, fp32 per-channel log_a
+clipped to [-8, 0], fp32 state); `value` is prefill tokens/s (each token
+counted once across heads).  The decode leg (256 sequences x 32 heads,
+dk=dv=128, 100 chained steps, fp32 state streamed once per step) is timed in
+the same run and reported under "decode" in state GB/s.  All inputs are seeded
+synthetic tensors, resident on the GPU before timing starts.
+
+Timing uses HIP events recorded on the stream the kernels are launched on
+(torch's current stream, which the library receives).  The fp64 CPU oracle is
+timed afterwards on a bounded sample of the same prefill workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --copy-calibration   # plain device copy of known size, for counters
+    python bench.py --record-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+        # writes profiles/traffic_counters.json from four rocprofv3 --pmc output
+        # folders (FETCH_SIZE and WRITE_SIZE of a bench run, then of --copy-calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (MFMA %peak) + decode-step state GB/s, 1 MI355X"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = {
+    "prefill": ["kda_recurrent_state_amd/csrc/kda_chunk.hip", "kda_recurrent_state_amd/csrc/kda_device.hpp"],
+    "decode": ["kda_recurrent_state_amd/csrc/kda_decode.hip", "kda_recurrent_state_amd/csrc/kda_device.hpp"],
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(kind):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_algorithmic(w, chunk_alg=64):
+    """Algorithmic bytes and flops of one prefill pass (what the method must move
+    and compute, not what the kernel executes).  Bytes per token-head: q, k, v
+    in bf16, log_a fp32 per channel, beta fp32, o bf16; plus S0 read and S_T
+    written once per (sequence, head).  Flops per chunk of C tokens per head:
+    10 C^2 dk + 6 C^2 dv + 8 C dk dv + (2/3) C^3 (four C x C Gram products, W,
+    U, E, O, the two state products, and the triangular solve) at C = 64."""
+    th = w.n_seqs * w.seqlen * w.heads
+    per_th = 2 * (2 * w.dk + w.dv) + 4 * w.dk + 4 + 2 * w.dv
+    states = w.n_seqs * w.heads * 2 * 4 * w.dk * w.dv
+    C, dk, dv = chunk_alg, w.dk, w.dv
+    per_chunk = 10 * C * C * dk + 6 * C * C * dv + 8 * C * dk * dv + (2.0 / 3.0) * C ** 3
+    return th * per_th + states, th * per_chunk / C
+
+
+def decode_algorithmic(w):
+    """Bytes of one decode step: the fp32 state read and written once, plus the
+    token's q, k, v (bf16), log_a (fp32 per channel), beta and o."""
+    per = 2 * 4 * w.dk * w.dv + 2 * (2 * w.dk + w.dv) + 4 * w.dk + 4 + 2 * w.dv
+    return w.n_seqs * w.heads * per
+
+
+def stored_traffic(kind, launch_bytes):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except OSError:
+        return None
+    ent = data.get(kind)
+    if not ent or ent.get("source_hash") != source_hash(kind):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def time_events(fn, iters, stream):
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3  # seconds
+
+
+def copy_calibration(steps):
+    """A plain device-to-device copy of 1 GiB, `steps` times: the reference
+    against which the FETCH_SIZE / WRITE_SIZE counters are scaled."""
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": steps}))
+
+
+KERNEL_SYMBOLS = {"prefill": "kda_chunk_kernel", "decode": "kda_decode_kernel"}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _counter_means(folder, counter):
+    """Mean counter value (KiB per dispatch) per kernel name in a rocprofv3 csv folder."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    acc = {}
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def record_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) scaled by what the same counters read for a plain 1 GiB copy."""
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    cfetch, cwrite = _counter_means(cfetch_dir, "FETCH_SIZE"), _counter_means(cwrite_dir, "WRITE_SIZE")
+    copy_kib = (1 << 30) / 1024.0
+    fr = copy_kib / cfetch[COPY_KERNEL]
+    wr = copy_kib / cwrite[COPY_KERNEL]
+    out = {"copy_calibration": {"kernel": COPY_KERNEL, "bytes_each_way": 1 << 30,
+                                "fetch_kib": cfetch[COPY_KERNEL], "write_kib": cwrite[COPY_KERNEL],
+                                "fetch_scale": fr, "write_scale": wr}}
+    for kind, sym in KERNEL_SYMBOLS.items():
+        f = [v for k, v in fetch.items() if sym in k]
+        w = [v for k, v in write.items() if sym in k]
+        if len(f) != 1 or len(w) != 1:
+            continue
+        rb, wb = f[0] * fr * 1024.0, w[0] * wr * 1024.0
+        out[kind] = {"kernel": sym, "source_hash": source_hash(kind), "fetch_kib_raw": f[0],
+                     "write_kib_raw": w[0], "hbm_read_bytes": rb, "hbm_write_bytes": wb,
+                     "hbm_bytes_per_launch": rb + wb}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--record-traffic", nargs=4, metavar="DIR", default=None)
+    args = ap.parse_args()
+
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the layer shards over (sequence, head) with no "
+              "exchange, so run it once per GPU; --gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+
+    import numpy as np
+    import torch
+
+    import kda_recurrent_state_amd as kda
+    from kda_recurrent_state_amd.workloads import WORKLOADS, generate
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {"metric": METRIC}
+
+    # ---------------- prefill: KDA B=2, H=32, T=32768 ----------------
+    wp = WORKLOADS["kda_b2_h32_t32768_d128_bf16"]
+    if args.only in (None, "prefill"):
+        log("generating prefill inputs")
+        x = generate(wp, seed=3, device=dev)
+        o = torch.empty((x["q"].shape[0], wp.heads, wp.dv), dtype=wp.dtype, device=dev)
+        ST = torch.empty((wp.n_seqs, wp.heads, wp.dk, wp.dv), dtype=torch.float32, device=dev)
+
+        def step():
+            kda.chunk_fwd(x["q"], x["k"], x["v"], x["log_a"], x["beta"], S0=x["S0"],
+                          cu_seqlens=x["cu_seqlens"], out=o, final_state=ST)
+
+        log("prefill warmup")
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        log("prefill timed")
+        t = time_events(step, args.steps, stream)
+        torch.cuda.synchronize()
+        per = t / args.steps
+        tokens = wp.n_seqs * wp.seqlen
+        B, F = prefill_algorithmic(wp)
+        gbs = B / per / 1e9
+        tflops = F / per / 1e12
+        out.update({
+            "value": tokens / per, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": per * 1e3, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic: seeded tensors with the layer's shapes and value distributions (no dataset)",
+            "config": {"workload": wp.name, "batch": wp.n_seqs, "heads": wp.heads, "seq_len": wp.seqlen,
+                       "dk": wp.dk, "dv": wp.dv, "state": "fp32", "chunk": 32, "dv_split": "auto"},
+        })
+        out["roofline"] = {
+            "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "traffic": stored_traffic("prefill", B),
+            "kernel": "kda_chunk_kernel", "algorithmic_bytes_per_launch": B,
+            "avg_launch_ms": per * 1e3,
+        }
+        out["mfma"] = {"algorithmic_tflop_per_launch": F / 1e12, "achieved_tflops": tflops,
+                       "peak_tflops": PEAK_BF16_TFLOPS, "pct_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+                       "note": "algorithmic flops at C=64; bf16 dense peak"}
+        # quick parity on the timed output: first 2048 tokens of (sequence 0, head 0)
+        from oracle import kda_oracle
+        sl = lambda t: t[:2048, 0:1].cpu()
+        ro, _ = kda_oracle(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_a"]), sl(x["beta"]),
+                           S0=x["S0"][0:1, 0:1].cpu())
+        go = o[:2048, 0].double().cpu().numpy()
+        perr = float(np.abs(go - ro[:, 0]).max() / np.abs(ro).max())
+        out["parity"] = {"prefill_o_max_rel_err": perr, "tol": 2e-2, "sample": "seq 0, head 0, tokens 0..2047"}
+        log(f"prefill: {per*1e3:.3f} ms/step, {tokens/per/1e6:.2f} Mtok/s, {gbs:.0f} GB/s, "
+            f"{tflops:.1f} TFLOP/s, parity {perr:.2e}")
+
+        if not args.no_cpu_baseline:
+            ncpu = min(16, os.cpu_count() or 1)
+            log(f"cpu oracle on the whole prefill batch, {ncpu} threads")
+            hx = {k: x[k].cpu() for k in ("q", "k", "v", "log_a", "beta", "S0")}
+            t0 = time.perf_counter()
+            kda_oracle(hx["q"], hx["k"], hx["v"], hx["log_a"], hx["beta"], S0=hx["S0"],
+                       cu_seqlens=x["cu_seqlens"].cpu().numpy(), threads=ncpu)
+            dt = time.perf_counter() - t0
+            out["cpu_baseline"] = {
+                "value": tokens / dt, "unit": "tokens/s", "cores": ncpu, "kind": "oracle",
+                "sample": f"the whole timed prefill batch ({wp.n_seqs} x {wp.seqlen} tokens x "
+                          f"{wp.heads} heads), fp64 token-by-token, one pass, {dt:.1f} s",
+                "gpu_speedup": (tokens / per) / (tokens / dt),
+            }
+            log(f"cpu oracle: {tokens/dt:.0f} tokens/s ({dt:.1f} s)")
+        del x, o, ST
+        torch.cuda.empty_cache()
+
+    # ---------------- decode: 256 sequences x 32 heads, 100 chained steps ----------------
+    if args.only in (None, "decode"):
+        wd = WORKLOADS["kda_decode_b256_h32_d128"]
+        steps = args.decode_steps
+        from kda_recurrent_state_amd.workloads import scaled
+        wds = scaled(wd, steps=steps)
+        log("generating decode inputs")
+        y = generate(wds, seed=4, device=dev)
+        S = y["S"].clone()
+        od = torch.empty((wd.n_seqs, wd.heads, wd.dv), dtype=wd.dtype, device=dev)
+        ctr = [0]
+
+        def dstep():
+            i = ctr[0] % steps
+            ctr[0] += 1
+            kda.decode_step(y["q"][i], y["k"][i], y["v"][i], y["log_a"][i], y["beta"][i], S, out=od)
+
+        for _ in range(min(args.warmup, steps)):
+            dstep()
+        torch.cuda.synchronize()
+        ctr[0] = 0
+        log("decode timed")
+        t = time_events(dstep, steps, stream)
+        per = t / steps
+        Bd = decode_algorithmic(wd)
+        gbs = Bd / per / 1e9
+        state_gbs = 2 * 4 * wd.n_seqs * wd.heads * wd.dk * wd.dv / per / 1e9
+        out.setdefault("value", None)
+        out["decode"] = {
+            "workload": wd.name, "value": gbs, "unit": "GB/s", "us_per_step": per * 1e6,
+            "steps": steps, "state_only_GBps": state_gbs, "tokens_per_s": wd.n_seqs / per,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": stored_traffic("decode", Bd),
+                         "kernel": "kda_decode_kernel", "algorithmic_bytes_per_launch": Bd,
+                         "avg_launch_us": per * 1e6},
+        }
+        log(f"decode: {per*1e6:.1f} us/step, {gbs:.0f} GB/s ({100*gbs/PEAK_HBM_GBS:.1f}% of HBM peak)")
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

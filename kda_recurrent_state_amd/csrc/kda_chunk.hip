@@ -10,10 +10,14 @@
 //   Kb = K e^{g_{t-1}}, Kc = K e^{-g_{t-1}}, Kt = K e^{-g_t}, Qb = Q e^{g_t}
 //   A  = strict_lower(diag(b) Kb Kc^T),  L = strict_lower(Kb Kt^T)
 //   P1 = lower(Qb Kc^T),                 P2 = lower(Qb Kt^T)
-//   T  = (I + A)^-1,  Tb = T diag(b),  W = Tb Kb,  U = Tb L (b V)
-//   E  = -(W S + U)
-//   O  = Qb S + P1 E + P2 (b V)
-//   S <- Diag(e^{g_C}) S + (Kc e^{g_C})^T E + (Kt e^{g_C})^T (b V)
+//   T  = (I + A)^-1,  Tb = T diag(b)
+//   E  = -Tb (Kb S + L (b V))             (the chunk's erase coefficients)
+//   O  = Qb S + P2 (b V) + P1 E
+//   S <- Diag(e^{g_C}) S + (Kt e^{g_C})^T (b V) + (Kc e^{g_C})^T E
+//
+// Only the solve and the E-dependent terms wait for T; Z = Kb S + L (b V), the
+// first two terms of O and of the state update are formed while one wavefront
+// inverts (I + A).
 //
 // The per-channel decay ("a gate per channel", page "The efficiency lineage",
 // item 10) spans hundreds of nats over a chunk, which is the numerical-range
@@ -25,11 +29,20 @@
 // e^{mu_bt - mu_bi} <= 1.  The state-side operands are referenced to the chunk
 // start or end, where every factor is <= 1.
 //
-// Work decomposition: one workgroup (4 wavefronts) per (sequence, head,
-// dv-slice of width DVS).  The workgroup walks its sequence chunk by chunk;
-// the fp32 state slice [DK x DVS] lives in matrix-core accumulators across the
-// walk.  Inputs are read from HBM once per slice (slices of one head are
-// placed on one XCD so they share its L2) and o is written once.
+// Work decomposition: one workgroup (8 wavefronts) per (sequence, head,
+// dv-slice of width DVS).  The workgroup walks its sequence chunk by chunk,
+// loading the next chunk's inputs into registers while it computes the
+// current one; the fp32 state slice [DK x DVS] lives in matrix-core
+// accumulators across the walk.  Inputs are read from HBM once per slice
+// (slices of one head are placed on one XCD so they share its L2) and o is
+// written once.  Per chunk there are six phases separated by LDS-only
+// barriers:
+//   P1  prefetched inputs -> decay sums per 4-token group, (b V)^T; prefetch next
+//   P2  decay factors and all eight gated operands
+//   P3  the four Gram products
+//   P4  wavefront 0: (I + A)^-1;  the others: Z, first O terms, Gamma S + Kt^T bV
+//   P5  E = -Tb Z
+//   P6  O += P1 E, S += Kc^T E
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -39,19 +52,50 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 template <typename T, int DK, int DVS, int C>
 struct ChunkCfg {
-    static constexpr int NT = 256, NW = NT / WAVE;
+    static constexpr int NT = 512, NW = NT / WAVE;     // 8 wavefronts, 2 per SIMD
     static constexpr int NB = C / 16;                  // 16-token sub-blocks
     static constexpr int NPAIR = NB * (NB - 1) / 2;    // off-diagonal block pairs
+    static constexpr int NBP = NB * (NB + 1) / 2;      // block pairs incl. diagonal
     static constexpr int PAD = 16 / sizeof(T);         // one 16-byte pad per row
     static constexpr int LDK = DK + PAD;               // rows with dk contiguous
     static constexpr int LDC = C + PAD;                // rows with tokens contiguous
     static constexpr int LDA = C + 4;                  // fp32 C x C matrices
-    static constexpr int NU = (DK / 4) * (C / 4);      // 4 tokens x 4 channels units
+    static constexpr int NCP = DK / 2;                 // channel pairs
+    static constexpr int NU = NCP * (C / 4);           // 4 tokens x 2 channels units
     static constexpr int UPT = (NU + NT - 1) / NT;     // units per thread
-    static constexpr int NUV = (DVS / 4) * (C / 4);    // value units
+    static constexpr int NUV = (DVS / 4) * (C / 4);    // 4 tokens x 4 value columns units
+    static constexpr int UVPT = (NUV + NT - 1) / NT;
     static constexpr int NST = (DK / 16) * (DVS / 16); // state tiles
     static constexpr int STPW = (NST + NW - 1) / NW;   // state tiles per wavefront
+    static constexpr int NOT = (DVS / 16) * (C / 16);  // output (and Z, E) tiles
+    static constexpr int OTPW = (NOT + NW - 1) / NW;
+    static constexpr int OTPWX = (NOT + NW - 2) / (NW - 1);  // per wavefront 1..NW-1
 };
+
+// Unit (4 tokens x 2 channels) of thread slot uu: a wavefront covers 32
+// consecutive channel pairs of two token groups, so its row-major stores are
+// contiguous and its transposed stores use every LDS bank.
+template <int NCP>
+__device__ __forceinline__ void unit_of(int uu, int& c, int& tg) {
+    if constexpr (NCP >= 32) {
+        const int w = uu >> 6, l = uu & 63;
+        constexpr int HALVES = NCP / 32;  // 32-pair groups of the channel pairs
+        c = 2 * ((l & 31) + 32 * (w % HALVES));
+        tg = (l >> 5) + 2 * (w / HALVES);
+    } else {
+        c = 2 * (uu % NCP);
+        tg = uu / NCP;
+    }
+}
+
+// Transposed operands ([channel][token]) are written four channels at a time
+// by one thread.  Their rows are stored in four planes, channel c at row
+// (c & 3) * (N/4 + 4) + (c >> 2), so neither those writes nor the matrix-core
+// fragment reads of 16 consecutive channels collide on LDS banks.
+template <int N>
+__device__ __forceinline__ int prow(int c) { return (c & 3) * (N / 4 + 4) + (c >> 2); }
+template <int N>
+constexpr int prows() { return N + 16; }
 
 template <typename T, int DK, int DVS, int C>
 struct ChunkLds {
@@ -60,27 +104,23 @@ struct ChunkLds {
     alignas(16) T Qr[C * G::LDK];    // Q e^{g_t - mid}       Gram rows (P1, P2)
     alignas(16) T Kce[C * G::LDK];   // K e^{mid - g_{t-1}}   Gram columns (A, P1)
     alignas(16) T Kci[C * G::LDK];   // K e^{mid - g_t}       Gram columns (L, P2)
+    alignas(16) T Kbar[C * G::LDK];  // K e^{g_{t-1}}
     alignas(16) T Qbar[C * G::LDK];  // Q e^{g_t}
-    alignas(16) T W[C * G::LDK];     // Tb Kbar
-    alignas(16) T ST[DVS * G::LDK];  // state slice, transposed [j][c]
-    alignas(16) T KbarT[DK * G::LDC];  // (K e^{g_{t-1}})^T
-    alignas(16) T KccT[DK * G::LDC];   // (K e^{g_C - g_{t-1}})^T
-    alignas(16) T KtcT[DK * G::LDC];   // (K e^{g_C - g_t})^T
-    alignas(16) T VT[DVS * G::LDC];    // (b V)^T
-    alignas(16) T YT[DVS * G::LDC];    // (L b V)^T
-    alignas(16) T ET[DVS * G::LDC];    // E^T
+    alignas(16) T ST[DVS * G::LDK];  // state slice at the chunk start, [j][c]
+    alignas(16) T KccT[prows<DK>() * G::LDC];  // (K e^{g_C - g_{t-1}})^T, plane rows
+    alignas(16) T KtcT[prows<DK>() * G::LDC];  // (K e^{g_C - g_t})^T, plane rows
+    alignas(16) T VT[prows<DVS>() * G::LDC];   // (b V)^T, plane rows
+    alignas(16) T ZT[DVS * G::LDC];  // (Kbar S + L b V)^T
+    alignas(16) T ET[DVS * G::LDC];  // E^T
     alignas(16) T L[C * G::LDC];
     alignas(16) T P1[C * G::LDC];
     alignas(16) T P2[C * G::LDC];
     alignas(16) T Tb[C * G::LDC];
-    alignas(16) float A[C * G::LDA];   // diag(b) strict_lower(Kb Kc^T), fp32
-    alignas(16) float Tm[C * G::LDA];  // (I + A)^-1, fp32
-    alignas(16) float X[(G::NB > 1 ? G::NB - 1 : 1) * 256];
-    alignas(16) float grp[(C / 4) * DK];  // per 4-token group: summed log2 decay
-    alignas(16) float emu[G::NB * DK];    // e^{mu_b}
-    alignas(16) float ecmu[G::NB * DK];   // e^{g_C - mu_b}
+    alignas(16) float A[C * G::LDA];           // diag(b) strict_lower(Kb Kc^T), fp32
+    alignas(16) float X[2 * G::NB * 256];      // panel exchange of the blocked solve
+    alignas(16) float grp[(C / 4) * DK];       // per 4-token group: summed log2 decay
     alignas(16) float F[(G::NPAIR > 0 ? G::NPAIR : 1) * DK];  // e^{mu_bt - mu_bi}
-    alignas(16) float gam[DK];            // e^{g_C}
+    alignas(16) float gam[DK];                 // e^{g_C}
     alignas(16) float beta[C];
 };
 
@@ -101,8 +141,181 @@ struct ChunkParams {
     int64_t eq_len;  // used when cu is null
 };
 
+// Workgroup barrier that orders LDS only: global loads issued before it stay in
+// flight (the next chunk's inputs are prefetched across it).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Orders LDS traffic between lanes of one wavefront (no workgroup barrier).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ float uniform(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+template <typename T> struct Vec2;
+template <> struct Vec2<bf16> {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 type;
+    static __device__ __forceinline__ float lo(type v) { return (float)v[0]; }
+    static __device__ __forceinline__ float hi(type v) { return (float)v[1]; }
+    static __device__ __forceinline__ type make(float a, float b) { type r; r[0] = (bf16)a; r[1] = (bf16)b; return r; }
+};
+template <> struct Vec2<float> {
+    typedef __attribute__((__vector_size__(2 * sizeof(float)))) float type;
+    static __device__ __forceinline__ float lo(type v) { return v[0]; }
+    static __device__ __forceinline__ float hi(type v) { return v[1]; }
+    static __device__ __forceinline__ type make(float a, float b) { type r; r[0] = a; r[1] = b; return r; }
+};
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+template <typename T>
+__device__ __forceinline__ void store2(T* p, float a, float b) {
+    *reinterpret_cast<typename Vec2<T>::type*>(p) = Vec2<T>::make(a, b);
+}
+
+// Raw inputs of one 4-token x 2-channel unit, held in registers one chunk ahead.
+template <typename T>
+struct UnitIn {
+    typename Vec2<T>::type q[4], k[4];
+    f32x2 la[4];
+};
+template <typename T>
+struct ValIn {
+    typename Vec4<T>::type v[4];
+    float b[4];
+};
+
+// Value units are spread over the wavefronts (v is narrower than k).
+template <int NW>
+__device__ __forceinline__ int value_unit(int tid, int u, int nt) { return (tid & 63) * NW + (tid >> 6) + nt * u; }
+
 template <typename T, int DK, int DVS, int C, bool SCALAR>
-__global__ void __launch_bounds__(256) kda_chunk_kernel(ChunkParams p) {
+__device__ __forceinline__ void load_chunk(const ChunkParams& p, const T* gq, const T* gk, const T* gv,
+                                           int64_t t0, int Lc, int h, int dv0, int tid,
+                                           UnitIn<T> (&ui)[ChunkCfg<T, DK, DVS, C>::UPT],
+                                           ValIn<T> (&vi)[ChunkCfg<T, DK, DVS, C>::UVPT]) {
+    typedef ChunkCfg<T, DK, DVS, C> G;
+    const int H = p.H, DV = p.DV;
+    const int64_t r0 = t0 * H + h;  // row of the chunk's first token
+#pragma unroll
+    for (int u = 0; u < G::UPT; ++u) {
+        const int uu = tid + G::NT * u;
+        if (uu < G::NU) {
+            int c, tg;
+            unit_of<G::NCP>(uu, c, tg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // rows past the chunk's end re-read its last row; beta and log_a are
+                // masked at use, which makes the other values irrelevant
+                const int64_t row = r0 + (int64_t)min(4 * tg + i, Lc - 1) * H;
+                ui[u].q[i] = *reinterpret_cast<const typename Vec2<T>::type*>(gq + row * DK + c);
+                ui[u].k[i] = *reinterpret_cast<const typename Vec2<T>::type*>(gk + row * DK + c);
+                if (SCALAR) {
+                    const float x = p.log_a[row];
+                    ui[u].la[i] = f32x2{x, x};
+                } else {
+                    ui[u].la[i] = *reinterpret_cast<const f32x2*>(p.log_a + row * DK + c);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < G::UVPT; ++u) {
+        const int uv = value_unit<G::NW>(tid, u, G::NT);
+        if (uv < G::NUV) {
+            const int j = 4 * (uv % (DVS / 4)), tg = uv / (DVS / 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = r0 + (int64_t)min(4 * tg + i, Lc - 1) * H;
+                vi[u].v[i] = *reinterpret_cast<const typename Vec4<T>::type*>(gv + row * DV + dv0 + j);
+                vi[u].b[i] = p.beta[row];
+            }
+        }
+    }
+}
+
+// (I + A)^-1 diag(b) for a strictly lower C x C matrix A (fp32, row-major, ld
+// LDA), on one wavefront, written as Tb (row-major, ld LDC, upper blocks left
+// untouched).  Blocked right-looking forward substitution on fp32 matrix
+// cores: the right-hand sides (identity columns of one 16-column block) live
+// in 16 x 16 accumulator tiles, where lane group g holds rows 4g..4g+3; each
+// 4-row panel is solved inside the lanes that hold it, passed to all lanes
+// through LDS (X, double-buffered), and every tile below is updated with one
+// 16x16x4 product.  Block columns are independent chains.  All coefficients
+// are read before the chain starts (the uniform ones into scalar registers);
+// the code has no lane-dependent branches.
+template <typename T, int C, int LDA, int LDC>
+__device__ __forceinline__ void block_inverse(const float* A, const float* beta, float* X, T* Tb, int lane) {
+    constexpr int NB = C / 16, NP = 4 * NB;
+    const int l16 = lane & 15, lg = lane >> 4;
+    float cf[NP][6];
+    float aop[NP][NB];
+#pragma unroll
+    for (int sp = 0; sp < NP; ++sp) {
+        const int r0 = 4 * sp;
+        cf[sp][0] = uniform(A[(r0 + 1) * LDA + r0]);
+        cf[sp][1] = uniform(A[(r0 + 2) * LDA + r0]);
+        cf[sp][2] = uniform(A[(r0 + 2) * LDA + r0 + 1]);
+        cf[sp][3] = uniform(A[(r0 + 3) * LDA + r0]);
+        cf[sp][4] = uniform(A[(r0 + 3) * LDA + r0 + 1]);
+        cf[sp][5] = uniform(A[(r0 + 3) * LDA + r0 + 2]);
+#pragma unroll
+        for (int tr = 0; tr < NB; ++tr) {
+            const int row = 16 * tr + l16;
+            const float x = (tr >= sp / 4) ? A[row * LDA + r0 + lg] : 0.f;
+            aop[sp][tr] = (row > r0 + 3) ? -x : 0.f;
+        }
+    }
+    f32x4 R[NB][NB];  // R[bc][tr]: rows of tile tr, columns of block column bc
+#pragma unroll
+    for (int bc = 0; bc < NB; ++bc)
+#pragma unroll
+        for (int tr = 0; tr < NB; ++tr)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) R[bc][tr][r] = (tr == bc && 4 * lg + r == l16) ? 1.f : 0.f;
+#pragma unroll
+    for (int sp = 0; sp < NP; ++sp) {  // panel: rows 4 sp .. 4 sp + 3
+        const int ts = sp / 4, g = sp % 4;
+        float* Xb = X + (sp & 1) * (NB * 256);
+#pragma unroll
+        for (int bc = 0; bc <= ts; ++bc) {
+            f32x4 x = R[bc][ts];
+            x[1] -= cf[sp][0] * x[0];
+            x[2] -= cf[sp][1] * x[0] + cf[sp][2] * x[1];
+            x[3] -= cf[sp][3] * x[0] + cf[sp][4] * x[1] + cf[sp][5] * x[2];
+            R[bc][ts] = (lg == g) ? x : R[bc][ts];
+            // every lane group writes its own slot; group g's slot is the panel
+            *reinterpret_cast<f32x4*>(&Xb[bc * 256 + lg * 64 + 4 * l16]) = x;
+        }
+        wave_sync();
+#pragma unroll
+        for (int bc = 0; bc <= ts; ++bc) {
+            const float bk = Xb[bc * 256 + g * 64 + 4 * l16 + lg];  // B[k = lg][n = l16]
+#pragma unroll
+            for (int tr = ts; tr < NB; ++tr)
+                R[bc][tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[sp][tr], bk, R[bc][tr], 0, 0, 0);
+        }
+    }
+    // Tb = T diag(b): lane holds column 16 bc + l16, rows 16 tr + 4 lg + r
+#pragma unroll
+    for (int bc = 0; bc < NB; ++bc) {
+        const float bcol = beta[16 * bc + l16];
+#pragma unroll
+        for (int tr = bc; tr < NB; ++tr)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Tb[(16 * tr + 4 * lg + r) * LDC + 16 * bc + l16] = from_f32<T>(R[bc][tr][r] * bcol);
+    }
+}
+
+template <typename T, int DK, int DVS, int C, bool SCALAR>
+__global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
     typedef ChunkCfg<T, DK, DVS, C> G;
     typedef Mma<T> M;
     constexpr int NT = G::NT, NW = G::NW, NB = G::NB, LDK = G::LDK, LDC = G::LDC, LDA = G::LDA;
@@ -133,118 +346,163 @@ __global__ void __launch_bounds__(256) kda_chunk_kernel(ChunkParams p) {
     // upper blocks of the masked C x C products are never written: zero once
     for (int e = tid; e < C * LDC; e += NT) {
         s.L[e] = from_f32<T>(0.f); s.P1[e] = from_f32<T>(0.f); s.P2[e] = from_f32<T>(0.f);
+        s.Tb[e] = from_f32<T>(0.f);
     }
 
-    // state slice in accumulators: tile ix = wv + NW * i -> (mi, ni)
+    // state slice in accumulators: tile ix = wv + NW * i -> (mi, ni); copy in LDS
     f32x4 acc[G::STPW];
     const int64_t sbase = ((int64_t)n * H + h) * DK * DV + dv0;
 #pragma unroll
     for (int i = 0; i < G::STPW; ++i) {
         const int ix = wv + NW * i;
         acc[i] = zero4();
-        if (ix < G::NST && p.S0) {
+        if (ix < G::NST) {
             const int mi = ix / (DVS / 16), ni = ix % (DVS / 16);
+            if (p.S0) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[i][r] = p.S0[sbase + (int64_t)(16 * mi + 4 * lgrp + r) * DV + 16 * ni + lrow];
+                for (int r = 0; r < 4; ++r)
+                    acc[i][r] = p.S0[sbase + (int64_t)(16 * mi + 4 * lgrp + r) * DV + 16 * ni + lrow];
+            }
+            store4(&s.ST[(16 * ni + lrow) * LDK + 16 * mi + 4 * lgrp], acc[i]);
         }
     }
+
+    UnitIn<T> ui[G::UPT];
+    ValIn<T> vi[G::UVPT];
+    if (tb < te)
+        load_chunk<T, DK, DVS, C, SCALAR>(p, gq, gk, gv, tb, (int)((te - tb) < C ? (te - tb) : C), h, dv0,
+                                          tid, ui, vi);
+
+    // outputs of a chunk are stored at the start of the next iteration, after
+    // the wait for the prefetched inputs (stores share the vector-memory counter)
+    f32x4 opend[G::OTPWX];
+    int64_t t0_prev = tb;
+    int Lc_prev = 0;
+    auto store_o = [&]() {
+        if (wv == 0) return;
+#pragma unroll
+        for (int i = 0; i < G::OTPWX; ++i) {
+            const int w = (wv - 1) + (NW - 1) * i;
+            if (w < G::NOT) {
+                const int mj = w / (C / 16), nt = w % (C / 16);
+                const int t = 16 * nt + lrow;
+                if (t < Lc_prev) store4(go + ((t0_prev + t) * H + h) * DV + dv0 + 16 * mj + 4 * lgrp, opend[i]);
+            }
+        }
+    };
 
     for (int64_t t0 = tb; t0 < te; t0 += C) {
         const int Lc = (int)((te - t0) < C ? (te - t0) : C);
 
-        // ---- I1: loads, decay sums per 4-token group, b V ----------------------------
-        f32x4 lam[G::UPT][4], qv[G::UPT][4], kv[G::UPT][4];
+        // ---- P1: decay sums per 4-token group, (b V)^T, beta; prefetch next chunk ---
+        f32x2 lam[G::UPT][4];
+        typename Vec2<T>::type qraw[G::UPT][4], kraw[G::UPT][4];
 #pragma unroll
         for (int u = 0; u < G::UPT; ++u) {
             const int uu = tid + NT * u;
             if (uu < G::NU) {
-                const int c = 4 * (uu % (DK / 4)), tg = uu / (DK / 4);
-                f32x4 run = zero4();
+                int c, tg;
+                unit_of<G::NCP>(uu, c, tg);
+                f32x2 run = f32x2{0.f, 0.f};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int t = 4 * tg + i;
-                    const int64_t row = (t0 + t) * H + h;
-                    f32x4 la4 = zero4(), q4 = zero4(), k4 = zero4();
-                    if (t < Lc) {
-                        if (SCALAR) {
-                            const float x = p.log_a[row];
-                            la4 = f32x4{x, x, x, x};
-                        } else {
-                            la4 = *reinterpret_cast<const f32x4*>(p.log_a + row * DK + c);
-                        }
-                        q4 = load4(gq + row * DK + c);
-                        k4 = load4(gk + row * DK + c);
-                    }
-                    run += la4 * LOG2E;
+                    run += (4 * tg + i < Lc) ? ui[u].la[i] * LOG2E : f32x2{0.f, 0.f};
                     lam[u][i] = run;
-                    qv[u][i] = q4;
-                    kv[u][i] = k4;
+                    qraw[u][i] = ui[u].q[i];
+                    kraw[u][i] = ui[u].k[i];
                 }
-                *reinterpret_cast<f32x4*>(&s.grp[tg * DK + c]) = run;
+                *reinterpret_cast<f32x2*>(&s.grp[tg * DK + c]) = run;
             }
         }
-        for (int t = tid; t < C; t += NT) s.beta[t] = t < Lc ? p.beta[(t0 + t) * H + h] : 0.f;
-        for (int uv = tid; uv < G::NUV; uv += NT) {
-            const int j = 4 * (uv % (DVS / 4)), tg = uv / (DVS / 4);
-            f32x4 vals[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * tg + i;
-                vals[i] = zero4();
-                if (t < Lc) {
-                    const int64_t row = (t0 + t) * H + h;
-                    vals[i] = p.beta[row] * load4(gv + row * DV + dv0 + j);
+        for (int u = 0; u < G::UVPT; ++u) {
+            const int uv = value_unit<NW>(tid, u, NT);
+            if (uv < G::NUV) {
+                const int j = 4 * (uv % (DVS / 4)), tg = uv / (DVS / 4);
+                f32x4 vals[4], bb;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bb[i] = 4 * tg + i < Lc ? vi[u].b[i] : 0.f;
+                    vals[i] = bb[i] * Vec4<T>::to_f32(vi[u].v[i]);
                 }
-            }
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                store4(&s.VT[(j + e) * LDC + 4 * tg],
-                       f32x4{vals[0][e], vals[1][e], vals[2][e], vals[3][e]});
+                for (int e = 0; e < 4; ++e)
+                    store4(&s.VT[prow<DVS>(j + e) * LDC + 4 * tg], f32x4{vals[0][e], vals[1][e], vals[2][e], vals[3][e]});
+                if (j == 0) *reinterpret_cast<f32x4*>(&s.beta[4 * tg]) = bb;
+            }
         }
-        __syncthreads();
+        if (Lc_prev > 0) store_o();
+        t0_prev = t0;
+        Lc_prev = Lc;
+        {
+            const int64_t t1 = t0 + C;
+            if (t1 < te)
+                load_chunk<T, DK, DVS, C, SCALAR>(p, gq, gk, gv, t1, (int)((te - t1) < C ? (te - t1) : C), h,
+                                                  dv0, tid, ui, vi);
+        }
+        lds_barrier();
 
-        // ---- I2: decay factors, Gram operands, per-block constants -------------------
-        // rin = e^{g_t - mid}, rex = e^{g_{t-1} - mid}; cin, cex their reciprocals.
+        // ---- P2: decay factors and all gated operands ------------------------------
+        // rin = e^{g_t - mid}, rex = e^{g_{t-1} - mid}, cin, cex their reciprocals,
+        // em = e^{mu_b}, ec = e^{g_C - mu_b} (mu_b the mid-point of the sub-block).
         // Exponents are clamped to the fp32 range so no factor is inf or zero.
-        f32x4 rin[G::UPT][4], rex[G::UPT][4], cin[G::UPT][4], cex[G::UPT][4];
 #pragma unroll
         for (int u = 0; u < G::UPT; ++u) {
             const int uu = tid + NT * u;
             if (uu < G::NU) {
-                const int c = 4 * (uu % (DK / 4)), tg = uu / (DK / 4);
+                int c, tg;
+                unit_of<G::NCP>(uu, c, tg);
                 const int b = tg / 4, gib = tg % 4;
-                f32x4 off = zero4();
-                for (int g = 0; g < gib; ++g) off += *reinterpret_cast<const f32x4*>(&s.grp[(4 * b + g) * DK + c]);
-                const f32x4 mid = *reinterpret_cast<const f32x4*>(&s.grp[(4 * b) * DK + c]) +
-                                  *reinterpret_cast<const f32x4*>(&s.grp[(4 * b + 1) * DK + c]);
-                f32x4 prev, prevc;
+                f32x2 off = {0.f, 0.f}, rho = {0.f, 0.f}, tot = {0.f, 0.f}, mid = {0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int g = 0; g < C / 4; ++g) {
+                    const f32x2 x = *reinterpret_cast<const f32x2*>(&s.grp[g * DK + c]);
+                    tot += x;
+                    if (g < 4 * b) rho += x;
+                    if (g >= 4 * b && g < 4 * b + gib) off += x;
+                    if (g == 4 * b || g == 4 * b + 1) mid += x;
+                }
+                f32x2 em, ec, prev, prevc;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    em[e] = __builtin_amdgcn_exp2f(__builtin_amdgcn_fmed3f(rho[e] + mid[e], -126.f, 0.f));
+                    ec[e] = __builtin_amdgcn_exp2f(__builtin_amdgcn_fmed3f(tot[e] - rho[e] - mid[e], -126.f, 0.f));
                     prev[e] = __builtin_amdgcn_exp2f(__builtin_amdgcn_fmed3f(off[e] - mid[e], -126.f, 126.f));
                     prevc[e] = __builtin_amdgcn_rcpf(prev[e]);
                 }
+                f32x2 kc[4], kt[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = 4 * tg + i;
-                    f32x4 ri, ci;
+                    f32x2 ri, ci;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
+                    for (int e = 0; e < 2; ++e) {
                         ri[e] = __builtin_amdgcn_exp2f(
                             __builtin_amdgcn_fmed3f(off[e] + lam[u][i][e] - mid[e], -126.f, 126.f));
                         ci[e] = __builtin_amdgcn_rcpf(ri[e]);
                     }
-                    rin[u][i] = ri; cin[u][i] = ci;
-                    rex[u][i] = prev; cex[u][i] = prevc;
-                    prev = ri; prevc = ci;
-                    store4(&s.Kr[t * LDK + c], kv[u][i] * rex[u][i]);
-                    store4(&s.Qr[t * LDK + c], qv[u][i] * ri);
-                    store4(&s.Kce[t * LDK + c], kv[u][i] * cex[u][i]);
-                    store4(&s.Kci[t * LDK + c], kv[u][i] * ci);
+                    const f32x2 k = f32x2{Vec2<T>::lo(kraw[u][i]), Vec2<T>::hi(kraw[u][i])};
+                    const f32x2 q = f32x2{Vec2<T>::lo(qraw[u][i]), Vec2<T>::hi(qraw[u][i])};
+                    const f32x2 kr = k * prev, qr = q * ri, kce = k * prevc, kci = k * ci;
+                    store2(&s.Kr[t * LDK + c], kr[0], kr[1]);
+                    store2(&s.Qr[t * LDK + c], qr[0], qr[1]);
+                    store2(&s.Kce[t * LDK + c], kce[0], kce[1]);
+                    store2(&s.Kci[t * LDK + c], kci[0], kci[1]);
+                    store2(&s.Kbar[t * LDK + c], kr[0] * em[0], kr[1] * em[1]);
+                    store2(&s.Qbar[t * LDK + c], qr[0] * em[0], qr[1] * em[1]);
+                    kc[i] = kce * ec;
+                    kt[i] = kci * ec;
+                    prev = ri;
+                    prevc = ci;
+                }
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    store4(&s.KccT[prow<DK>(c + e) * LDC + 4 * tg], f32x4{kc[0][e], kc[1][e], kc[2][e], kc[3][e]});
+                    store4(&s.KtcT[prow<DK>(c + e) * LDC + 4 * tg], f32x4{kt[0][e], kt[1][e], kt[2][e], kt[3][e]});
                 }
             }
         }
-        // per (sub-block, channel) constants
+        // per (sub-block, channel): e^{mu_bt - mu_bi} for block pairs, e^{g_C}
         for (int e = tid; e < NB * DK; e += NT) {
             const int b = e / DK, c = e % DK;
             float rho[NB + 1], mu[NB];
@@ -256,173 +514,111 @@ __global__ void __launch_bounds__(256) kda_chunk_kernel(ChunkParams p) {
                 mu[bb] = rho[bb] + g0 + g1;
                 rho[bb + 1] = rho[bb] + ((g0 + g1) + (g2 + g3));
             }
-            const float gC = rho[NB];
-            s.emu[b * DK + c] = exp2f(mu[b]);
-            s.ecmu[b * DK + c] = exp2f(gC - mu[b]);
-            if (b == 0) s.gam[c] = exp2f(gC);
+            if (b == 0) s.gam[c] = exp2f(rho[NB]);
             for (int bi = 0; bi < b; ++bi) s.F[(b * (b - 1) / 2 + bi) * DK + c] = exp2f(mu[b] - mu[bi]);
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- I3: Gram products (matrix cores) and state-side operands ----------------
-        for (int w = wv; w < NB * (NB + 1); w += NW) {
-            const int pr = w >> 1, rt = w & 1;  // block pair, row type (0: K rows, 1: Q rows)
+        // ---- P3: Gram products: tile w is product w % 4 (0 A, 1 L, 2 P1, 3 P2) of
+        //      block pair w / 4, transposed (G^T) so it lands row-major in LDS --------
+        for (int w = wv; w < 4 * G::NBP; w += NW) {
+            const int g = w % 4, pr = w / 4;
             int bt = 0;
             while ((bt + 1) * (bt + 2) / 2 <= pr) ++bt;
             const int bi = pr - bt * (bt + 1) / 2;
-            const T* rows = (rt ? s.Qr : s.Kr) + 16 * bt * LDK;
-            const T* cols_e = s.Kce + 16 * bi * LDK;
-            const T* cols_i = s.Kci + 16 * bi * LDK;
-            const float* F = s.F + (bt * (bt - 1) / 2 + bi) * DK;
-            f32x4 ge = zero4(), gi = zero4();
+            const T* rows = (g < 2 ? s.Kr : s.Qr) + (16 * bt + lrow) * LDK;
+            const T* cols = ((g & 1) == 0 ? s.Kce : s.Kci) + (16 * bi + lrow) * LDK;
+            constexpr int NK = DK / M::K;
+            typename M::frag fr[NK], fc[NK];
 #pragma unroll
-            for (int kk = 0; kk < DK; kk += M::K) {
-                typename M::frag rb = M::load(rows + kk, LDK, lane);
-                if (bt != bi) rb = M::scale(rb, F + kk + lgrp * M::KPL);
-                ge = M::mma(M::load(cols_e + kk, LDK, lane), rb, ge);
-                gi = M::mma(M::load(cols_i + kk, LDK, lane), rb, gi);
+            for (int k = 0; k < NK; ++k) {
+                fr[k] = M::loadr(rows + k * M::K, lane);
+                fc[k] = M::loadr(cols + k * M::K, lane);
             }
-            // tile holds G^T: lane column t, rows i = 16 bi + 4 lgrp + r
+            if (bt != bi) {
+                const float* F = s.F + (bt * (bt - 1) / 2 + bi) * DK + lgrp * M::KPL;
+#pragma unroll
+                for (int k = 0; k < NK; ++k) fr[k] = M::scale(fr[k], F + k * M::K);
+            }
+            f32x4 acc_g = zero4();
+#pragma unroll
+            for (int k = 0; k < NK; ++k) acc_g = M::mma(fc[k], fr[k], acc_g);
             const int t = 16 * bt + lrow, i0 = 16 * bi + 4 * lgrp;
-            f32x4 me, mi;
+            f32x4 m;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + r;
-                me[r] = (rt ? i <= t : i < t) ? ge[r] : 0.f;
-                mi[r] = (rt ? i <= t : i < t) ? gi[r] : 0.f;
-            }
-            if (rt == 0) {
-                *reinterpret_cast<f32x4*>(&s.A[t * LDA + i0]) = s.beta[t] * me;
-                store4(&s.L[t * LDC + i0], mi);
-            } else {
-                store4(&s.P1[t * LDC + i0], me);
-                store4(&s.P2[t * LDC + i0], mi);
-            }
+            for (int r = 0; r < 4; ++r) m[r] = (g < 2 ? i0 + r < t : i0 + r <= t) ? acc_g[r] : 0.f;
+            if (g == 0) *reinterpret_cast<f32x4*>(&s.A[t * LDA + i0]) = s.beta[t] * m;
+            else store4(&(g == 1 ? s.L : (g == 2 ? s.P1 : s.P2))[t * LDC + i0], m);
         }
-#pragma unroll
-        for (int u = 0; u < G::UPT; ++u) {
-            const int uu = tid + NT * u;
-            if (uu < G::NU) {
-                const int c = 4 * (uu % (DK / 4)), tg = uu / (DK / 4);
-                const int b = tg / 4;
-                const f32x4 em = *reinterpret_cast<const f32x4*>(&s.emu[b * DK + c]);
-                const f32x4 ec = *reinterpret_cast<const f32x4*>(&s.ecmu[b * DK + c]);
-                f32x4 kb[4], kc[4], kt[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 4 * tg + i;
-                    store4(&s.Qbar[t * LDK + c], qv[u][i] * rin[u][i] * em);
-                    kb[i] = kv[u][i] * rex[u][i] * em;
-                    kc[i] = kv[u][i] * cex[u][i] * ec;
-                    kt[i] = kv[u][i] * cin[u][i] * ec;
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    store4(&s.KbarT[(c + e) * LDC + 4 * tg], f32x4{kb[0][e], kb[1][e], kb[2][e], kb[3][e]});
-                    store4(&s.KccT[(c + e) * LDC + 4 * tg], f32x4{kc[0][e], kc[1][e], kc[2][e], kc[3][e]});
-                    store4(&s.KtcT[(c + e) * LDC + 4 * tg], f32x4{kt[0][e], kt[1][e], kt[2][e], kt[3][e]});
-                }
-            }
-        }
-        __syncthreads();
+        lds_barrier();
 
-        // ---- I4: diagonal blocks of (I + A)^-1; Y = L (b V); state -> LDS -------------
-        if (wv < NB) {
-            const int b = wv;
-            if (lane < 16) {
-                const int j = lane;
-                float x[16];
+        // ---- P4: wavefront 0 inverts (I + A); the others form Z = Kbar S + L (bV),
+        //      O^T = S^T Qbar^T + (bV)^T P2^T and Gamma S + Kt^T bV for their tiles ---
+        f32x4 oacc[G::OTPWX];
+        if (wv == 0) {
+            block_inverse<T, C, LDA, LDC>(s.A, s.beta, s.X, s.Tb, lane);
+        } else {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float* arow = &s.A[(16 * b + r) * LDA + 16 * b];
-                    float a = (r == j) ? 1.f : 0.f;
-#pragma unroll
-                    for (int m = 0; m < r; ++m) a -= arow[m] * x[m];
-                    x[r] = a;
+            for (int i = 0; i < G::OTPWX; ++i) {
+                const int w = (wv - 1) + (NW - 1) * i;
+                oacc[i] = zero4();
+                if (w < G::NOT) {
+                    const int mt = w / (DVS / 16), nj = w % (DVS / 16);
+                    f32x4 z = tile_mma<T, DK>(s.Kbar + 16 * mt * LDK, LDK, s.ST + 16 * nj * LDK, LDK, zero4(), lane);
+                    z = tile_mma_r<T, C>(s.L + (16 * mt + lrow) * LDC, s.VT + prow<DVS>(16 * nj + lrow) * LDC, z, lane);
+                    store4(&s.ZT[(16 * nj + lrow) * LDC + 16 * mt + 4 * lgrp], z);
+                    const int mj = w / (C / 16), nt = w % (C / 16);
+                    f32x4 x = tile_mma<T, DK>(s.ST + 16 * mj * LDK, LDK, s.Qbar + 16 * nt * LDK, LDK, zero4(), lane);
+                    oacc[i] = tile_mma_r<T, C>(s.VT + prow<DVS>(16 * mj + lrow) * LDC, s.P2 + (16 * nt + lrow) * LDC,
+                                               x, lane);
                 }
+            }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s.Tm[(16 * b + r) * LDA + 16 * b + j] = x[r];
+            for (int i = 0; i < G::STPW; ++i) {
+                const int ix = wv + NW * i;
+                if (ix < G::NST) {
+                    const int mi = ix / (DVS / 16), ni = ix % (DVS / 16);
+                    const f32x4 gm = *reinterpret_cast<const f32x4*>(&s.gam[16 * mi + 4 * lgrp]);
+                    acc[i] = tile_mma_r<T, C>(s.KtcT + prow<DK>(16 * mi + lrow) * LDC,
+                                              s.VT + prow<DVS>(16 * ni + lrow) * LDC, acc[i] * gm, lane);
+                }
             }
         }
-        {
-            constexpr int NY = (C / 16) * (DVS / 16);
-            for (int w = (wv + NW - NB) % NW; w < NY; w += NW) {
+        lds_barrier();
+
+        // ---- P5: E = -Tb Z; wavefront 0 applies Gamma S + Kt^T bV to its state tiles --
+#pragma unroll
+        for (int i = 0; i < G::OTPW; ++i) {
+            const int w = wv + NW * i;
+            if (w < G::NOT) {
                 const int mt = w / (DVS / 16), nj = w % (DVS / 16);
-                f32x4 y = tile_mma<T, C>(s.L + 16 * mt * LDC, LDC, s.VT + 16 * nj * LDC, LDC, zero4(), lane);
-                store4(&s.YT[(16 * nj + lrow) * LDC + 16 * mt + 4 * lgrp], y);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < G::STPW; ++i) {
-            const int ix = wv + NW * i;
-            if (ix < G::NST) {
-                const int mi = ix / (DVS / 16), ni = ix % (DVS / 16);
-                store4(&s.ST[(16 * ni + lrow) * LDK + 16 * mi + 4 * lgrp], acc[i]);
-            }
-        }
-        __syncthreads();
-
-        // ---- I5: off-diagonal blocks of (I + A)^-1, level by level ------------------
-        for (int bi = 1; bi < NB; ++bi) {
-            for (int e = tid; e < bi * 256; e += NT) {
-                const int bj = e / 256, r = (e / 16) % 16, jj = e % 16;
-                float a = 0.f;
-                for (int kb = bj; kb < bi; ++kb)
-#pragma unroll
-                    for (int m = 0; m < 16; ++m)
-                        a += s.A[(16 * bi + r) * LDA + 16 * kb + m] * s.Tm[(16 * kb + m) * LDA + 16 * bj + jj];
-                s.X[e] = a;
-            }
-            __syncthreads();
-            for (int e = tid; e < bi * 256; e += NT) {
-                const int bj = e / 256, r = (e / 16) % 16, jj = e % 16;
-                float a = 0.f;
-#pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    if (m <= r) a -= s.Tm[(16 * bi + r) * LDA + 16 * bi + m] * s.X[bj * 256 + m * 16 + jj];
-                s.Tm[(16 * bi + r) * LDA + 16 * bj + jj] = a;
-            }
-            __syncthreads();
-        }
-        for (int e = tid; e < C * C; e += NT) {
-            const int t = e / C, i = e % C;
-            s.Tb[t * LDC + i] = from_f32<T>(i <= t ? s.Tm[t * LDA + i] * s.beta[i] : 0.f);
-        }
-        __syncthreads();
-
-        // ---- I6: W = Tb Kbar, computed as W^T = Kbar^T Tb^T ------------------------
-        {
-            constexpr int NWT = (DK / 16) * (C / 16);
-            for (int w = wv; w < NWT; w += NW) {
-                const int mc = w / (C / 16), nt = w % (C / 16);
-                f32x4 x = tile_mma<T, C>(s.KbarT + 16 * mc * LDC, LDC, s.Tb + 16 * nt * LDC, LDC, zero4(), lane);
-                store4(&s.W[(16 * nt + lrow) * LDK + 16 * mc + 4 * lgrp], x);
-            }
-        }
-        __syncthreads();
-
-        // ---- I7: E = -(Tb Y + W S) ------------------------------------------------
-        {
-            constexpr int NE = (C / 16) * (DVS / 16);
-            for (int w = wv; w < NE; w += NW) {
-                const int mt = w / (DVS / 16), nj = w % (DVS / 16);
-                f32x4 x = tile_mma<T, C>(s.Tb + 16 * mt * LDC, LDC, s.YT + 16 * nj * LDC, LDC, zero4(), lane);
-                x = tile_mma<T, DK>(s.W + 16 * mt * LDK, LDK, s.ST + 16 * nj * LDK, LDK, x, lane);
+                f32x4 x = tile_mma<T, C>(s.Tb + 16 * mt * LDC, LDC, s.ZT + 16 * nj * LDC, LDC, zero4(), lane);
                 store4(&s.ET[(16 * nj + lrow) * LDC + 16 * mt + 4 * lgrp], -x);
             }
         }
-        __syncthreads();
+        if (wv == 0) {
+#pragma unroll
+            for (int i = 0; i < G::STPW; ++i) {
+                const int ix = wv + NW * i;
+                if (ix < G::NST) {
+                    const int mi = ix / (DVS / 16), ni = ix % (DVS / 16);
+                    const f32x4 gm = *reinterpret_cast<const f32x4*>(&s.gam[16 * mi + 4 * lgrp]);
+                    acc[i] = tile_mma_r<T, C>(s.KtcT + prow<DK>(16 * mi + lrow) * LDC,
+                                              s.VT + prow<DVS>(16 * ni + lrow) * LDC, acc[i] * gm, lane);
+                }
+            }
+        }
+        lds_barrier();
 
-        // ---- I8: outputs O^T = S^T Qbar^T + E^T P1^T + (bV)^T P2^T; state update ------
-        {
-            constexpr int NO = (DVS / 16) * (C / 16);
-            for (int w = wv; w < NO; w += NW) {
-                const int mj = w / (C / 16), nt = w % (C / 16);
-                f32x4 x = tile_mma<T, DK>(s.ST + 16 * mj * LDK, LDK, s.Qbar + 16 * nt * LDK, LDK, zero4(), lane);
-                x = tile_mma<T, C>(s.ET + 16 * mj * LDC, LDC, s.P1 + 16 * nt * LDC, LDC, x, lane);
-                x = tile_mma<T, C>(s.VT + 16 * mj * LDC, LDC, s.P2 + 16 * nt * LDC, LDC, x, lane);
-                const int t = 16 * nt + lrow;
-                if (t < Lc) store4(go + ((t0 + t) * H + h) * DV + dv0 + 16 * mj + 4 * lgrp, x);
+        // ---- P6: O^T += E^T P1^T (stored next iteration); S += Kc^T E; state -> LDS ---
+        if (wv != 0) {
+#pragma unroll
+            for (int i = 0; i < G::OTPWX; ++i) {
+                const int w = (wv - 1) + (NW - 1) * i;
+                if (w < G::NOT) {
+                    const int mj = w / (C / 16), nt = w % (C / 16);
+                    opend[i] = tile_mma<T, C>(s.ET + 16 * mj * LDC, LDC, s.P1 + 16 * nt * LDC, LDC, oacc[i], lane);
+                }
             }
         }
 #pragma unroll
@@ -430,16 +626,15 @@ __global__ void __launch_bounds__(256) kda_chunk_kernel(ChunkParams p) {
             const int ix = wv + NW * i;
             if (ix < G::NST) {
                 const int mi = ix / (DVS / 16), ni = ix % (DVS / 16);
-                const f32x4 gm = *reinterpret_cast<const f32x4*>(&s.gam[16 * mi + 4 * lgrp]);
-                f32x4 x = acc[i] * gm;
-                x = tile_mma<T, C>(s.KccT + 16 * mi * LDC, LDC, s.ET + 16 * ni * LDC, LDC, x, lane);
-                x = tile_mma<T, C>(s.KtcT + 16 * mi * LDC, LDC, s.VT + 16 * ni * LDC, LDC, x, lane);
-                acc[i] = x;
+                acc[i] = tile_mma_r<T, C>(s.KccT + prow<DK>(16 * mi + lrow) * LDC, s.ET + (16 * ni + lrow) * LDC,
+                                          acc[i], lane);
+                store4(&s.ST[(16 * ni + lrow) * LDK + 16 * mi + 4 * lgrp], acc[i]);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
+    if (Lc_prev > 0) store_o();
     if (p.ST) {
 #pragma unroll
         for (int i = 0; i < G::STPW; ++i) {
@@ -468,7 +663,7 @@ static hipError_t launch_cfg(const ChunkArgs& a, hipStream_t stream) {
     p.eq_len = a.cu_seqlens ? 0 : a.total_tokens / (a.num_seqs > 0 ? a.num_seqs : 1);
     const int64_t blocks = (int64_t)a.num_seqs * a.num_heads * a.split;
     p.xcd_group = (blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
-    hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC>), dim3((unsigned)blocks), dim3(ChunkCfg<T, DK, DVS, C>::NT), 0,
                        stream, p);
     return hipGetLastError();
 }

@@ -72,6 +72,10 @@ template <> struct Mma<bf16> {
     static __device__ __forceinline__ frag load(const bf16* p, int ld, int lane) {
         return *reinterpret_cast<const bf16x8*>(p + (lane & 15) * ld + (lane >> 4) * 8);
     }
+    // fragment whose row (this lane's m or n) starts at `row`
+    static __device__ __forceinline__ frag loadr(const bf16* row, int lane) {
+        return *reinterpret_cast<const bf16x8*>(row + (lane >> 4) * 8);
+    }
     static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
@@ -91,21 +95,35 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ frag load(const float* p, int ld, int lane) {
         return p[(lane & 15) * ld + (lane >> 4)];
     }
+    static __device__ __forceinline__ frag loadr(const float* row, int lane) { return row[lane >> 4]; }
     static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ frag scale(frag a, const float* f) { return a * f[0]; }
 };
 
-// acc += A[16 x Kdim] * B[Kdim x 16]; A given as [m][k] at pa (ld lda), B as
-// [n][k] at pb (ld ldb), both k-contiguous in LDS.
+// acc += A[16 x Kdim] * B[Kdim x 16], with this lane's A row starting at `ra`
+// and its B row (column of B) at `rb`, both k-contiguous in LDS.  All
+// fragments are read before the first product so their latencies overlap.
+template <typename T, int KDIM>
+__device__ __forceinline__ f32x4 tile_mma_r(const T* ra, const T* rb, f32x4 acc, int lane) {
+    constexpr int NK = KDIM / Mma<T>::K;
+    typename Mma<T>::frag a[NK], b[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+        a[k] = Mma<T>::loadr(ra + k * Mma<T>::K, lane);
+        b[k] = Mma<T>::loadr(rb + k * Mma<T>::K, lane);
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k) acc = Mma<T>::mma(a[k], b[k], acc);
+    return acc;
+}
+
+// Same, for A given as [m][k] at pa (ld lda) and B as [n][k] at pb (ld ldb).
 template <typename T, int KDIM>
 __device__ __forceinline__ f32x4 tile_mma(const T* pa, int lda, const T* pb, int ldb, f32x4 acc,
                                           int lane) {
-#pragma unroll
-    for (int k = 0; k < KDIM; k += Mma<T>::K)
-        acc = Mma<T>::mma(Mma<T>::load(pa + k, lda, lane), Mma<T>::load(pb + k, ldb, lane), acc);
-    return acc;
+    return tile_mma_r<T, KDIM>(pa + (lane & 15) * lda, pb + (lane & 15) * ldb, acc, lane);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
