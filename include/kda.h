@@ -60,7 +60,7 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, inconsistent dims */
     KDA_ERR_UNSUPPORTED = 2,      /* a (dk, dv, dtype, chunk) combination not compiled */
-    KDA_ERR_MISALIGNED = 3,       /* a pointer not 16-byte aligned */
+    KDA_ERR_MISALIGNED = 3,       /* a pointer below its required alignment (see above) */
     KDA_ERR_HIP = 4               /* the HIP runtime rejected a launch */
 } kda_status_t;
 
