@@ -168,6 +168,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--method", choices=["auto", "single", "two-pass"], default="auto")
+    ap.add_argument("--workspace-mib", type=int, default=0, help="two-pass workspace size (default: preferred)")
     ap.add_argument("--record-traffic", nargs=4, metavar="DIR", default=None)
     args = ap.parse_args()
 
@@ -201,10 +203,20 @@ def main():
         x = generate(wp, seed=3, device=dev)
         o = torch.empty((x["q"].shape[0], wp.heads, wp.dv), dtype=wp.dtype, device=dev)
         ST = torch.empty((wp.n_seqs, wp.heads, wp.dk, wp.dv), dtype=torch.float32, device=dev)
+        method = {"auto": kda.METHOD_AUTO, "single": kda.METHOD_SINGLE, "two-pass": kda.METHOD_TWO_PASS}[args.method]
+        wsb = kda.chunk_workspace_size(x["q"], x["v"], num_seqs=wp.n_seqs, method=method, max_seqlen=wp.seqlen)
+        if args.workspace_mib:
+            wsb = max(wsb and kda.chunk_workspace_size(x["q"], x["v"], num_seqs=wp.n_seqs, method=method,
+                                                       max_seqlen=wp.seqlen, minimum=True),
+                      args.workspace_mib << 20)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+        used = "two-pass" if wsb else "single"
+        log(f"prefill method {used}, workspace {wsb / 2**20:.1f} MiB")
 
         def step():
             kda.chunk_fwd(x["q"], x["k"], x["v"], x["log_a"], x["beta"], S0=x["S0"],
-                          cu_seqlens=x["cu_seqlens"], out=o, final_state=ST)
+                          cu_seqlens=x["cu_seqlens"], out=o, final_state=ST, method=method, workspace=ws,
+                          max_seqlen=wp.seqlen)
 
         log("prefill warmup")
         for _ in range(args.warmup):
@@ -224,7 +236,8 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic: seeded tensors with the layer's shapes and value distributions (no dataset)",
             "config": {"workload": wp.name, "batch": wp.n_seqs, "heads": wp.heads, "seq_len": wp.seqlen,
-                       "dk": wp.dk, "dv": wp.dv, "state": "fp32", "chunk": 32, "dv_split": "auto"},
+                       "dk": wp.dk, "dv": wp.dv, "state": "fp32", "chunk": 32, "dv_split": "auto",
+                       "method": used, "workspace_MiB": round(wsb / 2**20, 1)},
         })
         out["roofline"] = {
             "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -46,6 +46,7 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -69,6 +70,17 @@ typedef enum {
     KDA_BF16 = 1  /* q, k, v, o in bfloat16: products on bf16 matrix cores, fp32 state */
 } kda_dtype_t;
 
+/* Prefill algorithm.  Both compute the same chunkwise form. */
+typedef enum {
+    KDA_METHOD_AUTO = 0,      /* two-pass when compiled for the shape and a workspace is
+                                 given, else single-pass */
+    KDA_METHOD_SINGLE = 1,    /* one kernel; each workgroup walks its sequence and forms
+                                 every chunk's operators itself; no workspace */
+    KDA_METHOD_TWO_PASS = 2   /* a chunk-parallel pass writes each chunk's operators to
+                                 the workspace, a sequential pass applies them; needs a
+                                 workspace (kda_chunk_workspace_size); bf16 only */
+} kda_method_t;
+
 typedef struct {
     int32_t num_seqs;     /* N: sequences (prefill) or sequences of one token (decode) */
     int32_t num_heads;    /* H */
@@ -83,6 +95,11 @@ typedef struct {
     int32_t dv_split;     /* prefill: workgroups per (sequence, head) along dv;
                              0 = choose from the problem size, else 1, 2, 4 or 8
                              (each slice dv / split must be 16, 32 or 64) */
+    int32_t method;       /* prefill: kda_method_t */
+    int32_t reserved;     /* must be 0 */
+    int64_t max_seqlen;   /* prefill: an upper bound on the longest sequence, or 0 if
+                             unknown (then total_tokens is assumed).  Used only to size
+                             the two-pass workspace segments. */
 } kda_dims_t;
 
 /*
@@ -100,12 +117,28 @@ typedef struct {
  *   o         [T, H, dv]   qkv_dtype output, o_t = q_t S_t
  *   S_T       [N, H, dk, dv] float32 final states, or NULL to skip.  May alias
  *             S0 (every workgroup reads its part of S0 before it writes S_T).
- * Results do not depend on chunk_size or dv_split beyond rounding order.
+ *   workspace device scratch for the two-pass method (256-byte aligned), or
+ *             NULL; workspace_bytes its size.  The two-pass method processes the
+ *             sequences in segments of as many chunks as the workspace holds
+ *             (at least one); its contents are not needed after the call.
+ *             Calls that share a workspace must be ordered on one stream.
+ * Results do not depend on method, chunk_size or dv_split beyond rounding order.
  * Returns a kda_status_t.
  */
 KDA_API int kda_chunk_fwd(const kda_dims_t* dims, const void* q, const void* k, const void* v,
                   const float* log_a, const float* beta, const float* S0,
-                  const int32_t* cu_seqlens, void* o, float* S_T, void* stream);
+                  const int32_t* cu_seqlens, void* o, float* S_T, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace the two-pass prefill prefers for these dims (segments of about
+ * 128 MiB of operator blocks, which stay in the last-level cache between the
+ * two passes), or 0 if the call would run single-pass (method SINGLE, or no
+ * two-pass kernel for the shape).  The minimum that still runs two-pass is
+ * what one chunk per (sequence, head) needs: see kda_chunk_workspace_min.
+ */
+KDA_API int kda_chunk_workspace_size(const kda_dims_t* dims, size_t* bytes);
+KDA_API int kda_chunk_workspace_min(const kda_dims_t* dims, size_t* bytes);
 
 /*
  * One decode step: one token per sequence (T == N).

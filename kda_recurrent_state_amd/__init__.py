@@ -22,7 +22,8 @@ import threading
 
 import torch  # loads the HIP runtime the library then shares
 
-__all__ = ["chunk_fwd", "decode_step", "KdaError", "library_path", "load_library"]
+__all__ = ["chunk_fwd", "chunk_workspace_size", "decode_step", "KdaError", "library_path", "load_library",
+           "METHOD_AUTO", "METHOD_SINGLE", "METHOD_TWO_PASS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -42,7 +43,11 @@ class _Dims(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("total_tokens", ctypes.c_int64), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("qkv_dtype", ctypes.c_int32), ("scalar_decay", ctypes.c_int32),
-                ("chunk_size", ctypes.c_int32), ("dv_split", ctypes.c_int32)]
+                ("chunk_size", ctypes.c_int32), ("dv_split", ctypes.c_int32),
+                ("method", ctypes.c_int32), ("reserved", ctypes.c_int32), ("max_seqlen", ctypes.c_int64)]
+
+
+METHOD_AUTO, METHOD_SINGLE, METHOD_TWO_PASS = 0, 1, 2
 
 
 def library_path() -> str:
@@ -62,7 +67,12 @@ def load_library(build_if_missing: bool = True):
             lib = ctypes.CDLL(_LIB_PATH)
             P = ctypes.c_void_p
             lib.kda_chunk_fwd.restype = ctypes.c_int
-            lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P]
+            lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P,
+                                          ctypes.c_size_t, P]
+            for name in ("kda_chunk_workspace_size", "kda_chunk_workspace_min"):
+                fn = getattr(lib, name)
+                fn.restype = ctypes.c_int
+                fn.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(ctypes.c_size_t)]
             lib.kda_decode_step.restype = ctypes.c_int
             lib.kda_decode_step.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P]
             lib.kda_status_string.restype = ctypes.c_char_p
@@ -110,12 +120,19 @@ def _stream_handle(device):
 
 
 def chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, chunk_size: int = 0,
-              dv_split: int = 0, out=None, final_state=True, num_seqs: int | None = None):
+              dv_split: int = 0, out=None, final_state=True, num_seqs: int | None = None,
+              method: int = METHOD_AUTO, workspace=None, max_seqlen: int | None = None):
     """Chunked prefill over packed sequences; returns (o, S_T or None).
 
     cu_seqlens: int32 device tensor [N+1], or None for num_seqs (default 1)
     sequences of equal length.  final_state=False skips S_T; passing a tensor
-    writes S_T into it (it may be S0 itself)."""
+    writes S_T into it (it may be S0 itself).
+
+    method: METHOD_AUTO, METHOD_SINGLE or METHOD_TWO_PASS.  The two-pass method
+    needs device scratch: pass a uint8 tensor as `workspace`, or leave it None
+    to have one of the library's preferred size allocated (torch's caching
+    allocator) for this call.  max_seqlen bounds the longest sequence (with
+    cu_seqlens); when None it is read from cu_seqlens, which synchronises."""
     lib = load_library()
     _need(q, "q", ndim=3)
     T, H, dk = q.shape
@@ -152,11 +169,40 @@ def chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, chunk_size: int
         ST = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     else:
         ST = None
-    d = _Dims(N, H, T, dk, dv, _dtype_code(q), scalar, int(chunk_size), int(dv_split))
+    if max_seqlen is None:
+        if cu_seqlens is not None and N > 0 and method != METHOD_SINGLE:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
+        else:
+            max_seqlen = 0
+    d = _Dims(N, H, T, dk, dv, _dtype_code(q), scalar, int(chunk_size), int(dv_split), int(method), 0,
+              int(max_seqlen))
+    if workspace is None and method != METHOD_SINGLE:
+        need = ctypes.c_size_t(0)
+        _check(lib, lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(need)))
+        if need.value > 0:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
     st = lib.kda_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
-                           _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(ST), _stream_handle(q.device))
+                           _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(ST), _ptr(workspace),
+                           ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+                           _stream_handle(q.device))
     _check(lib, st)
     return o, ST
+
+
+def chunk_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, dv_split=0,
+                         method=METHOD_AUTO, max_seqlen=0, minimum=False):
+    """Bytes of workspace the prefill prefers (or, minimum=True, needs) for these
+    shapes; 0 when it would run single-pass."""
+    lib = load_library()
+    T, H, dk = q.shape
+    d = _Dims(int(num_seqs), H, T, dk, v.shape[2], _dtype_code(q), int(bool(scalar_decay)), int(chunk_size),
+              int(dv_split), int(method), 0, int(max_seqlen))
+    need = ctypes.c_size_t(0)
+    fn = lib.kda_chunk_workspace_min if minimum else lib.kda_chunk_workspace_size
+    _check(lib, fn(ctypes.byref(d), ctypes.byref(need)))
+    return need.value
 
 
 def decode_step(q, k, v, log_a, beta, S, *, out=None, S_out=None):
@@ -184,7 +230,7 @@ def decode_step(q, k, v, log_a, beta, S, *, out=None, S_out=None):
     _need(So, "S_out", torch.float32)
     o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     _need(o, "out", q.dtype)
-    d = _Dims(N, H, N, dk, dv, _dtype_code(q), scalar, 0, 0)
+    d = _Dims(N, H, N, dk, dv, _dtype_code(q), scalar, 0, 0, 0, 0, 0)
     st = lib.kda_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
                              _ptr(S), _ptr(So), _ptr(o), _stream_handle(q.device))
     _check(lib, st)

@@ -75,6 +75,76 @@ int choose_split(const kda_dims_t* d, int chunk) {
     return best;
 }
 
+// Plan of a prefill call: which method, chunk, split and, for the two-pass
+// method, the workspace layout [states of all units][operator blocks].
+struct Plan {
+    int method = KDA_METHOD_SINGLE;
+    int chunk = 32, split = 0;
+    int64_t units = 0, max_chunks = 0;
+    size_t block = 0, state_bytes = 0, min_bytes = 0, pref_bytes = 0;
+    bool two_pass_ok = false;
+};
+
+constexpr size_t kSegmentTarget = size_t(128) << 20;  // operator bytes per segment
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Smallest split with at least 256 workgroups among the two-pass shapes.
+int choose_split_two_pass(const kda_dims_t* d, int chunk) {
+    const int64_t units = (int64_t)d->num_seqs * d->num_heads;
+    int best = 0;
+    for (int split = 1; split <= 8; split *= 2) {
+        if (d->dv % split) break;
+        if (!kda::two_pass_supported(d->qkv_dtype, d->dk, d->dv / split, chunk)) continue;
+        best = split;
+        if (units * split >= 256) break;
+    }
+    return best;
+}
+
+// Validates the dims-level prefill arguments and fills the plan's shape part.
+int plan_prefill(const kda_dims_t* d, bool have_cu, Plan* pl) {
+    int st = check_dims(d);
+    if (st) return st;
+    pl->chunk = d->chunk_size == 0 ? 32 : d->chunk_size;
+    if (pl->chunk != 32 && pl->chunk != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size = %d: must be 0, 32 or 64", d->chunk_size);
+    if (d->method < KDA_METHOD_AUTO || d->method > KDA_METHOD_TWO_PASS)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "method = %d is not a kda_method_t", d->method);
+    if (d->reserved != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "reserved = %d must be 0", d->reserved);
+    if (d->max_seqlen < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "max_seqlen = %lld < 0", (long long)d->max_seqlen);
+    if (d->dv_split != 0 && d->dv_split != 1 && d->dv_split != 2 && d->dv_split != 4 && d->dv_split != 8)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "dv_split = %d: must be 0, 1, 2, 4 or 8", d->dv_split);
+    pl->units = (int64_t)d->num_seqs * d->num_heads;
+    if (d->num_seqs == 0) return KDA_OK;
+    int64_t maxlen = d->total_tokens;
+    if (!have_cu) maxlen = d->total_tokens / d->num_seqs;
+    else if (d->max_seqlen > 0) maxlen = d->max_seqlen < d->total_tokens ? d->max_seqlen : d->total_tokens;
+    pl->max_chunks = (maxlen + pl->chunk - 1) / pl->chunk;
+    // two-pass shape
+    int split2 = d->dv_split;
+    if (split2 == 0) split2 = choose_split_two_pass(d, pl->chunk);
+    else if (d->dv % split2 || !kda::two_pass_supported(d->qkv_dtype, d->dk, d->dv / split2, pl->chunk))
+        split2 = 0;
+    pl->block = (size_t)kda::prep_block_bytes(d->dk, pl->chunk);
+    pl->two_pass_ok = split2 > 0 && pl->block > 0 && d->method != KDA_METHOD_SINGLE;
+    if (d->method == KDA_METHOD_TWO_PASS && !pl->two_pass_ok)
+        return fail(KDA_ERR_UNSUPPORTED, "no two-pass prefill for dtype %d, dk %d, dv %d, chunk %d, dv_split %d",
+                    d->qkv_dtype, d->dk, d->dv, pl->chunk, d->dv_split);
+    if (pl->two_pass_ok) {
+        pl->state_bytes = round256((size_t)pl->units * d->dk * d->dv * 4);
+        const size_t per_chunk = (size_t)pl->units * pl->block;
+        int64_t m = (int64_t)(kSegmentTarget / per_chunk);
+        if (m > pl->max_chunks) m = pl->max_chunks;
+        if (m < 1) m = 1;
+        pl->min_bytes = pl->state_bytes + per_chunk;
+        pl->pref_bytes = pl->state_bytes + per_chunk * (size_t)m;
+        pl->split = split2;
+    }
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,14 +164,32 @@ const char* kda_status_string(int status) {
 
 const char* kda_last_error(void) { return g_last_error; }
 
+int kda_chunk_workspace_size(const kda_dims_t* d, size_t* bytes) {
+    if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    Plan pl;
+    int st = plan_prefill(d, true, &pl);
+    if (st) return st;
+    *bytes = pl.two_pass_ok ? pl.pref_bytes : 0;
+    return ok();
+}
+
+int kda_chunk_workspace_min(const kda_dims_t* d, size_t* bytes) {
+    if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    Plan pl;
+    int st = plan_prefill(d, true, &pl);
+    if (st) return st;
+    *bytes = pl.two_pass_ok ? pl.min_bytes : 0;
+    return ok();
+}
+
 int kda_chunk_fwd(const kda_dims_t* d, const void* q, const void* k, const void* v,
                   const float* log_a, const float* beta, const float* S0,
-                  const int32_t* cu_seqlens, void* o, float* S_T, void* stream) {
-    int st = check_dims(d);
+                  const int32_t* cu_seqlens, void* o, float* S_T, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    Plan pl;
+    int st = plan_prefill(d, cu_seqlens != nullptr, &pl);
     if (st) return st;
-    const int chunk = d->chunk_size == 0 ? 32 : d->chunk_size;
-    if (chunk != 32 && chunk != 64)
-        return fail(KDA_ERR_UNSUPPORTED, "chunk_size = %d: must be 0, 32 or 64", d->chunk_size);
+    const int chunk = pl.chunk;
     if (d->num_seqs == 0) {
         if (d->total_tokens != 0)
             return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs = 0 but total_tokens = %lld",
@@ -123,18 +211,59 @@ int kda_chunk_fwd(const kda_dims_t* d, const void* q, const void* k, const void*
     if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u))
         return fail(KDA_ERR_MISALIGNED, "cu_seqlens is not 4-byte aligned");
 
+    // method
+    bool two_pass = false;
+    if (pl.two_pass_ok) {
+        const bool have_ws = workspace && workspace_bytes >= pl.min_bytes;
+        if (d->method == KDA_METHOD_TWO_PASS && !have_ws)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "two-pass prefill needs a workspace of at least %zu bytes (got %zu)",
+                        pl.min_bytes, workspace ? workspace_bytes : (size_t)0);
+        two_pass = have_ws;
+    }
+    if (two_pass) {
+        if ((uintptr_t)workspace & 255u) return fail(KDA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+        const size_t per_chunk = (size_t)pl.units * pl.block;
+        int64_t m = (int64_t)((workspace_bytes - pl.state_bytes) / per_chunk);
+        if (m > pl.max_chunks) m = pl.max_chunks;
+        if (m < 1) m = 1;
+        if (pl.units * m > 0x7fffffff || pl.units * pl.split > 0x7fffffff)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "too many (sequence, head) units: %lld", (long long)pl.units);
+        const int64_t nseg = pl.max_chunks > 0 ? (pl.max_chunks + m - 1) / m : 1;
+        uint8_t* ws = static_cast<uint8_t*>(workspace);
+        float* run = S_T ? S_T : reinterpret_cast<float*>(ws);
+        uint8_t* blocks = ws + pl.state_bytes;
+        const int64_t eq_len = cu_seqlens ? 0 : d->total_tokens / d->num_seqs;
+        for (int64_t sgi = 0; sgi < nseg; ++sgi) {
+            const int64_t chunk0 = sgi * m;
+            hipError_t e = hipSuccess;
+            if (d->total_tokens > 0) {
+                kda::PrepLaunch pa;
+                pa.q = q; pa.k = k; pa.log_a = log_a; pa.beta = beta; pa.cu_seqlens = cu_seqlens;
+                pa.eq_len = eq_len; pa.ws = blocks; pa.num_heads = d->num_heads; pa.units = pl.units;
+                pa.m = (int32_t)m; pa.chunk0 = chunk0; pa.dk = d->dk; pa.chunk = chunk; pa.scalar = d->scalar_decay;
+                e = kda::launch_prep(pa, (hipStream_t)stream);
+                if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill operator pass launch: %s", hipGetErrorString(e));
+            }
+            kda::ScanLaunch sa;
+            sa.v = v; sa.o = o; sa.cu_seqlens = cu_seqlens; sa.eq_len = eq_len; sa.ws = blocks;
+            sa.S_in = sgi == 0 ? S0 : run; sa.S_out = run; sa.num_heads = d->num_heads; sa.units = pl.units;
+            sa.dk = d->dk; sa.dv = d->dv; sa.split = pl.split; sa.m = (int32_t)m; sa.chunk = chunk;
+            sa.chunk0 = chunk0;
+            e = kda::launch_scan(sa, (hipStream_t)stream);
+            if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill state pass launch: %s", hipGetErrorString(e));
+        }
+        return ok();
+    }
+
     int split = d->dv_split;
     if (split == 0) {
         split = choose_split(d, chunk);
         if (split == 0)
             return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, dk %d, dv %d, chunk %d",
                         d->qkv_dtype, d->dk, d->dv, chunk);
-    } else {
-        if (split != 1 && split != 2 && split != 4 && split != 8)
-            return fail(KDA_ERR_INVALID_ARGUMENT, "dv_split = %d: must be 0, 1, 2, 4 or 8", split);
-        if (d->dv % split || !kda::chunk_supported(d->qkv_dtype, d->dk, d->dv / split, chunk, d->scalar_decay))
-            return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, dk %d, dv %d / split %d, chunk %d",
-                        d->qkv_dtype, d->dk, d->dv, split, chunk);
+    } else if (d->dv % split || !kda::chunk_supported(d->qkv_dtype, d->dk, d->dv / split, chunk, d->scalar_decay)) {
+        return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, dk %d, dv %d / split %d, chunk %d",
+                    d->qkv_dtype, d->dk, d->dv, split, chunk);
     }
     const int64_t blocks = (int64_t)d->num_seqs * d->num_heads * split;
     if (blocks > 0x7fffffff)

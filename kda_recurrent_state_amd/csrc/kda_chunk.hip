@@ -43,12 +43,10 @@
 //   P4  wavefront 0: (I + A)^-1;  the others: Z, first O terms, Gamma S + Kt^T bV
 //   P5  E = -Tb Z
 //   P6  O += P1 E, S += Kc^T E
-#include "kda_device.hpp"
+#include "kda_chunk_common.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
-
-constexpr float LOG2E = 1.4426950408889634f;
 
 template <typename T, int DK, int DVS, int C>
 struct ChunkCfg {
@@ -71,31 +69,6 @@ struct ChunkCfg {
     static constexpr int OTPW = (NOT + NW - 1) / NW;
     static constexpr int OTPWX = (NOT + NW - 2) / (NW - 1);  // per wavefront 1..NW-1
 };
-
-// Unit (4 tokens x 2 channels) of thread slot uu: a wavefront covers 32
-// consecutive channel pairs of two token groups, so its row-major stores are
-// contiguous and its transposed stores use every LDS bank.
-template <int NCP>
-__device__ __forceinline__ void unit_of(int uu, int& c, int& tg) {
-    if constexpr (NCP >= 32) {
-        const int w = uu >> 6, l = uu & 63;
-        constexpr int HALVES = NCP / 32;  // 32-pair groups of the channel pairs
-        c = 2 * ((l & 31) + 32 * (w % HALVES));
-        tg = (l >> 5) + 2 * (w / HALVES);
-    } else {
-        c = 2 * (uu % NCP);
-        tg = uu / NCP;
-    }
-}
-
-// Transposed operands ([channel][token]) are written four channels at a time
-// by one thread.  Their rows are stored in four planes, channel c at row
-// (c & 3) * (N/4 + 4) + (c >> 2), so neither those writes nor the matrix-core
-// fragment reads of 16 consecutive channels collide on LDS banks.
-template <int N>
-__device__ __forceinline__ int prow(int c) { return (c & 3) * (N / 4 + 4) + (c >> 2); }
-template <int N>
-constexpr int prows() { return N + 16; }
 
 template <typename T, int DK, int DVS, int C>
 struct ChunkLds {
@@ -140,44 +113,6 @@ struct ChunkParams {
     int H, DV, split, xcd_group;
     int64_t eq_len;  // used when cu is null
 };
-
-// Workgroup barrier that orders LDS only: global loads issued before it stay in
-// flight (the next chunk's inputs are prefetched across it).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Orders LDS traffic between lanes of one wavefront (no workgroup barrier).
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
-__device__ __forceinline__ float uniform(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-}
-
-template <typename T> struct Vec2;
-template <> struct Vec2<bf16> {
-    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 type;
-    static __device__ __forceinline__ float lo(type v) { return (float)v[0]; }
-    static __device__ __forceinline__ float hi(type v) { return (float)v[1]; }
-    static __device__ __forceinline__ type make(float a, float b) { type r; r[0] = (bf16)a; r[1] = (bf16)b; return r; }
-};
-template <> struct Vec2<float> {
-    typedef __attribute__((__vector_size__(2 * sizeof(float)))) float type;
-    static __device__ __forceinline__ float lo(type v) { return v[0]; }
-    static __device__ __forceinline__ float hi(type v) { return v[1]; }
-    static __device__ __forceinline__ type make(float a, float b) { type r; r[0] = a; r[1] = b; return r; }
-};
-typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
-
-template <typename T>
-__device__ __forceinline__ void store2(T* p, float a, float b) {
-    *reinterpret_cast<typename Vec2<T>::type*>(p) = Vec2<T>::make(a, b);
-}
 
 // Raw inputs of one 4-token x 2-channel unit, held in registers one chunk ahead.
 template <typename T>
@@ -237,80 +172,6 @@ __device__ __forceinline__ void load_chunk(const ChunkParams& p, const T* gq, co
                 vi[u].b[i] = p.beta[row];
             }
         }
-    }
-}
-
-// (I + A)^-1 diag(b) for a strictly lower C x C matrix A (fp32, row-major, ld
-// LDA), on one wavefront, written as Tb (row-major, ld LDC, upper blocks left
-// untouched).  Blocked right-looking forward substitution on fp32 matrix
-// cores: the right-hand sides (identity columns of one 16-column block) live
-// in 16 x 16 accumulator tiles, where lane group g holds rows 4g..4g+3; each
-// 4-row panel is solved inside the lanes that hold it, passed to all lanes
-// through LDS (X, double-buffered), and every tile below is updated with one
-// 16x16x4 product.  Block columns are independent chains.  All coefficients
-// are read before the chain starts (the uniform ones into scalar registers);
-// the code has no lane-dependent branches.
-template <typename T, int C, int LDA, int LDC>
-__device__ __forceinline__ void block_inverse(const float* A, const float* beta, float* X, T* Tb, int lane) {
-    constexpr int NB = C / 16, NP = 4 * NB;
-    const int l16 = lane & 15, lg = lane >> 4;
-    float cf[NP][6];
-    float aop[NP][NB];
-#pragma unroll
-    for (int sp = 0; sp < NP; ++sp) {
-        const int r0 = 4 * sp;
-        cf[sp][0] = uniform(A[(r0 + 1) * LDA + r0]);
-        cf[sp][1] = uniform(A[(r0 + 2) * LDA + r0]);
-        cf[sp][2] = uniform(A[(r0 + 2) * LDA + r0 + 1]);
-        cf[sp][3] = uniform(A[(r0 + 3) * LDA + r0]);
-        cf[sp][4] = uniform(A[(r0 + 3) * LDA + r0 + 1]);
-        cf[sp][5] = uniform(A[(r0 + 3) * LDA + r0 + 2]);
-#pragma unroll
-        for (int tr = 0; tr < NB; ++tr) {
-            const int row = 16 * tr + l16;
-            const float x = (tr >= sp / 4) ? A[row * LDA + r0 + lg] : 0.f;
-            aop[sp][tr] = (row > r0 + 3) ? -x : 0.f;
-        }
-    }
-    f32x4 R[NB][NB];  // R[bc][tr]: rows of tile tr, columns of block column bc
-#pragma unroll
-    for (int bc = 0; bc < NB; ++bc)
-#pragma unroll
-        for (int tr = 0; tr < NB; ++tr)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) R[bc][tr][r] = (tr == bc && 4 * lg + r == l16) ? 1.f : 0.f;
-#pragma unroll
-    for (int sp = 0; sp < NP; ++sp) {  // panel: rows 4 sp .. 4 sp + 3
-        const int ts = sp / 4, g = sp % 4;
-        float* Xb = X + (sp & 1) * (NB * 256);
-#pragma unroll
-        for (int bc = 0; bc <= ts; ++bc) {
-            f32x4 x = R[bc][ts];
-            x[1] -= cf[sp][0] * x[0];
-            x[2] -= cf[sp][1] * x[0] + cf[sp][2] * x[1];
-            x[3] -= cf[sp][3] * x[0] + cf[sp][4] * x[1] + cf[sp][5] * x[2];
-            R[bc][ts] = (lg == g) ? x : R[bc][ts];
-            // every lane group writes its own slot; group g's slot is the panel
-            *reinterpret_cast<f32x4*>(&Xb[bc * 256 + lg * 64 + 4 * l16]) = x;
-        }
-        wave_sync();
-#pragma unroll
-        for (int bc = 0; bc <= ts; ++bc) {
-            const float bk = Xb[bc * 256 + g * 64 + 4 * l16 + lg];  // B[k = lg][n = l16]
-#pragma unroll
-            for (int tr = ts; tr < NB; ++tr)
-                R[bc][tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[sp][tr], bk, R[bc][tr], 0, 0, 0);
-        }
-    }
-    // Tb = T diag(b): lane holds column 16 bc + l16, rows 16 tr + 4 lg + r
-#pragma unroll
-    for (int bc = 0; bc < NB; ++bc) {
-        const float bcol = beta[16 * bc + l16];
-#pragma unroll
-        for (int tr = bc; tr < NB; ++tr)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Tb[(16 * tr + 4 * lg + r) * LDC + 16 * bc + l16] = from_f32<T>(R[bc][tr][r] * bcol);
     }
 }
 

@@ -35,4 +35,38 @@ hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int64_t heads, c
 bool chunk_supported(int dtype, int dk, int dvs, int chunk, int scalar);
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t stream);
 
+// Two-pass prefill: a chunk-parallel pass writes one operator block per
+// (sequence, head, chunk) of a segment of m chunks; a sequential pass applies them.
+struct PrepLaunch {
+    const void* q;
+    const void* k;
+    const float* log_a;
+    const float* beta;
+    const int32_t* cu_seqlens;  // device; may be null (equal lengths eq_len)
+    int64_t eq_len;
+    void* ws;                   // blocks [units][m]
+    int32_t num_heads;
+    int64_t units;              // num_seqs * num_heads
+    int32_t m;                  // chunks per unit in the segment
+    int64_t chunk0;             // first chunk of the segment
+    int32_t dk, chunk, scalar;
+};
+struct ScanLaunch {
+    const void* v;
+    void* o;
+    const int32_t* cu_seqlens;
+    int64_t eq_len;
+    const void* ws;
+    const float* S_in;          // may be null (zero state)
+    float* S_out;
+    int32_t num_heads;
+    int64_t units;
+    int32_t dk, dv, split, m, chunk;
+    int64_t chunk0;
+};
+int prep_block_bytes(int dk, int chunk);  // 0 if no prep kernel for (dk, chunk)
+hipError_t launch_prep(const PrepLaunch& a, hipStream_t stream);
+bool two_pass_supported(int dtype, int dk, int dvs, int chunk);
+hipError_t launch_scan(const ScanLaunch& a, hipStream_t stream);
+
 }  // namespace kda

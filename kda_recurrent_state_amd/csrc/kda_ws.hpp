@@ -1,0 +1,64 @@
+// kda_ws.hpp -- layout of the per-chunk operator blocks that the two-pass
+// prefill hands from its chunk-parallel pass (kda_prep.hip) to its sequential
+// pass (kda_scan.hip).
+//
+// For one chunk of one (sequence, head) the block holds, in bf16 unless noted:
+//   W   [C][DK]   T diag(b) Kb                      (rows: tokens)
+//   QP  [C][DK]   Qb - P1 W                         (rows: tokens)
+//   KC  [DK][C]   (Kc Diag(e^{g_C}))^T              (rows: key channels)
+//   KT  [DK][C]   (diag(b) Kt Diag(e^{g_C}))^T      (rows: key channels)
+//   M1  [C][C]    T diag(b) L diag(b)               (rows: tokens)
+//   M2  [C][C]    P2 diag(b) - P1 M1                (rows: tokens)
+//   GAM [DK]      e^{g_C}, fp32
+// so that the sequential pass computes, per chunk and value column block,
+//   E = -(W S + M1 V),  O = QP S + M2 V,  S <- Diag(GAM) S + KC E + KT V.
+//
+// Every matrix is stored as the matrix-core operand it becomes: its rows are
+// the operand's m (or n) index, and its contraction index (columns) is
+// permuted inside each 32-wide block so that a 16 x 16 accumulator tile pair
+// can be fed back as an operand without leaving registers:
+//   position p = 8 * ((x % 16) / 4) + 4 * (x / 16) + x % 4   for x = index % 32
+// (lane group g of an accumulator holds rows 4g..4g+3 of each 16-row tile;
+// the operand wants 8 consecutive contraction positions 8g..8g+7 per lane).
+// The 16-byte pieces of each row are also XOR-swizzled with the row index so
+// that 16 lanes reading the same column piece of 16 rows hit distinct LDS
+// banks after a verbatim copy into LDS.
+#pragma once
+
+#include <stdint.h>
+
+namespace kda {
+
+template <int DK, int C>
+struct WsBlock {
+    static constexpr int W = 0;
+    static constexpr int QP = W + C * DK * 2;
+    static constexpr int KC = QP + C * DK * 2;
+    static constexpr int KT = KC + DK * C * 2;
+    static constexpr int M1 = KT + DK * C * 2;
+    static constexpr int M2 = M1 + C * C * 2;
+    static constexpr int GAM = M2 + C * C * 2;
+    static constexpr int BYTES = (GAM + DK * 4 + 255) / 256 * 256;  // 256-byte aligned blocks
+};
+
+// permuted position of contraction index x
+__host__ __device__ constexpr int kperm(int x) {
+    return (x & ~31) + 8 * ((x & 15) >> 2) + 4 * ((x & 31) >> 4) + (x & 3);
+}
+
+// byte offset of the 16-byte piece `piece` of row `row` in a matrix whose rows
+// are RB bytes long (RB = 64, 128 or 256)
+template <int RB>
+__host__ __device__ constexpr int swz(int row, int piece) {
+    constexpr int NP = RB / 16;                  // pieces per row
+    constexpr int RPW = NP >= 16 ? 1 : 16 / NP;  // rows per 256-byte window
+    return row * RB + 16 * (piece ^ ((row / RPW) % NP));
+}
+
+// byte offset of element (row, position p) of a bf16 matrix with RB-byte rows
+template <int RB>
+__host__ __device__ constexpr int swz_elem(int row, int p) {
+    return swz<RB>(row, p >> 3) + 2 * (p & 7);
+}
+
+}  // namespace kda

@@ -146,3 +146,98 @@ def chunk_forward(q, k, v, la, beta, S0=None, C=64, bf16=False):
         Oc, S = chunk_step(pad(q, 0), pad(k, 0), pad(v, 0), pad(la, 0), pad(beta, 0), S, bf16=bf16)
         O[s:e] = Oc[:n]
     return O, S
+
+
+def chunk_operators(q, k, la, beta, bf16=False):
+    """The value-independent operators of one chunk, in the factored form the
+    two-kernel GPU prefill uses (a chunk-parallel pass computes these; the
+    sequential pass only applies them):
+
+      W  = T diag(b) Kb              M1 = T diag(b) L diag(b)
+      Q' = Qb - P1 W                 M2 = P2 diag(b) - P1 M1
+      Kc' = Kc Diag(e^{g_C})         Kt' = diag(b) Kt Diag(e^{g_C}),   G = e^{g_C}
+
+    so that, with E = -(W S + M1 V):
+      O = Q' S + M2 V,   S_C = Diag(G) S + Kc'^T E + Kt'^T V.
+    bf16=True rounds each operator once, where the GPU stores it."""
+    C, dk = q.shape
+    rnd = _bf16 if bf16 else (lambda x: x)
+    nb = C // SUB
+    lam = np.zeros((C, dk))
+    Lam = np.zeros((nb, dk))
+    for b in range(nb):
+        lam[b * SUB:(b + 1) * SUB] = np.cumsum(la[b * SUB:(b + 1) * SUB], axis=0)
+        Lam[b] = lam[(b + 1) * SUB - 1]
+    rho = np.concatenate([np.zeros((1, dk)), np.cumsum(Lam, axis=0)])
+    gC = rho[nb]
+    mid = np.array([lam[b * SUB + SUB // 2 - 1] for b in range(nb)])
+    mu = rho[:nb] + mid
+    rin = np.zeros((C, dk))
+    rex = np.zeros((C, dk))
+    for t in range(C):
+        b = t // SUB
+        rin[t] = np.exp(lam[t] - mid[b])
+        prev = lam[t - 1] if t % SUB else np.zeros(dk)
+        rex[t] = np.exp(prev - mid[b])
+    cin, cex = 1.0 / rin, 1.0 / rex
+    blk = np.arange(C) // SUB
+    emu = np.exp(mu)[blk]
+    ecmu = np.exp(gC[None, :] - mu)[blk]
+    Kr, Qr, Kce, Kci = rnd(k * rex), rnd(q * rin), rnd(k * cex), rnd(k * cin)
+    Kbar = rnd(k * rex * emu)
+    Qbar = q * rin * emu
+    A = np.zeros((C, C)); L = np.zeros((C, C)); P1 = np.zeros((C, C)); P2 = np.zeros((C, C))
+    for bt in range(nb):
+        st = slice(bt * SUB, (bt + 1) * SUB)
+        for bi in range(bt + 1):
+            si = slice(bi * SUB, (bi + 1) * SUB)
+            if bt == bi:
+                kr, qr = Kr[st], Qr[st]
+            else:
+                F = np.exp(mu[bt] - mu[bi])
+                kr, qr = rnd(Kr[st] * F), rnd(Qr[st] * F)
+            A[st, si] = kr @ Kce[si].T
+            L[st, si] = kr @ Kci[si].T
+            P1[st, si] = qr @ Kce[si].T
+            P2[st, si] = qr @ Kci[si].T
+    A = np.tril(A, -1) * beta[:, None]
+    Lb = rnd(np.tril(L, -1) * beta[None, :])
+    P1 = rnd(np.tril(P1))
+    P2b = np.tril(P2) * beta[None, :]
+    Tb = rnd(_unit_lower_inverse(A) * beta[None, :])
+    W = rnd(Tb @ Kbar)
+    M1 = rnd(Tb @ Lb)
+    Qp = rnd(Qbar - P1 @ W)
+    M2 = rnd(P2b - P1 @ M1)
+    Kc2 = rnd(k * cex * ecmu)
+    Kt2 = rnd(beta[:, None] * k * cin * ecmu)
+    return dict(W=W, Qp=Qp, M1=M1, M2=M2, Kc=Kc2, Kt=Kt2, G=np.exp(gC))
+
+
+def chunk_apply(ops, v, S, bf16=False):
+    """The sequential part: apply one chunk's operators to the state."""
+    rnd = _bf16 if bf16 else (lambda x: x)
+    V = rnd(v)
+    Sr = rnd(S)
+    E = rnd(-(ops["W"] @ Sr + ops["M1"] @ V))
+    O = ops["Qp"] @ Sr + ops["M2"] @ V
+    S_new = ops["G"][:, None] * S + ops["Kc"].T @ E + ops["Kt"].T @ V
+    return O, S_new
+
+
+def chunk_forward_split(q, k, v, la, beta, S0=None, C=32, bf16=False):
+    """chunk_forward through chunk_operators / chunk_apply (same padding)."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    if la.ndim == 1:
+        la = np.repeat(la[:, None], dk, axis=1)
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    O = np.zeros((T, dv))
+    for s in range(0, T, C):
+        e = min(T, s + C)
+        n = e - s
+        pad = lambda x: np.concatenate([x[s:e], np.zeros((C - n,) + x.shape[1:])]) if n < C else x[s:e]
+        ops = chunk_operators(pad(q), pad(k), pad(la), pad(beta), bf16=bf16)
+        Oc, S = chunk_apply(ops, pad(v), S, bf16=bf16)
+        O[s:e] = Oc[:n]
+    return O, S

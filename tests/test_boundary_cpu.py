@@ -31,8 +31,8 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    assert {"kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_last_error",
-            "kda_version"} <= set(names)
+    assert {"kda_chunk_fwd", "kda_chunk_workspace_size", "kda_chunk_workspace_min", "kda_decode_step",
+            "kda_status_string", "kda_last_error", "kda_version"} <= set(names)
 
 
 def test_every_declared_symbol_exported(lib):
@@ -42,15 +42,17 @@ def test_every_declared_symbol_exported(lib):
 
 def dims(**kw):
     base = dict(num_seqs=2, num_heads=4, total_tokens=128, dk=128, dv=128, qkv_dtype=1,
-                scalar_decay=0, chunk_size=0, dv_split=0)
+                scalar_decay=0, chunk_size=0, dv_split=0, method=0, reserved=0, max_seqlen=0)
     base.update(kw)
     return kda._Dims(**base)
 
 
-def prefill(lib, d, q=GOOD, k=GOOD, v=GOOD, la=GOOD, beta=GOOD, S0=None, cu=GOOD, o=GOOD, ST=GOOD):
+def prefill(lib, d, q=GOOD, k=GOOD, v=GOOD, la=GOOD, beta=GOOD, S0=None, cu=GOOD, o=GOOD, ST=GOOD,
+            ws=None, ws_bytes=0):
     P = lambda x: None if x is None else ctypes.c_void_p(x)
     dp = None if d is None else ctypes.byref(d)
-    return lib.kda_chunk_fwd(dp, P(q), P(k), P(v), P(la), P(beta), P(S0), P(cu), P(o), P(ST), None)
+    return lib.kda_chunk_fwd(dp, P(q), P(k), P(v), P(la), P(beta), P(S0), P(cu), P(o), P(ST), P(ws),
+                             ctypes.c_size_t(ws_bytes), None)
 
 
 def decode(lib, d, q=GOOD, k=GOOD, v=GOOD, la=GOOD, beta=GOOD, Si=GOOD, So=GOOD, o=GOOD):
@@ -80,6 +82,13 @@ def decode(lib, d, q=GOOD, k=GOOD, v=GOOD, la=GOOD, beta=GOOD, Si=GOOD, So=GOOD,
     (dict(d=dims(total_tokens=127), cu=None), INVALID),
     (dict(d=dims(num_seqs=0, total_tokens=5)), INVALID),
     (dict(d=dims(num_seqs=0, total_tokens=0), q=None, cu=None), OK),  # nothing to do
+    (dict(d=dims(method=3)), INVALID),
+    (dict(d=dims(reserved=1)), INVALID),
+    (dict(d=dims(max_seqlen=-1)), INVALID),
+    (dict(d=dims(method=2, qkv_dtype=0, dk=64, dv=64)), UNSUPPORTED),  # two-pass is bf16 only
+    (dict(d=dims(method=2)), INVALID),                                   # no workspace
+    (dict(d=dims(method=2), ws=GOOD, ws_bytes=64), INVALID),             # workspace too small
+    (dict(d=dims(method=2), ws=GOOD + 16, ws_bytes=1 << 30), MISALIGNED),
 ])
 def test_prefill_validation(lib, case, expect):
     st = prefill(lib, **case)
@@ -108,6 +117,22 @@ def test_scalar_arrays_need_only_4_byte_alignment(lib):
     assert st == MISALIGNED and lib.kda_last_error().decode().startswith("o is not")
     st = decode(lib, dims(total_tokens=2), la=GOOD + 4, beta=GOOD + 4, o=GOOD + 2)
     assert st == MISALIGNED and lib.kda_last_error().decode().startswith("o is not")
+
+
+def test_workspace_sizes(lib):
+    size, least = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    d = dims(num_seqs=2, num_heads=32, total_tokens=2 * 32768)
+    assert lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(size)) == OK
+    assert lib.kda_chunk_workspace_min(ctypes.byref(d), ctypes.byref(least)) == OK
+    units, state = 64, 64 * 128 * 128 * 4
+    assert least.value > state and (least.value - state) % units == 0
+    block = (least.value - state) // units
+    assert block % 256 == 0 and size.value >= least.value and (size.value - state) % (units * block) == 0
+    assert (size.value - state) <= (128 << 20)  # segments of at most 128 MiB of blocks
+    d = dims(method=1)
+    assert lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(size)) == OK and size.value == 0
+    d = dims(qkv_dtype=0, dk=64, dv=64)  # fp32 runs single-pass only
+    assert lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(size)) == OK and size.value == 0
 
 
 def test_status_strings(lib):

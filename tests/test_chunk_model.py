@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from oracle import kda_oracle
-from tests.chunk_model import chunk_forward
+from tests.chunk_model import chunk_forward, chunk_forward_split
 
 
 def draw(T, dk, dv, seed, la_std=2.0, clip=-8.0, scalar=False, s0=0.02):
@@ -78,3 +78,21 @@ def test_padding_rows_change_nothing():
     # and the chunk model, padded the same way, agrees over a ragged last chunk
     o, S = chunk_forward(qp, kp, vp, lap, bp, S0=S0, C=32)
     assert rel(o[:T], ro) < 1e-10 and rel(S, rS) < 1e-10
+
+
+@pytest.mark.parametrize("T,C", [(100, 32), (96, 64), (33, 32)])
+def test_factored_operators_equal_token_loop(T, C):
+    """The factored form (value-independent operators W, Q', M1, M2, Kc', Kt',
+    G per chunk, then O = Q' S + M2 V, S <- G S + Kc'^T E + Kt'^T V with
+    E = -(W S + M1 V)) is the same map."""
+    q, k, v, la, beta, S0 = draw(T, 16, 8, seed=2 * T + C)
+    ro, rS = oracle_one(q, k, v, la, beta, S0)
+    o, S = chunk_forward_split(q, k, v, la, beta, S0=S0, C=C)
+    assert rel(o, ro) < 1e-10 and rel(S, rS) < 1e-10
+
+
+def test_factored_operators_in_bf16_meet_bf16_bar():
+    q, k, v, la, beta, S0 = draw(160, 128, 32, seed=4)
+    ro, rS = oracle_one(q, k, v, la, beta, S0)
+    o, S = chunk_forward_split(q, k, v, la, beta, S0=S0, C=32, bf16=True)
+    assert rel(o, ro) < 2e-2 and rel(S, rS) < 2e-2

@@ -46,27 +46,74 @@ def test_prefill_fp32_varlen(dk, dv, scalar):
     check_all(inp, o, ST, 1e-4)
 
 
+SINGLE, TWO = kda.METHOD_SINGLE, kda.METHOD_TWO_PASS
+
+
+def run_method(inp, method, **kw):
+    """Prefill with an explicit method; skips when that method is not compiled."""
+    try:
+        return gpu_prefill(inp, method=method, **kw)
+    except kda.KdaError as e:
+        if e.status == 2:
+            pytest.skip(f"method {method} not compiled for this shape: {e}")
+        raise
+
+
+@pytest.mark.parametrize("method", [SINGLE, TWO])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (32, 32), (128, 64), (64, 128), (128, 32)])
 @pytest.mark.parametrize("scalar", [False, True])
-def test_prefill_bf16_varlen(dk, dv, scalar):
-    log(f"prefill bf16 varlen dk={dk} dv={dv} scalar={scalar}")
+def test_prefill_bf16_varlen(dk, dv, scalar, method):
+    log(f"prefill bf16 varlen dk={dk} dv={dv} scalar={scalar} method={method}")
     w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=4, heads=3, dk=dk, dv=dv, scalar_decay=scalar)
     inp = generate(w, seed=dk + dv + scalar, device=DEV, lengths=[45, 0, 170, 96])
-    o, ST = gpu_prefill(inp)
+    o, ST = run_method(inp, method)
     check_all(inp, o, ST, 2e-2)
 
 
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_two_pass_segments(chunk):
+    """The two-pass method with the smallest workspace (one chunk per segment),
+    a middle one, and the preferred one agree with the oracle and each other;
+    without S_T the running state lives in the workspace."""
+    log(f"two-pass segments chunk={chunk}")
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=3, heads=2, dk=64, dv=64)
+    inp = generate(w, seed=21 + chunk, device=DEV, lengths=[300, 7, 161])
+    q, v = inp["q"], inp["v"]
+    least = kda.chunk_workspace_size(q, v, num_seqs=3, chunk_size=chunk, method=TWO, max_seqlen=300,
+                                     minimum=True)
+    pref = kda.chunk_workspace_size(q, v, num_seqs=3, chunk_size=chunk, method=TWO, max_seqlen=300)
+    assert 0 < least <= pref
+    ref = None
+    for nbytes in sorted({least, least + (pref - least) // 2, pref}):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        o, ST = run_method(inp, TWO, chunk_size=chunk, workspace=ws, max_seqlen=300)
+        check_all(inp, o, ST, 2e-2, f"workspace {nbytes}")
+        o2, none = run_method(inp, TWO, chunk_size=chunk, workspace=ws, max_seqlen=300, final_state=False)
+        assert none is None and torch.equal(o2, o)
+        if ref is None:
+            ref = (o, ST)
+        else:
+            assert torch.equal(o, ref[0]) and torch.equal(ST, ref[1])  # segmenting is exact
+
+
+def test_two_pass_matches_single_pass():
+    log("two-pass vs single-pass, d=128")
+    w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seqlen=1000, heads=2)
+    inp = generate(w, seed=22, device=DEV)
+    o1, S1 = run_method(inp, SINGLE)
+    o2, S2 = run_method(inp, TWO)
+    check_all(inp, o2, S2, 2e-2, "two-pass")
+    assert max_rel_err(o2, o1) <= 2e-2 and max_rel_err(S2, S1) <= 2e-2
+
+
+@pytest.mark.parametrize("method", [SINGLE, TWO])
 @pytest.mark.parametrize("split", [1, 2, 4, 8])
-def test_prefill_dv_split_invariance(split):
+def test_prefill_dv_split_invariance(split, method):
     """Splitting dv over workgroups changes nothing beyond rounding."""
-    log(f"prefill dv_split={split}")
+    log(f"prefill dv_split={split} method={method}")
     w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seqlen=200, heads=2, dk=64, dv=64)
     inp = generate(w, seed=5, device=DEV)
-    try:
-        o, ST = gpu_prefill(inp, dv_split=split)
-    except kda.KdaError as e:
-        assert e.status == 2  # configuration not compiled
-        pytest.skip(f"dv_split={split} not compiled for dk=dv=64")
+    o, ST = run_method(inp, method, dv_split=split)
     check_all(inp, o, ST, 2e-2, f"split {split}")
 
 
@@ -100,25 +147,27 @@ def test_prefill_continuation_and_alias():
     check_all(inp, o, ST, 2e-2, "one pass")
 
 
-def test_prefill_deterministic():
-    log("prefill determinism")
+@pytest.mark.parametrize("method", [SINGLE, TWO])
+def test_prefill_deterministic(method):
+    log(f"prefill determinism method={method}")
     w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seqlen=256, heads=4)
     inp = generate(w, seed=8, device=DEV)
-    a = gpu_prefill(inp)
-    b = gpu_prefill(inp)
+    a = run_method(inp, method)
+    b = run_method(inp, method)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_prefill_empty_and_no_state():
+@pytest.mark.parametrize("method", [SINGLE, TWO])
+def test_prefill_empty_and_no_state(method):
     """All sequences empty: S_T = S0; S0 = None means zeros."""
-    log("prefill empty sequences")
+    log(f"prefill empty sequences method={method}")
     w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=3, heads=2)
     inp = generate(w, seed=9, device=DEV, lengths=[0, 0, 0])
-    o, ST = gpu_prefill(inp)
+    o, ST = run_method(inp, method)
     assert torch.equal(ST, inp["S0"])
     inp2 = generate(w, seed=10, device=DEV, lengths=[20, 0, 64])
     inp2["S0"] = None
-    o2, ST2 = gpu_prefill(inp2)
+    o2, ST2 = run_method(inp2, method)
     check_all(inp2, o2, ST2, 2e-2, "S0=None")
 
 
@@ -160,12 +209,13 @@ def _sampled(inp, o, ST, units, tol):
     assert worst_o <= tol and worst_s <= tol
 
 
-def test_prefill_kda_b2_h32_t32768_sampled():
+@pytest.mark.parametrize("method", [SINGLE, TWO])
+def test_prefill_kda_b2_h32_t32768_sampled(method):
     """B=2, H=32, T=32768, log_a clipped at -8: whole batch on the GPU, 4 units
-    checked against the oracle."""
-    log("prefill C3 full: KDA B=2 H=32 T=32768")
+    checked against the oracle (the two-pass run is the benchmark's launch)."""
+    log(f"prefill C3 full: KDA B=2 H=32 T=32768 method={method}")
     inp = generate(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seed=3, device=DEV)
-    o, ST = gpu_prefill(inp)
+    o, ST = run_method(inp, method)
     _sampled(inp, o, ST, [(0, 0), (0, 31), (1, 7), (1, 20)], 2e-2)
 
 
