@@ -19,9 +19,11 @@
 //   KC = (K e^{g_C - g_{t-1}})^T,  KT = (diag(b) K e^{g_C - g_t})^T,  GAM = e^{g_C}
 // where Kb, Qb in W and QP are referenced to the chunk start (factors <= 1).
 //
-// One workgroup (4 wavefronts) per chunk.  Phases, separated by LDS barriers:
-//   1 load, decay sums per 4-token group        2 factors, gated operands, KC/KT/GAM out
-//   3 Gram products                             4 wavefront 0: (I + A)^-1 diag(b)
+// Persistent workgroups of 8 wavefronts, each walking a strided list of
+// chunks; the next chunk's inputs are loaded while the current one is in
+// phases 3-6.  Phases, separated by LDS barriers:
+//   1 decay sums per 4-token group              2 factors, gated operands, KC/KT/GAM out
+//   3 Gram products                             4 (I + A)^-1 diag(b) (C = 32: two wavefronts)
 //   5 W, M1 (to the block and, transposed, to LDS)   6 QP, M2 out
 #include "kda_chunk_common.hpp"
 #include "kda_launch.hpp"
@@ -31,7 +33,7 @@ namespace kda {
 
 template <int DK, int C>
 struct PrepCfg {
-    static constexpr int NT = 256, NW = NT / WAVE;
+    static constexpr int NT = 512, NW = NT / WAVE;
     static constexpr int NB = C / 16;
     static constexpr int NPAIR = NB * (NB - 1) / 2;
     static constexpr int NBP = NB * (NB + 1) / 2;
@@ -40,32 +42,40 @@ struct PrepCfg {
     static constexpr int LDA = C + 4;   // fp32 rows over tokens
     static constexpr int NCP = DK / 2;
     static constexpr int NU = NCP * (C / 4);
-    static constexpr int UPT = (NU + NT - 1) / NT;
+    static_assert(NU <= NT, "one 4-token x 2-channel unit per thread");
+    static constexpr bool SPLIT_SOLVE = (C == 32);  // two wavefronts invert the diagonal blocks
 };
 
 template <int DK, int C>
 struct PrepLds {
     typedef PrepCfg<DK, C> G;
     union {
-        struct {  // Gram operands (mid-point references), dead after phase 3
+        struct {  // phases 2-3: Gram operands (mid-point references)
             bf16 Kr[C * G::LDK], Qr[C * G::LDK], Kce[C * G::LDK], Kci[C * G::LDK];
         } g;
-        struct {  // phase 5 results read in phase 6
+        struct {  // phase 4: the solve's working set
+            float Tf[C * G::LDA];       // (I + A)^-1, fp32, unscaled (split solve)
+            float Xs[16 * 17];          // one 16 x 16 product, fp32
+            float X[2 * G::NB * 256];   // panel exchange
+        } v;
+        struct {  // phases 5-6
             bf16 WT[DK * G::LDC];  // W^T  [channel][token]
             bf16 M1T[C * G::LDC];  // M1^T [i][t]
         } w;
     } u;
+    union {
+        float grp[(C / 4) * DK];   // phases 1-2: summed log2 decay per 4-token group
+        float A[C * G::LDA];       // phases 3-4: diag(b) strict_lower(Kb Kc^T)
+    } u2;
     alignas(16) bf16 KbT[DK * G::LDC];  // (K e^{g_{t-1}})^T [channel][token]
     alignas(16) bf16 Qb[C * G::LDK];    // Q e^{g_t} [token][channel]
     alignas(16) bf16 LbT[C * G::LDC];   // (L diag(b))^T [i][t]
     alignas(16) bf16 P1[C * G::LDC];    // [t][i]
     alignas(16) bf16 Tb[C * G::LDC];    // (I + A)^-1 diag(b) [t][s]
-    alignas(16) float A[C * G::LDA];    // diag(b) strict_lower(Kb Kc^T)
     alignas(16) float P2[C * G::LDA];   // P2 diag(b) [t][i]
-    alignas(16) float X[2 * G::NB * 256];
-    alignas(16) float grp[(C / 4) * DK];
     alignas(16) float F[(G::NPAIR > 0 ? G::NPAIR : 1) * DK];
     alignas(16) float beta[C];
+    alignas(16) float ones[16];  // unit column scale of the split solve (outside the unions)
 };
 
 struct PrepParams {
@@ -78,11 +88,101 @@ struct PrepParams {
     uint8_t* ws;      // operator blocks [unit][m]
     int H;
     int m;            // chunks per unit in this segment (block stride)
+    int items;        // units * m
     int64_t chunk0;   // first chunk index of the segment
 };
 
+// Raw inputs of one chunk for one thread: its 4-token x 2-channel unit, and
+// beta of token `tid` (threads below C).
+struct PrepIn {
+    Vec2<bf16>::type q[4], k[4];
+    f32x2 la[4];
+    float b;
+};
+
 template <int DK, int C, bool SCALAR>
-__global__ void __launch_bounds__(256) kda_prep_kernel(PrepParams p) {
+__device__ __forceinline__ bool prep_locate(const PrepParams& p, int item, int64_t& t0, int& Lc, int& h) {
+    const int unit = item / p.m, j = item % p.m;
+    const int n = unit / p.H;
+    h = unit % p.H;
+    int64_t tb, te;
+    if (p.cu) { tb = p.cu[n]; te = p.cu[n + 1]; }
+    else { tb = (int64_t)n * p.eq_len; te = tb + p.eq_len; }
+    t0 = tb + (p.chunk0 + j) * C;
+    Lc = (int)((te - t0) < C ? (te - t0) : C);
+    return t0 < te;
+}
+
+template <int DK, int C, bool SCALAR>
+__device__ __forceinline__ void prep_load(const PrepParams& p, int64_t t0, int Lc, int h, int tid, int c, int tg,
+                                          PrepIn& in) {
+    typedef Vec2<bf16>::type b2;
+    const bf16* __restrict__ gq = static_cast<const bf16*>(p.q);
+    const bf16* __restrict__ gk = static_cast<const bf16*>(p.k);
+    const int H = p.H;
+    const int64_t r0 = t0 * H + h;
+    if (tid < PrepCfg<DK, C>::NU) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // rows past the chunk's end repeat its last row; b and log a are masked there
+            const int64_t row = r0 + (int64_t)min(4 * tg + i, Lc - 1) * H;
+            in.q[i] = *reinterpret_cast<const b2*>(gq + row * DK + c);
+            in.k[i] = *reinterpret_cast<const b2*>(gk + row * DK + c);
+            if (SCALAR) { const float x = p.log_a[row]; in.la[i] = f32x2{x, x}; }
+            else in.la[i] = *reinterpret_cast<const f32x2*>(p.log_a + row * DK + c);
+        }
+    }
+    in.b = (tid < Lc) ? p.beta[r0 + (int64_t)tid * H] : 0.f;
+}
+
+// Unit-lower (I + A)^-1 diag(b) for C = 32 on two wavefronts: each inverts one
+// 16 x 16 diagonal block (fp32), then wavefront 0 forms the off-diagonal block
+// T21 = -T22 A21 T11 with two fp32 matrix-core products.  Ends with Tb written.
+template <int DK, int C>
+__device__ __forceinline__ void split_solve(PrepLds<DK, C>& s, int wv, int lane, int tid) {
+    typedef PrepCfg<DK, C> G;
+    constexpr int LDA = G::LDA, LDC = G::LDC;
+    const int l16 = lane & 15, lg = lane >> 4;
+    if (wv < 2)
+        block_inverse<float, 16, LDA, LDA>(s.u2.A + 16 * wv * LDA + 16 * wv, s.ones, s.u.v.X + wv * 512,
+                                           s.u.v.Tf + 16 * wv * LDA + 16 * wv, lane);
+    lds_barrier();
+    if (wv == 0) {
+        // X = A21 T11 (rows i of block 1, columns n of block 0)
+        f32x4 x = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kk = 4 * ks + lg;
+            const float a = s.u2.A[(16 + l16) * LDA + kk];
+            const float b = s.u.v.Tf[kk * LDA + l16];
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s.u.v.Xs[(4 * lg + r) * 17 + l16] = x[r];
+        wave_sync();
+        // T21 = -T22 X
+        f32x4 t = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kk = 4 * ks + lg;
+            const float a = s.u.v.Tf[(16 + l16) * LDA + 16 + kk];
+            const float b = s.u.v.Xs[kk * 17 + l16];
+            t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t, 0, 0, 0);
+        }
+        const float bn = s.beta[l16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s.Tb[(16 + 4 * lg + r) * LDC + l16] = (bf16)(-t[r] * bn);
+    }
+    // diagonal blocks
+    for (int e = tid; e < 512; e += G::NT) {
+        const int w = e >> 8, i = (e >> 4) & 15, jj = e & 15;
+        const int row = 16 * w + i, col = 16 * w + jj;
+        s.Tb[row * LDC + col] = (bf16)(s.u.v.Tf[row * LDA + col] * s.beta[col]);
+    }
+}
+
+template <int DK, int C, bool SCALAR>
+__global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
     typedef PrepCfg<DK, C> G;
     typedef WsBlock<DK, C> WS;
     typedef Mma<bf16> M;
@@ -91,69 +191,52 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(PrepParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int lrow = lane & 15, lgrp = lane >> 4;
-    const int H = p.H;
-    const int item = blockIdx.x;
-    const int unit = item / p.m, j = item % p.m;
-    const int n = unit / H, h = unit % H;
-    int64_t tb, te;
-    if (p.cu) { tb = p.cu[n]; te = p.cu[n + 1]; }
-    else { tb = (int64_t)n * p.eq_len; te = tb + p.eq_len; }
-    const int64_t t0 = tb + (p.chunk0 + j) * C;
-    if (t0 >= te) return;  // the whole workgroup leaves together
-    const int Lc = (int)((te - t0) < C ? (te - t0) : C);
-    uint8_t* __restrict__ blk = p.ws + (size_t)item * WS::BYTES;
-    const bf16* __restrict__ gq = static_cast<const bf16*>(p.q);
-    const bf16* __restrict__ gk = static_cast<const bf16*>(p.k);
+    int c = 0, tg = 0;
+    if (tid < G::NU) unit_of<G::NCP>(tid, c, tg);
 
-    // upper blocks of the masked products are never written
+    // upper blocks of the masked products are never written: zero them once
     for (int e = tid; e < C * LDC; e += NT) {
         s.LbT[e] = (bf16)0.f; s.P1[e] = (bf16)0.f; s.Tb[e] = (bf16)0.f;
     }
     for (int e = tid; e < C * LDA; e += NT) s.P2[e] = 0.f;
+    if (tid < 16) s.ones[tid] = 1.f;
 
-    // ---- 1: inputs (rows past the chunk's end repeat its last row; b and log a are
-    //      masked there), decay sums per 4-token group in the log2 domain ----------
-    typedef Vec2<bf16>::type b2;
-    b2 qv[G::UPT][4], kv[G::UPT][4];
-    f32x2 lam[G::UPT][4];
-    const int64_t r0 = t0 * H + h;
-#pragma unroll
-    for (int u = 0; u < G::UPT; ++u) {
-        const int uu = tid + NT * u;
-        if (uu < G::NU) {
-            int c, tg;
-            unit_of<G::NCP>(uu, c, tg);
+    // this workgroup's chunks: item = blockIdx.x + k gridDim.x, empty ones skipped
+    auto next_item = [&](int it, int64_t& t0, int& Lc, int& h) {
+        while (it < p.items && !prep_locate<DK, C, SCALAR>(p, it, t0, Lc, h)) it += gridDim.x;
+        return it;
+    };
+    int64_t t0 = 0;
+    int Lc = 0, h = 0;
+    int item = next_item(blockIdx.x, t0, Lc, h);
+    PrepIn in;
+    if (item < p.items) prep_load<DK, C, SCALAR>(p, t0, Lc, h, tid, c, tg, in);
+
+    while (item < p.items) {
+        uint8_t* __restrict__ blk = p.ws + (size_t)item * WS::BYTES;
+
+        // ---- 1: decay sums per 4-token group in the log2 domain ------------------
+        f32x2 lam[4];
+        if (tid < G::NU) {
             f32x2 run = f32x2{0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t row = r0 + (int64_t)min(4 * tg + i, Lc - 1) * H;
-                qv[u][i] = *reinterpret_cast<const b2*>(gq + row * DK + c);
-                kv[u][i] = *reinterpret_cast<const b2*>(gk + row * DK + c);
-                f32x2 la;
-                if (SCALAR) { const float x = p.log_a[row]; la = f32x2{x, x}; }
-                else la = *reinterpret_cast<const f32x2*>(p.log_a + row * DK + c);
-                run += (4 * tg + i < Lc) ? la * LOG2E : f32x2{0.f, 0.f};
-                lam[u][i] = run;
+                run += (4 * tg + i < Lc) ? in.la[i] * LOG2E : f32x2{0.f, 0.f};
+                lam[i] = run;
             }
-            *reinterpret_cast<f32x2*>(&s.grp[tg * DK + c]) = run;
+            *reinterpret_cast<f32x2*>(&s.u2.grp[tg * DK + c]) = run;
         }
-    }
-    for (int t = tid; t < C; t += NT) s.beta[t] = t < Lc ? p.beta[r0 + (int64_t)t * H] : 0.f;
-    lds_barrier();
+        if (tid < C) s.beta[tid] = in.b;
+        lds_barrier();
 
-    // ---- 2: factors (exponents clamped to the fp32 range) and gated operands -------
-    //   rin = e^{g_t - mid}, rex = e^{g_{t-1} - mid}, em = e^{mu_b}, ec = e^{g_C - mu_b}
-#pragma unroll
-    for (int u = 0; u < G::UPT; ++u) {
-        const int uu = tid + NT * u;
-        if (uu < G::NU) {
-            int c, tg;
-            unit_of<G::NCP>(uu, c, tg);
+        // ---- 2: factors (exponents clamped to the fp32 range) and gated operands ---
+        //   rin = e^{g_t - mid}, rex = e^{g_{t-1} - mid}, em = e^{mu_b}, ec = e^{g_C - mu_b}
+        if (tid < G::NU) {
             const int b = tg / 4, gib = tg % 4;
             f32x2 off = {0.f, 0.f}, rho = {0.f, 0.f}, tot = {0.f, 0.f}, mid = {0.f, 0.f};
 #pragma unroll
             for (int g = 0; g < C / 4; ++g) {
-                const f32x2 x = *reinterpret_cast<const f32x2*>(&s.grp[g * DK + c]);
+                const f32x2 x = *reinterpret_cast<const f32x2*>(&s.u2.grp[g * DK + c]);
                 tot += x;
                 if (g < 4 * b) rho += x;
                 if (g >= 4 * b && g < 4 * b + gib) off += x;
@@ -175,11 +258,11 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     ri[e] = __builtin_amdgcn_exp2f(
-                        __builtin_amdgcn_fmed3f(off[e] + lam[u][i][e] - mid[e], -126.f, 126.f));
+                        __builtin_amdgcn_fmed3f(off[e] + lam[i][e] - mid[e], -126.f, 126.f));
                     ci[e] = __builtin_amdgcn_rcpf(ri[e]);
                 }
-                const f32x2 k = f32x2{Vec2<bf16>::lo(kv[u][i]), Vec2<bf16>::hi(kv[u][i])};
-                const f32x2 q = f32x2{Vec2<bf16>::lo(qv[u][i]), Vec2<bf16>::hi(qv[u][i])};
+                const f32x2 k = f32x2{Vec2<bf16>::lo(in.k[i]), Vec2<bf16>::hi(in.k[i])};
+                const f32x2 q = f32x2{Vec2<bf16>::lo(in.q[i]), Vec2<bf16>::hi(in.q[i])};
                 const f32x2 kr = k * prev, qr = q * ri, kce = k * prevc, kci = k * ci;
                 store2(&s.u.g.Kr[t * LDK + c], kr[0], kr[1]);
                 store2(&s.u.g.Qr[t * LDK + c], qr[0], qr[1]);
@@ -202,127 +285,140 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(PrepParams p) {
                        f32x4{kt[0][e], kt[1][e], kt[2][e], kt[3][e]});
             }
         }
-    }
-    // per (sub-block, channel): e^{mu_bt - mu_bi} for block pairs; e^{g_C} to the block
-    for (int e = tid; e < NB * DK; e += NT) {
-        const int b = e / DK, c = e % DK;
-        float rho[NB + 1], mu[NB];
-        rho[0] = 0.f;
+        // per (sub-block, channel): e^{mu_bt - mu_bi} for block pairs; e^{g_C} to the block
+        for (int e = tid; e < NB * DK; e += NT) {
+            const int b = e / DK, ch = e % DK;
+            float rho[NB + 1], mu[NB];
+            rho[0] = 0.f;
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-            const float g0 = s.grp[(4 * bb) * DK + c], g1 = s.grp[(4 * bb + 1) * DK + c];
-            const float g2 = s.grp[(4 * bb + 2) * DK + c], g3 = s.grp[(4 * bb + 3) * DK + c];
-            mu[bb] = rho[bb] + g0 + g1;
-            rho[bb + 1] = rho[bb] + ((g0 + g1) + (g2 + g3));
+            for (int bb = 0; bb < NB; ++bb) {
+                const float g0 = s.u2.grp[(4 * bb) * DK + ch], g1 = s.u2.grp[(4 * bb + 1) * DK + ch];
+                const float g2 = s.u2.grp[(4 * bb + 2) * DK + ch], g3 = s.u2.grp[(4 * bb + 3) * DK + ch];
+                mu[bb] = rho[bb] + g0 + g1;
+                rho[bb + 1] = rho[bb] + ((g0 + g1) + (g2 + g3));
+            }
+            if (b == 0) reinterpret_cast<float*>(blk + WS::GAM)[ch] = exp2f(rho[NB]);
+            for (int bi = 0; bi < b; ++bi) s.F[(b * (b - 1) / 2 + bi) * DK + ch] = exp2f(mu[b] - mu[bi]);
         }
-        if (b == 0) reinterpret_cast<float*>(blk + WS::GAM)[c] = exp2f(rho[NB]);
-        for (int bi = 0; bi < b; ++bi) s.F[(b * (b - 1) / 2 + bi) * DK + c] = exp2f(mu[b] - mu[bi]);
-    }
-    lds_barrier();
+        lds_barrier();
 
-    // ---- 3: Gram products; tile w is product w % 4 (0 A, 1 L, 2 P1, 3 P2) of block
-    //      pair w / 4.  A, P1, P2 land row-major [t][i], L transposed [i][t] --------
-    for (int w = wv; w < 4 * G::NBP; w += NW) {
-        const int g = w % 4, pr = w / 4;
-        int bt = 0;
-        while ((bt + 1) * (bt + 2) / 2 <= pr) ++bt;
-        const int bi = pr - bt * (bt + 1) / 2;
-        const bf16* rows = (g < 2 ? s.u.g.Kr : s.u.g.Qr) + (16 * bt + lrow) * LDK;
-        const bf16* cols = ((g & 1) == 0 ? s.u.g.Kce : s.u.g.Kci) + (16 * bi + lrow) * LDK;
-        constexpr int NK = DK / M::K;
-        M::frag fr[NK], fc[NK];
+        // next chunk's inputs: in flight during phases 3-6
+        int64_t nt0 = 0;
+        int nLc = 0, nh = 0;
+        const int nitem = next_item(item + gridDim.x, nt0, nLc, nh);
+        if (nitem < p.items) prep_load<DK, C, SCALAR>(p, nt0, nLc, nh, tid, c, tg, in);
+
+        // ---- 3: Gram products; tile w is product w % 4 (0 A, 1 L, 2 P1, 3 P2) of block
+        //      pair w / 4.  A, P1, P2 land row-major [t][i], L transposed [i][t] ------
+        for (int w = wv; w < 4 * G::NBP; w += NW) {
+            const int g = w % 4, pr = w / 4;
+            int bt = 0;
+            while ((bt + 1) * (bt + 2) / 2 <= pr) ++bt;
+            const int bi = pr - bt * (bt + 1) / 2;
+            const bf16* rows = (g < 2 ? s.u.g.Kr : s.u.g.Qr) + (16 * bt + lrow) * LDK;
+            const bf16* cols = ((g & 1) == 0 ? s.u.g.Kce : s.u.g.Kci) + (16 * bi + lrow) * LDK;
+            constexpr int NK = DK / M::K;
+            M::frag fr[NK], fc[NK];
 #pragma unroll
-        for (int k = 0; k < NK; ++k) {
-            fr[k] = M::loadr(rows + k * M::K, lane);
-            fc[k] = M::loadr(cols + k * M::K, lane);
+            for (int k = 0; k < NK; ++k) {
+                fr[k] = M::loadr(rows + k * M::K, lane);
+                fc[k] = M::loadr(cols + k * M::K, lane);
+            }
+            if (bt != bi) {
+                const float* F = s.F + (bt * (bt - 1) / 2 + bi) * DK + lgrp * M::KPL;
+#pragma unroll
+                for (int k = 0; k < NK; ++k) fr[k] = M::scale(fr[k], F + k * M::K);
+            }
+            f32x4 acc = zero4();
+            if (g == 1) {
+#pragma unroll
+                for (int k = 0; k < NK; ++k) acc = M::mma(fr[k], fc[k], acc);
+                // rows t = 16 bt + 4 lgrp + r, column i = 16 bi + lrow
+                const int i = 16 * bi + lrow, tt = 16 * bt + 4 * lgrp;
+                const float bi_ = s.beta[i];
+                f32x4 m;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[r] = (i < tt + r) ? acc[r] * bi_ : 0.f;
+                store4(&s.LbT[i * LDC + tt], m);
+            } else {
+#pragma unroll
+                for (int k = 0; k < NK; ++k) acc = M::mma(fc[k], fr[k], acc);
+                // column t = 16 bt + lrow, rows i = 16 bi + 4 lgrp + r
+                const int t = 16 * bt + lrow, i0 = 16 * bi + 4 * lgrp;
+                f32x4 m;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[r] = (g == 0 ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f;
+                if (g == 0) *reinterpret_cast<f32x4*>(&s.u2.A[t * LDA + i0]) = s.beta[t] * m;
+                else if (g == 2) store4(&s.P1[t * LDC + i0], m);
+                else *reinterpret_cast<f32x4*>(&s.P2[t * LDA + i0]) =
+                         m * *reinterpret_cast<const f32x4*>(&s.beta[i0]);
+            }
         }
-        if (bt != bi) {
-            const float* F = s.F + (bt * (bt - 1) / 2 + bi) * DK + lgrp * M::KPL;
-#pragma unroll
-            for (int k = 0; k < NK; ++k) fr[k] = M::scale(fr[k], F + k * M::K);
-        }
-        f32x4 acc = zero4();
-        if (g == 1) {
-#pragma unroll
-            for (int k = 0; k < NK; ++k) acc = M::mma(fr[k], fc[k], acc);
-            // rows t = 16 bt + 4 lgrp + r, column i = 16 bi + lrow
-            const int i = 16 * bi + lrow, tt = 16 * bt + 4 * lgrp;
-            const float bi_ = s.beta[i];
-            f32x4 m;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) m[r] = (i < tt + r) ? acc[r] * bi_ : 0.f;
-            store4(&s.LbT[i * LDC + tt], m);
+        lds_barrier();
+
+        // ---- 4: Tb = (I + A)^-1 diag(b) ---------------------------------------------
+        if constexpr (G::SPLIT_SOLVE) {
+            split_solve<DK, C>(s, wv, lane, tid);
         } else {
-#pragma unroll
-            for (int k = 0; k < NK; ++k) acc = M::mma(fc[k], fr[k], acc);
-            // column t = 16 bt + lrow, rows i = 16 bi + 4 lgrp + r
-            const int t = 16 * bt + lrow, i0 = 16 * bi + 4 * lgrp;
-            f32x4 m;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) m[r] = (g == 0 ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f;
-            if (g == 0) *reinterpret_cast<f32x4*>(&s.A[t * LDA + i0]) = s.beta[t] * m;
-            else if (g == 2) store4(&s.P1[t * LDC + i0], m);
-            else *reinterpret_cast<f32x4*>(&s.P2[t * LDA + i0]) =
-                     m * *reinterpret_cast<const f32x4*>(&s.beta[i0]);
+            if (wv == 0) block_inverse<bf16, C, LDA, LDC>(s.u2.A, s.beta, s.u.v.X, s.Tb, lane);
         }
-    }
-    lds_barrier();
+        lds_barrier();
 
-    // ---- 4: Tb = (I + A)^-1 diag(b) ----------------------------------------------
-    if (wv == 0) block_inverse<bf16, C, LDA, LDC>(s.A, s.beta, s.X, s.Tb, lane);
-    lds_barrier();
-
-    // ---- 5: W = Tb Kb and M1 = Tb L diag(b).  Each tile is formed in both
-    //      orientations from the same fragments: W^T (rows: channels) goes to the
-    //      block, W (rows: tokens) to LDS as [channel][token] for phase 6 ----------
-    constexpr int NWT = (DK / 16) * (C / 16), NMT = (C / 16) * (C / 16);
-    for (int w = wv; w < NWT + NMT; w += NW) {
-        const bool isw = w < NWT;
-        const int x = isw ? w : w - NWT;
-        const int ra = x / (C / 16), tt = x % (C / 16);  // row tile of KbT (or LbT), token tile
-        const bf16* pa = (isw ? s.KbT : s.LbT) + (16 * ra + lrow) * LDC;
-        const bf16* pb = s.Tb + (16 * tt + lrow) * LDC;
-        constexpr int NK = C / M::K;
-        M::frag fa[NK], fb[NK];
+        // ---- 5: W = Tb Kb and M1 = Tb L diag(b).  Each tile is formed in both
+        //      orientations from the same fragments: W^T (rows: channels) goes to the
+        //      block, W (rows: tokens) to LDS as [channel][token] for phase 6 --------
+        constexpr int NWT = (DK / 16) * (C / 16), NMT = (C / 16) * (C / 16);
+        for (int w = wv; w < NWT + NMT; w += NW) {
+            const bool isw = w < NWT;
+            const int x = isw ? w : w - NWT;
+            const int ra = x / (C / 16), tt = x % (C / 16);  // row tile of KbT (or LbT), token tile
+            const bf16* pa = (isw ? s.KbT : s.LbT) + (16 * ra + lrow) * LDC;
+            const bf16* pb = s.Tb + (16 * tt + lrow) * LDC;
+            constexpr int NK = C / M::K;
+            M::frag fa[NK], fb[NK];
 #pragma unroll
-        for (int k = 0; k < NK; ++k) {
-            fa[k] = M::loadr(pa + k * M::K, lane);
-            fb[k] = M::loadr(pb + k * M::K, lane);
-        }
-        f32x4 xt = zero4(), xn = zero4();
+            for (int k = 0; k < NK; ++k) {
+                fa[k] = M::loadr(pa + k * M::K, lane);
+                fb[k] = M::loadr(pb + k * M::K, lane);
+            }
+            f32x4 xt = zero4(), xn = zero4();
 #pragma unroll
-        for (int k = 0; k < NK; ++k) {
-            xt = M::mma(fa[k], fb[k], xt);  // rows: channel (or i), column: token t
-            xn = M::mma(fb[k], fa[k], xn);  // rows: token t, column: channel (or i)
+            for (int k = 0; k < NK; ++k) {
+                xt = M::mma(fa[k], fb[k], xt);  // rows: channel (or i), column: token t
+                xn = M::mma(fb[k], fa[k], xn);  // rows: token t, column: channel (or i)
+            }
+            const int t = 16 * tt + lrow, a0 = 16 * ra + 4 * lgrp;
+            const int an = 16 * ra + lrow, t0n = 16 * tt + 4 * lgrp;
+            if (isw) {
+                store4(reinterpret_cast<bf16*>(blk + WS::W + swz_elem<2 * DK>(t, kperm(a0))), xt);
+                store4(&s.u.w.WT[an * LDC + t0n], xn);
+            } else {
+                store4(reinterpret_cast<bf16*>(blk + WS::M1 + swz_elem<2 * C>(t, kperm(a0))), xt);
+                store4(&s.u.w.M1T[an * LDC + t0n], xn);
+            }
         }
-        const int t = 16 * tt + lrow, a0 = 16 * ra + 4 * lgrp;
-        const int an = 16 * ra + lrow, t0n = 16 * tt + 4 * lgrp;
-        if (isw) {
-            store4(reinterpret_cast<bf16*>(blk + WS::W + swz_elem<2 * DK>(t, kperm(a0))), xt);
-            store4(&s.u.w.WT[an * LDC + t0n], xn);
-        } else {
-            store4(reinterpret_cast<bf16*>(blk + WS::M1 + swz_elem<2 * C>(t, kperm(a0))), xt);
-            store4(&s.u.w.M1T[an * LDC + t0n], xn);
-        }
-    }
-    lds_barrier();
+        lds_barrier();
 
-    // ---- 6: QP = Qb - P1 W and M2 = P2 diag(b) - P1 M1, as their transposes -------
-    for (int w = wv; w < NWT + NMT; w += NW) {
-        const bool isq = w < NWT;
-        const int x = isq ? w : w - NWT;
-        const int ra = x / (C / 16), tt = x % (C / 16);
-        const bf16* pa = (isq ? s.u.w.WT : s.u.w.M1T) + (16 * ra + lrow) * LDC;
-        const bf16* pb = s.P1 + (16 * tt + lrow) * LDC;
-        const f32x4 pw = tile_mma_r<bf16, C>(pa, pb, zero4(), lane);
-        const int t = 16 * tt + lrow, a0 = 16 * ra + 4 * lgrp;
-        if (isq) {
-            const f32x4 qb = load4(&s.Qb[t * LDK + a0]);
-            store4(reinterpret_cast<bf16*>(blk + WS::QP + swz_elem<2 * DK>(t, kperm(a0))), qb - pw);
-        } else {
-            const f32x4 p2 = *reinterpret_cast<const f32x4*>(&s.P2[t * LDA + a0]);
-            store4(reinterpret_cast<bf16*>(blk + WS::M2 + swz_elem<2 * C>(t, kperm(a0))), p2 - pw);
+        // ---- 6: QP = Qb - P1 W and M2 = P2 diag(b) - P1 M1, as their transposes -----
+        for (int w = wv; w < NWT + NMT; w += NW) {
+            const bool isq = w < NWT;
+            const int x = isq ? w : w - NWT;
+            const int ra = x / (C / 16), tt = x % (C / 16);
+            const bf16* pa = (isq ? s.u.w.WT : s.u.w.M1T) + (16 * ra + lrow) * LDC;
+            const bf16* pb = s.P1 + (16 * tt + lrow) * LDC;
+            const f32x4 pw = tile_mma_r<bf16, C>(pa, pb, zero4(), lane);
+            const int t = 16 * tt + lrow, a0 = 16 * ra + 4 * lgrp;
+            if (isq) {
+                const f32x4 qb = load4(&s.Qb[t * LDK + a0]);
+                store4(reinterpret_cast<bf16*>(blk + WS::QP + swz_elem<2 * DK>(t, kperm(a0))), qb - pw);
+            } else {
+                const f32x4 p2 = *reinterpret_cast<const f32x4*>(&s.P2[t * LDA + a0]);
+                store4(reinterpret_cast<bf16*>(blk + WS::M2 + swz_elem<2 * C>(t, kperm(a0))), p2 - pw);
+            }
         }
+        lds_barrier();  // LDS of this chunk is reused by the next
+
+        item = nitem; t0 = nt0; Lc = nLc; h = nh;
     }
 }
 
@@ -333,7 +429,15 @@ static hipError_t prep_cfg(const PrepLaunch& a, hipStream_t stream) {
     p.q = a.q; p.k = a.k; p.log_a = a.log_a; p.beta = a.beta; p.cu = a.cu_seqlens;
     p.eq_len = a.eq_len; p.ws = static_cast<uint8_t*>(a.ws); p.H = a.num_heads; p.m = a.m;
     p.chunk0 = a.chunk0;
-    const int64_t blocks = (int64_t)a.units * a.m;
+    p.items = (int)(a.units * a.m);
+    // persistent workgroups: as many as fit at once (two per compute unit when the
+    // LDS image allows), each walking items blockIdx.x, + gridDim.x, ...
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int per_cu = sizeof(PrepLds<DK, C>) <= 80 * 1024 ? 2 : 1;
+    int64_t blocks = (int64_t)cus * per_cu;
+    if (blocks > p.items) blocks = p.items;
+    if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL((kda_prep_kernel<DK, C, SC>), dim3((unsigned)blocks), dim3(PrepCfg<DK, C>::NT), 0,
                        stream, p);
     return hipGetLastError();

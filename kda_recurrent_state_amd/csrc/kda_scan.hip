@@ -15,10 +15,10 @@
 // accumulator tiles of S and E are fed straight back as bf16 operands (the
 // block layout's permuted contraction order makes that a register move).
 //
-// Workgroup: NS compute wavefronts (the slice's column blocks) plus two loader
-// wavefronts that copy the next chunk's operator block and value tile into
-// the other half of a double buffer in LDS while the current chunk is being
-// applied.  One barrier per chunk.  Slices of one (sequence, head) are placed
+// Workgroup: NS compute wavefronts (the slice's column blocks) plus four loader
+// wavefronts that keep the operator blocks and value tiles of the next three
+// chunks in flight and copy the next one into the other half of a double
+// buffer in LDS while the current chunk is being applied.  One barrier per chunk.  Slices of one (sequence, head) are placed
 // on one XCD so that they read each operator block through the same L2.
 #include "kda_device.hpp"
 #include "kda_chunk_common.hpp"
@@ -32,7 +32,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 template <int DK, int DVS, int C>
 struct ScanCfg {
     static constexpr int NS = DVS / 16;         // compute wavefronts
-    static constexpr int NL = 2;                // loader wavefronts
+    static constexpr int NL = 4;                // loader wavefronts
+    static constexpr int PD = 3;                // chunks in flight in the loaders' registers
     static constexpr int NT = WAVE * (NS + NL);
     static constexpr int LT = WAVE * NL;        // loader threads
     static constexpr int BYTES = WsBlock<DK, C>::BYTES;
@@ -53,6 +54,60 @@ struct ScanParams {
     float* S_out;
     int H, DV, split, m, xcd_group;
     int64_t chunk0;
+};
+
+// Register-staged copy of operator blocks and value tiles into LDS.
+template <int DK, int DVS, int C>
+struct ScanLoader {
+    typedef ScanCfg<DK, DVS, C> G;
+    i32x4 pc[G::PD][G::LPT];
+    bf16x8 vv[G::PD][G::VPT];
+    int ltid, H, DV, dv0, h;
+    const uint8_t* src;
+    const bf16* gv;
+    int64_t tb, te, chunk0;
+
+    // Every thread issues the same number of loads on every path (indices past the
+    // end are clamped to a valid piece or chunk and their data is never stored),
+    // so the compiler can wait for exactly the oldest register set.
+    template <int S>
+    __device__ __forceinline__ void fetch(int jj, int nch) {
+        jj = min(jj, nch - 1);
+        const i32x4* b = reinterpret_cast<const i32x4*>(src + (size_t)jj * G::BYTES);
+#pragma unroll
+        for (int i = 0; i < G::LPT; ++i) pc[S][i] = b[min(ltid + G::LT * i, G::NPC - 1)];
+        const int64_t t0 = tb + (chunk0 + jj) * C;
+        const int Lc = (int)((te - t0) < C ? (te - t0) : C);
+#pragma unroll
+        for (int i = 0; i < G::VPT; ++i) {
+            const int idx = (ltid + G::LT * i) % G::NVP;
+            const int t = idx / (DVS / 8), j0 = 8 * (idx % (DVS / 8));
+            // rows past the chunk's end repeat its last row: they meet zero operator columns
+            const int64_t row = (t0 + min(t, Lc - 1)) * H + h;
+            vv[S][i] = *reinterpret_cast<const bf16x8*>(gv + row * DV + dv0 + j0);
+        }
+    }
+
+    template <int S>
+    __device__ __forceinline__ void put(int jj, uint8_t* bdst, uint8_t* vdst) {
+        (void)jj;
+        i32x4* dst = reinterpret_cast<i32x4*>(bdst);
+#pragma unroll
+        for (int i = 0; i < G::LPT; ++i) {
+            const int idx = ltid + G::LT * i;
+            if (idx < G::NPC) dst[idx] = pc[S][i];
+        }
+#pragma unroll
+        for (int i = 0; i < G::VPT; ++i) {
+            const int idx = ltid + G::LT * i;
+            if (idx < G::NVP) {
+                const int t = idx / (DVS / 8), j0 = 8 * (idx % (DVS / 8));
+                const int pos = kperm(t);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) *reinterpret_cast<bf16*>(vdst + swz_elem<2 * C>(j0 + e, pos)) = vv[S][i][e];
+            }
+        }
+    }
 };
 
 template <int DK, int DVS, int C>
@@ -84,59 +139,36 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, C>::NT)) kda_scan_kernel(Sca
 
     if (wv >= NS) {
         // ---------------- loader wavefronts ----------------
-        const int ltid = tid - WAVE * NS;
-        const bf16* __restrict__ gv = static_cast<const bf16*>(p.v);
-        i32x4 pc[G::LPT];
-        bf16x8 vv[G::VPT];
-        auto fetch = [&](int jj) {
-            const i32x4* src = reinterpret_cast<const i32x4*>(wsu + (size_t)jj * BYTES);
-#pragma unroll
-            for (int i = 0; i < G::LPT; ++i) {
-                const int idx = ltid + LT * i;
-                if (idx < G::NPC) pc[i] = src[idx];
-            }
-            const int64_t t0 = tb + (p.chunk0 + jj) * C;
-            const int Lc = (int)((te - t0) < C ? (te - t0) : C);
-#pragma unroll
-            for (int i = 0; i < G::VPT; ++i) {
-                const int idx = ltid + LT * i;
-                if (idx < G::NVP) {
-                    const int t = idx / (DVS / 8), j0 = 8 * (idx % (DVS / 8));
-                    // rows past the chunk's end repeat its last row: they meet zero operator columns
-                    const int64_t row = (t0 + min(t, Lc - 1)) * H + h;
-                    vv[i] = *reinterpret_cast<const bf16x8*>(gv + row * DV + dv0 + j0);
-                }
-            }
-        };
-        auto put = [&](int jj) {
-            i32x4* dst = reinterpret_cast<i32x4*>(buf[jj & 1]);
-#pragma unroll
-            for (int i = 0; i < G::LPT; ++i) {
-                const int idx = ltid + LT * i;
-                if (idx < G::NPC) dst[idx] = pc[i];
-            }
-            uint8_t* vd = vt[jj & 1];
-#pragma unroll
-            for (int i = 0; i < G::VPT; ++i) {
-                const int idx = ltid + LT * i;
-                if (idx < G::NVP) {
-                    const int t = idx / (DVS / 8), j0 = 8 * (idx % (DVS / 8));
-                    const int pos = kperm(t);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        *reinterpret_cast<bf16*>(vd + swz_elem<2 * C>(j0 + e, pos)) = vv[i][e];
-                }
-            }
-        };
+        // Chunk c's block is fetched into register set c % PD at step c - PD and
+        // written to LDS buffer c % 2 at step c - 1, so PD - 1 steps of compute
+        // cover its memory latency.  Step i (one per chunk, ending in the
+        // barrier) writes chunk i + 1 and fetches chunk i + PD.
+        ScanLoader<DK, DVS, C> L;
+        L.ltid = tid - WAVE * NS;
+        L.src = wsu; L.gv = static_cast<const bf16*>(p.v);
+        L.tb = tb; L.te = te; L.chunk0 = p.chunk0; L.H = H; L.DV = DV; L.dv0 = dv0; L.h = h;
+        static_assert(G::PD == 3, "the loader loop is unrolled for three register sets");
         if (nch > 0) {
-            fetch(0);
-            put(0);
+            L.template fetch<0>(0, nch);
+            L.template fetch<1>(1, nch);
+            L.template fetch<2>(2, nch);
+            L.template put<0>(0, buf[0], vt[0]);
         }
         lds_barrier();
-        for (int jj = 0; jj < nch; ++jj) {
-            if (jj + 1 < nch) fetch(jj + 1);
-            if (jj + 1 < nch) put(jj + 1);
+        for (int i = 0; i < nch; i += 3) {
+            if (i + 1 < nch) L.template put<1>(i + 1, buf[(i + 1) & 1], vt[(i + 1) & 1]);
+            L.template fetch<0>(i + 3, nch);
             lds_barrier();
+            if (i + 1 < nch) {
+                if (i + 2 < nch) L.template put<2>(i + 2, buf[(i + 2) & 1], vt[(i + 2) & 1]);
+                L.template fetch<1>(i + 4, nch);
+                lds_barrier();
+            }
+            if (i + 2 < nch) {
+                if (i + 3 < nch) L.template put<0>(i + 3, buf[(i + 3) & 1], vt[(i + 3) & 1]);
+                L.template fetch<2>(i + 5, nch);
+                lds_barrier();
+            }
         }
         return;
     }
