@@ -10,16 +10,22 @@
 //   O = QP S + M2 V                      (read after the update, per token)
 //   S <- Diag(GAM) S + KC E + KT V
 // Each column block of S evolves on its own: the operators are shared, the
-// columns never mix.  So one wavefront owns one 16-column block of the state
-// (dk x 16 fp32 in matrix-core accumulators) for the whole walk, and the
+// columns never mix.  One wavefront owns CB column blocks of the state
+// (dk x 16 fp32 each, in matrix-core accumulators) for the whole walk, and the
 // accumulator tiles of S and E are fed straight back as bf16 operands (the
-// block layout's permuted contraction order makes that a register move).
+// block layout's permuted contraction order makes that a register move).  Two
+// column blocks per wavefront let every operator fragment read from LDS serve
+// two products and give the matrix cores two independent chains.
 //
-// Workgroup: NS compute wavefronts (the slice's column blocks) plus four loader
-// wavefronts that keep the operator blocks and value tiles of the next three
-// chunks in flight and copy the next one into the other half of a double
-// buffer in LDS while the current chunk is being applied.  One barrier per chunk.  Slices of one (sequence, head) are placed
-// on one XCD so that they read each operator block through the same L2.
+// Memory path: the operator block and the value tile of a chunk are copied
+// verbatim from global memory into one of three or four LDS slots by the
+// LDS-DMA form of the global load (each lane's 16 bytes land at slot base +
+// 16 * lane, no registers involved).  The copy of chunk j + AHEAD is issued
+// while chunk j is computed; each wavefront waits for its own copies of chunk
+// j + 1 with a vector-memory counter wait, and the workgroup barrier in the
+// middle of chunk j makes them visible to all wavefronts and frees chunk j's
+// slot.  The next chunk's first operands are read right after that barrier,
+// so their LDS latency is hidden behind the state update of chunk j.
 #include "kda_device.hpp"
 #include "kda_chunk_common.hpp"
 #include "kda_launch.hpp"
@@ -27,21 +33,26 @@
 
 namespace kda {
 
-typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-
-template <int DK, int DVS, int C>
+template <int DK, int DVS, int CB>
 struct ScanCfg {
-    static constexpr int NS = DVS / 16;         // compute wavefronts
-    static constexpr int NL = 4;                // loader wavefronts
-    static constexpr int PD = 3;                // chunks in flight in the loaders' registers
-    static constexpr int NT = WAVE * (NS + NL);
-    static constexpr int LT = WAVE * NL;        // loader threads
+    static constexpr int C = 32;
+    static constexpr int NW = DVS / (16 * CB);       // compute wavefronts
+    static constexpr int NL = 2;                     // copy wavefronts
+    static constexpr int NT = WAVE * (NW + NL);
+    static constexpr int LT = WAVE * NL;             // copy threads
     static constexpr int BYTES = WsBlock<DK, C>::BYTES;
-    static constexpr int NPC = BYTES / 16;      // 16-byte pieces per block
-    static constexpr int LPT = (NPC + LT - 1) / LT;
-    static constexpr int VTB = DVS * 2 * C;     // value tile bytes: [column][token]
-    static constexpr int NVP = C * DVS / 8;     // 16-byte value pieces per chunk
-    static constexpr int VPT = (NVP + LT - 1) / LT;
+    static constexpr int NPB = BYTES / 16;           // 16-byte pieces of an operator block
+    static constexpr int VPR = DVS / 8;              // pieces per value row of the slice
+    static constexpr int NPV = C * VPR;              // pieces of a chunk's value tile
+    static constexpr int NPS = NPB + NPV;
+    static constexpr int ROUNDS = (NPS + LT - 1) / LT;  // copy instructions per copy wavefront and chunk
+    static constexpr int SLOT = ROUNDS * LT * 16;    // LDS bytes per slot (copies past NPS land in the pad)
+    // slots: four (copies three chunks ahead) where they fit in LDS and the
+    // counter wait can express them, else three
+    static constexpr int NBUF = (4 * SLOT <= 160 * 1024 && 2 * ROUNDS < 64) ? 4 : 3;
+    static constexpr int AHEAD = NBUF - 1;
+    static_assert(BYTES % 16 == 0, "operator blocks are whole 16-byte pieces");
+    static_assert(NW >= 1 && NW * 16 * CB == DVS, "slice = wavefronts x column blocks x 16");
 };
 
 struct ScanParams {
@@ -56,69 +67,31 @@ struct ScanParams {
     int64_t chunk0;
 };
 
-// Register-staged copy of operator blocks and value tiles into LDS.
-template <int DK, int DVS, int C>
-struct ScanLoader {
-    typedef ScanCfg<DK, DVS, C> G;
-    i32x4 pc[G::PD][G::LPT];
-    bf16x8 vv[G::PD][G::VPT];
-    int ltid, H, DV, dv0, h;
-    const uint8_t* src;
-    const bf16* gv;
-    int64_t tb, te, chunk0;
+// Ends a chunk: waits until at most N vector-memory operations of this
+// wavefront are outstanding and all its LDS reads have returned, then joins the
+// workgroup barrier.  A release fence is not used here: on LDS it would also
+// wait for the copies still in flight into the other slots.  The empty asm
+// statements keep the compiler from moving memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void slot_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // vmcnt(N) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
-    // Every thread issues the same number of loads on every path (indices past the
-    // end are clamped to a valid piece or chunk and their data is never stored),
-    // so the compiler can wait for exactly the oldest register set.
-    template <int S>
-    __device__ __forceinline__ void fetch(int jj, int nch) {
-        jj = min(jj, nch - 1);
-        const i32x4* b = reinterpret_cast<const i32x4*>(src + (size_t)jj * G::BYTES);
-#pragma unroll
-        for (int i = 0; i < G::LPT; ++i) pc[S][i] = b[min(ltid + G::LT * i, G::NPC - 1)];
-        const int64_t t0 = tb + (chunk0 + jj) * C;
-        const int Lc = (int)((te - t0) < C ? (te - t0) : C);
-#pragma unroll
-        for (int i = 0; i < G::VPT; ++i) {
-            const int idx = (ltid + G::LT * i) % G::NVP;
-            const int t = idx / (DVS / 8), j0 = 8 * (idx % (DVS / 8));
-            // rows past the chunk's end repeat its last row: they meet zero operator columns
-            const int64_t row = (t0 + min(t, Lc - 1)) * H + h;
-            vv[S][i] = *reinterpret_cast<const bf16x8*>(gv + row * DV + dv0 + j0);
-        }
-    }
+template <int DK, int DVS, int CB>
+__global__ void __launch_bounds__((ScanCfg<DK, DVS, CB>::NT), 1) kda_scan_kernel(ScanParams p) {
+    typedef ScanCfg<DK, DVS, CB> G;
+    typedef WsBlock<DK, G::C> WS;
+    constexpr int C = G::C, LT = G::LT, ROUNDS = G::ROUNDS;
+    constexpr int NR = DK / 16, NKS = DK / 32, NTT = C / 16;
+    constexpr int RBK = 2 * DK, RBC = 2 * C;  // row bytes of token-row and channel-row operators
+    __shared__ alignas(16) uint8_t lds[G::NBUF * G::SLOT];
 
-    template <int S>
-    __device__ __forceinline__ void put(int jj, uint8_t* bdst, uint8_t* vdst) {
-        (void)jj;
-        i32x4* dst = reinterpret_cast<i32x4*>(bdst);
-#pragma unroll
-        for (int i = 0; i < G::LPT; ++i) {
-            const int idx = ltid + G::LT * i;
-            if (idx < G::NPC) dst[idx] = pc[S][i];
-        }
-#pragma unroll
-        for (int i = 0; i < G::VPT; ++i) {
-            const int idx = ltid + G::LT * i;
-            if (idx < G::NVP) {
-                const int t = idx / (DVS / 8), j0 = 8 * (idx % (DVS / 8));
-                const int pos = kperm(t);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) *reinterpret_cast<bf16*>(vdst + swz_elem<2 * C>(j0 + e, pos)) = vv[S][i][e];
-            }
-        }
-    }
-};
-
-template <int DK, int DVS, int C>
-__global__ void __launch_bounds__((ScanCfg<DK, DVS, C>::NT)) kda_scan_kernel(ScanParams p) {
-    typedef ScanCfg<DK, DVS, C> G;
-    typedef WsBlock<DK, C> WS;
-    constexpr int NS = G::NS, LT = G::LT, BYTES = G::BYTES;
-    __shared__ alignas(16) uint8_t buf[2][BYTES];
-    __shared__ alignas(16) uint8_t vt[2][G::VTB];
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
     const int lr = lane & 15, lg = lane >> 4;
     const int H = p.H, DV = p.DV;
     int item = blockIdx.x;
@@ -135,181 +108,251 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, C>::NT)) kda_scan_kernel(Sca
     const int64_t nch_all = (te - tb + C - 1) / C;
     const int64_t c_end = min(nch_all, p.chunk0 + p.m);
     const int nch = c_end > p.chunk0 ? (int)(c_end - p.chunk0) : 0;
-    const uint8_t* __restrict__ wsu = p.ws + (size_t)unit * p.m * BYTES;
+    const uint8_t* __restrict__ wsu = p.ws + (size_t)unit * p.m * G::BYTES;
+    const bf16* __restrict__ gv = static_cast<const bf16*>(p.v);
+    bf16* __restrict__ go = static_cast<bf16*>(p.o);
 
-    if (wv >= NS) {
-        // ---------------- loader wavefronts ----------------
-        // Chunk c's block is fetched into register set c % PD at step c - PD and
-        // written to LDS buffer c % 2 at step c - 1, so PD - 1 steps of compute
-        // cover its memory latency.  Step i (one per chunk, ending in the
-        // barrier) writes chunk i + 1 and fetches chunk i + PD.
-        ScanLoader<DK, DVS, C> L;
-        L.ltid = tid - WAVE * NS;
-        L.src = wsu; L.gv = static_cast<const bf16*>(p.v);
-        L.tb = tb; L.te = te; L.chunk0 = p.chunk0; L.H = H; L.DV = DV; L.dv0 = dv0; L.h = h;
-        static_assert(G::PD == 3, "the loader loop is unrolled for three register sets");
+    // Lane parts of every LDS address, fixed for the whole walk.  The swizzle of
+    // a row depends only on the row's position inside its 16-row tile, so tile
+    // and matrix offsets are compile-time immediates on top of these.
+    uint32_t oW[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) oW[ks] = swz<RBK>(lr, 4 * ks + lg);  // W, QP fragments
+    const uint32_t oC = swz<RBC>(lr, lg);                                   // KC, KT, M1, M2 fragments
+    const uint32_t oG = WS::GAM + 16 * lg;                                  // GAM rows 4 lg .. 4 lg + 3
+    const uint32_t oV = G::NPB * 16 + 2 * (4 * lg * DVS + 16 * wv * CB + lr);  // value tile [token][column]
+
+    // Copy chunk jj's operator block and value tile into slot sl: piece
+    // r * NT + tid of the slot comes from the block (below NPB), from the value
+    // tile (below NPS), or repeats the last piece (the pad past NPS).
+    // (run by the copy wavefronts only: lt = tid - 64 NW, lw = wv - NW)
+    const int lt = tid - WAVE * G::NW, lw = wv - G::NW;
+    auto copy = [&](int jj, int sl) {
+        const uint8_t* blk = wsu + (size_t)jj * G::BYTES;
+        const int64_t t0 = tb + (p.chunk0 + jj) * C;
+        const int Lc = (int)((te - t0) < C ? (te - t0) : C);
+        uint8_t* slot = lds + sl * G::SLOT + lw * (WAVE * 16);
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
+            const uint8_t* src;
+            if ((r + 1) * LT <= G::NPB) {
+                src = (blk + r * LT * 16) + (uint32_t)(16 * lt);
+            } else {
+                const int pc = min(r * LT + lt, G::NPS - 1);
+                const int q = max(pc - G::NPB, 0), t = q / G::VPR, u = q % G::VPR;
+                // rows past the chunk's end repeat its last row: they meet zero operator columns
+                const int64_t row = (t0 + min(t, Lc - 1)) * H + h;
+                const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(gv + row * DV + dv0 + 8 * u);
+                src = pc < G::NPB ? blk + 16 * pc : vsrc;
+            }
+            __builtin_amdgcn_global_load_lds(src, slot + r * LT * 16, 16, 0, 0);
+        }
+    };
+
+    if (wv >= G::NW) {
+        // ---- copy wavefronts: chunk jj + AHEAD is copied during chunk jj; before
+        // the barrier of chunk jj, chunk jj + 1's copies (the oldest in flight) are
+        // waited for.  One barrier before the walk and one per chunk, like the
+        // compute wavefronts.
         if (nch > 0) {
-            L.template fetch<0>(0, nch);
-            L.template fetch<1>(1, nch);
-            L.template fetch<2>(2, nch);
-            L.template put<0>(0, buf[0], vt[0]);
+#pragma unroll
+            for (int c = 0; c < G::AHEAD; ++c) copy(min(c, nch - 1), c);
         }
-        lds_barrier();
-        for (int i = 0; i < nch; i += 3) {
-            if (i + 1 < nch) L.template put<1>(i + 1, buf[(i + 1) & 1], vt[(i + 1) & 1]);
-            L.template fetch<0>(i + 3, nch);
-            lds_barrier();
-            if (i + 1 < nch) {
-                if (i + 2 < nch) L.template put<2>(i + 2, buf[(i + 2) & 1], vt[(i + 2) & 1]);
-                L.template fetch<1>(i + 4, nch);
-                lds_barrier();
-            }
-            if (i + 2 < nch) {
-                if (i + 3 < nch) L.template put<0>(i + 3, buf[(i + 3) & 1], vt[(i + 3) & 1]);
-                L.template fetch<2>(i + 5, nch);
-                lds_barrier();
-            }
+        slot_barrier<(G::AHEAD - 1) * ROUNDS>();
+        for (int jj = 0; jj < nch; ++jj) {
+            copy(min(jj + G::AHEAD, nch - 1), (jj + G::AHEAD) % G::NBUF);
+            slot_barrier<(G::AHEAD - 1) * ROUNDS>();
         }
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no copy outlives the workgroup
         return;
     }
 
-    // ---------------- compute wavefronts: columns dv0 + 16 wv .. + 15 ----------------
-    bf16* __restrict__ go = static_cast<bf16*>(p.o);
-    constexpr int NR = DK / 16, NKS = DK / 32, NTT = C / 16, NKC = C / 32;
-    f32x4 acc[NR];  // state rows 16 r + 4 lg + i, column lr of the block
-    const int64_t sb = (int64_t)unit * DK * DV + dv0 + 16 * wv + lr;
+    // ---- state: column blocks cb of this wavefront, rows 16 r + 4 lg + i ------------
+    f32x4 acc[CB][NR];
+    const int64_t sb = (int64_t)unit * DK * DV + dv0 + 16 * wv * CB + lr;
+    if (p.S_in) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[r][i] = p.S_in ? p.S_in[sb + (int64_t)(16 * r + 4 * lg + i) * DV] : 0.f;
-    bf16x8 sfr[NKS];
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[cb][r][i] = p.S_in[sb + 16 * cb + (int64_t)(16 * r + 4 * lg + i) * DV];
+    } else {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[cb][r] = zero4();
+    }
+    bf16x8 sfr[CB][NKS];
     auto make_sfr = [&]() {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sfr[ks][i] = (bf16)acc[2 * ks][i];
-                sfr[ks][4 + i] = (bf16)acc[2 * ks + 1][i];
-            }
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sfr[cb][ks][i] = (bf16)acc[cb][2 * ks][i];
+                    sfr[cb][ks][4 + i] = (bf16)acc[cb][2 * ks + 1][i];
+                }
     };
     make_sfr();
-    lds_barrier();
+
+    slot_barrier<0>();
+
+    // outputs of the chunk just computed (bf16, rows past the chunk end skipped)
+    f32x4 ot[CB][NTT];
+    int64_t o_t0 = 0;
+    int o_Lc = 0;
+    const int64_t o_lane = (int64_t)lr * H * DV + 16 * wv * CB + 4 * lg;
+    auto store_o = [&]() {
+        bf16* base = go + (o_t0 * H + h) * DV + dv0 + o_lane;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+                if (16 * tt + lr < o_Lc) store4(base + (int64_t)16 * tt * H * DV + 16 * cb, ot[cb][tt]);
+    };
+
+    auto frag = [](const uint8_t* a) { return *reinterpret_cast<const bf16x8*>(a); };
+    // Group 1 of a chunk: the E and O operands and the value fragment (column j
+    // of the block, tokens in the permuted order: positions 8 lg .. 8 lg + 7 hold
+    // tokens 4 lg .. 4 lg + 3 and 16 + 4 lg .. 16 + 4 lg + 3).  It is read right
+    // after the barrier that publishes the chunk, while the previous chunk's
+    // state update runs on the matrix cores.
+    bf16x8 wf[NTT][NKS], m1f[NTT], qpf[NTT][NKS], m2f[NTT], vfr[CB];
+    bf16 vraw[CB][8];  // value elements as read; packed into vfr where first used
+    auto read_group1 = [&](const uint8_t* B) {
+        const bf16* bV = reinterpret_cast<const bf16*>(B + oV);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vraw[cb][e] = bV[e * DVS + 16 * cb];
+                vraw[cb][4 + e] = bV[(16 + e) * DVS + 16 * cb];
+            }
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+            m1f[tt] = frag(B + oC + WS::M1 + 16 * tt * RBC);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) wf[tt][ks] = frag(B + oW[ks] + WS::W + 16 * tt * RBK);
+        }
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+            m2f[tt] = frag(B + oC + WS::M2 + 16 * tt * RBC);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) qpf[tt][ks] = frag(B + oW[ks] + WS::QP + 16 * tt * RBK);
+        }
+    };
+    if (nch > 0) read_group1(lds);
 
     for (int jj = 0; jj < nch; ++jj) {
-        const uint8_t* B = buf[jj & 1];
-        const uint8_t* Vt = vt[jj & 1];
-        // operand fragment of a matrix with 2 DK-byte rows (fk) or 2 C-byte rows (fc)
-        auto fk = [&](int off, int row, int piece) -> bf16x8 {
-            return *reinterpret_cast<const bf16x8*>(B + off + swz<2 * DK>(row, piece));
-        };
-        auto fc = [&](int off, int row, int piece) -> bf16x8 {
-            return *reinterpret_cast<const bf16x8*>(B + off + swz<2 * C>(row, piece));
-        };
+        const uint8_t* B = lds + (jj % G::NBUF) * G::SLOT;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vfr[cb][e] = vraw[cb][e];
+        __builtin_amdgcn_sched_barrier(0);
 
-        bf16x8 vfr[NKC];
+        // E = -(W S + M1 V): rows tokens, column j (lane)
+        f32x4 z[CB][NTT];
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-            vfr[kc] = *reinterpret_cast<const bf16x8*>(Vt + swz<2 * C>(16 * wv + lr, 4 * kc + lg));
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                f32x4 x = Mma<bf16>::mma(m1f[tt], vfr[cb], zero4());
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) x = Mma<bf16>::mma(wf[tt][ks], sfr[cb][ks], x);
+                z[cb][tt] = x;
+            }
+        __builtin_amdgcn_sched_barrier(0);
 
-        // E = -(W S + M1 V), token tiles tt
-        f32x4 z[NTT];
+        // group 2: state-update operands, in flight during the O products
+        bf16x8 ktf[NR], kcf[NR];
+        f32x4 gmv[NR];
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            bf16x8 a[NKS + NKC];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) a[ks] = fk(WS::W, 16 * tt + lr, 4 * ks + lg);
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) a[NKS + kc] = fc(WS::M1, 16 * tt + lr, 4 * kc + lg);
-            f32x4 x = zero4();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) x = Mma<bf16>::mma(a[ks], sfr[ks], x);
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) x = Mma<bf16>::mma(a[NKS + kc], vfr[kc], x);
-            z[tt] = x;
+        for (int r = 0; r < NR; ++r) {
+            ktf[r] = frag(B + oC + WS::KT + 16 * r * RBC);
+            kcf[r] = frag(B + oC + WS::KC + 16 * r * RBC);
+            gmv[r] = *reinterpret_cast<const f32x4*>(B + oG + 64 * r);
         }
-        bf16x8 efr[NKC];
+        __builtin_amdgcn_sched_barrier(0);
+
+        // O^T = S^T QP^T + V^T M2^T with the state at the chunk start
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                f32x4 x = Mma<bf16>::mma(vfr[cb], m2f[tt], zero4());
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) x = Mma<bf16>::mma(sfr[cb][ks], qpf[tt][ks], x);
+                ot[cb][tt] = x;
+            }
+        bf16x8 efr[CB], vkeep[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            vkeep[cb] = vfr[cb];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                efr[kc][i] = (bf16)(-z[2 * kc][i]);
-                efr[kc][4 + i] = (bf16)(-z[2 * kc + 1][i]);
+                efr[cb][i] = (bf16)(-z[cb][0][i]);
+                efr[cb][4 + i] = (bf16)(-z[cb][1][i]);
             }
-
-        // O^T = S^T QP^T + V^T M2^T (state at the chunk start), token tiles tt
-        f32x4 ot[NTT];
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            bf16x8 b[NKS + NKC];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) b[ks] = fk(WS::QP, 16 * tt + lr, 4 * ks + lg);
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) b[NKS + kc] = fc(WS::M2, 16 * tt + lr, 4 * kc + lg);
-            f32x4 x = zero4();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) x = Mma<bf16>::mma(sfr[ks], b[ks], x);
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) x = Mma<bf16>::mma(vfr[kc], b[NKS + kc], x);
-            ot[tt] = x;
         }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // This chunk's LDS reads have all returned; the barrier frees its slot
+        // for the copy wavefronts and publishes chunk jj + 1.
+        slot_barrier<63>();
+        // next chunk's group 1 (after the last chunk: a harmless read of a stale slot)
+        read_group1(lds + ((jj + 1) % G::NBUF) * G::SLOT);
+        __builtin_amdgcn_sched_barrier(0);
 
         // S <- Diag(GAM) S + KT V + KC E
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const f32x4 gm = *reinterpret_cast<const f32x4*>(B + WS::GAM + 4 * (16 * r + 4 * lg));
-            bf16x8 kt[NKC], kc_[NKC];
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-                kt[kc] = fc(WS::KT, 16 * r + lr, 4 * kc + lg);
-                kc_[kc] = fc(WS::KC, 16 * r + lr, 4 * kc + lg);
+            for (int cb = 0; cb < CB; ++cb) {
+                f32x4 x = acc[cb][r] * gmv[r];
+                x = Mma<bf16>::mma(ktf[r], vkeep[cb], x);
+                acc[cb][r] = Mma<bf16>::mma(kcf[r], efr[cb], x);
             }
-            f32x4 x = acc[r] * gm;
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) x = Mma<bf16>::mma(kt[kc], vfr[kc], x);
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) x = Mma<bf16>::mma(kc_[kc], efr[kc], x);
-            acc[r] = x;
-        }
+        __builtin_amdgcn_sched_barrier(0);
         make_sfr();
 
-        // outputs: lane holds columns 4 lg .. 4 lg + 3 of token 16 tt + lr
-        const int64_t t0 = tb + (p.chunk0 + jj) * C;
-        const int Lc = (int)((te - t0) < C ? (te - t0) : C);
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            const int t = 16 * tt + lr;
-            if (t < Lc) store4(go + ((t0 + t) * H + h) * DV + dv0 + 16 * wv + 4 * lg, ot[tt]);
-        }
-        lds_barrier();
+        o_t0 = tb + (p.chunk0 + jj) * C;
+        o_Lc = (int)((te - o_t0) < C ? (te - o_t0) : C);
+        store_o();
     }
 
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p.S_out[sb + (int64_t)(16 * r + 4 * lg + i) * DV] = acc[r][i];
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p.S_out[sb + 16 * cb + (int64_t)(16 * r + 4 * lg + i) * DV] = acc[cb][r][i];
 }
 
 // ------------------------------------------------------------------------------------
-template <int DK, int DVS, int C>
+template <int DK, int DVS, int CB>
 static hipError_t scan_cfg(const ScanLaunch& a, hipStream_t stream) {
     ScanParams p;
     p.v = a.v; p.o = a.o; p.cu = a.cu_seqlens; p.eq_len = a.eq_len;
     p.ws = static_cast<const uint8_t*>(a.ws); p.S_in = a.S_in; p.S_out = a.S_out;
     p.H = a.num_heads; p.DV = a.dv; p.split = a.split; p.m = a.m; p.chunk0 = a.chunk0;
     const int64_t blocks = (int64_t)a.units * a.split;
-    p.xcd_group = (blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
-    hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, C>), dim3((unsigned)blocks), dim3(ScanCfg<DK, DVS, C>::NT), 0,
+    p.xcd_group = (a.split > 1 && blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
+    hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, CB>), dim3((unsigned)blocks), dim3(ScanCfg<DK, DVS, CB>::NT), 0,
                        stream, p);
     return hipGetLastError();
 }
 
-#define KDA_SCAN_CASE(DK_, DVS_, C_) \
-    if (dk == DK_ && dvs == DVS_ && chunk == C_) { if (a) *err = scan_cfg<DK_, DVS_, C_>(*a, stream); return true; }
+// Compiled slices: 16-column slices use one block per wavefront; wider ones two.
+#define KDA_SCAN_CASE(DK_, DVS_, CB_) \
+    if (dk == DK_ && dvs == DVS_) { if (a) *err = scan_cfg<DK_, DVS_, CB_>(*a, stream); return true; }
 
 static bool scan_dispatch(int dk, int dvs, int chunk, const ScanLaunch* a, hipStream_t stream, hipError_t* err) {
-    KDA_SCAN_CASE(128, 16, 32) KDA_SCAN_CASE(128, 32, 32) KDA_SCAN_CASE(128, 64, 32)
-    KDA_SCAN_CASE(64, 16, 32) KDA_SCAN_CASE(64, 32, 32) KDA_SCAN_CASE(64, 64, 32)
-    KDA_SCAN_CASE(64, 16, 64) KDA_SCAN_CASE(64, 32, 64) KDA_SCAN_CASE(64, 64, 64)
+    if (chunk != 32) return false;
+    KDA_SCAN_CASE(128, 16, 1) KDA_SCAN_CASE(128, 32, 1) KDA_SCAN_CASE(128, 64, 2) KDA_SCAN_CASE(128, 128, 2)
+    KDA_SCAN_CASE(64, 16, 1) KDA_SCAN_CASE(64, 32, 1) KDA_SCAN_CASE(64, 64, 2) KDA_SCAN_CASE(64, 128, 2)
     return false;
 }
 

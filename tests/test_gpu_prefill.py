@@ -70,14 +70,15 @@ def test_prefill_bf16_varlen(dk, dv, scalar, method):
     check_all(inp, o, ST, 2e-2)
 
 
-@pytest.mark.parametrize("chunk", [32, 64])
-def test_two_pass_segments(chunk):
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+def test_two_pass_segments(dk, dv):
     """The two-pass method with the smallest workspace (one chunk per segment),
     a middle one, and the preferred one agree with the oracle and each other;
     without S_T the running state lives in the workspace."""
-    log(f"two-pass segments chunk={chunk}")
-    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=3, heads=2, dk=64, dv=64)
-    inp = generate(w, seed=21 + chunk, device=DEV, lengths=[300, 7, 161])
+    chunk = 32
+    log(f"two-pass segments dk={dk} dv={dv}")
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=3, heads=2, dk=dk, dv=dv)
+    inp = generate(w, seed=21 + dk, device=DEV, lengths=[300, 7, 161])
     q, v = inp["q"], inp["v"]
     least = kda.chunk_workspace_size(q, v, num_seqs=3, chunk_size=chunk, method=TWO, max_seqlen=300,
                                      minimum=True)
