@@ -66,6 +66,7 @@ struct ScanLaunch {
 };
 int prep_block_bytes(int dk, int chunk);  // 0 if no prep kernel for (dk, chunk)
 hipError_t launch_prep(const PrepLaunch& a, hipStream_t stream);
+hipError_t launch_prep2(const PrepLaunch& a, hipStream_t stream);  // dk = 128, chunk 32
 bool two_pass_supported(int dtype, int dk, int dvs, int chunk);
 hipError_t launch_scan(const ScanLaunch& a, hipStream_t stream);
 

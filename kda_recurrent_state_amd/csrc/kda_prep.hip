@@ -451,7 +451,7 @@ int prep_block_bytes(int dk, int chunk) {
 }
 
 hipError_t launch_prep(const PrepLaunch& a, hipStream_t stream) {
-    if (a.dk == 128 && a.chunk == 32) return a.scalar ? prep_cfg<128, 32, true>(a, stream) : prep_cfg<128, 32, false>(a, stream);
+    if (a.dk == 128 && a.chunk == 32) return launch_prep2(a, stream);
     if (a.dk == 64 && a.chunk == 32) return a.scalar ? prep_cfg<64, 32, true>(a, stream) : prep_cfg<64, 32, false>(a, stream);
     if (a.dk == 64 && a.chunk == 64) return a.scalar ? prep_cfg<64, 64, true>(a, stream) : prep_cfg<64, 64, false>(a, stream);
     return hipErrorInvalidValue;

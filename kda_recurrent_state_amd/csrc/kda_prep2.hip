@@ -1,0 +1,422 @@
+// kda_prep2.hip -- chunk-parallel pass of the two-pass KDA prefill for dk = 128
+// on gfx950 (the operator blocks of kda_ws.hpp, same math as kda_prep.hip).
+//
+// The chunkwise (WY) form (page "The argument, in one page", section
+// "Everything, in one table", row "Chunkwise / WY") separates each chunk's
+// state-independent work from the short state recurrence.  Per chunk of 32
+// tokens (g_t the running sum of log a, b = beta, mid-point reference mu_b of
+// each 16-token block, F = e^{mu_1 - mu_0}):
+//   A  = strict_lower(diag(b) Kb Kc^T)   L = strict_lower(Kb Kt^T)
+//   P1 = lower(Qb Kc^T)                  P2 = lower(Qb Kt^T)
+//   Tb = (I + A)^-1 diag(b),  R = P1 Tb
+//   W  = Tb Kb,  QP = Qb - R Kb,  M1 = Tb L diag(b),  M2 = P2 diag(b) - R L diag(b)
+//   KC = (K e^{g_C - g_{t-1}})^T,  KT = (diag(b) K e^{g_C - g_t})^T,  GAM = e^{g_C}
+//
+// Work decomposition: one workgroup of four wavefronts per chunk (persistent
+// workgroups walk a strided list of chunks, two per compute unit).  In the
+// elementwise phase thread (c2, o) owns the channel pair 2 c2, 2 c2 + 1 and
+// the token octet o (tokens 8 o .. 8 o + 7; octets 0 and 2 end at their
+// block's mid-point, octets 1 and 3 start right after it).  Its decay factors
+// relative to the mid-point are running products of a = 2^{log2e log a} and
+// 1 / a along its eight tokens, so each token costs two exponentials and no
+// cross-thread scan; the octet totals, exchanged through LDS, give e^{mu_b},
+// e^{g_C - mu_b}, F and e^{g_C}.  Per-token log a is clamped at -10.4 (log2
+// -15), which keeps every running product inside fp32 range.
+//
+// Phases (LDS barriers between them):
+//   A1 inputs -> factors -> mid-referenced Gram operands, octet products
+//   A2 chunk-referenced operands: KbT, Qb to LDS; KC, KT, GAM to the block
+//   B  the four Gram products on bf16 matrix cores (12 tiles, 3 per wavefront)
+//   C  (I + A)^-1 by blocked forward substitution; Tb and Tb^T to LDS
+//   D  R, W, QP, M1, M2 on matrix cores, each output lane writing 16 bytes
+// The next chunk's inputs are loaded into registers during phases B-D.
+#include "kda_chunk_common.hpp"
+#include "kda_launch.hpp"
+#include "kda_ws.hpp"
+
+namespace kda {
+
+namespace p2 {
+constexpr int DK = 128, C = 32, NT = 256;
+constexpr int LDK = DK + 8;  // bf16 rows over channels
+constexpr int LDC = C + 8;   // bf16 rows over tokens
+constexpr int LDA = C + 4;   // fp32 rows over tokens
+constexpr float LA_MIN = -15.f;  // log2 clamp of a per-token decay
+}  // namespace p2
+
+struct Prep2Lds {
+    union {
+        struct {  // phases A1-B: mid-referenced Gram operands [token][channel]
+            bf16 Kr[p2::C * p2::LDK], Qr[p2::C * p2::LDK], Kce[p2::C * p2::LDK], Kci[p2::C * p2::LDK];
+        } g;
+        struct {  // phase C
+            float Tf[p2::C * p2::LDA];  // (I + A)^-1, fp32, lower triangle
+            float Xs[16 * 17];
+            float X[2 * 512];
+        } v;
+    } u;
+    alignas(16) bf16 KbT[p2::DK * p2::LDC];  // (K e^{g_{t-1}})^T [channel][permuted token]
+    alignas(16) bf16 Qb[p2::C * p2::LDK];    // Q e^{g_t} [token][channel]
+    alignas(16) float A[p2::C * p2::LDA];    // diag(b) strict_lower(Kb Kc^T) [t][i]
+    alignas(16) float P2b[p2::C * p2::LDA];  // lower(Qb Kt^T) diag(b) [t][i]
+    alignas(16) bf16 P1[p2::C * p2::LDC];    // lower(Qb Kc^T) [t][i]
+    alignas(16) bf16 LbT[p2::C * p2::LDC];   // (L diag(b))^T [i][permuted t]
+    alignas(16) bf16 Tb[p2::C * p2::LDC];    // (I + A)^-1 diag(b) [t][permuted s]
+    alignas(16) bf16 TbT[p2::C * p2::LDC];   // its transpose [s][t]
+    alignas(16) float F[p2::DK];             // e^{mu_1 - mu_0}
+    alignas(16) float Pq[4 * p2::DK];        // product of a over each token octet
+    alignas(16) float beta[p2::C];
+    alignas(16) float ones[16];
+};
+
+struct Prep2Params {
+    const void* q;
+    const void* k;
+    const float* log_a;
+    const float* beta;
+    const int32_t* cu;
+    int64_t eq_len;
+    uint8_t* ws;      // operator blocks [unit][m]
+    int H;
+    int m;            // chunks per unit in this segment (block stride)
+    int items;        // units * m
+    int64_t chunk0;   // first chunk index of the segment
+};
+
+// Raw inputs of one thread: tokens 8 o + j of its channel pair, and b of token
+// `tid` (threads below C).
+struct Prep2In {
+    Vec2<bf16>::type q[8], k[8];
+    f32x2 la[8];
+    float b;
+};
+
+__device__ __forceinline__ bool prep2_locate(const Prep2Params& p, int item, int64_t& t0, int& Lc, int& h) {
+    const int unit = item / p.m, j = item % p.m;
+    const int n = unit / p.H;
+    h = unit % p.H;
+    int64_t tb, te;
+    if (p.cu) { tb = p.cu[n]; te = p.cu[n + 1]; }
+    else { tb = (int64_t)n * p.eq_len; te = tb + p.eq_len; }
+    t0 = tb + (p.chunk0 + j) * p2::C;
+    Lc = (int)((te - t0) < p2::C ? (te - t0) : p2::C);
+    return t0 < te;
+}
+
+template <bool SCALAR>
+__device__ __forceinline__ void prep2_load(const Prep2Params& p, int64_t t0, int Lc, int h, int tid, int c2, int o,
+                                           Prep2In& in) {
+    typedef Vec2<bf16>::type b2;
+    const bf16* __restrict__ gq = static_cast<const bf16*>(p.q);
+    const bf16* __restrict__ gk = static_cast<const bf16*>(p.k);
+    const int64_t r0 = t0 * p.H + h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        // rows past the chunk's end repeat its last row; b and log a are masked there
+        const int64_t row = r0 + (int64_t)min(8 * o + j, Lc - 1) * p.H;
+        in.q[j] = *reinterpret_cast<const b2*>(gq + row * p2::DK + 2 * c2);
+        in.k[j] = *reinterpret_cast<const b2*>(gk + row * p2::DK + 2 * c2);
+        if (SCALAR) { const float x = p.log_a[row]; in.la[j] = f32x2{x, x}; }
+        else in.la[j] = *reinterpret_cast<const f32x2*>(p.log_a + row * p2::DK + 2 * c2);
+    }
+    in.b = (tid < Lc) ? p.beta[r0 + (int64_t)tid * p.H] : 0.f;
+}
+
+template <bool SCALAR>
+__global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
+    using namespace p2;
+    typedef WsBlock<DK, C> WS;
+    typedef Mma<bf16> M;
+    __shared__ Prep2Lds s;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int c2 = lane, o = wv;  // elementwise phase: channel pair, token octet
+    const int blk_b = o >> 1;     // 16-token block of the octet
+
+    // upper blocks of the masked products are never written: zero them once
+    for (int e = tid; e < C * LDC; e += NT) {
+        s.LbT[e] = (bf16)0.f; s.P1[e] = (bf16)0.f;
+    }
+    for (int e = tid; e < C * LDA; e += NT) s.P2b[e] = 0.f;
+    if (tid < 16) s.ones[tid] = 1.f;
+
+    auto next_item = [&](int it, int64_t& t0, int& Lc, int& h) {
+        while (it < p.items && !prep2_locate(p, it, t0, Lc, h)) it += gridDim.x;
+        return it;
+    };
+    int64_t t0 = 0;
+    int Lc = 0, h = 0;
+    int item = next_item(blockIdx.x, t0, Lc, h);
+    Prep2In in;
+    if (item < p.items) prep2_load<SCALAR>(p, t0, Lc, h, tid, c2, o, in);
+
+    while (item < p.items) {
+        uint8_t* __restrict__ blk = p.ws + (size_t)item * WS::BYTES;
+
+        // ---- A1: factors relative to the block mid-point, Gram operands ---------------
+        f32x2 a[8], ai[8], E[8], Ei[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool valid = 8 * o + j < Lc;
+            f32x2 la2 = valid ? in.la[j] * LOG2E : f32x2{0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float x = fmaxf(la2[e], LA_MIN);
+                a[j][e] = __builtin_amdgcn_exp2f(x);
+                ai[j][e] = __builtin_amdgcn_exp2f(-x);
+            }
+        }
+        f32x2 P;
+        if ((o & 1) == 0) {  // tokens up to the mid-point: backward from it
+            E[7] = f32x2{1.f, 1.f};
+            Ei[7] = f32x2{1.f, 1.f};
+#pragma unroll
+            for (int j = 6; j >= 0; --j) {
+                E[j] = E[j + 1] * ai[j + 1];
+                Ei[j] = Ei[j + 1] * a[j + 1];
+            }
+            P = Ei[0] * a[0];
+        } else {  // tokens after it: forward
+            E[0] = a[0];
+            Ei[0] = ai[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) {
+                E[j] = E[j - 1] * a[j];
+                Ei[j] = Ei[j - 1] * ai[j];
+            }
+            P = E[7];
+        }
+        *reinterpret_cast<f32x2*>(&s.Pq[o * DK + 2 * c2]) = P;
+        if (tid < C) s.beta[tid] = in.b;
+
+        f32x2 kr[8], qr[8], kce[8], kci[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = 8 * o + j;
+            const f32x2 k = f32x2{Vec2<bf16>::lo(in.k[j]), Vec2<bf16>::hi(in.k[j])};
+            const f32x2 q = f32x2{Vec2<bf16>::lo(in.q[j]), Vec2<bf16>::hi(in.q[j])};
+            kr[j] = k * (E[j] * ai[j]);   // k e^{g_{t-1} - mu}
+            qr[j] = q * E[j];             // q e^{g_t - mu}
+            kce[j] = k * (Ei[j] * a[j]);  // k e^{mu - g_{t-1}}
+            kci[j] = k * Ei[j];           // k e^{mu - g_t}
+            store2(&s.u.g.Kr[t * LDK + 2 * c2], kr[j][0], kr[j][1]);
+            store2(&s.u.g.Qr[t * LDK + 2 * c2], qr[j][0], qr[j][1]);
+            store2(&s.u.g.Kce[t * LDK + 2 * c2], kce[j][0], kce[j][1]);
+            store2(&s.u.g.Kci[t * LDK + 2 * c2], kci[j][0], kci[j][1]);
+        }
+        lds_barrier();
+
+        // ---- A2: chunk-referenced operands ---------------------------------------------
+        {
+            const f32x2 P0 = *reinterpret_cast<const f32x2*>(&s.Pq[0 * DK + 2 * c2]);
+            const f32x2 P1 = *reinterpret_cast<const f32x2*>(&s.Pq[1 * DK + 2 * c2]);
+            const f32x2 P2 = *reinterpret_cast<const f32x2*>(&s.Pq[2 * DK + 2 * c2]);
+            const f32x2 P3 = *reinterpret_cast<const f32x2*>(&s.Pq[3 * DK + 2 * c2]);
+            const f32x2 F = P1 * P2;         // e^{mu_1 - mu_0}
+            const f32x2 em0 = P0;            // e^{mu_0}
+            const f32x2 ec1 = P3;            // e^{g_C - mu_1}
+            const f32x2 em = blk_b ? em0 * F : em0;
+            const f32x2 ec = blk_b ? ec1 : F * ec1;
+            if (o == 0) {
+                *reinterpret_cast<f32x2*>(&s.F[2 * c2]) = F;
+                *reinterpret_cast<f32x2*>(blk + WS::GAM + 8 * c2) = (em0 * F) * ec1;
+            }
+            // KbT rows (channels), tokens at their permuted positions: tokens 8 o .. 8 o + 3
+            // and 8 o + 4 .. 8 o + 7 land at two 4-element runs
+            const int pos0 = kperm(8 * o), pos1 = kperm(8 * o + 4);
+            f32x4 kb0[2], kb1[2], kc0[2], kc1[2], kt0[2], kt1[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    kb0[e][j] = kr[j][e] * em[e];
+                    kb1[e][j] = kr[4 + j][e] * em[e];
+                    kc0[e][j] = kce[j][e] * ec[e];
+                    kc1[e][j] = kce[4 + j][e] * ec[e];
+                    kt0[e][j] = kci[j][e] * ec[e] * s.beta[8 * o + j];
+                    kt1[e][j] = kci[4 + j][e] * ec[e] * s.beta[8 * o + 4 + j];
+                }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int c = 2 * c2 + e;
+                store4(&s.KbT[c * LDC + pos0], kb0[e]);
+                store4(&s.KbT[c * LDC + pos1], kb1[e]);
+                store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c, pos0)), kc0[e]);
+                store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c, pos1)), kc1[e]);
+                store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos0)), kt0[e]);
+                store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos1)), kt1[e]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const f32x2 qb = qr[j] * em;
+                store2(&s.Qb[(8 * o + j) * LDK + 2 * c2], qb[0], qb[1]);
+            }
+        }
+        lds_barrier();
+
+        // next chunk's inputs: in flight during phases B-D
+        int64_t nt0 = 0;
+        int nLc = 0, nh = 0;
+        const int nitem = next_item(item + gridDim.x, nt0, nLc, nh);
+        if (nitem < p.items) prep2_load<SCALAR>(p, nt0, nLc, nh, tid, c2, o, in);
+
+        // ---- B: Gram products; tile w is product w % 4 (0 A, 1 L, 2 P1, 3 P2) of block
+        //      pair w / 4 ((0,0), (1,0), (1,1)) -------------------------------------------
+        for (int w = wv; w < 12; w += 4) {
+            const int g = w % 4, pr = w / 4;
+            const int bt = pr == 0 ? 0 : 1, bi = pr == 2 ? 1 : 0;
+            const bf16* rows = (g < 2 ? s.u.g.Kr : s.u.g.Qr) + (16 * bt + lr) * LDK;
+            const bf16* cols = ((g & 1) == 0 ? s.u.g.Kce : s.u.g.Kci) + (16 * bi + lr) * LDK;
+            constexpr int NK = DK / M::K;
+            M::frag fr[NK], fc[NK];
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                fr[kk] = M::loadr(rows + kk * M::K, lane);
+                fc[kk] = M::loadr(cols + kk * M::K, lane);
+            }
+            if (bt != bi) {
+                const float* Fp = s.F + lg * M::KPL;
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) fr[kk] = M::scale(fr[kk], Fp + kk * M::K);
+            }
+            f32x4 acc = zero4();
+            if (g == 1) {
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) acc = M::mma(fr[kk], fc[kk], acc);
+                // rows t = 16 bt + 4 lg + r, column i = 16 bi + lr; LbT[i] at permuted t
+                const int i = 16 * bi + lr, tt = 16 * bt + 4 * lg;
+                const float bi_ = s.beta[i];
+                f32x4 m;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[r] = (i < tt + r) ? acc[r] * bi_ : 0.f;
+                store4(&s.LbT[i * LDC + kperm(tt)], m);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) acc = M::mma(fc[kk], fr[kk], acc);
+                // column t = 16 bt + lr, rows i = 16 bi + 4 lg + r
+                const int t = 16 * bt + lr, i0 = 16 * bi + 4 * lg;
+                f32x4 m;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[r] = (g == 0 ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f;
+                if (g == 0) *reinterpret_cast<f32x4*>(&s.A[t * LDA + i0]) = s.beta[t] * m;
+                else if (g == 2) store4(&s.P1[t * LDC + i0], m);
+                else *reinterpret_cast<f32x4*>(&s.P2b[t * LDA + i0]) =
+                         m * *reinterpret_cast<const f32x4*>(&s.beta[i0]);
+            }
+        }
+        lds_barrier();
+
+        // ---- C: T = (I + A)^-1: diagonal blocks on wavefronts 0 and 1, then
+        //      T21 = -T22 A21 T11 on wavefront 0 ---------------------------------------------
+        if (wv < 2)
+            block_inverse<float, 16, LDA, LDA>(s.A + 16 * wv * LDA + 16 * wv, s.ones, s.u.v.X + wv * 512,
+                                               s.u.v.Tf + 16 * wv * LDA + 16 * wv, lane);
+        lds_barrier();
+        if (wv == 0) {
+            f32x4 x = zero4();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int kk = 4 * ks + lg;
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(s.A[(16 + lr) * LDA + kk], s.u.v.Tf[kk * LDA + lr], x, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s.u.v.Xs[(4 * lg + r) * 17 + lr] = x[r];
+            wave_sync();
+            f32x4 t = zero4();
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int kk = 4 * ks + lg;
+                t = __builtin_amdgcn_mfma_f32_16x16x4f32(s.u.v.Tf[(16 + lr) * LDA + 16 + kk], s.u.v.Xs[kk * 17 + lr], t,
+                                                         0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s.u.v.Tf[(16 + 4 * lg + r) * LDA + lr] = -t[r];
+        }
+        lds_barrier();
+        // Tb = T diag(b) at permuted columns, and its transpose at natural columns
+#pragma unroll
+        for (int e = tid; e < C * C; e += NT) {
+            const int t = e >> 5, s_ = e & 31;
+            const float x = (s_ <= t) ? s.u.v.Tf[t * LDA + s_] * s.beta[s_] : 0.f;
+            s.Tb[t * LDC + kperm(s_)] = (bf16)x;
+            s.TbT[s_ * LDC + t] = (bf16)x;
+        }
+        lds_barrier();
+
+        // ---- D: wavefront w: token tile tt = w & 1; channel pairs 2 (w >> 1) and
+        //      2 (w >> 1) + 1 of W and QP; M1 (w < 2) or M2 (w >= 2) --------------------------
+        {
+            const int tt = wv & 1, half = wv >> 1;
+            const int t = 16 * tt + lr;
+            // R = P1 Tb as a B-operand fragment: out[s][t] = sum_i TbT[s][i] P1[t][i]
+            const M::frag p1f = M::loadr(s.P1 + t * LDC, lane);
+            const f32x4 r0 = M::mma(M::loadr(s.TbT + lr * LDC, lane), p1f, zero4());
+            const f32x4 r1 = M::mma(M::loadr(s.TbT + (16 + lr) * LDC, lane), p1f, zero4());
+            M::frag rfr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { rfr[i] = (bf16)r0[i]; rfr[4 + i] = (bf16)r1[i]; }
+            const M::frag tbf = M::loadr(s.Tb + t * LDC, lane);
+            typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int cp = 2 * half + cc;  // 32-channel block
+                const M::frag kb0 = M::loadr(s.KbT + (32 * cp + lr) * LDC, lane);
+                const M::frag kb1 = M::loadr(s.KbT + (32 * cp + 16 + lr) * LDC, lane);
+                const f32x4 w0 = M::mma(kb0, tbf, zero4()), w1 = M::mma(kb1, tbf, zero4());
+                const f32x4 x0 = M::mma(kb0, rfr, zero4()), x1 = M::mma(kb1, rfr, zero4());
+                const f32x4 q0 = load4(&s.Qb[t * LDK + 32 * cp + 4 * lg]);
+                const f32x4 q1 = load4(&s.Qb[t * LDK + 32 * cp + 16 + 4 * lg]);
+                bf16x8 wo, qo;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    wo[r] = (bf16)w0[r]; wo[4 + r] = (bf16)w1[r];
+                    qo[r] = (bf16)(q0[r] - x0[r]); qo[4 + r] = (bf16)(q1[r] - x1[r]);
+                }
+                *reinterpret_cast<bf16x8*>(blk + WS::W + swz<2 * DK>(t, 4 * cp + lg)) = wo;
+                *reinterpret_cast<bf16x8*>(blk + WS::QP + swz<2 * DK>(t, 4 * cp + lg)) = qo;
+            }
+            const M::frag lb0 = M::loadr(s.LbT + lr * LDC, lane);
+            const M::frag lb1 = M::loadr(s.LbT + (16 + lr) * LDC, lane);
+            bf16x8 mo;
+            if (half == 0) {  // M1 = Tb (L diag(b)): out[i][t]
+                const f32x4 m0 = M::mma(lb0, tbf, zero4()), m1 = M::mma(lb1, tbf, zero4());
+#pragma unroll
+                for (int r = 0; r < 4; ++r) { mo[r] = (bf16)m0[r]; mo[4 + r] = (bf16)m1[r]; }
+                *reinterpret_cast<bf16x8*>(blk + WS::M1 + swz<2 * C>(t, lg)) = mo;
+            } else {  // M2 = P2 diag(b) - R (L diag(b))
+                const f32x4 m0 = M::mma(lb0, rfr, zero4()), m1 = M::mma(lb1, rfr, zero4());
+                const f32x4 pa = *reinterpret_cast<const f32x4*>(&s.P2b[t * LDA + 4 * lg]);
+                const f32x4 pb = *reinterpret_cast<const f32x4*>(&s.P2b[t * LDA + 16 + 4 * lg]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) { mo[r] = (bf16)(pa[r] - m0[r]); mo[4 + r] = (bf16)(pb[r] - m1[r]); }
+                *reinterpret_cast<bf16x8*>(blk + WS::M2 + swz<2 * C>(t, lg)) = mo;
+            }
+        }
+        lds_barrier();  // LDS of this chunk is reused by the next
+
+        item = nitem; t0 = nt0; Lc = nLc; h = nh;
+    }
+}
+
+hipError_t launch_prep2(const PrepLaunch& a, hipStream_t stream) {
+    Prep2Params p;
+    p.q = a.q; p.k = a.k; p.log_a = a.log_a; p.beta = a.beta; p.cu = a.cu_seqlens;
+    p.eq_len = a.eq_len; p.ws = static_cast<uint8_t*>(a.ws); p.H = a.num_heads; p.m = a.m;
+    p.chunk0 = a.chunk0;
+    p.items = (int)(a.units * a.m);
+    // persistent workgroups, two per compute unit, walking items blockIdx.x, + gridDim.x, ...
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int64_t blocks = (int64_t)cus * 2;
+    if (blocks > p.items) blocks = p.items;
+    if (blocks < 1) blocks = 1;
+    if (a.scalar)
+        hipLaunchKernelGGL((kda_prep2_kernel<true>), dim3((unsigned)blocks), dim3(p2::NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((kda_prep2_kernel<false>), dim3((unsigned)blocks), dim3(p2::NT), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace kda
