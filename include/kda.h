@@ -131,11 +131,12 @@ KDA_API int kda_chunk_fwd(const kda_dims_t* dims, const void* q, const void* k, 
                   size_t workspace_bytes, void* stream);
 
 /*
- * Workspace the two-pass prefill prefers for these dims (segments of about
- * 128 MiB of operator blocks, which stay in the last-level cache between the
- * two passes), or 0 if the call would run single-pass (method SINGLE, or no
- * two-pass kernel for the shape).  The minimum that still runs two-pass is
- * what one chunk per (sequence, head) needs: see kda_chunk_workspace_min.
+ * Workspace the two-pass prefill prefers for these dims (segments of up to
+ * 4 GiB of operator blocks: about 1.2 KB per token and head at dk = 128, so a
+ * whole 2 x 32-head x 32K-token batch runs as one segment), or 0 if the call
+ * would run single-pass (method SINGLE, or no two-pass kernel for the shape).
+ * The minimum that still runs two-pass is what one chunk per (sequence, head)
+ * needs: see kda_chunk_workspace_min.
  */
 KDA_API int kda_chunk_workspace_size(const kda_dims_t* dims, size_t* bytes);
 KDA_API int kda_chunk_workspace_min(const kda_dims_t* dims, size_t* bytes);

@@ -85,7 +85,10 @@ struct Plan {
     bool two_pass_ok = false;
 };
 
-constexpr size_t kSegmentTarget = size_t(128) << 20;  // operator bytes per segment
+// Operator bytes per segment of the preferred workspace.  Each segment costs a
+// launch of both passes and a ramp of each; on the 288 GB parts a few GiB is
+// cheap, and fewer, longer segments measured faster than cache-sized ones.
+constexpr size_t kSegmentTarget = size_t(4) << 30;
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 

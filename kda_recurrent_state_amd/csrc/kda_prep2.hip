@@ -26,7 +26,7 @@
 // Phases (LDS barriers between them):
 //   A1 inputs -> factors -> mid-referenced Gram operands, octet products
 //   A2 chunk-referenced operands: KbT, Qb to LDS; KC, KT, GAM to the block
-//   B  the four Gram products on bf16 matrix cores (12 tiles, 3 per wavefront)
+//   B  the four Gram products on bf16 matrix cores (wavefront g: product g)
 //   C  (I + A)^-1 by blocked forward substitution; Tb and Tb^T to LDS
 //   D  R, W, QP, M1, M2 on matrix cores, each output lane writing 16 bytes
 // The next chunk's inputs are loaded into registers during phases B-D.
@@ -83,13 +83,79 @@ struct Prep2Params {
     int64_t chunk0;   // first chunk index of the segment
 };
 
-// Raw inputs of one thread: tokens 8 o + j of its channel pair, and b of token
-// `tid` (threads below C).
-struct Prep2In {
-    Vec2<bf16>::type q[8], k[8];
-    f32x2 la[8];
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+// Raw inputs of one thread as loaded: 16 bytes per lane and row, so each vector
+// memory instruction moves 1 KB.  lq/lk[g]: 8 channels (8 (lane >> 2) ..) of
+// token 8 o + 4 g + (lane & 3); la[p]: 4 channels (4 (lane >> 1) ..) of token
+// 8 o + 2 p + (lane & 1) (per-channel decay), or log a of token 8 o + j in
+// element j % 4 of la[j / 4] (scalar decay).  b: beta of token `tid` (threads
+// below C).
+struct Prep2Raw {
+    i32x4 lq[2], lk[2];
+    f32x4 la[4];
     float b;
 };
+
+// The thread's own inputs after redistribution inside lane quads: channels
+// 2 lane, 2 lane + 1 of tokens 8 o + j.
+struct Prep2In {
+    uint32_t q[8], k[8];  // bf16 pairs
+    f32x2 la[8];
+};
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) { return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false); }
+__device__ __forceinline__ float dppf_swap1(float x) {
+    return __builtin_bit_cast(float, dpp<0xB1>(__builtin_bit_cast(int, x)));  // quad_perm [1, 0, 3, 2]
+}
+
+// 4 x 4 transpose of dwords inside each lane quad: lane v of a quad ends with
+// dword v of every lane w of its quad (as its dword w).
+__device__ __forceinline__ i32x4 quad_transpose(i32x4 m, int lane) {
+    const int v = lane & 3;
+    i32x4 n1, n2;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int t = dpp<0xB1>(m[d ^ 1]);  // lane v ^ 1's dword d ^ 1
+        n1[d] = ((v ^ d) & 1) ? t : m[d];
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int t = dpp<0x4E>(n1[d ^ 2]);  // quad_perm [2, 3, 0, 1]: lane v ^ 2's dword d ^ 2
+        n2[d] = ((v ^ d) & 2) ? t : n1[d];
+    }
+    return n2;
+}
+
+template <bool SCALAR>
+__device__ __forceinline__ void prep2_unpack(const Prep2Raw& r, int lane, Prep2In& in) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const i32x4 tq = quad_transpose(r.lq[g], lane), tk = quad_transpose(r.lk[g], lane);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            in.q[4 * g + d] = (uint32_t)tq[d];
+            in.k[4 * g + d] = (uint32_t)tk[d];
+        }
+    }
+    if (SCALAR) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) in.la[j] = f32x2{r.la[j >> 2][j & 3], r.la[j >> 2][j & 3]};
+    } else {
+        // lane 2 m + u holds token 2 p + u, channels 4 m .. 4 m + 3; it keeps channels
+        // 4 m + 2 u, + 1 of both tokens, swapping the other half with its neighbour
+        const bool u = lane & 1;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const f32x4 v = r.la[p];
+            const float s0 = u ? v[0] : v[2], s1 = u ? v[1] : v[3];
+            const float r0 = dppf_swap1(s0), r1 = dppf_swap1(s1);
+            in.la[2 * p] = u ? f32x2{r0, r1} : f32x2{v[0], v[1]};
+            in.la[2 * p + 1] = u ? f32x2{v[2], v[3]} : f32x2{r0, r1};
+        }
+    }
+}
 
 __device__ __forceinline__ bool prep2_locate(const Prep2Params& p, int item, int64_t& t0, int& Lc, int& h) {
     const int unit = item / p.m, j = item % p.m;
@@ -104,20 +170,27 @@ __device__ __forceinline__ bool prep2_locate(const Prep2Params& p, int item, int
 }
 
 template <bool SCALAR>
-__device__ __forceinline__ void prep2_load(const Prep2Params& p, int64_t t0, int Lc, int h, int tid, int c2, int o,
-                                           Prep2In& in) {
-    typedef Vec2<bf16>::type b2;
+__device__ __forceinline__ void prep2_load(const Prep2Params& p, int64_t t0, int Lc, int h, int tid, int lane, int o,
+                                           Prep2Raw& in) {
     const bf16* __restrict__ gq = static_cast<const bf16*>(p.q);
     const bf16* __restrict__ gk = static_cast<const bf16*>(p.k);
     const int64_t r0 = t0 * p.H + h;
+    // rows past the chunk's end repeat its last row; b and log a are masked there
+    auto row = [&](int t) { return r0 + (int64_t)min(t, Lc - 1) * p.H; };
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        // rows past the chunk's end repeat its last row; b and log a are masked there
-        const int64_t row = r0 + (int64_t)min(8 * o + j, Lc - 1) * p.H;
-        in.q[j] = *reinterpret_cast<const b2*>(gq + row * p2::DK + 2 * c2);
-        in.k[j] = *reinterpret_cast<const b2*>(gk + row * p2::DK + 2 * c2);
-        if (SCALAR) { const float x = p.log_a[row]; in.la[j] = f32x2{x, x}; }
-        else in.la[j] = *reinterpret_cast<const f32x2*>(p.log_a + row * p2::DK + 2 * c2);
+    for (int g = 0; g < 2; ++g) {
+        const int64_t rw = row(8 * o + 4 * g + (lane & 3));
+        in.lq[g] = *reinterpret_cast<const i32x4*>(gq + rw * p2::DK + 8 * (lane >> 2));
+        in.lk[g] = *reinterpret_cast<const i32x4*>(gk + rw * p2::DK + 8 * (lane >> 2));
+    }
+    if (SCALAR) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) in.la[j >> 2][j & 3] = p.log_a[row(8 * o + j)];
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            in.la[q] = *reinterpret_cast<const f32x4*>(p.log_a + row(8 * o + 2 * q + (lane & 1)) * p2::DK +
+                                                       4 * (lane >> 1));
     }
     in.b = (tid < Lc) ? p.beta[r0 + (int64_t)tid * p.H] : 0.f;
 }
@@ -137,7 +210,7 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
 
     // upper blocks of the masked products are never written: zero them once
     for (int e = tid; e < C * LDC; e += NT) {
-        s.LbT[e] = (bf16)0.f; s.P1[e] = (bf16)0.f;
+        s.LbT[e] = (bf16)0.f; s.P1[e] = (bf16)0.f; s.Tb[e] = (bf16)0.f; s.TbT[e] = (bf16)0.f;
     }
     for (int e = tid; e < C * LDA; e += NT) s.P2b[e] = 0.f;
     if (tid < 16) s.ones[tid] = 1.f;
@@ -149,13 +222,27 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
     int64_t t0 = 0;
     int Lc = 0, h = 0;
     int item = next_item(blockIdx.x, t0, Lc, h);
-    Prep2In in;
-    if (item < p.items) prep2_load<SCALAR>(p, t0, Lc, h, tid, c2, o, in);
+    Prep2Raw raw;
+    if (item < p.items) prep2_load<SCALAR>(p, t0, Lc, h, tid, lane, o, raw);
 
     while (item < p.items) {
         uint8_t* __restrict__ blk = p.ws + (size_t)item * WS::BYTES;
+        // bounds of the next item in this workgroup's list, read now and used in
+        // phase B, so the scalar loads are not waited for on the spot
+        const int g_item = item + gridDim.x;
+        int64_t g_tb = 0, g_te = 0;
+        int g_h = 0, g_j = 0;
+        if (g_item < p.items) {
+            const int unit = g_item / p.m, n = unit / p.H;
+            g_h = unit % p.H;
+            g_j = g_item % p.m;
+            if (p.cu) { g_tb = p.cu[n]; g_te = p.cu[n + 1]; }
+            else { g_tb = (int64_t)n * p.eq_len; g_te = g_tb + p.eq_len; }
+        }
 
         // ---- A1: factors relative to the block mid-point, Gram operands ---------------
+        Prep2In in;
+        prep2_unpack<SCALAR>(raw, lane, in);
         f32x2 a[8], ai[8], E[8], Ei[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -189,14 +276,16 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
             P = E[7];
         }
         *reinterpret_cast<f32x2*>(&s.Pq[o * DK + 2 * c2]) = P;
-        if (tid < C) s.beta[tid] = in.b;
+        if (tid < C) s.beta[tid] = raw.b;
 
         f32x2 kr[8], qr[8], kce[8], kci[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int t = 8 * o + j;
-            const f32x2 k = f32x2{Vec2<bf16>::lo(in.k[j]), Vec2<bf16>::hi(in.k[j])};
-            const f32x2 q = f32x2{Vec2<bf16>::lo(in.q[j]), Vec2<bf16>::hi(in.q[j])};
+            const Vec2<bf16>::type kv = __builtin_bit_cast(Vec2<bf16>::type, in.k[j]);
+            const Vec2<bf16>::type qv = __builtin_bit_cast(Vec2<bf16>::type, in.q[j]);
+            const f32x2 k = f32x2{Vec2<bf16>::lo(kv), Vec2<bf16>::hi(kv)};
+            const f32x2 q = f32x2{Vec2<bf16>::lo(qv), Vec2<bf16>::hi(qv)};
             kr[j] = k * (E[j] * ai[j]);   // k e^{g_{t-1} - mu}
             qr[j] = q * E[j];             // q e^{g_t - mu}
             kce[j] = k * (Ei[j] * a[j]);  // k e^{mu - g_{t-1}}
@@ -226,27 +315,29 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
             // KbT rows (channels), tokens at their permuted positions: tokens 8 o .. 8 o + 3
             // and 8 o + 4 .. 8 o + 7 land at two 4-element runs
             const int pos0 = kperm(8 * o), pos1 = kperm(8 * o + 4);
-            f32x4 kb0[2], kb1[2], kc0[2], kc1[2], kt0[2], kt1[2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    kb0[e][j] = kr[j][e] * em[e];
-                    kb1[e][j] = kr[4 + j][e] * em[e];
-                    kc0[e][j] = kce[j][e] * ec[e];
-                    kc1[e][j] = kce[4 + j][e] * ec[e];
-                    kt0[e][j] = kci[j][e] * ec[e] * s.beta[8 * o + j];
-                    kt1[e][j] = kci[4 + j][e] * ec[e] * s.beta[8 * o + 4 + j];
-                }
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
+                f32x4 kb0, kb1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    kb0[j] = kr[j][e] * em[e];
+                    kb1[j] = kr[4 + j][e] * em[e];
+                }
                 const int c = 2 * c2 + e;
-                store4(&s.KbT[c * LDC + pos0], kb0[e]);
-                store4(&s.KbT[c * LDC + pos1], kb1[e]);
-                store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c, pos0)), kc0[e]);
-                store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c, pos1)), kc1[e]);
-                store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos0)), kt0[e]);
-                store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos1)), kt1[e]);
+                store4(&s.KbT[c * LDC + pos0], kb0);
+                store4(&s.KbT[c * LDC + pos1], kb1);
+                f32x4 kc0, kc1, kt0, kt1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    kc0[j] = kce[j][e] * ec[e];
+                    kc1[j] = kce[4 + j][e] * ec[e];
+                    kt0[j] = kci[j][e] * ec[e] * s.beta[8 * o + j];
+                    kt1[j] = kci[4 + j][e] * ec[e] * s.beta[8 * o + 4 + j];
+                }
+                store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c, pos0)), kc0);
+                store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c, pos1)), kc1);
+                store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos0)), kt0);
+                store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos1)), kt1);
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -259,51 +350,64 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
         // next chunk's inputs: in flight during phases B-D
         int64_t nt0 = 0;
         int nLc = 0, nh = 0;
-        const int nitem = next_item(item + gridDim.x, nt0, nLc, nh);
-        if (nitem < p.items) prep2_load<SCALAR>(p, nt0, nLc, nh, tid, c2, o, in);
+        int nitem = g_item;
+        if (g_item < p.items) {
+            nt0 = g_tb + (p.chunk0 + g_j) * C;
+            nh = g_h;
+            nLc = (int)((g_te - nt0) < C ? (g_te - nt0) : C);
+            if (nt0 >= g_te) nitem = next_item(g_item + gridDim.x, nt0, nLc, nh);  // empty: look further
+        }
+        if (nitem < p.items) prep2_load<SCALAR>(p, nt0, nLc, nh, tid, lane, o, raw);
 
-        // ---- B: Gram products; tile w is product w % 4 (0 A, 1 L, 2 P1, 3 P2) of block
-        //      pair w / 4 ((0,0), (1,0), (1,1)) -------------------------------------------
-        for (int w = wv; w < 12; w += 4) {
-            const int g = w % 4, pr = w / 4;
-            const int bt = pr == 0 ? 0 : 1, bi = pr == 2 ? 1 : 0;
-            const bf16* rows = (g < 2 ? s.u.g.Kr : s.u.g.Qr) + (16 * bt + lr) * LDK;
-            const bf16* cols = ((g & 1) == 0 ? s.u.g.Kce : s.u.g.Kci) + (16 * bi + lr) * LDK;
+        // ---- B: Gram products.  Wavefront g forms product g (0 A, 1 L, 2 P1, 3 P2) for
+        //      the block pairs (0,0), (1,0) and (1,1) from 16 fragments read at once; rows
+        //      of block 1 are scaled by F for the off-diagonal pair -------------------------
+        {
+            const int g = wv;
             constexpr int NK = DK / M::K;
-            M::frag fr[NK], fc[NK];
+            const bf16* rows = g < 2 ? s.u.g.Kr : s.u.g.Qr;
+            const bf16* cols = (g & 1) == 0 ? s.u.g.Kce : s.u.g.Kci;
+            M::frag r0[NK], r1[NK], c0[NK], c1[NK], r1f[NK];
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
-                fr[kk] = M::loadr(rows + kk * M::K, lane);
-                fc[kk] = M::loadr(cols + kk * M::K, lane);
+                r0[kk] = M::loadr(rows + lr * LDK + kk * M::K, lane);
+                r1[kk] = M::loadr(rows + (16 + lr) * LDK + kk * M::K, lane);
+                c0[kk] = M::loadr(cols + lr * LDK + kk * M::K, lane);
+                c1[kk] = M::loadr(cols + (16 + lr) * LDK + kk * M::K, lane);
             }
-            if (bt != bi) {
-                const float* Fp = s.F + lg * M::KPL;
+            const float* Fp = s.F + lg * M::KPL;
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) fr[kk] = M::scale(fr[kk], Fp + kk * M::K);
-            }
-            f32x4 acc = zero4();
-            if (g == 1) {
+            for (int kk = 0; kk < NK; ++kk) r1f[kk] = M::scale(r1[kk], Fp + kk * M::K);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) acc = M::mma(fr[kk], fc[kk], acc);
-                // rows t = 16 bt + 4 lg + r, column i = 16 bi + lr; LbT[i] at permuted t
-                const int i = 16 * bi + lr, tt = 16 * bt + 4 * lg;
-                const float bi_ = s.beta[i];
-                f32x4 m;
+            for (int pr = 0; pr < 3; ++pr) {
+                const int bt = pr == 0 ? 0 : 1, bi = pr == 2 ? 1 : 0;
+                const M::frag* fr = pr == 0 ? r0 : (pr == 1 ? r1f : r1);
+                const M::frag* fc = bi == 0 ? c0 : c1;
+                f32x4 acc = zero4();
+                if (g == 1) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) m[r] = (i < tt + r) ? acc[r] * bi_ : 0.f;
-                store4(&s.LbT[i * LDC + kperm(tt)], m);
-            } else {
+                    for (int kk = 0; kk < NK; ++kk) acc = M::mma(fr[kk], fc[kk], acc);
+                    // rows t = 16 bt + 4 lg + r, column i = 16 bi + lr; LbT[i] at permuted t
+                    const int i = 16 * bi + lr, tt = 16 * bt + 4 * lg;
+                    const float bi_ = s.beta[i];
+                    f32x4 m;
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) acc = M::mma(fc[kk], fr[kk], acc);
-                // column t = 16 bt + lr, rows i = 16 bi + 4 lg + r
-                const int t = 16 * bt + lr, i0 = 16 * bi + 4 * lg;
-                f32x4 m;
+                    for (int r = 0; r < 4; ++r) m[r] = (i < tt + r) ? acc[r] * bi_ : 0.f;
+                    store4(&s.LbT[i * LDC + kperm(tt)], m);
+                } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) m[r] = (g == 0 ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f;
-                if (g == 0) *reinterpret_cast<f32x4*>(&s.A[t * LDA + i0]) = s.beta[t] * m;
-                else if (g == 2) store4(&s.P1[t * LDC + i0], m);
-                else *reinterpret_cast<f32x4*>(&s.P2b[t * LDA + i0]) =
-                         m * *reinterpret_cast<const f32x4*>(&s.beta[i0]);
+                    for (int kk = 0; kk < NK; ++kk) acc = M::mma(fc[kk], fr[kk], acc);
+                    // column t = 16 bt + lr, rows i = 16 bi + 4 lg + r
+                    const int t = 16 * bt + lr, i0 = 16 * bi + 4 * lg;
+                    f32x4 m;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m[r] = (g == 0 ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f;
+                    if (g == 0) *reinterpret_cast<f32x4*>(&s.A[t * LDA + i0]) = s.beta[t] * m;
+                    else if (g == 2) store4(&s.P1[t * LDC + i0], m);
+                    else *reinterpret_cast<f32x4*>(&s.P2b[t * LDA + i0]) =
+                             m * *reinterpret_cast<const f32x4*>(&s.beta[i0]);
+                }
             }
         }
         lds_barrier();
@@ -331,17 +435,27 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
                 t = __builtin_amdgcn_mfma_f32_16x16x4f32(s.u.v.Tf[(16 + lr) * LDA + 16 + kk], s.u.v.Xs[kk * 17 + lr], t,
                                                          0, 0, 0);
             }
+            // T21 = -t: rows 16 + 4 lg + r, column lr.  Tb = T diag(b) at permuted
+            // columns; Tb^T rows are columns of T (four consecutive rows here)
+            const float bcol = s.beta[lr];
+            f32x4 tb;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s.u.v.Tf[(16 + 4 * lg + r) * LDA + lr] = -t[r];
-        }
-        lds_barrier();
-        // Tb = T diag(b) at permuted columns, and its transpose at natural columns
+            for (int r = 0; r < 4; ++r) {
+                tb[r] = -t[r] * bcol;
+                s.Tb[(16 + 4 * lg + r) * LDC + kperm(lr)] = (bf16)tb[r];
+            }
+            store4(&s.TbT[lr * LDC + 16 + 4 * lg], tb);
+        } else {
+            // diagonal blocks on wavefronts 1-3: (block, row t, column run 4 u .. 4 u + 3)
+            for (int e = tid - 64; e < 128; e += 192) {
+                const int bb = e >> 6, t = (e >> 2) & 15, u = e & 3;
+                const int row = 16 * bb + t, col = 16 * bb + 4 * u;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&s.u.v.Tf[row * LDA + col]) *
+                                *reinterpret_cast<const f32x4*>(&s.beta[col]);
+                store4(&s.Tb[row * LDC + kperm(col)], x);
 #pragma unroll
-        for (int e = tid; e < C * C; e += NT) {
-            const int t = e >> 5, s_ = e & 31;
-            const float x = (s_ <= t) ? s.u.v.Tf[t * LDA + s_] * s.beta[s_] : 0.f;
-            s.Tb[t * LDC + kperm(s_)] = (bf16)x;
-            s.TbT[s_ * LDC + t] = (bf16)x;
+                for (int r = 0; r < 4; ++r) s.TbT[(col + r) * LDC + row] = (bf16)x[r];
+            }
         }
         lds_barrier();
 
