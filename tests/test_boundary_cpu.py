@@ -129,8 +129,9 @@ def test_workspace_sizes(lib):
     block = (least.value - state) // units
     assert block % 256 == 0 and size.value >= least.value and (size.value - state) % (units * block) == 0
     assert (size.value - state) <= (4 << 30)  # segments of at most 4 GiB of blocks
-    chunks = 32768 // 32
-    assert size.value - state == units * block * chunks  # this batch fits one segment
+    d.max_seqlen = 32768  # with the longest sequence known, this batch fits one segment
+    assert lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(size)) == OK
+    assert size.value - state == units * block * (32768 // 32)
     d = dims(method=1)
     assert lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(size)) == OK and size.value == 0
     d = dims(qkv_dtype=0, dk=64, dv=64)  # fp32 runs single-pass only
