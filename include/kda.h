@@ -131,6 +131,33 @@ KDA_API int kda_chunk_fwd(const kda_dims_t* dims, const void* q, const void* k, 
                   size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked prefill that also exports the state at regular positions of every
+ * sequence, for prefix reuse and checkpointing: the state is the only record
+ * of the tokens before it, so a continuation from a shared prefix needs a
+ * stored copy (glossary page "Linear attention", section "Why it matters").
+ *   snapshot_every  L: tokens between snapshots, > 0 and a multiple of the
+ *                   chunk size (32, or 64 with chunk_size = 64).
+ *   snapshots       [R, H, dk, dv] float32 (4-byte aligned), not aliasing any
+ *                   other argument.  Sequence n of length len_n contributes
+ *                   floor(len_n / L) rows, in sequence order: its row s is the
+ *                   state after its first (s + 1) L tokens, at row
+ *                   P_n + s with P_n = sum over m < n of floor(len_m / L).
+ *                   The row for s = floor(len_n / L) - 1 equals S_T when L
+ *                   divides len_n.  Each row is exactly what S_T of a call on
+ *                   that prefix returns (same method, chunk and split).
+ *   snapshot_rows   R, the rows the buffer holds.  Rows at or past R are not
+ *                   written (the lengths are on the device, so the host
+ *                   cannot check R against P_N).
+ * All other arguments and the error behaviour are those of kda_chunk_fwd,
+ * which is this call with snapshots = NULL and snapshot_every = 0.
+ */
+KDA_API int kda_chunk_fwd_snapshots(const kda_dims_t* dims, const void* q, const void* k, const void* v,
+                            const float* log_a, const float* beta, const float* S0,
+                            const int32_t* cu_seqlens, void* o, float* S_T, float* snapshots,
+                            int64_t snapshot_rows, int64_t snapshot_every, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * Workspace the two-pass prefill prefers for these dims (segments of up to
  * 4 GiB of operator blocks: about 1.2 KB per token and head at dk = 128, so a
  * whole 2 x 32-head x 32K-token batch runs as one segment), or 0 if the call

@@ -7,6 +7,8 @@ runs in the library's HIP kernels.  There is no CPU or PyTorch fallback: if
 the library or a GPU is missing, calls raise.
 
     o, S_T = chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None)
+    o, S_T, snaps = chunk_fwd_snapshots(q, k, v, log_a, beta, S0, cu_seqlens,
+                                        snapshot_every=1024)   # prefix states
     o, S   = decode_step(q, k, v, log_a, beta, S)        # S updated in place
 
 Shapes (tokens of all sequences packed along the first axis):
@@ -22,7 +24,7 @@ import threading
 
 import torch  # loads the HIP runtime the library then shares
 
-__all__ = ["chunk_fwd", "chunk_workspace_size", "decode_step", "KdaError", "library_path", "load_library",
+__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "snapshot_rows", "chunk_workspace_size", "decode_step", "KdaError", "library_path", "load_library",
            "METHOD_AUTO", "METHOD_SINGLE", "METHOD_TWO_PASS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -69,6 +71,9 @@ def load_library(build_if_missing: bool = True):
             lib.kda_chunk_fwd.restype = ctypes.c_int
             lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P,
                                           ctypes.c_size_t, P]
+            lib.kda_chunk_fwd_snapshots.restype = ctypes.c_int
+            lib.kda_chunk_fwd_snapshots.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P,
+                                                    ctypes.c_int64, ctypes.c_int64, P, ctypes.c_size_t, P]
             for name in ("kda_chunk_workspace_size", "kda_chunk_workspace_min"):
                 fn = getattr(lib, name)
                 fn.restype = ctypes.c_int
@@ -133,6 +138,57 @@ def chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, chunk_size: int
     to have one of the library's preferred size allocated (torch's caching
     allocator) for this call.  max_seqlen bounds the longest sequence (with
     cu_seqlens); when None it is read from cu_seqlens, which synchronises."""
+    o, ST, _ = _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state,
+                        num_seqs, method, workspace, max_seqlen, 0, None)
+    return o, ST
+
+
+def snapshot_rows(cu_seqlens, snapshot_every: int, *, total_tokens: int | None = None,
+                  num_seqs: int | None = None) -> int:
+    """Rows of the snapshot buffer a call needs: the sum over sequences of
+    floor(len / snapshot_every).  From cu_seqlens (read on the host, which
+    synchronises when it is a device tensor) or from equal lengths
+    total_tokens / num_seqs."""
+    L = int(snapshot_every)
+    if L <= 0:
+        raise ValueError("snapshot_every must be > 0")
+    if cu_seqlens is None:
+        n = 1 if num_seqs is None else int(num_seqs)
+        return 0 if n == 0 else n * ((int(total_tokens) // n) // L)
+    cu = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    return sum((b - a) // L for a, b in zip(cu[:-1], cu[1:]))
+
+
+def chunk_fwd_snapshots(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, snapshot_every: int,
+                        snapshots=None, chunk_size: int = 0, dv_split: int = 0, out=None, final_state=True,
+                        num_seqs: int | None = None, method: int = METHOD_AUTO, workspace=None,
+                        max_seqlen: int | None = None):
+    """chunk_fwd that also returns the state after every `snapshot_every` tokens
+    of each sequence: (o, S_T or None, snapshots [R, H, dk, dv] float32).
+
+    Sequence n contributes floor(len_n / snapshot_every) rows, in sequence
+    order; its row s is the state after its first (s + 1) * snapshot_every
+    tokens.  snapshot_every must be a multiple of the chunk size.  Pass a
+    float32 tensor as `snapshots` to choose R (rows past R are not written),
+    or leave it None to allocate exactly the rows needed (snapshot_rows, which
+    reads cu_seqlens on the host)."""
+    _need(q, "q", ndim=3)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if snapshots is None:
+        N = (cu_seqlens.shape[0] - 1) if cu_seqlens is not None else (1 if num_seqs is None else int(num_seqs))
+        R = snapshot_rows(cu_seqlens, snapshot_every, total_tokens=T, num_seqs=N)
+        snapshots = torch.empty((R, H, dk, dv), dtype=torch.float32, device=q.device)
+    else:
+        _need(snapshots, "snapshots", torch.float32, 4)
+        if snapshots.shape[1:] != (H, dk, dv):
+            raise ValueError(f"snapshots must be [R,{H},{dk},{dv}] (got {tuple(snapshots.shape)})")
+    return _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state, num_seqs,
+                    method, workspace, max_seqlen, int(snapshot_every), snapshots)
+
+
+def _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state, num_seqs,
+             method, workspace, max_seqlen, snapshot_every, snapshots):
     lib = load_library()
     _need(q, "q", ndim=3)
     T, H, dk = q.shape
@@ -183,12 +239,20 @@ def chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, chunk_size: int
             workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, 1)
-    st = lib.kda_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
-                           _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(ST), _ptr(workspace),
-                           ctypes.c_size_t(0 if workspace is None else workspace.numel()),
-                           _stream_handle(q.device))
+    ws_bytes = ctypes.c_size_t(0 if workspace is None else workspace.numel())
+    if snapshots is None:
+        st = lib.kda_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
+                               _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(ST), _ptr(workspace), ws_bytes,
+                               _stream_handle(q.device))
+    else:
+        rows = snapshots.shape[0]
+        st = lib.kda_chunk_fwd_snapshots(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
+                                         _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(ST),
+                                         _ptr(snapshots) if rows > 0 else None, ctypes.c_int64(rows),
+                                         ctypes.c_int64(snapshot_every), _ptr(workspace), ws_bytes,
+                                         _stream_handle(q.device))
     _check(lib, st)
-    return o, ST
+    return o, ST, snapshots
 
 
 def chunk_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, dv_split=0,

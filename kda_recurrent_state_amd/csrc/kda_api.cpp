@@ -189,10 +189,39 @@ int kda_chunk_fwd(const kda_dims_t* d, const void* q, const void* k, const void*
                   const float* log_a, const float* beta, const float* S0,
                   const int32_t* cu_seqlens, void* o, float* S_T, void* workspace,
                   size_t workspace_bytes, void* stream) {
+    return kda_chunk_fwd_snapshots(d, q, k, v, log_a, beta, S0, cu_seqlens, o, S_T, nullptr, 0, 0, workspace,
+                                   workspace_bytes, stream);
+}
+
+int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, const void* v,
+                            const float* log_a, const float* beta, const float* S0,
+                            const int32_t* cu_seqlens, void* o, float* S_T, float* snapshots,
+                            int64_t snapshot_rows, int64_t snapshot_every, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     Plan pl;
     int st = plan_prefill(d, cu_seqlens != nullptr, &pl);
     if (st) return st;
     const int chunk = pl.chunk;
+    if (snapshot_every < 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "snapshot_every = %lld < 0", (long long)snapshot_every);
+    if (snapshot_every == 0 && snapshots && snapshot_rows > 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "a snapshot buffer needs snapshot_every > 0");
+    if (snapshot_every > 0) {
+        if (snapshot_every % chunk)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "snapshot_every = %lld is not a multiple of the chunk size %d",
+                        (long long)snapshot_every, chunk);
+        if (snapshot_every > 0x7fffffff)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "snapshot_every = %lld is too large", (long long)snapshot_every);
+        if (snapshot_rows < 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "snapshot_rows = %lld < 0", (long long)snapshot_rows);
+        if (snapshot_rows > 0 && !snapshots)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "snapshots is NULL but snapshot_rows = %lld",
+                        (long long)snapshot_rows);
+        if (snapshots && ((uintptr_t)snapshots & 3u))
+            return fail(KDA_ERR_MISALIGNED, "snapshots is not 4-byte aligned");
+    }
+    // no snapshot rows to write: the plain prefill
+    if (snapshot_every == 0 || snapshot_rows == 0) { snapshots = nullptr; snapshot_every = 0; snapshot_rows = 0; }
     if (d->num_seqs == 0) {
         if (d->total_tokens != 0)
             return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs = 0 but total_tokens = %lld",
@@ -251,7 +280,8 @@ int kda_chunk_fwd(const kda_dims_t* d, const void* q, const void* k, const void*
             sa.v = v; sa.o = o; sa.cu_seqlens = cu_seqlens; sa.eq_len = eq_len; sa.ws = blocks;
             sa.S_in = sgi == 0 ? S0 : run; sa.S_out = run; sa.num_heads = d->num_heads; sa.units = pl.units;
             sa.dk = d->dk; sa.dv = d->dv; sa.split = pl.split; sa.m = (int32_t)m; sa.chunk = chunk;
-            sa.chunk0 = chunk0;
+            sa.chunk0 = chunk0; sa.snap = snapshots; sa.snap_rows = snapshot_rows;
+            sa.snap_every = (int32_t)snapshot_every;
             e = kda::launch_scan(sa, (hipStream_t)stream);
             if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill state pass launch: %s", hipGetErrorString(e));
         }
@@ -278,6 +308,7 @@ int kda_chunk_fwd(const kda_dims_t* d, const void* q, const void* k, const void*
     a.num_seqs = d->num_seqs; a.num_heads = d->num_heads; a.total_tokens = d->total_tokens;
     a.dk = d->dk; a.dv = d->dv; a.dtype = d->qkv_dtype; a.scalar_decay = d->scalar_decay;
     a.chunk = chunk; a.split = split;
+    a.snap = snapshots; a.snap_rows = snapshot_rows; a.snap_every = (int32_t)snapshot_every;
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return ok();

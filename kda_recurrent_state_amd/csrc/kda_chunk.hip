@@ -112,6 +112,9 @@ struct ChunkParams {
     float* ST;
     int H, DV, split, xcd_group;
     int64_t eq_len;  // used when cu is null
+    float* snap;     // state snapshots [rows][H][DK][DV], or null
+    int64_t snap_rows;
+    int snap_every;  // tokens between snapshots (a multiple of C)
 };
 
 // Raw inputs of one 4-token x 2-channel unit, held in registers one chunk ahead.
@@ -226,6 +229,16 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
             }
             store4(&s.ST[(16 * ni + lrow) * LDK + 16 * mi + 4 * lgrp], acc[i]);
         }
+    }
+
+    // snapshots: the state after every snap_every tokens goes to row
+    // snap0 + (tokens / snap_every) - 1; snap_cd counts the chunks to the next
+    int64_t snap0 = 0;
+    int snap_ec = 1, snap_cd = 0;
+    if (p.snap) {
+        snap0 = snapshots_before(p.cu, p.eq_len, n, p.snap_every);
+        snap_ec = p.snap_every / C;
+        snap_cd = snap_ec;
     }
 
     UnitIn<T> ui[G::UPT];
@@ -492,6 +505,22 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 store4(&s.ST[(16 * ni + lrow) * LDK + 16 * mi + 4 * lgrp], acc[i]);
             }
         }
+        if (p.snap && --snap_cd == 0) {
+            snap_cd = snap_ec;
+            const int64_t done = t0 + C - tb;  // tokens of the sequence behind this state
+            const int64_t row = snap0 + done / p.snap_every - 1;
+            if (done <= te - tb && row < p.snap_rows) {
+                float* dst = p.snap + (row * H + h) * DK * DV + dv0 + lrow;
+#pragma unroll
+                for (int i = 0; i < G::STPW; ++i) {
+                    const int ix = wv + NW * i;
+                    if (ix < G::NST) {
+                        const int mi = ix / (DVS / 16), ni = ix % (DVS / 16);
+                        store_state_tile(dst + (int64_t)16 * mi * DV + 16 * ni, DV, lgrp, acc[i]);
+                    }
+                }
+            }
+        }
         lds_barrier();
     }
 
@@ -522,6 +551,7 @@ static hipError_t launch_cfg(const ChunkArgs& a, hipStream_t stream) {
     p.cu = a.cu_seqlens; p.o = a.o; p.ST = a.S_T;
     p.H = a.num_heads; p.DV = a.dv; p.split = a.split;
     p.eq_len = a.cu_seqlens ? 0 : a.total_tokens / (a.num_seqs > 0 ? a.num_seqs : 1);
+    p.snap = a.snap; p.snap_rows = a.snap_rows; p.snap_every = a.snap_every;
     const int64_t blocks = (int64_t)a.num_seqs * a.num_heads * a.split;
     p.xcd_group = (blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
     hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC>), dim3((unsigned)blocks), dim3(ChunkCfg<T, DK, DVS, C>::NT), 0,

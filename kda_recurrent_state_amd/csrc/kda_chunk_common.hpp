@@ -48,6 +48,27 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// Snapshot rows of the sequences before sequence n: the sum over m < n of
+// floor(len_m / every).  Called by whole wavefronts (lanes stride over the
+// sequences, then a butterfly sum); the result is the same in every lane.
+// cu null: every sequence has eq_len tokens.
+__device__ inline int64_t snapshots_before(const int32_t* cu, int64_t eq_len, int n, int every) {
+    if (!cu) return (int64_t)n * (eq_len / every);
+    int64_t s = 0;
+    for (int m = (int)(threadIdx.x & 63); m < n; m += 64) s += (cu[m + 1] - cu[m]) / every;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    return s;
+}
+
+// Stores one 16 x 16 fp32 accumulator tile (column lane % 16, rows
+// 4 (lane / 16) .. + 3) of a state slice into a row-major [dk][dv] state;
+// dst points at the tile's first row and this lane's column.
+__device__ __forceinline__ void store_state_tile(float* dst, int64_t DV, int lg, f32x4 t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(int64_t)(4 * lg + i) * DV] = t[i];
+}
+
 __device__ __forceinline__ float uniform(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }

@@ -24,6 +24,9 @@ struct ChunkArgs {
     int32_t scalar_decay;
     int32_t chunk;              // 32 or 64
     int32_t split;              // workgroups per (sequence, head) along dv
+    float* snap;                // state snapshots [rows, H, dk, dv], or null
+    int64_t snap_rows;
+    int32_t snap_every;         // tokens between snapshots (a multiple of chunk), 0 = none
 };
 
 bool decode_supported(int dtype, int dk, int dv);
@@ -63,6 +66,9 @@ struct ScanLaunch {
     int64_t units;
     int32_t dk, dv, split, m, chunk;
     int64_t chunk0;
+    float* snap;                // as in ChunkArgs
+    int64_t snap_rows;
+    int32_t snap_every;
 };
 int prep_block_bytes(int dk, int chunk);  // 0 if no prep kernel for (dk, chunk)
 hipError_t launch_prep(const PrepLaunch& a, hipStream_t stream);

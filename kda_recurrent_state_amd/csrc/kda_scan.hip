@@ -65,6 +65,9 @@ struct ScanParams {
     float* S_out;
     int H, DV, split, m, xcd_group;
     int64_t chunk0;
+    float* snap;          // state snapshots [rows][H][DK][DV], or null
+    int64_t snap_rows;
+    int snap_every;       // tokens between snapshots (a multiple of C)
 };
 
 // Ends a chunk: waits until at most N vector-memory operations of this
@@ -197,6 +200,16 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB>::NT), 1) kda_scan_kernel
     };
     make_sfr();
 
+    // snapshots: the state after every snap_every tokens of the sequence goes to
+    // row snap0 + (tokens / snap_every) - 1; snap_cd counts the chunks to the next
+    int64_t snap0 = 0;
+    int snap_ec = 1, snap_cd = 0;
+    if (p.snap) {
+        snap0 = snapshots_before(p.cu, p.eq_len, n, p.snap_every);
+        snap_ec = p.snap_every / C;
+        snap_cd = snap_ec - (int)(p.chunk0 % snap_ec);
+    }
+
     slot_barrier<0>();
 
     // outputs of the chunk just computed (bf16, rows past the chunk end skipped)
@@ -318,6 +331,19 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB>::NT), 1) kda_scan_kernel
         __builtin_amdgcn_sched_barrier(0);
         make_sfr();
 
+        if (p.snap && --snap_cd == 0) {
+            snap_cd = snap_ec;
+            const int64_t done = (p.chunk0 + jj + 1) * C;  // tokens of the sequence behind this state
+            const int64_t row = snap0 + done / p.snap_every - 1;
+            if (done <= te - tb && row < p.snap_rows) {
+                float* dst = p.snap + (row * H + h) * DK * DV + dv0 + 16 * wv * CB + lr;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) store_state_tile(dst + 16 * cb + (int64_t)16 * r * DV, DV, lg, acc[cb][r]);
+            }
+        }
+
         o_t0 = tb + (p.chunk0 + jj) * C;
         o_Lc = (int)((te - o_t0) < C ? (te - o_t0) : C);
         store_o();
@@ -338,6 +364,7 @@ static hipError_t scan_cfg(const ScanLaunch& a, hipStream_t stream) {
     p.v = a.v; p.o = a.o; p.cu = a.cu_seqlens; p.eq_len = a.eq_len;
     p.ws = static_cast<const uint8_t*>(a.ws); p.S_in = a.S_in; p.S_out = a.S_out;
     p.H = a.num_heads; p.DV = a.dv; p.split = a.split; p.m = a.m; p.chunk0 = a.chunk0;
+    p.snap = a.snap; p.snap_rows = a.snap_rows; p.snap_every = a.snap_every;
     const int64_t blocks = (int64_t)a.units * a.split;
     p.xcd_group = (a.split > 1 && blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
     hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, CB>), dim3((unsigned)blocks), dim3(ScanCfg<DK, DVS, CB>::NT), 0,

@@ -64,3 +64,24 @@ def decode_as_sequence(inp):
     out = dict(q=tr(inp["q"]), k=tr(inp["k"]), v=tr(inp["v"]), log_a=tr(inp["log_a"]),
                beta=tr(inp["beta"]), S0=inp["S"], cu_seqlens=torch.tensor(cu, dtype=torch.int32))
     return out, steps, N
+
+
+def oracle_snapshots(inp, every, n, h=None):
+    """Oracle states of sequence n after each whole `every` tokens: [R_n, H, dk, dv]
+    (or [R_n, dk, dv] for one head h).  The recurrence is run piece by piece,
+    each piece of `every` tokens starting from the fp64 state the previous one
+    ended with, which is the token-by-token recurrence itself cut at those points."""
+    cu = inp["cu_seqlens"].cpu().numpy()
+    s, e = int(cu[n]), int(cu[n + 1])
+    hs = slice(None) if h is None else slice(h, h + 1)
+    S0 = inp.get("S0")
+    S = None if S0 is None else np64(S0[n:n + 1, hs])
+    out = []
+    for p in range((e - s) // every):
+        a, b = s + p * every, s + (p + 1) * every
+        sl = lambda t: t[a:b, hs]
+        _, S = kda_oracle(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["log_a"]), sl(inp["beta"]), S0=S)
+        out.append(S[0] if h is None else S[0, 0])
+    q = inp["q"]
+    shape = ((q.shape[1],) if h is None else ()) + (q.shape[2], inp["v"].shape[2])
+    return np.stack(out) if out else np.zeros((0,) + shape)

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    assert {"kda_chunk_fwd", "kda_chunk_workspace_size", "kda_chunk_workspace_min", "kda_decode_step",
+    assert {"kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_chunk_workspace_size", "kda_chunk_workspace_min", "kda_decode_step",
             "kda_status_string", "kda_last_error", "kda_version"} <= set(names)
 
 
@@ -99,6 +99,31 @@ def test_prefill_validation(lib, case, expect):
         assert lib.kda_last_error().decode() == ""
 
 
+def prefill_snap(lib, d, snaps=GOOD, rows=4, every=64, cu=GOOD):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_chunk_fwd_snapshots(ctypes.byref(d), P(GOOD), P(GOOD), P(GOOD), P(GOOD), P(GOOD), None,
+                                       P(cu), P(GOOD), P(GOOD), P(snaps), ctypes.c_int64(rows),
+                                       ctypes.c_int64(every), None, ctypes.c_size_t(0), None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(every=48), INVALID),                          # not a multiple of the chunk (32)
+    (dict(every=32, d=dims(chunk_size=64)), INVALID),   # not a multiple of the chunk (64)
+    (dict(every=-32), INVALID),
+    (dict(every=0), INVALID),                           # a buffer but no interval
+    (dict(snaps=None), INVALID),                        # rows but no buffer
+    (dict(rows=-1), INVALID),
+    (dict(snaps=GOOD + 2), MISALIGNED),
+    (dict(every=1 << 40), INVALID),
+    (dict(d=dims(num_seqs=0, total_tokens=0)), OK),     # nothing to do
+    (dict(d=dims(num_seqs=0, total_tokens=0), every=0, snaps=None, rows=0), OK),
+])
+def test_snapshot_validation(lib, case, expect):
+    case.setdefault("d", dims())
+    st = prefill_snap(lib, **case)
+    assert st == expect, (st, lib.kda_last_error())
+
+
 @pytest.mark.parametrize("case,expect", [
     (dict(d=dims(total_tokens=3)), INVALID),
     (dict(d=dims(total_tokens=2), Si=None), INVALID),
@@ -150,3 +175,11 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 1, 32)
     with pytest.raises(RuntimeError, match="HIP device"):
         kda.chunk_fwd(x, x, x, torch.zeros(4, 1, 32), torch.zeros(4, 1))
+
+
+def test_snapshot_rows_counts_whole_intervals():
+    assert kda.snapshot_rows([0, 300, 307, 435, 435, 596], 64) == 4 + 0 + 2 + 0 + 2
+    assert kda.snapshot_rows(None, 64, total_tokens=640, num_seqs=2) == 2 * 5
+    assert kda.snapshot_rows(None, 64, total_tokens=0, num_seqs=0) == 0
+    with pytest.raises(ValueError):
+        kda.snapshot_rows([0, 10], 0)
