@@ -84,7 +84,9 @@ __device__ __forceinline__ void slot_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int DK, int DVS, int CB>
+// SNAP: the call asks for state snapshots (a separate instantiation, so that
+// the plain walk carries no snapshot code).
+template <int DK, int DVS, int CB, bool SNAP>
 __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB>::NT), 1) kda_scan_kernel(ScanParams p) {
     typedef ScanCfg<DK, DVS, CB> G;
     typedef WsBlock<DK, G::C> WS;
@@ -204,7 +206,7 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB>::NT), 1) kda_scan_kernel
     // row snap0 + (tokens / snap_every) - 1; snap_cd counts the chunks to the next
     int64_t snap0 = 0;
     int snap_ec = 1, snap_cd = 0;
-    if (p.snap) {
+    if (SNAP) {
         snap0 = snapshots_before(p.cu, p.eq_len, n, p.snap_every);
         snap_ec = p.snap_every / C;
         snap_cd = snap_ec - (int)(p.chunk0 % snap_ec);
@@ -331,7 +333,7 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB>::NT), 1) kda_scan_kernel
         __builtin_amdgcn_sched_barrier(0);
         make_sfr();
 
-        if (p.snap && --snap_cd == 0) {
+        if (SNAP && --snap_cd == 0) {
             snap_cd = snap_ec;
             const int64_t done = (p.chunk0 + jj + 1) * C;  // tokens of the sequence behind this state
             const int64_t row = snap0 + done / p.snap_every - 1;
@@ -367,8 +369,12 @@ static hipError_t scan_cfg(const ScanLaunch& a, hipStream_t stream) {
     p.snap = a.snap; p.snap_rows = a.snap_rows; p.snap_every = a.snap_every;
     const int64_t blocks = (int64_t)a.units * a.split;
     p.xcd_group = (a.split > 1 && blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
-    hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, CB>), dim3((unsigned)blocks), dim3(ScanCfg<DK, DVS, CB>::NT), 0,
-                       stream, p);
+    if (a.snap)
+        hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, CB, true>), dim3((unsigned)blocks),
+                           dim3(ScanCfg<DK, DVS, CB>::NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, CB, false>), dim3((unsigned)blocks),
+                           dim3(ScanCfg<DK, DVS, CB>::NT), 0, stream, p);
     return hipGetLastError();
 }
 
