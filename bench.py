@@ -6,13 +6,16 @@ clipped to [-8, 0], fp32 state); `value` is prefill tokens/s (each token
 counted once across heads).  The decode leg (256 sequences x 32 heads,
 dk=dv=128, 100 chained steps, fp32 state streamed once per step) is timed in
 the same run and reported under "decode" in state GB/s.  All inputs are seeded
-synthetic tensors, resident on the GPU before timing starts.
+synthetic tensors, resident on the GPU before timing starts.  The same
+prefill batch is also timed with state snapshots every 1024 tokens and with
+the decay-first ordering, and the decode leg with the decay-first ordering
+("variants", "decode.decay_first").
 
 Timing uses HIP events recorded on the stream the kernels are launched on
 (torch's current stream, which the library receives).  The fp64 CPU oracle is
 timed afterwards on a bounded sample of the same prefill workload.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-variants]
     python bench.py --copy-calibration   # plain device copy of known size, for counters
     python bench.py --record-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
         # writes profiles/traffic_counters.json from four rocprofv3 --pmc output
@@ -176,6 +179,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the snapshot and decay-first legs")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
     ap.add_argument("--method", choices=["auto", "single", "two-pass"], default="auto")
@@ -274,6 +278,54 @@ def main():
         log(f"prefill: {per*1e3:.3f} ms/step, {tokens/per/1e6:.2f} Mtok/s, {gbs:.0f} GB/s, "
             f"{tflops:.1f} TFLOP/s, parity {perr:.2e}")
 
+        if not args.no_variants:
+            # the same batch through the two other prefill entries: state snapshots every
+            # 1024 tokens (written into a preallocated buffer), and the decay-first order
+            vsteps = args.steps
+            every = 1024
+            rows = kda.snapshot_rows(None, every, total_tokens=tokens, num_seqs=wp.n_seqs)
+            snaps = torch.empty((rows, wp.heads, wp.dk, wp.dv), dtype=torch.float32, device=dev)
+
+            def snap_step():
+                kda.chunk_fwd_snapshots(x["q"], x["k"], x["v"], x["log_a"], x["beta"], S0=x["S0"],
+                                        cu_seqlens=x["cu_seqlens"], snapshot_every=every, snapshots=snaps,
+                                        out=o, final_state=ST, method=method, workspace=ws,
+                                        max_seqlen=wp.seqlen)
+            # each leg warms up like the main one: the clocks drop during the host-side
+            # parity check before it
+            for _ in range(max(args.warmup, 3)):
+                snap_step()
+            torch.cuda.synchronize()
+            ts = time_events(snap_step, vsteps, stream) / vsteps
+            del snaps
+            wsb1 = kda.chunk_workspace_size(x["q"], x["v"], num_seqs=wp.n_seqs, method=method,
+                                            max_seqlen=wp.seqlen, order=kda.ORDER_DECAY_FIRST)
+            ws1 = torch.empty(wsb1, dtype=torch.uint8, device=dev) if wsb1 else None
+
+            def d1_step():
+                kda.chunk_fwd(x["q"], x["k"], x["v"], x["log_a"], x["beta"], S0=x["S0"],
+                              cu_seqlens=x["cu_seqlens"], out=o, final_state=ST, method=method, workspace=ws1,
+                              max_seqlen=wp.seqlen, order=kda.ORDER_DECAY_FIRST)
+            for _ in range(max(args.warmup, 3)):
+                d1_step()
+            torch.cuda.synchronize()
+            t1 = time_events(d1_step, vsteps, stream) / vsteps
+            ro1, _ = kda_oracle(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_a"]), sl(x["beta"]),
+                                S0=x["S0"][0:1, 0:1].cpu(), order=1)
+            perr1 = float(np.abs(o[:2048, 0].double().cpu().numpy() - ro1[:, 0]).max() / np.abs(ro1).max())
+            del ws1
+            out["variants"] = {
+                "snapshots": {"snapshot_every": every, "rows": rows, "ms_per_step": ts * 1e3,
+                              "tokens_per_s": tokens / ts, "overhead_vs_plain": ts / per - 1.0,
+                              "snapshot_bytes": rows * wp.heads * wp.dk * wp.dv * 4},
+                "decay_first": {"ms_per_step": t1 * 1e3, "tokens_per_s": tokens / t1,
+                                "algorithmic_GBps": B / t1 / 1e9, "frac_hbm": B / t1 / 1e9 / PEAK_HBM_GBS,
+                                "workspace_MiB": round(wsb1 / 2**20, 1),
+                                "parity_o_max_rel_err": perr1, "tol": 2e-2},
+            }
+            log(f"prefill with snapshots every {every}: {ts*1e3:.3f} ms; decay-first: {t1*1e3:.3f} ms, "
+                f"parity {perr1:.2e}")
+
         if not args.no_cpu_baseline:
             ncpu = min(16, os.cpu_count() or 1)
             log(f"cpu oracle on the whole prefill batch, {ncpu} threads")
@@ -329,6 +381,21 @@ def main():
                          "avg_launch_us": per * 1e6},
         }
         log(f"decode: {per*1e6:.1f} us/step, {gbs:.0f} GB/s ({100*gbs/PEAK_HBM_GBS:.1f}% of HBM peak)")
+        if not args.no_variants:
+            def d1step():
+                i = ctr[0] % steps
+                ctr[0] += 1
+                kda.decode_step(y["q"][i], y["k"][i], y["v"][i], y["log_a"][i], y["beta"][i], S, out=od,
+                                order=kda.ORDER_DECAY_FIRST)
+            ctr[0] = 0
+            for _ in range(min(max(args.warmup, 3), steps)):
+                d1step()
+            torch.cuda.synchronize()
+            ctr[0] = 0
+            t1 = time_events(d1step, steps, stream) / steps
+            out["decode"]["decay_first"] = {"us_per_step": t1 * 1e6, "GBps": Bd / t1 / 1e9,
+                                            "frac_hbm": Bd / t1 / 1e9 / PEAK_HBM_GBS}
+            log(f"decode decay-first: {t1*1e6:.1f} us/step")
 
     print(json.dumps(out), flush=True)
 

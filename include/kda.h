@@ -10,7 +10,8 @@
  *
  * i.e. erase what S holds along the key k_t, decay every key row c of S by its
  * own a_t[c], then write beta_t k_t^T v_t; the output is the read after the
- * update, o_t = q_t S.  With one log_a value per (token, head) this is the
+ * update, o_t = q_t S.  kda_dims_t.order selects the variant that decays
+ * before it erases (kda_order_t below).  With one log_a value per (token, head) this is the
  * "Gated DeltaNet" row; with log_a = 0 it is the "Delta rule" row.
  *
  * Two entry points compute it:
@@ -81,6 +82,20 @@ typedef enum {
                                  workspace (kda_chunk_workspace_size); bf16 only */
 } kda_method_t;
 
+/*
+ * Order of decay and erase in the update.  The KDA row of the table (page "The
+ * argument, in one page", section "Everything, in one table") writes
+ * Diag(a)(I - beta k^T k) S: erase along k, then decay.  Gated delta-rule
+ * layers are also written with the decay applied to S first,
+ * (I - beta k^T k) Diag(a) S, so that the erase reads the decayed state; the
+ * two are the same map when a is one scalar per token and head
+ * (scalar_decay = 1), and differ with a per-channel a.
+ */
+typedef enum {
+    KDA_ORDER_ERASE_FIRST = 0,  /* S <- Diag(a)(I - beta k^T k) S + beta k^T v (the table's KDA row) */
+    KDA_ORDER_DECAY_FIRST = 1   /* S <- (I - beta k^T k) Diag(a) S + beta k^T v */
+} kda_order_t;
+
 typedef struct {
     int32_t num_seqs;     /* N: sequences (prefill) or sequences of one token (decode) */
     int32_t num_heads;    /* H */
@@ -96,7 +111,7 @@ typedef struct {
                              0 = choose from the problem size, else 1, 2, 4 or 8
                              (each slice dv / split must be 16, 32 or 64) */
     int32_t method;       /* prefill: kda_method_t */
-    int32_t reserved;     /* must be 0 */
+    int32_t order;        /* kda_order_t: where the decay sits in the update */
     int64_t max_seqlen;   /* prefill: an upper bound on the longest sequence, or 0 if
                              unknown (then total_tokens is assumed).  Used only to size
                              the two-pass workspace segments. */
@@ -137,7 +152,7 @@ KDA_API int kda_chunk_fwd(const kda_dims_t* dims, const void* q, const void* k, 
  * stored copy (glossary page "Linear attention", section "Why it matters").
  *   snapshot_every  L: tokens between snapshots, > 0 and a multiple of the
  *                   chunk size (32, or 64 with chunk_size = 64).
- *   snapshots       [R, H, dk, dv] float32 (4-byte aligned), not aliasing any
+ *   snapshots       [R, H, dk, dv] float32 (16-byte aligned), not aliasing any
  *                   other argument.  Sequence n of length len_n contributes
  *                   floor(len_n / L) rows, in sequence order: its row s is the
  *                   state after its first (s + 1) L tokens, at row

@@ -25,7 +25,7 @@ import threading
 import torch  # loads the HIP runtime the library then shares
 
 __all__ = ["chunk_fwd", "chunk_fwd_snapshots", "snapshot_rows", "chunk_workspace_size", "decode_step", "KdaError", "library_path", "load_library",
-           "METHOD_AUTO", "METHOD_SINGLE", "METHOD_TWO_PASS"]
+           "METHOD_AUTO", "METHOD_SINGLE", "METHOD_TWO_PASS", "ORDER_ERASE_FIRST", "ORDER_DECAY_FIRST"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -46,10 +46,14 @@ class _Dims(ctypes.Structure):
                 ("total_tokens", ctypes.c_int64), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("qkv_dtype", ctypes.c_int32), ("scalar_decay", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32), ("dv_split", ctypes.c_int32),
-                ("method", ctypes.c_int32), ("reserved", ctypes.c_int32), ("max_seqlen", ctypes.c_int64)]
+                ("method", ctypes.c_int32), ("order", ctypes.c_int32), ("max_seqlen", ctypes.c_int64)]
 
 
 METHOD_AUTO, METHOD_SINGLE, METHOD_TWO_PASS = 0, 1, 2
+# where the decay sits in the update (kda_order_t): the table's KDA row erases
+# first, S <- Diag(a)(I - b k^T k) S + b k^T v; DECAY_FIRST is
+# S <- (I - b k^T k) Diag(a) S + b k^T v.  Equal for a scalar decay.
+ORDER_ERASE_FIRST, ORDER_DECAY_FIRST = 0, 1
 
 
 def library_path() -> str:
@@ -126,7 +130,8 @@ def _stream_handle(device):
 
 def chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, chunk_size: int = 0,
               dv_split: int = 0, out=None, final_state=True, num_seqs: int | None = None,
-              method: int = METHOD_AUTO, workspace=None, max_seqlen: int | None = None):
+              method: int = METHOD_AUTO, workspace=None, max_seqlen: int | None = None,
+              order: int = ORDER_ERASE_FIRST):
     """Chunked prefill over packed sequences; returns (o, S_T or None).
 
     cu_seqlens: int32 device tensor [N+1], or None for num_seqs (default 1)
@@ -137,9 +142,10 @@ def chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, chunk_size: int
     needs device scratch: pass a uint8 tensor as `workspace`, or leave it None
     to have one of the library's preferred size allocated (torch's caching
     allocator) for this call.  max_seqlen bounds the longest sequence (with
-    cu_seqlens); when None it is read from cu_seqlens, which synchronises."""
+    cu_seqlens); when None it is read from cu_seqlens, which synchronises.
+    order: ORDER_ERASE_FIRST or ORDER_DECAY_FIRST."""
     o, ST, _ = _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state,
-                        num_seqs, method, workspace, max_seqlen, 0, None)
+                        num_seqs, method, workspace, max_seqlen, 0, None, order)
     return o, ST
 
 
@@ -162,7 +168,7 @@ def snapshot_rows(cu_seqlens, snapshot_every: int, *, total_tokens: int | None =
 def chunk_fwd_snapshots(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, snapshot_every: int,
                         snapshots=None, chunk_size: int = 0, dv_split: int = 0, out=None, final_state=True,
                         num_seqs: int | None = None, method: int = METHOD_AUTO, workspace=None,
-                        max_seqlen: int | None = None):
+                        max_seqlen: int | None = None, order: int = ORDER_ERASE_FIRST):
     """chunk_fwd that also returns the state after every `snapshot_every` tokens
     of each sequence: (o, S_T or None, snapshots [R, H, dk, dv] float32).
 
@@ -184,11 +190,11 @@ def chunk_fwd_snapshots(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, snaps
         if snapshots.shape[1:] != (H, dk, dv):
             raise ValueError(f"snapshots must be [R,{H},{dk},{dv}] (got {tuple(snapshots.shape)})")
     return _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state, num_seqs,
-                    method, workspace, max_seqlen, int(snapshot_every), snapshots)
+                    method, workspace, max_seqlen, int(snapshot_every), snapshots, order)
 
 
 def _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state, num_seqs,
-             method, workspace, max_seqlen, snapshot_every, snapshots):
+             method, workspace, max_seqlen, snapshot_every, snapshots, order):
     lib = load_library()
     _need(q, "q", ndim=3)
     T, H, dk = q.shape
@@ -230,7 +236,7 @@ def _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, fi
             max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
         else:
             max_seqlen = 0
-    d = _Dims(N, H, T, dk, dv, _dtype_code(q), scalar, int(chunk_size), int(dv_split), int(method), 0,
+    d = _Dims(N, H, T, dk, dv, _dtype_code(q), scalar, int(chunk_size), int(dv_split), int(method), int(order),
               int(max_seqlen))
     if workspace is None and method != METHOD_SINGLE:
         need = ctypes.c_size_t(0)
@@ -256,20 +262,20 @@ def _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, fi
 
 
 def chunk_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, dv_split=0,
-                         method=METHOD_AUTO, max_seqlen=0, minimum=False):
+                         method=METHOD_AUTO, max_seqlen=0, minimum=False, order=ORDER_ERASE_FIRST):
     """Bytes of workspace the prefill prefers (or, minimum=True, needs) for these
     shapes; 0 when it would run single-pass."""
     lib = load_library()
     T, H, dk = q.shape
     d = _Dims(int(num_seqs), H, T, dk, v.shape[2], _dtype_code(q), int(bool(scalar_decay)), int(chunk_size),
-              int(dv_split), int(method), 0, int(max_seqlen))
+              int(dv_split), int(method), int(order), int(max_seqlen))
     need = ctypes.c_size_t(0)
     fn = lib.kda_chunk_workspace_min if minimum else lib.kda_chunk_workspace_size
     _check(lib, fn(ctypes.byref(d), ctypes.byref(need)))
     return need.value
 
 
-def decode_step(q, k, v, log_a, beta, S, *, out=None, S_out=None):
+def decode_step(q, k, v, log_a, beta, S, *, out=None, S_out=None, order: int = ORDER_ERASE_FIRST):
     """One token per sequence: q, k [N,H,dk], v [N,H,dv], log_a [N,H,dk] or
     [N,H], beta [N,H], S [N,H,dk,dv].  Updates S in place unless S_out is
     given; returns (o, state_after)."""
@@ -294,7 +300,7 @@ def decode_step(q, k, v, log_a, beta, S, *, out=None, S_out=None):
     _need(So, "S_out", torch.float32)
     o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     _need(o, "out", q.dtype)
-    d = _Dims(N, H, N, dk, dv, _dtype_code(q), scalar, 0, 0, 0, 0, 0)
+    d = _Dims(N, H, N, dk, dv, _dtype_code(q), scalar, 0, 0, 0, int(order), 0)
     st = lib.kda_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
                              _ptr(S), _ptr(So), _ptr(o), _stream_handle(q.device))
     _check(lib, st)

@@ -46,6 +46,8 @@ int check_dims(const kda_dims_t* d) {
         return fail(KDA_ERR_INVALID_ARGUMENT, "qkv_dtype = %d is not KDA_F32 or KDA_BF16", d->qkv_dtype);
     if (d->scalar_decay != 0 && d->scalar_decay != 1)
         return fail(KDA_ERR_INVALID_ARGUMENT, "scalar_decay = %d is not 0 or 1", d->scalar_decay);
+    if (d->order != KDA_ORDER_ERASE_FIRST && d->order != KDA_ORDER_DECAY_FIRST)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "order = %d is not a kda_order_t", d->order);
     if (!width_ok(d->dk) || !width_ok(d->dv))
         return fail(KDA_ERR_UNSUPPORTED, "dk = %d, dv = %d: each must be 16, 32, 64 or 128", d->dk, d->dv);
     return KDA_OK;
@@ -74,6 +76,10 @@ int choose_split(const kda_dims_t* d, int chunk) {
     }
     return best;
 }
+
+// Order the kernels run: with one decay value per token and head the two
+// orders are the same map, and the erase-first kernels serve both.
+int kernel_order(const kda_dims_t* d) { return d->scalar_decay ? 0 : d->order; }
 
 // Plan of a prefill call: which method, chunk, split and, for the two-pass
 // method, the workspace layout [states of all units][operator blocks].
@@ -114,7 +120,6 @@ int plan_prefill(const kda_dims_t* d, bool have_cu, Plan* pl) {
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size = %d: must be 0, 32 or 64", d->chunk_size);
     if (d->method < KDA_METHOD_AUTO || d->method > KDA_METHOD_TWO_PASS)
         return fail(KDA_ERR_INVALID_ARGUMENT, "method = %d is not a kda_method_t", d->method);
-    if (d->reserved != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "reserved = %d must be 0", d->reserved);
     if (d->max_seqlen < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "max_seqlen = %lld < 0", (long long)d->max_seqlen);
     if (d->dv_split != 0 && d->dv_split != 1 && d->dv_split != 2 && d->dv_split != 4 && d->dv_split != 8)
@@ -130,7 +135,7 @@ int plan_prefill(const kda_dims_t* d, bool have_cu, Plan* pl) {
     if (split2 == 0) split2 = choose_split_two_pass(d, pl->chunk);
     else if (d->dv % split2 || !kda::two_pass_supported(d->qkv_dtype, d->dk, d->dv / split2, pl->chunk))
         split2 = 0;
-    pl->block = (size_t)kda::prep_block_bytes(d->dk, pl->chunk);
+    pl->block = (size_t)kda::prep_block_bytes(d->dk, pl->chunk, kernel_order(d));
     pl->two_pass_ok = split2 > 0 && pl->block > 0 && d->method != KDA_METHOD_SINGLE;
     if (d->method == KDA_METHOD_TWO_PASS && !pl->two_pass_ok)
         return fail(KDA_ERR_UNSUPPORTED, "no two-pass prefill for dtype %d, dk %d, dv %d, chunk %d, dv_split %d",
@@ -217,8 +222,8 @@ int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, c
         if (snapshot_rows > 0 && !snapshots)
             return fail(KDA_ERR_INVALID_ARGUMENT, "snapshots is NULL but snapshot_rows = %lld",
                         (long long)snapshot_rows);
-        if (snapshots && ((uintptr_t)snapshots & 3u))
-            return fail(KDA_ERR_MISALIGNED, "snapshots is not 4-byte aligned");
+        if (snapshots && !aligned16(snapshots))
+            return fail(KDA_ERR_MISALIGNED, "snapshots is not 16-byte aligned");
     }
     // no snapshot rows to write: the plain prefill
     if (snapshot_every == 0 || snapshot_rows == 0) { snapshots = nullptr; snapshot_every = 0; snapshot_rows = 0; }
@@ -273,6 +278,7 @@ int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, c
                 pa.q = q; pa.k = k; pa.log_a = log_a; pa.beta = beta; pa.cu_seqlens = cu_seqlens;
                 pa.eq_len = eq_len; pa.ws = blocks; pa.num_heads = d->num_heads; pa.units = pl.units;
                 pa.m = (int32_t)m; pa.chunk0 = chunk0; pa.dk = d->dk; pa.chunk = chunk; pa.scalar = d->scalar_decay;
+                pa.order = kernel_order(d);
                 e = kda::launch_prep(pa, (hipStream_t)stream);
                 if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill operator pass launch: %s", hipGetErrorString(e));
             }
@@ -280,7 +286,7 @@ int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, c
             sa.v = v; sa.o = o; sa.cu_seqlens = cu_seqlens; sa.eq_len = eq_len; sa.ws = blocks;
             sa.S_in = sgi == 0 ? S0 : run; sa.S_out = run; sa.num_heads = d->num_heads; sa.units = pl.units;
             sa.dk = d->dk; sa.dv = d->dv; sa.split = pl.split; sa.m = (int32_t)m; sa.chunk = chunk;
-            sa.chunk0 = chunk0; sa.snap = snapshots; sa.snap_rows = snapshot_rows;
+            sa.chunk0 = chunk0; sa.order = kernel_order(d); sa.snap = snapshots; sa.snap_rows = snapshot_rows;
             sa.snap_every = (int32_t)snapshot_every;
             e = kda::launch_scan(sa, (hipStream_t)stream);
             if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill state pass launch: %s", hipGetErrorString(e));
@@ -307,7 +313,7 @@ int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, c
     a.cu_seqlens = cu_seqlens; a.o = o; a.S_T = S_T;
     a.num_seqs = d->num_seqs; a.num_heads = d->num_heads; a.total_tokens = d->total_tokens;
     a.dk = d->dk; a.dv = d->dv; a.dtype = d->qkv_dtype; a.scalar_decay = d->scalar_decay;
-    a.chunk = chunk; a.split = split;
+    a.chunk = chunk; a.split = split; a.order = kernel_order(d);
     a.snap = snapshots; a.snap_rows = snapshot_rows; a.snap_every = (int32_t)snapshot_every;
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
@@ -331,7 +337,7 @@ int kda_decode_step(const kda_dims_t* d, const void* q, const void* k, const voi
         return fail(KDA_ERR_UNSUPPORTED, "no decode kernel for dtype %d, dk %d, dv %d", d->qkv_dtype, d->dk, d->dv);
     const int64_t heads = (int64_t)d->num_seqs * d->num_heads;
     if (heads > 0x7fffffff) return fail(KDA_ERR_INVALID_ARGUMENT, "too many states: %lld", (long long)heads);
-    hipError_t e = kda::launch_decode(d->qkv_dtype, d->dk, d->dv, d->scalar_decay, heads, q, k, v, log_a,
+    hipError_t e = kda::launch_decode(d->qkv_dtype, d->dk, d->dv, d->scalar_decay, kernel_order(d), heads, q, k, v, log_a,
                                       beta, S_in, S_out, o, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return ok();

@@ -29,6 +29,15 @@
 // e^{mu_bt - mu_bi} <= 1.  The state-side operands are referenced to the chunk
 // start or end, where every factor is <= 1.
 //
+// The decay-first ordering (ORD1: S <- (I - b k^T k) Diag(a) S + b k^T v,
+// per-channel decay only) has the same structure with Kb = K e^{g_t} and no
+// write outside the erase term:
+//   A  = strict_lower(diag(b) Kb Kt^T),  P2 = lower(Qb Kt^T),  Tb as above
+//   E  = -Tb (Kb S - V)   (= the chunk's new values, T diag(b) (V - Kb S))
+//   O  = Qb S + P2 E
+//   S <- Diag(e^{g_C}) S + (Kt e^{g_C})^T E
+// so L, P1, Kc and the (b V) terms drop out.
+//
 // Work decomposition: one workgroup (8 wavefronts) per (sequence, head,
 // dv-slice of width DVS).  The workgroup walks its sequence chunk by chunk,
 // loading the next chunk's inputs into registers while it computes the
@@ -178,7 +187,9 @@ __device__ __forceinline__ void load_chunk(const ChunkParams& p, const T* gq, co
     }
 }
 
-template <typename T, int DK, int DVS, int C, bool SCALAR>
+// SNAP: the call asks for state snapshots (a separate instantiation: the
+// snapshot stores would otherwise cost the plain walk registers).
+template <typename T, int DK, int DVS, int C, bool SCALAR, bool ORD1, bool SNAP>
 __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
     typedef ChunkCfg<T, DK, DVS, C> G;
     typedef Mma<T> M;
@@ -235,7 +246,7 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
     // snap0 + (tokens / snap_every) - 1; snap_cd counts the chunks to the next
     int64_t snap0 = 0;
     int snap_ec = 1, snap_cd = 0;
-    if (p.snap) {
+    if (SNAP) {
         snap0 = snapshots_before(p.cu, p.eq_len, n, p.snap_every);
         snap_ec = p.snap_every / C;
         snap_cd = snap_ec;
@@ -297,7 +308,8 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     bb[i] = 4 * tg + i < Lc ? vi[u].b[i] : 0.f;
-                    vals[i] = bb[i] * Vec4<T>::to_f32(vi[u].v[i]);
+                    // (b V)^T; ORD1: V^T, padded rows zero
+                    vals[i] = (ORD1 ? (4 * tg + i < Lc ? 1.f : 0.f) : bb[i]) * Vec4<T>::to_f32(vi[u].v[i]);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -357,10 +369,10 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                     }
                     const f32x2 k = f32x2{Vec2<T>::lo(kraw[u][i]), Vec2<T>::hi(kraw[u][i])};
                     const f32x2 q = f32x2{Vec2<T>::lo(qraw[u][i]), Vec2<T>::hi(qraw[u][i])};
-                    const f32x2 kr = k * prev, qr = q * ri, kce = k * prevc, kci = k * ci;
+                    const f32x2 kr = ORD1 ? k * ri : k * prev, qr = q * ri, kce = k * prevc, kci = k * ci;
                     store2(&s.Kr[t * LDK + c], kr[0], kr[1]);
                     store2(&s.Qr[t * LDK + c], qr[0], qr[1]);
-                    store2(&s.Kce[t * LDK + c], kce[0], kce[1]);
+                    if (!ORD1) store2(&s.Kce[t * LDK + c], kce[0], kce[1]);
                     store2(&s.Kci[t * LDK + c], kci[0], kci[1]);
                     store2(&s.Kbar[t * LDK + c], kr[0] * em[0], kr[1] * em[1]);
                     store2(&s.Qbar[t * LDK + c], qr[0] * em[0], qr[1] * em[1]);
@@ -371,7 +383,8 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 }
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    store4(&s.KccT[prow<DK>(c + e) * LDC + 4 * tg], f32x4{kc[0][e], kc[1][e], kc[2][e], kc[3][e]});
+                    if (!ORD1)
+                        store4(&s.KccT[prow<DK>(c + e) * LDC + 4 * tg], f32x4{kc[0][e], kc[1][e], kc[2][e], kc[3][e]});
                     store4(&s.KtcT[prow<DK>(c + e) * LDC + 4 * tg], f32x4{kt[0][e], kt[1][e], kt[2][e], kt[3][e]});
                 }
             }
@@ -394,14 +407,16 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
         lds_barrier();
 
         // ---- P3: Gram products: tile w is product w % 4 (0 A, 1 L, 2 P1, 3 P2) of
-        //      block pair w / 4, transposed (G^T) so it lands row-major in LDS --------
-        for (int w = wv; w < 4 * G::NBP; w += NW) {
-            const int g = w % 4, pr = w / 4;
+        //      block pair w / 4, transposed (G^T) so it lands row-major in LDS;
+        //      ORD1: A (w even, columns Kt) or P2 (w odd) of block pair w / 2 --------
+        constexpr int NG = ORD1 ? 2 : 4;
+        for (int w = wv; w < NG * G::NBP; w += NW) {
+            const int g = ORD1 ? ((w & 1) ? 3 : 0) : w % 4, pr = w / NG;
             int bt = 0;
             while ((bt + 1) * (bt + 2) / 2 <= pr) ++bt;
             const int bi = pr - bt * (bt + 1) / 2;
             const T* rows = (g < 2 ? s.Kr : s.Qr) + (16 * bt + lrow) * LDK;
-            const T* cols = ((g & 1) == 0 ? s.Kce : s.Kci) + (16 * bi + lrow) * LDK;
+            const T* cols = ((g & 1) == 0 && !ORD1 ? s.Kce : s.Kci) + (16 * bi + lrow) * LDK;
             constexpr int NK = DK / M::K;
             typename M::frag fr[NK], fc[NK];
 #pragma unroll
@@ -439,12 +454,17 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 if (w < G::NOT) {
                     const int mt = w / (DVS / 16), nj = w % (DVS / 16);
                     f32x4 z = tile_mma<T, DK>(s.Kbar + 16 * mt * LDK, LDK, s.ST + 16 * nj * LDK, LDK, zero4(), lane);
-                    z = tile_mma_r<T, C>(s.L + (16 * mt + lrow) * LDC, s.VT + prow<DVS>(16 * nj + lrow) * LDC, z, lane);
+                    if (ORD1)  // Z = Kbar S - V
+                        z -= load4(&s.VT[prow<DVS>(16 * nj + lrow) * LDC + 16 * mt + 4 * lgrp]);
+                    else
+                        z = tile_mma_r<T, C>(s.L + (16 * mt + lrow) * LDC, s.VT + prow<DVS>(16 * nj + lrow) * LDC, z,
+                                             lane);
                     store4(&s.ZT[(16 * nj + lrow) * LDC + 16 * mt + 4 * lgrp], z);
                     const int mj = w / (C / 16), nt = w % (C / 16);
                     f32x4 x = tile_mma<T, DK>(s.ST + 16 * mj * LDK, LDK, s.Qbar + 16 * nt * LDK, LDK, zero4(), lane);
-                    oacc[i] = tile_mma_r<T, C>(s.VT + prow<DVS>(16 * mj + lrow) * LDC, s.P2 + (16 * nt + lrow) * LDC,
-                                               x, lane);
+                    oacc[i] = ORD1 ? x
+                                   : tile_mma_r<T, C>(s.VT + prow<DVS>(16 * mj + lrow) * LDC,
+                                                      s.P2 + (16 * nt + lrow) * LDC, x, lane);
                 }
             }
 #pragma unroll
@@ -453,8 +473,9 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 if (ix < G::NST) {
                     const int mi = ix / (DVS / 16), ni = ix % (DVS / 16);
                     const f32x4 gm = *reinterpret_cast<const f32x4*>(&s.gam[16 * mi + 4 * lgrp]);
-                    acc[i] = tile_mma_r<T, C>(s.KtcT + prow<DK>(16 * mi + lrow) * LDC,
-                                              s.VT + prow<DVS>(16 * ni + lrow) * LDC, acc[i] * gm, lane);
+                    acc[i] = ORD1 ? acc[i] * gm
+                                  : tile_mma_r<T, C>(s.KtcT + prow<DK>(16 * mi + lrow) * LDC,
+                                                     s.VT + prow<DVS>(16 * ni + lrow) * LDC, acc[i] * gm, lane);
                 }
             }
         }
@@ -477,8 +498,9 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 if (ix < G::NST) {
                     const int mi = ix / (DVS / 16), ni = ix % (DVS / 16);
                     const f32x4 gm = *reinterpret_cast<const f32x4*>(&s.gam[16 * mi + 4 * lgrp]);
-                    acc[i] = tile_mma_r<T, C>(s.KtcT + prow<DK>(16 * mi + lrow) * LDC,
-                                              s.VT + prow<DVS>(16 * ni + lrow) * LDC, acc[i] * gm, lane);
+                    acc[i] = ORD1 ? acc[i] * gm
+                                  : tile_mma_r<T, C>(s.KtcT + prow<DK>(16 * mi + lrow) * LDC,
+                                                     s.VT + prow<DVS>(16 * ni + lrow) * LDC, acc[i] * gm, lane);
                 }
             }
         }
@@ -491,7 +513,8 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 const int w = (wv - 1) + (NW - 1) * i;
                 if (w < G::NOT) {
                     const int mj = w / (C / 16), nt = w % (C / 16);
-                    opend[i] = tile_mma<T, C>(s.ET + 16 * mj * LDC, LDC, s.P1 + 16 * nt * LDC, LDC, oacc[i], lane);
+                    opend[i] = tile_mma<T, C>(s.ET + 16 * mj * LDC, LDC, (ORD1 ? s.P2 : s.P1) + 16 * nt * LDC, LDC,
+                                              oacc[i], lane);
                 }
             }
         }
@@ -500,23 +523,23 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
             const int ix = wv + NW * i;
             if (ix < G::NST) {
                 const int mi = ix / (DVS / 16), ni = ix % (DVS / 16);
-                acc[i] = tile_mma_r<T, C>(s.KccT + prow<DK>(16 * mi + lrow) * LDC, s.ET + (16 * ni + lrow) * LDC,
-                                          acc[i], lane);
+                acc[i] = tile_mma_r<T, C>((ORD1 ? s.KtcT : s.KccT) + prow<DK>(16 * mi + lrow) * LDC,
+                                          s.ET + (16 * ni + lrow) * LDC, acc[i], lane);
                 store4(&s.ST[(16 * ni + lrow) * LDK + 16 * mi + 4 * lgrp], acc[i]);
             }
         }
-        if (p.snap && --snap_cd == 0) {
+        if (SNAP && --snap_cd == 0) {
             snap_cd = snap_ec;
             const int64_t done = t0 + C - tb;  // tokens of the sequence behind this state
             const int64_t row = snap0 + done / p.snap_every - 1;
             if (done <= te - tb && row < p.snap_rows) {
-                float* dst = p.snap + (row * H + h) * DK * DV + dv0 + lrow;
+                float* dst = p.snap + (row * H + h) * DK * DV + dv0;
 #pragma unroll
                 for (int i = 0; i < G::STPW; ++i) {
                     const int ix = wv + NW * i;
                     if (ix < G::NST) {
                         const int mi = ix / (DVS / 16), ni = ix % (DVS / 16);
-                        store_state_tile(dst + (int64_t)16 * mi * DV + 16 * ni, DV, lgrp, acc[i]);
+                        store_state_tile(dst + (int64_t)16 * mi * DV + 16 * ni, DV, lane, acc[i]);
                     }
                 }
             }
@@ -544,8 +567,9 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
 template <typename T, int DK, int DVS, int C>
 constexpr bool chunk_fits() { return chunk_lds_bytes<T, DK, DVS, C>() <= 160 * 1024; }
 
-template <typename T, int DK, int DVS, int C, bool SC>
+template <typename T, int DK, int DVS, int C, bool SC, bool ORD1>
 static hipError_t launch_cfg(const ChunkArgs& a, hipStream_t stream) {
+    constexpr int NT = ChunkCfg<T, DK, DVS, C>::NT;
     ChunkParams p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.log_a = a.log_a; p.beta = a.beta; p.S0 = a.S0;
     p.cu = a.cu_seqlens; p.o = a.o; p.ST = a.S_T;
@@ -554,16 +578,22 @@ static hipError_t launch_cfg(const ChunkArgs& a, hipStream_t stream) {
     p.snap = a.snap; p.snap_rows = a.snap_rows; p.snap_every = a.snap_every;
     const int64_t blocks = (int64_t)a.num_seqs * a.num_heads * a.split;
     p.xcd_group = (blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
-    hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC>), dim3((unsigned)blocks), dim3(ChunkCfg<T, DK, DVS, C>::NT), 0,
-                       stream, p);
+    if (a.snap)
+        hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC, ORD1, true>), dim3((unsigned)blocks), dim3(NT), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC, ORD1, false>), dim3((unsigned)blocks), dim3(NT), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
 template <typename T, int DK, int DVS, int C>
 static bool try_cfg(int scalar, bool launch, const ChunkArgs* a, hipStream_t stream, hipError_t* err) {
     if constexpr (chunk_fits<T, DK, DVS, C>()) {
-        if (launch) *err = scalar ? launch_cfg<T, DK, DVS, C, true>(*a, stream)
-                                  : launch_cfg<T, DK, DVS, C, false>(*a, stream);
+        // order 1 comes with per-channel decay only (the host maps scalar decay to order 0)
+        if (launch) *err = scalar     ? launch_cfg<T, DK, DVS, C, true, false>(*a, stream)
+                           : a->order ? launch_cfg<T, DK, DVS, C, false, true>(*a, stream)
+                                      : launch_cfg<T, DK, DVS, C, false, false>(*a, stream);
         return true;
     } else {
         return false;

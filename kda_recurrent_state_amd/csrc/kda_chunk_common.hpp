@@ -61,12 +61,38 @@ __device__ inline int64_t snapshots_before(const int32_t* cu, int64_t eq_len, in
     return s;
 }
 
-// Stores one 16 x 16 fp32 accumulator tile (column lane % 16, rows
-// 4 (lane / 16) .. + 3) of a state slice into a row-major [dk][dv] state;
-// dst points at the tile's first row and this lane's column.
-__device__ __forceinline__ void store_state_tile(float* dst, int64_t DV, int lg, f32x4 t) {
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) { return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false); }
+
+// 4 x 4 transpose of dwords inside each lane quad: lane v of a quad ends with
+// dword v of every lane w of its quad (as its dword w).
+__device__ __forceinline__ i32x4 quad_transpose(i32x4 m, int lane) {
+    const int v = lane & 3;
+    i32x4 n1, n2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(int64_t)(4 * lg + i) * DV] = t[i];
+    for (int d = 0; d < 4; ++d) {
+        const int t = dpp<0xB1>(m[d ^ 1]);  // quad_perm [1, 0, 3, 2]: lane v ^ 1's dword d ^ 1
+        n1[d] = ((v ^ d) & 1) ? t : m[d];
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int t = dpp<0x4E>(n1[d ^ 2]);  // quad_perm [2, 3, 0, 1]: lane v ^ 2's dword d ^ 2
+        n2[d] = ((v ^ d) & 2) ? t : n1[d];
+    }
+    return n2;
+}
+
+// Stores one 16 x 16 fp32 accumulator tile (lane: column lane % 16, rows
+// 4 (lane / 16) .. + 3) into a row-major state with row stride DV; dst points at
+// the tile's element (0, 0).  After a transpose inside lane quads each lane
+// holds four consecutive columns of one row and writes them with one 16-byte
+// store (whole wavefront: 16 rows x 64 bytes).
+__device__ __forceinline__ void store_state_tile(float* dst, int64_t DV, int lane, f32x4 t) {
+    const i32x4 x = quad_transpose(__builtin_bit_cast(i32x4, t), lane);
+    const int row = 4 * (lane >> 4) + (lane & 3), col = 4 * ((lane & 15) >> 2);
+    *reinterpret_cast<f32x4*>(dst + (int64_t)row * DV + col) = __builtin_bit_cast(f32x4, x);
 }
 
 __device__ __forceinline__ float uniform(float x) {

@@ -10,6 +10,12 @@
 //     S'[c][j] = a_c (S[c][j] - beta k_c y_j) + beta k_c v_j
 //     o_j      = z_j - beta (q*a . k) y_j + beta (q . k) v_j
 //
+// The decay-first ordering (ORD1, per-channel decay only),
+//     S' = (I - beta k^T k) Diag(a) S + beta k^T v,
+// reads y = (k * a) S instead:
+//     S'[c][j] = a_c S[c][j] - beta k_c y_j + beta k_c v_j
+//     o_j      = z_j - beta (q . k) y_j + beta (q . k) v_j
+//
 // One workgroup per state.  Thread (row group rg, column group cg) owns four
 // consecutive columns 4cg..4cg+3 of rows rg, rg + RG, ...; a wavefront covers
 // whole consecutive rows, so every 16-byte load and store is coalesced.
@@ -28,7 +34,7 @@ struct DecodeShape {
     static_assert(NT % WAVE == 0 && DK % RG == 0, "decode shape");
 };
 
-template <typename T, int DK, int DV, bool SCALAR>
+template <typename T, int DK, int DV, bool SCALAR, bool ORD1>
 __global__ void __launch_bounds__(256)
 kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const float* __restrict__ log_a, const float* __restrict__ beta,
@@ -85,7 +91,7 @@ kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg + RG * i;
-        const float kr = s_k[r], qr = s_qa[r];
+        const float kr = ORD1 ? s_k[r] * s_a[r] : s_k[r], qr = s_qa[r];
         y += kr * s[i];
         z += qr * s[i];
     }
@@ -120,46 +126,51 @@ kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         const int r = rg + RG * i;
         const float kr = s_k[r], ar = s_a[r];
         const float bk = b * kr;
-        f32x4 ns = ar * (s[i] - bk * y) + kr * bv;
+        f32x4 ns = ORD1 ? ar * s[i] - bk * y + kr * bv : ar * (s[i] - bk * y) + kr * bv;
         __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(So + r * DV + 4 * cg));
     }
-    // 5. output o = z - beta (q*a.k) y + beta (q.k) v
+    // 5. output o = z - beta (q*a.k) y + beta (q.k) v   (ORD1: (q.k) in both terms)
     if (rg == 0) {
-        const float d1 = s_dot[0], d2 = s_dot[1];
+        const float d1 = ORD1 ? s_dot[1] : s_dot[0], d2 = s_dot[1];
         f32x4 out = z - (b * d1) * y + (b * d2) * vv;
         store4(o + head * DV + 4 * cg, out);
     }
 }
 
-#define KDA_DECODE_CASE(T, DK_, DV_, SC)                                                         \
-    if (dk == DK_ && dv == DV_ && scalar == SC) {                                                \
+#define KDA_DECODE_CASE(T, DK_, DV_, SC, O1)                                                     \
+    if (dk == DK_ && dv == DV_) {                                                                \
         typedef DecodeShape<T, DK_, DV_, SC> Sh;                                                 \
-        hipLaunchKernelGGL((kda_decode_kernel<T, DK_, DV_, SC>), dim3(heads), dim3(Sh::NT), 0,    \
+        hipLaunchKernelGGL((kda_decode_kernel<T, DK_, DV_, SC, O1>), dim3(heads), dim3(Sh::NT), 0,\
                            stream, (const T*)q, (const T*)k, (const T*)v, log_a, beta, S_in,     \
                            S_out, (T*)o);                                                        \
         return hipGetLastError();                                                                \
     }
 
-#define KDA_DECODE_DIMS(T, SC)                                                                   \
-    KDA_DECODE_CASE(T, 16, 16, SC) KDA_DECODE_CASE(T, 16, 32, SC) KDA_DECODE_CASE(T, 16, 64, SC)   \
-    KDA_DECODE_CASE(T, 16, 128, SC) KDA_DECODE_CASE(T, 32, 16, SC) KDA_DECODE_CASE(T, 32, 32, SC)  \
-    KDA_DECODE_CASE(T, 32, 64, SC) KDA_DECODE_CASE(T, 32, 128, SC) KDA_DECODE_CASE(T, 64, 16, SC)  \
-    KDA_DECODE_CASE(T, 64, 32, SC) KDA_DECODE_CASE(T, 64, 64, SC) KDA_DECODE_CASE(T, 64, 128, SC)  \
-    KDA_DECODE_CASE(T, 128, 16, SC) KDA_DECODE_CASE(T, 128, 32, SC)                              \
-    KDA_DECODE_CASE(T, 128, 64, SC) KDA_DECODE_CASE(T, 128, 128, SC)
+#define KDA_DECODE_DIMS(T, SC, O1)                                                                      \
+    KDA_DECODE_CASE(T, 16, 16, SC, O1) KDA_DECODE_CASE(T, 16, 32, SC, O1) KDA_DECODE_CASE(T, 16, 64, SC, O1)  \
+    KDA_DECODE_CASE(T, 16, 128, SC, O1) KDA_DECODE_CASE(T, 32, 16, SC, O1) KDA_DECODE_CASE(T, 32, 32, SC, O1) \
+    KDA_DECODE_CASE(T, 32, 64, SC, O1) KDA_DECODE_CASE(T, 32, 128, SC, O1) KDA_DECODE_CASE(T, 64, 16, SC, O1) \
+    KDA_DECODE_CASE(T, 64, 32, SC, O1) KDA_DECODE_CASE(T, 64, 64, SC, O1) KDA_DECODE_CASE(T, 64, 128, SC, O1) \
+    KDA_DECODE_CASE(T, 128, 16, SC, O1) KDA_DECODE_CASE(T, 128, 32, SC, O1)                                  \
+    KDA_DECODE_CASE(T, 128, 64, SC, O1) KDA_DECODE_CASE(T, 128, 128, SC, O1)
 
 bool decode_supported(int dtype, int dk, int dv) {
     auto ok = [](int d) { return d == 16 || d == 32 || d == 64 || d == 128; };
     return (dtype == 0 || dtype == 1) && ok(dk) && ok(dv);
 }
 
-hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int64_t heads, const void* q,
+// order 1 comes with per-channel decay only (the host maps scalar decay to order 0)
+hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int order, int64_t heads, const void* q,
                          const void* k, const void* v, const float* log_a, const float* beta,
                          const float* S_in, float* S_out, void* o, hipStream_t stream) {
     if (dtype == 1) {
-        if (scalar) { KDA_DECODE_DIMS(bf16, true) } else { KDA_DECODE_DIMS(bf16, false) }
+        if (scalar) { KDA_DECODE_DIMS(bf16, true, false) }
+        else if (order) { KDA_DECODE_DIMS(bf16, false, true) }
+        else { KDA_DECODE_DIMS(bf16, false, false) }
     } else {
-        if (scalar) { KDA_DECODE_DIMS(float, true) } else { KDA_DECODE_DIMS(float, false) }
+        if (scalar) { KDA_DECODE_DIMS(float, true, false) }
+        else if (order) { KDA_DECODE_DIMS(float, false, true) }
+        else { KDA_DECODE_DIMS(float, false, false) }
     }
     return hipErrorInvalidValue;
 }

@@ -24,13 +24,14 @@ struct ChunkArgs {
     int32_t scalar_decay;
     int32_t chunk;              // 32 or 64
     int32_t split;              // workgroups per (sequence, head) along dv
+    int32_t order;              // 1: decay first (per-channel decay only), else 0
     float* snap;                // state snapshots [rows, H, dk, dv], or null
     int64_t snap_rows;
     int32_t snap_every;         // tokens between snapshots (a multiple of chunk), 0 = none
 };
 
 bool decode_supported(int dtype, int dk, int dv);
-hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int64_t heads, const void* q,
+hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int order, int64_t heads, const void* q,
                          const void* k, const void* v, const float* log_a, const float* beta,
                          const float* S_in, float* S_out, void* o, hipStream_t stream);
 
@@ -53,6 +54,7 @@ struct PrepLaunch {
     int32_t m;                  // chunks per unit in the segment
     int64_t chunk0;             // first chunk of the segment
     int32_t dk, chunk, scalar;
+    int32_t order;              // as in ChunkArgs
 };
 struct ScanLaunch {
     const void* v;
@@ -66,11 +68,12 @@ struct ScanLaunch {
     int64_t units;
     int32_t dk, dv, split, m, chunk;
     int64_t chunk0;
+    int32_t order;              // as in ChunkArgs
     float* snap;                // as in ChunkArgs
     int64_t snap_rows;
     int32_t snap_every;
 };
-int prep_block_bytes(int dk, int chunk);  // 0 if no prep kernel for (dk, chunk)
+int prep_block_bytes(int dk, int chunk, int order);  // 0 if no prep kernel for (dk, chunk)
 hipError_t launch_prep(const PrepLaunch& a, hipStream_t stream);
 hipError_t launch_prep2(const PrepLaunch& a, hipStream_t stream);  // dk = 128, chunk 32
 bool two_pass_supported(int dtype, int dk, int dvs, int chunk);

@@ -18,6 +18,10 @@
 //   W  = Tb Kb,  M1 = Tb L diag(b),  QP = Qb - P1 W,  M2 = P2 diag(b) - P1 M1
 //   KC = (K e^{g_C - g_{t-1}})^T,  KT = (diag(b) K e^{g_C - g_t})^T,  GAM = e^{g_C}
 // where Kb, Qb in W and QP are referenced to the chunk start (factors <= 1).
+// The decay-first ordering (ORD1) takes Kb = K e^{g_t}, Kc = Kt and needs only
+// A and P2 (unscaled, in place of P1); with L diag(b) = -I and P2 diag(b) = 0
+// the same phases 5 and 6 then give M1 = -Tb and M2 = P2 Tb (kda_ws.hpp), and
+// KC = (K e^{g_C - g_t})^T; no KT.
 //
 // Persistent workgroups of 8 wavefronts, each walking a strided list of
 // chunks; the next chunk's inputs are loaded while the current one is in
@@ -181,10 +185,10 @@ __device__ __forceinline__ void split_solve(PrepLds<DK, C>& s, int wv, int lane,
     }
 }
 
-template <int DK, int C, bool SCALAR>
+template <int DK, int C, bool SCALAR, bool ORD1>
 __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
     typedef PrepCfg<DK, C> G;
-    typedef WsBlock<DK, C> WS;
+    typedef WsBlock<DK, C, ORD1> WS;
     typedef Mma<bf16> M;
     constexpr int NT = G::NT, NW = G::NW, NB = G::NB, LDK = G::LDK, LDC = G::LDC, LDA = G::LDA;
     __shared__ PrepLds<DK, C> s;
@@ -200,6 +204,10 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
     }
     for (int e = tid; e < C * LDA; e += NT) s.P2[e] = 0.f;
     if (tid < 16) s.ones[tid] = 1.f;
+    if (ORD1) {  // L diag(b) = -I for the whole walk
+        lds_barrier();
+        if (tid < C) s.LbT[tid * LDC + tid] = (bf16)-1.f;
+    }
 
     // this workgroup's chunks: item = blockIdx.x + k gridDim.x, empty ones skipped
     auto next_item = [&](int it, int64_t& t0, int& Lc, int& h) {
@@ -263,14 +271,14 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
                 }
                 const f32x2 k = f32x2{Vec2<bf16>::lo(in.k[i]), Vec2<bf16>::hi(in.k[i])};
                 const f32x2 q = f32x2{Vec2<bf16>::lo(in.q[i]), Vec2<bf16>::hi(in.q[i])};
-                const f32x2 kr = k * prev, qr = q * ri, kce = k * prevc, kci = k * ci;
+                const f32x2 kr = ORD1 ? k * ri : k * prev, qr = q * ri, kce = k * prevc, kci = k * ci;
                 store2(&s.u.g.Kr[t * LDK + c], kr[0], kr[1]);
                 store2(&s.u.g.Qr[t * LDK + c], qr[0], qr[1]);
-                store2(&s.u.g.Kce[t * LDK + c], kce[0], kce[1]);
+                if (!ORD1) store2(&s.u.g.Kce[t * LDK + c], kce[0], kce[1]);
                 store2(&s.u.g.Kci[t * LDK + c], kci[0], kci[1]);
                 store2(&s.Qb[t * LDK + c], qr[0] * em[0], qr[1] * em[1]);
                 kb[i] = kr * em;
-                kc[i] = kce * ec;
+                kc[i] = ORD1 ? kci * ec : kce * ec;
                 kt[i] = kci * ec * s.beta[t];
                 prev = ri;
                 prevc = ci;
@@ -281,8 +289,9 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
                 store4(&s.KbT[(c + e) * LDC + 4 * tg], f32x4{kb[0][e], kb[1][e], kb[2][e], kb[3][e]});
                 store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c + e, pos)),
                        f32x4{kc[0][e], kc[1][e], kc[2][e], kc[3][e]});
-                store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c + e, pos)),
-                       f32x4{kt[0][e], kt[1][e], kt[2][e], kt[3][e]});
+                if (!ORD1)
+                    store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c + e, pos)),
+                           f32x4{kt[0][e], kt[1][e], kt[2][e], kt[3][e]});
             }
         }
         // per (sub-block, channel): e^{mu_bt - mu_bi} for block pairs; e^{g_C} to the block
@@ -309,14 +318,16 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
         if (nitem < p.items) prep_load<DK, C, SCALAR>(p, nt0, nLc, nh, tid, c, tg, in);
 
         // ---- 3: Gram products; tile w is product w % 4 (0 A, 1 L, 2 P1, 3 P2) of block
-        //      pair w / 4.  A, P1, P2 land row-major [t][i], L transposed [i][t] ------
-        for (int w = wv; w < 4 * G::NBP; w += NW) {
-            const int g = w % 4, pr = w / 4;
+        //      pair w / 4.  A, P1, P2 land row-major [t][i], L transposed [i][t].
+        //      ORD1: tile w is A (w even) or P2 (w odd, unscaled, into P1) of pair w / 2
+        constexpr int NG = ORD1 ? 2 : 4;
+        for (int w = wv; w < NG * G::NBP; w += NW) {
+            const int g = ORD1 ? ((w & 1) ? 3 : 0) : w % 4, pr = w / NG;
             int bt = 0;
             while ((bt + 1) * (bt + 2) / 2 <= pr) ++bt;
             const int bi = pr - bt * (bt + 1) / 2;
             const bf16* rows = (g < 2 ? s.u.g.Kr : s.u.g.Qr) + (16 * bt + lrow) * LDK;
-            const bf16* cols = ((g & 1) == 0 ? s.u.g.Kce : s.u.g.Kci) + (16 * bi + lrow) * LDK;
+            const bf16* cols = ((g & 1) == 0 && !ORD1 ? s.u.g.Kce : s.u.g.Kci) + (16 * bi + lrow) * LDK;
             constexpr int NK = DK / M::K;
             M::frag fr[NK], fc[NK];
 #pragma unroll
@@ -349,7 +360,7 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) m[r] = (g == 0 ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f;
                 if (g == 0) *reinterpret_cast<f32x4*>(&s.u2.A[t * LDA + i0]) = s.beta[t] * m;
-                else if (g == 2) store4(&s.P1[t * LDC + i0], m);
+                else if (g == 2 || ORD1) store4(&s.P1[t * LDC + i0], m);
                 else *reinterpret_cast<f32x4*>(&s.P2[t * LDA + i0]) =
                          m * *reinterpret_cast<const f32x4*>(&s.beta[i0]);
             }
@@ -423,7 +434,7 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
 }
 
 // ------------------------------------------------------------------------------------
-template <int DK, int C, bool SC>
+template <int DK, int C, bool SC, bool ORD1>
 static hipError_t prep_cfg(const PrepLaunch& a, hipStream_t stream) {
     PrepParams p;
     p.q = a.q; p.k = a.k; p.log_a = a.log_a; p.beta = a.beta; p.cu = a.cu_seqlens;
@@ -438,22 +449,30 @@ static hipError_t prep_cfg(const PrepLaunch& a, hipStream_t stream) {
     int64_t blocks = (int64_t)cus * per_cu;
     if (blocks > p.items) blocks = p.items;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((kda_prep_kernel<DK, C, SC>), dim3((unsigned)blocks), dim3(PrepCfg<DK, C>::NT), 0,
+    hipLaunchKernelGGL((kda_prep_kernel<DK, C, SC, ORD1>), dim3((unsigned)blocks), dim3(PrepCfg<DK, C>::NT), 0,
                        stream, p);
     return hipGetLastError();
 }
 
-int prep_block_bytes(int dk, int chunk) {
-    if (dk == 64 && chunk == 32) return WsBlock<64, 32>::BYTES;
-    if (dk == 128 && chunk == 32) return WsBlock<128, 32>::BYTES;
-    if (dk == 64 && chunk == 64) return WsBlock<64, 64>::BYTES;
+int prep_block_bytes(int dk, int chunk, int order) {
+    const bool o1 = order != 0;
+    if (dk == 64 && chunk == 32) return o1 ? WsBlock<64, 32, true>::BYTES : WsBlock<64, 32>::BYTES;
+    if (dk == 128 && chunk == 32) return o1 ? WsBlock<128, 32, true>::BYTES : WsBlock<128, 32>::BYTES;
+    if (dk == 64 && chunk == 64) return o1 ? WsBlock<64, 64, true>::BYTES : WsBlock<64, 64>::BYTES;
     return 0;
+}
+
+// order 1 comes with per-channel decay only (the host maps scalar decay to order 0)
+template <int DK, int C>
+static hipError_t prep_dispatch(const PrepLaunch& a, hipStream_t stream) {
+    if (a.scalar) return prep_cfg<DK, C, true, false>(a, stream);
+    return a.order ? prep_cfg<DK, C, false, true>(a, stream) : prep_cfg<DK, C, false, false>(a, stream);
 }
 
 hipError_t launch_prep(const PrepLaunch& a, hipStream_t stream) {
     if (a.dk == 128 && a.chunk == 32) return launch_prep2(a, stream);
-    if (a.dk == 64 && a.chunk == 32) return a.scalar ? prep_cfg<64, 32, true>(a, stream) : prep_cfg<64, 32, false>(a, stream);
-    if (a.dk == 64 && a.chunk == 64) return a.scalar ? prep_cfg<64, 64, true>(a, stream) : prep_cfg<64, 64, false>(a, stream);
+    if (a.dk == 64 && a.chunk == 32) return prep_dispatch<64, 32>(a, stream);
+    if (a.dk == 64 && a.chunk == 64) return prep_dispatch<64, 64>(a, stream);
     return hipErrorInvalidValue;
 }
 

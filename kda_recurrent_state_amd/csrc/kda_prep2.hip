@@ -12,6 +12,11 @@
 //   W  = Tb Kb,  QP = Qb - R Kb,  M1 = Tb L diag(b),  M2 = P2 diag(b) - R L diag(b)
 //   KC = (K e^{g_C - g_{t-1}})^T,  KT = (diag(b) K e^{g_C - g_t})^T,  GAM = e^{g_C}
 //
+// The decay-first ordering (ORD1, blocks of kda_ws.hpp without KT) takes
+// Kb = K e^{g_t} and Kc = Kt, forms only A and P2 (unscaled, in place of P1),
+// and runs phase D unchanged with L diag(b) = -I and P2 diag(b) = 0, which
+// gives M1 = -Tb and M2 = R; KC = (K e^{g_C - g_t})^T.
+//
 // Work decomposition: one workgroup of four wavefronts per chunk (persistent
 // workgroups walk a strided list of chunks, two per compute unit).  In the
 // elementwise phase thread (c2, o) owns the channel pair 2 c2, 2 c2 + 1 and
@@ -83,8 +88,6 @@ struct Prep2Params {
     int64_t chunk0;   // first chunk index of the segment
 };
 
-typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-
 // Raw inputs of one thread as loaded: 16 bytes per lane and row, so each vector
 // memory instruction moves 1 KB.  lq/lk[g]: 8 channels (8 (lane >> 2) ..) of
 // token 8 o + 4 g + (lane & 3); la[p]: 4 channels (4 (lane >> 1) ..) of token
@@ -104,28 +107,8 @@ struct Prep2In {
     f32x2 la[8];
 };
 
-template <int CTRL>
-__device__ __forceinline__ int dpp(int x) { return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false); }
 __device__ __forceinline__ float dppf_swap1(float x) {
     return __builtin_bit_cast(float, dpp<0xB1>(__builtin_bit_cast(int, x)));  // quad_perm [1, 0, 3, 2]
-}
-
-// 4 x 4 transpose of dwords inside each lane quad: lane v of a quad ends with
-// dword v of every lane w of its quad (as its dword w).
-__device__ __forceinline__ i32x4 quad_transpose(i32x4 m, int lane) {
-    const int v = lane & 3;
-    i32x4 n1, n2;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const int t = dpp<0xB1>(m[d ^ 1]);  // lane v ^ 1's dword d ^ 1
-        n1[d] = ((v ^ d) & 1) ? t : m[d];
-    }
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const int t = dpp<0x4E>(n1[d ^ 2]);  // quad_perm [2, 3, 0, 1]: lane v ^ 2's dword d ^ 2
-        n2[d] = ((v ^ d) & 2) ? t : n1[d];
-    }
-    return n2;
 }
 
 template <bool SCALAR>
@@ -195,10 +178,10 @@ __device__ __forceinline__ void prep2_load(const Prep2Params& p, int64_t t0, int
     in.b = (tid < Lc) ? p.beta[r0 + (int64_t)tid * p.H] : 0.f;
 }
 
-template <bool SCALAR>
+template <bool SCALAR, bool ORD1>
 __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
     using namespace p2;
-    typedef WsBlock<DK, C> WS;
+    typedef WsBlock<DK, C, ORD1> WS;
     typedef Mma<bf16> M;
     __shared__ Prep2Lds s;
 
@@ -214,6 +197,10 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
     }
     for (int e = tid; e < C * LDA; e += NT) s.P2b[e] = 0.f;
     if (tid < 16) s.ones[tid] = 1.f;
+    if (ORD1) {  // L diag(b) = -I for the whole walk
+        lds_barrier();
+        if (tid < C) s.LbT[tid * LDC + kperm(tid)] = (bf16)-1.f;
+    }
 
     auto next_item = [&](int it, int64_t& t0, int& Lc, int& h) {
         while (it < p.items && !prep2_locate(p, it, t0, Lc, h)) it += gridDim.x;
@@ -286,13 +273,13 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
             const Vec2<bf16>::type qv = __builtin_bit_cast(Vec2<bf16>::type, in.q[j]);
             const f32x2 k = f32x2{Vec2<bf16>::lo(kv), Vec2<bf16>::hi(kv)};
             const f32x2 q = f32x2{Vec2<bf16>::lo(qv), Vec2<bf16>::hi(qv)};
-            kr[j] = k * (E[j] * ai[j]);   // k e^{g_{t-1} - mu}
+            kr[j] = ORD1 ? k * E[j] : k * (E[j] * ai[j]);  // k e^{g_{t-1} - mu} (ORD1: g_t)
             qr[j] = q * E[j];             // q e^{g_t - mu}
             kce[j] = k * (Ei[j] * a[j]);  // k e^{mu - g_{t-1}}
             kci[j] = k * Ei[j];           // k e^{mu - g_t}
             store2(&s.u.g.Kr[t * LDK + 2 * c2], kr[j][0], kr[j][1]);
             store2(&s.u.g.Qr[t * LDK + 2 * c2], qr[j][0], qr[j][1]);
-            store2(&s.u.g.Kce[t * LDK + 2 * c2], kce[j][0], kce[j][1]);
+            if (!ORD1) store2(&s.u.g.Kce[t * LDK + 2 * c2], kce[j][0], kce[j][1]);
             store2(&s.u.g.Kci[t * LDK + 2 * c2], kci[j][0], kci[j][1]);
         }
         lds_barrier();
@@ -329,15 +316,17 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
                 f32x4 kc0, kc1, kt0, kt1;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    kc0[j] = kce[j][e] * ec[e];
-                    kc1[j] = kce[4 + j][e] * ec[e];
+                    kc0[j] = (ORD1 ? kci[j][e] : kce[j][e]) * ec[e];
+                    kc1[j] = (ORD1 ? kci[4 + j][e] : kce[4 + j][e]) * ec[e];
                     kt0[j] = kci[j][e] * ec[e] * s.beta[8 * o + j];
                     kt1[j] = kci[4 + j][e] * ec[e] * s.beta[8 * o + 4 + j];
                 }
                 store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c, pos0)), kc0);
                 store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c, pos1)), kc1);
-                store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos0)), kt0);
-                store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos1)), kt1);
+                if (!ORD1) {
+                    store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos0)), kt0);
+                    store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos1)), kt1);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -362,11 +351,12 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
         // ---- B: Gram products.  Wavefront g forms product g (0 A, 1 L, 2 P1, 3 P2) for
         //      the block pairs (0,0), (1,0) and (1,1) from 16 fragments read at once; rows
         //      of block 1 are scaled by F for the off-diagonal pair -------------------------
-        {
+        //      ORD1: only A (wavefront 0, columns Kt) and P2 (wavefront 3, unscaled, into P1)
+        if (!ORD1 || wv == 0 || wv == 3) {
             const int g = wv;
             constexpr int NK = DK / M::K;
             const bf16* rows = g < 2 ? s.u.g.Kr : s.u.g.Qr;
-            const bf16* cols = (g & 1) == 0 ? s.u.g.Kce : s.u.g.Kci;
+            const bf16* cols = (g & 1) == 0 && !ORD1 ? s.u.g.Kce : s.u.g.Kci;
             M::frag r0[NK], r1[NK], c0[NK], c1[NK], r1f[NK];
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
@@ -404,7 +394,7 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) m[r] = (g == 0 ? i0 + r < t : i0 + r <= t) ? acc[r] : 0.f;
                     if (g == 0) *reinterpret_cast<f32x4*>(&s.A[t * LDA + i0]) = s.beta[t] * m;
-                    else if (g == 2) store4(&s.P1[t * LDC + i0], m);
+                    else if (g == 2 || ORD1) store4(&s.P1[t * LDC + i0], m);
                     else *reinterpret_cast<f32x4*>(&s.P2b[t * LDA + i0]) =
                              m * *reinterpret_cast<const f32x4*>(&s.beta[i0]);
                 }
@@ -472,7 +462,6 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) { rfr[i] = (bf16)r0[i]; rfr[4 + i] = (bf16)r1[i]; }
             const M::frag tbf = M::loadr(s.Tb + t * LDC, lane);
-            typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int cp = 2 * half + cc;  // 32-channel block
@@ -526,10 +515,13 @@ hipError_t launch_prep2(const PrepLaunch& a, hipStream_t stream) {
     int64_t blocks = (int64_t)cus * 2;
     if (blocks > p.items) blocks = p.items;
     if (blocks < 1) blocks = 1;
+    // order 1 comes with per-channel decay only (the host maps scalar decay to order 0)
     if (a.scalar)
-        hipLaunchKernelGGL((kda_prep2_kernel<true>), dim3((unsigned)blocks), dim3(p2::NT), 0, stream, p);
+        hipLaunchKernelGGL((kda_prep2_kernel<true, false>), dim3((unsigned)blocks), dim3(p2::NT), 0, stream, p);
+    else if (a.order)
+        hipLaunchKernelGGL((kda_prep2_kernel<false, true>), dim3((unsigned)blocks), dim3(p2::NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((kda_prep2_kernel<false>), dim3((unsigned)blocks), dim3(p2::NT), 0, stream, p);
+        hipLaunchKernelGGL((kda_prep2_kernel<false, false>), dim3((unsigned)blocks), dim3(p2::NT), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -33,14 +33,14 @@
 
 namespace kda {
 
-template <int DK, int DVS, int CB>
+template <int DK, int DVS, int CB, bool ORD1 = false>
 struct ScanCfg {
     static constexpr int C = 32;
     static constexpr int NW = DVS / (16 * CB);       // compute wavefronts
     static constexpr int NL = 2;                     // copy wavefronts
     static constexpr int NT = WAVE * (NW + NL);
     static constexpr int LT = WAVE * NL;             // copy threads
-    static constexpr int BYTES = WsBlock<DK, C>::BYTES;
+    static constexpr int BYTES = WsBlock<DK, C, ORD1>::BYTES;
     static constexpr int NPB = BYTES / 16;           // 16-byte pieces of an operator block
     static constexpr int VPR = DVS / 8;              // pieces per value row of the slice
     static constexpr int NPV = C * VPR;              // pieces of a chunk's value tile
@@ -85,11 +85,12 @@ __device__ __forceinline__ void slot_barrier() {
 }
 
 // SNAP: the call asks for state snapshots (a separate instantiation, so that
-// the plain walk carries no snapshot code).
-template <int DK, int DVS, int CB, bool SNAP>
-__global__ void __launch_bounds__((ScanCfg<DK, DVS, CB>::NT), 1) kda_scan_kernel(ScanParams p) {
-    typedef ScanCfg<DK, DVS, CB> G;
-    typedef WsBlock<DK, G::C> WS;
+// the plain walk carries no snapshot code).  ORD1: decay-first blocks (no KT V
+// term in the state update).
+template <int DK, int DVS, int CB, bool SNAP, bool ORD1>
+__global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_kernel(ScanParams p) {
+    typedef ScanCfg<DK, DVS, CB, ORD1> G;
+    typedef WsBlock<DK, G::C, ORD1> WS;
     constexpr int C = G::C, LT = G::LT, ROUNDS = G::ROUNDS;
     constexpr int NR = DK / 16, NKS = DK / 32, NTT = C / 16;
     constexpr int RBK = 2 * DK, RBC = 2 * C;  // row bytes of token-row and channel-row operators
@@ -260,95 +261,104 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB>::NT), 1) kda_scan_kernel
     };
     if (nch > 0) read_group1(lds);
 
-    for (int jj = 0; jj < nch; ++jj) {
-        const uint8_t* B = lds + (jj % G::NBUF) * G::SLOT;
+    // Chunks run in stretches that end at the snapshot points (one stretch of all
+    // chunks without snapshots), so the snapshot store sits outside the chunk loop.
+    int jj = 0;
+    while (jj < nch) {
+        const int jend = SNAP ? min(nch, jj + snap_cd) : nch;
+        for (; jj < jend; ++jj) {
+            const uint8_t* B = lds + (jj % G::NBUF) * G::SLOT;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vfr[cb][e] = vraw[cb][e];
-        __builtin_amdgcn_sched_barrier(0);
+                for (int e = 0; e < 8; ++e) vfr[cb][e] = vraw[cb][e];
+            __builtin_amdgcn_sched_barrier(0);
 
-        // E = -(W S + M1 V): rows tokens, column j (lane)
-        f32x4 z[CB][NTT];
+            // E = -(W S + M1 V): rows tokens, column j (lane)
+            f32x4 z[CB][NTT];
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt)
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    f32x4 x = Mma<bf16>::mma(m1f[tt], vfr[cb], zero4());
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) x = Mma<bf16>::mma(wf[tt][ks], sfr[cb][ks], x);
+                    z[cb][tt] = x;
+                }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // group 2: state-update operands, in flight during the O products
+            bf16x8 ktf[NR], kcf[NR];
+            f32x4 gmv[NR];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                if (!ORD1) ktf[r] = frag(B + oC + WS::KT + 16 * r * RBC);
+                kcf[r] = frag(B + oC + WS::KC + 16 * r * RBC);
+                gmv[r] = *reinterpret_cast<const f32x4*>(B + oG + 64 * r);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // O^T = S^T QP^T + V^T M2^T with the state at the chunk start
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    f32x4 x = Mma<bf16>::mma(vfr[cb], m2f[tt], zero4());
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) x = Mma<bf16>::mma(sfr[cb][ks], qpf[tt][ks], x);
+                    ot[cb][tt] = x;
+                }
+            bf16x8 efr[CB], vkeep[CB];
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                f32x4 x = Mma<bf16>::mma(m1f[tt], vfr[cb], zero4());
+                vkeep[cb] = vfr[cb];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) x = Mma<bf16>::mma(wf[tt][ks], sfr[cb][ks], x);
-                z[cb][tt] = x;
+                for (int i = 0; i < 4; ++i) {
+                    efr[cb][i] = (bf16)(-z[cb][0][i]);
+                    efr[cb][4 + i] = (bf16)(-z[cb][1][i]);
+                }
             }
-        __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
 
-        // group 2: state-update operands, in flight during the O products
-        bf16x8 ktf[NR], kcf[NR];
-        f32x4 gmv[NR];
+            // This chunk's LDS reads have all returned; the barrier frees its slot
+            // for the copy wavefronts and publishes chunk jj + 1.
+            slot_barrier<63>();
+            // next chunk's group 1 (after the last chunk: a harmless read of a stale slot)
+            read_group1(lds + ((jj + 1) % G::NBUF) * G::SLOT);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // S <- Diag(GAM) S + KT V + KC E   (decay-first blocks: no KT V)
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            ktf[r] = frag(B + oC + WS::KT + 16 * r * RBC);
-            kcf[r] = frag(B + oC + WS::KC + 16 * r * RBC);
-            gmv[r] = *reinterpret_cast<const f32x4*>(B + oG + 64 * r);
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    f32x4 x = acc[cb][r] * gmv[r];
+                    if (!ORD1) x = Mma<bf16>::mma(ktf[r], vkeep[cb], x);
+                    acc[cb][r] = Mma<bf16>::mma(kcf[r], efr[cb], x);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            make_sfr();
+
+            o_t0 = tb + (p.chunk0 + jj) * C;
+            o_Lc = (int)((te - o_t0) < C ? (te - o_t0) : C);
+            store_o();
         }
-        __builtin_amdgcn_sched_barrier(0);
-
-        // O^T = S^T QP^T + V^T M2^T with the state at the chunk start
+        if (SNAP) {
+            // jj chunks done: a snapshot point unless the walk ended first
+            if ((p.chunk0 + jj) % snap_ec == 0) {
+                const int64_t done = (p.chunk0 + jj) * C;  // tokens of the sequence behind this state
+                const int64_t row = snap0 + done / p.snap_every - 1;
+                if (done <= te - tb && row < p.snap_rows) {
+                    float* dst = p.snap + (row * H + h) * DK * DV + dv0 + 16 * wv * CB;
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt)
+                    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                f32x4 x = Mma<bf16>::mma(vfr[cb], m2f[tt], zero4());
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) x = Mma<bf16>::mma(sfr[cb][ks], qpf[tt][ks], x);
-                ot[cb][tt] = x;
+                        for (int r = 0; r < NR; ++r)
+                            store_state_tile(dst + 16 * cb + (int64_t)16 * r * DV, DV, lane, acc[cb][r]);
+                }
             }
-        bf16x8 efr[CB], vkeep[CB];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            vkeep[cb] = vfr[cb];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                efr[cb][i] = (bf16)(-z[cb][0][i]);
-                efr[cb][4 + i] = (bf16)(-z[cb][1][i]);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        // This chunk's LDS reads have all returned; the barrier frees its slot
-        // for the copy wavefronts and publishes chunk jj + 1.
-        slot_barrier<63>();
-        // next chunk's group 1 (after the last chunk: a harmless read of a stale slot)
-        read_group1(lds + ((jj + 1) % G::NBUF) * G::SLOT);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // S <- Diag(GAM) S + KT V + KC E
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                f32x4 x = acc[cb][r] * gmv[r];
-                x = Mma<bf16>::mma(ktf[r], vkeep[cb], x);
-                acc[cb][r] = Mma<bf16>::mma(kcf[r], efr[cb], x);
-            }
-        __builtin_amdgcn_sched_barrier(0);
-        make_sfr();
-
-        if (SNAP && --snap_cd == 0) {
             snap_cd = snap_ec;
-            const int64_t done = (p.chunk0 + jj + 1) * C;  // tokens of the sequence behind this state
-            const int64_t row = snap0 + done / p.snap_every - 1;
-            if (done <= te - tb && row < p.snap_rows) {
-                float* dst = p.snap + (row * H + h) * DK * DV + dv0 + 16 * wv * CB + lr;
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) store_state_tile(dst + 16 * cb + (int64_t)16 * r * DV, DV, lg, acc[cb][r]);
-            }
         }
-
-        o_t0 = tb + (p.chunk0 + jj) * C;
-        o_Lc = (int)((te - o_t0) < C ? (te - o_t0) : C);
-        store_o();
     }
 
 #pragma unroll
@@ -360,7 +370,7 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB>::NT), 1) kda_scan_kernel
 }
 
 // ------------------------------------------------------------------------------------
-template <int DK, int DVS, int CB>
+template <int DK, int DVS, int CB, bool ORD1>
 static hipError_t scan_cfg(const ScanLaunch& a, hipStream_t stream) {
     ScanParams p;
     p.v = a.v; p.o = a.o; p.cu = a.cu_seqlens; p.eq_len = a.eq_len;
@@ -369,18 +379,21 @@ static hipError_t scan_cfg(const ScanLaunch& a, hipStream_t stream) {
     p.snap = a.snap; p.snap_rows = a.snap_rows; p.snap_every = a.snap_every;
     const int64_t blocks = (int64_t)a.units * a.split;
     p.xcd_group = (a.split > 1 && blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
+    constexpr int NT = ScanCfg<DK, DVS, CB, ORD1>::NT;
     if (a.snap)
-        hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, CB, true>), dim3((unsigned)blocks),
-                           dim3(ScanCfg<DK, DVS, CB>::NT), 0, stream, p);
+        hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, CB, true, ORD1>), dim3((unsigned)blocks), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, CB, false>), dim3((unsigned)blocks),
-                           dim3(ScanCfg<DK, DVS, CB>::NT), 0, stream, p);
+        hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, CB, false, ORD1>), dim3((unsigned)blocks), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 
 // Compiled slices: 16-column slices use one block per wavefront; wider ones two.
-#define KDA_SCAN_CASE(DK_, DVS_, CB_) \
-    if (dk == DK_ && dvs == DVS_) { if (a) *err = scan_cfg<DK_, DVS_, CB_>(*a, stream); return true; }
+#define KDA_SCAN_CASE(DK_, DVS_, CB_)                                                                 \
+    if (dk == DK_ && dvs == DVS_) {                                                                   \
+        if (a) *err = a->order ? scan_cfg<DK_, DVS_, CB_, true>(*a, stream)                         \
+                               : scan_cfg<DK_, DVS_, CB_, false>(*a, stream);                       \
+        return true;                                                                                  \
+    }
 
 static bool scan_dispatch(int dk, int dvs, int chunk, const ScanLaunch* a, hipStream_t stream, hipError_t* err) {
     if (chunk != 32) return false;
@@ -390,7 +403,7 @@ static bool scan_dispatch(int dk, int dvs, int chunk, const ScanLaunch* a, hipSt
 }
 
 bool two_pass_supported(int dtype, int dk, int dvs, int chunk) {
-    return dtype == 1 && prep_block_bytes(dk, chunk) > 0 && scan_dispatch(dk, dvs, chunk, nullptr, nullptr, nullptr);
+    return dtype == 1 && prep_block_bytes(dk, chunk, 0) > 0 && scan_dispatch(dk, dvs, chunk, nullptr, nullptr, nullptr);
 }
 
 hipError_t launch_scan(const ScanLaunch& a, hipStream_t stream) {

@@ -13,6 +13,15 @@
 // so that the sequential pass computes, per chunk and value column block,
 //   E = -(W S + M1 V),  O = QP S + M2 V,  S <- Diag(GAM) S + KC E + KT V.
 //
+// The decay-first ordering (S <- (I - b k^T k) Diag(a) S + b k^T v) has no
+// write term outside E, and its blocks (ORD1) hold no KT:
+//   W   T diag(b) Kd           with Kd = K e^{g_t}
+//   QP  Qb - R Kd              with R = lower(Qb Kx^T) T diag(b), Kx = K e^{-g_t}
+//   KC  (Kx Diag(e^{g_C}))^T
+//   M1  -T diag(b)
+//   M2  R
+// so that E = T diag(b) (V - Kd S) and S <- Diag(GAM) S + KC E.
+//
 // Every matrix is stored as the matrix-core operand it becomes: its rows are
 // the operand's m (or n) index, and its contraction index (columns) is
 // permuted inside each 32-wide block so that a 16 x 16 accumulator tile pair
@@ -29,13 +38,13 @@
 
 namespace kda {
 
-template <int DK, int C>
+template <int DK, int C, bool ORD1 = false>
 struct WsBlock {
     static constexpr int W = 0;
     static constexpr int QP = W + C * DK * 2;
     static constexpr int KC = QP + C * DK * 2;
-    static constexpr int KT = KC + DK * C * 2;
-    static constexpr int M1 = KT + DK * C * 2;
+    static constexpr int KT = KC + DK * C * 2;   // absent (zero bytes) in ORD1 blocks
+    static constexpr int M1 = KT + (ORD1 ? 0 : DK * C * 2);
     static constexpr int M2 = M1 + C * C * 2;
     static constexpr int GAM = M2 + C * C * 2;
     static constexpr int BYTES = (GAM + DK * 4 + 255) / 256 * 256;  // 256-byte aligned blocks

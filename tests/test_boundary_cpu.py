@@ -42,7 +42,7 @@ def test_every_declared_symbol_exported(lib):
 
 def dims(**kw):
     base = dict(num_seqs=2, num_heads=4, total_tokens=128, dk=128, dv=128, qkv_dtype=1,
-                scalar_decay=0, chunk_size=0, dv_split=0, method=0, reserved=0, max_seqlen=0)
+                scalar_decay=0, chunk_size=0, dv_split=0, method=0, order=0, max_seqlen=0)
     base.update(kw)
     return kda._Dims(**base)
 
@@ -83,7 +83,8 @@ def decode(lib, d, q=GOOD, k=GOOD, v=GOOD, la=GOOD, beta=GOOD, Si=GOOD, So=GOOD,
     (dict(d=dims(num_seqs=0, total_tokens=5)), INVALID),
     (dict(d=dims(num_seqs=0, total_tokens=0), q=None, cu=None), OK),  # nothing to do
     (dict(d=dims(method=3)), INVALID),
-    (dict(d=dims(reserved=1)), INVALID),
+    (dict(d=dims(order=2)), INVALID),
+    (dict(d=dims(order=-1)), INVALID),
     (dict(d=dims(max_seqlen=-1)), INVALID),
     (dict(d=dims(method=2, qkv_dtype=0, dk=64, dv=64)), UNSUPPORTED),  # two-pass is bf16 only
     (dict(d=dims(method=2)), INVALID),                                   # no workspace
@@ -114,6 +115,7 @@ def prefill_snap(lib, d, snaps=GOOD, rows=4, every=64, cu=GOOD):
     (dict(snaps=None), INVALID),                        # rows but no buffer
     (dict(rows=-1), INVALID),
     (dict(snaps=GOOD + 2), MISALIGNED),
+    (dict(snaps=GOOD + 4), MISALIGNED),
     (dict(every=1 << 40), INVALID),
     (dict(d=dims(num_seqs=0, total_tokens=0)), OK),     # nothing to do
     (dict(d=dims(num_seqs=0, total_tokens=0), every=0, snaps=None, rows=0), OK),
@@ -129,6 +131,7 @@ def test_snapshot_validation(lib, case, expect):
     (dict(d=dims(total_tokens=2), Si=None), INVALID),
     (dict(d=dims(total_tokens=2), So=GOOD + 4), MISALIGNED),
     (dict(d=dims(total_tokens=2, dk=24)), UNSUPPORTED),
+    (dict(d=dims(total_tokens=2, order=3)), INVALID),
     (dict(d=dims(num_seqs=0, total_tokens=0), q=None), OK),
 ])
 def test_decode_validation(lib, case, expect):
@@ -183,3 +186,17 @@ def test_snapshot_rows_counts_whole_intervals():
     assert kda.snapshot_rows(None, 64, total_tokens=0, num_seqs=0) == 0
     with pytest.raises(ValueError):
         kda.snapshot_rows([0, 10], 0)
+
+
+def test_decay_first_blocks_hold_no_write_operator(lib):
+    """Decay-first operator blocks drop the dk x C write operator: at dk = 128,
+    C = 32 a block is 8192 bytes smaller.  With a scalar decay both orders run
+    the same kernels and need the same workspace."""
+    def least(**kw):
+        n = ctypes.c_size_t(0)
+        assert lib.kda_chunk_workspace_min(ctypes.byref(dims(**kw)), ctypes.byref(n)) == OK
+        return n.value
+    units = 2 * 4
+    assert least(order=0) - least(order=1) == units * 8192
+    assert least(order=0, dk=64, dv=64) - least(order=1, dk=64, dv=64) == units * 4096
+    assert least(order=1, scalar_decay=1) == least(order=0, scalar_decay=1)
