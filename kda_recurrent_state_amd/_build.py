@@ -20,6 +20,11 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=fast",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-fvisibility=hidden", "-Wno-unused-result", "-I" + os.path.join(os.path.dirname(HERE), "include")]
+# The state pass runs one workgroup per compute unit, so each wavefront may use
+# accumulator registers on top of its 256 vector registers; left to itself the
+# compiler then keeps matrix-core results there and copies the state back and
+# forth every chunk.  This keeps them in vector registers (the walk fits).
+EXTRA = {"kda_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -37,7 +42,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"]
-        cmd = [hipcc, *lang, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *lang, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -25,7 +25,10 @@
 // j + 1 with a vector-memory counter wait, and the workgroup barrier in the
 // middle of chunk j makes them visible to all wavefronts and frees chunk j's
 // slot.  The next chunk's first operands are read right after that barrier,
-// so their LDS latency is hidden behind the state update of chunk j.
+// so their LDS latency is hidden behind the state update of chunk j.  The
+// compute wavefronts issue no global memory operations in the walk: they leave
+// each chunk's outputs in its slot's value tile (already read by then), and the
+// copy wavefronts store them, 16 bytes per lane, before they refill the slot.
 #include "kda_device.hpp"
 #include "kda_chunk_common.hpp"
 #include "kda_launch.hpp"
@@ -49,10 +52,13 @@ struct ScanCfg {
     static constexpr int SLOT = ROUNDS * LT * 16;    // LDS bytes per slot (copies past NPS land in the pad)
     // slots: four (copies three chunks ahead) where they fit in LDS and the
     // counter wait can express them, else three
-    static constexpr int NBUF = (4 * SLOT <= 160 * 1024 && 2 * ROUNDS < 64) ? 4 : 3;
+    static constexpr int NBUF = (4 * SLOT <= 160 * 1024 && 2 * ROUNDS + 3 < 64) ? 4 : 3;
     static constexpr int AHEAD = NBUF - 1;
+    static constexpr int TOUCH = 2;                  // L2 touches run this many chunks past AHEAD
+    static constexpr int PAD = SLOT - NPS * 16;      // unread tail of every slot
     static_assert(BYTES % 16 == 0, "operator blocks are whole 16-byte pieces");
     static_assert(NW >= 1 && NW * 16 * CB == DVS, "slice = wavefronts x column blocks x 16");
+    static_assert(PAD >= 4 * WAVE && NL <= NBUF, "each copy wavefront's touches land in a slot's pad");
 };
 
 struct ScanParams {
@@ -154,21 +160,61 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
             __builtin_amdgcn_global_load_lds(src, slot + r * LT * 16, 16, 0, 0);
         }
     };
+    // Touch the operator block of chunk jj into L2 (HBM latency is what limits
+    // the copies otherwise): one dword per 128-byte line, slice s taking lines
+    // s, s + split, ... (the slices of a head share the block through L2), one
+    // instruction per copy wavefront.  The dwords land in the pad of slot lw.
+    auto touch = [&](int jj) {
+        constexpr int LINES = (G::BYTES + 127) / 128;
+        const int nb = (LINES - slice + p.split - 1) / p.split;  // this slice's lines (>= 1)
+        const int line = min(lt, nb - 1) * p.split + slice;
+        __builtin_amdgcn_global_load_lds(wsu + (size_t)jj * G::BYTES + 128 * line, lds + lw * G::SLOT + G::NPS * 16,
+                                         4, 0, 0);
+    };
+    // Store chunk jj's outputs, which the compute wavefronts left in the value
+    // tile of its slot sl: each lane stores the 16-byte pieces that its own copy
+    // into that slot will overwrite next, so it reads them before it issues the
+    // copy (rows past the chunk's end are skipped).
+    auto store_out = [&](int jj, int sl) {
+        const int64_t t0 = tb + (p.chunk0 + jj) * C;
+        const int Lc = (int)((te - t0) < C ? (te - t0) : C);
+        const uint8_t* slot = lds + sl * G::SLOT;
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
+            if ((r + 1) * LT <= G::NPB || r * LT >= G::NPS) continue;  // rounds without output pieces
+            const int pc = r * LT + lt;
+            const int q = pc - G::NPB, t = q / G::VPR, u = q % G::VPR;
+            if (pc >= G::NPB && pc < G::NPS && t < Lc) {
+                const i32x4 x = *reinterpret_cast<const i32x4*>(slot + 16 * pc);
+                *reinterpret_cast<i32x4*>(go + ((t0 + t) * H + h) * DV + dv0 + 8 * u) = x;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 0xF);  // lgkmcnt(0): pieces read before the copy lands
+        asm volatile("" ::: "memory");
+    };
 
     if (wv >= G::NW) {
-        // ---- copy wavefronts: chunk jj + AHEAD is copied during chunk jj; before
-        // the barrier of chunk jj, chunk jj + 1's copies (the oldest in flight) are
-        // waited for.  One barrier before the walk and one per chunk, like the
-        // compute wavefronts.
+        // ---- copy wavefronts: chunk jj + AHEAD is copied during chunk jj and chunk
+        // jj + AHEAD + TOUCH touched; before the barrier of chunk jj, chunk jj + 1's
+        // copies are waited for: younger are the copies of AHEAD - 1 chunks and AHEAD
+        // touches (one follows every copy), and loads complete in order.  One barrier
+        // before the walk and one per chunk, like the compute wavefronts.
         if (nch > 0) {
 #pragma unroll
-            for (int c = 0; c < G::AHEAD; ++c) copy(min(c, nch - 1), c);
+            for (int c = 0; c < G::AHEAD; ++c) {
+                copy(min(c, nch - 1), c);
+                touch(min(c + G::TOUCH, nch - 1));
+            }
         }
-        slot_barrier<(G::AHEAD - 1) * ROUNDS>();
+        slot_barrier<(G::AHEAD - 1) * ROUNDS + G::AHEAD>();
         for (int jj = 0; jj < nch; ++jj) {
+            // the slot refilled now is chunk jj - 1's: its outputs leave first
+            if (jj > 0) store_out(jj - 1, (jj - 1) % G::NBUF);
             copy(min(jj + G::AHEAD, nch - 1), (jj + G::AHEAD) % G::NBUF);
-            slot_barrier<(G::AHEAD - 1) * ROUNDS>();
+            touch(min(jj + G::AHEAD + G::TOUCH, nch - 1));
+            slot_barrier<(G::AHEAD - 1) * ROUNDS + G::AHEAD>();
         }
+        if (nch > 0) store_out(nch - 1, (nch - 1) % G::NBUF);
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no copy outlives the workgroup
         return;
     }
@@ -215,27 +261,20 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
 
     slot_barrier<0>();
 
-    // outputs of the chunk just computed (bf16, rows past the chunk end skipped)
+    // outputs of a chunk go (bf16) into the value tile of its slot, which the
+    // value fragments have left by then; the copy wavefronts store them
     f32x4 ot[CB][NTT];
-    int64_t o_t0 = 0;
-    int o_Lc = 0;
-    const int64_t o_lane = (int64_t)lr * H * DV + 16 * wv * CB + 4 * lg;
-    auto store_o = [&]() {
-        bf16* base = go + (o_t0 * H + h) * DV + dv0 + o_lane;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int tt = 0; tt < NTT; ++tt)
-                if (16 * tt + lr < o_Lc) store4(base + (int64_t)16 * tt * H * DV + 16 * cb, ot[cb][tt]);
-    };
+    const uint32_t oO = G::NPB * 16 + 2 * (lr * DVS + 16 * wv * CB + 4 * lg);  // [token][column]
 
     auto frag = [](const uint8_t* a) { return *reinterpret_cast<const bf16x8*>(a); };
-    // Group 1 of a chunk: the E and O operands and the value fragment (column j
-    // of the block, tokens in the permuted order: positions 8 lg .. 8 lg + 7 hold
-    // tokens 4 lg .. 4 lg + 3 and 16 + 4 lg .. 16 + 4 lg + 3).  It is read right
-    // after the barrier that publishes the chunk, while the previous chunk's
-    // state update runs on the matrix cores.
-    bf16x8 wf[NTT][NKS], m1f[NTT], qpf[NTT][NKS], m2f[NTT], vfr[CB];
+    // Group 1 of a chunk: the E operands and the value fragment (column j of the
+    // block, tokens in the permuted order: positions 8 lg .. 8 lg + 7 hold tokens
+    // 4 lg .. 4 lg + 3 and 16 + 4 lg .. 16 + 4 lg + 3).  It is read right after
+    // the barrier that publishes the chunk, while the previous chunk's state
+    // update runs on the matrix cores.  The O operands are read with group 2,
+    // which keeps the registers live across the state update within the
+    // register file (no accumulator-register round trips).
+    bf16x8 wf[NTT][NKS], m1f[NTT], vfr[CB];
     bf16 vraw[CB][8];  // value elements as read; packed into vfr where first used
     auto read_group1 = [&](const uint8_t* B) {
         const bf16* bV = reinterpret_cast<const bf16*>(B + oV);
@@ -252,12 +291,6 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) wf[tt][ks] = frag(B + oW[ks] + WS::W + 16 * tt * RBK);
         }
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-            m2f[tt] = frag(B + oC + WS::M2 + 16 * tt * RBC);
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) qpf[tt][ks] = frag(B + oW[ks] + WS::QP + 16 * tt * RBK);
-        }
     };
     if (nch > 0) read_group1(lds);
 
@@ -267,7 +300,7 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
     while (jj < nch) {
         const int jend = SNAP ? min(nch, jj + snap_cd) : nch;
         for (; jj < jend; ++jj) {
-            const uint8_t* B = lds + (jj % G::NBUF) * G::SLOT;
+            uint8_t* B = lds + (jj % G::NBUF) * G::SLOT;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -287,9 +320,16 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
                 }
             __builtin_amdgcn_sched_barrier(0);
 
-            // group 2: state-update operands, in flight during the O products
-            bf16x8 ktf[NR], kcf[NR];
+            // group 2: the O operands, then the state-update operands (in flight
+            // during the O products)
+            bf16x8 qpf[NTT][NKS], m2f[NTT], ktf[NR], kcf[NR];
             f32x4 gmv[NR];
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+                m2f[tt] = frag(B + oC + WS::M2 + 16 * tt * RBC);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) qpf[tt][ks] = frag(B + oW[ks] + WS::QP + 16 * tt * RBK);
+            }
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 if (!ORD1) ktf[r] = frag(B + oC + WS::KT + 16 * r * RBC);
@@ -318,10 +358,17 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
                     efr[cb][4 + i] = (bf16)(-z[cb][1][i]);
                 }
             }
+            // outputs into this slot's value tile, stored by the copy wavefronts
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+                    store4(reinterpret_cast<bf16*>(B + oO + 2 * (16 * tt * DVS + 16 * cb)),
+                           ot[cb][tt]);
             __builtin_amdgcn_sched_barrier(0);
 
-            // This chunk's LDS reads have all returned; the barrier frees its slot
-            // for the copy wavefronts and publishes chunk jj + 1.
+            // This chunk's LDS reads and output writes are done; the barrier hands
+            // its slot to the copy wavefronts and publishes chunk jj + 1.
             slot_barrier<63>();
             // next chunk's group 1 (after the last chunk: a harmless read of a stale slot)
             read_group1(lds + ((jj + 1) % G::NBUF) * G::SLOT);
@@ -338,10 +385,6 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
                 }
             __builtin_amdgcn_sched_barrier(0);
             make_sfr();
-
-            o_t0 = tb + (p.chunk0 + jj) * C;
-            o_Lc = (int)((te - o_t0) < C ? (te - o_t0) : C);
-            store_o();
         }
         if (SNAP) {
             // jj chunks done: a snapshot point unless the walk ended first
