@@ -283,14 +283,15 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
                 prev = ri;
                 prevc = ci;
             }
-            const int pos = kperm(4 * tg);
+            // KC, KT: tokens 4 tg .. 4 tg + 3 are half of piece tg / 2 of channel row c + e
+            const int half = 8 * (tg & 1);
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 store4(&s.KbT[(c + e) * LDC + 4 * tg], f32x4{kb[0][e], kb[1][e], kb[2][e], kb[3][e]});
-                store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c + e, pos)),
+                store4(reinterpret_cast<bf16*>(blk + WS::KC + piece<DK>(c + e, tg >> 1) + half),
                        f32x4{kc[0][e], kc[1][e], kc[2][e], kc[3][e]});
                 if (!ORD1)
-                    store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c + e, pos)),
+                    store4(reinterpret_cast<bf16*>(blk + WS::KT + piece<DK>(c + e, tg >> 1) + half),
                            f32x4{kt[0][e], kt[1][e], kt[2][e], kt[3][e]});
             }
         }
@@ -401,10 +402,10 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
             const int t = 16 * tt + lrow, a0 = 16 * ra + 4 * lgrp;
             const int an = 16 * ra + lrow, t0n = 16 * tt + 4 * lgrp;
             if (isw) {
-                store4(reinterpret_cast<bf16*>(blk + WS::W + swz_elem<2 * DK>(t, kperm(a0))), xt);
+                store4(reinterpret_cast<bf16*>(blk + WS::W + swz_elem<2 * DK>(kinv(t), kperm(a0))), xt);
                 store4(&s.u.w.WT[an * LDC + t0n], xn);
             } else {
-                store4(reinterpret_cast<bf16*>(blk + WS::M1 + swz_elem<2 * C>(t, kperm(a0))), xt);
+                store4(reinterpret_cast<bf16*>(blk + WS::M1 + piece<C>(kinv(t), a0 >> 3) + 2 * (a0 & 7)), xt);
                 store4(&s.u.w.M1T[an * LDC + t0n], xn);
             }
         }
@@ -424,7 +425,7 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
                 store4(reinterpret_cast<bf16*>(blk + WS::QP + swz_elem<2 * DK>(t, kperm(a0))), qb - pw);
             } else {
                 const f32x4 p2 = *reinterpret_cast<const f32x4*>(&s.P2[t * LDA + a0]);
-                store4(reinterpret_cast<bf16*>(blk + WS::M2 + swz_elem<2 * C>(t, kperm(a0))), p2 - pw);
+                store4(reinterpret_cast<bf16*>(blk + WS::M2 + piece<C>(t, a0 >> 3) + 2 * (a0 & 7)), p2 - pw);
             }
         }
         lds_barrier();  // LDS of this chunk is reused by the next

@@ -313,20 +313,15 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
                 const int c = 2 * c2 + e;
                 store4(&s.KbT[c * LDC + pos0], kb0);
                 store4(&s.KbT[c * LDC + pos1], kb1);
-                f32x4 kc0, kc1, kt0, kt1;
+                // KC, KT: the octet's 8 tokens are piece o of channel row c
+                bf16x8 kc, kt;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    kc0[j] = (ORD1 ? kci[j][e] : kce[j][e]) * ec[e];
-                    kc1[j] = (ORD1 ? kci[4 + j][e] : kce[4 + j][e]) * ec[e];
-                    kt0[j] = kci[j][e] * ec[e] * s.beta[8 * o + j];
-                    kt1[j] = kci[4 + j][e] * ec[e] * s.beta[8 * o + 4 + j];
+                for (int j = 0; j < 8; ++j) {
+                    kc[j] = (bf16)((ORD1 ? kci[j][e] : kce[j][e]) * ec[e]);
+                    kt[j] = (bf16)(kci[j][e] * ec[e] * s.beta[8 * o + j]);
                 }
-                store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c, pos0)), kc0);
-                store4(reinterpret_cast<bf16*>(blk + WS::KC + swz_elem<2 * C>(c, pos1)), kc1);
-                if (!ORD1) {
-                    store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos0)), kt0);
-                    store4(reinterpret_cast<bf16*>(blk + WS::KT + swz_elem<2 * C>(c, pos1)), kt1);
-                }
+                *reinterpret_cast<bf16x8*>(blk + WS::KC + piece<DK>(c, o)) = kc;
+                if (!ORD1) *reinterpret_cast<bf16x8*>(blk + WS::KT + piece<DK>(c, o)) = kt;
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -477,24 +472,27 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
                     wo[r] = (bf16)w0[r]; wo[4 + r] = (bf16)w1[r];
                     qo[r] = (bf16)(q0[r] - x0[r]); qo[4 + r] = (bf16)(q1[r] - x1[r]);
                 }
-                *reinterpret_cast<bf16x8*>(blk + WS::W + swz<2 * DK>(t, 4 * cp + lg)) = wo;
+                *reinterpret_cast<bf16x8*>(blk + WS::W + swz<2 * DK>(kinv(t), 4 * cp + lg)) = wo;
                 *reinterpret_cast<bf16x8*>(blk + WS::QP + swz<2 * DK>(t, 4 * cp + lg)) = qo;
             }
-            const M::frag lb0 = M::loadr(s.LbT + lr * LDC, lane);
-            const M::frag lb1 = M::loadr(s.LbT + (16 + lr) * LDC, lane);
+            // rows i of (L diag(b))^T taken so that lane group lg ends with columns
+            // 8 lg .. 8 lg + 7 of M1 or M2 (tile 0: i = 8 lg + r, tile 1: 8 lg + 4 + r)
+            const int li = 8 * (lr >> 2) + (lr & 3);
+            const M::frag lb0 = M::loadr(s.LbT + li * LDC, lane);
+            const M::frag lb1 = M::loadr(s.LbT + (li + 4) * LDC, lane);
             bf16x8 mo;
-            if (half == 0) {  // M1 = Tb (L diag(b)): out[i][t]
+            if (half == 0) {  // M1 = Tb (L diag(b)): out[i][t], row t of M1 at W's row for t
                 const f32x4 m0 = M::mma(lb0, tbf, zero4()), m1 = M::mma(lb1, tbf, zero4());
 #pragma unroll
                 for (int r = 0; r < 4; ++r) { mo[r] = (bf16)m0[r]; mo[4 + r] = (bf16)m1[r]; }
-                *reinterpret_cast<bf16x8*>(blk + WS::M1 + swz<2 * C>(t, lg)) = mo;
+                *reinterpret_cast<bf16x8*>(blk + WS::M1 + piece<C>(kinv(t), lg)) = mo;
             } else {  // M2 = P2 diag(b) - R (L diag(b))
                 const f32x4 m0 = M::mma(lb0, rfr, zero4()), m1 = M::mma(lb1, rfr, zero4());
-                const f32x4 pa = *reinterpret_cast<const f32x4*>(&s.P2b[t * LDA + 4 * lg]);
-                const f32x4 pb = *reinterpret_cast<const f32x4*>(&s.P2b[t * LDA + 16 + 4 * lg]);
+                const f32x4 pa = *reinterpret_cast<const f32x4*>(&s.P2b[t * LDA + 8 * lg]);
+                const f32x4 pb = *reinterpret_cast<const f32x4*>(&s.P2b[t * LDA + 8 * lg + 4]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) { mo[r] = (bf16)(pa[r] - m0[r]); mo[4 + r] = (bf16)(pb[r] - m1[r]); }
-                *reinterpret_cast<bf16x8*>(blk + WS::M2 + swz<2 * C>(t, lg)) = mo;
+                *reinterpret_cast<bf16x8*>(blk + WS::M2 + piece<C>(t, lg)) = mo;
             }
         }
         lds_barrier();  // LDS of this chunk is reused by the next

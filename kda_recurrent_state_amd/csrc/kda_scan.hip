@@ -99,7 +99,7 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
     typedef WsBlock<DK, G::C, ORD1> WS;
     constexpr int C = G::C, LT = G::LT, ROUNDS = G::ROUNDS;
     constexpr int NR = DK / 16, NKS = DK / 32, NTT = C / 16;
-    constexpr int RBK = 2 * DK, RBC = 2 * C;  // row bytes of token-row and channel-row operators
+    constexpr int RBK = 2 * DK;  // row bytes of W and QP
     __shared__ alignas(16) uint8_t lds[G::NBUF * G::SLOT];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -130,9 +130,10 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
     uint32_t oW[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) oW[ks] = swz<RBK>(lr, 4 * ks + lg);  // W, QP fragments
-    const uint32_t oC = swz<RBC>(lr, lg);                                   // KC, KT, M1, M2 fragments
+    const uint32_t oM = piece<C>(lr, lg);                                   // M1, M2 fragments
+    const uint32_t oK = piece<DK>(lr, lg);                                  // KC, KT fragments
     const uint32_t oG = WS::GAM + 16 * lg;                                  // GAM rows 4 lg .. 4 lg + 3
-    const uint32_t oV = G::NPB * 16 + 2 * (4 * lg * DVS + 16 * wv * CB + lr);  // value tile [token][column]
+    const uint32_t oV = G::NPB * 16 + 2 * (8 * lg * DVS + 16 * wv * CB + lr);  // value tile [token][column]
 
     // Copy chunk jj's operator block and value tile into slot sl: piece
     // r * NT + tid of the slot comes from the block (below NPB), from the value
@@ -268,8 +269,7 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
 
     auto frag = [](const uint8_t* a) { return *reinterpret_cast<const bf16x8*>(a); };
     // Group 1 of a chunk: the E operands and the value fragment (column j of the
-    // block, tokens in the permuted order: positions 8 lg .. 8 lg + 7 hold tokens
-    // 4 lg .. 4 lg + 3 and 16 + 4 lg .. 16 + 4 lg + 3).  It is read right after
+    // value tile, tokens 8 lg .. 8 lg + 7).  It is read right after
     // the barrier that publishes the chunk, while the previous chunk's state
     // update runs on the matrix cores.  The O operands are read with group 2,
     // which keeps the registers live across the state update within the
@@ -281,13 +281,10 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vraw[cb][e] = bV[e * DVS + 16 * cb];
-                vraw[cb][4 + e] = bV[(16 + e) * DVS + 16 * cb];
-            }
+            for (int e = 0; e < 8; ++e) vraw[cb][e] = bV[e * DVS + 16 * cb];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
-            m1f[tt] = frag(B + oC + WS::M1 + 16 * tt * RBC);
+            m1f[tt] = frag(B + oM + WS::M1 + 16 * 16 * tt);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) wf[tt][ks] = frag(B + oW[ks] + WS::W + 16 * tt * RBK);
         }
@@ -307,7 +304,8 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
                 for (int e = 0; e < 8; ++e) vfr[cb][e] = vraw[cb][e];
             __builtin_amdgcn_sched_barrier(0);
 
-            // E = -(W S + M1 V): rows tokens, column j (lane)
+            // E = -(W S + M1 V): rows in W's row order, so that each lane's two
+            // accumulator quads are tokens 8 lg .. 8 lg + 7, column j (lane)
             f32x4 z[CB][NTT];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
@@ -326,14 +324,14 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
             f32x4 gmv[NR];
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
-                m2f[tt] = frag(B + oC + WS::M2 + 16 * tt * RBC);
+                m2f[tt] = frag(B + oM + WS::M2 + 16 * 16 * tt);
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) qpf[tt][ks] = frag(B + oW[ks] + WS::QP + 16 * tt * RBK);
             }
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                if (!ORD1) ktf[r] = frag(B + oC + WS::KT + 16 * r * RBC);
-                kcf[r] = frag(B + oC + WS::KC + 16 * r * RBC);
+                if (!ORD1) ktf[r] = frag(B + oK + WS::KT + 16 * 16 * r);
+                kcf[r] = frag(B + oK + WS::KC + 16 * 16 * r);
                 gmv[r] = *reinterpret_cast<const f32x4*>(B + oG + 64 * r);
             }
             __builtin_amdgcn_sched_barrier(0);

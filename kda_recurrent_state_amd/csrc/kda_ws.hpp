@@ -22,16 +22,24 @@
 //   M2  R
 // so that E = T diag(b) (V - Kd S) and S <- Diag(GAM) S + KC E.
 //
-// Every matrix is stored as the matrix-core operand it becomes: its rows are
-// the operand's m (or n) index, and its contraction index (columns) is
-// permuted inside each 32-wide block so that a 16 x 16 accumulator tile pair
-// can be fed back as an operand without leaving registers:
-//   position p = 8 * ((x % 16) / 4) + 4 * (x / 16) + x % 4   for x = index % 32
-// (lane group g of an accumulator holds rows 4g..4g+3 of each 16-row tile;
-// the operand wants 8 consecutive contraction positions 8g..8g+7 per lane).
-// The 16-byte pieces of each row are also XOR-swizzled with the row index so
-// that 16 lanes reading the same column piece of 16 rows hit distinct LDS
-// banks after a verbatim copy into LDS.
+// Every matrix is stored as the matrix-core operand it becomes.  A lane
+// group g of a 16 x 16 accumulator holds rows 4g..4g+3 of each 16-row tile,
+// and an operand lane group g wants 8 consecutive contraction positions
+// 8g..8g+7, so a tile pair fed back as an operand reads its rows in the order
+//   kperm(x) = 8 * ((x % 16) / 4) + 4 * (x / 16) + x % 4      (x = index % 32)
+// and the blocks are laid out to match:
+//   - W, QP: 32-channel blocks of their columns (the contraction with S) in
+//     kperm order; rows are 256-byte lines of 16-byte pieces XOR-swizzled by
+//     the row, so that 16 lanes reading one piece of 16 rows hit distinct LDS
+//     banks after a verbatim copy.  QP row t is token t; W row w is token
+//     kperm(w), so that the products W S come out with E's rows in that order
+//     and E feeds the state update with tokens in natural order.
+//   - M1, M2, KC, KT: token contraction in natural order, stored piece-major:
+//     the 16-byte piece holding columns 8g..8g+7 of row r sits at byte
+//     16 * (g * ROWS + r).  Rows of M1 follow W, rows of M2 follow QP; rows of
+//     KC and KT are key channels.  Operand reads of 16 consecutive rows are
+//     then 256 contiguous bytes, and the chunk-parallel pass writes whole
+//     pieces of 8 consecutive tokens.
 #pragma once
 
 #include <stdint.h>
@@ -54,6 +62,15 @@ struct WsBlock {
 __host__ __device__ constexpr int kperm(int x) {
     return (x & ~31) + 8 * ((x & 15) >> 2) + 4 * ((x & 31) >> 4) + (x & 3);
 }
+// its inverse: the index held at position p (kperm(kinv(p)) == p)
+__host__ __device__ constexpr int kinv(int p) {
+    return (p & ~31) + 16 * ((p >> 2) & 1) + 4 * ((p & 31) >> 3) + (p & 3);
+}
+static_assert(kperm(kinv(5)) == 5 && kperm(kinv(22)) == 22 && kinv(kperm(13)) == 13, "kinv inverts kperm");
+
+// byte offset of the 16-byte piece g of row r in a piece-major matrix of ROWS rows
+template <int ROWS>
+__host__ __device__ constexpr int piece(int r, int g) { return 16 * (g * ROWS + r); }
 
 // byte offset of the 16-byte piece `piece` of row `row` in a matrix whose rows
 // are RB bytes long (RB = 64, 128 or 256)
