@@ -75,8 +75,33 @@ def _f64(x) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
 
 
+# Prologue of the layer's inputs.  The pages fix no gate parameterisation; these
+# are the transforms that turn a layer's raw projections into the recurrence's
+# inputs in the usual learned gates (and in this project's input recipe): unit
+# keys, a logistic write strength, a negative-softplus log-decay.
+PROLOGUE_EPS = 1e-6
+
+
+def prologue(k, log_a, beta, normalize_k=False, beta_logits=False, log_a_raw=False, log_a_min=None):
+    """Apply the input prologue in fp64 and return (k, log_a, beta) as float64:
+      normalize_k:  k_t <- k_t / sqrt(sum_c k_tc^2 + PROLOGUE_EPS), per token and head
+      beta_logits:  beta_t <- 1 / (1 + exp(-beta_t))
+      log_a_raw:    log_a <- -softplus(log_a) = -(max(x, 0) + log(1 + exp(-|x|))),
+                    then clipped from below at log_a_min when that is given."""
+    k, log_a, beta = _f64(k), _f64(log_a), _f64(beta)
+    if normalize_k:
+        k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + PROLOGUE_EPS)
+    if beta_logits:
+        beta = 1.0 / (1.0 + np.exp(-beta))
+    if log_a_raw:
+        log_a = -(np.maximum(log_a, 0.0) + np.log1p(np.exp(-np.abs(log_a))))
+        if log_a_min is not None:
+            log_a = np.maximum(log_a, float(log_a_min))
+    return k, log_a, beta
+
+
 def kda_oracle(q, k, v, log_a, beta, S0=None, cu_seqlens=None, order: int = 0,
-               threads: int | None = None, lib=None):
+               threads: int | None = None, lib=None, pro: dict | None = None):
     """Run the fp64 recurrence.
 
     q, k: [T, H, dk]; v: [T, H, dv]; log_a: [T, H, dk] (per channel) or [T, H]
@@ -84,9 +109,13 @@ def kda_oracle(q, k, v, log_a, beta, S0=None, cu_seqlens=None, order: int = 0,
     cu_seqlens: [N+1] int offsets, or None for a single sequence of length T.
     order 0 is the table's KDA row (erase, decay, write); 1 is decay-first.
 
+    pro: keyword arguments of prologue(), applied to the inputs first.
+
     Returns (o [T, H, dv], S_T [N, H, dk, dv]) as float64 arrays.
     """
     q, k, v, log_a, beta = (_f64(x) for x in (q, k, v, log_a, beta))
+    if pro:
+        k, log_a, beta = prologue(k, log_a, beta, **pro)
     T, H, dk = q.shape
     dv = v.shape[2]
     if k.shape != (T, H, dk) or v.shape[:2] != (T, H) or beta.shape != (T, H):

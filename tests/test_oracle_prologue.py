@@ -1,0 +1,76 @@
+"""The oracle's input prologue (unit keys, logistic beta, negative-softplus
+log-decay) against closed forms and identities (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import PROLOGUE_EPS, kda_oracle, prologue
+
+
+def test_logistic_beta_closed_forms():
+    x = np.array([0.0, 1.0, -1.0, 30.0, -30.0, 2.5])
+    _, _, b = prologue(np.ones((6, 1, 2)), np.zeros((6, 1)), x, beta_logits=True)
+    assert b[0] == 0.5
+    assert abs(b[1] - 1.0 / (1.0 + math.e ** -1.0)) < 1e-15
+    assert abs(b[1] + b[2] - 1.0) < 1e-15          # sigma(x) + sigma(-x) = 1
+    assert abs(b[3] - 1.0) < 1e-12 and 0.0 < b[4] < 1e-12
+    assert abs(math.log(b[5] / (1.0 - b[5])) - 2.5) < 1e-12  # the logit inverts it
+
+
+def test_negative_softplus_closed_forms():
+    x = np.array([0.0, 1.0, -1.0, 40.0, -40.0, 3.0])
+    _, la, _ = prologue(np.ones((6, 1, 2)), x.reshape(6, 1), np.zeros((6, 1)), log_a_raw=True)
+    la = la[:, 0]
+    assert abs(la[0] + math.log(2.0)) < 1e-15
+    assert abs((-la[1]) - (-la[2]) - 1.0) < 1e-14   # softplus(x) - softplus(-x) = x
+    assert abs(-la[3] - 40.0) < 1e-14                 # softplus(x) -> x
+    assert 0.0 > la[4] > -1e-16                       # softplus(x) -> e^x
+    assert abs(math.exp(la[5]) - 1.0 / (1.0 + math.e ** 3.0)) < 1e-15  # a = sigma(-x)
+    assert np.all(la <= 0.0)
+    _, lac, _ = prologue(np.ones((6, 1, 2)), x.reshape(6, 1), np.zeros((6, 1)), log_a_raw=True, log_a_min=-8.0)
+    assert lac[3, 0] == -8.0 and lac[0, 0] == la[0]  # the clip touches only the tail
+
+
+def test_key_normalisation():
+    rng = np.random.default_rng(0)
+    k = rng.normal(size=(7, 3, 16)) * rng.uniform(0.5, 4.0, size=(7, 3, 1))
+    kn, _, _ = prologue(k, np.zeros((7, 3)), np.zeros((7, 3)), normalize_k=True)
+    norms = np.linalg.norm(kn, axis=-1)
+    sq = np.sum(k * k, axis=-1)
+    assert np.allclose(norms, np.sqrt(sq / (sq + PROLOGUE_EPS)), rtol=1e-14)  # unit up to eps
+    cos = np.sum(kn * k, axis=-1) / (np.linalg.norm(kn, axis=-1) * np.linalg.norm(k, axis=-1))
+    assert np.allclose(cos, 1.0, atol=1e-14)          # direction kept
+    z, _, _ = prologue(np.zeros((2, 1, 4)), np.zeros((2, 1)), np.zeros((2, 1)), normalize_k=True)
+    assert np.all(z == 0.0)                           # a zero key stays zero (eps keeps it finite)
+
+
+def test_prologue_is_scale_invariant_in_k():
+    """With normalised keys the layer does not see the scale of k (up to eps)."""
+    rng = np.random.default_rng(1)
+    T, H, dk, dv = 9, 2, 8, 4
+    q, k, v = rng.normal(size=(T, H, dk)), rng.normal(size=(T, H, dk)), rng.normal(size=(T, H, dv))
+    la, b = rng.normal(size=(T, H, dk)), rng.normal(size=(T, H))
+    pro = dict(normalize_k=True, beta_logits=True, log_a_raw=True)
+    o1, s1 = kda_oracle(q, k, v, la, b, pro=pro)
+    o2, s2 = kda_oracle(q, 5.0 * k, v, la, b, pro=pro)
+    assert np.max(np.abs(o1 - o2)) < 1e-6 * np.max(np.abs(o1))
+    assert np.max(np.abs(s1 - s2)) < 1e-6 * np.max(np.abs(s1))
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_prologue_feeds_the_recurrence(order):
+    """Oracle with the prologue equals the oracle on inputs transformed in closed
+    form by numpy's own logistic and log-add-exp (a different route to the same
+    values)."""
+    rng = np.random.default_rng(2 + order)
+    T, H, dk, dv = 11, 2, 6, 5
+    q, k, v = rng.normal(size=(T, H, dk)), rng.normal(size=(T, H, dk)) * 3.0, rng.normal(size=(T, H, dv))
+    x, b = rng.normal(size=(T, H, dk)) * 2.0, rng.normal(size=(T, H))
+    o1, s1 = kda_oracle(q, k, v, x, b, order=order,
+                        pro=dict(normalize_k=True, beta_logits=True, log_a_raw=True, log_a_min=-3.0))
+    kn = k / np.sqrt(np.einsum("thc,thc->th", k, k)[..., None] + PROLOGUE_EPS)
+    la = np.maximum(-np.logaddexp(0.0, x), -3.0)
+    bb = np.exp(-np.logaddexp(0.0, -b))
+    o2, s2 = kda_oracle(q, kn, v, la, bb, order=order)
+    assert np.max(np.abs(o1 - o2)) < 1e-12 and np.max(np.abs(s1 - s2)) < 1e-12
