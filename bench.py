@@ -7,9 +7,10 @@ counted once across heads).  The decode leg (256 sequences x 32 heads,
 dk=dv=128, 100 chained steps, fp32 state streamed once per step) is timed in
 the same run and reported under "decode" in state GB/s.  All inputs are seeded
 synthetic tensors, resident on the GPU before timing starts.  The same
-prefill batch is also timed with state snapshots every 1024 tokens and with
-the decay-first ordering, and the decode leg with the decay-first ordering
-("variants", "decode.decay_first").
+prefill batch is also timed with state snapshots every 1024 tokens, with the
+decay-first ordering, and from raw inputs through the input prologue (against
+torch transforming them first), and the decode leg with the decay-first
+ordering ("variants", "decode.decay_first").
 
 Timing uses HIP events recorded on the stream the kernels are launched on
 (torch's current stream, which the library receives).  The fp64 CPU oracle is
@@ -314,17 +315,48 @@ def main():
                                 S0=x["S0"][0:1, 0:1].cpu(), order=1)
             perr1 = float(np.abs(o[:2048, 0].double().cpu().numpy() - ro1[:, 0]).max() / np.abs(ro1).max())
             del ws1
+            # input prologue: raw keys, beta logits and log-decay pre-activations of the same
+            # shapes, transformed in the operator pass, against torch transforming them first
+            from kda_recurrent_state_amd.workloads import generate_raw
+            xr = generate_raw(wp, seed=3, device=dev)
+            pro = dict(normalize_k=True, beta_logits=True, log_a_raw=True, log_a_min=wp.la_clip)
+
+            def pro_step():
+                kda.chunk_fwd(x["q"], xr["k"], x["v"], xr["log_a"], xr["beta"], S0=x["S0"],
+                              cu_seqlens=x["cu_seqlens"], out=o, final_state=ST, method=method, workspace=ws,
+                              max_seqlen=wp.seqlen, prologue=pro)
+
+            def torch_step():
+                kf = xr["k"].float()
+                kn = (kf * torch.rsqrt((kf * kf).sum(-1, keepdim=True) + 1e-6)).to(wp.dtype)
+                la = (-torch.nn.functional.softplus(xr["log_a"])).clamp_(min=wp.la_clip)
+                kda.chunk_fwd(x["q"], kn, x["v"], la, torch.sigmoid(xr["beta"]), S0=x["S0"],
+                              cu_seqlens=x["cu_seqlens"], out=o, final_state=ST, method=method, workspace=ws,
+                              max_seqlen=wp.seqlen)
+            for _ in range(max(args.warmup, 3)):
+                pro_step()
+            torch.cuda.synchronize()
+            tp = time_events(pro_step, vsteps, stream) / vsteps
+            for _ in range(max(args.warmup, 3)):
+                torch_step()
+            torch.cuda.synchronize()
+            tt = time_events(torch_step, vsteps, stream) / vsteps
+            del xr
             out["variants"] = {
                 "snapshots": {"snapshot_every": every, "rows": rows, "ms_per_step": ts * 1e3,
                               "tokens_per_s": tokens / ts, "overhead_vs_plain": ts / per - 1.0,
                               "snapshot_bytes": rows * wp.heads * wp.dk * wp.dv * 4},
+                "prologue": {"ms_per_step": tp * 1e3, "tokens_per_s": tokens / tp,
+                             "overhead_vs_plain": tp / per - 1.0, "torch_prologue_then_plain_ms": tt * 1e3,
+                             "note": "raw k, beta logits, log-decay pre-activations transformed in the operator "
+                                     "pass vs by torch before the plain call"},
                 "decay_first": {"ms_per_step": t1 * 1e3, "tokens_per_s": tokens / t1,
                                 "algorithmic_GBps": B / t1 / 1e9, "frac_hbm": B / t1 / 1e9 / PEAK_HBM_GBS,
                                 "workspace_MiB": round(wsb1 / 2**20, 1),
                                 "parity_o_max_rel_err": perr1, "tol": 2e-2},
             }
             log(f"prefill with snapshots every {every}: {ts*1e3:.3f} ms; decay-first: {t1*1e3:.3f} ms, "
-                f"parity {perr1:.2e}")
+                f"parity {perr1:.2e}; prologue fused {tp*1e3:.3f} ms vs torch first {tt*1e3:.3f} ms")
 
         if not args.no_cpu_baseline:
             ncpu = min(16, os.cpu_count() or 1)

@@ -173,6 +173,32 @@ KDA_API int kda_chunk_fwd_snapshots(const kda_dims_t* dims, const void* q, const
                             size_t workspace_bytes, void* stream);
 
 /*
+ * Optional input prologue, applied as the kernels load their inputs, so that a
+ * layer's raw projections need no separate pass over memory.  The pages fix no
+ * gate parameterisation; these are the transforms of the usual learned gates:
+ */
+typedef struct {
+    int32_t normalize_k;  /* 1: k_t <- k_t / sqrt(sum_c k_tc^2 + 1e-6), per token and head (fp32) */
+    int32_t beta_logits;  /* 1: beta holds logits: beta_t <- 1 / (1 + exp(-beta_t)) */
+    int32_t log_a_raw;    /* 1: log_a holds pre-activations x (any finite value):
+                             log a <- max(-softplus(x), log_a_min), softplus(x) = log(1 + e^x) */
+    float log_a_min;      /* lower clip of log a with log_a_raw: <= 0, or -INFINITY for none */
+} kda_prologue_t;
+
+/*
+ * kda_chunk_fwd_snapshots with an input prologue (NULL, or all fields 0: none).
+ * The prologue runs in the two-pass method's operator pass (bf16, dk = 64 or
+ * 128); a call that would run single-pass (fp32 inputs, other shapes,
+ * KDA_METHOD_SINGLE, or no workspace) returns KDA_ERR_UNSUPPORTED when any
+ * transform is requested.  Everything else is as kda_chunk_fwd_snapshots.
+ */
+KDA_API int kda_chunk_fwd_ex(const kda_dims_t* dims, const kda_prologue_t* prologue, const void* q,
+                     const void* k, const void* v, const float* log_a, const float* beta,
+                     const float* S0, const int32_t* cu_seqlens, void* o, float* S_T,
+                     float* snapshots, int64_t snapshot_rows, int64_t snapshot_every,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Workspace the two-pass prefill prefers for these dims (segments of up to
  * 4 GiB of operator blocks: about 1.2 KB per token and head at dk = 128, so a
  * whole 2 x 32-head x 32K-token batch runs as one segment), or 0 if the call
@@ -197,6 +223,12 @@ KDA_API int kda_chunk_workspace_min(const kda_dims_t* dims, size_t* bytes);
 KDA_API int kda_decode_step(const kda_dims_t* dims, const void* q, const void* k, const void* v,
                     const float* log_a, const float* beta, const float* S_in, float* S_out,
                     void* o, void* stream);
+
+/* kda_decode_step with an input prologue (NULL, or all fields 0: none); every
+ * shape that kda_decode_step supports. */
+KDA_API int kda_decode_step_ex(const kda_dims_t* dims, const kda_prologue_t* prologue, const void* q,
+                       const void* k, const void* v, const float* log_a, const float* beta,
+                       const float* S_in, float* S_out, void* o, void* stream);
 
 /* Static text for a status code. */
 KDA_API const char* kda_status_string(int status);

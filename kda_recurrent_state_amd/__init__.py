@@ -49,6 +49,24 @@ class _Dims(ctypes.Structure):
                 ("method", ctypes.c_int32), ("order", ctypes.c_int32), ("max_seqlen", ctypes.c_int64)]
 
 
+class _Prologue(ctypes.Structure):
+    _fields_ = [("normalize_k", ctypes.c_int32), ("beta_logits", ctypes.c_int32), ("log_a_raw", ctypes.c_int32),
+                ("log_a_min", ctypes.c_float)]
+
+
+def _prologue(pro):
+    """kda_prologue_t from a dict with keys normalize_k, beta_logits, log_a_raw,
+    log_a_min (None: no prologue)."""
+    if pro is None:
+        return None
+    unknown = set(pro) - {"normalize_k", "beta_logits", "log_a_raw", "log_a_min"}
+    if unknown:
+        raise ValueError(f"unknown prologue fields {sorted(unknown)}")
+    lo = pro.get("log_a_min")
+    return _Prologue(int(bool(pro.get("normalize_k"))), int(bool(pro.get("beta_logits"))),
+                     int(bool(pro.get("log_a_raw"))), float("-inf") if lo is None else float(lo))
+
+
 METHOD_AUTO, METHOD_SINGLE, METHOD_TWO_PASS = 0, 1, 2
 # where the decay sits in the update (kda_order_t): the table's KDA row erases
 # first, S <- Diag(a)(I - b k^T k) S + b k^T v; DECAY_FIRST is
@@ -75,6 +93,12 @@ def load_library(build_if_missing: bool = True):
             lib.kda_chunk_fwd.restype = ctypes.c_int
             lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P,
                                           ctypes.c_size_t, P]
+            lib.kda_chunk_fwd_ex.restype = ctypes.c_int
+            lib.kda_chunk_fwd_ex.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Prologue), P, P, P, P, P, P, P,
+                                             P, P, P, ctypes.c_int64, ctypes.c_int64, P, ctypes.c_size_t, P]
+            lib.kda_decode_step_ex.restype = ctypes.c_int
+            lib.kda_decode_step_ex.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Prologue), P, P, P, P, P, P,
+                                               P, P, P]
             lib.kda_chunk_fwd_snapshots.restype = ctypes.c_int
             lib.kda_chunk_fwd_snapshots.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P,
                                                     ctypes.c_int64, ctypes.c_int64, P, ctypes.c_size_t, P]
@@ -131,7 +155,7 @@ def _stream_handle(device):
 def chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, chunk_size: int = 0,
               dv_split: int = 0, out=None, final_state=True, num_seqs: int | None = None,
               method: int = METHOD_AUTO, workspace=None, max_seqlen: int | None = None,
-              order: int = ORDER_ERASE_FIRST):
+              order: int = ORDER_ERASE_FIRST, prologue: dict | None = None):
     """Chunked prefill over packed sequences; returns (o, S_T or None).
 
     cu_seqlens: int32 device tensor [N+1], or None for num_seqs (default 1)
@@ -143,9 +167,12 @@ def chunk_fwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, chunk_size: int
     to have one of the library's preferred size allocated (torch's caching
     allocator) for this call.  max_seqlen bounds the longest sequence (with
     cu_seqlens); when None it is read from cu_seqlens, which synchronises.
-    order: ORDER_ERASE_FIRST or ORDER_DECAY_FIRST."""
+    order: ORDER_ERASE_FIRST or ORDER_DECAY_FIRST.
+    prologue: None, or a dict of kda_prologue_t fields (normalize_k, beta_logits,
+    log_a_raw, log_a_min) transforming raw k, beta logits and log-decay
+    pre-activations on load (two-pass prefill only)."""
     o, ST, _ = _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state,
-                        num_seqs, method, workspace, max_seqlen, 0, None, order)
+                        num_seqs, method, workspace, max_seqlen, 0, None, order, prologue)
     return o, ST
 
 
@@ -168,7 +195,8 @@ def snapshot_rows(cu_seqlens, snapshot_every: int, *, total_tokens: int | None =
 def chunk_fwd_snapshots(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, snapshot_every: int,
                         snapshots=None, chunk_size: int = 0, dv_split: int = 0, out=None, final_state=True,
                         num_seqs: int | None = None, method: int = METHOD_AUTO, workspace=None,
-                        max_seqlen: int | None = None, order: int = ORDER_ERASE_FIRST):
+                        max_seqlen: int | None = None, order: int = ORDER_ERASE_FIRST,
+                        prologue: dict | None = None):
     """chunk_fwd that also returns the state after every `snapshot_every` tokens
     of each sequence: (o, S_T or None, snapshots [R, H, dk, dv] float32).
 
@@ -190,11 +218,11 @@ def chunk_fwd_snapshots(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, snaps
         if snapshots.shape[1:] != (H, dk, dv):
             raise ValueError(f"snapshots must be [R,{H},{dk},{dv}] (got {tuple(snapshots.shape)})")
     return _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state, num_seqs,
-                    method, workspace, max_seqlen, int(snapshot_every), snapshots, order)
+                    method, workspace, max_seqlen, int(snapshot_every), snapshots, order, prologue)
 
 
 def _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state, num_seqs,
-             method, workspace, max_seqlen, snapshot_every, snapshots, order):
+             method, workspace, max_seqlen, snapshot_every, snapshots, order, prologue):
     lib = load_library()
     _need(q, "q", ndim=3)
     T, H, dk = q.shape
@@ -246,7 +274,15 @@ def _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, fi
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, 1)
     ws_bytes = ctypes.c_size_t(0 if workspace is None else workspace.numel())
-    if snapshots is None:
+    pro = _prologue(prologue)
+    if pro is not None:
+        rows = 0 if snapshots is None else snapshots.shape[0]
+        st = lib.kda_chunk_fwd_ex(ctypes.byref(d), ctypes.byref(pro), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a),
+                                  _ptr(beta), _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(ST),
+                                  _ptr(snapshots) if rows > 0 else None, ctypes.c_int64(rows),
+                                  ctypes.c_int64(snapshot_every if rows > 0 else 0), _ptr(workspace), ws_bytes,
+                                  _stream_handle(q.device))
+    elif snapshots is None:
         st = lib.kda_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
                                _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(ST), _ptr(workspace), ws_bytes,
                                _stream_handle(q.device))
@@ -275,7 +311,8 @@ def chunk_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, 
     return need.value
 
 
-def decode_step(q, k, v, log_a, beta, S, *, out=None, S_out=None, order: int = ORDER_ERASE_FIRST):
+def decode_step(q, k, v, log_a, beta, S, *, out=None, S_out=None, order: int = ORDER_ERASE_FIRST,
+                prologue: dict | None = None):
     """One token per sequence: q, k [N,H,dk], v [N,H,dv], log_a [N,H,dk] or
     [N,H], beta [N,H], S [N,H,dk,dv].  Updates S in place unless S_out is
     given; returns (o, state_after)."""
@@ -301,7 +338,12 @@ def decode_step(q, k, v, log_a, beta, S, *, out=None, S_out=None, order: int = O
     o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     _need(o, "out", q.dtype)
     d = _Dims(N, H, N, dk, dv, _dtype_code(q), scalar, 0, 0, 0, int(order), 0)
-    st = lib.kda_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
-                             _ptr(S), _ptr(So), _ptr(o), _stream_handle(q.device))
+    pro = _prologue(prologue)
+    if pro is not None:
+        st = lib.kda_decode_step_ex(ctypes.byref(d), ctypes.byref(pro), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a),
+                                    _ptr(beta), _ptr(S), _ptr(So), _ptr(o), _stream_handle(q.device))
+    else:
+        st = lib.kda_decode_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
+                                 _ptr(S), _ptr(So), _ptr(o), _stream_handle(q.device))
     _check(lib, st)
     return o, So

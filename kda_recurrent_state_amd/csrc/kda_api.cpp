@@ -5,6 +5,7 @@
 // than the thread-local text of the last error.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -75,6 +76,24 @@ int choose_split(const kda_dims_t* d, int chunk) {
         if (units * split >= 256) break;
     }
     return best;
+}
+
+// Validates a prologue (NULL: none) and copies it for the launchers.
+int check_prologue(const kda_prologue_t* pr, kda::Prologue* out) {
+    *out = kda::Prologue();
+    if (!pr) return KDA_OK;
+    auto flag = [](int32_t f) { return f == 0 || f == 1; };
+    if (!flag(pr->normalize_k) || !flag(pr->beta_logits) || !flag(pr->log_a_raw))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "prologue flags must be 0 or 1 (got %d, %d, %d)", pr->normalize_k,
+                    pr->beta_logits, pr->log_a_raw);
+    if (pr->log_a_raw && (isnan(pr->log_a_min) || pr->log_a_min > 0.f))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "prologue log_a_min = %g must be <= 0 (or -INFINITY)",
+                    (double)pr->log_a_min);
+    out->normalize_k = pr->normalize_k;
+    out->beta_logits = pr->beta_logits;
+    out->log_a_raw = pr->log_a_raw;
+    out->log_a_min = pr->log_a_raw ? pr->log_a_min : 0.f;
+    return KDA_OK;
 }
 
 // Order the kernels run: with one decay value per token and head the two
@@ -203,9 +222,19 @@ int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, c
                             const int32_t* cu_seqlens, void* o, float* S_T, float* snapshots,
                             int64_t snapshot_rows, int64_t snapshot_every, void* workspace,
                             size_t workspace_bytes, void* stream) {
+    return kda_chunk_fwd_ex(d, nullptr, q, k, v, log_a, beta, S0, cu_seqlens, o, S_T, snapshots, snapshot_rows,
+                            snapshot_every, workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_fwd_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const void* q, const void* k,
+                     const void* v, const float* log_a, const float* beta, const float* S0,
+                     const int32_t* cu_seqlens, void* o, float* S_T, float* snapshots, int64_t snapshot_rows,
+                     int64_t snapshot_every, void* workspace, size_t workspace_bytes, void* stream) {
     Plan pl;
     int st = plan_prefill(d, cu_seqlens != nullptr, &pl);
     if (st) return st;
+    kda::Prologue pro;
+    if ((st = check_prologue(prologue, &pro))) return st;
     const int chunk = pl.chunk;
     if (snapshot_every < 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "snapshot_every = %lld < 0", (long long)snapshot_every);
@@ -257,6 +286,9 @@ int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, c
                         pl.min_bytes, workspace ? workspace_bytes : (size_t)0);
         two_pass = have_ws;
     }
+    if (pro.any() && !two_pass)
+        return fail(KDA_ERR_UNSUPPORTED, "an input prologue needs the two-pass prefill (bf16, dk 64 or 128, method "
+                                         "AUTO or TWO_PASS, a workspace)");
     if (two_pass) {
         if ((uintptr_t)workspace & 255u) return fail(KDA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
         const size_t per_chunk = (size_t)pl.units * pl.block;
@@ -278,7 +310,7 @@ int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, c
                 pa.q = q; pa.k = k; pa.log_a = log_a; pa.beta = beta; pa.cu_seqlens = cu_seqlens;
                 pa.eq_len = eq_len; pa.ws = blocks; pa.num_heads = d->num_heads; pa.units = pl.units;
                 pa.m = (int32_t)m; pa.chunk0 = chunk0; pa.dk = d->dk; pa.chunk = chunk; pa.scalar = d->scalar_decay;
-                pa.order = kernel_order(d);
+                pa.order = kernel_order(d); pa.pro = pro;
                 e = kda::launch_prep(pa, (hipStream_t)stream);
                 if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill operator pass launch: %s", hipGetErrorString(e));
             }
@@ -323,8 +355,16 @@ int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, c
 int kda_decode_step(const kda_dims_t* d, const void* q, const void* k, const void* v,
                     const float* log_a, const float* beta, const float* S_in, float* S_out,
                     void* o, void* stream) {
+    return kda_decode_step_ex(d, nullptr, q, k, v, log_a, beta, S_in, S_out, o, stream);
+}
+
+int kda_decode_step_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const void* q, const void* k,
+                       const void* v, const float* log_a, const float* beta, const float* S_in, float* S_out,
+                       void* o, void* stream) {
     int st = check_dims(d);
     if (st) return st;
+    kda::Prologue pro;
+    if ((st = check_prologue(prologue, &pro))) return st;
     if (d->total_tokens != d->num_seqs)
         return fail(KDA_ERR_INVALID_ARGUMENT, "decode needs total_tokens (%lld) == num_seqs (%d)",
                     (long long)d->total_tokens, d->num_seqs);
@@ -337,8 +377,8 @@ int kda_decode_step(const kda_dims_t* d, const void* q, const void* k, const voi
         return fail(KDA_ERR_UNSUPPORTED, "no decode kernel for dtype %d, dk %d, dv %d", d->qkv_dtype, d->dk, d->dv);
     const int64_t heads = (int64_t)d->num_seqs * d->num_heads;
     if (heads > 0x7fffffff) return fail(KDA_ERR_INVALID_ARGUMENT, "too many states: %lld", (long long)heads);
-    hipError_t e = kda::launch_decode(d->qkv_dtype, d->dk, d->dv, d->scalar_decay, kernel_order(d), heads, q, k, v, log_a,
-                                      beta, S_in, S_out, o, (hipStream_t)stream);
+    hipError_t e = kda::launch_decode(d->qkv_dtype, d->dk, d->dv, d->scalar_decay, kernel_order(d), pro, heads, q, k,
+                                      v, log_a, beta, S_in, S_out, o, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return ok();
 }

@@ -84,6 +84,28 @@ __device__ __forceinline__ i32x4 quad_transpose(i32x4 m, int lane) {
     return n2;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) { return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, x))); }
+__device__ __forceinline__ float readlanef(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+// Sum of x over each row of 16 lanes, left in every lane of the row (quad
+// swaps, then rotations of the row by 4 and by 8).
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dppf<0xB1>(x);
+    x += dppf<0x4E>(x);
+    x += dppf<0x124>(x);
+    x += dppf<0x128>(x);
+    return x;
+}
+
+// Input prologue (kda_prologue_t): log a = max(-softplus(x), lo) with
+// softplus(x) = max(x, 0) + log(1 + e^{-|x|}); beta = 1 / (1 + e^{-x}).
+__device__ __forceinline__ float prologue_log_a(float x, float lo) {
+    return fmaxf(-(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)))), lo);
+}
+__device__ __forceinline__ float prologue_beta(float x) { return 1.f / (1.f + __expf(-x)); }
+
 // Stores one 16 x 16 fp32 accumulator tile (lane: column lane % 16, rows
 // 4 (lane / 16) .. + 3) into a row-major state with row stride DV; dst points at
 // the tile's element (0, 0).  After a transpose inside lane quads each lane

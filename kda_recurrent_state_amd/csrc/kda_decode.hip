@@ -16,6 +16,12 @@
 //     S'[c][j] = a_c S[c][j] - beta k_c y_j + beta k_c v_j
 //     o_j      = z_j - beta (q . k) y_j + beta (q . k) v_j
 //
+// With an input prologue (kda_prologue_t) the raw token inputs are transformed
+// on load: beta = 1 / (1 + e^{-x}), log a = max(-softplus(x), min) so that
+// a = max(1 / (1 + e^{x}), e^{min}), and k is scaled by r = (|k|^2 + eps)^{-1/2},
+// which enters y, the two dot products and the update linearly (y and the dots
+// are scaled after their reductions).
+//
 // One workgroup per state.  Thread (row group rg, column group cg) owns four
 // consecutive columns 4cg..4cg+3 of rows rg, rg + RG, ...; a wavefront covers
 // whole consecutive rows, so every 16-byte load and store is coalesced.
@@ -38,10 +44,10 @@ template <typename T, int DK, int DV, bool SCALAR, bool ORD1>
 __global__ void __launch_bounds__(256)
 kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const float* __restrict__ log_a, const float* __restrict__ beta,
-                  const float* S_in, float* S_out, T* __restrict__ o) {
+                  const float* S_in, float* S_out, T* __restrict__ o, Prologue pro) {
     typedef DecodeShape<T, DK, DV, SCALAR> Sh;
     constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NW = Sh::NW;
-    __shared__ float s_k[DK], s_q[DK], s_qa[DK], s_a[DK], s_v[DV], s_dot[2];
+    __shared__ float s_k[DK], s_q[DK], s_qa[DK], s_a[DK], s_v[DV], s_dot[3];
     __shared__ f32x4 s_red[2][NW][CG];
 
     const int tid = threadIdx.x;
@@ -58,9 +64,11 @@ kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + (rg + RG * i) * DV + 4 * cg));
 
     // 2. per-token vectors
-    const float b = beta[head];
+    float b = beta[head];
+    if (pro.beta_logits) b = 1.f / (1.f + __expf(-b));
     for (int c = tid; c < DK; c += Sh::NT) {
-        const float la = SCALAR ? log_a[head] : log_a[head * DK + c];
+        float la = SCALAR ? log_a[head] : log_a[head * DK + c];
+        if (pro.log_a_raw) la = fmaxf(-(fmaxf(la, 0.f) + log1pf(__expf(-fabsf(la)))), pro.log_a_min);
         const float a = __expf(la);
         const float qc = to_f32(q[head * DK + c]);
         s_k[c] = to_f32(k[head * DK + c]);
@@ -71,19 +79,22 @@ kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     for (int j = tid; j < DV; j += Sh::NT) s_v[j] = to_f32(v[head * DV + j]);
     __syncthreads();
 
-    // q.a.k and q.k for the output (wave 0)
+    // q.a.k and q.k for the output, and the key's scale (wave 0)
     if (wv == 0) {
-        float d1 = 0.f, d2 = 0.f;
+        float d1 = 0.f, d2 = 0.f, kk = 0.f;
         for (int c = lane; c < DK; c += WAVE) {
             d1 += s_qa[c] * s_k[c];
             d2 += s_q[c] * s_k[c];
+            kk += s_k[c] * s_k[c];
         }
 #pragma unroll
         for (int off = WAVE / 2; off > 0; off >>= 1) {
             d1 += __shfl_xor(d1, off);
             d2 += __shfl_xor(d2, off);
+            kk += __shfl_xor(kk, off);
         }
-        if (lane == 0) { s_dot[0] = d1; s_dot[1] = d2; }
+        const float r = pro.normalize_k ? rsqrtf(kk + PROLOGUE_EPS) : 1.f;
+        if (lane == 0) { s_dot[0] = d1 * r; s_dot[1] = d2 * r; s_dot[2] = r; }
     }
 
     // 3. partial y = k S and z = (q*a) S over this thread's rows
@@ -116,6 +127,8 @@ kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         y += s_red[0][w][cg];
         z += s_red[1][w][cg];
     }
+    const float kr_scale = s_dot[2];  // 1 without the prologue's key normalisation
+    y *= kr_scale;
 
     // 4. update in registers and write the state once
     f32x4 vv;
@@ -124,7 +137,7 @@ kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg + RG * i;
-        const float kr = s_k[r], ar = s_a[r];
+        const float kr = s_k[r] * kr_scale, ar = s_a[r];
         const float bk = b * kr;
         f32x4 ns = ORD1 ? ar * s[i] - bk * y + kr * bv : ar * (s[i] - bk * y) + kr * bv;
         __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(So + r * DV + 4 * cg));
@@ -142,7 +155,7 @@ kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
         typedef DecodeShape<T, DK_, DV_, SC> Sh;                                                 \
         hipLaunchKernelGGL((kda_decode_kernel<T, DK_, DV_, SC, O1>), dim3(heads), dim3(Sh::NT), 0,\
                            stream, (const T*)q, (const T*)k, (const T*)v, log_a, beta, S_in,     \
-                           S_out, (T*)o);                                                        \
+                           S_out, (T*)o, pro);                                                   \
         return hipGetLastError();                                                                \
     }
 
@@ -160,7 +173,8 @@ bool decode_supported(int dtype, int dk, int dv) {
 }
 
 // order 1 comes with per-channel decay only (the host maps scalar decay to order 0)
-hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int order, int64_t heads, const void* q,
+hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int order, const Prologue& pro, int64_t heads,
+                         const void* q,
                          const void* k, const void* v, const float* log_a, const float* beta,
                          const float* S_in, float* S_out, void* o, hipStream_t stream) {
     if (dtype == 1) {

@@ -6,6 +6,14 @@
 
 namespace kda {
 
+// Input prologue switches (kda_prologue_t), passed to the kernels that run it.
+struct Prologue {
+    int32_t normalize_k = 0, beta_logits = 0, log_a_raw = 0;
+    float log_a_min = 0.f;
+    bool any() const { return normalize_k || beta_logits || log_a_raw; }
+};
+constexpr float PROLOGUE_EPS = 1e-6f;
+
 struct ChunkArgs {
     const void* q;
     const void* k;
@@ -31,7 +39,8 @@ struct ChunkArgs {
 };
 
 bool decode_supported(int dtype, int dk, int dv);
-hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int order, int64_t heads, const void* q,
+hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int order, const Prologue& pro, int64_t heads,
+                         const void* q,
                          const void* k, const void* v, const float* log_a, const float* beta,
                          const float* S_in, float* S_out, void* o, hipStream_t stream);
 
@@ -55,6 +64,7 @@ struct PrepLaunch {
     int64_t chunk0;             // first chunk of the segment
     int32_t dk, chunk, scalar;
     int32_t order;              // as in ChunkArgs
+    Prologue pro;
 };
 struct ScanLaunch {
     const void* v;

@@ -94,6 +94,7 @@ struct PrepParams {
     int m;            // chunks per unit in this segment (block stride)
     int items;        // units * m
     int64_t chunk0;   // first chunk index of the segment
+    Prologue pro;     // input prologue (instantiations with PRO only)
 };
 
 // Raw inputs of one chunk for one thread: its 4-token x 2-channel unit, and
@@ -185,7 +186,10 @@ __device__ __forceinline__ void split_solve(PrepLds<DK, C>& s, int wv, int lane,
     }
 }
 
-template <int DK, int C, bool SCALAR, bool ORD1>
+// PRO: the call has an input prologue (k scaled per token by (|k|^2 + eps)^{-1/2},
+// each token's channels being one half-wavefront; beta and log a transformed
+// where they are loaded).
+template <int DK, int C, bool SCALAR, bool ORD1, bool PRO>
 __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
     typedef PrepCfg<DK, C> G;
     typedef WsBlock<DK, C, ORD1> WS;
@@ -225,16 +229,31 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
 
         // ---- 1: decay sums per 4-token group in the log2 domain ------------------
         f32x2 lam[4];
+        float kscale[4] = {1.f, 1.f, 1.f, 1.f};
         if (tid < G::NU) {
             f32x2 run = f32x2{0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                run += (4 * tg + i < Lc) ? in.la[i] * LOG2E : f32x2{0.f, 0.f};
+                f32x2 lx = in.la[i];
+                if (PRO && p.pro.log_a_raw)
+                    lx = f32x2{prologue_log_a(lx[0], p.pro.log_a_min), prologue_log_a(lx[1], p.pro.log_a_min)};
+                run += (4 * tg + i < Lc) ? lx * LOG2E : f32x2{0.f, 0.f};
                 lam[i] = run;
             }
             *reinterpret_cast<f32x2*>(&s.u2.grp[tg * DK + c]) = run;
+            if (PRO && p.pro.normalize_k) {
+                static_assert(G::NCP == 32, "a token's channels are one half-wavefront");
+                const bool hi = (tid & 63) >= 32;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float k0 = Vec2<bf16>::lo(in.k[i]), k1 = Vec2<bf16>::hi(in.k[i]);
+                    const float x = row_sum16(k0 * k0 + k1 * k1);
+                    const float lo2 = readlanef(x, 0) + readlanef(x, 16), hi2 = readlanef(x, 32) + readlanef(x, 48);
+                    kscale[i] = rsqrtf((hi ? hi2 : lo2) + PROLOGUE_EPS);
+                }
+            }
         }
-        if (tid < C) s.beta[tid] = in.b;
+        if (tid < C) s.beta[tid] = (PRO && p.pro.beta_logits && tid < Lc) ? prologue_beta(in.b) : in.b;
         lds_barrier();
 
         // ---- 2: factors (exponents clamped to the fp32 range) and gated operands ---
@@ -269,7 +288,7 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
                         __builtin_amdgcn_fmed3f(off[e] + lam[i][e] - mid[e], -126.f, 126.f));
                     ci[e] = __builtin_amdgcn_rcpf(ri[e]);
                 }
-                const f32x2 k = f32x2{Vec2<bf16>::lo(in.k[i]), Vec2<bf16>::hi(in.k[i])};
+                const f32x2 k = f32x2{Vec2<bf16>::lo(in.k[i]), Vec2<bf16>::hi(in.k[i])} * kscale[i];
                 const f32x2 q = f32x2{Vec2<bf16>::lo(in.q[i]), Vec2<bf16>::hi(in.q[i])};
                 const f32x2 kr = ORD1 ? k * ri : k * prev, qr = q * ri, kce = k * prevc, kci = k * ci;
                 store2(&s.u.g.Kr[t * LDK + c], kr[0], kr[1]);
@@ -435,13 +454,14 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
 }
 
 // ------------------------------------------------------------------------------------
-template <int DK, int C, bool SC, bool ORD1>
+template <int DK, int C, bool SC, bool ORD1, bool PRO>
 static hipError_t prep_cfg(const PrepLaunch& a, hipStream_t stream) {
     PrepParams p;
     p.q = a.q; p.k = a.k; p.log_a = a.log_a; p.beta = a.beta; p.cu = a.cu_seqlens;
     p.eq_len = a.eq_len; p.ws = static_cast<uint8_t*>(a.ws); p.H = a.num_heads; p.m = a.m;
     p.chunk0 = a.chunk0;
     p.items = (int)(a.units * a.m);
+    p.pro = a.pro;
     // persistent workgroups: as many as fit at once (two per compute unit when the
     // LDS image allows), each walking items blockIdx.x, + gridDim.x, ...
     int dev = 0, cus = 256;
@@ -450,7 +470,7 @@ static hipError_t prep_cfg(const PrepLaunch& a, hipStream_t stream) {
     int64_t blocks = (int64_t)cus * per_cu;
     if (blocks > p.items) blocks = p.items;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((kda_prep_kernel<DK, C, SC, ORD1>), dim3((unsigned)blocks), dim3(PrepCfg<DK, C>::NT), 0,
+    hipLaunchKernelGGL((kda_prep_kernel<DK, C, SC, ORD1, PRO>), dim3((unsigned)blocks), dim3(PrepCfg<DK, C>::NT), 0,
                        stream, p);
     return hipGetLastError();
 }
@@ -466,8 +486,12 @@ int prep_block_bytes(int dk, int chunk, int order) {
 // order 1 comes with per-channel decay only (the host maps scalar decay to order 0)
 template <int DK, int C>
 static hipError_t prep_dispatch(const PrepLaunch& a, hipStream_t stream) {
-    if (a.scalar) return prep_cfg<DK, C, true, false>(a, stream);
-    return a.order ? prep_cfg<DK, C, false, true>(a, stream) : prep_cfg<DK, C, false, false>(a, stream);
+    if (a.pro.any()) {
+        if (a.scalar) return prep_cfg<DK, C, true, false, true>(a, stream);
+        return a.order ? prep_cfg<DK, C, false, true, true>(a, stream) : prep_cfg<DK, C, false, false, true>(a, stream);
+    }
+    if (a.scalar) return prep_cfg<DK, C, true, false, false>(a, stream);
+    return a.order ? prep_cfg<DK, C, false, true, false>(a, stream) : prep_cfg<DK, C, false, false, false>(a, stream);
 }
 
 hipError_t launch_prep(const PrepLaunch& a, hipStream_t stream) {

@@ -86,6 +86,7 @@ struct Prep2Params {
     int m;            // chunks per unit in this segment (block stride)
     int items;        // units * m
     int64_t chunk0;   // first chunk index of the segment
+    Prologue pro;     // input prologue (instantiations with PRO only)
 };
 
 // Raw inputs of one thread as loaded: 16 bytes per lane and row, so each vector
@@ -178,7 +179,10 @@ __device__ __forceinline__ void prep2_load(const Prep2Params& p, int64_t t0, int
     in.b = (tid < Lc) ? p.beta[r0 + (int64_t)tid * p.H] : 0.f;
 }
 
-template <bool SCALAR, bool ORD1>
+// PRO: the call has an input prologue; k is scaled per token by
+// (|k|^2 + eps)^{-1/2} (each token's row is one wavefront: 64 lanes x 2 channels),
+// beta and log a are transformed where they are loaded.
+template <bool SCALAR, bool ORD1, bool PRO>
 __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
     using namespace p2;
     typedef WsBlock<DK, C, ORD1> WS;
@@ -230,11 +234,30 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
         // ---- A1: factors relative to the block mid-point, Gram operands ---------------
         Prep2In in;
         prep2_unpack<SCALAR>(raw, lane, in);
+        float kscale[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kscale[j] = 1.f;
+        if (PRO && p.pro.normalize_k) {
+            float ss[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const Vec2<bf16>::type kv = __builtin_bit_cast(Vec2<bf16>::type, in.k[j]);
+                const float k0 = Vec2<bf16>::lo(kv), k1 = Vec2<bf16>::hi(kv);
+                ss[j] = row_sum16(k0 * k0 + k1 * k1);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                kscale[j] = rsqrtf(readlanef(ss[j], 0) + readlanef(ss[j], 16) + readlanef(ss[j], 32) +
+                                   readlanef(ss[j], 48) + PROLOGUE_EPS);
+        }
         f32x2 a[8], ai[8], E[8], Ei[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const bool valid = 8 * o + j < Lc;
-            f32x2 la2 = valid ? in.la[j] * LOG2E : f32x2{0.f, 0.f};
+            f32x2 lx = in.la[j];
+            if (PRO && p.pro.log_a_raw)
+                lx = f32x2{prologue_log_a(lx[0], p.pro.log_a_min), prologue_log_a(lx[1], p.pro.log_a_min)};
+            f32x2 la2 = valid ? lx * LOG2E : f32x2{0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const float x = fmaxf(la2[e], LA_MIN);
@@ -263,7 +286,7 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
             P = E[7];
         }
         *reinterpret_cast<f32x2*>(&s.Pq[o * DK + 2 * c2]) = P;
-        if (tid < C) s.beta[tid] = raw.b;
+        if (tid < C) s.beta[tid] = (PRO && p.pro.beta_logits && tid < Lc) ? prologue_beta(raw.b) : raw.b;
 
         f32x2 kr[8], qr[8], kce[8], kci[8];
 #pragma unroll
@@ -271,7 +294,7 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
             const int t = 8 * o + j;
             const Vec2<bf16>::type kv = __builtin_bit_cast(Vec2<bf16>::type, in.k[j]);
             const Vec2<bf16>::type qv = __builtin_bit_cast(Vec2<bf16>::type, in.q[j]);
-            const f32x2 k = f32x2{Vec2<bf16>::lo(kv), Vec2<bf16>::hi(kv)};
+            const f32x2 k = f32x2{Vec2<bf16>::lo(kv), Vec2<bf16>::hi(kv)} * kscale[j];
             const f32x2 q = f32x2{Vec2<bf16>::lo(qv), Vec2<bf16>::hi(qv)};
             kr[j] = ORD1 ? k * E[j] : k * (E[j] * ai[j]);  // k e^{g_{t-1} - mu} (ORD1: g_t)
             qr[j] = q * E[j];             // q e^{g_t - mu}
@@ -507,6 +530,7 @@ hipError_t launch_prep2(const PrepLaunch& a, hipStream_t stream) {
     p.eq_len = a.eq_len; p.ws = static_cast<uint8_t*>(a.ws); p.H = a.num_heads; p.m = a.m;
     p.chunk0 = a.chunk0;
     p.items = (int)(a.units * a.m);
+    p.pro = a.pro;
     // persistent workgroups, two per compute unit, walking items blockIdx.x, + gridDim.x, ...
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -514,12 +538,16 @@ hipError_t launch_prep2(const PrepLaunch& a, hipStream_t stream) {
     if (blocks > p.items) blocks = p.items;
     if (blocks < 1) blocks = 1;
     // order 1 comes with per-channel decay only (the host maps scalar decay to order 0)
-    if (a.scalar)
-        hipLaunchKernelGGL((kda_prep2_kernel<true, false>), dim3((unsigned)blocks), dim3(p2::NT), 0, stream, p);
-    else if (a.order)
-        hipLaunchKernelGGL((kda_prep2_kernel<false, true>), dim3((unsigned)blocks), dim3(p2::NT), 0, stream, p);
-    else
-        hipLaunchKernelGGL((kda_prep2_kernel<false, false>), dim3((unsigned)blocks), dim3(p2::NT), 0, stream, p);
+    const dim3 grid((unsigned)blocks), block(p2::NT);
+    if (a.pro.any()) {
+        if (a.scalar) hipLaunchKernelGGL((kda_prep2_kernel<true, false, true>), grid, block, 0, stream, p);
+        else if (a.order) hipLaunchKernelGGL((kda_prep2_kernel<false, true, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((kda_prep2_kernel<false, false, true>), grid, block, 0, stream, p);
+    } else {
+        if (a.scalar) hipLaunchKernelGGL((kda_prep2_kernel<true, false, false>), grid, block, 0, stream, p);
+        else if (a.order) hipLaunchKernelGGL((kda_prep2_kernel<false, true, false>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((kda_prep2_kernel<false, false, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

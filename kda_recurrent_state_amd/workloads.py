@@ -78,6 +78,21 @@ def _lengths(w: Workload, seed: int) -> np.ndarray:
     return np.full(w.n_seqs, w.seqlen, dtype=np.int64)
 
 
+def generate_raw(w: Workload, seed: int, device="cpu", lengths=None, k_scale: float = 3.0):
+    """The same batch before the input prologue: k unnormalised (scaled by
+    k_scale), log_a as the pre-activation x of log a = -softplus(x) and beta as
+    logits, for calls with an input prologue.  Other tensors as generate()."""
+    out = generate(w, seed, device, lengths)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed + 7919)
+    f32 = torch.float32
+    k = torch.randn(out["k"].shape, generator=g, device=device, dtype=f32) * k_scale
+    la = torch.randn(out["log_a"].shape, generator=g, device=device, dtype=f32) * w.la_std
+    beta = torch.randn(out["beta"].shape, generator=g, device=device, dtype=f32)
+    out.update(k=k.to(w.dtype), log_a=la.contiguous(), beta=beta.contiguous())
+    return out
+
+
 def generate(w: Workload, seed: int, device="cpu", lengths=None):
     """Draw one batch.  Prefill returns q/k/v [T,H,d], log_a [T,H,dk] or [T,H],
     beta [T,H], S0 [N,H,dk,dv] or None, cu_seqlens int32 [N+1] (all on device).

@@ -200,3 +200,45 @@ def test_decay_first_blocks_hold_no_write_operator(lib):
     assert least(order=0) - least(order=1) == units * 8192
     assert least(order=0, dk=64, dv=64) - least(order=1, dk=64, dv=64) == units * 4096
     assert least(order=1, scalar_decay=1) == least(order=0, scalar_decay=1)
+
+
+def prefill_ex(lib, d, pro, ws=None, ws_bytes=0):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    pp = None if pro is None else ctypes.byref(pro)
+    return lib.kda_chunk_fwd_ex(ctypes.byref(d), pp, P(GOOD), P(GOOD), P(GOOD), P(GOOD), P(GOOD), None, P(GOOD),
+                                P(GOOD), P(GOOD), None, ctypes.c_int64(0), ctypes.c_int64(0), P(ws),
+                                ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("fields,d,expect", [
+    ((2, 0, 0, 0.0), dims(), INVALID),                     # flags are 0 or 1
+    ((0, 0, 1, 0.5), dims(), INVALID),                     # log_a_min above 0
+    ((0, 0, 1, float("nan")), dims(), INVALID),
+    ((1, 1, 1, -8.0), dims(qkv_dtype=0, dk=64, dv=64), UNSUPPORTED),  # fp32 runs single-pass
+    ((1, 0, 0, 0.0), dims(method=1), UNSUPPORTED),          # single-pass asked for
+    ((0, 1, 0, 0.0), dims(), UNSUPPORTED),                  # no workspace: single-pass
+    ((0, 0, 0, 0.0), dims(num_seqs=0, total_tokens=0), OK),
+    ((1, 1, 1, float("-inf")), dims(num_seqs=0, total_tokens=0), OK),
+])
+def test_prologue_validation(lib, fields, d, expect):
+    pro = kda._Prologue(*fields)
+    st = prefill_ex(lib, d, pro)
+    assert st == expect, (st, lib.kda_last_error())
+    if expect == UNSUPPORTED:
+        assert "prologue" in lib.kda_last_error().decode()
+
+
+def test_decode_prologue_validation(lib):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    bad = kda._Prologue(0, 3, 0, 0.0)
+    st = lib.kda_decode_step_ex(ctypes.byref(dims(total_tokens=2)), ctypes.byref(bad), P(GOOD), P(GOOD), P(GOOD),
+                                P(GOOD), P(GOOD), P(GOOD), P(GOOD), P(GOOD), None)
+    assert st == INVALID
+
+
+def test_binding_prologue_fields():
+    assert kda._prologue(None) is None
+    p = kda._prologue(dict(normalize_k=True, log_a_raw=1))
+    assert (p.normalize_k, p.beta_logits, p.log_a_raw, p.log_a_min) == (1, 0, 1, float("-inf"))
+    with pytest.raises(ValueError):
+        kda._prologue(dict(normalise_k=True))
