@@ -99,10 +99,15 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
-// Input prologue (kda_prologue_t): log a = max(-softplus(x), lo) with
-// softplus(x) = max(x, 0) + log(1 + e^{-|x|}); beta = 1 / (1 + e^{-x}).
+// Input prologue (kda_prologue_t).  log a = max(-softplus(x), lo) is formed in
+// the log2 domain from the hardware exp2 and log2: -log2(1 + 2^{x log2 e}),
+// clipped at lo2 = lo log2 e (softplus below ~1e-7 rounds to 0, and an overflow
+// to infinity meets the clip or gives a = 0).  beta = 1 / (1 + e^{-x}).
+__device__ __forceinline__ float prologue_log2_a(float x, float lo2) {
+    return fmaxf(-__builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(x * LOG2E)), lo2);
+}
 __device__ __forceinline__ float prologue_log_a(float x, float lo) {
-    return fmaxf(-(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)))), lo);
+    return prologue_log2_a(x, lo * LOG2E) * 0.6931471805599453f;
 }
 __device__ __forceinline__ float prologue_beta(float x) { return 1.f / (1.f + __expf(-x)); }
 

@@ -234,10 +234,12 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
             f32x2 run = f32x2{0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                f32x2 lx = in.la[i];
-                if (PRO && p.pro.log_a_raw)
-                    lx = f32x2{prologue_log_a(lx[0], p.pro.log_a_min), prologue_log_a(lx[1], p.pro.log_a_min)};
-                run += (4 * tg + i < Lc) ? lx * LOG2E : f32x2{0.f, 0.f};
+                f32x2 l2 = in.la[i] * LOG2E;
+                if (PRO && p.pro.log_a_raw) {
+                    const float lo2 = p.pro.log_a_min * LOG2E;
+                    l2 = f32x2{prologue_log2_a(in.la[i][0], lo2), prologue_log2_a(in.la[i][1], lo2)};
+                }
+                run += (4 * tg + i < Lc) ? l2 : f32x2{0.f, 0.f};
                 lam[i] = run;
             }
             *reinterpret_cast<f32x2*>(&s.u2.grp[tg * DK + c]) = run;

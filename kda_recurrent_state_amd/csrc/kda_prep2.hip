@@ -254,10 +254,12 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const bool valid = 8 * o + j < Lc;
-            f32x2 lx = in.la[j];
-            if (PRO && p.pro.log_a_raw)
-                lx = f32x2{prologue_log_a(lx[0], p.pro.log_a_min), prologue_log_a(lx[1], p.pro.log_a_min)};
-            f32x2 la2 = valid ? lx * LOG2E : f32x2{0.f, 0.f};
+            f32x2 la2 = in.la[j] * LOG2E;
+            if (PRO && p.pro.log_a_raw) {
+                const float lo2 = p.pro.log_a_min * LOG2E;
+                la2 = f32x2{prologue_log2_a(in.la[j][0], lo2), prologue_log2_a(in.la[j][1], lo2)};
+            }
+            if (!valid) la2 = f32x2{0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const float x = fmaxf(la2[e], LA_MIN);
