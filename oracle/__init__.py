@@ -51,7 +51,7 @@ def load_library(path: str | None = None):
         return lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB):
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
                 build()
             _lib = ctypes.CDLL(_LIB)
             _declare(_lib)
@@ -64,6 +64,10 @@ def _declare(lib) -> None:
     lib.kda_oracle_fwd.restype = ctypes.c_int
     lib.kda_oracle_fwd.argtypes = [I64, P, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P,
                                    ctypes.c_int, P, P, ctypes.c_int]
+    if hasattr(lib, "kda_oracle_bwd"):
+        lib.kda_oracle_bwd.restype = ctypes.c_int
+        lib.kda_oracle_bwd.argtypes = [I64, P, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P,
+                                       ctypes.c_int, P, P, P, P, P, P, P, P, ctypes.c_int]
 
 
 def _f64(x) -> np.ndarray:
@@ -149,3 +153,57 @@ def kda_oracle(q, k, v, log_a, beta, S0=None, cu_seqlens=None, order: int = 0,
     if rc != 0:
         raise RuntimeError("kda_oracle_fwd failed with code %d" % rc)
     return o, ST
+
+
+def kda_oracle_bwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, dO=None, dST=None,
+                   order: int = 0, threads: int | None = None, lib=None):
+    """Gradient of kda_oracle in fp64.
+
+    For a scalar loss whose derivatives with respect to kda_oracle's outputs are
+    dO [T, H, dv] and dST [N, H, dk, dv] (None: zero), return a dict with the
+    derivatives with respect to its inputs: "dq", "dk" [T, H, dk], "dv" [T, H, dv],
+    "dlog_a" (the shape of log_a), "dbeta" [T, H] and "dS0" [N, H, dk, dv], as
+    float64 arrays.  The walk is the chain rule applied to one token's update at a
+    time, backwards from the last token (kda_oracle.c, kda_oracle_bwd).
+    """
+    q, k, v, log_a, beta = (_f64(x) for x in (q, k, v, log_a, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if k.shape != (T, H, dk) or v.shape[:2] != (T, H) or beta.shape != (T, H):
+        raise ValueError("inconsistent shapes")
+    if log_a.shape == (T, H, dk):
+        scalar = 0
+    elif log_a.shape == (T, H):
+        scalar = 1
+    else:
+        raise ValueError("log_a must be [T,H,dk] or [T,H]")
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64))
+    N = cu.shape[0] - 1
+    if cu[-1] != T:
+        raise ValueError("cu_seqlens[-1] must equal T")
+    s0 = None if S0 is None else _f64(S0)
+    if s0 is not None and s0.shape != (N, H, dk, dv):
+        raise ValueError("S0 must be [N,H,dk,dv]")
+    do = np.zeros((T, H, dv)) if dO is None else _f64(dO)
+    if do.shape != (T, H, dv):
+        raise ValueError("dO must be [T,H,dv]")
+    dst = None if dST is None else _f64(dST)
+    if dst is not None and dst.shape != (N, H, dk, dv):
+        raise ValueError("dST must be [N,H,dk,dv]")
+    out = {"dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
+           "dlog_a": np.zeros(log_a.shape), "dbeta": np.zeros((T, H)),
+           "dS0": np.zeros((N, H, dk, dv))}
+    nt = threads if threads is not None else (os.cpu_count() or 1)
+    L = lib if lib is not None else load_library()
+    ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    rc = L.kda_oracle_bwd(N, ptr(cu), H, dk, dv, ptr(q), ptr(k), ptr(v), ptr(log_a), scalar,
+                          ptr(beta), ptr(s0), int(order), ptr(do), ptr(dst), ptr(out["dq"]),
+                          ptr(out["dk"]), ptr(out["dv"]), ptr(out["dlog_a"]), ptr(out["dbeta"]),
+                          ptr(out["dS0"]), int(nt))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_bwd failed with code %d" % rc)
+    return out
