@@ -210,6 +210,49 @@ KDA_API int kda_chunk_workspace_size(const kda_dims_t* dims, size_t* bytes);
 KDA_API int kda_chunk_workspace_min(const kda_dims_t* dims, size_t* bytes);
 
 /*
+ * Gradient of the prefill, for training.  On the pages the delta rule's cost is
+ * a sequential dependency that blocks parallel training, and the chunkwise (WY)
+ * form is what makes it parallel (page "The argument, in one page", section
+ * "Everything, in one table", rows "Delta rule" and "Chunkwise / WY"); this is
+ * the derivative of that same map, S_t = Diag(a_t)(I - beta_t k_t^T k_t) S_{t-1}
+ * + beta_t k_t^T v_t, o_t = q_t S_t (row "KDA"; with scalar_decay, row "Gated
+ * DeltaNet").
+ *
+ * For a loss L with dL/do = dO and dL/dS_T = dS_T, the call writes the
+ * derivatives of L with respect to every input of kda_chunk_fwd:
+ *   q, k, v, log_a, beta, S0, cu_seqlens   as for kda_chunk_fwd (the forward inputs)
+ *   dO        [T, H, dv]   qkv_dtype
+ *   dS_T      [N, H, dk, dv] float32, or NULL for zero
+ *   dq, dk    [T, H, dk]   qkv_dtype outputs
+ *   dv        [T, H, dv]   qkv_dtype output
+ *   dlog_a    float32 output with the shape of log_a ([T, H] with a scalar decay:
+ *             the sum over channels)
+ *   dbeta     [T, H]       float32 output
+ *   dS0       [N, H, dk, dv] float32 output, or NULL to skip; written also when
+ *             S0 is NULL (the derivative at the zero initial state)
+ *   workspace device memory of at least kda_chunk_bwd_workspace_size bytes,
+ *             256-byte aligned; its contents are not needed after the call.
+ *             Calls that share a workspace must be ordered on one stream.
+ * The call first reruns the prefill (method, chunk_size and dv_split as in dims)
+ * keeping the state at every 64th token, then three kernels walk 16-token
+ * pieces: operators per piece, the derivative with respect to the state
+ * backwards through each sequence, and the gradients of each 64-token chunk.
+ * Supported: the erase-first order (KDA_ORDER_DECAY_FIRST with a per-channel
+ * decay returns KDA_ERR_UNSUPPORTED), dk == dv, bf16 with dk in {32, 64, 128},
+ * fp32 with dk in {16, 32, 64}.  No input prologue.  Outputs must not alias
+ * inputs or each other.  Returns a kda_status_t.
+ */
+KDA_API int kda_chunk_bwd(const kda_dims_t* dims, const void* q, const void* k, const void* v,
+                  const float* log_a, const float* beta, const float* S0,
+                  const int32_t* cu_seqlens, const void* dO, const float* dS_T, void* dq, void* dk,
+                  void* dv, float* dlog_a, float* dbeta, float* dS0, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Workspace kda_chunk_bwd needs for these dims (about 2.6 KB per token and head
+ * at dk = dv = 128, plus what the prefill's two-pass method prefers). */
+KDA_API int kda_chunk_bwd_workspace_size(const kda_dims_t* dims, size_t* bytes);
+
+/*
  * One decode step: one token per sequence (T == N).
  *   q, k      [N, H, dk]   qkv_dtype
  *   v         [N, H, dv]   qkv_dtype

@@ -24,7 +24,8 @@ import threading
 
 import torch  # loads the HIP runtime the library then shares
 
-__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "snapshot_rows", "chunk_workspace_size", "decode_step", "KdaError", "library_path", "load_library",
+__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "snapshot_rows", "chunk_workspace_size", "chunk_bwd",
+           "chunk_bwd_workspace_size", "decode_step", "KdaError", "library_path", "load_library",
            "METHOD_AUTO", "METHOD_SINGLE", "METHOD_TWO_PASS", "ORDER_ERASE_FIRST", "ORDER_DECAY_FIRST"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -102,7 +103,10 @@ def load_library(build_if_missing: bool = True):
             lib.kda_chunk_fwd_snapshots.restype = ctypes.c_int
             lib.kda_chunk_fwd_snapshots.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P,
                                                     ctypes.c_int64, ctypes.c_int64, P, ctypes.c_size_t, P]
-            for name in ("kda_chunk_workspace_size", "kda_chunk_workspace_min"):
+            lib.kda_chunk_bwd.restype = ctypes.c_int
+            lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                          ctypes.c_size_t, P]
+            for name in ("kda_chunk_workspace_size", "kda_chunk_workspace_min", "kda_chunk_bwd_workspace_size"):
                 fn = getattr(lib, name)
                 fn.restype = ctypes.c_int
                 fn.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(ctypes.c_size_t)]
@@ -308,6 +312,83 @@ def chunk_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, 
     need = ctypes.c_size_t(0)
     fn = lib.kda_chunk_workspace_min if minimum else lib.kda_chunk_workspace_size
     _check(lib, fn(ctypes.byref(d), ctypes.byref(need)))
+    return need.value
+
+
+def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, chunk_size: int = 0,
+              dv_split: int = 0, num_seqs: int | None = None, method: int = METHOD_AUTO, workspace=None,
+              max_seqlen: int | None = None, initial_state_grad=True):
+    """Gradient of chunk_fwd (erase-first order) for upstream derivatives dO
+    [T,H,dv] (and dS_T [N,H,dk,dv], None for zero).  Returns a dict with "dq",
+    "dk" [T,H,dk] and "dv" [T,H,dv] in q's dtype, "dlog_a" (log_a's shape) and
+    "dbeta" [T,H] in float32, and "dS0" [N,H,dk,dv] float32 (None when
+    initial_state_grad is False).  The forward inputs are passed again; the call
+    reruns the prefill to recover its states.  workspace: a uint8 tensor of at
+    least chunk_bwd_workspace_size bytes, or None to have one allocated for this
+    call.  chunk_size, dv_split and method choose the prefill rerun."""
+    lib = load_library()
+    _need(q, "q", ndim=3)
+    T, H, dk = q.shape
+    _need(k, "k", q.dtype, 3)
+    _need(v, "v", q.dtype, 3)
+    dv = v.shape[2]
+    if k.shape != q.shape or v.shape[:2] != (T, H):
+        raise ValueError("q, k, v shapes disagree")
+    _need(log_a, "log_a", torch.float32)
+    if log_a.shape == (T, H, dk):
+        scalar = 0
+    elif log_a.shape == (T, H):
+        scalar = 1
+    else:
+        raise ValueError(f"log_a must be [T,H,dk] or [T,H] (got {tuple(log_a.shape)})")
+    _need(beta, "beta", torch.float32)
+    if beta.shape != (T, H):
+        raise ValueError("beta must be [T,H]")
+    _need(dO, "dO", q.dtype, 3)
+    if dO.shape != v.shape:
+        raise ValueError("dO must have v's shape")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = 1 if num_seqs is None else int(num_seqs)
+    for name, x in (("S0", S0), ("dS_T", dS_T)):
+        if x is not None:
+            _need(x, name, torch.float32)
+            if x.shape != (N, H, dk, dv):
+                raise ValueError(f"{name} must be [{N},{H},{dk},{dv}] (got {tuple(x.shape)})")
+    if max_seqlen is None:
+        if cu_seqlens is not None and N > 0:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
+        else:
+            max_seqlen = 0
+    d = _Dims(N, H, T, dk, dv, _dtype_code(q), scalar, int(chunk_size), int(dv_split), int(method),
+              ORDER_ERASE_FIRST, int(max_seqlen))
+    if workspace is None:
+        need = ctypes.c_size_t(0)
+        _check(lib, lib.kda_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(need)))
+        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dlog_a": torch.empty_like(log_a), "dbeta": torch.empty_like(beta),
+           "dS0": torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device) if initial_state_grad else None}
+    st = lib.kda_chunk_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta), _ptr(S0),
+                           _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]),
+                           _ptr(out["dv"]), _ptr(out["dlog_a"]), _ptr(out["dbeta"]), _ptr(out["dS0"]),
+                           _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream_handle(q.device))
+    _check(lib, st)
+    return out
+
+
+def chunk_bwd_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, dv_split=0,
+                             method=METHOD_AUTO, max_seqlen=0):
+    """Bytes of workspace chunk_bwd needs for these shapes."""
+    lib = load_library()
+    T, H, dk = q.shape
+    d = _Dims(int(num_seqs), H, T, dk, v.shape[2], _dtype_code(q), int(bool(scalar_decay)), int(chunk_size),
+              int(dv_split), int(method), ORDER_ERASE_FIRST, int(max_seqlen))
+    need = ctypes.c_size_t(0)
+    _check(lib, lib.kda_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(need)))
     return need.value
 
 

@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_prep.hip", "kda_prep2.hip", "kda_scan.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_prep.hip", "kda_prep2.hip", "kda_scan.hip",
+           "kda_bwd.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=fast",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -24,7 +25,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
 # accumulator registers on top of its 256 vector registers; left to itself the
 # compiler then keeps matrix-core results there and copies the state back and
 # forth every chunk.  This keeps them in vector registers (the walk fits).
-EXTRA = {"kda_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"kda_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # the gradient pass holds a state and its derivative per wavefront; in this
+         # form it fits without spilling to scratch memory at dk = dv = 128
+         "kda_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

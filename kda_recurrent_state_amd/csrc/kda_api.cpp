@@ -352,6 +352,41 @@ int kda_chunk_fwd_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const 
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+// Backward workspace: [prefill's two-pass workspace][o scratch][states every 64
+// tokens][operator blocks per 16 tokens][state derivatives per 64-token chunk].
+struct BwdPlan {
+    Plan fwd;
+    size_t fwd_ws = 0, o_bytes = 0, snap_bytes = 0, ops_bytes = 0, x_bytes = 0, total = 0;
+    int64_t snap_rows = 0, maxlen = 0;
+};
+
+int plan_bwd(const kda_dims_t* d, bool have_cu, BwdPlan* bp) {
+    int st = plan_prefill(d, have_cu, &bp->fwd);
+    if (st) return st;
+    if (d->order == KDA_ORDER_DECAY_FIRST && !d->scalar_decay)
+        return fail(KDA_ERR_UNSUPPORTED, "the backward supports the erase-first order only");
+    if (!kda::bwd_supported(d->qkv_dtype, d->dk, d->dv))
+        return fail(KDA_ERR_UNSUPPORTED, "no backward for dtype %d, dk %d, dv %d", d->qkv_dtype, d->dk, d->dv);
+    const int64_t T = d->total_tokens, N = d->num_seqs, H = d->num_heads;
+    const size_t state = (size_t)d->dk * d->dv * 4;
+    bp->fwd_ws = bp->fwd.two_pass_ok ? bp->fwd.pref_bytes : 0;
+    bp->o_bytes = round256((size_t)T * H * d->dv * (d->qkv_dtype == KDA_BF16 ? 2 : 4));
+    bp->snap_rows = T / 64;
+    bp->snap_bytes = round256((size_t)bp->snap_rows * H * state);
+    bp->ops_bytes = round256((size_t)(T / 16 + N) * H * kda::bwd_block_bytes(d->qkv_dtype, d->dk));
+    bp->x_bytes = round256((size_t)(T / 64 + N) * H * state);
+    bp->total = round256(bp->fwd_ws) + bp->o_bytes + bp->snap_bytes + bp->ops_bytes + bp->x_bytes;
+    bp->maxlen = N > 0 ? bp->fwd.max_chunks * bp->fwd.chunk : 0;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int kda_decode_step(const kda_dims_t* d, const void* q, const void* k, const void* v,
                     const float* log_a, const float* beta, const float* S_in, float* S_out,
                     void* o, void* stream) {
@@ -380,6 +415,85 @@ int kda_decode_step_ex(const kda_dims_t* d, const kda_prologue_t* prologue, cons
     hipError_t e = kda::launch_decode(d->qkv_dtype, d->dk, d->dv, d->scalar_decay, kernel_order(d), pro, heads, q, k,
                                       v, log_a, beta, S_in, S_out, o, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int kda_chunk_bwd_workspace_size(const kda_dims_t* d, size_t* bytes) {
+    if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    BwdPlan bp;
+    int st = plan_bwd(d, true, &bp);
+    if (st) return st;
+    *bytes = bp.total;
+    return ok();
+}
+
+int kda_chunk_bwd(const kda_dims_t* d, const void* q, const void* k, const void* v, const float* log_a,
+                  const float* beta, const float* S0, const int32_t* cu_seqlens, const void* dO, const float* dS_T,
+                  void* dq, void* dk, void* dv, float* dlog_a, float* dbeta, float* dS0, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    BwdPlan bp;
+    int st = plan_bwd(d, cu_seqlens != nullptr, &bp);
+    if (st) return st;
+    if (d->num_seqs == 0) {
+        if (d->total_tokens != 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs = 0 but total_tokens = %lld", (long long)d->total_tokens);
+        return ok();
+    }
+    if (!cu_seqlens && d->total_tokens % d->num_seqs != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "cu_seqlens is NULL but total_tokens = %lld is not a multiple of num_seqs = %d",
+                    (long long)d->total_tokens, d->num_seqs);
+    if (d->total_tokens > 0) {
+        const void* ptrs[] = {q, k, v, log_a, beta, dO, dq, dk, dv, dlog_a, dbeta};
+        const char* names[] = {"q", "k", "v", "log_a", "beta", "dO", "dq", "dk", "dv", "dlog_a", "dbeta"};
+        const int a4 = d->scalar_decay ? 4 : 16;
+        const int align[] = {16, 16, 16, a4, 4, 16, 16, 16, 16, a4, 4};
+        if ((st = check_ptrs(ptrs, names, align, 11))) return st;
+    }
+    if (S0 && !aligned16(S0)) return fail(KDA_ERR_MISALIGNED, "S0 is not 16-byte aligned");
+    if (dS_T && !aligned16(dS_T)) return fail(KDA_ERR_MISALIGNED, "dS_T is not 16-byte aligned");
+    if (dS0 && !aligned16(dS0)) return fail(KDA_ERR_MISALIGNED, "dS0 is not 16-byte aligned");
+    if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u))
+        return fail(KDA_ERR_MISALIGNED, "cu_seqlens is not 4-byte aligned");
+    if (!workspace || workspace_bytes < bp.total)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "the backward needs a workspace of at least %zu bytes (got %zu)",
+                    bp.total, workspace ? workspace_bytes : (size_t)0);
+    if ((uintptr_t)workspace & 255u) return fail(KDA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+    const int64_t units = (int64_t)d->num_seqs * d->num_heads;
+    const int64_t nsub_max = (bp.maxlen + 15) / 16, nch_max = (bp.maxlen + 63) / 64;
+    if (units > 65535 || nsub_max > 0x7fffffff)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "too many (sequence, head) units for the backward: %lld",
+                    (long long)units);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* fwd_ws = bp.fwd_ws ? ws : nullptr;
+    size_t off = round256(bp.fwd_ws);
+    void* o_scratch = ws + off;
+    off += bp.o_bytes;
+    float* snap = reinterpret_cast<float*>(ws + off);
+    off += bp.snap_bytes;
+    void* ops = ws + off;
+    off += bp.ops_bytes;
+    float* xbuf = reinterpret_cast<float*>(ws + off);
+
+    // the prefill again, keeping the state at every 64th token (nothing to keep
+    // when no sequence reaches 64 tokens)
+    if (bp.snap_rows > 0) {
+        kda_dims_t d2 = *d;
+        d2.order = KDA_ORDER_ERASE_FIRST;
+        st = kda_chunk_fwd_snapshots(&d2, q, k, v, log_a, beta, S0, cu_seqlens, o_scratch, nullptr, snap,
+                                     bp.snap_rows, 64, fwd_ws, bp.fwd_ws, stream);
+        if (st) return st;
+    }
+
+    kda::BwdLaunch a;
+    a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.beta = beta; a.S0 = S0;
+    a.cu_seqlens = cu_seqlens; a.eq_len = cu_seqlens ? 0 : d->total_tokens / d->num_seqs;
+    a.dO = dO; a.dST = dS_T; a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_a = dlog_a; a.dbeta = dbeta; a.dS0 = dS0;
+    a.snap = snap; a.ops = ops; a.xbuf = xbuf;
+    a.num_heads = d->num_heads; a.units = units; a.nsub_max = (int32_t)nsub_max; a.nch_max = (int32_t)nch_max;
+    a.kdim = d->dk; a.vdim = d->dv; a.dtype = d->qkv_dtype; a.scalar = d->scalar_decay;
+    hipError_t e = kda::launch_bwd(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -1,0 +1,1109 @@
+// kda_bwd.hip -- gradient of the prefill (the erase-then-decay ordering of the
+// table row "KDA" on page "The argument, in one page", in its chunkwise form, row
+// "Chunkwise / WY" of the same table).
+//
+// For a loss with derivatives dO (outputs) and dS_T (final states), the call
+// returns dq, dk, dv, dlog_a, dbeta and dS0.  Per (sequence, head) the tokens are
+// cut into sub-chunks of 16.  With S the state at a sub-chunk start, X the
+// derivative with respect to the state at its end, g the cumulative log-decay from
+// the sub-chunk start (gm: exclusive, gC: at the end), b = beta:
+//
+//   Kb = k e^{gm}, Qb = q e^{g}, Kcc = k e^{gC-gm}, Ktc = k e^{gC-g}, gamma = e^{gC}
+//   A0 = strict_lower(Kb (k e^{-gm})^T), L = strict_lower(Kb (k e^{-g})^T),
+//   P1 = lower(Qb (k e^{-gm})^T), P2 = lower(Qb (k e^{-g})^T), T = (I + diag(b) A0)^-1
+//   forward:  Y0 = Kb S + L bV, E = -T diag(b) Y0, Y = Y0 + A0 E,
+//             S_next = gamma S + Kcc^T E + Ktc^T bV
+//   backward: G = T^T (P1^T dO + Kcc X), F = -diag(b) G, R = Ktc X + P2^T dO + L^T F,
+//             X_prev = gamma X + Qb^T dO + Kb^T F
+//   dv = diag(b) R, dbeta = rowsum(R V) - rowsum(G Y),
+//   dq   = e^{g} (dO S^T)      + e^{g-m}  [lower(dO E^T) Kc' + lower(dO bV^T) Kt']
+//   gs   = e^{gm} (G S^T)      + e^{gm-m} [strict_lower(G E^T) Kc' + strict_lower(G bV^T) Kt']
+//   vds  = e^{gC-g} (V X^T)    + e^{m-g}  [upper(V dO^T) Qb' + strict_upper(V F^T) Kb']
+//   ayds = e^{gC-gm} (Y X^T)   + e^{m-gm} [upper(Y dO^T) Qb' + strict_upper(Y F^T) Kb']
+//   dk = diag(b) (vds - ayds - gs),
+//   dlog_a_i = phi_i - b_i k_i vds_i, phi_i = phi_{-1} + sum_{j<=i} (k dk + 2 b k gs)_j
+//              - sum_{j<i} (q dq)_j, phi_{-1} = rowsum(X_prev * S)
+// where the primed operands carry the decay relative to a per-channel reference
+// m = gC / 2 (Kc' = k e^{m-gm}, Kt' = k e^{m-g}, Qb' = q e^{g-m}, Kb' = k e^{gm-m}),
+// so every factor stays below e^{span/2}.  A sub-chunk whose span -gC exceeds 160
+// nats in some channel takes one exponent per term instead.
+//
+// Three kernels follow the forward prefill, which leaves the state at every 64th
+// token: kda_bwd_ops (one wavefront per sub-chunk: the C x C products, the solve,
+// the operators of the reverse walk), kda_bwd_scan (one workgroup per (sequence,
+// head, value slice): the reverse walk X <- X_prev, keeping X at every 64-token
+// boundary) and kda_bwd_grad (one workgroup per 64-token chunk: its sub-chunks in
+// reverse, each start state recomputed from the chunk's kept state, all products
+// on matrix cores).
+#include "kda_chunk_common.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int SC = 16;                   // sub-chunk tokens
+constexpr int CHB = 64;                  // tokens between kept states
+constexpr float SPAN2_MAX = 160.f * LOG2E;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float ex2n(float x) { return __builtin_amdgcn_exp2f(fminf(x, 0.f)); }
+
+// ---------------------------------------------------------------- products
+// A 16-deep contraction in bf16 runs as the 32-deep instruction with the upper
+// half of k zero (lanes 32..63 supply zeros), so that every accumulation chain
+// uses a single instruction type.
+__device__ __forceinline__ f32x4 mma16(const bf16* ra, const bf16* rb, f32x4 acc, int lane) {
+    bf16x8 a = {}, b = {};
+    if (lane < 32) {
+        a = *reinterpret_cast<const bf16x8*>(ra + 8 * (lane >> 4));
+        b = *reinterpret_cast<const bf16x8*>(rb + 8 * (lane >> 4));
+    }
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(const float* ra, const float* rb, f32x4 acc, int lane) {
+    return tile_mma_r<float, 16>(ra, rb, acc, lane);
+}
+
+// acc += A[16 x KD] B[KD x 16]; ra / rb: this lane's A row and B column, both
+// k-contiguous in LDS (row (lane % 16) of A stored [m][k], of B stored [n][k]).
+template <typename MT, int KD>
+__device__ __forceinline__ f32x4 mmak(const MT* ra, const MT* rb, f32x4 acc, int lane) {
+    if constexpr (sizeof(MT) == 2) {
+        constexpr int N32 = KD / 32;
+        static_assert(KD % 16 == 0, "contraction must be a multiple of 16");
+        if constexpr (N32 > 0) acc = tile_mma_r<bf16, N32 * 32>(ra, rb, acc, lane);
+        if constexpr (KD % 32 == 16) acc = mma16(ra + N32 * 32, rb + N32 * 32, acc, lane);
+        return acc;
+    } else {
+        return tile_mma_r<float, KD>(ra, rb, acc, lane);
+    }
+}
+
+// An accumulator tile holds D[m][n] with m = 4 (lane / 16) + r, n = lane % 16.
+// store_nat writes it to Z[n][m] (four consecutive m per lane), store_rm to Z[m][n].
+template <typename MT>
+__device__ __forceinline__ void store_nat(MT* z, int ld, f32x4 d, int lane) {
+    store4<MT>(z + (lane & 15) * ld + 4 * (lane >> 4), d);
+}
+template <typename MT>
+__device__ __forceinline__ void store_rm(MT* z, int ld, f32x4 d, int lane) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[(4 * (lane >> 4) + r) * ld + (lane & 15)] = from_f32<MT>(d[r]);
+}
+
+// fp32 state tile <-> row-major global [rows][ld] (inverse of store_state_tile).
+__device__ __forceinline__ f32x4 load_state_tile(const float* src, int64_t ld, int lane) {
+    const int row = 4 * (lane >> 4) + (lane & 3), col = 4 * ((lane & 15) >> 2);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (int64_t)row * ld + col);
+    return __builtin_bit_cast(f32x4, quad_transpose(__builtin_bit_cast(i32x4, v), lane));
+}
+
+// 16 bytes of MT as one vector of MT (keeps every access in the element type).
+template <typename MT> struct V16;
+template <> struct V16<bf16> { typedef bf16x8 type; };
+template <> struct V16<float> { typedef f32x4 type; };
+template <typename MT>
+__device__ __forceinline__ void copy16(MT* dst, const MT* src) {
+    *reinterpret_cast<typename V16<MT>::type*>(dst) = *reinterpret_cast<const typename V16<MT>::type*>(src);
+}
+// eight values rounded to MT, stored at dst (16 bytes for bf16, 32 for fp32)
+template <typename MT>
+__device__ __forceinline__ void store8(MT* dst, const float* x) {
+    if constexpr (sizeof(MT) == 2) {
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
+        *reinterpret_cast<bf16x8*>(dst) = v;
+    } else {
+        reinterpret_cast<f32x4*>(dst)[0] = f32x4{x[0], x[1], x[2], x[3]};
+        reinterpret_cast<f32x4*>(dst)[1] = f32x4{x[4], x[5], x[6], x[7]};
+    }
+}
+
+// ------------------------------------------------------------ sequences
+struct SeqSpan {
+    int64_t t0;
+    int len;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, int64_t eq_len, int n) {
+    if (!cu) return SeqSpan{(int64_t)n * eq_len, (int)eq_len};
+    return SeqSpan{(int64_t)cu[n], cu[n + 1] - cu[n]};
+}
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// sum over sequences m < n of ceil(len_m / div) (wavefront-wide; every lane gets it)
+__device__ __forceinline__ int64_t ceil_blocks_before(const int32_t* cu, int64_t eq_len, int n, int div) {
+    if (!cu) return (int64_t)n * ((eq_len + div - 1) / div);
+    int64_t s = 0;
+    for (int m = (int)(threadIdx.x & 63); m < n; m += 64) s += (cu[m + 1] - cu[m] + div - 1) / div;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    return s;
+}
+
+// ------------------------------------------------------- operator block
+// Per (sequence, head, sub-chunk), written by kda_bwd_ops:
+//   W    [16][DK]   diag(b) T^T Kcc                (reverse walk: F = -(W X + M dO))
+//   M    [16][16]   diag(b) T^T P1^T
+//   QK   [DK][32]   [Qb^T | Kb^T]                  (X_prev = gamma X + QK [dO; F])
+//   gam  [DK]       e^{gC} (fp32)
+//   mats 7 x [16][16]: T diag(b), T^T, L, L^T, A0, P1^T, P2^T (row-major)
+//   flag int32: 1 if the sub-chunk needs one exponent per term
+template <typename MT, int DK>
+struct OpBlock {
+    static constexpr int S = (int)sizeof(MT);
+    static constexpr int W = 0;
+    static constexpr int M = W + 16 * DK * S;
+    static constexpr int QK = M + 256 * S;
+    static constexpr int GAM = QK + 32 * DK * S;
+    static constexpr int MATS = GAM + 4 * DK;
+    static constexpr int FLAG = MATS + 7 * 256 * S;
+    static constexpr int BYTES = FLAG + 16;
+    static constexpr int WALK = MATS;  // bytes the reverse walk reads
+    static_assert(BYTES % 16 == 0 && WALK % 16 == 0, "16-byte pieces");
+};
+enum { MAT_TB = 0, MAT_TT, MAT_L, MAT_LT, MAT_A0, MAT_P1T, MAT_P2T };
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_a;
+    const float* beta;
+    const float* S0;
+    const int32_t* cu;
+    int64_t eq_len;
+    const void* dO;
+    const float* dST;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dla;
+    float* dbeta;
+    float* dS0;
+    const float* snap;       // forward states, row per 64 tokens of each sequence
+    uint8_t* ops;            // operator blocks
+    float* xbuf;             // state derivatives at 64-token chunk ends
+    int32_t H;
+    int32_t scalar;
+    int32_t split;
+};
+
+// Loads a sub-chunk's 16 rows of a [T, H, D] tensor into LDS z[16][ld] (zeros past nrow).
+template <typename MT, int D>
+__device__ __forceinline__ void load_rows(MT* z, int ld, const MT* g, int64_t t0, int H, int h, int nrow, int tid,
+                                          int nthr) {
+    constexpr int PER = 16 / (int)sizeof(MT);  // elements per 16-byte piece
+    constexpr int PR = D / PER;                // pieces per row
+    typedef typename V16<MT>::type VT;
+    for (int p = tid; p < 16 * PR; p += nthr) {
+        const int i = p / PR, e = (p % PR) * PER;
+        VT x = {};
+        if (i < nrow) x = *reinterpret_cast<const VT*>(g + ((t0 + i) * H + h) * (int64_t)D + e);
+        *reinterpret_cast<VT*>(z + i * ld + e) = x;
+    }
+}
+
+// G2[i][c] = log2 e * sum_{j < i} log a_j (i = 0..16), beta, and the reference m2 = G2[16] / 2.
+template <int DK>
+__device__ __forceinline__ void load_decay(float* G2, float* bt, const float* la, const float* beta, int64_t t0,
+                                           int H, int h, int nrow, int scalar, int tid, int nthr) {
+    for (int c = tid; c < DK; c += nthr) {
+        float s = 0.f;
+        G2[c] = 0.f;
+#pragma unroll 4
+        for (int i = 0; i < SC; ++i) {
+            float x = 0.f;
+            if (i < nrow) x = scalar ? la[(t0 + i) * H + h] : la[((t0 + i) * H + h) * (int64_t)DK + c];
+            s += x * LOG2E;
+            G2[(i + 1) * DK + c] = s;
+        }
+    }
+    for (int i = tid; i < SC; i += nthr) bt[i] = i < nrow ? beta[(t0 + i) * H + h] : 0.f;
+}
+
+// ===================================================================== ops
+// One wavefront per (sequence, head, sub-chunk).
+template <typename MT, int DK>
+__global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
+    typedef OpBlock<MT, DK> OB;
+    constexpr int P = 16 / (int)sizeof(MT);
+    constexpr int LDK = DK + P, L16 = 16 + P;
+    __shared__ __attribute__((aligned(16))) MT kr[16 * LDK];
+    __shared__ __attribute__((aligned(16))) MT qr[16 * LDK];
+    __shared__ __attribute__((aligned(16))) MT KCT[DK * L16];
+    __shared__ __attribute__((aligned(16))) MT P1rm[16 * L16];
+    __shared__ __attribute__((aligned(16))) MT bTT[16 * L16];
+    __shared__ float G2[(SC + 1) * DK];
+    __shared__ float bt[SC];
+    __shared__ float Gf[4][16][17];  // A0, L, P1, P2 (fp32, row-major, masked)
+    __shared__ float Tf[16][17];
+
+    const int lane = threadIdx.x;
+    const int s = blockIdx.x;
+    const int64_t unit = blockIdx.y;
+    const int n = (int)(unit / p.H), h = (int)(unit % p.H);
+    const SeqSpan sq = seq_span(p.cu, p.eq_len, n);
+    if (s * SC >= sq.len) return;
+    const int nrow = min(SC, sq.len - s * SC);
+    const int nsub = ceil_div(sq.len, SC);
+    const int64_t bi = ceil_blocks_before(p.cu, p.eq_len, n, SC) * p.H + (int64_t)h * nsub + s;
+    uint8_t* blk = p.ops + bi * OB::BYTES;
+    const int64_t t0 = sq.t0 + (int64_t)s * SC;
+
+    load_rows<MT, DK>(kr, LDK, static_cast<const MT*>(p.k), t0, p.H, h, nrow, lane, 64);
+    load_rows<MT, DK>(qr, LDK, static_cast<const MT*>(p.q), t0, p.H, h, nrow, lane, 64);
+    load_decay<DK>(G2, bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, lane, 64);
+    __syncthreads();
+
+    float span = 0.f;
+    for (int c = lane; c < DK; c += 64) span = fmaxf(span, -G2[SC * DK + c]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) span = fmaxf(span, __shfl_xor(span, off));
+    const bool exact = span > SPAN2_MAX;
+
+    // C x C products
+    if (!exact) {
+        // (m = t, n = i); A rows: k (A0, L) or q (P1, P2) times e^{h_t - m}; B rows: k times e^{m - h_i}
+        f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+        const int r16 = lane & 15;
+        constexpr int KPL = Mma<MT>::KPL, KS = Mma<MT>::K;
+#pragma unroll
+        for (int kb = 0; kb < DK; kb += KS) {
+            typename Mma<MT>::frag ak, aq, bm, bg;
+            float fk[KPL], fq[KPL], fm[KPL], fg[KPL];
+            const int c0 = kb + (lane >> 4) * KPL;
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) {
+                const int c = c0 + e;
+                const float m2 = 0.5f * G2[SC * DK + c];
+                fk[e] = ex2(G2[r16 * DK + c] - m2);          // e^{gm_t - m}
+                fq[e] = ex2(G2[(r16 + 1) * DK + c] - m2);    // e^{g_t - m}
+                fm[e] = ex2(m2 - G2[r16 * DK + c]);          // e^{m - gm_i}
+                fg[e] = ex2(m2 - G2[(r16 + 1) * DK + c]);    // e^{m - g_i}
+            }
+            const typename Mma<MT>::frag kx = Mma<MT>::loadr(kr + r16 * LDK + kb, lane);
+            const typename Mma<MT>::frag qx = Mma<MT>::loadr(qr + r16 * LDK + kb, lane);
+            ak = Mma<MT>::scale(kx, fk);
+            aq = Mma<MT>::scale(qx, fq);
+            bm = Mma<MT>::scale(kx, fm);
+            bg = Mma<MT>::scale(kx, fg);
+            acc[0] = Mma<MT>::mma(ak, bm, acc[0]);  // A0
+            acc[1] = Mma<MT>::mma(ak, bg, acc[1]);  // L
+            acc[2] = Mma<MT>::mma(aq, bm, acc[2]);  // P1
+            acc[3] = Mma<MT>::mma(aq, bg, acc[3]);  // P2
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * (lane >> 4) + r, i = lane & 15;
+                const bool keep = g < 2 ? i < t : i <= t;
+                Gf[g][t][i] = keep ? acc[g][r] : 0.f;
+            }
+    } else {
+        for (int pi = lane; pi < 256; pi += 64) {
+            const int t = pi >> 4, i = pi & 15;
+            float a0 = 0.f, l = 0.f, p1 = 0.f, p2 = 0.f;
+            if (i <= t) {
+                for (int c = 0; c < DK; ++c) {
+                    const float kt = to_f32(kr[t * LDK + c]), qt = to_f32(qr[t * LDK + c]), ki = to_f32(kr[i * LDK + c]);
+                    const float gmt = G2[t * DK + c], gt = G2[(t + 1) * DK + c];
+                    const float gmi = G2[i * DK + c], gi = G2[(i + 1) * DK + c];
+                    if (i < t) {
+                        a0 += kt * ki * ex2(gmt - gmi);
+                        l += kt * ki * ex2(gmt - gi);
+                    }
+                    p1 += qt * ki * ex2(gt - gmi);
+                    p2 += qt * ki * ex2(gt - gi);
+                }
+            }
+            Gf[0][t][i] = a0; Gf[1][t][i] = l; Gf[2][t][i] = p1; Gf[3][t][i] = p2;
+        }
+    }
+    __syncthreads();
+
+    // T = (I + diag(b) A0)^-1, one column per lane
+    if (lane < 16) {
+        const int j = lane;
+        float t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float acc = i == j ? 1.f : 0.f;
+            if (i > j) {
+                float sdot = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < i; ++kk) sdot += Gf[0][i][kk] * t[kk];  // t[kk] = 0 for kk < j
+                acc = -bt[i] * sdot;
+            }
+            t[i] = acc;
+        }
+        const float bj = bt[j];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            Tf[i][j] = t[i];
+            bTT[j * L16 + i] = from_f32<MT>(bj * t[i]);  // (diag(b) T^T)[j][i] = b_j T[i][j]
+        }
+    }
+    // Kcc^T [c][s] = k_s e^{gC - gm_s}, P1 row-major
+    for (int x = lane; x < DK * 16; x += 64) {
+        const int c = x >> 4, s2 = x & 15;
+        KCT[c * L16 + s2] = from_f32<MT>(to_f32(kr[s2 * LDK + c]) * ex2(G2[SC * DK + c] - G2[s2 * DK + c]));
+    }
+    for (int x = lane; x < 256; x += 64) P1rm[(x >> 4) * L16 + (x & 15)] = from_f32<MT>(Gf[2][x >> 4][x & 15]);
+    __syncthreads();
+
+    // the seven 16 x 16 matrices of the gradient pass, 8 elements per piece
+    MT* mats = reinterpret_cast<MT*>(blk + OB::MATS);
+    for (int pc = lane; pc < 7 * 32; pc += 64) {
+        const int mi = pc >> 5, row = (pc >> 1) & 15, c0 = (pc & 1) * 8;
+        float out[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int col = c0 + e;
+            float x;
+            switch (mi) {
+                case MAT_TB: x = Tf[row][col] * bt[col]; break;
+                case MAT_TT: x = Tf[col][row]; break;
+                case MAT_L: x = Gf[1][row][col]; break;
+                case MAT_LT: x = Gf[1][col][row]; break;
+                case MAT_A0: x = Gf[0][row][col]; break;
+                case MAT_P1T: x = Gf[2][col][row]; break;
+                default: x = Gf[3][col][row]; break;
+            }
+            out[e] = x;
+        }
+        store8<MT>(mats + mi * 256 + row * 16 + c0, out);
+    }
+
+    // W (m = c, n = t): W^T[c][t] = sum_s Kcc^T[c][s] (b_t T[s][t]); natural store gives W[t][c]
+    MT* Wg = reinterpret_cast<MT*>(blk + OB::W);
+    for (int cb = 0; cb < DK / 16; ++cb) {
+        f32x4 acc = mma16(KCT + (cb * 16 + (lane & 15)) * L16, bTT + (lane & 15) * L16, zero4(), lane);
+        store_nat<MT>(Wg + cb * 16, DK, acc, lane);
+    }
+    // M (m = i, n = t): M^T[i][t] = sum_s P1[i][s] (b_t T[s][t]); natural store gives M[t][i]
+    {
+        f32x4 acc = mma16(P1rm + (lane & 15) * L16, bTT + (lane & 15) * L16, zero4(), lane);
+        store_nat<MT>(reinterpret_cast<MT*>(blk + OB::M), 16, acc, lane);
+    }
+    // QK [c][32] = [q_s e^{g_s} | k_s e^{gm_s}]
+    {
+        MT* qk = reinterpret_cast<MT*>(blk + OB::QK);
+        for (int pc = lane; pc < DK * 4; pc += 64) {
+            const int c = pc >> 2, s0 = (pc & 3) * 8;
+            float out[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int s2 = s0 + e;
+                out[e] = s2 < 16 ? to_f32(qr[s2 * LDK + c]) * ex2(G2[(s2 + 1) * DK + c])
+                                 : to_f32(kr[(s2 - 16) * LDK + c]) * ex2(G2[(s2 - 16) * DK + c]);
+            }
+            store8<MT>(qk + c * 32 + s0, out);
+        }
+    }
+    float* gam = reinterpret_cast<float*>(blk + OB::GAM);
+    for (int c = lane; c < DK; c += 64) gam[c] = ex2(G2[SC * DK + c]);
+    if (lane == 0) *reinterpret_cast<int*>(blk + OB::FLAG) = exact ? 1 : 0;
+}
+
+// ==================================================================== scan
+// Reverse walk of the state derivative for one (sequence, head, value slice).
+template <typename MT, int DK, int DVS>
+__global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV) {
+    typedef OpBlock<MT, DK> OB;
+    constexpr int P = 16 / (int)sizeof(MT);
+    constexpr int LDK = DK + P, L16 = 16 + P, L32 = 32 + P;
+    constexpr int PER = 16 / (int)sizeof(MT);
+    constexpr int NCB = DK / 16, NJB = DVS / 16, CBW = (NCB + 3) / 4;
+    constexpr int WALKP = OB::WALK / 16;          // 16-byte pieces of the walk's operators
+    constexpr int DOP = 16 * DVS / PER;           // 16-byte pieces of the dO slice
+    constexpr int NP = (WALKP + DOP + 255) / 256; // pieces per thread
+    __shared__ __attribute__((aligned(16))) MT Wl[2][16 * LDK];
+    __shared__ __attribute__((aligned(16))) MT Ml[2][16 * L16];
+    __shared__ __attribute__((aligned(16))) MT QKl[2][DK * L32];
+    __shared__ __attribute__((aligned(16))) float gl[2][DK];
+    __shared__ __attribute__((aligned(16))) MT DFT[2][DVS * L32];  // [j][dO^T (16) | F^T (16)]
+    __shared__ __attribute__((aligned(16))) MT XT[DVS * LDK];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t unit = blockIdx.y;
+    const int slice = blockIdx.x;
+    const int n = (int)(unit / p.H), h = (int)(unit % p.H);
+    const SeqSpan sq = seq_span(p.cu, p.eq_len, n);
+    const int nsub = ceil_div(sq.len, SC), nch = ceil_div(sq.len, CHB);
+    const int j0 = slice * DVS;
+    const int64_t sbase = ceil_blocks_before(p.cu, p.eq_len, n, SC) * p.H + (int64_t)h * nsub;
+    const int64_t cbase = ceil_blocks_before(p.cu, p.eq_len, n, CHB) * p.H + (int64_t)h * nch;
+    const int64_t st_off = unit * (int64_t)DK * DV + j0;  // this slice of [N, H, DK, DV]
+
+    f32x4 X[CBW][NJB];
+#pragma unroll
+    for (int a = 0; a < CBW; ++a)
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+            const int cb = w + 4 * a;
+            X[a][jb] = zero4();
+            if (cb < NCB && p.dST) X[a][jb] = load_state_tile(p.dST + st_off + (int64_t)cb * 16 * DV + jb * 16, DV, lane);
+        }
+
+    const MT* dO = static_cast<const MT*>(p.dO);
+    typedef typename V16<MT>::type VT;
+    VT pre[NP];
+    auto fetch = [&](int s) {
+        const uint8_t* blk = p.ops + (sbase + s) * OB::BYTES;
+        const int64_t t0 = sq.t0 + (int64_t)s * SC;
+        const int nrow = min(SC, sq.len - s * SC);
+#pragma unroll
+        for (int a = 0; a < NP; ++a) {
+            const int pc = tid + 256 * a;
+            VT x = {};
+            if (pc < WALKP) {
+                x = *reinterpret_cast<const VT*>(blk + 16 * pc);
+            } else if (pc < WALKP + DOP) {
+                const int q2 = pc - WALKP, i = q2 / (DVS / PER), e = (q2 % (DVS / PER)) * PER;
+                if (i < nrow) x = *reinterpret_cast<const VT*>(dO + ((t0 + i) * p.H + h) * (int64_t)DV + j0 + e);
+            }
+            pre[a] = x;
+        }
+    };
+    auto place = [&](int b) {
+#pragma unroll
+        for (int a = 0; a < NP; ++a) {
+            const int pc = tid + 256 * a;
+            const int off = 16 * pc;
+            if (pc < WALKP) {
+                if (off < OB::M) {
+                    const int row = off / (DK * (int)sizeof(MT)), col = (off % (DK * (int)sizeof(MT))) / (int)sizeof(MT);
+                    *reinterpret_cast<VT*>(&Wl[b][row * LDK + col]) = pre[a];
+                } else if (off < OB::QK) {
+                    const int o = (off - OB::M) / (int)sizeof(MT), row = o / 16, col = o % 16;
+                    *reinterpret_cast<VT*>(&Ml[b][row * L16 + col]) = pre[a];
+                } else if (off < OB::GAM) {
+                    const int o = (off - OB::QK) / (int)sizeof(MT), row = o / 32, col = o % 32;
+                    *reinterpret_cast<VT*>(&QKl[b][row * L32 + col]) = pre[a];
+                } else {
+                    // gamma is fp32 in the block whatever MT is
+                    *reinterpret_cast<f32x4*>(&gl[b][(off - OB::GAM) / 4]) = __builtin_bit_cast(f32x4, pre[a]);
+                }
+            } else if (pc < WALKP + DOP) {
+                const int q2 = pc - WALKP, i = q2 / (DVS / PER), e = (q2 % (DVS / PER)) * PER;
+#pragma unroll
+                for (int u = 0; u < PER; ++u) DFT[b][(e + u) * L32 + i] = pre[a][u];
+            }
+        }
+    };
+
+    if (nsub > 0) {
+        fetch(nsub - 1);
+        place((nsub - 1) & 1);
+    }
+    for (int s = nsub - 1; s >= 0; --s) {
+        const int b = s & 1;
+        // derivative at the end of a 64-token chunk
+        if (s % (CHB / SC) == CHB / SC - 1 || s == nsub - 1) {
+            float* dst = p.xbuf + (cbase + s / (CHB / SC)) * (int64_t)DK * DV + j0;
+#pragma unroll
+            for (int a = 0; a < CBW; ++a)
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) {
+                    const int cb = w + 4 * a;
+                    if (cb < NCB) store_state_tile(dst + (int64_t)cb * 16 * DV + jb * 16, DV, lane, X[a][jb]);
+                }
+        }
+#pragma unroll
+        for (int a = 0; a < CBW; ++a)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int cb = w + 4 * a;
+                if (cb < NCB) store_nat<MT>(XT + jb * 16 * LDK + cb * 16, LDK, X[a][jb], lane);
+            }
+        if (s > 0) fetch(s - 1);
+        __syncthreads();
+        // F = -(W X + M dO)   (m = t, n = j)
+        for (int jb = w; jb < NJB; jb += 4) {
+            f32x4 acc = mmak<MT, DK>(&Wl[b][(lane & 15) * LDK], XT + (jb * 16 + (lane & 15)) * LDK, zero4(), lane);
+            acc = mmak<MT, 16>(&Ml[b][(lane & 15) * L16], &DFT[b][(jb * 16 + (lane & 15)) * L32], acc, lane);
+            store_nat<MT>(&DFT[b][jb * 16 * L32 + 16], L32, -acc, lane);
+        }
+        __syncthreads();
+        // X <- gamma X + [Qb^T | Kb^T] [dO; F]   (m = c, n = j)
+#pragma unroll
+        for (int a = 0; a < CBW; ++a) {
+            const int cb = w + 4 * a;
+            if (cb < NCB) {
+                f32x4 gmm;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gmm[r] = gl[b][cb * 16 + 4 * (lane >> 4) + r];
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+                    X[a][jb] = mmak<MT, 32>(&QKl[b][(cb * 16 + (lane & 15)) * L32],
+                                            &DFT[b][(jb * 16 + (lane & 15)) * L32], gmm * X[a][jb], lane);
+            }
+        }
+        if (s > 0) place((s - 1) & 1);
+    }
+    if (p.dS0) {
+#pragma unroll
+        for (int a = 0; a < CBW; ++a)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int cb = w + 4 * a;
+                if (cb < NCB) store_state_tile(p.dS0 + st_off + (int64_t)cb * 16 * DV + jb * 16, DV, lane, X[a][jb]);
+            }
+    }
+}
+
+// ==================================================================== grad
+template <typename MT, int DK, int DV>
+struct GradSmem {
+    static constexpr int P = 16 / (int)sizeof(MT);
+    static constexpr int LDK = DK + P, LDV = DV + P, L16 = 16 + P, L32 = 32 + P;
+    static constexpr int DMX = DK > DV ? DK : DV;
+    static constexpr int LMX = (DK > DV ? DK : DV) + P;
+    MT kr[16 * LDK], qr[16 * LDK], vr[16 * LDV], dor[16 * LDV];
+    MT mats[7][16 * L16];
+    MT SB[DMX * LMX];         // S^T / X^T [j][c], or X / S row-major [c][j]
+    MT GA[16 * LDK], GB[16 * LDK];
+    MT CT[DK * L32];          // [Kcc^T | Ktc^T], [Qb^T | Kb^T], [Kc'^T | Kt'^T], [Qb'^T | Kb'^T]
+    MT EBVT[DV * L32];        // [E^T | (bV)^T]
+    MT DFT[DV * L32];         // [dO^T | F^T]
+    MT Y0T[DV * L16];         // Y0^T, then dE^T
+    MT Erm[16 * LDV], Yrm[16 * LDV], Grm[16 * LDV];
+    MT MQ[16 * L32], MG[16 * L32], MV[16 * L32], MY[16 * L32];
+    float G2[(SC + 1) * DK];
+    float bt[SC];
+    float phi0[DK];
+    float red[3][4][16];      // per-wave partials: R.V, G.Y, dlog_a (scalar gate)
+    int exact;
+};
+
+// The four masked products of a sub-chunk whose decay spans too much for the
+// factor split, one exponent per term: out[t][c] = sum_i M[t][i] y_ic e^{+-(h_tc - h'_ic)}
+// for this lane's rows t = 4 g4 + r and channel c.  Masked-out pairs hold 0;
+// clamping their exponents at 0 keeps them finite.
+template <typename MT, int DK, typename SM>
+__device__ __attribute__((noinline)) void exact_terms(const SM& sm, int c, int g4, f32x4& mq, f32x4& mg, f32x4& mv,
+                                                      f32x4& my) {
+    constexpr int LDK = SM::LDK, L32 = SM::L32;
+    for (int r = 0; r < 4; ++r) {
+        const int t = 4 * g4 + r;
+        float aq = 0.f, ag = 0.f, av = 0.f, ay = 0.f;
+        const float gmt = sm.G2[t * DK + c], gt = sm.G2[(t + 1) * DK + c];
+        for (int i = 0; i < 16; ++i) {
+            const float ki = to_f32(sm.kr[i * LDK + c]), qi = to_f32(sm.qr[i * LDK + c]);
+            const float gmi = sm.G2[i * DK + c], gi = sm.G2[(i + 1) * DK + c];
+            aq += to_f32(sm.MQ[t * L32 + i]) * ki * ex2n(gt - gmi) + to_f32(sm.MQ[t * L32 + 16 + i]) * ki * ex2n(gt - gi);
+            ag += to_f32(sm.MG[t * L32 + i]) * ki * ex2n(gmt - gmi) + to_f32(sm.MG[t * L32 + 16 + i]) * ki * ex2n(gmt - gi);
+            av += to_f32(sm.MV[t * L32 + i]) * qi * ex2n(gi - gt) + to_f32(sm.MV[t * L32 + 16 + i]) * ki * ex2n(gmi - gt);
+            ay += to_f32(sm.MY[t * L32 + i]) * qi * ex2n(gi - gmt) + to_f32(sm.MY[t * L32 + 16 + i]) * ki * ex2n(gmi - gmt);
+        }
+        mq[r] = aq; mg[r] = ag; mv[r] = av; my[r] = ay;
+    }
+}
+
+template <typename MT, int DK, int DV>
+__global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdParams p) {
+    typedef GradSmem<MT, DK, DV> SM;
+    typedef OpBlock<MT, DK> OB;
+    constexpr int LDK = SM::LDK, LDV = SM::LDV, L16 = SM::L16, L32 = SM::L32;
+    constexpr int NCB = DK / 16, NJB = DV / 16, CBW = (NCB + 3) / 4, JBW = (NJB + 3) / 4;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+    SM& sm = *reinterpret_cast<SM*>(smem_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int jc = blockIdx.x;
+    const int64_t unit = blockIdx.y;
+    const int n = (int)(unit / p.H), h = (int)(unit % p.H);
+    const SeqSpan sq = seq_span(p.cu, p.eq_len, n);
+    if (jc * CHB >= sq.len) return;
+    const int nsub = ceil_div(sq.len, SC), nch = ceil_div(sq.len, CHB);
+    const int clen = min(CHB, sq.len - jc * CHB);
+    const int ns = ceil_div(clen, SC);
+    const int64_t sbase = ceil_blocks_before(p.cu, p.eq_len, n, SC) * p.H + (int64_t)h * nsub + jc * (CHB / SC);
+    const int64_t xrow = ceil_blocks_before(p.cu, p.eq_len, n, CHB) * p.H + (int64_t)h * nch + jc;
+    // forward state at the chunk start: S0, or the kept state after jc chunks
+    const float* s_start = nullptr;
+    if (jc == 0) {
+        if (p.S0) s_start = p.S0 + unit * (int64_t)DK * DV;
+    } else {
+        int64_t before;
+        if (!p.cu) before = (int64_t)n * (p.eq_len / CHB);
+        else before = snapshots_before(p.cu, p.eq_len, n, CHB);
+        s_start = p.snap + ((before + jc - 1) * p.H + h) * (int64_t)DK * DV;
+    }
+    const MT* Kg = static_cast<const MT*>(p.k);
+    const MT* Qg = static_cast<const MT*>(p.q);
+    const MT* Vg = static_cast<const MT*>(p.v);
+    const MT* Og = static_cast<const MT*>(p.dO);
+
+    f32x4 S[CBW][NJB], X[CBW][NJB];
+    auto load_state = [&](f32x4 (&Z)[CBW][NJB], const float* src) {
+#pragma unroll
+        for (int a = 0; a < CBW; ++a)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int cb = w + 4 * a;
+                Z[a][jb] = zero4();
+                if (cb < NCB && src) Z[a][jb] = load_state_tile(src + (int64_t)cb * 16 * DV + jb * 16, DV, lane);
+            }
+    };
+    load_state(X, p.xbuf + xrow * (int64_t)DK * DV);
+
+    for (int sg = ns - 1; sg >= 0; --sg) {
+        load_state(S, s_start);
+        for (int sf = 0; sf <= sg; ++sf) {
+            const bool grad = sf == sg;
+            const int64_t t0 = sq.t0 + (int64_t)jc * CHB + sf * SC;
+            const int nrow = min(SC, clen - sf * SC);
+            const uint8_t* blk = p.ops + (sbase + sf) * OB::BYTES;
+            __syncthreads();
+            // ---- inputs of sub-chunk sf, S^T
+            load_rows<MT, DK>(sm.kr, LDK, Kg, t0, p.H, h, nrow, tid, 256);
+            load_rows<MT, DV>(sm.vr, LDV, Vg, t0, p.H, h, nrow, tid, 256);
+            if (grad) {
+                load_rows<MT, DK>(sm.qr, LDK, Qg, t0, p.H, h, nrow, tid, 256);
+                load_rows<MT, DV>(sm.dor, LDV, Og, t0, p.H, h, nrow, tid, 256);
+            }
+            load_decay<DK>(sm.G2, sm.bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, tid, 256);
+            {
+                constexpr int PER = 16 / (int)sizeof(MT);
+                const MT* mats = reinterpret_cast<const MT*>(blk + OB::MATS);
+                const int nm = grad ? 7 : 3;  // T diag(b), T^T, L first ... all when grading
+                for (int pc = tid; pc < 7 * 256 / PER; pc += 256) {
+                    const int mi = pc / (256 / PER), o = (pc % (256 / PER)) * PER;
+                    if (!grad && mi != MAT_TB && mi != MAT_L) continue;
+                    (void)nm;
+                    copy16<MT>(&sm.mats[mi][(o / 16) * L16 + o % 16], mats + mi * 256 + o);
+                }
+                if (grad && tid == 0) sm.exact = *reinterpret_cast<const int*>(blk + OB::FLAG);
+            }
+#pragma unroll
+            for (int a = 0; a < CBW; ++a)
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) {
+                    const int cb = w + 4 * a;
+                    if (cb < NCB) store_nat<MT>(sm.SB + jb * 16 * LDK + cb * 16, LDK, S[a][jb], lane);
+                }
+            __syncthreads();
+            // ---- Kb rows, (bV)^T, [Kcc^T | Ktc^T]
+            for (int x = tid; x < 16 * DK; x += 256) {
+                const int t = x / DK, c = x % DK;
+                sm.GA[t * LDK + c] = from_f32<MT>(to_f32(sm.kr[t * LDK + c]) * ex2(sm.G2[t * DK + c]));
+            }
+            for (int x = tid; x < 16 * DV; x += 256) {
+                const int i = x % 16, j = x / 16;
+                sm.EBVT[j * L32 + 16 + i] = from_f32<MT>(sm.bt[i] * to_f32(sm.vr[i * LDV + j]));
+            }
+            if (!grad) {
+                for (int x = tid; x < 16 * DK; x += 256) {
+                    const int s2 = x % 16, c = x / 16;
+                    const float kv = to_f32(sm.kr[s2 * LDK + c]), gc = sm.G2[SC * DK + c];
+                    sm.CT[c * L32 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[s2 * DK + c]));
+                    sm.CT[c * L32 + 16 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[(s2 + 1) * DK + c]));
+                }
+            }
+            __syncthreads();
+            // ---- Y0 = Kb S + L bV   (m = t, n = j)
+            f32x4 Y0[JBW];
+#pragma unroll
+            for (int a = 0; a < JBW; ++a) {
+                const int jb = w + 4 * a;
+                Y0[a] = zero4();
+                if (jb < NJB) {
+                    Y0[a] = mmak<MT, DK>(sm.GA + r16 * LDK, sm.SB + (jb * 16 + r16) * LDK, zero4(), lane);
+                    Y0[a] = mmak<MT, 16>(sm.mats[MAT_L] + r16 * L16, sm.EBVT + (jb * 16 + r16) * L32 + 16, Y0[a], lane);
+                    store_nat<MT>(sm.Y0T + jb * 16 * L16, L16, Y0[a], lane);
+                }
+            }
+            __syncthreads();
+            // ---- E = -T diag(b) Y0
+#pragma unroll
+            for (int a = 0; a < JBW; ++a) {
+                const int jb = w + 4 * a;
+                if (jb < NJB) {
+                    const f32x4 e = -mmak<MT, 16>(sm.mats[MAT_TB] + r16 * L16, sm.Y0T + (jb * 16 + r16) * L16, zero4(), lane);
+                    store_nat<MT>(sm.EBVT + jb * 16 * L32, L32, e, lane);
+                    if (grad) store_rm<MT>(sm.Erm + jb * 16, LDV, e, lane);
+                }
+            }
+            __syncthreads();
+            if (!grad) {
+                // ---- S <- gamma S + [Kcc^T | Ktc^T] [E; bV]
+#pragma unroll
+                for (int a = 0; a < CBW; ++a) {
+                    const int cb = w + 4 * a;
+                    if (cb < NCB) {
+                        f32x4 gmm;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) gmm[r] = ex2(sm.G2[SC * DK + cb * 16 + 4 * g4 + r]);
+#pragma unroll
+                        for (int jb = 0; jb < NJB; ++jb)
+                            S[a][jb] = mmak<MT, 32>(sm.CT + (cb * 16 + r16) * L32, sm.EBVT + (jb * 16 + r16) * L32,
+                                                    gmm * S[a][jb], lane);
+                    }
+                }
+                continue;
+            }
+
+            // ================= gradient of sub-chunk sg (start state S, end derivative X)
+            // ---- Y = Y0 + A0 E  (row-major); X^T; dO^T; Kcc, Ktc rows; [Qb^T | Kb^T]
+#pragma unroll
+            for (int a = 0; a < JBW; ++a) {
+                const int jb = w + 4 * a;
+                if (jb < NJB) {
+                    const f32x4 y = mmak<MT, 16>(sm.mats[MAT_A0] + r16 * L16, sm.EBVT + (jb * 16 + r16) * L32, Y0[a], lane);
+                    store_rm<MT>(sm.Yrm + jb * 16, LDV, y, lane);
+                }
+            }
+#pragma unroll
+            for (int a = 0; a < CBW; ++a)
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) {
+                    const int cb = w + 4 * a;
+                    if (cb < NCB) store_nat<MT>(sm.SB + jb * 16 * LDK + cb * 16, LDK, X[a][jb], lane);
+                }
+            for (int x = tid; x < 16 * DV; x += 256) {
+                const int i = x % 16, j = x / 16;
+                sm.DFT[j * L32 + i] = sm.dor[i * LDV + j];
+            }
+            for (int x = tid; x < 16 * DK; x += 256) {
+                const int t = x / DK, c = x % DK;
+                const float kv = to_f32(sm.kr[t * LDK + c]), gc = sm.G2[SC * DK + c];
+                sm.GA[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[t * DK + c]));
+                sm.GB[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[(t + 1) * DK + c]));
+            }
+            for (int x = tid; x < 16 * DK; x += 256) {
+                const int s2 = x % 16, c = x / 16;
+                sm.CT[c * L32 + s2] = from_f32<MT>(to_f32(sm.qr[s2 * LDK + c]) * ex2(sm.G2[(s2 + 1) * DK + c]));
+                sm.CT[c * L32 + 16 + s2] = from_f32<MT>(to_f32(sm.kr[s2 * LDK + c]) * ex2(sm.G2[s2 * DK + c]));
+            }
+            __syncthreads();
+            // ---- dE = Kcc X + P1^T dO  (m = t, n = j) -> dE^T
+#pragma unroll
+            for (int a = 0; a < JBW; ++a) {
+                const int jb = w + 4 * a;
+                if (jb < NJB) {
+                    f32x4 d = mmak<MT, DK>(sm.GA + r16 * LDK, sm.SB + (jb * 16 + r16) * LDK, zero4(), lane);
+                    d = mmak<MT, 16>(sm.mats[MAT_P1T] + r16 * L16, sm.DFT + (jb * 16 + r16) * L32, d, lane);
+                    store_nat<MT>(sm.Y0T + jb * 16 * L16, L16, d, lane);
+                }
+            }
+            __syncthreads();
+            // ---- G^T = dE^T T  (m = j, n = t): G row-major, F^T = -b G^T, partial G.Y
+            {
+                float gy[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int a = 0; a < JBW; ++a) {
+                    const int jb = w + 4 * a;
+                    if (jb < NJB) {
+                        const f32x4 gt = mmak<MT, 16>(sm.Y0T + (jb * 16 + r16) * L16, sm.mats[MAT_TT] + r16 * L16, zero4(), lane);
+                        store_nat<MT>(sm.Grm + jb * 16, LDV, gt, lane);
+                        const float bneg = -sm.bt[r16];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = jb * 16 + 4 * g4 + r;
+                            sm.DFT[j * L32 + 16 + r16] = from_f32<MT>(bneg * gt[r]);
+                            gy[0] += gt[r] * to_f32(sm.Yrm[r16 * LDV + j]);
+                        }
+                    }
+                }
+                float v0 = gy[0];
+                v0 += __shfl_xor(v0, 16);
+                v0 += __shfl_xor(v0, 32);
+                if (g4 == 0) sm.red[1][w][r16] = v0;
+            }
+            __syncthreads();
+            // ---- R = Ktc X + P2^T dO + L^T F  (m = t, n = j): dv, partial R.V
+            {
+                float rv[4] = {0.f, 0.f, 0.f, 0.f};
+                MT* dvg = static_cast<MT*>(p.dv);
+#pragma unroll
+                for (int a = 0; a < JBW; ++a) {
+                    const int jb = w + 4 * a;
+                    if (jb < NJB) {
+                        f32x4 rr = mmak<MT, DK>(sm.GB + r16 * LDK, sm.SB + (jb * 16 + r16) * LDK, zero4(), lane);
+                        rr = mmak<MT, 16>(sm.mats[MAT_P2T] + r16 * L16, sm.DFT + (jb * 16 + r16) * L32, rr, lane);
+                        rr = mmak<MT, 16>(sm.mats[MAT_LT] + r16 * L16, sm.DFT + (jb * 16 + r16) * L32 + 16, rr, lane);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int t = 4 * g4 + r, j = jb * 16 + r16;
+                            rv[r] += rr[r] * to_f32(sm.vr[t * LDV + j]);
+                            if (t < nrow) dvg[((t0 + t) * p.H + h) * (int64_t)DV + j] = from_f32<MT>(sm.bt[t] * rr[r]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) rv[r] = row_sum16(rv[r]);
+                if (r16 == 0)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm.red[0][w][4 * g4 + r] = rv[r];
+            }
+            __syncthreads();
+            // ---- X row-major; dbeta
+#pragma unroll
+            for (int a = 0; a < CBW; ++a)
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) {
+                    const int cb = w + 4 * a;
+                    if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, X[a][jb], lane);
+                }
+            if (tid < 16 && tid < nrow) {
+                const float db = sm.red[0][0][tid] + sm.red[0][1][tid] + sm.red[0][2][tid] + sm.red[0][3][tid] -
+                                 (sm.red[1][0][tid] + sm.red[1][1][tid] + sm.red[1][2][tid] + sm.red[1][3][tid]);
+                p.dbeta[(t0 + tid) * p.H + h] = db;
+            }
+            __syncthreads();
+            // ---- state parts with X: vds_s = V X^T, ayds_s = Y X^T  (m = t, n = c)
+            f32x4 vds[CBW], ayds[CBW], dqs[CBW], gss[CBW];
+#pragma unroll
+            for (int a = 0; a < CBW; ++a) {
+                const int cb = w + 4 * a;
+                vds[a] = ayds[a] = zero4();
+                if (cb < NCB) {
+                    vds[a] = mmak<MT, DV>(sm.vr + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
+                    ayds[a] = mmak<MT, DV>(sm.Yrm + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
+                }
+            }
+            // ---- the eight 16 x 16 products (m = i, n = t), stored row-major [t][i] with their masks
+            for (int mi = w; mi < 8; mi += 4) {
+                const MT *A, *B;
+                switch (mi) {
+                    case 0: A = sm.Erm; B = sm.dor; break;  // lower(dO E^T)
+                    case 1: A = sm.vr; B = sm.dor; break;   // lower(dO bV^T)
+                    case 2: A = sm.Erm; B = sm.Grm; break;  // strict_lower(G E^T)
+                    case 3: A = sm.vr; B = sm.Grm; break;   // strict_lower(G bV^T)
+                    case 4: A = sm.dor; B = sm.vr; break;   // upper(V dO^T)
+                    case 5: A = sm.Grm; B = sm.vr; break;   // strict_upper(V F^T)
+                    case 6: A = sm.dor; B = sm.Yrm; break;  // upper(Y dO^T)
+                    default: A = sm.Grm; B = sm.Yrm; break; // strict_upper(Y F^T)
+                }
+                f32x4 d = mmak<MT, DV>(A + r16 * LDV, B + r16 * LDV, zero4(), lane);
+                MT* dst = mi < 2 ? sm.MQ : mi < 4 ? sm.MG : mi < 6 ? sm.MV : sm.MY;
+                const int coff = (mi & 1) * 16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * g4 + r, t = r16;
+                    float x = d[r];
+                    if (mi == 1 || mi == 3) x *= sm.bt[i];
+                    if (mi == 5 || mi == 7) x *= -sm.bt[i];
+                    const bool keep = mi < 2 ? i <= t : mi < 4 ? i < t : (mi & 1) ? i > t : i >= t;
+                    dst[t * L32 + coff + i] = from_f32<MT>(keep ? x : 0.f);
+                }
+            }
+            // ---- X <- gamma X + [Qb^T | Kb^T] [dO; F]; phi_{-1} = rowsum(X_prev * S)
+#pragma unroll
+            for (int a = 0; a < CBW; ++a) {
+                const int cb = w + 4 * a;
+                if (cb < NCB) {
+                    f32x4 gmm;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) gmm[r] = ex2(sm.G2[SC * DK + cb * 16 + 4 * g4 + r]);
+                    f32x4 ph = zero4();
+#pragma unroll
+                    for (int jb = 0; jb < NJB; ++jb) {
+                        X[a][jb] = mmak<MT, 32>(sm.CT + (cb * 16 + r16) * L32, sm.DFT + (jb * 16 + r16) * L32,
+                                                gmm * X[a][jb], lane);
+                        ph += X[a][jb] * S[a][jb];
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ph[r] = row_sum16(ph[r]);
+                    if (r16 == 0)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) sm.phi0[cb * 16 + 4 * g4 + r] = ph[r];
+                }
+            }
+            __syncthreads();
+            // ---- S row-major; [Kc'^T | Kt'^T]
+#pragma unroll
+            for (int a = 0; a < CBW; ++a)
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) {
+                    const int cb = w + 4 * a;
+                    if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, S[a][jb], lane);
+                }
+            for (int x = tid; x < 16 * DK; x += 256) {
+                const int i = x % 16, c = x / 16;
+                const float kv = to_f32(sm.kr[i * LDK + c]), m2 = 0.5f * sm.G2[SC * DK + c];
+                sm.CT[c * L32 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[i * DK + c]));
+                sm.CT[c * L32 + 16 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[(i + 1) * DK + c]));
+            }
+            __syncthreads();
+            const bool exact = sm.exact != 0;
+            f32x4 mq[CBW], mg[CBW], mv[CBW], my[CBW];
+#pragma unroll
+            for (int a = 0; a < CBW; ++a) {
+                const int cb = w + 4 * a;
+                dqs[a] = gss[a] = mq[a] = mg[a] = zero4();
+                if (cb < NCB) {
+                    dqs[a] = mmak<MT, DV>(sm.dor + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
+                    gss[a] = mmak<MT, DV>(sm.Grm + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
+                    if (!exact) {
+                        mq[a] = mmak<MT, 32>(sm.MQ + r16 * L32, sm.CT + (cb * 16 + r16) * L32, zero4(), lane);
+                        mg[a] = mmak<MT, 32>(sm.MG + r16 * L32, sm.CT + (cb * 16 + r16) * L32, zero4(), lane);
+                    }
+                }
+            }
+            __syncthreads();
+            for (int x = tid; x < 16 * DK; x += 256) {
+                const int i = x % 16, c = x / 16;
+                const float m2 = 0.5f * sm.G2[SC * DK + c];
+                sm.CT[c * L32 + i] = from_f32<MT>(to_f32(sm.qr[i * LDK + c]) * ex2(sm.G2[(i + 1) * DK + c] - m2));
+                sm.CT[c * L32 + 16 + i] = from_f32<MT>(to_f32(sm.kr[i * LDK + c]) * ex2(sm.G2[i * DK + c] - m2));
+            }
+            __syncthreads();
+            // ---- masked products, combination, outputs  (m = t, n = c)
+            MT* dqg = static_cast<MT*>(p.dq);
+            MT* dkg = static_cast<MT*>(p.dk);
+            float dla_s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int a = 0; a < CBW; ++a) {
+                const int cb = w + 4 * a;
+                if (cb >= NCB) continue;
+                const int c = cb * 16 + r16;
+                if (!exact) {
+                    mv[a] = mmak<MT, 32>(sm.MV + r16 * L32, sm.CT + c * L32, zero4(), lane);
+                    my[a] = mmak<MT, 32>(sm.MY + r16 * L32, sm.CT + c * L32, zero4(), lane);
+                } else {
+                    exact_terms<MT, DK>(sm, c, g4, mq[a], mg[a], mv[a], my[a]);
+                }
+                const float gc = sm.G2[SC * DK + c], m2 = 0.5f * gc;
+                float av[4], au[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * g4 + r;
+                    const float gmt = sm.G2[t * DK + c], gt = sm.G2[(t + 1) * DK + c];
+                    const float fq = exact ? 1.f : ex2(gt - m2), fg = exact ? 1.f : ex2(gmt - m2);
+                    const float fv = exact ? 1.f : ex2(m2 - gt), fy = exact ? 1.f : ex2(m2 - gmt);
+                    const float dq = ex2(gt) * dqs[a][r] + fq * mq[a][r];
+                    const float gs = ex2(gmt) * gss[a][r] + fg * mg[a][r];
+                    const float vd = ex2(gc - gt) * vds[a][r] + fv * mv[a][r];
+                    const float ay = ex2(gc - gmt) * ayds[a][r] + fy * my[a][r];
+                    const float b = sm.bt[t];
+                    const float kt = to_f32(sm.kr[t * LDK + c]), qt = to_f32(sm.qr[t * LDK + c]);
+                    const float dk = b * (vd - ay - gs);
+                    av[r] = kt * dk + 2.f * b * kt * gs;
+                    au[r] = qt * dq;
+                    mv[a][r] = b * kt * vd;  // reuse: the b k vds term
+                    if (t < nrow) {
+                        dqg[((t0 + t) * p.H + h) * (int64_t)DK + c] = from_f32<MT>(dq);
+                        dkg[((t0 + t) * p.H + h) * (int64_t)DK + c] = from_f32<MT>(dk);
+                    }
+                }
+                // phi_t = phi_{-1} + sum_{j<=t} av_j - sum_{j<t} au_j, over the 16 tokens of column c
+                float ia[4], eu[4];
+                float sa = 0.f, su = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    eu[r] = su;
+                    sa += av[r]; su += au[r];
+                    ia[r] = sa;
+                }
+                // exclusive prefix over the four lane groups (t blocks of 4)
+                float pa = 0.f, pu = 0.f;
+                {
+                    const float a1 = __shfl(sa, (lane - 16) & 63), u1 = __shfl(su, (lane - 16) & 63);
+                    const float a2 = __shfl(sa, (lane - 32) & 63), u2 = __shfl(su, (lane - 32) & 63);
+                    const float a3 = __shfl(sa, (lane - 48) & 63), u3 = __shfl(su, (lane - 48) & 63);
+                    if (g4 >= 1) { pa += a1; pu += u1; }
+                    if (g4 >= 2) { pa += a2; pu += u2; }
+                    if (g4 >= 3) { pa += a3; pu += u3; }
+                }
+                const float ph0 = sm.phi0[c];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * g4 + r;
+                    const float dl = ph0 + pa + ia[r] - (pu + eu[r]) - mv[a][r];
+                    if (p.scalar) dla_s[r] += dl;
+                    else if (t < nrow) p.dla[((t0 + t) * p.H + h) * (int64_t)DK + c] = dl;
+                }
+            }
+            if (p.scalar) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dla_s[r] = row_sum16(dla_s[r]);
+                if (r16 == 0)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm.red[2][w][4 * g4 + r] = dla_s[r];
+                __syncthreads();
+                if (tid < 16 && tid < nrow)
+                    p.dla[(t0 + tid) * p.H + h] = sm.red[2][0][tid] + sm.red[2][1][tid] + sm.red[2][2][tid] + sm.red[2][3][tid];
+            }
+        }
+    }
+}
+
+template <typename MT, int DK>
+hipError_t ops_dispatch(const BwdParams& p, int64_t units, int nsub_max, hipStream_t st) {
+    hipLaunchKernelGGL((kda_bwd_ops_kernel<MT, DK>), dim3((unsigned)nsub_max, (unsigned)units), dim3(64), 0, st, p);
+    return hipGetLastError();
+}
+template <typename MT, int DK, int DVS>
+hipError_t scan_dispatch(const BwdParams& p, int64_t units, int dv, hipStream_t st) {
+    hipLaunchKernelGGL((kda_bwd_scan_kernel<MT, DK, DVS>), dim3((unsigned)(dv / DVS), (unsigned)units), dim3(256), 0,
+                       st, p, dv);
+    return hipGetLastError();
+}
+template <typename MT, int DK, int DV>
+hipError_t grad_dispatch(const BwdParams& p, int64_t units, int nch_max, hipStream_t st) {
+    const size_t sm = sizeof(GradSmem<MT, DK, DV>);
+    static_assert(sizeof(GradSmem<MT, DK, DV>) <= 160 * 1024, "gradient pass LDS");
+    auto kern = kda_bwd_grad_kernel<MT, DK, DV>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)sm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nch_max, (unsigned)units), dim3(256), sm, st, p);
+    return hipGetLastError();
+}
+
+template <typename MT, int DK, int DV>
+hipError_t run_all(const BwdLaunch& a, const BwdParams& p, hipStream_t st) {
+    hipError_t e = hipSuccess;
+    if (a.nsub_max > 0) e = ops_dispatch<MT, DK>(p, a.units, a.nsub_max, st);
+    if (e != hipSuccess) return e;
+    constexpr int DVS = DV >= 32 ? 32 : DV;
+    e = scan_dispatch<MT, DK, DVS>(p, a.units, DV, st);  // also writes dS0 of empty sequences
+    if (e != hipSuccess || a.nch_max == 0) return e;
+    return grad_dispatch<MT, DK, DV>(p, a.units, a.nch_max, st);
+}
+
+}  // namespace
+
+int bwd_block_bytes(int dtype, int dk) {
+    if (dtype == 1) {
+        if (dk == 32) return OpBlock<bf16, 32>::BYTES;
+        if (dk == 64) return OpBlock<bf16, 64>::BYTES;
+        if (dk == 128) return OpBlock<bf16, 128>::BYTES;
+    } else if (dtype == 0) {
+        if (dk == 16) return OpBlock<float, 16>::BYTES;
+        if (dk == 32) return OpBlock<float, 32>::BYTES;
+        if (dk == 64) return OpBlock<float, 64>::BYTES;
+    }
+    return 0;
+}
+
+bool bwd_supported(int dtype, int dk, int dv) {
+    if (dtype == 1) return (dk == 32 || dk == 64 || dk == 128) && (dv == 32 || dv == 64 || dv == 128) && dk == dv;
+    if (dtype == 0) return (dk == 16 || dk == 32 || dk == 64) && dk == dv;
+    return false;
+}
+
+hipError_t launch_bwd(const BwdLaunch& a, hipStream_t st) {
+    BwdParams p;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.log_a = a.log_a; p.beta = a.beta; p.S0 = a.S0;
+    p.cu = a.cu_seqlens; p.eq_len = a.eq_len; p.dO = a.dO; p.dST = a.dST;
+    p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dla = a.dlog_a; p.dbeta = a.dbeta; p.dS0 = a.dS0;
+    p.snap = a.snap; p.ops = static_cast<uint8_t*>(a.ops); p.xbuf = a.xbuf;
+    p.H = a.num_heads; p.scalar = a.scalar; p.split = 0;
+    if (a.dtype == 1) {
+        if (a.kdim == 128 && a.vdim == 128) return run_all<bf16, 128, 128>(a, p, st);
+        if (a.kdim == 64 && a.vdim == 64) return run_all<bf16, 64, 64>(a, p, st);
+        if (a.kdim == 32 && a.vdim == 32) return run_all<bf16, 32, 32>(a, p, st);
+    } else {
+        if (a.kdim == 64 && a.vdim == 64) return run_all<float, 64, 64>(a, p, st);
+        if (a.kdim == 32 && a.vdim == 32) return run_all<float, 32, 32>(a, p, st);
+        if (a.kdim == 16 && a.vdim == 16) return run_all<float, 16, 16>(a, p, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -89,4 +89,35 @@ hipError_t launch_prep2(const PrepLaunch& a, hipStream_t stream);  // dk = 128, 
 bool two_pass_supported(int dtype, int dk, int dvs, int chunk);
 hipError_t launch_scan(const ScanLaunch& a, hipStream_t stream);
 
+// Backward of the prefill (erase-first order): three kernels after a forward
+// prefill that kept the state at every 64th token of each sequence.
+struct BwdLaunch {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_a;
+    const float* beta;
+    const float* S0;            // may be null (zero initial states)
+    const int32_t* cu_seqlens;  // device; may be null (equal lengths eq_len)
+    int64_t eq_len;
+    const void* dO;
+    const float* dST;           // may be null (zero)
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dlog_a;
+    float* dbeta;
+    float* dS0;                 // may be null (not written)
+    const float* snap;          // forward states, one row per 64 tokens of each sequence
+    void* ops;                  // operator blocks, bwd_block_bytes each
+    float* xbuf;                // derivatives at chunk ends, [chunks][dk][dv]
+    int32_t num_heads;
+    int64_t units;
+    int32_t nsub_max, nch_max;  // 16- and 64-token pieces of the longest sequence
+    int32_t kdim, vdim, dtype, scalar;
+};
+int bwd_block_bytes(int dtype, int dk);
+bool bwd_supported(int dtype, int dk, int dv);
+hipError_t launch_bwd(const BwdLaunch& a, hipStream_t stream);
+
 }  // namespace kda

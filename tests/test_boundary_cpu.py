@@ -242,3 +242,60 @@ def test_binding_prologue_fields():
     assert (p.normalize_k, p.beta_logits, p.log_a_raw, p.log_a_min) == (1, 0, 1, float("-inf"))
     with pytest.raises(ValueError):
         kda._prologue(dict(normalise_k=True))
+
+
+# ---- kda_chunk_bwd: argument checks (nothing is launched) ----
+def bwd_ws(lib, d):
+    need = ctypes.c_size_t(0)
+    st = lib.kda_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(need))
+    return st, need.value
+
+
+def backward(lib, d, ws_bytes=None, **ptrs):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    names = ["q", "k", "v", "la", "beta", "S0", "cu", "dO", "dST", "dq", "dk", "dv", "dla", "dbeta", "dS0", "ws"]
+    vals = {n: GOOD for n in names}
+    vals.update(S0=None, dST=None, dS0=None)
+    vals.update(ptrs)
+    if ws_bytes is None:
+        st, ws_bytes = bwd_ws(lib, d)
+        assert st == OK
+    return lib.kda_chunk_bwd(ctypes.byref(d), *[P(vals[n]) for n in names[:-1]], P(vals["ws"]),
+                             ctypes.c_size_t(ws_bytes), None)
+
+
+def test_bwd_workspace_size(lib):
+    st, b128 = bwd_ws(lib, dims(total_tokens=4096, num_seqs=2, max_seqlen=2048))
+    assert st == OK and b128 > 0
+    # grows with the tokens: kept states every 64 tokens, blocks every 16, derivatives every 64
+    st, b256 = bwd_ws(lib, dims(total_tokens=8192, num_seqs=2, max_seqlen=4096))
+    assert st == OK and b256 > 1.9 * b128 - (1 << 30)
+    assert bwd_ws(lib, dims(order=1))[0] == UNSUPPORTED               # decay-first, per-channel
+    assert bwd_ws(lib, dims(order=1, scalar_decay=1))[0] == OK       # one map with a scalar gate
+    assert bwd_ws(lib, dims(dk=128, dv=64))[0] == UNSUPPORTED
+    assert bwd_ws(lib, dims(dk=16, dv=16))[0] == UNSUPPORTED          # bf16 needs dk >= 32
+    assert bwd_ws(lib, dims(dk=16, dv=16, qkv_dtype=0))[0] == OK
+    assert bwd_ws(lib, dims(dk=128, dv=128, qkv_dtype=0))[0] == UNSUPPORTED
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(ws_bytes=1024), INVALID),                 # workspace too small
+    (dict(ws=None), INVALID),
+    (dict(ws=GOOD + 16), MISALIGNED),               # 256-byte alignment
+    (dict(dO=None), INVALID),
+    (dict(dq=None), INVALID),
+    (dict(dbeta=None), INVALID),
+    (dict(dla=GOOD + 4), MISALIGNED),               # per-channel dlog_a is read in 16-byte pieces
+    (dict(dST=GOOD + 8), MISALIGNED),
+    (dict(dS0=GOOD + 8), MISALIGNED),
+    (dict(q=GOOD + 2), MISALIGNED),
+])
+def test_bwd_validation(lib, case, expect):
+    d = dims()
+    assert backward(lib, d, **case) == expect
+
+
+def test_bwd_refuses_unsupported_shapes(lib):
+    assert backward(lib, dims(order=1), ws_bytes=1 << 20) == UNSUPPORTED
+    assert "erase-first" in lib.kda_last_error().decode()
+    assert backward(lib, dims(dk=64, dv=128), ws_bytes=1 << 20) == UNSUPPORTED
