@@ -10,7 +10,8 @@ synthetic tensors, resident on the GPU before timing starts.  The same
 prefill batch is also timed with state snapshots every 1024 tokens, with the
 decay-first ordering, and from raw inputs through the input prologue (against
 torch transforming them first), and the decode leg with the decay-first
-ordering ("variants", "decode.decay_first").
+ordering ("variants", "decode.decay_first").  The gradient of the same prefill
+(kda_chunk_bwd, for seeded upstream derivatives) is timed as "backward".
 
 Timing uses HIP events recorded on the stream the kernels are launched on
 (torch's current stream, which the library receives).  The fp64 CPU oracle is
@@ -73,6 +74,20 @@ def prefill_algorithmic(w, chunk_alg=64):
     C, dk, dv = chunk_alg, w.dk, w.dv
     per_chunk = 10 * C * C * dk + 6 * C * C * dv + 8 * C * dk * dv + (2.0 / 3.0) * C ** 3
     return th * per_th + states, th * per_chunk / C
+
+
+def backward_algorithmic(w, chunk_alg=64):
+    """Algorithmic bytes and flops of one gradient call.  Bytes per token-head:
+    q, k, v and dO read in bf16, log_a and beta read in fp32; dq, dk, dv written
+    in bf16, dlog_a and dbeta in fp32; per (sequence, head) S0 and dS_T read and
+    dS0 written (fp32).  Flops: twice the prefill's (reverse mode runs two
+    products of the same size for every product of the chunk form), plus once
+    the prefill's for recovering the forward states."""
+    th = w.n_seqs * w.seqlen * w.heads
+    per_th = 2 * (2 * w.dk + 2 * w.dv) + 4 * w.dk + 4 + 2 * (2 * w.dk + w.dv) + 4 * w.dk + 4
+    states = w.n_seqs * w.heads * 3 * 4 * w.dk * w.dv
+    _, F = prefill_algorithmic(w, chunk_alg)
+    return th * per_th + states, 3.0 * F
 
 
 def decode_algorithmic(w):
@@ -181,6 +196,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the snapshot and decay-first legs")
+    ap.add_argument("--no-backward", action="store_true", help="skip the gradient leg")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
     ap.add_argument("--method", choices=["auto", "single", "two-pass"], default="auto")
@@ -358,6 +374,52 @@ def main():
             log(f"prefill with snapshots every {every}: {ts*1e3:.3f} ms; decay-first: {t1*1e3:.3f} ms, "
                 f"parity {perr1:.2e}; prologue fused {tp*1e3:.3f} ms vs torch first {tt*1e3:.3f} ms")
 
+        if not args.no_backward:
+            # gradient of the same prefill for seeded upstream derivatives dO, dS_T
+            g = torch.Generator(device=dev)
+            g.manual_seed(5)
+            dO = torch.randn(o.shape, generator=g, device=dev).to(wp.dtype)
+            dST = torch.randn(ST.shape, generator=g, device=dev)
+            wsbb = kda.chunk_bwd_workspace_size(x["q"], x["v"], num_seqs=wp.n_seqs, method=method,
+                                                max_seqlen=wp.seqlen)
+            wsB = torch.empty(wsbb, dtype=torch.uint8, device=dev)
+
+            def bwd_step():
+                return kda.chunk_bwd(x["q"], x["k"], x["v"], x["log_a"], x["beta"], dO, S0=x["S0"],
+                                     cu_seqlens=x["cu_seqlens"], dS_T=dST, method=method, workspace=wsB,
+                                     max_seqlen=wp.seqlen)
+            for _ in range(max(args.warmup, 3)):
+                bwd_step()
+            torch.cuda.synchronize()
+            log("backward timed")
+            tb = time_events(bwd_step, args.steps, stream) / args.steps
+            # the prefill rerun alone (states kept every 64 tokens), to split the call
+            snaps64 = torch.empty((tokens // 64, wp.heads, wp.dk, wp.dv), dtype=torch.float32, device=dev)
+
+            def rerun_step():
+                kda.chunk_fwd_snapshots(x["q"], x["k"], x["v"], x["log_a"], x["beta"], S0=x["S0"],
+                                        cu_seqlens=x["cu_seqlens"], snapshot_every=64, snapshots=snaps64,
+                                        out=o, final_state=False, method=method, workspace=ws,
+                                        max_seqlen=wp.seqlen)
+            for _ in range(max(args.warmup, 3)):
+                rerun_step()
+            torch.cuda.synchronize()
+            tr = time_events(rerun_step, args.steps, stream) / args.steps
+            del snaps64, wsB
+            Bb, Fb = backward_algorithmic(wp)
+            out["backward"] = {
+                "ms_per_step": tb * 1e3, "tokens_per_s": tokens / tb,
+                "prefill_rerun_ms": tr * 1e3, "gradient_kernels_ms": (tb - tr) * 1e3,
+                "algorithmic_bytes": Bb, "algorithmic_GBps": Bb / tb / 1e9, "frac_hbm": Bb / tb / 1e9 / PEAK_HBM_GBS,
+                "algorithmic_tflop": Fb / 1e12, "achieved_tflops": Fb / tb / 1e12,
+                "pct_bf16_peak": 100.0 * Fb / tb / 1e12 / PEAK_BF16_TFLOPS,
+                "workspace_MiB": round(wsbb / 2**20, 1),
+                "kernels": "prefill rerun (kda_prep2_kernel + kda_scan_kernel, states every 64 tokens) + "
+                           "kda_bwd_ops_kernel + kda_bwd_scan_kernel + kda_bwd_grad_kernel",
+            }
+            log(f"backward: {tb*1e3:.3f} ms/step ({tokens/tb/1e6:.2f} Mtok/s), prefill rerun {tr*1e3:.3f} ms, "
+                f"gradient kernels {(tb-tr)*1e3:.3f} ms")
+
         if not args.no_cpu_baseline:
             ncpu = min(16, os.cpu_count() or 1)
             log(f"cpu oracle on the whole prefill batch, {ncpu} threads")
@@ -373,6 +435,35 @@ def main():
                 "gpu_speedup": (tokens / per) / (tokens / dt),
             }
             log(f"cpu oracle: {tokens/dt:.0f} tokens/s ({dt:.1f} s)")
+            if not args.no_backward:
+                # the oracle's gradient on a bounded sample: the first 2048 tokens of both
+                # sequences, all heads, and the GPU gradient of the same sample beside it
+                from oracle import kda_oracle_bwd
+                ns = 2048
+                idx = torch.cat([torch.arange(n * wp.seqlen, n * wp.seqlen + ns) for n in range(wp.n_seqs)]).to(dev)
+                cus = torch.arange(0, (wp.n_seqs + 1) * ns, ns, dtype=torch.int32, device=dev)
+                sx = {k: x[k].index_select(0, idx).contiguous() for k in ("q", "k", "v", "log_a", "beta")}
+                sdO = dO.index_select(0, idx).contiguous()
+                hs = {k: v_.cpu() for k, v_ in sx.items()}
+                t0 = time.perf_counter()
+                ref = kda_oracle_bwd(hs["q"], hs["k"], hs["v"], hs["log_a"], hs["beta"], S0=x["S0"].cpu(),
+                                     cu_seqlens=cus.cpu().numpy(), dO=sdO.cpu(), dST=dST.cpu(), threads=ncpu)
+                dtb = time.perf_counter() - t0
+                gg = kda.chunk_bwd(sx["q"], sx["k"], sx["v"], sx["log_a"], sx["beta"], sdO, S0=x["S0"],
+                                   cu_seqlens=cus, dS_T=dST, max_seqlen=ns)
+                torch.cuda.synchronize()
+                berr = {n_: float(np.abs(gg[n_].double().cpu().numpy() - ref[n_]).max() / np.abs(ref[n_]).max())
+                        for n_ in ref}
+                out["backward"]["parity"] = {"max_rel_err": berr, "tol": 2e-2,
+                                             "sample": f"first {ns} tokens of each sequence, all heads"}
+                out["backward"]["cpu_baseline"] = {
+                    "value": wp.n_seqs * ns / dtb, "unit": "tokens/s", "cores": ncpu, "kind": "oracle",
+                    "sample": f"gradient of the first {ns} tokens of each sequence, all {wp.heads} heads, "
+                              f"fp64 token-by-token with replay, {dtb:.1f} s",
+                    "gpu_speedup": (tokens / tb) / (wp.n_seqs * ns / dtb)}
+                log(f"cpu oracle gradient: {wp.n_seqs * ns / dtb:.0f} tokens/s ({dtb:.1f} s); "
+                    f"gpu sample parity {max(berr.values()):.2e}")
+                del dO, dST
         del x, o, ST
         torch.cuda.empty_cache()
 
