@@ -356,10 +356,11 @@ int kda_chunk_fwd_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const 
 
 namespace {
 // Backward workspace: [prefill's two-pass workspace][o scratch][states every 64
-// tokens][operator blocks per 16 tokens][state derivatives per 64-token chunk].
+// tokens][operator blocks per 16 tokens][state derivatives per 64-token chunk]
+// [per chunk: start state, E and Y of each 16-token piece, kept by the gradient pass].
 struct BwdPlan {
     Plan fwd;
-    size_t fwd_ws = 0, o_bytes = 0, snap_bytes = 0, ops_bytes = 0, x_bytes = 0, total = 0;
+    size_t fwd_ws = 0, o_bytes = 0, snap_bytes = 0, ops_bytes = 0, x_bytes = 0, scr_bytes = 0, total = 0;
     int64_t snap_rows = 0, maxlen = 0;
 };
 
@@ -378,7 +379,8 @@ int plan_bwd(const kda_dims_t* d, bool have_cu, BwdPlan* bp) {
     bp->snap_bytes = round256((size_t)bp->snap_rows * H * state);
     bp->ops_bytes = round256((size_t)(T / 16 + N) * H * kda::bwd_block_bytes(d->qkv_dtype, d->dk));
     bp->x_bytes = round256((size_t)(T / 64 + N) * H * state);
-    bp->total = round256(bp->fwd_ws) + bp->o_bytes + bp->snap_bytes + bp->ops_bytes + bp->x_bytes;
+    bp->scr_bytes = round256((size_t)(T / 64 + N) * H * (size_t)kda::bwd_scratch_bytes(d->qkv_dtype, d->dk, d->dv));
+    bp->total = round256(bp->fwd_ws) + bp->o_bytes + bp->snap_bytes + bp->ops_bytes + bp->x_bytes + bp->scr_bytes;
     bp->maxlen = N > 0 ? bp->fwd.max_chunks * bp->fwd.chunk : 0;
     return KDA_OK;
 }
@@ -474,6 +476,8 @@ int kda_chunk_bwd(const kda_dims_t* d, const void* q, const void* k, const void*
     void* ops = ws + off;
     off += bp.ops_bytes;
     float* xbuf = reinterpret_cast<float*>(ws + off);
+    off += bp.x_bytes;
+    void* scr = ws + off;
 
     // the prefill again, keeping the state at every 64th token (nothing to keep
     // when no sequence reaches 64 tokens)
@@ -489,7 +493,7 @@ int kda_chunk_bwd(const kda_dims_t* d, const void* q, const void* k, const void*
     a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.beta = beta; a.S0 = S0;
     a.cu_seqlens = cu_seqlens; a.eq_len = cu_seqlens ? 0 : d->total_tokens / d->num_seqs;
     a.dO = dO; a.dST = dS_T; a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_a = dlog_a; a.dbeta = dbeta; a.dS0 = dS0;
-    a.snap = snap; a.ops = ops; a.xbuf = xbuf;
+    a.snap = snap; a.ops = ops; a.xbuf = xbuf; a.scr = scr;
     a.num_heads = d->num_heads; a.units = units; a.nsub_max = (int32_t)nsub_max; a.nch_max = (int32_t)nch_max;
     a.kdim = d->dk; a.vdim = d->dv; a.dtype = d->qkv_dtype; a.scalar = d->scalar_decay;
     hipError_t e = kda::launch_bwd(a, (hipStream_t)stream);

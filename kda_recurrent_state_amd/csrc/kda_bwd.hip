@@ -42,6 +42,7 @@ namespace kda {
 namespace {
 
 constexpr int SC = 16;                   // sub-chunk tokens
+constexpr int GW = 8;                    // wavefronts of a gradient-pass workgroup
 constexpr int CHB = 64;                  // tokens between kept states
 constexpr float SPAN2_MAX = 160.f * LOG2E;
 
@@ -183,6 +184,7 @@ struct BwdParams {
     const float* snap;       // forward states, row per 64 tokens of each sequence
     uint8_t* ops;            // operator blocks
     float* xbuf;             // state derivatives at 64-token chunk ends
+    void* scr;               // per chunk: start state, E and Y of its sub-chunks
     int32_t H;
     int32_t scalar;
     int32_t split;
@@ -203,22 +205,37 @@ __device__ __forceinline__ void load_rows(MT* z, int ld, const MT* g, int64_t t0
     }
 }
 
-// G2[i][c] = log2 e * sum_{j < i} log a_j (i = 0..16), beta, and the reference m2 = G2[16] / 2.
+// G2[i][c] = log2 e * sum_{j < i} log a_j (i = 0..16) and beta.  The decays of the 16
+// tokens arrive in one round of 16-byte loads into G2's rows 1..16, then each
+// channel's prefix sum runs in LDS.  Contains a barrier: every thread calls it.
 template <int DK>
 __device__ __forceinline__ void load_decay(float* G2, float* bt, const float* la, const float* beta, int64_t t0,
                                            int H, int h, int nrow, int scalar, int tid, int nthr) {
+    constexpr int Q = DK / 4;  // 16-byte pieces per token
+    for (int p = tid; p < SC * Q; p += nthr) {
+        const int i = p / Q, c4 = (p % Q) * 4;
+        f32x4 x = zero4();
+        if (i < nrow) {
+            if (scalar) {
+                const float a = la[(t0 + i) * H + h];
+                x = f32x4{a, a, a, a};
+            } else {
+                x = *reinterpret_cast<const f32x4*>(la + ((t0 + i) * H + h) * (int64_t)DK + c4);
+            }
+        }
+        *reinterpret_cast<f32x4*>(G2 + (i + 1) * DK + c4) = x * LOG2E;
+    }
+    for (int i = tid; i < SC; i += nthr) bt[i] = i < nrow ? beta[(t0 + i) * H + h] : 0.f;
+    __syncthreads();
     for (int c = tid; c < DK; c += nthr) {
         float s = 0.f;
         G2[c] = 0.f;
-#pragma unroll 4
-        for (int i = 0; i < SC; ++i) {
-            float x = 0.f;
-            if (i < nrow) x = scalar ? la[(t0 + i) * H + h] : la[((t0 + i) * H + h) * (int64_t)DK + c];
-            s += x * LOG2E;
-            G2[(i + 1) * DK + c] = s;
+#pragma unroll
+        for (int i = 1; i <= SC; ++i) {
+            s += G2[i * DK + c];
+            G2[i * DK + c] = s;
         }
     }
-    for (int i = tid; i < SC; i += nthr) bt[i] = i < nrow ? beta[(t0 + i) * H + h] : 0.f;
 }
 
 // ===================================================================== ops
@@ -233,7 +250,7 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) MT KCT[DK * L16];
     __shared__ __attribute__((aligned(16))) MT P1rm[16 * L16];
     __shared__ __attribute__((aligned(16))) MT bTT[16 * L16];
-    __shared__ float G2[(SC + 1) * DK];
+    __shared__ __attribute__((aligned(16))) float G2[(SC + 1) * DK];
     __shared__ float bt[SC];
     __shared__ float Gf[4][16][17];  // A0, L, P1, P2 (fp32, row-major, masked)
     __shared__ float Tf[16][17];
@@ -573,7 +590,7 @@ struct GradSmem {
     float G2[(SC + 1) * DK];
     float bt[SC];
     float phi0[DK];
-    float red[3][4][16];      // per-wave partials: R.V, G.Y, dlog_a (scalar gate)
+    float red[3][GW][16];     // per-wave partials: R.V, G.Y, dlog_a (scalar gate)
     int exact;
 };
 
@@ -602,11 +619,13 @@ __device__ __attribute__((noinline)) void exact_terms(const SM& sm, int c, int g
 }
 
 template <typename MT, int DK, int DV>
-__global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
     typedef GradSmem<MT, DK, DV> SM;
     typedef OpBlock<MT, DK> OB;
     constexpr int LDK = SM::LDK, LDV = SM::LDV, L16 = SM::L16, L32 = SM::L32;
-    constexpr int NCB = DK / 16, NJB = DV / 16, CBW = (NCB + 3) / 4, JBW = (NJB + 3) / 4;
+    constexpr int NCB = DK / 16, NJB = DV / 16, CBW = (NCB + GW - 1) / GW, JBW = (NJB + GW - 1) / GW;
+    constexpr int NT = 64 * GW;
+    constexpr int SUBE = DK * DV + 2 * 16 * DV;  // kept per sub-chunk: start state, E, Y (elements of MT)
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
@@ -636,67 +655,68 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdParams p) {
     const MT* Qg = static_cast<const MT*>(p.q);
     const MT* Vg = static_cast<const MT*>(p.v);
     const MT* Og = static_cast<const MT*>(p.dO);
+    // this chunk's scratch: per sub-chunk its start state, E and Y, each tile as the
+    // owning lanes hold it (4 consecutive values per lane)
+    MT* scr = static_cast<MT*>(p.scr) + xrow * (int64_t)(CHB / SC) * SUBE;
+    auto kS = [&](int s2, int cb, int jb) { return scr + (int64_t)s2 * SUBE + ((cb * NJB + jb) * 64 + lane) * 4; };
+    auto kE = [&](int s2, int jb) { return scr + (int64_t)s2 * SUBE + DK * DV + (jb * 64 + lane) * 4; };
+    auto kY = [&](int s2, int jb) { return scr + (int64_t)s2 * SUBE + DK * DV + 16 * DV + (jb * 64 + lane) * 4; };
 
-    f32x4 S[CBW][NJB], X[CBW][NJB];
     auto load_state = [&](f32x4 (&Z)[CBW][NJB], const float* src) {
 #pragma unroll
         for (int a = 0; a < CBW; ++a)
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb) {
-                const int cb = w + 4 * a;
+                const int cb = w + GW * a;
                 Z[a][jb] = zero4();
                 if (cb < NCB && src) Z[a][jb] = load_state_tile(src + (int64_t)cb * 16 * DV + jb * 16, DV, lane);
             }
     };
-    load_state(X, p.xbuf + xrow * (int64_t)DK * DV);
+    auto load_mats = [&](const uint8_t* blk, unsigned mask) {
+        constexpr int PER = 16 / (int)sizeof(MT);
+        const MT* mats = reinterpret_cast<const MT*>(blk + OB::MATS);
+        for (int pc = tid; pc < 7 * 256 / PER; pc += NT) {
+            const int mi = pc / (256 / PER), o = (pc % (256 / PER)) * PER;
+            if (mask >> mi & 1u) copy16<MT>(&sm.mats[mi][(o / 16) * L16 + o % 16], mats + mi * 256 + o);
+        }
+    };
 
-    for (int sg = ns - 1; sg >= 0; --sg) {
+    // ================= forward walk: start state, E and Y of every sub-chunk
+    {
+        f32x4 S[CBW][NJB];
         load_state(S, s_start);
-        for (int sf = 0; sf <= sg; ++sf) {
-            const bool grad = sf == sg;
+        for (int sf = 0; sf < ns; ++sf) {
             const int64_t t0 = sq.t0 + (int64_t)jc * CHB + sf * SC;
             const int nrow = min(SC, clen - sf * SC);
             const uint8_t* blk = p.ops + (sbase + sf) * OB::BYTES;
+            const bool last = sf == ns - 1;
             __syncthreads();
-            // ---- inputs of sub-chunk sf, S^T
-            load_rows<MT, DK>(sm.kr, LDK, Kg, t0, p.H, h, nrow, tid, 256);
-            load_rows<MT, DV>(sm.vr, LDV, Vg, t0, p.H, h, nrow, tid, 256);
-            if (grad) {
-                load_rows<MT, DK>(sm.qr, LDK, Qg, t0, p.H, h, nrow, tid, 256);
-                load_rows<MT, DV>(sm.dor, LDV, Og, t0, p.H, h, nrow, tid, 256);
-            }
-            load_decay<DK>(sm.G2, sm.bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, tid, 256);
-            {
-                constexpr int PER = 16 / (int)sizeof(MT);
-                const MT* mats = reinterpret_cast<const MT*>(blk + OB::MATS);
-                const int nm = grad ? 7 : 3;  // T diag(b), T^T, L first ... all when grading
-                for (int pc = tid; pc < 7 * 256 / PER; pc += 256) {
-                    const int mi = pc / (256 / PER), o = (pc % (256 / PER)) * PER;
-                    if (!grad && mi != MAT_TB && mi != MAT_L) continue;
-                    (void)nm;
-                    copy16<MT>(&sm.mats[mi][(o / 16) * L16 + o % 16], mats + mi * 256 + o);
-                }
-                if (grad && tid == 0) sm.exact = *reinterpret_cast<const int*>(blk + OB::FLAG);
-            }
+            load_rows<MT, DK>(sm.kr, LDK, Kg, t0, p.H, h, nrow, tid, NT);
+            load_rows<MT, DV>(sm.vr, LDV, Vg, t0, p.H, h, nrow, tid, NT);
+            load_decay<DK>(sm.G2, sm.bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, tid, NT);
+            load_mats(blk, 1u << MAT_TB | 1u << MAT_L | 1u << MAT_A0);
 #pragma unroll
             for (int a = 0; a < CBW; ++a)
 #pragma unroll
                 for (int jb = 0; jb < NJB; ++jb) {
-                    const int cb = w + 4 * a;
-                    if (cb < NCB) store_nat<MT>(sm.SB + jb * 16 * LDK + cb * 16, LDK, S[a][jb], lane);
+                    const int cb = w + GW * a;
+                    if (cb < NCB) {
+                        store_nat<MT>(sm.SB + jb * 16 * LDK + cb * 16, LDK, S[a][jb], lane);
+                        store4<MT>(kS(sf, cb, jb), S[a][jb]);
+                    }
                 }
             __syncthreads();
             // ---- Kb rows, (bV)^T, [Kcc^T | Ktc^T]
-            for (int x = tid; x < 16 * DK; x += 256) {
+            for (int x = tid; x < 16 * DK; x += NT) {
                 const int t = x / DK, c = x % DK;
                 sm.GA[t * LDK + c] = from_f32<MT>(to_f32(sm.kr[t * LDK + c]) * ex2(sm.G2[t * DK + c]));
             }
-            for (int x = tid; x < 16 * DV; x += 256) {
+            for (int x = tid; x < 16 * DV; x += NT) {
                 const int i = x % 16, j = x / 16;
                 sm.EBVT[j * L32 + 16 + i] = from_f32<MT>(sm.bt[i] * to_f32(sm.vr[i * LDV + j]));
             }
-            if (!grad) {
-                for (int x = tid; x < 16 * DK; x += 256) {
+            if (!last) {
+                for (int x = tid; x < 16 * DK; x += NT) {
                     const int s2 = x % 16, c = x / 16;
                     const float kv = to_f32(sm.kr[s2 * LDK + c]), gc = sm.G2[SC * DK + c];
                     sm.CT[c * L32 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[s2 * DK + c]));
@@ -708,7 +728,7 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdParams p) {
             f32x4 Y0[JBW];
 #pragma unroll
             for (int a = 0; a < JBW; ++a) {
-                const int jb = w + 4 * a;
+                const int jb = w + GW * a;
                 Y0[a] = zero4();
                 if (jb < NJB) {
                     Y0[a] = mmak<MT, DK>(sm.GA + r16 * LDK, sm.SB + (jb * 16 + r16) * LDK, zero4(), lane);
@@ -720,19 +740,26 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdParams p) {
             // ---- E = -T diag(b) Y0
 #pragma unroll
             for (int a = 0; a < JBW; ++a) {
-                const int jb = w + 4 * a;
+                const int jb = w + GW * a;
                 if (jb < NJB) {
                     const f32x4 e = -mmak<MT, 16>(sm.mats[MAT_TB] + r16 * L16, sm.Y0T + (jb * 16 + r16) * L16, zero4(), lane);
                     store_nat<MT>(sm.EBVT + jb * 16 * L32, L32, e, lane);
-                    if (grad) store_rm<MT>(sm.Erm + jb * 16, LDV, e, lane);
+                    store4<MT>(kE(sf, jb), e);
                 }
             }
             __syncthreads();
-            if (!grad) {
-                // ---- S <- gamma S + [Kcc^T | Ktc^T] [E; bV]
+            // ---- Y = Y0 + A0 E; S <- gamma S + [Kcc^T | Ktc^T] [E; bV]
+#pragma unroll
+            for (int a = 0; a < JBW; ++a) {
+                const int jb = w + GW * a;
+                if (jb < NJB)
+                    store4<MT>(kY(sf, jb), mmak<MT, 16>(sm.mats[MAT_A0] + r16 * L16, sm.EBVT + (jb * 16 + r16) * L32,
+                                                         Y0[a], lane));
+            }
+            if (!last) {
 #pragma unroll
                 for (int a = 0; a < CBW; ++a) {
-                    const int cb = w + 4 * a;
+                    const int cb = w + GW * a;
                     if (cb < NCB) {
                         f32x4 gmm;
 #pragma unroll
@@ -743,290 +770,320 @@ __global__ __launch_bounds__(256) void kda_bwd_grad_kernel(BwdParams p) {
                                                     gmm * S[a][jb], lane);
                     }
                 }
-                continue;
             }
+        }
+    }
 
-            // ================= gradient of sub-chunk sg (start state S, end derivative X)
-            // ---- Y = Y0 + A0 E  (row-major); X^T; dO^T; Kcc, Ktc rows; [Qb^T | Kb^T]
+    // ================= backward walk over the sub-chunks
+    f32x4 X[CBW][NJB];
+    load_state(X, p.xbuf + xrow * (int64_t)DK * DV);
+    for (int sg = ns - 1; sg >= 0; --sg) {
+        const int64_t t0 = sq.t0 + (int64_t)jc * CHB + sg * SC;
+        const int nrow = min(SC, clen - sg * SC);
+        const uint8_t* blk = p.ops + (sbase + sg) * OB::BYTES;
+        __syncthreads();
+        load_rows<MT, DK>(sm.kr, LDK, Kg, t0, p.H, h, nrow, tid, NT);
+        load_rows<MT, DV>(sm.vr, LDV, Vg, t0, p.H, h, nrow, tid, NT);
+        load_rows<MT, DK>(sm.qr, LDK, Qg, t0, p.H, h, nrow, tid, NT);
+        load_rows<MT, DV>(sm.dor, LDV, Og, t0, p.H, h, nrow, tid, NT);
+        load_decay<DK>(sm.G2, sm.bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, tid, NT);
+        load_mats(blk, 1u << MAT_TT | 1u << MAT_LT | 1u << MAT_P1T | 1u << MAT_P2T);
+        if (tid == 0) sm.exact = *reinterpret_cast<const int*>(blk + OB::FLAG);
+        // kept E and Y (row-major), the start state S (registers)
+        f32x4 S[CBW][NJB];
+#pragma unroll
+        for (int a = 0; a < JBW; ++a) {
+            const int jb = w + GW * a;
+            if (jb < NJB) {
+                store_rm<MT>(sm.Erm + jb * 16, LDV, load4<MT>(kE(sg, jb)), lane);
+                store_rm<MT>(sm.Yrm + jb * 16, LDV, load4<MT>(kY(sg, jb)), lane);
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < CBW; ++a)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int cb = w + GW * a;
+                S[a][jb] = cb < NCB ? load4<MT>(kS(sg, cb, jb)) : zero4();
+            }
+        __syncthreads();
+        // ================= gradient of sub-chunk sg (start state S, end derivative X)
+        // ---- X^T; dO^T; Kcc, Ktc rows; [Qb^T | Kb^T]
+#pragma unroll
+        for (int a = 0; a < CBW; ++a)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int cb = w + GW * a;
+                if (cb < NCB) store_nat<MT>(sm.SB + jb * 16 * LDK + cb * 16, LDK, X[a][jb], lane);
+            }
+        for (int x = tid; x < 16 * DV; x += NT) {
+            const int i = x % 16, j = x / 16;
+            sm.DFT[j * L32 + i] = sm.dor[i * LDV + j];
+        }
+        for (int x = tid; x < 16 * DK; x += NT) {
+            const int t = x / DK, c = x % DK;
+            const float kv = to_f32(sm.kr[t * LDK + c]), gc = sm.G2[SC * DK + c];
+            sm.GA[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[t * DK + c]));
+            sm.GB[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[(t + 1) * DK + c]));
+        }
+        for (int x = tid; x < 16 * DK; x += NT) {
+            const int s2 = x % 16, c = x / 16;
+            sm.CT[c * L32 + s2] = from_f32<MT>(to_f32(sm.qr[s2 * LDK + c]) * ex2(sm.G2[(s2 + 1) * DK + c]));
+            sm.CT[c * L32 + 16 + s2] = from_f32<MT>(to_f32(sm.kr[s2 * LDK + c]) * ex2(sm.G2[s2 * DK + c]));
+        }
+        __syncthreads();
+        // ---- dE = Kcc X + P1^T dO  (m = t, n = j) -> dE^T
+#pragma unroll
+        for (int a = 0; a < JBW; ++a) {
+            const int jb = w + GW * a;
+            if (jb < NJB) {
+                f32x4 d = mmak<MT, DK>(sm.GA + r16 * LDK, sm.SB + (jb * 16 + r16) * LDK, zero4(), lane);
+                d = mmak<MT, 16>(sm.mats[MAT_P1T] + r16 * L16, sm.DFT + (jb * 16 + r16) * L32, d, lane);
+                store_nat<MT>(sm.Y0T + jb * 16 * L16, L16, d, lane);
+            }
+        }
+        __syncthreads();
+        // ---- G^T = dE^T T  (m = j, n = t): G row-major, F^T = -b G^T, partial G.Y
+        {
+            float gy[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int a = 0; a < JBW; ++a) {
-                const int jb = w + 4 * a;
+                const int jb = w + GW * a;
                 if (jb < NJB) {
-                    const f32x4 y = mmak<MT, 16>(sm.mats[MAT_A0] + r16 * L16, sm.EBVT + (jb * 16 + r16) * L32, Y0[a], lane);
-                    store_rm<MT>(sm.Yrm + jb * 16, LDV, y, lane);
+                    const f32x4 gt = mmak<MT, 16>(sm.Y0T + (jb * 16 + r16) * L16, sm.mats[MAT_TT] + r16 * L16, zero4(), lane);
+                    store_nat<MT>(sm.Grm + jb * 16, LDV, gt, lane);
+                    const float bneg = -sm.bt[r16];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = jb * 16 + 4 * g4 + r;
+                        sm.DFT[j * L32 + 16 + r16] = from_f32<MT>(bneg * gt[r]);
+                        gy[0] += gt[r] * to_f32(sm.Yrm[r16 * LDV + j]);
+                    }
+                }
+            }
+            float v0 = gy[0];
+            v0 += __shfl_xor(v0, 16);
+            v0 += __shfl_xor(v0, 32);
+            if (g4 == 0) sm.red[1][w][r16] = v0;
+        }
+        __syncthreads();
+        // ---- R = Ktc X + P2^T dO + L^T F  (m = t, n = j): dv, partial R.V
+        {
+            float rv[4] = {0.f, 0.f, 0.f, 0.f};
+            MT* dvg = static_cast<MT*>(p.dv);
+#pragma unroll
+            for (int a = 0; a < JBW; ++a) {
+                const int jb = w + GW * a;
+                if (jb < NJB) {
+                    f32x4 rr = mmak<MT, DK>(sm.GB + r16 * LDK, sm.SB + (jb * 16 + r16) * LDK, zero4(), lane);
+                    rr = mmak<MT, 16>(sm.mats[MAT_P2T] + r16 * L16, sm.DFT + (jb * 16 + r16) * L32, rr, lane);
+                    rr = mmak<MT, 16>(sm.mats[MAT_LT] + r16 * L16, sm.DFT + (jb * 16 + r16) * L32 + 16, rr, lane);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 4 * g4 + r, j = jb * 16 + r16;
+                        rv[r] += rr[r] * to_f32(sm.vr[t * LDV + j]);
+                        if (t < nrow) dvg[((t0 + t) * p.H + h) * (int64_t)DV + j] = from_f32<MT>(sm.bt[t] * rr[r]);
+                    }
                 }
             }
 #pragma unroll
-            for (int a = 0; a < CBW; ++a)
+            for (int r = 0; r < 4; ++r) rv[r] = row_sum16(rv[r]);
+            if (r16 == 0)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.red[0][w][4 * g4 + r] = rv[r];
+        }
+        __syncthreads();
+        // ---- X row-major; dbeta
+#pragma unroll
+        for (int a = 0; a < CBW; ++a)
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int cb = w + GW * a;
+                if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, X[a][jb], lane);
+            }
+        if (tid < 16 && tid < nrow) {
+            float db = 0.f;
+#pragma unroll
+            for (int u = 0; u < GW; ++u) db += sm.red[0][u][tid] - sm.red[1][u][tid];
+            p.dbeta[(t0 + tid) * p.H + h] = db;
+        }
+        __syncthreads();
+        // ---- state parts with X: vds_s = V X^T, ayds_s = Y X^T  (m = t, n = c)
+        f32x4 vds[CBW], ayds[CBW], dqs[CBW], gss[CBW];
+#pragma unroll
+        for (int a = 0; a < CBW; ++a) {
+            const int cb = w + GW * a;
+            vds[a] = ayds[a] = zero4();
+            if (cb < NCB) {
+                vds[a] = mmak<MT, DV>(sm.vr + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
+                ayds[a] = mmak<MT, DV>(sm.Yrm + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
+            }
+        }
+        // ---- the eight 16 x 16 products (m = i, n = t), stored row-major [t][i] with their masks
+        for (int mi = w; mi < 8; mi += GW) {
+            const MT *A, *B;
+            switch (mi) {
+                case 0: A = sm.Erm; B = sm.dor; break;  // lower(dO E^T)
+                case 1: A = sm.vr; B = sm.dor; break;   // lower(dO bV^T)
+                case 2: A = sm.Erm; B = sm.Grm; break;  // strict_lower(G E^T)
+                case 3: A = sm.vr; B = sm.Grm; break;   // strict_lower(G bV^T)
+                case 4: A = sm.dor; B = sm.vr; break;   // upper(V dO^T)
+                case 5: A = sm.Grm; B = sm.vr; break;   // strict_upper(V F^T)
+                case 6: A = sm.dor; B = sm.Yrm; break;  // upper(Y dO^T)
+                default: A = sm.Grm; B = sm.Yrm; break; // strict_upper(Y F^T)
+            }
+            f32x4 d = mmak<MT, DV>(A + r16 * LDV, B + r16 * LDV, zero4(), lane);
+            MT* dst = mi < 2 ? sm.MQ : mi < 4 ? sm.MG : mi < 6 ? sm.MV : sm.MY;
+            const int coff = (mi & 1) * 16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * g4 + r, t = r16;
+                float x = d[r];
+                if (mi == 1 || mi == 3) x *= sm.bt[i];
+                if (mi == 5 || mi == 7) x *= -sm.bt[i];
+                const bool keep = mi < 2 ? i <= t : mi < 4 ? i < t : (mi & 1) ? i > t : i >= t;
+                dst[t * L32 + coff + i] = from_f32<MT>(keep ? x : 0.f);
+            }
+        }
+        // ---- X <- gamma X + [Qb^T | Kb^T] [dO; F]; phi_{-1} = rowsum(X_prev * S)
+#pragma unroll
+        for (int a = 0; a < CBW; ++a) {
+            const int cb = w + GW * a;
+            if (cb < NCB) {
+                f32x4 gmm;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gmm[r] = ex2(sm.G2[SC * DK + cb * 16 + 4 * g4 + r]);
+                f32x4 ph = zero4();
 #pragma unroll
                 for (int jb = 0; jb < NJB; ++jb) {
-                    const int cb = w + 4 * a;
-                    if (cb < NCB) store_nat<MT>(sm.SB + jb * 16 * LDK + cb * 16, LDK, X[a][jb], lane);
-                }
-            for (int x = tid; x < 16 * DV; x += 256) {
-                const int i = x % 16, j = x / 16;
-                sm.DFT[j * L32 + i] = sm.dor[i * LDV + j];
-            }
-            for (int x = tid; x < 16 * DK; x += 256) {
-                const int t = x / DK, c = x % DK;
-                const float kv = to_f32(sm.kr[t * LDK + c]), gc = sm.G2[SC * DK + c];
-                sm.GA[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[t * DK + c]));
-                sm.GB[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[(t + 1) * DK + c]));
-            }
-            for (int x = tid; x < 16 * DK; x += 256) {
-                const int s2 = x % 16, c = x / 16;
-                sm.CT[c * L32 + s2] = from_f32<MT>(to_f32(sm.qr[s2 * LDK + c]) * ex2(sm.G2[(s2 + 1) * DK + c]));
-                sm.CT[c * L32 + 16 + s2] = from_f32<MT>(to_f32(sm.kr[s2 * LDK + c]) * ex2(sm.G2[s2 * DK + c]));
-            }
-            __syncthreads();
-            // ---- dE = Kcc X + P1^T dO  (m = t, n = j) -> dE^T
-#pragma unroll
-            for (int a = 0; a < JBW; ++a) {
-                const int jb = w + 4 * a;
-                if (jb < NJB) {
-                    f32x4 d = mmak<MT, DK>(sm.GA + r16 * LDK, sm.SB + (jb * 16 + r16) * LDK, zero4(), lane);
-                    d = mmak<MT, 16>(sm.mats[MAT_P1T] + r16 * L16, sm.DFT + (jb * 16 + r16) * L32, d, lane);
-                    store_nat<MT>(sm.Y0T + jb * 16 * L16, L16, d, lane);
-                }
-            }
-            __syncthreads();
-            // ---- G^T = dE^T T  (m = j, n = t): G row-major, F^T = -b G^T, partial G.Y
-            {
-                float gy[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int a = 0; a < JBW; ++a) {
-                    const int jb = w + 4 * a;
-                    if (jb < NJB) {
-                        const f32x4 gt = mmak<MT, 16>(sm.Y0T + (jb * 16 + r16) * L16, sm.mats[MAT_TT] + r16 * L16, zero4(), lane);
-                        store_nat<MT>(sm.Grm + jb * 16, LDV, gt, lane);
-                        const float bneg = -sm.bt[r16];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = jb * 16 + 4 * g4 + r;
-                            sm.DFT[j * L32 + 16 + r16] = from_f32<MT>(bneg * gt[r]);
-                            gy[0] += gt[r] * to_f32(sm.Yrm[r16 * LDV + j]);
-                        }
-                    }
-                }
-                float v0 = gy[0];
-                v0 += __shfl_xor(v0, 16);
-                v0 += __shfl_xor(v0, 32);
-                if (g4 == 0) sm.red[1][w][r16] = v0;
-            }
-            __syncthreads();
-            // ---- R = Ktc X + P2^T dO + L^T F  (m = t, n = j): dv, partial R.V
-            {
-                float rv[4] = {0.f, 0.f, 0.f, 0.f};
-                MT* dvg = static_cast<MT*>(p.dv);
-#pragma unroll
-                for (int a = 0; a < JBW; ++a) {
-                    const int jb = w + 4 * a;
-                    if (jb < NJB) {
-                        f32x4 rr = mmak<MT, DK>(sm.GB + r16 * LDK, sm.SB + (jb * 16 + r16) * LDK, zero4(), lane);
-                        rr = mmak<MT, 16>(sm.mats[MAT_P2T] + r16 * L16, sm.DFT + (jb * 16 + r16) * L32, rr, lane);
-                        rr = mmak<MT, 16>(sm.mats[MAT_LT] + r16 * L16, sm.DFT + (jb * 16 + r16) * L32 + 16, rr, lane);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t = 4 * g4 + r, j = jb * 16 + r16;
-                            rv[r] += rr[r] * to_f32(sm.vr[t * LDV + j]);
-                            if (t < nrow) dvg[((t0 + t) * p.H + h) * (int64_t)DV + j] = from_f32<MT>(sm.bt[t] * rr[r]);
-                        }
-                    }
+                    X[a][jb] = mmak<MT, 32>(sm.CT + (cb * 16 + r16) * L32, sm.DFT + (jb * 16 + r16) * L32,
+                                            gmm * X[a][jb], lane);
+                    ph += X[a][jb] * S[a][jb];
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) rv[r] = row_sum16(rv[r]);
+                for (int r = 0; r < 4; ++r) ph[r] = row_sum16(ph[r]);
                 if (r16 == 0)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sm.red[0][w][4 * g4 + r] = rv[r];
+                    for (int r = 0; r < 4; ++r) sm.phi0[cb * 16 + 4 * g4 + r] = ph[r];
             }
-            __syncthreads();
-            // ---- X row-major; dbeta
+        }
+        __syncthreads();
+        // ---- S row-major; [Kc'^T | Kt'^T]
 #pragma unroll
-            for (int a = 0; a < CBW; ++a)
+        for (int a = 0; a < CBW; ++a)
 #pragma unroll
-                for (int jb = 0; jb < NJB; ++jb) {
-                    const int cb = w + 4 * a;
-                    if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, X[a][jb], lane);
-                }
-            if (tid < 16 && tid < nrow) {
-                const float db = sm.red[0][0][tid] + sm.red[0][1][tid] + sm.red[0][2][tid] + sm.red[0][3][tid] -
-                                 (sm.red[1][0][tid] + sm.red[1][1][tid] + sm.red[1][2][tid] + sm.red[1][3][tid]);
-                p.dbeta[(t0 + tid) * p.H + h] = db;
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int cb = w + GW * a;
+                if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, S[a][jb], lane);
             }
-            __syncthreads();
-            // ---- state parts with X: vds_s = V X^T, ayds_s = Y X^T  (m = t, n = c)
-            f32x4 vds[CBW], ayds[CBW], dqs[CBW], gss[CBW];
+        for (int x = tid; x < 16 * DK; x += NT) {
+            const int i = x % 16, c = x / 16;
+            const float kv = to_f32(sm.kr[i * LDK + c]), m2 = 0.5f * sm.G2[SC * DK + c];
+            sm.CT[c * L32 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[i * DK + c]));
+            sm.CT[c * L32 + 16 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[(i + 1) * DK + c]));
+        }
+        __syncthreads();
+        const bool exact = sm.exact != 0;
+        f32x4 mq[CBW], mg[CBW], mv[CBW], my[CBW];
 #pragma unroll
-            for (int a = 0; a < CBW; ++a) {
-                const int cb = w + 4 * a;
-                vds[a] = ayds[a] = zero4();
-                if (cb < NCB) {
-                    vds[a] = mmak<MT, DV>(sm.vr + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
-                    ayds[a] = mmak<MT, DV>(sm.Yrm + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
-                }
-            }
-            // ---- the eight 16 x 16 products (m = i, n = t), stored row-major [t][i] with their masks
-            for (int mi = w; mi < 8; mi += 4) {
-                const MT *A, *B;
-                switch (mi) {
-                    case 0: A = sm.Erm; B = sm.dor; break;  // lower(dO E^T)
-                    case 1: A = sm.vr; B = sm.dor; break;   // lower(dO bV^T)
-                    case 2: A = sm.Erm; B = sm.Grm; break;  // strict_lower(G E^T)
-                    case 3: A = sm.vr; B = sm.Grm; break;   // strict_lower(G bV^T)
-                    case 4: A = sm.dor; B = sm.vr; break;   // upper(V dO^T)
-                    case 5: A = sm.Grm; B = sm.vr; break;   // strict_upper(V F^T)
-                    case 6: A = sm.dor; B = sm.Yrm; break;  // upper(Y dO^T)
-                    default: A = sm.Grm; B = sm.Yrm; break; // strict_upper(Y F^T)
-                }
-                f32x4 d = mmak<MT, DV>(A + r16 * LDV, B + r16 * LDV, zero4(), lane);
-                MT* dst = mi < 2 ? sm.MQ : mi < 4 ? sm.MG : mi < 6 ? sm.MV : sm.MY;
-                const int coff = (mi & 1) * 16;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 4 * g4 + r, t = r16;
-                    float x = d[r];
-                    if (mi == 1 || mi == 3) x *= sm.bt[i];
-                    if (mi == 5 || mi == 7) x *= -sm.bt[i];
-                    const bool keep = mi < 2 ? i <= t : mi < 4 ? i < t : (mi & 1) ? i > t : i >= t;
-                    dst[t * L32 + coff + i] = from_f32<MT>(keep ? x : 0.f);
-                }
-            }
-            // ---- X <- gamma X + [Qb^T | Kb^T] [dO; F]; phi_{-1} = rowsum(X_prev * S)
-#pragma unroll
-            for (int a = 0; a < CBW; ++a) {
-                const int cb = w + 4 * a;
-                if (cb < NCB) {
-                    f32x4 gmm;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) gmm[r] = ex2(sm.G2[SC * DK + cb * 16 + 4 * g4 + r]);
-                    f32x4 ph = zero4();
-#pragma unroll
-                    for (int jb = 0; jb < NJB; ++jb) {
-                        X[a][jb] = mmak<MT, 32>(sm.CT + (cb * 16 + r16) * L32, sm.DFT + (jb * 16 + r16) * L32,
-                                                gmm * X[a][jb], lane);
-                        ph += X[a][jb] * S[a][jb];
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) ph[r] = row_sum16(ph[r]);
-                    if (r16 == 0)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) sm.phi0[cb * 16 + 4 * g4 + r] = ph[r];
-                }
-            }
-            __syncthreads();
-            // ---- S row-major; [Kc'^T | Kt'^T]
-#pragma unroll
-            for (int a = 0; a < CBW; ++a)
-#pragma unroll
-                for (int jb = 0; jb < NJB; ++jb) {
-                    const int cb = w + 4 * a;
-                    if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, S[a][jb], lane);
-                }
-            for (int x = tid; x < 16 * DK; x += 256) {
-                const int i = x % 16, c = x / 16;
-                const float kv = to_f32(sm.kr[i * LDK + c]), m2 = 0.5f * sm.G2[SC * DK + c];
-                sm.CT[c * L32 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[i * DK + c]));
-                sm.CT[c * L32 + 16 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[(i + 1) * DK + c]));
-            }
-            __syncthreads();
-            const bool exact = sm.exact != 0;
-            f32x4 mq[CBW], mg[CBW], mv[CBW], my[CBW];
-#pragma unroll
-            for (int a = 0; a < CBW; ++a) {
-                const int cb = w + 4 * a;
-                dqs[a] = gss[a] = mq[a] = mg[a] = zero4();
-                if (cb < NCB) {
-                    dqs[a] = mmak<MT, DV>(sm.dor + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
-                    gss[a] = mmak<MT, DV>(sm.Grm + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
-                    if (!exact) {
-                        mq[a] = mmak<MT, 32>(sm.MQ + r16 * L32, sm.CT + (cb * 16 + r16) * L32, zero4(), lane);
-                        mg[a] = mmak<MT, 32>(sm.MG + r16 * L32, sm.CT + (cb * 16 + r16) * L32, zero4(), lane);
-                    }
-                }
-            }
-            __syncthreads();
-            for (int x = tid; x < 16 * DK; x += 256) {
-                const int i = x % 16, c = x / 16;
-                const float m2 = 0.5f * sm.G2[SC * DK + c];
-                sm.CT[c * L32 + i] = from_f32<MT>(to_f32(sm.qr[i * LDK + c]) * ex2(sm.G2[(i + 1) * DK + c] - m2));
-                sm.CT[c * L32 + 16 + i] = from_f32<MT>(to_f32(sm.kr[i * LDK + c]) * ex2(sm.G2[i * DK + c] - m2));
-            }
-            __syncthreads();
-            // ---- masked products, combination, outputs  (m = t, n = c)
-            MT* dqg = static_cast<MT*>(p.dq);
-            MT* dkg = static_cast<MT*>(p.dk);
-            float dla_s[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int a = 0; a < CBW; ++a) {
-                const int cb = w + 4 * a;
-                if (cb >= NCB) continue;
-                const int c = cb * 16 + r16;
+        for (int a = 0; a < CBW; ++a) {
+            const int cb = w + GW * a;
+            dqs[a] = gss[a] = mq[a] = mg[a] = zero4();
+            if (cb < NCB) {
+                dqs[a] = mmak<MT, DV>(sm.dor + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
+                gss[a] = mmak<MT, DV>(sm.Grm + r16 * LDV, sm.SB + (cb * 16 + r16) * LDV, zero4(), lane);
                 if (!exact) {
-                    mv[a] = mmak<MT, 32>(sm.MV + r16 * L32, sm.CT + c * L32, zero4(), lane);
-                    my[a] = mmak<MT, 32>(sm.MY + r16 * L32, sm.CT + c * L32, zero4(), lane);
-                } else {
-                    exact_terms<MT, DK>(sm, c, g4, mq[a], mg[a], mv[a], my[a]);
-                }
-                const float gc = sm.G2[SC * DK + c], m2 = 0.5f * gc;
-                float av[4], au[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * g4 + r;
-                    const float gmt = sm.G2[t * DK + c], gt = sm.G2[(t + 1) * DK + c];
-                    const float fq = exact ? 1.f : ex2(gt - m2), fg = exact ? 1.f : ex2(gmt - m2);
-                    const float fv = exact ? 1.f : ex2(m2 - gt), fy = exact ? 1.f : ex2(m2 - gmt);
-                    const float dq = ex2(gt) * dqs[a][r] + fq * mq[a][r];
-                    const float gs = ex2(gmt) * gss[a][r] + fg * mg[a][r];
-                    const float vd = ex2(gc - gt) * vds[a][r] + fv * mv[a][r];
-                    const float ay = ex2(gc - gmt) * ayds[a][r] + fy * my[a][r];
-                    const float b = sm.bt[t];
-                    const float kt = to_f32(sm.kr[t * LDK + c]), qt = to_f32(sm.qr[t * LDK + c]);
-                    const float dk = b * (vd - ay - gs);
-                    av[r] = kt * dk + 2.f * b * kt * gs;
-                    au[r] = qt * dq;
-                    mv[a][r] = b * kt * vd;  // reuse: the b k vds term
-                    if (t < nrow) {
-                        dqg[((t0 + t) * p.H + h) * (int64_t)DK + c] = from_f32<MT>(dq);
-                        dkg[((t0 + t) * p.H + h) * (int64_t)DK + c] = from_f32<MT>(dk);
-                    }
-                }
-                // phi_t = phi_{-1} + sum_{j<=t} av_j - sum_{j<t} au_j, over the 16 tokens of column c
-                float ia[4], eu[4];
-                float sa = 0.f, su = 0.f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    eu[r] = su;
-                    sa += av[r]; su += au[r];
-                    ia[r] = sa;
-                }
-                // exclusive prefix over the four lane groups (t blocks of 4)
-                float pa = 0.f, pu = 0.f;
-                {
-                    const float a1 = __shfl(sa, (lane - 16) & 63), u1 = __shfl(su, (lane - 16) & 63);
-                    const float a2 = __shfl(sa, (lane - 32) & 63), u2 = __shfl(su, (lane - 32) & 63);
-                    const float a3 = __shfl(sa, (lane - 48) & 63), u3 = __shfl(su, (lane - 48) & 63);
-                    if (g4 >= 1) { pa += a1; pu += u1; }
-                    if (g4 >= 2) { pa += a2; pu += u2; }
-                    if (g4 >= 3) { pa += a3; pu += u3; }
-                }
-                const float ph0 = sm.phi0[c];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * g4 + r;
-                    const float dl = ph0 + pa + ia[r] - (pu + eu[r]) - mv[a][r];
-                    if (p.scalar) dla_s[r] += dl;
-                    else if (t < nrow) p.dla[((t0 + t) * p.H + h) * (int64_t)DK + c] = dl;
+                    mq[a] = mmak<MT, 32>(sm.MQ + r16 * L32, sm.CT + (cb * 16 + r16) * L32, zero4(), lane);
+                    mg[a] = mmak<MT, 32>(sm.MG + r16 * L32, sm.CT + (cb * 16 + r16) * L32, zero4(), lane);
                 }
             }
-            if (p.scalar) {
+        }
+        __syncthreads();
+        for (int x = tid; x < 16 * DK; x += NT) {
+            const int i = x % 16, c = x / 16;
+            const float m2 = 0.5f * sm.G2[SC * DK + c];
+            sm.CT[c * L32 + i] = from_f32<MT>(to_f32(sm.qr[i * LDK + c]) * ex2(sm.G2[(i + 1) * DK + c] - m2));
+            sm.CT[c * L32 + 16 + i] = from_f32<MT>(to_f32(sm.kr[i * LDK + c]) * ex2(sm.G2[i * DK + c] - m2));
+        }
+        __syncthreads();
+        // ---- masked products, combination, outputs  (m = t, n = c)
+        MT* dqg = static_cast<MT*>(p.dq);
+        MT* dkg = static_cast<MT*>(p.dk);
+        float dla_s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dla_s[r] = row_sum16(dla_s[r]);
-                if (r16 == 0)
+        for (int a = 0; a < CBW; ++a) {
+            const int cb = w + GW * a;
+            if (cb >= NCB) continue;
+            const int c = cb * 16 + r16;
+            if (!exact) {
+                mv[a] = mmak<MT, 32>(sm.MV + r16 * L32, sm.CT + c * L32, zero4(), lane);
+                my[a] = mmak<MT, 32>(sm.MY + r16 * L32, sm.CT + c * L32, zero4(), lane);
+            } else {
+                exact_terms<MT, DK>(sm, c, g4, mq[a], mg[a], mv[a], my[a]);
+            }
+            const float gc = sm.G2[SC * DK + c], m2 = 0.5f * gc;
+            float av[4], au[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sm.red[2][w][4 * g4 + r] = dla_s[r];
-                __syncthreads();
-                if (tid < 16 && tid < nrow)
-                    p.dla[(t0 + tid) * p.H + h] = sm.red[2][0][tid] + sm.red[2][1][tid] + sm.red[2][2][tid] + sm.red[2][3][tid];
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                const float gmt = sm.G2[t * DK + c], gt = sm.G2[(t + 1) * DK + c];
+                const float fq = exact ? 1.f : ex2(gt - m2), fg = exact ? 1.f : ex2(gmt - m2);
+                const float fv = exact ? 1.f : ex2(m2 - gt), fy = exact ? 1.f : ex2(m2 - gmt);
+                const float dq = ex2(gt) * dqs[a][r] + fq * mq[a][r];
+                const float gs = ex2(gmt) * gss[a][r] + fg * mg[a][r];
+                const float vd = ex2(gc - gt) * vds[a][r] + fv * mv[a][r];
+                const float ay = ex2(gc - gmt) * ayds[a][r] + fy * my[a][r];
+                const float b = sm.bt[t];
+                const float kt = to_f32(sm.kr[t * LDK + c]), qt = to_f32(sm.qr[t * LDK + c]);
+                const float dk = b * (vd - ay - gs);
+                av[r] = kt * dk + 2.f * b * kt * gs;
+                au[r] = qt * dq;
+                mv[a][r] = b * kt * vd;  // reuse: the b k vds term
+                if (t < nrow) {
+                    dqg[((t0 + t) * p.H + h) * (int64_t)DK + c] = from_f32<MT>(dq);
+                    dkg[((t0 + t) * p.H + h) * (int64_t)DK + c] = from_f32<MT>(dk);
+                }
+            }
+            // phi_t = phi_{-1} + sum_{j<=t} av_j - sum_{j<t} au_j, over the 16 tokens of column c
+            float ia[4], eu[4];
+            float sa = 0.f, su = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                eu[r] = su;
+                sa += av[r]; su += au[r];
+                ia[r] = sa;
+            }
+            // exclusive prefix over the four lane groups (t blocks of 4)
+            float pa = 0.f, pu = 0.f;
+            {
+                const float a1 = __shfl(sa, (lane - 16) & 63), u1 = __shfl(su, (lane - 16) & 63);
+                const float a2 = __shfl(sa, (lane - 32) & 63), u2 = __shfl(su, (lane - 32) & 63);
+                const float a3 = __shfl(sa, (lane - 48) & 63), u3 = __shfl(su, (lane - 48) & 63);
+                if (g4 >= 1) { pa += a1; pu += u1; }
+                if (g4 >= 2) { pa += a2; pu += u2; }
+                if (g4 >= 3) { pa += a3; pu += u3; }
+            }
+            const float ph0 = sm.phi0[c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                const float dl = ph0 + pa + ia[r] - (pu + eu[r]) - mv[a][r];
+                if (p.scalar) dla_s[r] += dl;
+                else if (t < nrow) p.dla[((t0 + t) * p.H + h) * (int64_t)DK + c] = dl;
+            }
+        }
+        if (p.scalar) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dla_s[r] = row_sum16(dla_s[r]);
+            if (r16 == 0)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.red[2][w][4 * g4 + r] = dla_s[r];
+            __syncthreads();
+            if (tid < 16 && tid < nrow) {
+                float dl = 0.f;
+#pragma unroll
+                for (int u = 0; u < GW; ++u) dl += sm.red[2][u][tid];
+                p.dla[(t0 + tid) * p.H + h] = dl;
             }
         }
     }
@@ -1051,7 +1108,7 @@ hipError_t grad_dispatch(const BwdParams& p, int64_t units, int nch_max, hipStre
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sm);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nch_max, (unsigned)units), dim3(256), sm, st, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nch_max, (unsigned)units), dim3(64 * GW), sm, st, p);
     return hipGetLastError();
 }
 
@@ -1081,6 +1138,11 @@ int bwd_block_bytes(int dtype, int dk) {
     return 0;
 }
 
+int64_t bwd_scratch_bytes(int dtype, int dk, int dv) {
+    const int64_t s = dtype == 1 ? 2 : 4;
+    return (int64_t)(CHB / SC) * ((int64_t)dk * dv + 2 * 16 * dv) * s;
+}
+
 bool bwd_supported(int dtype, int dk, int dv) {
     if (dtype == 1) return (dk == 32 || dk == 64 || dk == 128) && (dv == 32 || dv == 64 || dv == 128) && dk == dv;
     if (dtype == 0) return (dk == 16 || dk == 32 || dk == 64) && dk == dv;
@@ -1092,7 +1154,7 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t st) {
     p.q = a.q; p.k = a.k; p.v = a.v; p.log_a = a.log_a; p.beta = a.beta; p.S0 = a.S0;
     p.cu = a.cu_seqlens; p.eq_len = a.eq_len; p.dO = a.dO; p.dST = a.dST;
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dla = a.dlog_a; p.dbeta = a.dbeta; p.dS0 = a.dS0;
-    p.snap = a.snap; p.ops = static_cast<uint8_t*>(a.ops); p.xbuf = a.xbuf;
+    p.snap = a.snap; p.ops = static_cast<uint8_t*>(a.ops); p.xbuf = a.xbuf; p.scr = a.scr;
     p.H = a.num_heads; p.scalar = a.scalar; p.split = 0;
     if (a.dtype == 1) {
         if (a.kdim == 128 && a.vdim == 128) return run_all<bf16, 128, 128>(a, p, st);

@@ -111,12 +111,14 @@ struct BwdLaunch {
     const float* snap;          // forward states, one row per 64 tokens of each sequence
     void* ops;                  // operator blocks, bwd_block_bytes each
     float* xbuf;                // derivatives at chunk ends, [chunks][dk][dv]
+    void* scr;                  // bwd_scratch_bytes per chunk
     int32_t num_heads;
     int64_t units;
     int32_t nsub_max, nch_max;  // 16- and 64-token pieces of the longest sequence
     int32_t kdim, vdim, dtype, scalar;
 };
 int bwd_block_bytes(int dtype, int dk);
+int64_t bwd_scratch_bytes(int dtype, int dk, int dv);  // per 64-token chunk
 bool bwd_supported(int dtype, int dk, int dv);
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t stream);
 
