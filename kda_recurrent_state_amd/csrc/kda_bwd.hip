@@ -672,29 +672,107 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 if (cb < NCB && src) Z[a][jb] = load_state_tile(src + (int64_t)cb * 16 * DV + jb * 16, DV, lane);
             }
     };
-    auto load_mats = [&](const uint8_t* blk, unsigned mask) {
-        constexpr int PER = 16 / (int)sizeof(MT);
-        const MT* mats = reinterpret_cast<const MT*>(blk + OB::MATS);
-        for (int pc = tid; pc < 7 * 256 / PER; pc += NT) {
-            const int mi = pc / (256 / PER), o = (pc % (256 / PER)) * PER;
-            if (mask >> mi & 1u) copy16<MT>(&sm.mats[mi][(o / 16) * L16 + o % 16], mats + mi * 256 + o);
+    // A step's inputs (rows of k, v and, walking backwards, q and dO; the decays;
+    // the step's 16 x 16 matrices) are fetched into registers one step ahead and
+    // placed in LDS at the start of the step.  Pieces of 16 bytes, numbered
+    // [k | v | q | dO | decays | matrices], thread tid holding tid + NT a.
+    typedef typename V16<MT>::type VT;
+    constexpr int PER = 16 / (int)sizeof(MT);
+    constexpr int PRK = DK / PER, PRV = DV / PER, PLA = DK / 4, PM = 256 / PER;
+    constexpr int NPF = (16 * (2 * PRK + 2 * PRV + PLA) + 4 * PM + NT - 1) / NT;
+    VT pf[NPF];
+    float pfb = 0.f;
+    auto mat_of = [](bool bwd, int idx) {
+        return bwd ? (idx == 0 ? MAT_TT : idx == 1 ? MAT_LT : idx == 2 ? MAT_P1T : MAT_P2T)
+                   : (idx == 0 ? MAT_TB : idx == 1 ? MAT_L : MAT_A0);
+    };
+    // piece pc of a step: which tensor, row i and offset e (elements) within it
+    struct Piece { int kind, i, e; };
+    auto decode = [&](int pc, bool bwd) -> Piece {
+        const int B0 = 16 * PRK, B1 = B0 + 16 * PRV, B2 = bwd ? B1 + 16 * PRK : B1, B3 = bwd ? B2 + 16 * PRV : B1;
+        const int B4 = B3 + 16 * PLA, B5 = B4 + (bwd ? 4 : 3) * PM;
+        if (pc < B0) return Piece{0, pc / PRK, (pc % PRK) * PER};
+        if (pc < B1) return Piece{1, (pc - B0) / PRV, ((pc - B0) % PRV) * PER};
+        if (pc < B2) return Piece{2, (pc - B1) / PRK, ((pc - B1) % PRK) * PER};
+        if (pc < B3) return Piece{3, (pc - B2) / PRV, ((pc - B2) % PRV) * PER};
+        if (pc < B4) return Piece{4, (pc - B3) / PLA, ((pc - B3) % PLA) * 4};
+        if (pc < B5) return Piece{5, (pc - B4) / PM, ((pc - B4) % PM) * PER};
+        return Piece{6, 0, 0};
+    };
+    auto issue = [&](int s2, bool bwd) {
+        const int64_t t0 = sq.t0 + (int64_t)jc * CHB + s2 * SC;
+        const int nrow = min(SC, clen - s2 * SC);
+        const MT* mats = reinterpret_cast<const MT*>(p.ops + (sbase + s2) * OB::BYTES + OB::MATS);
+#pragma unroll
+        for (int a = 0; a < NPF; ++a) {
+            const Piece pc = decode(tid + NT * a, bwd);
+            VT x = {};
+            const int64_t row = (t0 + pc.i) * p.H + h;
+            if (pc.kind <= 4 && pc.i >= nrow) {
+            } else if (pc.kind == 0) {
+                x = *reinterpret_cast<const VT*>(Kg + row * DK + pc.e);
+            } else if (pc.kind == 1) {
+                x = *reinterpret_cast<const VT*>(Vg + row * DV + pc.e);
+            } else if (pc.kind == 2) {
+                x = *reinterpret_cast<const VT*>(Qg + row * DK + pc.e);
+            } else if (pc.kind == 3) {
+                x = *reinterpret_cast<const VT*>(Og + row * DV + pc.e);
+            } else if (pc.kind == 4) {
+                f32x4 d;
+                if (p.scalar) {
+                    const float a1 = p.log_a[row];
+                    d = f32x4{a1, a1, a1, a1};
+                } else {
+                    d = *reinterpret_cast<const f32x4*>(p.log_a + row * DK + pc.e);
+                }
+                x = __builtin_bit_cast(VT, d);
+            } else if (pc.kind == 5) {
+                x = *reinterpret_cast<const VT*>(mats + mat_of(bwd, pc.i) * 256 + pc.e);
+            }
+            pf[a] = x;
+        }
+        pfb = tid < nrow && tid < SC ? p.beta[(t0 + tid) * p.H + h] : 0.f;
+    };
+    // places the fetched pieces in LDS; the decays as log2 e * log a in rows 1..16 of G2
+    auto commit = [&](bool bwd) {
+#pragma unroll
+        for (int a = 0; a < NPF; ++a) {
+            const Piece pc = decode(tid + NT * a, bwd);
+            if (pc.kind == 0) *reinterpret_cast<VT*>(sm.kr + pc.i * LDK + pc.e) = pf[a];
+            else if (pc.kind == 1) *reinterpret_cast<VT*>(sm.vr + pc.i * LDV + pc.e) = pf[a];
+            else if (pc.kind == 2) *reinterpret_cast<VT*>(sm.qr + pc.i * LDK + pc.e) = pf[a];
+            else if (pc.kind == 3) *reinterpret_cast<VT*>(sm.dor + pc.i * LDV + pc.e) = pf[a];
+            else if (pc.kind == 4)
+                *reinterpret_cast<f32x4*>(sm.G2 + (pc.i + 1) * DK + pc.e) = __builtin_bit_cast(f32x4, pf[a]) * LOG2E;
+            else if (pc.kind == 5)
+                *reinterpret_cast<VT*>(&sm.mats[mat_of(bwd, pc.i)][(pc.e / 16) * L16 + pc.e % 16]) = pf[a];
+        }
+        if (tid < SC) sm.bt[tid] = pfb;
+    };
+    // G2[i][c] = running sum over the first i tokens (after commit and a barrier)
+    auto prefix_decay = [&]() {
+        for (int c = tid; c < DK; c += NT) {
+            float s2 = 0.f;
+            sm.G2[c] = 0.f;
+#pragma unroll
+            for (int i = 1; i <= SC; ++i) {
+                s2 += sm.G2[i * DK + c];
+                sm.G2[i * DK + c] = s2;
+            }
         }
     };
 
     // ================= forward walk: start state, E and Y of every sub-chunk
     {
         f32x4 S[CBW][NJB];
+        issue(0, false);
         load_state(S, s_start);
         for (int sf = 0; sf < ns; ++sf) {
-            const int64_t t0 = sq.t0 + (int64_t)jc * CHB + sf * SC;
-            const int nrow = min(SC, clen - sf * SC);
-            const uint8_t* blk = p.ops + (sbase + sf) * OB::BYTES;
             const bool last = sf == ns - 1;
             __syncthreads();
-            load_rows<MT, DK>(sm.kr, LDK, Kg, t0, p.H, h, nrow, tid, NT);
-            load_rows<MT, DV>(sm.vr, LDV, Vg, t0, p.H, h, nrow, tid, NT);
-            load_decay<DK>(sm.G2, sm.bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, tid, NT);
-            load_mats(blk, 1u << MAT_TB | 1u << MAT_L | 1u << MAT_A0);
+            commit(false);
+            if (!last) issue(sf + 1, false);
+            else issue(ns - 1, true);  // the backward walk starts at the last sub-chunk
 #pragma unroll
             for (int a = 0; a < CBW; ++a)
 #pragma unroll
@@ -705,6 +783,8 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                         store4<MT>(kS(sf, cb, jb), S[a][jb]);
                     }
                 }
+            __syncthreads();
+            prefix_decay();
             __syncthreads();
             // ---- Kb rows, (bV)^T, [Kcc^T | Ktc^T]
             for (int x = tid; x < 16 * DK; x += NT) {
@@ -781,22 +861,15 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         const int64_t t0 = sq.t0 + (int64_t)jc * CHB + sg * SC;
         const int nrow = min(SC, clen - sg * SC);
         const uint8_t* blk = p.ops + (sbase + sg) * OB::BYTES;
-        __syncthreads();
-        load_rows<MT, DK>(sm.kr, LDK, Kg, t0, p.H, h, nrow, tid, NT);
-        load_rows<MT, DV>(sm.vr, LDV, Vg, t0, p.H, h, nrow, tid, NT);
-        load_rows<MT, DK>(sm.qr, LDK, Qg, t0, p.H, h, nrow, tid, NT);
-        load_rows<MT, DV>(sm.dor, LDV, Og, t0, p.H, h, nrow, tid, NT);
-        load_decay<DK>(sm.G2, sm.bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, tid, NT);
-        load_mats(blk, 1u << MAT_TT | 1u << MAT_LT | 1u << MAT_P1T | 1u << MAT_P2T);
-        if (tid == 0) sm.exact = *reinterpret_cast<const int*>(blk + OB::FLAG);
-        // kept E and Y (row-major), the start state S (registers)
-        f32x4 S[CBW][NJB];
+        // kept E, Y and start state S of this sub-chunk (the loads go out first)
+        f32x4 S[CBW][NJB], Ek[JBW], Yk[JBW];
 #pragma unroll
         for (int a = 0; a < JBW; ++a) {
             const int jb = w + GW * a;
+            Ek[a] = Yk[a] = zero4();
             if (jb < NJB) {
-                store_rm<MT>(sm.Erm + jb * 16, LDV, load4<MT>(kE(sg, jb)), lane);
-                store_rm<MT>(sm.Yrm + jb * 16, LDV, load4<MT>(kY(sg, jb)), lane);
+                Ek[a] = load4<MT>(kE(sg, jb));
+                Yk[a] = load4<MT>(kY(sg, jb));
             }
         }
 #pragma unroll
@@ -806,6 +879,21 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 const int cb = w + GW * a;
                 S[a][jb] = cb < NCB ? load4<MT>(kS(sg, cb, jb)) : zero4();
             }
+        const int exact_flag = *reinterpret_cast<const int*>(blk + OB::FLAG);
+        __syncthreads();
+        commit(true);
+        if (sg > 0) issue(sg - 1, true);
+        if (tid == 0) sm.exact = exact_flag;
+#pragma unroll
+        for (int a = 0; a < JBW; ++a) {
+            const int jb = w + GW * a;
+            if (jb < NJB) {
+                store_rm<MT>(sm.Erm + jb * 16, LDV, Ek[a], lane);
+                store_rm<MT>(sm.Yrm + jb * 16, LDV, Yk[a], lane);
+            }
+        }
+        __syncthreads();
+        prefix_decay();
         __syncthreads();
         // ================= gradient of sub-chunk sg (start state S, end derivative X)
         // ---- X^T; dO^T; Kcc, Ktc rows; [Qb^T | Kb^T]
