@@ -153,3 +153,31 @@ def test_bwd_matches_finite_difference_of_gpu_forward():
     an = float((np64(got["dlog_a"]) * np64(u)).sum())
     log(f"  directional: analytic {an:.6g} central difference {fd:.6g}")
     assert abs(an - fd) <= 2e-3 * max(1.0, abs(fd))
+
+
+def test_bwd_full_size_sampled():
+    # the bench batch (2 x 32 heads x 32768 tokens, dk = dv = 128, bf16) through the
+    # gradient call the bench times; the oracle walks one whole (sequence, head)
+    from kda_recurrent_state_amd.workloads import WORKLOADS, generate
+    w = WORKLOADS["kda_b2_h32_t32768_d128_bf16"]
+    inp = generate(w, 3, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    T = inp["q"].shape[0]
+    dO = torch.randn((T, w.heads, w.dv), generator=g, device=DEV).to(w.dtype)
+    dST = torch.randn((w.n_seqs, w.heads, w.dk, w.dv), generator=g, device=DEV)
+    got = kda.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], dO, S0=inp["S0"],
+                        cu_seqlens=inp["cu_seqlens"], dS_T=dST, max_seqlen=w.seqlen)
+    torch.cuda.synchronize()
+    n, h = 1, 21
+    s, e = n * w.seqlen, (n + 1) * w.seqlen
+    c = lambda t: t[s:e, h:h + 1].cpu()
+    log(f"  oracle gradient of sequence {n}, head {h} ({w.seqlen} tokens)")
+    ref = kda_oracle_bwd(c(inp["q"]), c(inp["k"]), c(inp["v"]), c(inp["log_a"]), c(inp["beta"]),
+                         S0=inp["S0"][n:n + 1, h:h + 1].cpu(), dO=c(dO), dST=dST[n:n + 1, h:h + 1].cpu())
+    errs = {}
+    for name in ("dq", "dk", "dv", "dlog_a", "dbeta"):
+        errs[name] = max_rel_err(got[name][s:e, h:h + 1], ref[name])
+    errs["dS0"] = max_rel_err(got["dS0"][n:n + 1, h:h + 1], ref["dS0"])
+    log("  full size: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL[torch.bfloat16] for v in errs.values()), errs
