@@ -248,7 +248,7 @@ KDA_API int kda_chunk_bwd(const kda_dims_t* dims, const void* q, const void* k, 
                   void* dv, float* dlog_a, float* dbeta, float* dS0, void* workspace,
                   size_t workspace_bytes, void* stream);
 
-/* Workspace kda_chunk_bwd needs for these dims (about 2.6 KB per token and head
+/* Workspace kda_chunk_bwd needs for these dims (about 5.9 KB per token and head
  * at dk = dv = 128, plus what the prefill's two-pass method prefers). */
 KDA_API int kda_chunk_bwd_workspace_size(const kda_dims_t* dims, size_t* bytes);
 
