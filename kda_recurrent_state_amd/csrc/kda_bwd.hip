@@ -28,6 +28,10 @@
 // so every factor stays below e^{span/2}.  A sub-chunk whose span -gC exceeds 160
 // nats in some channel takes one exponent per term instead.
 //
+// Barriers inside the walks order LDS only (lds_barrier), so global loads fetched
+// for the next step stay in flight across them; every global value a walk reads
+// back is read by the lane that wrote it or reaches LDS through registers.
+//
 // Three kernels follow the forward prefill, which leaves the state at every 64th
 // token: kda_bwd_ops (one wavefront per sub-chunk: the C x C products, the solve,
 // the operators of the reverse walk), kda_bwd_scan (one workgroup per (sequence,
@@ -426,7 +430,7 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
 // ==================================================================== scan
 // Reverse walk of the state derivative for one (sequence, head, value slice).
 template <typename MT, int DK, int DVS>
-__global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV) {
+__global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV, int nitems) {
     typedef OpBlock<MT, DK> OB;
     constexpr int P = 16 / (int)sizeof(MT);
     constexpr int LDK = DK + P, L16 = 16 + P, L32 = 32 + P;
@@ -434,7 +438,9 @@ __global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV) 
     constexpr int NCB = DK / 16, NJB = DVS / 16, CBW = (NCB + 3) / 4;
     constexpr int WALKP = OB::WALK / 16;          // 16-byte pieces of the walk's operators
     constexpr int DOP = 16 * DVS / PER;           // 16-byte pieces of the dO slice
-    constexpr int NP = (WALKP + DOP + 255) / 256; // pieces per thread
+    constexpr int NB = (WALKP + 255) / 256;        // block pieces per thread
+    constexpr int NP = NB + 1;                     // and one dO piece
+    static_assert(DOP <= 256 && (DOP & (DOP - 1)) == 0, "dO pieces");
     __shared__ __attribute__((aligned(16))) MT Wl[2][16 * LDK];
     __shared__ __attribute__((aligned(16))) MT Ml[2][16 * L16];
     __shared__ __attribute__((aligned(16))) MT QKl[2][DK * L32];
@@ -443,8 +449,15 @@ __global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV) 
     __shared__ __attribute__((aligned(16))) MT XT[DVS * LDK];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t unit = blockIdx.y;
-    const int slice = blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs round-robin; item = (bid % 8) * per + bid / 8
+    // puts consecutive items, the value slices of one (sequence, head), on one XCD,
+    // so its operator blocks come from HBM once and from that XCD's L2 after.
+    const int per = (nitems + 7) / 8;
+    const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (item >= nitems) return;
+    const int nsl = DV / DVS;
+    const int64_t unit = item / nsl;
+    const int slice = item % nsl;
     const int n = (int)(unit / p.H), h = (int)(unit % p.H);
     const SeqSpan sq = seq_span(p.cu, p.eq_len, n);
     const int nsub = ceil_div(sq.len, SC), nch = ceil_div(sq.len, CHB);
@@ -465,56 +478,59 @@ __global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV) 
 
     const MT* dO = static_cast<const MT*>(p.dO);
     typedef typename V16<MT>::type VT;
-    VT pre[NP];
-    auto fetch = [&](int s) {
+    // Operators and dO rows are fetched two steps ahead into one of two register
+    // sets (the loop is unrolled by two so that each set is a fixed set of
+    // registers) and placed in one of two LDS buffers one step ahead.
+    VT pre[2][NP];
+    // Every thread issues the same NP loads, at addresses that are always valid
+    // (block pieces past the end repeat earlier ones, dO rows past the sub-chunk
+    // repeat its first row) and without branches, so the loads stay in program
+    // order and a later use waits only for its own set, not for the set issued
+    // after it.  place() skips the repeats and zeroes the rows past the end.
+    const int dp = tid & (DOP - 1), di = dp / (DVS / PER), de = (dp % (DVS / PER)) * PER;
+    auto fetch = [&](int s, VT (&dst)[NP]) {
         const uint8_t* blk = p.ops + (sbase + s) * OB::BYTES;
         const int64_t t0 = sq.t0 + (int64_t)s * SC;
         const int nrow = min(SC, sq.len - s * SC);
 #pragma unroll
-        for (int a = 0; a < NP; ++a) {
-            const int pc = tid + 256 * a;
-            VT x = {};
-            if (pc < WALKP) {
-                x = *reinterpret_cast<const VT*>(blk + 16 * pc);
-            } else if (pc < WALKP + DOP) {
-                const int q2 = pc - WALKP, i = q2 / (DVS / PER), e = (q2 % (DVS / PER)) * PER;
-                if (i < nrow) x = *reinterpret_cast<const VT*>(dO + ((t0 + i) * p.H + h) * (int64_t)DV + j0 + e);
-            }
-            pre[a] = x;
+        for (int a = 0; a < NB; ++a) {
+            const int pc = tid + 256 * a, pcc = pc >= WALKP ? pc - WALKP : pc;
+            dst[a] = *reinterpret_cast<const VT*>(blk + 16 * pcc);
         }
+        const int row = di < nrow ? di : 0;
+        dst[NB] = *reinterpret_cast<const VT*>(dO + ((t0 + row) * p.H + h) * (int64_t)DV + j0 + de);
     };
-    auto place = [&](int b) {
+    // places sub-chunk s's fetched pieces in LDS buffer b
+    auto place = [&](int b, const VT (&src)[NP], int s) {
 #pragma unroll
-        for (int a = 0; a < NP; ++a) {
+        for (int a = 0; a < NB; ++a) {
             const int pc = tid + 256 * a;
             const int off = 16 * pc;
-            if (pc < WALKP) {
-                if (off < OB::M) {
-                    const int row = off / (DK * (int)sizeof(MT)), col = (off % (DK * (int)sizeof(MT))) / (int)sizeof(MT);
-                    *reinterpret_cast<VT*>(&Wl[b][row * LDK + col]) = pre[a];
-                } else if (off < OB::QK) {
-                    const int o = (off - OB::M) / (int)sizeof(MT), row = o / 16, col = o % 16;
-                    *reinterpret_cast<VT*>(&Ml[b][row * L16 + col]) = pre[a];
-                } else if (off < OB::GAM) {
-                    const int o = (off - OB::QK) / (int)sizeof(MT), row = o / 32, col = o % 32;
-                    *reinterpret_cast<VT*>(&QKl[b][row * L32 + col]) = pre[a];
-                } else {
-                    // gamma is fp32 in the block whatever MT is
-                    *reinterpret_cast<f32x4*>(&gl[b][(off - OB::GAM) / 4]) = __builtin_bit_cast(f32x4, pre[a]);
-                }
-            } else if (pc < WALKP + DOP) {
-                const int q2 = pc - WALKP, i = q2 / (DVS / PER), e = (q2 % (DVS / PER)) * PER;
-#pragma unroll
-                for (int u = 0; u < PER; ++u) DFT[b][(e + u) * L32 + i] = pre[a][u];
+            if (pc >= WALKP) continue;
+            if (off < OB::M) {
+                const int row = off / (DK * (int)sizeof(MT)), col = (off % (DK * (int)sizeof(MT))) / (int)sizeof(MT);
+                *reinterpret_cast<VT*>(&Wl[b][row * LDK + col]) = src[a];
+            } else if (off < OB::QK) {
+                const int o = (off - OB::M) / (int)sizeof(MT), row = o / 16, col = o % 16;
+                *reinterpret_cast<VT*>(&Ml[b][row * L16 + col]) = src[a];
+            } else if (off < OB::GAM) {
+                const int o = (off - OB::QK) / (int)sizeof(MT), row = o / 32, col = o % 32;
+                *reinterpret_cast<VT*>(&QKl[b][row * L32 + col]) = src[a];
+            } else {
+                // gamma is fp32 in the block whatever MT is
+                *reinterpret_cast<f32x4*>(&gl[b][(off - OB::GAM) / 4]) = __builtin_bit_cast(f32x4, src[a]);
             }
         }
+        if (tid < DOP) {
+            const int nrow = min(SC, sq.len - s * SC);
+            const VT x = di < nrow ? src[NB] : VT{};
+#pragma unroll
+            for (int u = 0; u < PER; ++u) DFT[b][(de + u) * L32 + di] = x[u];
+        }
     };
-
-    if (nsub > 0) {
-        fetch(nsub - 1);
-        place((nsub - 1) & 1);
-    }
-    for (int s = nsub - 1; s >= 0; --s) {
+    // One step of the walk, sub-chunk s: on entry LDS buffer s & 1 holds its
+    // operators and register set RS holds those of s - 1 (fetched two steps ago).
+    auto step = [&](int s, VT (&cur)[NP], VT (&nxt)[NP]) {
         const int b = s & 1;
         // derivative at the end of a 64-token chunk
         if (s % (CHB / SC) == CHB / SC - 1 || s == nsub - 1) {
@@ -534,15 +550,15 @@ __global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV) 
                 const int cb = w + 4 * a;
                 if (cb < NCB) store_nat<MT>(XT + jb * 16 * LDK + cb * 16, LDK, X[a][jb], lane);
             }
-        if (s > 0) fetch(s - 1);
-        __syncthreads();
+        if (s > 1) fetch(s - 2, nxt);
+        lds_barrier();
         // F = -(W X + M dO)   (m = t, n = j)
         for (int jb = w; jb < NJB; jb += 4) {
             f32x4 acc = mmak<MT, DK>(&Wl[b][(lane & 15) * LDK], XT + (jb * 16 + (lane & 15)) * LDK, zero4(), lane);
             acc = mmak<MT, 16>(&Ml[b][(lane & 15) * L16], &DFT[b][(jb * 16 + (lane & 15)) * L32], acc, lane);
             store_nat<MT>(&DFT[b][jb * 16 * L32 + 16], L32, -acc, lane);
         }
-        __syncthreads();
+        lds_barrier();
         // X <- gamma X + [Qb^T | Kb^T] [dO; F]   (m = c, n = j)
 #pragma unroll
         for (int a = 0; a < CBW; ++a) {
@@ -557,7 +573,18 @@ __global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV) 
                                             &DFT[b][(jb * 16 + (lane & 15)) * L32], gmm * X[a][jb], lane);
             }
         }
-        if (s > 0) place((s - 1) & 1);
+        if (s > 0) place((s - 1) & 1, cur, s - 1);
+    };
+
+    if (nsub > 0) {
+        fetch(nsub - 1, pre[0]);
+        place((nsub - 1) & 1, pre[0], nsub - 1);
+    }
+    if (nsub > 1) fetch(nsub - 2, pre[0]);
+    // step s uses set (nsub - 1 - s) & 1 for s - 1 and fills the other with s - 2
+    for (int s = nsub - 1; s >= 0; s -= 2) {
+        step(s, pre[0], pre[1]);
+        if (s >= 1) step(s - 1, pre[1], pre[0]);
     }
     if (p.dS0) {
 #pragma unroll
@@ -769,7 +796,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         load_state(S, s_start);
         for (int sf = 0; sf < ns; ++sf) {
             const bool last = sf == ns - 1;
-            __syncthreads();
+            lds_barrier();
             commit(false);
             if (!last) issue(sf + 1, false);
             else issue(ns - 1, true);  // the backward walk starts at the last sub-chunk
@@ -783,9 +810,9 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                         store4<MT>(kS(sf, cb, jb), S[a][jb]);
                     }
                 }
-            __syncthreads();
+            lds_barrier();
             prefix_decay();
-            __syncthreads();
+            lds_barrier();
             // ---- Kb rows, (bV)^T, [Kcc^T | Ktc^T]
             for (int x = tid; x < 16 * DK; x += NT) {
                 const int t = x / DK, c = x % DK;
@@ -803,7 +830,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                     sm.CT[c * L32 + 16 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[(s2 + 1) * DK + c]));
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // ---- Y0 = Kb S + L bV   (m = t, n = j)
             f32x4 Y0[JBW];
 #pragma unroll
@@ -816,7 +843,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                     store_nat<MT>(sm.Y0T + jb * 16 * L16, L16, Y0[a], lane);
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // ---- E = -T diag(b) Y0
 #pragma unroll
             for (int a = 0; a < JBW; ++a) {
@@ -827,7 +854,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                     store4<MT>(kE(sf, jb), e);
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // ---- Y = Y0 + A0 E; S <- gamma S + [Kcc^T | Ktc^T] [E; bV]
 #pragma unroll
             for (int a = 0; a < JBW; ++a) {
@@ -880,7 +907,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 S[a][jb] = cb < NCB ? load4<MT>(kS(sg, cb, jb)) : zero4();
             }
         const int exact_flag = *reinterpret_cast<const int*>(blk + OB::FLAG);
-        __syncthreads();
+        lds_barrier();
         commit(true);
         if (sg > 0) issue(sg - 1, true);
         if (tid == 0) sm.exact = exact_flag;
@@ -892,9 +919,9 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 store_rm<MT>(sm.Yrm + jb * 16, LDV, Yk[a], lane);
             }
         }
-        __syncthreads();
+        lds_barrier();
         prefix_decay();
-        __syncthreads();
+        lds_barrier();
         // ================= gradient of sub-chunk sg (start state S, end derivative X)
         // ---- X^T; dO^T; Kcc, Ktc rows; [Qb^T | Kb^T]
 #pragma unroll
@@ -919,7 +946,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             sm.CT[c * L32 + s2] = from_f32<MT>(to_f32(sm.qr[s2 * LDK + c]) * ex2(sm.G2[(s2 + 1) * DK + c]));
             sm.CT[c * L32 + 16 + s2] = from_f32<MT>(to_f32(sm.kr[s2 * LDK + c]) * ex2(sm.G2[s2 * DK + c]));
         }
-        __syncthreads();
+        lds_barrier();
         // ---- dE = Kcc X + P1^T dO  (m = t, n = j) -> dE^T
 #pragma unroll
         for (int a = 0; a < JBW; ++a) {
@@ -930,7 +957,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 store_nat<MT>(sm.Y0T + jb * 16 * L16, L16, d, lane);
             }
         }
-        __syncthreads();
+        lds_barrier();
         // ---- G^T = dE^T T  (m = j, n = t): G row-major, F^T = -b G^T, partial G.Y
         {
             float gy[4] = {0.f, 0.f, 0.f, 0.f};
@@ -954,7 +981,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             v0 += __shfl_xor(v0, 32);
             if (g4 == 0) sm.red[1][w][r16] = v0;
         }
-        __syncthreads();
+        lds_barrier();
         // ---- R = Ktc X + P2^T dO + L^T F  (m = t, n = j): dv, partial R.V
         {
             float rv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -980,7 +1007,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sm.red[0][w][4 * g4 + r] = rv[r];
         }
-        __syncthreads();
+        lds_barrier();
         // ---- X row-major; dbeta
 #pragma unroll
         for (int a = 0; a < CBW; ++a)
@@ -995,7 +1022,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             for (int u = 0; u < GW; ++u) db += sm.red[0][u][tid] - sm.red[1][u][tid];
             p.dbeta[(t0 + tid) * p.H + h] = db;
         }
-        __syncthreads();
+        lds_barrier();
         // ---- state parts with X: vds_s = V X^T, ayds_s = Y X^T  (m = t, n = c)
         f32x4 vds[CBW], ayds[CBW], dqs[CBW], gss[CBW];
 #pragma unroll
@@ -1055,7 +1082,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                     for (int r = 0; r < 4; ++r) sm.phi0[cb * 16 + 4 * g4 + r] = ph[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
         // ---- S row-major; [Kc'^T | Kt'^T]
 #pragma unroll
         for (int a = 0; a < CBW; ++a)
@@ -1070,7 +1097,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             sm.CT[c * L32 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[i * DK + c]));
             sm.CT[c * L32 + 16 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[(i + 1) * DK + c]));
         }
-        __syncthreads();
+        lds_barrier();
         const bool exact = sm.exact != 0;
         f32x4 mq[CBW], mg[CBW], mv[CBW], my[CBW];
 #pragma unroll
@@ -1086,14 +1113,14 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         for (int x = tid; x < 16 * DK; x += NT) {
             const int i = x % 16, c = x / 16;
             const float m2 = 0.5f * sm.G2[SC * DK + c];
             sm.CT[c * L32 + i] = from_f32<MT>(to_f32(sm.qr[i * LDK + c]) * ex2(sm.G2[(i + 1) * DK + c] - m2));
             sm.CT[c * L32 + 16 + i] = from_f32<MT>(to_f32(sm.kr[i * LDK + c]) * ex2(sm.G2[i * DK + c] - m2));
         }
-        __syncthreads();
+        lds_barrier();
         // ---- masked products, combination, outputs  (m = t, n = c)
         MT* dqg = static_cast<MT*>(p.dq);
         MT* dkg = static_cast<MT*>(p.dk);
@@ -1166,7 +1193,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             if (r16 == 0)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sm.red[2][w][4 * g4 + r] = dla_s[r];
-            __syncthreads();
+            lds_barrier();
             if (tid < 16 && tid < nrow) {
                 float dl = 0.f;
 #pragma unroll
@@ -1184,8 +1211,9 @@ hipError_t ops_dispatch(const BwdParams& p, int64_t units, int nsub_max, hipStre
 }
 template <typename MT, int DK, int DVS>
 hipError_t scan_dispatch(const BwdParams& p, int64_t units, int dv, hipStream_t st) {
-    hipLaunchKernelGGL((kda_bwd_scan_kernel<MT, DK, DVS>), dim3((unsigned)(dv / DVS), (unsigned)units), dim3(256), 0,
-                       st, p, dv);
+    const int64_t nitems = (int64_t)(dv / DVS) * units;
+    const int64_t nblk = (nitems + 7) / 8 * 8;
+    hipLaunchKernelGGL((kda_bwd_scan_kernel<MT, DK, DVS>), dim3((unsigned)nblk), dim3(256), 0, st, p, dv, (int)nitems);
     return hipGetLastError();
 }
 template <typename MT, int DK, int DV>
