@@ -243,21 +243,31 @@ __device__ __forceinline__ void load_decay(float* G2, float* bt, const float* la
 }
 
 // ===================================================================== ops
-// One wavefront per (sequence, head, sub-chunk).
+// One wavefront per (sequence, head, sub-chunk).  LDS is reused as the sub-chunk's
+// inputs die (19 KB at dk = 128, so that eight wavefronts share a compute unit):
+// q's rows give way to Kcc^T once the Gram products are in registers, and k's
+// rows and the decays to the masked products and T once Kcc^T is formed.
 template <typename MT, int DK>
 __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     typedef OpBlock<MT, DK> OB;
     constexpr int P = 16 / (int)sizeof(MT);
     constexpr int LDK = DK + P, L16 = 16 + P;
-    __shared__ __attribute__((aligned(16))) MT kr[16 * LDK];
-    __shared__ __attribute__((aligned(16))) MT qr[16 * LDK];
-    __shared__ __attribute__((aligned(16))) MT KCT[DK * L16];
+    constexpr int ROWB = 16 * LDK * (int)sizeof(MT);          // bytes of 16 padded rows
+    constexpr int G2B = (SC + 1) * DK * 4;                    // bytes of the decay sums
+    static_assert(DK * 16 * (int)sizeof(MT) <= ROWB, "Kcc^T fits in q's rows");
+    constexpr int GTB = (4 * 16 * 17 + 16 * 17) * 4;          // bytes of the products and T
+    constexpr int UKB = ROWB + G2B > GTB ? ROWB + G2B : GTB;
+    __shared__ __attribute__((aligned(16))) uint8_t u_k[UKB];          // kr | G2, later Gf | Tf
+    __shared__ __attribute__((aligned(16))) uint8_t u_q[ROWB];         // qr, later KCT
     __shared__ __attribute__((aligned(16))) MT P1rm[16 * L16];
     __shared__ __attribute__((aligned(16))) MT bTT[16 * L16];
-    __shared__ __attribute__((aligned(16))) float G2[(SC + 1) * DK];
     __shared__ float bt[SC];
-    __shared__ float Gf[4][16][17];  // A0, L, P1, P2 (fp32, row-major, masked)
-    __shared__ float Tf[16][17];
+    MT* kr = reinterpret_cast<MT*>(u_k);
+    float* G2 = reinterpret_cast<float*>(u_k + ROWB);
+    MT* qr = reinterpret_cast<MT*>(u_q);
+    MT* KCT = reinterpret_cast<MT*>(u_q);                             // [DK][16], unpadded
+    float (*Gf)[16][17] = reinterpret_cast<float (*)[16][17]>(u_k);  // A0, L, P1, P2 (fp32, masked)
+    float (*Tf)[17] = reinterpret_cast<float (*)[17]>(u_k + 4 * 16 * 17 * 4);
 
     const int lane = threadIdx.x;
     const int s = blockIdx.x;
@@ -276,16 +286,38 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     load_decay<DK>(G2, bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, lane, 64);
     __syncthreads();
 
+    // QK [c][32] = [q_s e^{g_s} | k_s e^{gm_s}], gamma
+    {
+        MT* qk = reinterpret_cast<MT*>(blk + OB::QK);
+        for (int pc = lane; pc < DK * 4; pc += 64) {
+            const int c = pc >> 2, s0 = (pc & 3) * 8;
+            float out[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int s2 = s0 + e;
+                out[e] = s2 < 16 ? to_f32(qr[s2 * LDK + c]) * ex2(G2[(s2 + 1) * DK + c])
+                                 : to_f32(kr[(s2 - 16) * LDK + c]) * ex2(G2[(s2 - 16) * DK + c]);
+            }
+            store8<MT>(qk + c * 32 + s0, out);
+        }
+        float* gam = reinterpret_cast<float*>(blk + OB::GAM);
+        for (int c = lane; c < DK; c += 64) gam[c] = ex2(G2[SC * DK + c]);
+    }
+
     float span = 0.f;
     for (int c = lane; c < DK; c += 64) span = fmaxf(span, -G2[SC * DK + c]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) span = fmaxf(span, __shfl_xor(span, off));
     const bool exact = span > SPAN2_MAX;
+    if (lane == 0) *reinterpret_cast<int*>(blk + OB::FLAG) = exact ? 1 : 0;
 
-    // C x C products
+    // C x C products, kept in registers until k's rows and the decays are dead:
+    // factored, acc[g][r] is element (t = 4 (lane / 16) + r, i = lane % 16);
+    // exact, ex[g][j] is element (t, i) = ((lane + 64 j) / 16, (lane + 64 j) % 16)
+    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    float ex[4][4];
     if (!exact) {
         // (m = t, n = i); A rows: k (A0, L) or q (P1, P2) times e^{h_t - m}; B rows: k times e^{m - h_i}
-        f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
         const int r16 = lane & 15;
         constexpr int KPL = Mma<MT>::KPL, KS = Mma<MT>::K;
 #pragma unroll
@@ -313,17 +345,10 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
             acc[2] = Mma<MT>::mma(aq, bm, acc[2]);  // P1
             acc[3] = Mma<MT>::mma(aq, bg, acc[3]);  // P2
         }
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * (lane >> 4) + r, i = lane & 15;
-                const bool keep = g < 2 ? i < t : i <= t;
-                Gf[g][t][i] = keep ? acc[g][r] : 0.f;
-            }
     } else {
-        for (int pi = lane; pi < 256; pi += 64) {
-            const int t = pi >> 4, i = pi & 15;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int pi = lane + 64 * j, t = pi >> 4, i = pi & 15;
             float a0 = 0.f, l = 0.f, p1 = 0.f, p2 = 0.f;
             if (i <= t) {
                 for (int c = 0; c < DK; ++c) {
@@ -338,7 +363,33 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
                     p2 += qt * ki * ex2(gt - gi);
                 }
             }
-            Gf[0][t][i] = a0; Gf[1][t][i] = l; Gf[2][t][i] = p1; Gf[3][t][i] = p2;
+            ex[0][j] = a0; ex[1][j] = l; ex[2][j] = p1; ex[3][j] = p2;
+        }
+    }
+    __syncthreads();  // q's rows are dead
+
+    // Kcc^T [c][s] = k_s e^{gC - gm_s}
+    for (int x = lane; x < DK * 16; x += 64) {
+        const int c = x >> 4, s2 = x & 15;
+        KCT[c * 16 + s2] = from_f32<MT>(to_f32(kr[s2 * LDK + c]) * ex2(G2[SC * DK + c] - G2[s2 * DK + c]));
+    }
+    __syncthreads();  // k's rows and the decays are dead
+
+    if (!exact) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * (lane >> 4) + r, i = lane & 15;
+                const bool keep = g < 2 ? i < t : i <= t;
+                Gf[g][t][i] = keep ? acc[g][r] : 0.f;
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int pi = lane + 64 * j, t = pi >> 4, i = pi & 15;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) Gf[g][t][i] = ex[g][j];
         }
     }
     __syncthreads();
@@ -349,14 +400,14 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
         float t[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float acc = i == j ? 1.f : 0.f;
+            float a = i == j ? 1.f : 0.f;
             if (i > j) {
                 float sdot = 0.f;
 #pragma unroll
                 for (int kk = 0; kk < i; ++kk) sdot += Gf[0][i][kk] * t[kk];  // t[kk] = 0 for kk < j
-                acc = -bt[i] * sdot;
+                a = -bt[i] * sdot;
             }
-            t[i] = acc;
+            t[i] = a;
         }
         const float bj = bt[j];
 #pragma unroll
@@ -364,11 +415,6 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
             Tf[i][j] = t[i];
             bTT[j * L16 + i] = from_f32<MT>(bj * t[i]);  // (diag(b) T^T)[j][i] = b_j T[i][j]
         }
-    }
-    // Kcc^T [c][s] = k_s e^{gC - gm_s}, P1 row-major
-    for (int x = lane; x < DK * 16; x += 64) {
-        const int c = x >> 4, s2 = x & 15;
-        KCT[c * L16 + s2] = from_f32<MT>(to_f32(kr[s2 * LDK + c]) * ex2(G2[SC * DK + c] - G2[s2 * DK + c]));
     }
     for (int x = lane; x < 256; x += 64) P1rm[(x >> 4) * L16 + (x & 15)] = from_f32<MT>(Gf[2][x >> 4][x & 15]);
     __syncthreads();
@@ -399,32 +445,14 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     // W (m = c, n = t): W^T[c][t] = sum_s Kcc^T[c][s] (b_t T[s][t]); natural store gives W[t][c]
     MT* Wg = reinterpret_cast<MT*>(blk + OB::W);
     for (int cb = 0; cb < DK / 16; ++cb) {
-        f32x4 acc = mma16(KCT + (cb * 16 + (lane & 15)) * L16, bTT + (lane & 15) * L16, zero4(), lane);
-        store_nat<MT>(Wg + cb * 16, DK, acc, lane);
+        f32x4 a = mma16(KCT + (cb * 16 + (lane & 15)) * 16, bTT + (lane & 15) * L16, zero4(), lane);
+        store_nat<MT>(Wg + cb * 16, DK, a, lane);
     }
     // M (m = i, n = t): M^T[i][t] = sum_s P1[i][s] (b_t T[s][t]); natural store gives M[t][i]
     {
-        f32x4 acc = mma16(P1rm + (lane & 15) * L16, bTT + (lane & 15) * L16, zero4(), lane);
-        store_nat<MT>(reinterpret_cast<MT*>(blk + OB::M), 16, acc, lane);
+        f32x4 a = mma16(P1rm + (lane & 15) * L16, bTT + (lane & 15) * L16, zero4(), lane);
+        store_nat<MT>(reinterpret_cast<MT*>(blk + OB::M), 16, a, lane);
     }
-    // QK [c][32] = [q_s e^{g_s} | k_s e^{gm_s}]
-    {
-        MT* qk = reinterpret_cast<MT*>(blk + OB::QK);
-        for (int pc = lane; pc < DK * 4; pc += 64) {
-            const int c = pc >> 2, s0 = (pc & 3) * 8;
-            float out[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s2 = s0 + e;
-                out[e] = s2 < 16 ? to_f32(qr[s2 * LDK + c]) * ex2(G2[(s2 + 1) * DK + c])
-                                 : to_f32(kr[(s2 - 16) * LDK + c]) * ex2(G2[(s2 - 16) * DK + c]);
-            }
-            store8<MT>(qk + c * 32 + s0, out);
-        }
-    }
-    float* gam = reinterpret_cast<float*>(blk + OB::GAM);
-    for (int c = lane; c < DK; c += 64) gam[c] = ex2(G2[SC * DK + c]);
-    if (lane == 0) *reinterpret_cast<int*>(blk + OB::FLAG) = exact ? 1 : 0;
 }
 
 // ==================================================================== scan
