@@ -912,19 +912,19 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
     // ================= backward walk over the sub-chunks
     f32x4 X[CBW][NJB];
     load_state(X, p.xbuf + xrow * (int64_t)DK * DV);
-    for (int sg = ns - 1; sg >= 0; --sg) {
-        const int64_t t0 = sq.t0 + (int64_t)jc * CHB + sg * SC;
-        const int nrow = min(SC, clen - sg * SC);
-        const uint8_t* blk = p.ops + (sbase + sg) * OB::BYTES;
-        // kept E, Y and start state S of this sub-chunk (the loads go out first)
-        f32x4 S[CBW][NJB], Ek[JBW], Yk[JBW];
+    // The kept E, Y and start state S of a sub-chunk, as stored (MT).  Those of the
+    // next sub-chunk are loaded at the end of a step, before its output stores, so
+    // that waiting for them does not also wait for the stores (the counter of
+    // outstanding memory operations drains in order).
+    typedef typename Vec4<MT>::type V4;
+    V4 S[CBW][NJB], Ek[JBW], Yk[JBW];
+    auto load_kept = [&](int s2) {
 #pragma unroll
         for (int a = 0; a < JBW; ++a) {
             const int jb = w + GW * a;
-            Ek[a] = Yk[a] = zero4();
             if (jb < NJB) {
-                Ek[a] = load4<MT>(kE(sg, jb));
-                Yk[a] = load4<MT>(kY(sg, jb));
+                Ek[a] = *reinterpret_cast<const V4*>(kE(s2, jb));
+                Yk[a] = *reinterpret_cast<const V4*>(kY(s2, jb));
             }
         }
 #pragma unroll
@@ -932,8 +932,14 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb) {
                 const int cb = w + GW * a;
-                S[a][jb] = cb < NCB ? load4<MT>(kS(sg, cb, jb)) : zero4();
+                if (cb < NCB) S[a][jb] = *reinterpret_cast<const V4*>(kS(s2, cb, jb));
             }
+    };
+    load_kept(ns - 1);
+    for (int sg = ns - 1; sg >= 0; --sg) {
+        const int64_t t0 = sq.t0 + (int64_t)jc * CHB + sg * SC;
+        const int nrow = min(SC, clen - sg * SC);
+        const uint8_t* blk = p.ops + (sbase + sg) * OB::BYTES;
         const int exact_flag = *reinterpret_cast<const int*>(blk + OB::FLAG);
         lds_barrier();
         commit(true);
@@ -943,8 +949,8 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         for (int a = 0; a < JBW; ++a) {
             const int jb = w + GW * a;
             if (jb < NJB) {
-                store_rm<MT>(sm.Erm + jb * 16, LDV, Ek[a], lane);
-                store_rm<MT>(sm.Yrm + jb * 16, LDV, Yk[a], lane);
+                store_rm<MT>(sm.Erm + jb * 16, LDV, Vec4<MT>::to_f32(Ek[a]), lane);
+                store_rm<MT>(sm.Yrm + jb * 16, LDV, Vec4<MT>::to_f32(Yk[a]), lane);
             }
         }
         lds_barrier();
@@ -1101,7 +1107,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 for (int jb = 0; jb < NJB; ++jb) {
                     X[a][jb] = mmak<MT, 32>(sm.CT + (cb * 16 + r16) * L32, sm.DFT + (jb * 16 + r16) * L32,
                                             gmm * X[a][jb], lane);
-                    ph += X[a][jb] * S[a][jb];
+                    ph += X[a][jb] * Vec4<MT>::to_f32(S[a][jb]);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) ph[r] = row_sum16(ph[r]);
@@ -1117,7 +1123,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb) {
                 const int cb = w + GW * a;
-                if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, S[a][jb], lane);
+                if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, Vec4<MT>::to_f32(S[a][jb]), lane);
             }
         for (int x = tid; x < 16 * DK; x += NT) {
             const int i = x % 16, c = x / 16;
@@ -1153,6 +1159,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         MT* dqg = static_cast<MT*>(p.dq);
         MT* dkg = static_cast<MT*>(p.dk);
         float dla_s[4] = {0.f, 0.f, 0.f, 0.f};
+        float oq[CBW][4], ok[CBW][4], od[CBW][4];
 #pragma unroll
         for (int a = 0; a < CBW; ++a) {
             const int cb = w + GW * a;
@@ -1182,10 +1189,8 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 av[r] = kt * dk + 2.f * b * kt * gs;
                 au[r] = qt * dq;
                 mv[a][r] = b * kt * vd;  // reuse: the b k vds term
-                if (t < nrow) {
-                    dqg[((t0 + t) * p.H + h) * (int64_t)DK + c] = from_f32<MT>(dq);
-                    dkg[((t0 + t) * p.H + h) * (int64_t)DK + c] = from_f32<MT>(dk);
-                }
+                oq[a][r] = dq;
+                ok[a][r] = dk;
             }
             // phi_t = phi_{-1} + sum_{j<=t} av_j - sum_{j<t} au_j, over the 16 tokens of column c
             float ia[4], eu[4];
@@ -1209,10 +1214,26 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             const float ph0 = sm.phi0[c];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g4 + r;
                 const float dl = ph0 + pa + ia[r] - (pu + eu[r]) - mv[a][r];
                 if (p.scalar) dla_s[r] += dl;
-                else if (t < nrow) p.dla[((t0 + t) * p.H + h) * (int64_t)DK + c] = dl;
+                od[a][r] = dl;
+            }
+        }
+        if (sg > 0) load_kept(sg - 1);
+#pragma unroll
+        for (int a = 0; a < CBW; ++a) {
+            const int cb = w + GW * a;
+            if (cb >= NCB) continue;
+            const int c = cb * 16 + r16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                if (t < nrow) {
+                    const int64_t o = ((t0 + t) * p.H + h) * (int64_t)DK + c;
+                    dqg[o] = from_f32<MT>(oq[a][r]);
+                    dkg[o] = from_f32<MT>(ok[a][r]);
+                    if (!p.scalar) p.dla[o] = od[a][r];
+                }
             }
         }
         if (p.scalar) {
