@@ -212,7 +212,7 @@ __device__ __forceinline__ void load_rows(MT* z, int ld, const MT* g, int64_t t0
 // G2[i][c] = log2 e * sum_{j < i} log a_j (i = 0..16) and beta.  The decays of the 16
 // tokens arrive in one round of 16-byte loads into G2's rows 1..16, then each
 // channel's prefix sum runs in LDS.  Contains a barrier: every thread calls it.
-template <int DK>
+template <int DK, int G2L>
 __device__ __forceinline__ void load_decay(float* G2, float* bt, const float* la, const float* beta, int64_t t0,
                                            int H, int h, int nrow, int scalar, int tid, int nthr) {
     constexpr int Q = DK / 4;  // 16-byte pieces per token
@@ -227,7 +227,7 @@ __device__ __forceinline__ void load_decay(float* G2, float* bt, const float* la
                 x = *reinterpret_cast<const f32x4*>(la + ((t0 + i) * H + h) * (int64_t)DK + c4);
             }
         }
-        *reinterpret_cast<f32x4*>(G2 + (i + 1) * DK + c4) = x * LOG2E;
+        *reinterpret_cast<f32x4*>(G2 + (i + 1) * G2L + c4) = x * LOG2E;
     }
     for (int i = tid; i < SC; i += nthr) bt[i] = i < nrow ? beta[(t0 + i) * H + h] : 0.f;
     __syncthreads();
@@ -236,8 +236,8 @@ __device__ __forceinline__ void load_decay(float* G2, float* bt, const float* la
         G2[c] = 0.f;
 #pragma unroll
         for (int i = 1; i <= SC; ++i) {
-            s += G2[i * DK + c];
-            G2[i * DK + c] = s;
+            s += G2[i * G2L + c];
+            G2[i * G2L + c] = s;
         }
     }
 }
@@ -253,7 +253,8 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     constexpr int P = 16 / (int)sizeof(MT);
     constexpr int LDK = DK + P, L16 = 16 + P;
     constexpr int ROWB = 16 * LDK * (int)sizeof(MT);          // bytes of 16 padded rows
-    constexpr int G2B = (SC + 1) * DK * 4;                    // bytes of the decay sums
+    constexpr int G2L = DK + 4;                               // decay-sum row stride (no bank conflicts)
+    constexpr int G2B = (SC + 1) * G2L * 4;                   // bytes of the decay sums
     static_assert(DK * 16 * (int)sizeof(MT) <= ROWB, "Kcc^T fits in q's rows");
     constexpr int GTB = (4 * 16 * 17 + 16 * 17) * 4;          // bytes of the products and T
     constexpr int UKB = ROWB + G2B > GTB ? ROWB + G2B : GTB;
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
 
     load_rows<MT, DK>(kr, LDK, static_cast<const MT*>(p.k), t0, p.H, h, nrow, lane, 64);
     load_rows<MT, DK>(qr, LDK, static_cast<const MT*>(p.q), t0, p.H, h, nrow, lane, 64);
-    load_decay<DK>(G2, bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, lane, 64);
+    load_decay<DK, G2L>(G2, bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, lane, 64);
     __syncthreads();
 
     // QK [c][32] = [q_s e^{g_s} | k_s e^{gm_s}], gamma
@@ -295,17 +296,17 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int s2 = s0 + e;
-                out[e] = s2 < 16 ? to_f32(qr[s2 * LDK + c]) * ex2(G2[(s2 + 1) * DK + c])
-                                 : to_f32(kr[(s2 - 16) * LDK + c]) * ex2(G2[(s2 - 16) * DK + c]);
+                out[e] = s2 < 16 ? to_f32(qr[s2 * LDK + c]) * ex2(G2[(s2 + 1) * G2L + c])
+                                 : to_f32(kr[(s2 - 16) * LDK + c]) * ex2(G2[(s2 - 16) * G2L + c]);
             }
             store8<MT>(qk + c * 32 + s0, out);
         }
         float* gam = reinterpret_cast<float*>(blk + OB::GAM);
-        for (int c = lane; c < DK; c += 64) gam[c] = ex2(G2[SC * DK + c]);
+        for (int c = lane; c < DK; c += 64) gam[c] = ex2(G2[SC * G2L + c]);
     }
 
     float span = 0.f;
-    for (int c = lane; c < DK; c += 64) span = fmaxf(span, -G2[SC * DK + c]);
+    for (int c = lane; c < DK; c += 64) span = fmaxf(span, -G2[SC * G2L + c]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) span = fmaxf(span, __shfl_xor(span, off));
     const bool exact = span > SPAN2_MAX;
@@ -328,11 +329,11 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < KPL; ++e) {
                 const int c = c0 + e;
-                const float m2 = 0.5f * G2[SC * DK + c];
-                fk[e] = ex2(G2[r16 * DK + c] - m2);          // e^{gm_t - m}
-                fq[e] = ex2(G2[(r16 + 1) * DK + c] - m2);    // e^{g_t - m}
-                fm[e] = ex2(m2 - G2[r16 * DK + c]);          // e^{m - gm_i}
-                fg[e] = ex2(m2 - G2[(r16 + 1) * DK + c]);    // e^{m - g_i}
+                const float m2 = 0.5f * G2[SC * G2L + c];
+                fk[e] = ex2(G2[r16 * G2L + c] - m2);          // e^{gm_t - m}
+                fq[e] = ex2(G2[(r16 + 1) * G2L + c] - m2);    // e^{g_t - m}
+                fm[e] = ex2(m2 - G2[r16 * G2L + c]);          // e^{m - gm_i}
+                fg[e] = ex2(m2 - G2[(r16 + 1) * G2L + c]);    // e^{m - g_i}
             }
             const typename Mma<MT>::frag kx = Mma<MT>::loadr(kr + r16 * LDK + kb, lane);
             const typename Mma<MT>::frag qx = Mma<MT>::loadr(qr + r16 * LDK + kb, lane);
@@ -353,8 +354,8 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
             if (i <= t) {
                 for (int c = 0; c < DK; ++c) {
                     const float kt = to_f32(kr[t * LDK + c]), qt = to_f32(qr[t * LDK + c]), ki = to_f32(kr[i * LDK + c]);
-                    const float gmt = G2[t * DK + c], gt = G2[(t + 1) * DK + c];
-                    const float gmi = G2[i * DK + c], gi = G2[(i + 1) * DK + c];
+                    const float gmt = G2[t * G2L + c], gt = G2[(t + 1) * G2L + c];
+                    const float gmi = G2[i * G2L + c], gi = G2[(i + 1) * G2L + c];
                     if (i < t) {
                         a0 += kt * ki * ex2(gmt - gmi);
                         l += kt * ki * ex2(gmt - gi);
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     // Kcc^T [c][s] = k_s e^{gC - gm_s}
     for (int x = lane; x < DK * 16; x += 64) {
         const int c = x >> 4, s2 = x & 15;
-        KCT[c * 16 + s2] = from_f32<MT>(to_f32(kr[s2 * LDK + c]) * ex2(G2[SC * DK + c] - G2[s2 * DK + c]));
+        KCT[c * 16 + s2] = from_f32<MT>(to_f32(kr[s2 * LDK + c]) * ex2(G2[SC * G2L + c] - G2[s2 * G2L + c]));
     }
     __syncthreads();  // k's rows and the decays are dead
 
@@ -642,7 +643,10 @@ struct GradSmem {
     MT Y0T[DV * L16];         // Y0^T, then dE^T
     MT Erm[16 * LDV], Yrm[16 * LDV], Grm[16 * LDV];
     MT MQ[16 * L32], MG[16 * L32], MV[16 * L32], MY[16 * L32];
-    float G2[(SC + 1) * DK];
+    // decay sums, rows padded by 4 so that 16 lanes reading one channel of 16
+    // tokens hit 16 different banks
+    static constexpr int G2L = DK + 4;
+    float G2[(SC + 1) * G2L];
     float bt[SC];
     float phi0[DK];
     float red[3][GW][16];     // per-wave partials: R.V, G.Y, dlog_a (scalar gate)
@@ -660,10 +664,10 @@ __device__ __attribute__((noinline)) void exact_terms(const SM& sm, int c, int g
     for (int r = 0; r < 4; ++r) {
         const int t = 4 * g4 + r;
         float aq = 0.f, ag = 0.f, av = 0.f, ay = 0.f;
-        const float gmt = sm.G2[t * DK + c], gt = sm.G2[(t + 1) * DK + c];
+        const float gmt = sm.G2[t * SM::G2L + c], gt = sm.G2[(t + 1) * SM::G2L + c];
         for (int i = 0; i < 16; ++i) {
             const float ki = to_f32(sm.kr[i * LDK + c]), qi = to_f32(sm.qr[i * LDK + c]);
-            const float gmi = sm.G2[i * DK + c], gi = sm.G2[(i + 1) * DK + c];
+            const float gmi = sm.G2[i * SM::G2L + c], gi = sm.G2[(i + 1) * SM::G2L + c];
             aq += to_f32(sm.MQ[t * L32 + i]) * ki * ex2n(gt - gmi) + to_f32(sm.MQ[t * L32 + 16 + i]) * ki * ex2n(gt - gi);
             ag += to_f32(sm.MG[t * L32 + i]) * ki * ex2n(gmt - gmi) + to_f32(sm.MG[t * L32 + 16 + i]) * ki * ex2n(gmt - gi);
             av += to_f32(sm.MV[t * L32 + i]) * qi * ex2n(gi - gt) + to_f32(sm.MV[t * L32 + 16 + i]) * ki * ex2n(gmi - gt);
@@ -798,7 +802,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             else if (pc.kind == 2) *reinterpret_cast<VT*>(sm.qr + pc.i * LDK + pc.e) = pf[a];
             else if (pc.kind == 3) *reinterpret_cast<VT*>(sm.dor + pc.i * LDV + pc.e) = pf[a];
             else if (pc.kind == 4)
-                *reinterpret_cast<f32x4*>(sm.G2 + (pc.i + 1) * DK + pc.e) = __builtin_bit_cast(f32x4, pf[a]) * LOG2E;
+                *reinterpret_cast<f32x4*>(sm.G2 + (pc.i + 1) * SM::G2L + pc.e) = __builtin_bit_cast(f32x4, pf[a]) * LOG2E;
             else if (pc.kind == 5)
                 *reinterpret_cast<VT*>(&sm.mats[mat_of(bwd, pc.i)][(pc.e / 16) * L16 + pc.e % 16]) = pf[a];
         }
@@ -811,8 +815,8 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             sm.G2[c] = 0.f;
 #pragma unroll
             for (int i = 1; i <= SC; ++i) {
-                s2 += sm.G2[i * DK + c];
-                sm.G2[i * DK + c] = s2;
+                s2 += sm.G2[i * SM::G2L + c];
+                sm.G2[i * SM::G2L + c] = s2;
             }
         }
     };
@@ -844,7 +848,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             // ---- Kb rows, (bV)^T, [Kcc^T | Ktc^T]
             for (int x = tid; x < 16 * DK; x += NT) {
                 const int t = x / DK, c = x % DK;
-                sm.GA[t * LDK + c] = from_f32<MT>(to_f32(sm.kr[t * LDK + c]) * ex2(sm.G2[t * DK + c]));
+                sm.GA[t * LDK + c] = from_f32<MT>(to_f32(sm.kr[t * LDK + c]) * ex2(sm.G2[t * SM::G2L + c]));
             }
             for (int x = tid; x < 16 * DV; x += NT) {
                 const int i = x % 16, j = x / 16;
@@ -853,9 +857,9 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             if (!last) {
                 for (int x = tid; x < 16 * DK; x += NT) {
                     const int s2 = x % 16, c = x / 16;
-                    const float kv = to_f32(sm.kr[s2 * LDK + c]), gc = sm.G2[SC * DK + c];
-                    sm.CT[c * L32 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[s2 * DK + c]));
-                    sm.CT[c * L32 + 16 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[(s2 + 1) * DK + c]));
+                    const float kv = to_f32(sm.kr[s2 * LDK + c]), gc = sm.G2[SC * SM::G2L + c];
+                    sm.CT[c * L32 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[s2 * SM::G2L + c]));
+                    sm.CT[c * L32 + 16 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[(s2 + 1) * SM::G2L + c]));
                 }
             }
             lds_barrier();
@@ -898,7 +902,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                     if (cb < NCB) {
                         f32x4 gmm;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) gmm[r] = ex2(sm.G2[SC * DK + cb * 16 + 4 * g4 + r]);
+                        for (int r = 0; r < 4; ++r) gmm[r] = ex2(sm.G2[SC * SM::G2L + cb * 16 + 4 * g4 + r]);
 #pragma unroll
                         for (int jb = 0; jb < NJB; ++jb)
                             S[a][jb] = mmak<MT, 32>(sm.CT + (cb * 16 + r16) * L32, sm.EBVT + (jb * 16 + r16) * L32,
@@ -971,14 +975,14 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         }
         for (int x = tid; x < 16 * DK; x += NT) {
             const int t = x / DK, c = x % DK;
-            const float kv = to_f32(sm.kr[t * LDK + c]), gc = sm.G2[SC * DK + c];
-            sm.GA[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[t * DK + c]));
-            sm.GB[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[(t + 1) * DK + c]));
+            const float kv = to_f32(sm.kr[t * LDK + c]), gc = sm.G2[SC * SM::G2L + c];
+            sm.GA[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[t * SM::G2L + c]));
+            sm.GB[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[(t + 1) * SM::G2L + c]));
         }
         for (int x = tid; x < 16 * DK; x += NT) {
             const int s2 = x % 16, c = x / 16;
-            sm.CT[c * L32 + s2] = from_f32<MT>(to_f32(sm.qr[s2 * LDK + c]) * ex2(sm.G2[(s2 + 1) * DK + c]));
-            sm.CT[c * L32 + 16 + s2] = from_f32<MT>(to_f32(sm.kr[s2 * LDK + c]) * ex2(sm.G2[s2 * DK + c]));
+            sm.CT[c * L32 + s2] = from_f32<MT>(to_f32(sm.qr[s2 * LDK + c]) * ex2(sm.G2[(s2 + 1) * SM::G2L + c]));
+            sm.CT[c * L32 + 16 + s2] = from_f32<MT>(to_f32(sm.kr[s2 * LDK + c]) * ex2(sm.G2[s2 * SM::G2L + c]));
         }
         lds_barrier();
         // ---- dE = Kcc X + P1^T dO  (m = t, n = j) -> dE^T
@@ -1101,7 +1105,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             if (cb < NCB) {
                 f32x4 gmm;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) gmm[r] = ex2(sm.G2[SC * DK + cb * 16 + 4 * g4 + r]);
+                for (int r = 0; r < 4; ++r) gmm[r] = ex2(sm.G2[SC * SM::G2L + cb * 16 + 4 * g4 + r]);
                 f32x4 ph = zero4();
 #pragma unroll
                 for (int jb = 0; jb < NJB; ++jb) {
@@ -1127,9 +1131,9 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             }
         for (int x = tid; x < 16 * DK; x += NT) {
             const int i = x % 16, c = x / 16;
-            const float kv = to_f32(sm.kr[i * LDK + c]), m2 = 0.5f * sm.G2[SC * DK + c];
-            sm.CT[c * L32 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[i * DK + c]));
-            sm.CT[c * L32 + 16 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[(i + 1) * DK + c]));
+            const float kv = to_f32(sm.kr[i * LDK + c]), m2 = 0.5f * sm.G2[SC * SM::G2L + c];
+            sm.CT[c * L32 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[i * SM::G2L + c]));
+            sm.CT[c * L32 + 16 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[(i + 1) * SM::G2L + c]));
         }
         lds_barrier();
         const bool exact = sm.exact != 0;
@@ -1150,9 +1154,9 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         lds_barrier();
         for (int x = tid; x < 16 * DK; x += NT) {
             const int i = x % 16, c = x / 16;
-            const float m2 = 0.5f * sm.G2[SC * DK + c];
-            sm.CT[c * L32 + i] = from_f32<MT>(to_f32(sm.qr[i * LDK + c]) * ex2(sm.G2[(i + 1) * DK + c] - m2));
-            sm.CT[c * L32 + 16 + i] = from_f32<MT>(to_f32(sm.kr[i * LDK + c]) * ex2(sm.G2[i * DK + c] - m2));
+            const float m2 = 0.5f * sm.G2[SC * SM::G2L + c];
+            sm.CT[c * L32 + i] = from_f32<MT>(to_f32(sm.qr[i * LDK + c]) * ex2(sm.G2[(i + 1) * SM::G2L + c] - m2));
+            sm.CT[c * L32 + 16 + i] = from_f32<MT>(to_f32(sm.kr[i * LDK + c]) * ex2(sm.G2[i * SM::G2L + c] - m2));
         }
         lds_barrier();
         // ---- masked products, combination, outputs  (m = t, n = c)
@@ -1171,12 +1175,12 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             } else {
                 exact_terms<MT, DK>(sm, c, g4, mq[a], mg[a], mv[a], my[a]);
             }
-            const float gc = sm.G2[SC * DK + c], m2 = 0.5f * gc;
+            const float gc = sm.G2[SC * SM::G2L + c], m2 = 0.5f * gc;
             float av[4], au[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * g4 + r;
-                const float gmt = sm.G2[t * DK + c], gt = sm.G2[(t + 1) * DK + c];
+                const float gmt = sm.G2[t * SM::G2L + c], gt = sm.G2[(t + 1) * SM::G2L + c];
                 const float fq = exact ? 1.f : ex2(gt - m2), fg = exact ? 1.f : ex2(gmt - m2);
                 const float fv = exact ? 1.f : ex2(m2 - gt), fy = exact ? 1.f : ex2(m2 - gmt);
                 const float dq = ex2(gt) * dqs[a][r] + fq * mq[a][r];
