@@ -922,7 +922,9 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
     // outstanding memory operations drains in order).
     typedef typename Vec4<MT>::type V4;
     V4 S[CBW][NJB], Ek[JBW], Yk[JBW];
+    int kflag = 0;
     auto load_kept = [&](int s2) {
+        kflag = *reinterpret_cast<const int*>(p.ops + (sbase + s2) * OB::BYTES + OB::FLAG);
 #pragma unroll
         for (int a = 0; a < JBW; ++a) {
             const int jb = w + GW * a;
@@ -940,15 +942,18 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             }
     };
     load_kept(ns - 1);
+    // a step's inputs are placed in LDS at the end of the step before (here for the
+    // first), after that step's last LDS read and before its output stores
+    lds_barrier();
+    commit(true);
+    if (ns > 1) issue(ns - 2, true);
     for (int sg = ns - 1; sg >= 0; --sg) {
         const int64_t t0 = sq.t0 + (int64_t)jc * CHB + sg * SC;
         const int nrow = min(SC, clen - sg * SC);
         const uint8_t* blk = p.ops + (sbase + sg) * OB::BYTES;
-        const int exact_flag = *reinterpret_cast<const int*>(blk + OB::FLAG);
         lds_barrier();
-        commit(true);
-        if (sg > 0) issue(sg - 1, true);
-        if (tid == 0) sm.exact = exact_flag;
+        prefix_decay();
+        if (tid == 0) sm.exact = kflag;
 #pragma unroll
         for (int a = 0; a < JBW; ++a) {
             const int jb = w + GW * a;
@@ -957,8 +962,6 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 store_rm<MT>(sm.Yrm + jb * 16, LDV, Vec4<MT>::to_f32(Yk[a]), lane);
             }
         }
-        lds_barrier();
-        prefix_decay();
         lds_barrier();
         // ================= gradient of sub-chunk sg (start state S, end derivative X)
         // ---- X^T; dO^T; Kcc, Ktc rows; [Qb^T | Kb^T]
@@ -1223,23 +1226,6 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 od[a][r] = dl;
             }
         }
-        if (sg > 0) load_kept(sg - 1);
-#pragma unroll
-        for (int a = 0; a < CBW; ++a) {
-            const int cb = w + GW * a;
-            if (cb >= NCB) continue;
-            const int c = cb * 16 + r16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g4 + r;
-                if (t < nrow) {
-                    const int64_t o = ((t0 + t) * p.H + h) * (int64_t)DK + c;
-                    dqg[o] = from_f32<MT>(oq[a][r]);
-                    dkg[o] = from_f32<MT>(ok[a][r]);
-                    if (!p.scalar) p.dla[o] = od[a][r];
-                }
-            }
-        }
         if (p.scalar) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) dla_s[r] = row_sum16(dla_s[r]);
@@ -1252,6 +1238,30 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
 #pragma unroll
                 for (int u = 0; u < GW; ++u) dl += sm.red[2][u][tid];
                 p.dla[(t0 + tid) * p.H + h] = dl;
+            }
+        }
+        // this step's dead kept slot takes the stores of rows past the end, so that
+        // every path issues the same stores (and a later wait can count them)
+        MT* dummy = kS(sg, 0, 0);
+        if (sg > 0) {
+            lds_barrier();
+            commit(true);
+            if (sg > 1) issue(sg - 2, true);
+            load_kept(sg - 1);
+        }
+#pragma unroll
+        for (int a = 0; a < CBW; ++a) {
+            const int cb = w + GW * a;
+            if (cb >= NCB) continue;
+            const int c = cb * 16 + r16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g4 + r;
+                const bool live = t < nrow;
+                const int64_t o = ((t0 + (live ? t : 0)) * p.H + h) * (int64_t)DK + c;
+                *(live ? dqg + o : dummy) = from_f32<MT>(oq[a][r]);
+                *(live ? dkg + o : dummy) = from_f32<MT>(ok[a][r]);
+                *(live && !p.scalar ? p.dla + o : reinterpret_cast<float*>(dummy)) = od[a][r];
             }
         }
     }
