@@ -821,6 +821,14 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         }
     };
 
+    // The kept E, Y and start state S of a sub-chunk, as stored (MT).  The forward
+    // walk's last step leaves those of the last sub-chunk here; the others are
+    // loaded at the end of the backward step before, ahead of its output stores,
+    // so that waiting for them does not also wait for the stores (the counter of
+    // outstanding memory operations drains in order).
+    typedef typename Vec4<MT>::type V4;
+    V4 Sk[CBW][NJB], Ek[JBW], Yk[JBW];
+
     // ================= forward walk: start state, E and Y of every sub-chunk
     {
         f32x4 S[CBW][NJB];
@@ -839,7 +847,8 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                     const int cb = w + GW * a;
                     if (cb < NCB) {
                         store_nat<MT>(sm.SB + jb * 16 * LDK + cb * 16, LDK, S[a][jb], lane);
-                        store4<MT>(kS(sf, cb, jb), S[a][jb]);
+                        if (last) Sk[a][jb] = Vec4<MT>::from_f32(S[a][jb]);
+                        else store4<MT>(kS(sf, cb, jb), S[a][jb]);
                     }
                 }
             lds_barrier();
@@ -883,7 +892,8 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 if (jb < NJB) {
                     const f32x4 e = -mmak<MT, 16>(sm.mats[MAT_TB] + r16 * L16, sm.Y0T + (jb * 16 + r16) * L16, zero4(), lane);
                     store_nat<MT>(sm.EBVT + jb * 16 * L32, L32, e, lane);
-                    store4<MT>(kE(sf, jb), e);
+                    if (last) Ek[a] = Vec4<MT>::from_f32(e);
+                    else store4<MT>(kE(sf, jb), e);
                 }
             }
             lds_barrier();
@@ -891,9 +901,11 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
 #pragma unroll
             for (int a = 0; a < JBW; ++a) {
                 const int jb = w + GW * a;
-                if (jb < NJB)
-                    store4<MT>(kY(sf, jb), mmak<MT, 16>(sm.mats[MAT_A0] + r16 * L16, sm.EBVT + (jb * 16 + r16) * L32,
-                                                         Y0[a], lane));
+                if (jb < NJB) {
+                    const f32x4 y = mmak<MT, 16>(sm.mats[MAT_A0] + r16 * L16, sm.EBVT + (jb * 16 + r16) * L32, Y0[a], lane);
+                    if (last) Yk[a] = Vec4<MT>::from_f32(y);
+                    else store4<MT>(kY(sf, jb), y);
+                }
             }
             if (!last) {
 #pragma unroll
@@ -916,13 +928,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
     // ================= backward walk over the sub-chunks
     f32x4 X[CBW][NJB];
     load_state(X, p.xbuf + xrow * (int64_t)DK * DV);
-    // The kept E, Y and start state S of a sub-chunk, as stored (MT).  Those of the
-    // next sub-chunk are loaded at the end of a step, before its output stores, so
-    // that waiting for them does not also wait for the stores (the counter of
-    // outstanding memory operations drains in order).
-    typedef typename Vec4<MT>::type V4;
-    V4 S[CBW][NJB], Ek[JBW], Yk[JBW];
-    int kflag = 0;
+    int kflag = *reinterpret_cast<const int*>(p.ops + (sbase + ns - 1) * OB::BYTES + OB::FLAG);
     auto load_kept = [&](int s2) {
         kflag = *reinterpret_cast<const int*>(p.ops + (sbase + s2) * OB::BYTES + OB::FLAG);
 #pragma unroll
@@ -938,10 +944,9 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb) {
                 const int cb = w + GW * a;
-                if (cb < NCB) S[a][jb] = *reinterpret_cast<const V4*>(kS(s2, cb, jb));
+                if (cb < NCB) Sk[a][jb] = *reinterpret_cast<const V4*>(kS(s2, cb, jb));
             }
     };
-    load_kept(ns - 1);
     // a step's inputs are placed in LDS at the end of the step before (here for the
     // first), after that step's last LDS read and before its output stores
     lds_barrier();
@@ -1114,7 +1119,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 for (int jb = 0; jb < NJB; ++jb) {
                     X[a][jb] = mmak<MT, 32>(sm.CT + (cb * 16 + r16) * L32, sm.DFT + (jb * 16 + r16) * L32,
                                             gmm * X[a][jb], lane);
-                    ph += X[a][jb] * Vec4<MT>::to_f32(S[a][jb]);
+                    ph += X[a][jb] * Vec4<MT>::to_f32(Sk[a][jb]);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) ph[r] = row_sum16(ph[r]);
@@ -1130,7 +1135,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
 #pragma unroll
             for (int jb = 0; jb < NJB; ++jb) {
                 const int cb = w + GW * a;
-                if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, Vec4<MT>::to_f32(S[a][jb]), lane);
+                if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, Vec4<MT>::to_f32(Sk[a][jb]), lane);
             }
         for (int x = tid; x < 16 * DK; x += NT) {
             const int i = x % 16, c = x / 16;
