@@ -125,6 +125,8 @@ __device__ __forceinline__ void store8(MT* dst, const float* x) {
     }
 }
 
+template <bool B> struct BoolC { static constexpr bool value = B; };
+
 // ------------------------------------------------------------ sequences
 struct SeqSpan {
     int64_t t0;
@@ -829,16 +831,21 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
     typedef typename Vec4<MT>::type V4;
     V4 Sk[CBW][NJB], Ek[JBW], Yk[JBW];
 
+    // The state derivative at the chunk end: its loads go out during the forward
+    // walk's last step (peeled, so that they take the registers of the state, which
+    // that step no longer updates) and it is brought into tile order after the walk,
+    // as load_state_tile does.
+    f32x4 X[CBW][NJB];
     // ================= forward walk: start state, E and Y of every sub-chunk
     {
         f32x4 S[CBW][NJB];
         issue(0, false);
         load_state(S, s_start);
-        for (int sf = 0; sf < ns; ++sf) {
-            const bool last = sf == ns - 1;
+        auto fwd_step = [&](int sf, auto lastc) {
+            constexpr bool last = decltype(lastc)::value;
             lds_barrier();
             commit(false);
-            if (!last) issue(sf + 1, false);
+            if constexpr (!last) issue(sf + 1, false);
             else issue(ns - 1, true);  // the backward walk starts at the last sub-chunk
 #pragma unroll
             for (int a = 0; a < CBW; ++a)
@@ -847,10 +854,23 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                     const int cb = w + GW * a;
                     if (cb < NCB) {
                         store_nat<MT>(sm.SB + jb * 16 * LDK + cb * 16, LDK, S[a][jb], lane);
-                        if (last) Sk[a][jb] = Vec4<MT>::from_f32(S[a][jb]);
+                        if constexpr (last) Sk[a][jb] = Vec4<MT>::from_f32(S[a][jb]);
                         else store4<MT>(kS(sf, cb, jb), S[a][jb]);
                     }
                 }
+            if constexpr (last) {
+                const float* xsrc = p.xbuf + xrow * (int64_t)DK * DV;
+                const int row = 4 * (lane >> 4) + (lane & 3), col = 4 * ((lane & 15) >> 2);
+#pragma unroll
+                for (int a = 0; a < CBW; ++a)
+#pragma unroll
+                    for (int jb = 0; jb < NJB; ++jb) {
+                        const int cb = w + GW * a;
+                        X[a][jb] = zero4();
+                        if (cb < NCB)
+                            X[a][jb] = *reinterpret_cast<const f32x4*>(xsrc + (int64_t)(cb * 16 + row) * DV + jb * 16 + col);
+                    }
+            }
             lds_barrier();
             prefix_decay();
             lds_barrier();
@@ -863,7 +883,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 const int i = x % 16, j = x / 16;
                 sm.EBVT[j * L32 + 16 + i] = from_f32<MT>(sm.bt[i] * to_f32(sm.vr[i * LDV + j]));
             }
-            if (!last) {
+            if constexpr (!last) {
                 for (int x = tid; x < 16 * DK; x += NT) {
                     const int s2 = x % 16, c = x / 16;
                     const float kv = to_f32(sm.kr[s2 * LDK + c]), gc = sm.G2[SC * SM::G2L + c];
@@ -892,7 +912,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 if (jb < NJB) {
                     const f32x4 e = -mmak<MT, 16>(sm.mats[MAT_TB] + r16 * L16, sm.Y0T + (jb * 16 + r16) * L16, zero4(), lane);
                     store_nat<MT>(sm.EBVT + jb * 16 * L32, L32, e, lane);
-                    if (last) Ek[a] = Vec4<MT>::from_f32(e);
+                    if constexpr (last) Ek[a] = Vec4<MT>::from_f32(e);
                     else store4<MT>(kE(sf, jb), e);
                 }
             }
@@ -903,11 +923,11 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 const int jb = w + GW * a;
                 if (jb < NJB) {
                     const f32x4 y = mmak<MT, 16>(sm.mats[MAT_A0] + r16 * L16, sm.EBVT + (jb * 16 + r16) * L32, Y0[a], lane);
-                    if (last) Yk[a] = Vec4<MT>::from_f32(y);
+                    if constexpr (last) Yk[a] = Vec4<MT>::from_f32(y);
                     else store4<MT>(kY(sf, jb), y);
                 }
             }
-            if (!last) {
+            if constexpr (!last) {
 #pragma unroll
                 for (int a = 0; a < CBW; ++a) {
                     const int cb = w + GW * a;
@@ -922,12 +942,17 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                     }
                 }
             }
-        }
+        };
+        for (int sf = 0; sf < ns - 1; ++sf) fwd_step(sf, BoolC<false>{});
+        fwd_step(ns - 1, BoolC<true>{});
     }
 
     // ================= backward walk over the sub-chunks
-    f32x4 X[CBW][NJB];
-    load_state(X, p.xbuf + xrow * (int64_t)DK * DV);
+#pragma unroll
+    for (int a = 0; a < CBW; ++a)
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+            X[a][jb] = __builtin_bit_cast(f32x4, quad_transpose(__builtin_bit_cast(i32x4, X[a][jb]), lane));
     int kflag = *reinterpret_cast<const int*>(p.ops + (sbase + ns - 1) * OB::BYTES + OB::FLAG);
     auto load_kept = [&](int s2) {
         kflag = *reinterpret_cast<const int*>(p.ops + (sbase + s2) * OB::BYTES + OB::FLAG);
