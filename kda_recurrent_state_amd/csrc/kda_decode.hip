@@ -57,26 +57,31 @@ kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     const float* Sp = S_in + head * (int64_t)(DK * DV);
     float* So = S_out + head * (int64_t)(DK * DV);
 
-    // 1. start streaming the state tile: RPT 16-byte loads in flight per thread
+    // 1. the token's vectors first (their loads then complete ahead of the state's,
+    //    the counter of outstanding loads draining in order), then the state tile:
+    //    RPT 16-byte loads in flight per thread
+    static_assert(DK <= Sh::NT && DV <= Sh::NT, "one vector element per thread");
+    const int cc = tid < DK ? tid : 0, jj = tid < DV ? tid : 0;
+    float b = beta[head];
+    float la = SCALAR ? log_a[head] : log_a[head * DK + cc];
+    const T qv = q[head * DK + cc], kv = k[head * DK + cc], vv0 = v[head * DV + jj];
     f32x4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + (rg + RG * i) * DV + 4 * cg));
 
     // 2. per-token vectors
-    float b = beta[head];
     if (pro.beta_logits) b = 1.f / (1.f + __expf(-b));
-    for (int c = tid; c < DK; c += Sh::NT) {
-        float la = SCALAR ? log_a[head] : log_a[head * DK + c];
+    if (tid < DK) {
         if (pro.log_a_raw) la = fmaxf(-(fmaxf(la, 0.f) + log1pf(__expf(-fabsf(la)))), pro.log_a_min);
         const float a = __expf(la);
-        const float qc = to_f32(q[head * DK + c]);
-        s_k[c] = to_f32(k[head * DK + c]);
-        s_a[c] = a;
-        s_q[c] = qc;
-        s_qa[c] = qc * a;
+        const float qc = to_f32(qv);
+        s_k[tid] = to_f32(kv);
+        s_a[tid] = a;
+        s_q[tid] = qc;
+        s_qa[tid] = qc * a;
     }
-    for (int j = tid; j < DV; j += Sh::NT) s_v[j] = to_f32(v[head * DV + j]);
+    if (tid < DV) s_v[tid] = to_f32(vv0);
     __syncthreads();
 
     // q.a.k and q.k for the output, and the key's scale (wave 0)
