@@ -560,7 +560,7 @@ __global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV, 
         }
     };
     // One step of the walk, sub-chunk s: on entry LDS buffer s & 1 holds its
-    // operators and register set RS holds those of s - 1 (fetched two steps ago).
+    // operators and register set cur holds those of s - 1 (fetched two steps ago).
     auto step = [&](int s, VT (&cur)[NP], VT (&nxt)[NP]) {
         const int b = s & 1;
         // derivative at the end of a 64-token chunk
@@ -735,7 +735,8 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
     };
     // A step's inputs (rows of k, v and, walking backwards, q and dO; the decays;
     // the step's 16 x 16 matrices) are fetched into registers one step ahead and
-    // placed in LDS at the start of the step.  Pieces of 16 bytes, numbered
+    // placed in LDS at the start of the step (walking backwards: at the end of the
+    // step before, after its last LDS read).  Pieces of 16 bytes, numbered
     // [k | v | q | dO | decays | matrices], thread tid holding tid + NT a.
     typedef typename V16<MT>::type VT;
     constexpr int PER = 16 / (int)sizeof(MT);
@@ -980,7 +981,6 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
     for (int sg = ns - 1; sg >= 0; --sg) {
         const int64_t t0 = sq.t0 + (int64_t)jc * CHB + sg * SC;
         const int nrow = min(SC, clen - sg * SC);
-        const uint8_t* blk = p.ops + (sbase + sg) * OB::BYTES;
         lds_barrier();
         prefix_decay();
         if (tid == 0) sm.exact = kflag;
