@@ -196,53 +196,76 @@ struct BwdParams {
     int32_t split;
 };
 
-// Loads a sub-chunk's 16 rows of a [T, H, D] tensor into LDS z[16][ld] (zeros past nrow).
+// A sub-chunk's inputs for one wavefront, in two halves: fetch issues every load
+// (into registers, at addresses that are always valid: rows past the sub-chunk
+// repeat its first row), place writes them to LDS (those rows as zeros).  All
+// loads are in flight before the first is waited for.
 template <typename MT, int D>
-__device__ __forceinline__ void load_rows(MT* z, int ld, const MT* g, int64_t t0, int H, int h, int nrow, int tid,
-                                          int nthr) {
-    constexpr int PER = 16 / (int)sizeof(MT);  // elements per 16-byte piece
-    constexpr int PR = D / PER;                // pieces per row
+struct RowFetch {  // 16 rows of a [T, H, D] tensor, for LDS z[16][ld]
+    static constexpr int PER = 16 / (int)sizeof(MT), PR = D / PER, NPT = (16 * PR + 63) / 64;
     typedef typename V16<MT>::type VT;
-    for (int p = tid; p < 16 * PR; p += nthr) {
-        const int i = p / PR, e = (p % PR) * PER;
-        VT x = {};
-        if (i < nrow) x = *reinterpret_cast<const VT*>(g + ((t0 + i) * H + h) * (int64_t)D + e);
-        *reinterpret_cast<VT*>(z + i * ld + e) = x;
+    VT x[NPT];
+    __device__ __forceinline__ void fetch(const MT* g, int64_t t0, int H, int h, int nrow, int lane) {
+#pragma unroll
+        for (int a = 0; a < NPT; ++a) {
+            const int pc = min(lane + 64 * a, 16 * PR - 1), i = pc / PR, e = (pc % PR) * PER;
+            x[a] = *reinterpret_cast<const VT*>(g + ((t0 + (i < nrow ? i : 0)) * H + h) * (int64_t)D + e);
+        }
     }
-}
-
-// G2[i][c] = log2 e * sum_{j < i} log a_j (i = 0..16) and beta.  The decays of the 16
-// tokens arrive in one round of 16-byte loads into G2's rows 1..16, then each
-// channel's prefix sum runs in LDS.  Contains a barrier: every thread calls it.
+    __device__ __forceinline__ void place(MT* z, int ld, int nrow, int lane) const {
+#pragma unroll
+        for (int a = 0; a < NPT; ++a) {
+            const int pc = lane + 64 * a, i = pc / PR, e = (pc % PR) * PER;
+            if (pc < 16 * PR) *reinterpret_cast<VT*>(z + i * ld + e) = i < nrow ? x[a] : VT{};
+        }
+    }
+};
+// The decays (log a, per channel or one per token) and beta of a sub-chunk: place
+// writes log2 e * log a into rows 1..16 of G2 (rows G2L apart) and beta into bt;
+// prefix (after a barrier) turns the rows into running sums, G2[i][c] =
+// log2 e * sum_{j < i} log a_j for i = 0..16.
 template <int DK, int G2L>
-__device__ __forceinline__ void load_decay(float* G2, float* bt, const float* la, const float* beta, int64_t t0,
-                                           int H, int h, int nrow, int scalar, int tid, int nthr) {
-    constexpr int Q = DK / 4;  // 16-byte pieces per token
-    for (int p = tid; p < SC * Q; p += nthr) {
-        const int i = p / Q, c4 = (p % Q) * 4;
-        f32x4 x = zero4();
-        if (i < nrow) {
-            if (scalar) {
-                const float a = la[(t0 + i) * H + h];
-                x = f32x4{a, a, a, a};
-            } else {
-                x = *reinterpret_cast<const f32x4*>(la + ((t0 + i) * H + h) * (int64_t)DK + c4);
+struct DecayFetch {
+    static constexpr int Q = DK / 4, NPT = (16 * Q + 63) / 64;  // 16-byte pieces
+    f32x4 x[NPT];
+    float b, as;
+    __device__ __forceinline__ void fetch(const float* la, const float* beta, int64_t t0, int H, int h, int nrow,
+                                          int scalar, int lane) {
+        const int64_t rb = (t0 + min(lane & (SC - 1), nrow - 1)) * H + h;
+        b = beta[rb];
+        as = la[scalar ? rb : rb * DK];
+        if (!scalar) {
+#pragma unroll
+            for (int a = 0; a < NPT; ++a) {
+                const int pc = min(lane + 64 * a, 16 * Q - 1), i = pc / Q, c4 = (pc % Q) * 4;
+                x[a] = *reinterpret_cast<const f32x4*>(la + ((t0 + (i < nrow ? i : 0)) * H + h) * (int64_t)DK + c4);
             }
         }
-        *reinterpret_cast<f32x4*>(G2 + (i + 1) * G2L + c4) = x * LOG2E;
     }
-    for (int i = tid; i < SC; i += nthr) bt[i] = i < nrow ? beta[(t0 + i) * H + h] : 0.f;
-    __syncthreads();
-    for (int c = tid; c < DK; c += nthr) {
-        float s = 0.f;
-        G2[c] = 0.f;
+    __device__ __forceinline__ void place(float* G2, float* bt, int nrow, int scalar, int lane) const {
 #pragma unroll
-        for (int i = 1; i <= SC; ++i) {
-            s += G2[i * G2L + c];
-            G2[i * G2L + c] = s;
+        for (int a = 0; a < NPT; ++a) {
+            const int pc = lane + 64 * a, i = pc / Q, c4 = (pc % Q) * 4;
+            if (pc < 16 * Q) {
+                const float s1 = __shfl(as, i);  // the token's decay, scalar gate
+                const f32x4 v = scalar ? f32x4{s1, s1, s1, s1} : x[a];
+                *reinterpret_cast<f32x4*>(G2 + (i + 1) * G2L + c4) = i < nrow ? v * LOG2E : zero4();
+            }
+        }
+        if (lane < SC) bt[lane] = lane < nrow ? b : 0.f;
+    }
+    __device__ __forceinline__ static void prefix(float* G2, int lane) {
+        for (int c = lane; c < DK; c += 64) {
+            float s = 0.f;
+            G2[c] = 0.f;
+#pragma unroll
+            for (int i = 1; i <= SC; ++i) {
+                s += G2[i * G2L + c];
+                G2[i * G2L + c] = s;
+            }
         }
     }
-}
+};
 
 // ===================================================================== ops
 // One wavefront per (sequence, head, sub-chunk).  LDS is reused as the sub-chunk's
@@ -280,13 +303,24 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     if (s * SC >= sq.len) return;
     const int nrow = min(SC, sq.len - s * SC);
     const int nsub = ceil_div(sq.len, SC);
-    const int64_t bi = ceil_blocks_before(p.cu, p.eq_len, n, SC) * p.H + (int64_t)h * nsub + s;
-    uint8_t* blk = p.ops + bi * OB::BYTES;
     const int64_t t0 = sq.t0 + (int64_t)s * SC;
 
-    load_rows<MT, DK>(kr, LDK, static_cast<const MT*>(p.k), t0, p.H, h, nrow, lane, 64);
-    load_rows<MT, DK>(qr, LDK, static_cast<const MT*>(p.q), t0, p.H, h, nrow, lane, 64);
-    load_decay<DK, G2L>(G2, bt, p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, lane, 64);
+    uint8_t* blk;
+    {
+        RowFetch<MT, DK> fk, fq;
+        DecayFetch<DK, G2L> fd;
+        fk.fetch(static_cast<const MT*>(p.k), t0, p.H, h, nrow, lane);
+        fq.fetch(static_cast<const MT*>(p.q), t0, p.H, h, nrow, lane);
+        fd.fetch(p.log_a, p.beta, t0, p.H, h, nrow, p.scalar, lane);
+        // the block's index (which reads the sequence lengths) while the inputs load
+        const int64_t bi = ceil_blocks_before(p.cu, p.eq_len, n, SC) * p.H + (int64_t)h * nsub + s;
+        blk = p.ops + bi * OB::BYTES;
+        fk.place(kr, LDK, nrow, lane);
+        fq.place(qr, LDK, nrow, lane);
+        fd.place(G2, bt, nrow, p.scalar, lane);
+        __syncthreads();
+        DecayFetch<DK, G2L>::prefix(G2, lane);
+    }
     __syncthreads();
 
     // QK [c][32] = [q_s e^{g_s} | k_s e^{gm_s}], gamma
@@ -422,27 +456,28 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     for (int x = lane; x < 256; x += 64) P1rm[(x >> 4) * L16 + (x & 15)] = from_f32<MT>(Gf[2][x >> 4][x & 15]);
     __syncthreads();
 
-    // the seven 16 x 16 matrices of the gradient pass, 8 elements per piece
+    // the seven 16 x 16 matrices of the gradient pass, 8 elements per piece: one
+    // matrix at a time (lanes 0..31), so that which matrix is the same across the
+    // wavefront
     MT* mats = reinterpret_cast<MT*>(blk + OB::MATS);
-    for (int pc = lane; pc < 7 * 32; pc += 64) {
-        const int mi = pc >> 5, row = (pc >> 1) & 15, c0 = (pc & 1) * 8;
-        float out[8];
+    if (lane < 32) {
+        const int row = lane >> 1, c0 = (lane & 1) * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int col = c0 + e;
-            float x;
-            switch (mi) {
-                case MAT_TB: x = Tf[row][col] * bt[col]; break;
-                case MAT_TT: x = Tf[col][row]; break;
-                case MAT_L: x = Gf[1][row][col]; break;
-                case MAT_LT: x = Gf[1][col][row]; break;
-                case MAT_A0: x = Gf[0][row][col]; break;
-                case MAT_P1T: x = Gf[2][col][row]; break;
-                default: x = Gf[3][col][row]; break;
+        for (int mi = 0; mi < 7; ++mi) {
+            float out[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = c0 + e;
+                out[e] = mi == MAT_TB ? Tf[row][col] * bt[col]
+                       : mi == MAT_TT ? Tf[col][row]
+                       : mi == MAT_L ? Gf[1][row][col]
+                       : mi == MAT_LT ? Gf[1][col][row]
+                       : mi == MAT_A0 ? Gf[0][row][col]
+                       : mi == MAT_P1T ? Gf[2][col][row]
+                                       : Gf[3][col][row];
             }
-            out[e] = x;
+            store8<MT>(mats + mi * 256 + row * 16 + c0, out);
         }
-        store8<MT>(mats + mi * 256 + row * 16 + c0, out);
     }
 
     // W (m = c, n = t): W^T[c][t] = sum_s Kcc^T[c][s] (b_t T[s][t]); natural store gives W[t][c]
