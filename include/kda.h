@@ -36,10 +36,13 @@
  *     Faults during execution surface at the caller's next synchronisation.
  *   - No scaling of q and no normalisation of k happen inside: callers fold
  *     any 1/sqrt(dk) into q and normalise k themselves.
- *   - log_a must be finite and <= 0 (0 < a <= 1); beta is unrestricted.
- *     Chunked prefill splits decay factors around 16-token references, which
- *     stays in floating-point range while every log_a >= -10; below that,
- *     results are accurate only where the decayed terms are negligible.
+ *   - log_a must be finite and <= 0 (0 < a <= 1); beta is unrestricted.  Every
+ *     such decay is supported exactly (to rounding): the chunked prefill splits
+ *     decay factors around 16-token references in chunks whose tokens all have
+ *     log_a >= -8.3 (log2 a >= -12), and takes a chunk with a steeper token by
+ *     one exponential of a run of consecutive decays per term (slower: an extra
+ *     kernel pass over the marked chunks in the two-pass method).  Decode takes
+ *     a = exp(log_a) per token.
  *   - Alignment: q, k, v, o and the fp32 states must be 16-byte aligned, as
  *     must a per-channel log_a in prefill; beta, a scalar log_a, any decode
  *     log_a, and cu_seqlens need 4-byte alignment.

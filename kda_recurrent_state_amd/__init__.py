@@ -125,17 +125,28 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t, name, dtype=None, ndim=None):
+def _need(t, name, dtype=None, ndim=None, shape=None):
+    """Type, dtype, rank, exact shape and layout of one argument.  The library
+    cannot see tensor sizes, so every buffer it writes is checked here."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise RuntimeError(f"{name} must be on a HIP device (got {t.device}); there is no CPU path")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions (got {tuple(t.shape)})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(ref, **tensors):
+    """Every tensor on ref's HIP device (checked after all shapes)."""
+    if ref.device.type != "cuda":
+        raise RuntimeError(f"tensors must be on a HIP device (got {ref.device}); there is no CPU path")
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise RuntimeError(f"{name} is on {t.device}, not on {ref.device}")
 
 
 def _check(lib, status):
@@ -254,11 +265,18 @@ def _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, fi
         _need(S0, "S0", torch.float32)
         if S0.shape != (N, H, dk, dv):
             raise ValueError(f"S0 must be [{N},{H},{dk},{dv}] (got {tuple(S0.shape)})")
+    if out is not None:
+        _need(out, "out", q.dtype, shape=(T, H, dv))
+    if isinstance(final_state, torch.Tensor):
+        _need(final_state, "final_state", torch.float32, shape=(N, H, dk, dv))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+    _same_device(q, k=k, v=v, log_a=log_a, beta=beta, S0=S0, cu_seqlens=cu_seqlens, out=out,
+                 final_state=final_state if isinstance(final_state, torch.Tensor) else None,
+                 snapshots=snapshots, workspace=workspace)
     o = out if out is not None else torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
-    _need(o, "out", q.dtype)
     if isinstance(final_state, torch.Tensor):
         ST = final_state
-        _need(ST, "final_state", torch.float32)
     elif final_state:
         ST = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     else:
@@ -275,8 +293,6 @@ def _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, fi
         _check(lib, lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(need)))
         if need.value > 0:
             workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
-    if workspace is not None:
-        _need(workspace, "workspace", torch.uint8, 1)
     ws_bytes = ctypes.c_size_t(0 if workspace is None else workspace.numel())
     pro = _prologue(prologue)
     if pro is not None:
@@ -357,6 +373,10 @@ def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, 
             _need(x, name, torch.float32)
             if x.shape != (N, H, dk, dv):
                 raise ValueError(f"{name} must be [{N},{H},{dk},{dv}] (got {tuple(x.shape)})")
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+    _same_device(q, k=k, v=v, log_a=log_a, beta=beta, dO=dO, S0=S0, dS_T=dS_T, cu_seqlens=cu_seqlens,
+                 workspace=workspace)
     if max_seqlen is None:
         if cu_seqlens is not None and N > 0:
             max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
@@ -368,7 +388,6 @@ def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, 
         need = ctypes.c_size_t(0)
         _check(lib, lib.kda_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(need)))
         workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=q.device)
-    _need(workspace, "workspace", torch.uint8, 1)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
            "dlog_a": torch.empty_like(log_a), "dbeta": torch.empty_like(beta),
            "dS0": torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device) if initial_state_grad else None}
@@ -414,10 +433,13 @@ def decode_step(q, k, v, log_a, beta, S, *, out=None, S_out=None, order: int = O
     _need(S, "S", torch.float32)
     if S.shape != (N, H, dk, dv) or k.shape != q.shape or v.shape[:2] != (N, H) or beta.shape != (N, H):
         raise ValueError("decode shapes disagree")
+    if S_out is not None:
+        _need(S_out, "S_out", torch.float32, shape=(N, H, dk, dv))
+    if out is not None:
+        _need(out, "out", q.dtype, shape=(N, H, dv))
+    _same_device(q, k=k, v=v, log_a=log_a, beta=beta, S=S, S_out=S_out, out=out)
     So = S if S_out is None else S_out
-    _need(So, "S_out", torch.float32)
     o = out if out is not None else torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
-    _need(o, "out", q.dtype)
     d = _Dims(N, H, N, dk, dv, _dtype_code(q), scalar, 0, 0, 0, int(order), 0)
     pro = _prologue(prologue)
     if pro is not None:

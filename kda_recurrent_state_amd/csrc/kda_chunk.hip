@@ -27,7 +27,11 @@
 // within e^{+-8 max|log a|}, upper-triangle overflow is discarded by select),
 // and a block pair (bt > bi) additionally scales the row factor by
 // e^{mu_bt - mu_bi} <= 1.  The state-side operands are referenced to the chunk
-// start or end, where every factor is <= 1.
+// start or end, where every factor is <= 1.  This split is exact to ~2^-30 while
+// every valid token of the chunk has log2 a >= STEEP_LOG2 (kda_chunk_common.hpp);
+// a chunk with a steeper token forms the chunk-referenced operands with one
+// exponential each and its Gram products by exact_gram, which is exact for any
+// decay (phases P2 and P3 below).
 //
 // The decay-first ordering (ORD1: S <- (I - b k^T k) Diag(a) S + b k^T v,
 // per-channel decay only) has the same structure with Kb = K e^{g_t} and no
@@ -104,6 +108,7 @@ struct ChunkLds {
     alignas(16) float F[(G::NPAIR > 0 ? G::NPAIR : 1) * DK];  // e^{mu_bt - mu_bi}
     alignas(16) float gam[DK];                 // e^{g_C}
     alignas(16) float beta[C];
+    int steep[G::NW];                          // per wavefront: a token below STEEP_LOG2
 };
 
 template <typename T, int DK, int DVS, int C>
@@ -182,6 +187,82 @@ __device__ __forceinline__ void load_chunk(const ChunkParams& p, const T* gq, co
                 const int64_t row = r0 + (int64_t)min(4 * tg + i, Lc - 1) * H;
                 vi[u].v[i] = *reinterpret_cast<const typename Vec4<T>::type*>(gv + row * DV + dv0 + j);
                 vi[u].b[i] = p.beta[row];
+            }
+        }
+    }
+}
+
+// P2 of a chunk with a token below STEEP_LOG2: the chunk-referenced operands
+// Kbar, Qbar, Kcc^T, Ktc^T with one exponential each, from running sums of log2 a
+// referenced to the chunk start (prefixes: group sums before the unit's group,
+// then its own decays) or end (suffixes), every exponent a run of consecutive
+// decays; the raw rows go to Kr, Qr and the log2 decays ([C][DK] fp32) over Kce
+// and Kci for exact_gram.  e^{g_C} comes from the block loop after it, as in the
+// factored path.  The unit's decays are read again from memory (rare path; the
+// walk does not keep them in registers).
+template <typename T, int DK, int DVS, int C, bool SCALAR, bool ORD1>
+__device__ __forceinline__ void chunk_steep_operands(const ChunkParams& p, ChunkLds<T, DK, DVS, C>& s, int64_t t0,
+                                                     int Lc, int h, int tid,
+                                                     const typename Vec2<T>::type (&qraw)[ChunkCfg<T, DK, DVS, C>::UPT][4],
+                                                     const typename Vec2<T>::type (&kraw)[ChunkCfg<T, DK, DVS, C>::UPT][4]) {
+    typedef ChunkCfg<T, DK, DVS, C> G;
+    constexpr int NT = G::NT, LDK = G::LDK, LDC = G::LDC;
+    float* LA = reinterpret_cast<float*>(s.Kce);
+    static_assert(sizeof(s.Kce) + sizeof(s.Kci) >= C * DK * sizeof(float), "log2 decays fit over Kce, Kci");
+    auto ex2v = [](f32x2 x) { return f32x2{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1])}; };
+#pragma unroll
+    for (int u = 0; u < G::UPT; ++u) {
+        const int uu = tid + NT * u;
+        if (uu < G::NU) {
+            int c, tg;
+            unit_of<G::NCP>(uu, c, tg);
+            f32x2 l2[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = (t0 + min(4 * tg + i, Lc - 1)) * p.H + h;
+                const f32x2 x = SCALAR ? f32x2{p.log_a[row], p.log_a[row]}
+                                       : *reinterpret_cast<const f32x2*>(p.log_a + row * DK + c);
+                l2[i] = 4 * tg + i < Lc ? x * LOG2E : f32x2{0.f, 0.f};
+            }
+            f32x2 pre = {0.f, 0.f}, suf = {0.f, 0.f};
+#pragma unroll
+            for (int g = 0; g < C / 4; ++g) {
+                const f32x2 x = *reinterpret_cast<const f32x2*>(&s.grp[g * DK + c]);
+                if (g < tg) pre += x;
+                if (g > tg) suf += x;
+            }
+            f32x2 sx[4];  // g_C - g_t
+            {
+                f32x2 run = suf;
+#pragma unroll
+                for (int i = 3; i >= 0; --i) {
+                    sx[i] = run;
+                    run += l2[i];
+                }
+            }
+            f32x2 kc[4], kt[4];
+            f32x2 gp = pre;  // g_{t-1}
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * tg + i;
+                const f32x2 k = f32x2{Vec2<T>::lo(kraw[u][i]), Vec2<T>::hi(kraw[u][i])};
+                const f32x2 q = f32x2{Vec2<T>::lo(qraw[u][i]), Vec2<T>::hi(qraw[u][i])};
+                const f32x2 g = gp + l2[i];
+                const f32x2 kb = k * ex2v(ORD1 ? g : gp), qb = q * ex2v(g);
+                kc[i] = k * ex2v(sx[i] + l2[i]);
+                kt[i] = k * ex2v(sx[i]);
+                store2(&s.Kbar[t * LDK + c], kb[0], kb[1]);
+                store2(&s.Qbar[t * LDK + c], qb[0], qb[1]);
+                store2(&s.Kr[t * LDK + c], k[0], k[1]);
+                store2(&s.Qr[t * LDK + c], q[0], q[1]);
+                *reinterpret_cast<f32x2*>(&LA[t * DK + c]) = l2[i];
+                gp = g;
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                if (!ORD1)
+                    store4(&s.KccT[prow<DK>(c + e) * LDC + 4 * tg], f32x4{kc[0][e], kc[1][e], kc[2][e], kc[3][e]});
+                store4(&s.KtcT[prow<DK>(c + e) * LDC + 4 * tg], f32x4{kt[0][e], kt[1][e], kt[2][e], kt[3][e]});
             }
         }
     }
@@ -282,6 +363,7 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
         // ---- P1: decay sums per 4-token group, (b V)^T, beta; prefetch next chunk ---
         f32x2 lam[G::UPT][4];
         typename Vec2<T>::type qraw[G::UPT][4], kraw[G::UPT][4];
+        bool steep = false;
 #pragma unroll
         for (int u = 0; u < G::UPT; ++u) {
             const int uu = tid + NT * u;
@@ -291,7 +373,9 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 f32x2 run = f32x2{0.f, 0.f};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    run += (4 * tg + i < Lc) ? ui[u].la[i] * LOG2E : f32x2{0.f, 0.f};
+                    const f32x2 l2 = (4 * tg + i < Lc) ? ui[u].la[i] * LOG2E : f32x2{0.f, 0.f};
+                    steep |= l2[0] < STEEP_LOG2 || l2[1] < STEEP_LOG2;
+                    run += l2;
                     lam[u][i] = run;
                     qraw[u][i] = ui[u].q[i];
                     kraw[u][i] = ui[u].k[i];
@@ -317,6 +401,10 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 if (j == 0) *reinterpret_cast<f32x4*>(&s.beta[4 * tg]) = bb;
             }
         }
+        {
+            const bool ws = wave_any(steep);
+            if (lane == 0) s.steep[wv] = ws;
+        }
         if (Lc_prev > 0) store_o();
         t0_prev = t0;
         Lc_prev = Lc;
@@ -332,6 +420,13 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
         // rin = e^{g_t - mid}, rex = e^{g_{t-1} - mid}, cin, cex their reciprocals,
         // em = e^{mu_b}, ec = e^{g_C - mu_b} (mu_b the mid-point of the sub-block).
         // Exponents are clamped to the fp32 range so no factor is inf or zero.
+        int steep_any = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) steep_any |= s.steep[w];
+        const bool steep_chunk = __builtin_amdgcn_readfirstlane(steep_any) != 0;
+        if (steep_chunk) {
+            chunk_steep_operands<T, DK, DVS, C, SCALAR, ORD1>(p, s, t0, Lc, h, tid, qraw, kraw);
+        } else {
 #pragma unroll
         for (int u = 0; u < G::UPT; ++u) {
             const int uu = tid + NT * u;
@@ -389,6 +484,7 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 }
             }
         }
+        }
         // per (sub-block, channel): e^{mu_bt - mu_bi} for block pairs, e^{g_C}
         for (int e = tid; e < NB * DK; e += NT) {
             const int b = e / DK, c = e % DK;
@@ -410,6 +506,17 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
         //      block pair w / 4, transposed (G^T) so it lands row-major in LDS;
         //      ORD1: A (w even, columns Kt) or P2 (w odd) of block pair w / 2 --------
         constexpr int NG = ORD1 ? 2 : 4;
+        if (steep_chunk) {
+            exact_gram<T, DK, C, NW, ORD1>(s.Kr, s.Qr, LDK, reinterpret_cast<const float*>(s.Kce), DK, wv, lane,
+                                           [&](int t, int i, float av, float lv, float p1v, float p2v) {
+                s.A[t * LDA + i] = s.beta[t] * av;
+                s.P2[t * LDC + i] = from_f32<T>(p2v);
+                if (!ORD1) {
+                    s.L[t * LDC + i] = from_f32<T>(lv);
+                    s.P1[t * LDC + i] = from_f32<T>(p1v);
+                }
+            });
+        } else
         for (int w = wv; w < NG * G::NBP; w += NW) {
             const int g = ORD1 ? ((w & 1) ? 3 : 0) : w % 4, pr = w / NG;
             int bt = 0;

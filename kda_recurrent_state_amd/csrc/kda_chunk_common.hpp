@@ -100,16 +100,93 @@ __device__ __forceinline__ float row_sum16(float x) {
 }
 
 // Input prologue (kda_prologue_t).  log a = max(-softplus(x), lo) is formed in
-// the log2 domain from the hardware exp2 and log2: -log2(1 + 2^{x log2 e}),
-// clipped at lo2 = lo log2 e (softplus below ~1e-7 rounds to 0, and an overflow
-// to infinity meets the clip or gives a = 0).  beta = 1 / (1 + e^{-x}).
+// the log2 domain from the hardware exp2 and log2, in the form that cannot
+// overflow: softplus2(y) = max(y, 0) + log2(1 + 2^{-|y|}) with y = x log2 e, so
+// the result is finite for every finite x (and -x log2 e for large x), then
+// clipped at lo2 = lo log2 e.  beta = 1 / (1 + e^{-x}).
 __device__ __forceinline__ float prologue_log2_a(float x, float lo2) {
-    return fmaxf(-__builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(x * LOG2E)), lo2);
-}
-__device__ __forceinline__ float prologue_log_a(float x, float lo) {
-    return prologue_log2_a(x, lo * LOG2E) * 0.6931471805599453f;
+    const float y = x * LOG2E;
+    return fmaxf(-(fmaxf(y, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(y)))), lo2);
 }
 __device__ __forceinline__ float prologue_beta(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// Decay range of the factored chunk products.  Inside a 16-token block the
+// Gram operands carry decay factors relative to the block's mid-point, each a
+// product of at most 8 per-token decays, so while every valid token of a chunk
+// has log2 a >= STEEP_LOG2 every such factor lies in [2^-96, 2^96].  A factor
+// referenced to the chunk start or end that would fall below the fp32 range
+// (2^-126) then changes the product it enters by at most 2^{96 - 126}.  A chunk
+// with a steeper token (log a < -8.3) takes exact_gram and chunk-referenced
+// operands formed with one exponential each instead.
+constexpr float STEEP_LOG2 = -12.f;
+
+// True in every lane when some lane's `steep` is set (one wavefront).
+__device__ __forceinline__ bool wave_any(bool steep) { return __ballot(steep) != 0; }
+
+// Masked C x C Gram products of one chunk with one exponential per term, for
+// chunks whose decay is too steep for the factor split.  With la_j the log2
+// decay of token j (0 on padded rows) and a sum over key channels c,
+//   A  (t, i) = sum_c k_t k_i 2^{la_i + ... + la_{t-1}}       i <  t
+//   L  (t, i) = sum_c k_t k_i 2^{la_{i+1} + ... + la_{t-1}}   i <  t
+//   P1 (t, i) = sum_c q_t k_i 2^{la_i + ... + la_t}           i <= t
+//   P2 (t, i) = sum_c q_t k_i 2^{la_{i+1} + ... + la_t}       i <= t
+// and for the decay-first order (ORD1) only
+//   A  (t, i) = sum_c k_t k_i 2^{la_{i+1} + ... + la_t}       i <  t,   with P2 as above.
+// Each exponent is a running sum of consecutive log2 decays (all <= 0), so no
+// factor leaves the fp32 range and none is the difference of two large sums.
+// Work: wavefront w takes key rows i = 4 qd + r (qd = w, w + NW, ...; r the
+// lane's 16-lane group, which covers DK / 16 channels per lane), sweeps t
+// upward keeping its running exponents, and sums each entry over the 16 lanes
+// of the group.  emit(t, i, a, l, p1, p2) runs in lane 16 r for every i <= t
+// (a = l = 0 at i == t; l = p1 = 0 for ORD1).  K, Q: raw rows [C][ldk] (16-byte
+// aligned); LA: log2 decays [C][ldl].
+template <typename T, int DK, int C, int NW, bool ORD1, typename Emit>
+__device__ __forceinline__ void exact_gram(const T* K, const T* Q, int ldk, const float* LA, int ldl, int wv,
+                                           int lane, Emit emit) {
+    constexpr int CPL = DK / 16;
+    const int r = lane >> 4, c0 = (lane & 15) * CPL;
+#pragma unroll 1
+    for (int qd = wv; qd < C / 4; qd += NW) {
+        const int i = 4 * qd + r;
+        float ki[CPL], lai[CPL], s[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            ki[e] = to_f32(K[i * ldk + c0 + e]);
+            lai[e] = LA[i * ldl + c0 + e];
+            s[e] = 0.f;  // la_{i+1} + ... + la_{t-1}
+        }
+#pragma unroll 1
+        for (int t = 4 * qd; t < C; ++t) {
+            const bool below = t > i;
+            float a = 0.f, l = 0.f, p1 = 0.f, p2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                const float kt = to_f32(K[t * ldk + c0 + e]), qt = to_f32(Q[t * ldk + c0 + e]);
+                const float lt = LA[t * ldl + c0 + e];
+                const float kk = kt * ki[e], qk = qt * ki[e];
+                const float e2 = below ? s[e] + lt : 0.f;  // la_{i+1} + ... + la_t
+                const float f2 = __builtin_amdgcn_exp2f(e2);
+                p2 += qk * f2;
+                if (ORD1) {
+                    a += kk * f2;
+                } else {
+                    const float e1 = below ? e2 + lai[e] : lt;  // la_i + ... + la_t
+                    a += kk * __builtin_amdgcn_exp2f(s[e] + lai[e]);
+                    l += kk * __builtin_amdgcn_exp2f(s[e]);
+                    p1 += qk * __builtin_amdgcn_exp2f(e1);
+                }
+                if (below) s[e] += lt;
+            }
+            a = row_sum16(a);
+            p2 = row_sum16(p2);
+            if (!ORD1) {
+                l = row_sum16(l);
+                p1 = row_sum16(p1);
+            }
+            if (t >= i && (lane & 15) == 0) emit(t, i, below ? a : 0.f, below ? l : 0.f, p1, p2);
+        }
+    }
+}
 
 // Stores one 16 x 16 fp32 accumulator tile (lane: column lane % 16, rows
 // 4 (lane / 16) .. + 3) into a row-major state with row stride DV; dst points at

@@ -23,6 +23,13 @@
 // the same phases 5 and 6 then give M1 = -Tb and M2 = P2 Tb (kda_ws.hpp), and
 // KC = (K e^{g_C - g_t})^T; no KT.
 //
+// Decay range: the factor split (phase 2) is exact to ~2^-30 while every valid
+// token of a chunk has log2 a >= STEEP_LOG2 (kda_chunk_common.hpp).  A chunk with
+// a steeper token is marked (GAM[0] = -1; a true GAM lies in [0, 1]) and its
+// whole block is formed again by kda_prep_exact_kernel with every decay factor
+// one exponential of a run of consecutive log2 decays, which is exact for any
+// decay.
+//
 // Persistent workgroups of 8 wavefronts, each walking a strided list of
 // chunks; the next chunk's inputs are loaded while the current one is in
 // phases 3-6.  Phases, separated by LDS barriers:
@@ -66,6 +73,10 @@ struct PrepLds {
             bf16 WT[DK * G::LDC];  // W^T  [channel][token]
             bf16 M1T[C * G::LDC];  // M1^T [i][t]
         } w;
+        struct {  // exact kernel, phases 2-3: raw rows and log2 decays for exact_gram
+            bf16 K[C * G::LDK], Q[C * G::LDK];
+            float LA[C * DK];
+        } x;
     } u;
     union {
         float grp[(C / 4) * DK];   // phases 1-2: summed log2 decay per 4-token group
@@ -80,6 +91,8 @@ struct PrepLds {
     alignas(16) float F[(G::NPAIR > 0 ? G::NPAIR : 1) * DK];
     alignas(16) float beta[C];
     alignas(16) float ones[16];  // unit column scale of the split solve (outside the unions)
+    int steep[G::NW];            // per wavefront: a token below STEEP_LOG2
+    int list[G::NT];             // exact kernel: marked items of one round
 };
 
 struct PrepParams {
@@ -186,6 +199,207 @@ __device__ __forceinline__ void split_solve(PrepLds<DK, C>& s, int wv, int lane,
     }
 }
 
+// Phases 4-6 of one chunk (after the Gram products): Tb = (I + A)^-1 diag(b), then
+// W, M1, QP and M2 to the block.  Shared by both kernels.
+template <int DK, int C, bool ORD1>
+__device__ __forceinline__ void prep_solve_store(PrepLds<DK, C>& s, uint8_t* __restrict__ blk, int tid, int lane,
+                                                 int wv) {
+    typedef PrepCfg<DK, C> G;
+    typedef WsBlock<DK, C, ORD1> WS;
+    typedef Mma<bf16> M;
+    constexpr int NW = G::NW, LDK = G::LDK, LDC = G::LDC, LDA = G::LDA;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    // ---- 4: Tb = (I + A)^-1 diag(b) ---------------------------------------------
+    if constexpr (G::SPLIT_SOLVE) {
+        split_solve<DK, C>(s, wv, lane, tid);
+    } else {
+        if (wv == 0) block_inverse<bf16, C, LDA, LDC>(s.u2.A, s.beta, s.u.v.X, s.Tb, lane);
+    }
+    lds_barrier();
+
+    // ---- 5: W = Tb Kb and M1 = Tb L diag(b).  Each tile is formed in both
+    //      orientations from the same fragments: W^T (rows: channels) goes to the
+    //      block, W (rows: tokens) to LDS as [channel][token] for phase 6 --------
+    constexpr int NWT = (DK / 16) * (C / 16), NMT = (C / 16) * (C / 16);
+    for (int w = wv; w < NWT + NMT; w += NW) {
+        const bool isw = w < NWT;
+        const int x = isw ? w : w - NWT;
+        const int ra = x / (C / 16), tt = x % (C / 16);  // row tile of KbT (or LbT), token tile
+        const bf16* pa = (isw ? s.KbT : s.LbT) + (16 * ra + lrow) * LDC;
+        const bf16* pb = s.Tb + (16 * tt + lrow) * LDC;
+        constexpr int NK = C / M::K;
+        M::frag fa[NK], fb[NK];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            fa[k] = M::loadr(pa + k * M::K, lane);
+            fb[k] = M::loadr(pb + k * M::K, lane);
+        }
+        f32x4 xt = zero4(), xn = zero4();
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            xt = M::mma(fa[k], fb[k], xt);  // rows: channel (or i), column: token t
+            xn = M::mma(fb[k], fa[k], xn);  // rows: token t, column: channel (or i)
+        }
+        const int t = 16 * tt + lrow, a0 = 16 * ra + 4 * lgrp;
+        const int an = 16 * ra + lrow, t0n = 16 * tt + 4 * lgrp;
+        if (isw) {
+            store4(reinterpret_cast<bf16*>(blk + WS::W + swz_elem<2 * DK>(kinv(t), kperm(a0))), xt);
+            store4(&s.u.w.WT[an * LDC + t0n], xn);
+        } else {
+            store4(reinterpret_cast<bf16*>(blk + WS::M1 + piece<C>(kinv(t), a0 >> 3) + 2 * (a0 & 7)), xt);
+            store4(&s.u.w.M1T[an * LDC + t0n], xn);
+        }
+    }
+    lds_barrier();
+
+    // ---- 6: QP = Qb - P1 W and M2 = P2 diag(b) - P1 M1, as their transposes -----
+    for (int w = wv; w < NWT + NMT; w += NW) {
+        const bool isq = w < NWT;
+        const int x = isq ? w : w - NWT;
+        const int ra = x / (C / 16), tt = x % (C / 16);
+        const bf16* pa = (isq ? s.u.w.WT : s.u.w.M1T) + (16 * ra + lrow) * LDC;
+        const bf16* pb = s.P1 + (16 * tt + lrow) * LDC;
+        const f32x4 pw = tile_mma_r<bf16, C>(pa, pb, zero4(), lane);
+        const int t = 16 * tt + lrow, a0 = 16 * ra + 4 * lgrp;
+        if (isq) {
+            const f32x4 qb = load4(&s.Qb[t * LDK + a0]);
+            store4(reinterpret_cast<bf16*>(blk + WS::QP + swz_elem<2 * DK>(t, kperm(a0))), qb - pw);
+        } else {
+            const f32x4 p2 = *reinterpret_cast<const f32x4*>(&s.P2[t * LDA + a0]);
+            store4(reinterpret_cast<bf16*>(blk + WS::M2 + piece<C>(t, a0 >> 3) + 2 * (a0 & 7)), p2 - pw);
+        }
+    }
+}
+
+// Phases 1-2 of a marked chunk in kda_prep_exact_kernel.  Kb, Qb, KC, KT and GAM
+// are formed with one exponential each from running sums of log2 a referenced to
+// the chunk start (prefixes) or end (suffixes), every exponent a run of
+// consecutive decays; the raw rows (k after the prologue's scaling) and the
+// log2 decays go to LDS for exact_gram.  Thread unit (c, tg) as in phase 1 of
+// kda_prep_kernel; two LDS barriers.
+template <int DK, int C, bool ORD1, bool PRO>
+__device__ __forceinline__ void prep_steep_operands(const PrepParams& p, PrepLds<DK, C>& s, const PrepIn& in,
+                                                    uint8_t* blk, int tid, int c, int tg, int Lc) {
+    typedef PrepCfg<DK, C> G;
+    typedef WsBlock<DK, C, ORD1> WS;
+    constexpr int LDK = G::LDK, LDC = G::LDC;
+    f32x2 l2[4];
+    float kscale[4] = {1.f, 1.f, 1.f, 1.f};
+    if (tid < G::NU) {
+        f32x2 run = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            l2[i] = in.la[i] * LOG2E;
+            if (PRO && p.pro.log_a_raw) {
+                const float lo2 = p.pro.log_a_min * LOG2E;
+                l2[i] = f32x2{prologue_log2_a(in.la[i][0], lo2), prologue_log2_a(in.la[i][1], lo2)};
+            }
+            if (4 * tg + i >= Lc) l2[i] = f32x2{0.f, 0.f};
+            run += l2[i];
+        }
+        *reinterpret_cast<f32x2*>(&s.u2.grp[tg * DK + c]) = run;
+        if (PRO && p.pro.normalize_k) {
+            const bool hi = (tid & 63) >= 32;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float k0 = Vec2<bf16>::lo(in.k[i]), k1 = Vec2<bf16>::hi(in.k[i]);
+                const float x = row_sum16(k0 * k0 + k1 * k1);
+                const float lo2 = readlanef(x, 0) + readlanef(x, 16), hi2 = readlanef(x, 32) + readlanef(x, 48);
+                kscale[i] = rsqrtf((hi ? hi2 : lo2) + PROLOGUE_EPS);
+            }
+        }
+    }
+    if (tid < C) s.beta[tid] = (PRO && p.pro.beta_logits && tid < Lc) ? prologue_beta(in.b) : in.b;
+    lds_barrier();
+    if (tid < G::NU) {
+        f32x2 pre = {0.f, 0.f}, suf = {0.f, 0.f}, tot = {0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < C / 4; ++g) {
+            const f32x2 x = *reinterpret_cast<const f32x2*>(&s.u2.grp[g * DK + c]);
+            tot += x;
+            if (g < tg) pre += x;
+            if (g > tg) suf += x;
+        }
+        f32x2 sx[4];  // g_C - g_t
+        {
+            f32x2 run = suf;
+#pragma unroll
+            for (int i = 3; i >= 0; --i) {
+                sx[i] = run;
+                run += l2[i];
+            }
+        }
+        auto ex2v = [](f32x2 x) { return f32x2{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1])}; };
+        f32x2 kb[4], kc[4], kt[4];
+        f32x2 gp = pre;  // g_{t-1}
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * tg + i;
+            const f32x2 k = f32x2{Vec2<bf16>::lo(in.k[i]), Vec2<bf16>::hi(in.k[i])} * kscale[i];
+            const f32x2 q = f32x2{Vec2<bf16>::lo(in.q[i]), Vec2<bf16>::hi(in.q[i])};
+            const f32x2 g = gp + l2[i];
+            kb[i] = k * ex2v(ORD1 ? g : gp);
+            kc[i] = k * ex2v(ORD1 ? sx[i] : sx[i] + l2[i]);
+            kt[i] = k * ex2v(sx[i]) * s.beta[t];
+            const f32x2 qb = q * ex2v(g);
+            store2(&s.Qb[t * LDK + c], qb[0], qb[1]);
+            store2(&s.u.x.K[t * LDK + c], k[0], k[1]);
+            store2(&s.u.x.Q[t * LDK + c], q[0], q[1]);
+            *reinterpret_cast<f32x2*>(&s.u.x.LA[t * DK + c]) = l2[i];
+            gp = g;
+        }
+        if (tg == 0) *reinterpret_cast<f32x2*>(blk + WS::GAM + 4 * c) = ex2v(tot);
+        const int half = 8 * (tg & 1);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            store4(&s.KbT[(c + e) * LDC + 4 * tg], f32x4{kb[0][e], kb[1][e], kb[2][e], kb[3][e]});
+            store4(reinterpret_cast<bf16*>(blk + WS::KC + piece<DK>(c + e, tg >> 1) + half),
+                   f32x4{kc[0][e], kc[1][e], kc[2][e], kc[3][e]});
+            if (!ORD1)
+                store4(reinterpret_cast<bf16*>(blk + WS::KT + piece<DK>(c + e, tg >> 1) + half),
+                       f32x4{kt[0][e], kt[1][e], kt[2][e], kt[3][e]});
+        }
+    }
+    lds_barrier();
+}
+
+// Phase 3 of a marked chunk: the masked Gram products by exact_gram, stored as
+// phase 3 of kda_prep_kernel stores the factored ones (ORD1: A and P2, P2 in P1's
+// slot; L diag(b) = -I and P2 diag(b) = 0 left as set up).
+template <int DK, int C, bool ORD1>
+__device__ __forceinline__ void prep_steep_gram(PrepLds<DK, C>& s, int wv, int lane) {
+    typedef PrepCfg<DK, C> G;
+    constexpr int LDC = G::LDC, LDA = G::LDA;
+    exact_gram<bf16, DK, C, G::NW, ORD1>(s.u.x.K, s.u.x.Q, G::LDK, s.u.x.LA, DK, wv, lane,
+                                         [&](int t, int i, float av, float lv, float p1v, float p2v) {
+        s.u2.A[t * LDA + i] = s.beta[t] * av;
+        if (ORD1) {
+            s.P1[t * LDC + i] = (bf16)p2v;
+        } else {
+            s.LbT[i * LDC + t] = (bf16)(lv * s.beta[i]);
+            s.P1[t * LDC + i] = (bf16)p1v;
+            s.P2[t * LDA + i] = p2v * s.beta[i];
+        }
+    });
+}
+
+// The masked matrices are never written outside their lower triangle: they start
+// at zero; ORD1 sets L diag(b) = -I.
+template <int DK, int C>
+__device__ __forceinline__ void prep_init_lds(PrepLds<DK, C>& s, int tid, bool ord1) {
+    typedef PrepCfg<DK, C> G;
+    constexpr int NT = G::NT, LDC = G::LDC, LDA = G::LDA;
+    for (int e = tid; e < C * LDC; e += NT) {
+        s.LbT[e] = (bf16)0.f; s.P1[e] = (bf16)0.f; s.Tb[e] = (bf16)0.f;
+    }
+    for (int e = tid; e < C * LDA; e += NT) s.P2[e] = 0.f;
+    if (tid < 16) s.ones[tid] = 1.f;
+    if (ord1) {
+        lds_barrier();
+        if (tid < C) s.LbT[tid * LDC + tid] = (bf16)-1.f;
+    }
+}
+
 // PRO: the call has an input prologue (k scaled per token by (|k|^2 + eps)^{-1/2},
 // each token's channels being one half-wavefront; beta and log a transformed
 // where they are loaded).
@@ -203,15 +417,7 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
     if (tid < G::NU) unit_of<G::NCP>(tid, c, tg);
 
     // upper blocks of the masked products are never written: zero them once
-    for (int e = tid; e < C * LDC; e += NT) {
-        s.LbT[e] = (bf16)0.f; s.P1[e] = (bf16)0.f; s.Tb[e] = (bf16)0.f;
-    }
-    for (int e = tid; e < C * LDA; e += NT) s.P2[e] = 0.f;
-    if (tid < 16) s.ones[tid] = 1.f;
-    if (ORD1) {  // L diag(b) = -I for the whole walk
-        lds_barrier();
-        if (tid < C) s.LbT[tid * LDC + tid] = (bf16)-1.f;
-    }
+    prep_init_lds<DK, C>(s, tid, ORD1);
 
     // this workgroup's chunks: item = blockIdx.x + k gridDim.x, empty ones skipped
     auto next_item = [&](int it, int64_t& t0, int& Lc, int& h) {
@@ -230,6 +436,7 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
         // ---- 1: decay sums per 4-token group in the log2 domain ------------------
         f32x2 lam[4];
         float kscale[4] = {1.f, 1.f, 1.f, 1.f};
+        bool steep = false;
         if (tid < G::NU) {
             f32x2 run = f32x2{0.f, 0.f};
 #pragma unroll
@@ -239,7 +446,9 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
                     const float lo2 = p.pro.log_a_min * LOG2E;
                     l2 = f32x2{prologue_log2_a(in.la[i][0], lo2), prologue_log2_a(in.la[i][1], lo2)};
                 }
-                run += (4 * tg + i < Lc) ? l2 : f32x2{0.f, 0.f};
+                if (4 * tg + i >= Lc) l2 = f32x2{0.f, 0.f};
+                steep |= l2[0] < STEEP_LOG2 || l2[1] < STEEP_LOG2;
+                run += l2;
                 lam[i] = run;
             }
             *reinterpret_cast<f32x2*>(&s.u2.grp[tg * DK + c]) = run;
@@ -256,6 +465,10 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
             }
         }
         if (tid < C) s.beta[tid] = (PRO && p.pro.beta_logits && tid < Lc) ? prologue_beta(in.b) : in.b;
+        {
+            const bool ws = wave_any(steep);
+            if (lane == 0) s.steep[wv] = ws;
+        }
         lds_barrier();
 
         // ---- 2: factors (exponents clamped to the fp32 range) and gated operands ---
@@ -328,7 +541,12 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
                 mu[bb] = rho[bb] + g0 + g1;
                 rho[bb + 1] = rho[bb] + ((g0 + g1) + (g2 + g3));
             }
-            if (b == 0) reinterpret_cast<float*>(blk + WS::GAM)[ch] = exp2f(rho[NB]);
+            if (b == 0) {  // a steep chunk is marked for kda_prep_exact_kernel instead
+                int st = 0;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) st |= s.steep[w];
+                reinterpret_cast<float*>(blk + WS::GAM)[ch] = st ? -1.f : exp2f(rho[NB]);
+            }
             for (int bi = 0; bi < b; ++bi) s.F[(b * (b - 1) / 2 + bi) * DK + ch] = exp2f(mu[b] - mu[bi]);
         }
         lds_barrier();
@@ -389,69 +607,69 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
         }
         lds_barrier();
 
-        // ---- 4: Tb = (I + A)^-1 diag(b) ---------------------------------------------
-        if constexpr (G::SPLIT_SOLVE) {
-            split_solve<DK, C>(s, wv, lane, tid);
-        } else {
-            if (wv == 0) block_inverse<bf16, C, LDA, LDC>(s.u2.A, s.beta, s.u.v.X, s.Tb, lane);
-        }
-        lds_barrier();
-
-        // ---- 5: W = Tb Kb and M1 = Tb L diag(b).  Each tile is formed in both
-        //      orientations from the same fragments: W^T (rows: channels) goes to the
-        //      block, W (rows: tokens) to LDS as [channel][token] for phase 6 --------
-        constexpr int NWT = (DK / 16) * (C / 16), NMT = (C / 16) * (C / 16);
-        for (int w = wv; w < NWT + NMT; w += NW) {
-            const bool isw = w < NWT;
-            const int x = isw ? w : w - NWT;
-            const int ra = x / (C / 16), tt = x % (C / 16);  // row tile of KbT (or LbT), token tile
-            const bf16* pa = (isw ? s.KbT : s.LbT) + (16 * ra + lrow) * LDC;
-            const bf16* pb = s.Tb + (16 * tt + lrow) * LDC;
-            constexpr int NK = C / M::K;
-            M::frag fa[NK], fb[NK];
-#pragma unroll
-            for (int k = 0; k < NK; ++k) {
-                fa[k] = M::loadr(pa + k * M::K, lane);
-                fb[k] = M::loadr(pb + k * M::K, lane);
-            }
-            f32x4 xt = zero4(), xn = zero4();
-#pragma unroll
-            for (int k = 0; k < NK; ++k) {
-                xt = M::mma(fa[k], fb[k], xt);  // rows: channel (or i), column: token t
-                xn = M::mma(fb[k], fa[k], xn);  // rows: token t, column: channel (or i)
-            }
-            const int t = 16 * tt + lrow, a0 = 16 * ra + 4 * lgrp;
-            const int an = 16 * ra + lrow, t0n = 16 * tt + 4 * lgrp;
-            if (isw) {
-                store4(reinterpret_cast<bf16*>(blk + WS::W + swz_elem<2 * DK>(kinv(t), kperm(a0))), xt);
-                store4(&s.u.w.WT[an * LDC + t0n], xn);
-            } else {
-                store4(reinterpret_cast<bf16*>(blk + WS::M1 + piece<C>(kinv(t), a0 >> 3) + 2 * (a0 & 7)), xt);
-                store4(&s.u.w.M1T[an * LDC + t0n], xn);
-            }
-        }
-        lds_barrier();
-
-        // ---- 6: QP = Qb - P1 W and M2 = P2 diag(b) - P1 M1, as their transposes -----
-        for (int w = wv; w < NWT + NMT; w += NW) {
-            const bool isq = w < NWT;
-            const int x = isq ? w : w - NWT;
-            const int ra = x / (C / 16), tt = x % (C / 16);
-            const bf16* pa = (isq ? s.u.w.WT : s.u.w.M1T) + (16 * ra + lrow) * LDC;
-            const bf16* pb = s.P1 + (16 * tt + lrow) * LDC;
-            const f32x4 pw = tile_mma_r<bf16, C>(pa, pb, zero4(), lane);
-            const int t = 16 * tt + lrow, a0 = 16 * ra + 4 * lgrp;
-            if (isq) {
-                const f32x4 qb = load4(&s.Qb[t * LDK + a0]);
-                store4(reinterpret_cast<bf16*>(blk + WS::QP + swz_elem<2 * DK>(t, kperm(a0))), qb - pw);
-            } else {
-                const f32x4 p2 = *reinterpret_cast<const f32x4*>(&s.P2[t * LDA + a0]);
-                store4(reinterpret_cast<bf16*>(blk + WS::M2 + piece<C>(t, a0 >> 3) + 2 * (a0 & 7)), p2 - pw);
-            }
-        }
+        prep_solve_store<DK, C, ORD1>(s, blk, tid, lane, wv);
         lds_barrier();  // LDS of this chunk is reused by the next
 
         item = nitem; t0 = nt0; Lc = nLc; h = nh;
+    }
+}
+
+// Marked chunks of one segment, run after kda_prep_kernel on the same items: every
+// non-empty item whose block carries the mark (GAM[0] == -1) is formed again,
+// all of it, with every decay factor one exponential (prep_steep_operands,
+// exact_gram); phases 4-6 are those of kda_prep_kernel.  Workgroup b checks its
+// items b, b + G, ... (G = gridDim.x) NT at a time, one per thread, and forms the
+// marked ones of each round; unmarked blocks are not touched.
+template <int DK, int C, bool SCALAR, bool ORD1, bool PRO>
+__global__ void __launch_bounds__(512, 2) kda_prep_exact_kernel(PrepParams p) {
+    typedef PrepCfg<DK, C> G;
+    typedef WsBlock<DK, C, ORD1> WS;
+    constexpr int NT = G::NT, NW = G::NW;
+    __shared__ PrepLds<DK, C> s;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int c = 0, tg = 0;
+    if (tid < G::NU) unit_of<G::NCP>(tid, c, tg);
+    bool init = false;
+    for (int64_t base = 0; (int64_t)blockIdx.x + base * gridDim.x < p.items; base += NT) {
+        const int64_t it = (int64_t)blockIdx.x + (base + tid) * gridDim.x;
+        bool marked = false;
+        if (it < p.items) {
+            int64_t t0;
+            int Lc, h;
+            if (prep_locate<DK, C, SCALAR>(p, (int)it, t0, Lc, h))
+                marked = *reinterpret_cast<const float*>(p.ws + (size_t)it * WS::BYTES + WS::GAM) == -1.f;
+        }
+        const uint64_t m = __ballot(marked);
+        if (lane == 0) s.steep[wv] = __popcll(m);
+        lds_barrier();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int cnt = s.steep[w];
+            before += w < wv ? cnt : 0;
+            total += cnt;
+        }
+        if (marked) s.list[before + __popcll(m & ((1ull << lane) - 1))] = (int)it;
+        lds_barrier();
+        if (total > 0 && !init) {
+            prep_init_lds<DK, C>(s, tid, ORD1);
+            init = true;
+            lds_barrier();
+        }
+        for (int x = 0; x < total; ++x) {
+            const int item = __builtin_amdgcn_readfirstlane(s.list[x]);
+            int64_t t0;
+            int Lc, h;
+            prep_locate<DK, C, SCALAR>(p, item, t0, Lc, h);
+            uint8_t* __restrict__ blk = p.ws + (size_t)item * WS::BYTES;
+            PrepIn in;
+            prep_load<DK, C, SCALAR>(p, t0, Lc, h, tid, c, tg, in);
+            prep_steep_operands<DK, C, ORD1, PRO>(p, s, in, blk, tid, c, tg, Lc);
+            prep_steep_gram<DK, C, ORD1>(s, wv, lane);
+            lds_barrier();
+            prep_solve_store<DK, C, ORD1>(s, blk, tid, lane, wv);
+            lds_barrier();
+        }
     }
 }
 
@@ -474,6 +692,8 @@ static hipError_t prep_cfg(const PrepLaunch& a, hipStream_t stream) {
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL((kda_prep_kernel<DK, C, SC, ORD1, PRO>), dim3((unsigned)blocks), dim3(PrepCfg<DK, C>::NT), 0,
                        stream, p);
+    hipLaunchKernelGGL((kda_prep_exact_kernel<DK, C, SC, ORD1, PRO>), dim3((unsigned)blocks),
+                       dim3(PrepCfg<DK, C>::NT), 0, stream, p);
     return hipGetLastError();
 }
 

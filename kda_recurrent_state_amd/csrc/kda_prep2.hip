@@ -25,8 +25,13 @@
 // relative to the mid-point are running products of a = 2^{log2e log a} and
 // 1 / a along its eight tokens, so each token costs two exponentials and no
 // cross-thread scan; the octet totals, exchanged through LDS, give e^{mu_b},
-// e^{g_C - mu_b}, F and e^{g_C}.  Per-token log a is clamped at -10.4 (log2
-// -15), which keeps every running product inside fp32 range.
+// e^{g_C - mu_b}, F and e^{g_C}.  This factor split is exact to ~2^-30 while
+// every valid token of the chunk has log2 a >= STEEP_LOG2 (kda_chunk_common.hpp).
+// A chunk with a steeper token is marked (GAM[0] = -1; a true GAM lies in
+// [0, 1]) and its whole block is formed again by kda_prep2_exact_kernel, which
+// takes every decay factor as one exponential of a run of consecutive log2
+// decays; the clamp of log2 a at -15 below only keeps the discarded values of
+// such a chunk finite.
 //
 // Phases (LDS barriers between them):
 //   A1 inputs -> factors -> mid-referenced Gram operands, octet products
@@ -46,7 +51,7 @@ constexpr int DK = 128, C = 32, NT = 256;
 constexpr int LDK = DK + 8;  // bf16 rows over channels
 constexpr int LDC = C + 8;   // bf16 rows over tokens
 constexpr int LDA = C + 4;   // fp32 rows over tokens
-constexpr float LA_MIN = -15.f;  // log2 clamp of a per-token decay
+constexpr float LA_MIN = -15.f;  // log2 clamp inside the factor split (never reached in its range)
 }  // namespace p2
 
 struct Prep2Lds {
@@ -59,6 +64,10 @@ struct Prep2Lds {
             float Xs[16 * 17];
             float X[2 * 512];
         } v;
+        struct {  // exact kernel, phases A2-B: raw rows and log2 decays for exact_gram
+            bf16 K[p2::C * p2::LDK], Q[p2::C * p2::LDK];
+            float LA[p2::C * p2::DK];
+        } x;
     } u;
     alignas(16) bf16 KbT[p2::DK * p2::LDC];  // (K e^{g_{t-1}})^T [channel][permuted token]
     alignas(16) bf16 Qb[p2::C * p2::LDK];    // Q e^{g_t} [token][channel]
@@ -69,7 +78,10 @@ struct Prep2Lds {
     alignas(16) bf16 Tb[p2::C * p2::LDC];    // (I + A)^-1 diag(b) [t][permuted s]
     alignas(16) bf16 TbT[p2::C * p2::LDC];   // its transpose [s][t]
     alignas(16) float F[p2::DK];             // e^{mu_1 - mu_0}
-    alignas(16) float Pq[4 * p2::DK];        // product of a over each token octet
+    alignas(16) float Pq[4 * p2::DK];        // product of a over each token octet (exact kernel:
+                                             // sum of log2 a)
+    int steep[4];                            // per wavefront: a token below STEEP_LOG2
+    int list[p2::NT];                        // exact kernel: marked items of one round
     alignas(16) float beta[p2::C];
     alignas(16) float ones[16];
 };
@@ -179,6 +191,251 @@ __device__ __forceinline__ void prep2_load(const Prep2Params& p, int64_t t0, int
     in.b = (tid < Lc) ? p.beta[r0 + (int64_t)tid * p.H] : 0.f;
 }
 
+// Phases C and D of one chunk (after B): T = (I + A)^-1 and the block's W, QP, M1
+// and M2.  Reads A, P1, P2b, LbT, KbT, Qb and beta from LDS; shared by both kernels.
+template <bool ORD1>
+__device__ __forceinline__ void prep2_solve_store(Prep2Lds& s, uint8_t* __restrict__ blk, int tid, int lane,
+                                                  int wv) {
+    using namespace p2;
+    typedef WsBlock<DK, C, ORD1> WS;
+    typedef Mma<bf16> M;
+    const int lr = lane & 15, lg = lane >> 4;
+    // ---- C: T = (I + A)^-1: diagonal blocks on wavefronts 0 and 1, then
+    //      T21 = -T22 A21 T11 on wavefront 0 ---------------------------------------------
+    if (wv < 2)
+        block_inverse<float, 16, LDA, LDA>(s.A + 16 * wv * LDA + 16 * wv, s.ones, s.u.v.X + wv * 512,
+                                           s.u.v.Tf + 16 * wv * LDA + 16 * wv, lane);
+    lds_barrier();
+    if (wv == 0) {
+        f32x4 x = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kk = 4 * ks + lg;
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(s.A[(16 + lr) * LDA + kk], s.u.v.Tf[kk * LDA + lr], x, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s.u.v.Xs[(4 * lg + r) * 17 + lr] = x[r];
+        wave_sync();
+        f32x4 t = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kk = 4 * ks + lg;
+            t = __builtin_amdgcn_mfma_f32_16x16x4f32(s.u.v.Tf[(16 + lr) * LDA + 16 + kk], s.u.v.Xs[kk * 17 + lr], t,
+                                                     0, 0, 0);
+        }
+        // T21 = -t: rows 16 + 4 lg + r, column lr.  Tb = T diag(b) at permuted
+        // columns; Tb^T rows are columns of T (four consecutive rows here)
+        const float bcol = s.beta[lr];
+        f32x4 tb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            tb[r] = -t[r] * bcol;
+            s.Tb[(16 + 4 * lg + r) * LDC + kperm(lr)] = (bf16)tb[r];
+        }
+        store4(&s.TbT[lr * LDC + 16 + 4 * lg], tb);
+    } else {
+        // diagonal blocks on wavefronts 1-3: (block, row t, column run 4 u .. 4 u + 3)
+        for (int e = tid - 64; e < 128; e += 192) {
+            const int bb = e >> 6, t = (e >> 2) & 15, u = e & 3;
+            const int row = 16 * bb + t, col = 16 * bb + 4 * u;
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&s.u.v.Tf[row * LDA + col]) *
+                            *reinterpret_cast<const f32x4*>(&s.beta[col]);
+            store4(&s.Tb[row * LDC + kperm(col)], x);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s.TbT[(col + r) * LDC + row] = (bf16)x[r];
+        }
+    }
+    lds_barrier();
+
+    // ---- D: wavefront w: token tile tt = w & 1; channel pairs 2 (w >> 1) and
+    //      2 (w >> 1) + 1 of W and QP; M1 (w < 2) or M2 (w >= 2) --------------------------
+    {
+        const int tt = wv & 1, half = wv >> 1;
+        const int t = 16 * tt + lr;
+        // R = P1 Tb as a B-operand fragment: out[s][t] = sum_i TbT[s][i] P1[t][i]
+        const M::frag p1f = M::loadr(s.P1 + t * LDC, lane);
+        const f32x4 r0 = M::mma(M::loadr(s.TbT + lr * LDC, lane), p1f, zero4());
+        const f32x4 r1 = M::mma(M::loadr(s.TbT + (16 + lr) * LDC, lane), p1f, zero4());
+        M::frag rfr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { rfr[i] = (bf16)r0[i]; rfr[4 + i] = (bf16)r1[i]; }
+        const M::frag tbf = M::loadr(s.Tb + t * LDC, lane);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const int cp = 2 * half + cc;  // 32-channel block
+            const M::frag kb0 = M::loadr(s.KbT + (32 * cp + lr) * LDC, lane);
+            const M::frag kb1 = M::loadr(s.KbT + (32 * cp + 16 + lr) * LDC, lane);
+            const f32x4 w0 = M::mma(kb0, tbf, zero4()), w1 = M::mma(kb1, tbf, zero4());
+            const f32x4 x0 = M::mma(kb0, rfr, zero4()), x1 = M::mma(kb1, rfr, zero4());
+            const f32x4 q0 = load4(&s.Qb[t * LDK + 32 * cp + 4 * lg]);
+            const f32x4 q1 = load4(&s.Qb[t * LDK + 32 * cp + 16 + 4 * lg]);
+            bf16x8 wo, qo;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                wo[r] = (bf16)w0[r]; wo[4 + r] = (bf16)w1[r];
+                qo[r] = (bf16)(q0[r] - x0[r]); qo[4 + r] = (bf16)(q1[r] - x1[r]);
+            }
+            *reinterpret_cast<bf16x8*>(blk + WS::W + swz<2 * DK>(kinv(t), 4 * cp + lg)) = wo;
+            *reinterpret_cast<bf16x8*>(blk + WS::QP + swz<2 * DK>(t, 4 * cp + lg)) = qo;
+        }
+        // rows i of (L diag(b))^T taken so that lane group lg ends with columns
+        // 8 lg .. 8 lg + 7 of M1 or M2 (tile 0: i = 8 lg + r, tile 1: 8 lg + 4 + r)
+        const int li = 8 * (lr >> 2) + (lr & 3);
+        const M::frag lb0 = M::loadr(s.LbT + li * LDC, lane);
+        const M::frag lb1 = M::loadr(s.LbT + (li + 4) * LDC, lane);
+        bf16x8 mo;
+        if (half == 0) {  // M1 = Tb (L diag(b)): out[i][t], row t of M1 at W's row for t
+            const f32x4 m0 = M::mma(lb0, tbf, zero4()), m1 = M::mma(lb1, tbf, zero4());
+#pragma unroll
+            for (int r = 0; r < 4; ++r) { mo[r] = (bf16)m0[r]; mo[4 + r] = (bf16)m1[r]; }
+            *reinterpret_cast<bf16x8*>(blk + WS::M1 + piece<C>(kinv(t), lg)) = mo;
+        } else {  // M2 = P2 diag(b) - R (L diag(b))
+            const f32x4 m0 = M::mma(lb0, rfr, zero4()), m1 = M::mma(lb1, rfr, zero4());
+            const f32x4 pa = *reinterpret_cast<const f32x4*>(&s.P2b[t * LDA + 8 * lg]);
+            const f32x4 pb = *reinterpret_cast<const f32x4*>(&s.P2b[t * LDA + 8 * lg + 4]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) { mo[r] = (bf16)(pa[r] - m0[r]); mo[4 + r] = (bf16)(pb[r] - m1[r]); }
+            *reinterpret_cast<bf16x8*>(blk + WS::M2 + piece<C>(t, lg)) = mo;
+        }
+    }
+}
+
+// Phases A1-A2 of a marked chunk in kda_prep2_exact_kernel.  Kb, Qb, KC, KT and
+// GAM are formed with one exponential each from running sums of log2 a
+// referenced to the chunk start (prefixes) or end (suffixes): every exponent is
+// a run of consecutive decays, so each factor is exact for any decay.  The raw
+// rows (k after the prologue's scaling) and the log2 decays go to LDS for
+// exact_gram.  Thread (c2, o) as in A1 of kda_prep2_kernel; two LDS barriers.
+template <bool SCALAR, bool ORD1, bool PRO>
+__device__ __forceinline__ void prep2_steep_operands(const Prep2Params& p, Prep2Lds& s, const Prep2Raw& raw,
+                                                     uint8_t* blk, int tid, int lane, int c2, int o, int Lc) {
+    using namespace p2;
+    typedef WsBlock<DK, C, ORD1> WS;
+    Prep2In in;
+    prep2_unpack<SCALAR>(raw, lane, in);
+    float kscale[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kscale[j] = 1.f;
+    if (PRO && p.pro.normalize_k) {
+        float ss[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const Vec2<bf16>::type kv = __builtin_bit_cast(Vec2<bf16>::type, in.k[j]);
+            const float k0 = Vec2<bf16>::lo(kv), k1 = Vec2<bf16>::hi(kv);
+            ss[j] = row_sum16(k0 * k0 + k1 * k1);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            kscale[j] = rsqrtf(readlanef(ss[j], 0) + readlanef(ss[j], 16) + readlanef(ss[j], 32) +
+                               readlanef(ss[j], 48) + PROLOGUE_EPS);
+    }
+    f32x2 l2[8];
+    f32x2 lsum = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        l2[j] = in.la[j] * LOG2E;
+        if (PRO && p.pro.log_a_raw) {
+            const float lo2 = p.pro.log_a_min * LOG2E;
+            l2[j] = f32x2{prologue_log2_a(in.la[j][0], lo2), prologue_log2_a(in.la[j][1], lo2)};
+        }
+        if (8 * o + j >= Lc) l2[j] = f32x2{0.f, 0.f};
+        lsum += l2[j];
+    }
+    *reinterpret_cast<f32x2*>(&s.Pq[o * DK + 2 * c2]) = lsum;
+    if (tid < C) s.beta[tid] = (PRO && p.pro.beta_logits && tid < Lc) ? prologue_beta(raw.b) : raw.b;
+    lds_barrier();
+    // sums of the octets before and after this one, and the chunk total
+    f32x2 pre = {0.f, 0.f}, suf = {0.f, 0.f}, tot = {0.f, 0.f};
+#pragma unroll
+    for (int oo = 0; oo < 4; ++oo) {
+        const f32x2 x = *reinterpret_cast<const f32x2*>(&s.Pq[oo * DK + 2 * c2]);
+        tot += x;
+        if (oo < o) pre += x;
+        if (oo > o) suf += x;
+    }
+    f32x2 sx[8];  // g_C - g_t
+    {
+        f32x2 run = suf;
+#pragma unroll
+        for (int j = 7; j >= 0; --j) {
+            sx[j] = run;
+            run += l2[j];
+        }
+    }
+    auto ex2v = [](f32x2 x) { return f32x2{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1])}; };
+    f32x2 kb[8], kc[8], kt[8];
+    f32x2 gp = pre;  // g_{t-1}
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int t = 8 * o + j;
+        const Vec2<bf16>::type kv = __builtin_bit_cast(Vec2<bf16>::type, in.k[j]);
+        const Vec2<bf16>::type qv = __builtin_bit_cast(Vec2<bf16>::type, in.q[j]);
+        const f32x2 k = f32x2{Vec2<bf16>::lo(kv), Vec2<bf16>::hi(kv)} * kscale[j];
+        const f32x2 q = f32x2{Vec2<bf16>::lo(qv), Vec2<bf16>::hi(qv)};
+        const f32x2 g = gp + l2[j];
+        kb[j] = k * ex2v(ORD1 ? g : gp);
+        kc[j] = k * ex2v(ORD1 ? sx[j] : sx[j] + l2[j]);
+        kt[j] = k * ex2v(sx[j]) * s.beta[t];
+        const f32x2 qb = q * ex2v(g);
+        store2(&s.Qb[t * LDK + 2 * c2], qb[0], qb[1]);
+        store2(&s.u.x.K[t * LDK + 2 * c2], k[0], k[1]);
+        store2(&s.u.x.Q[t * LDK + 2 * c2], q[0], q[1]);
+        *reinterpret_cast<f32x2*>(&s.u.x.LA[t * DK + 2 * c2]) = l2[j];
+        gp = g;
+    }
+    if (o == 0) *reinterpret_cast<f32x2*>(blk + WS::GAM + 8 * c2) = ex2v(tot);
+    const int pos0 = kperm(8 * o), pos1 = kperm(8 * o + 4);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int c = 2 * c2 + e;
+        store4(&s.KbT[c * LDC + pos0], f32x4{kb[0][e], kb[1][e], kb[2][e], kb[3][e]});
+        store4(&s.KbT[c * LDC + pos1], f32x4{kb[4][e], kb[5][e], kb[6][e], kb[7][e]});
+        bf16x8 kcv, ktv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            kcv[j] = (bf16)kc[j][e];
+            ktv[j] = (bf16)kt[j][e];
+        }
+        *reinterpret_cast<bf16x8*>(blk + WS::KC + piece<DK>(c, o)) = kcv;
+        if (!ORD1) *reinterpret_cast<bf16x8*>(blk + WS::KT + piece<DK>(c, o)) = ktv;
+    }
+    lds_barrier();
+}
+
+// Phase B of a marked chunk: the masked Gram products by exact_gram, stored as
+// phase B of kda_prep2_kernel stores the factored ones (ORD1: A and P2, P2 in
+// P1's slot, L diag(b) = -I and P2 diag(b) = 0 left as set up).
+template <bool ORD1>
+__device__ __forceinline__ void prep2_steep_gram(Prep2Lds& s, int wv, int lane) {
+    using namespace p2;
+    exact_gram<bf16, DK, C, 4, ORD1>(s.u.x.K, s.u.x.Q, LDK, s.u.x.LA, DK, wv, lane,
+                                     [&](int t, int i, float av, float lv, float p1v, float p2v) {
+        s.A[t * LDA + i] = s.beta[t] * av;
+        if (ORD1) {
+            s.P1[t * LDC + i] = (bf16)p2v;
+        } else {
+            s.LbT[i * LDC + kperm(t)] = (bf16)(lv * s.beta[i]);
+            s.P1[t * LDC + i] = (bf16)p1v;
+            s.P2b[t * LDA + i] = p2v * s.beta[i];
+        }
+    });
+}
+
+// The masked matrices that are never written outside their lower triangle start
+// at zero (upper blocks stay zero for the whole walk); ORD1 sets L diag(b) = -I.
+__device__ __forceinline__ void prep2_init_lds(Prep2Lds& s, int tid, bool ord1) {
+    using namespace p2;
+    for (int e = tid; e < C * LDC; e += NT) {
+        s.LbT[e] = (bf16)0.f; s.P1[e] = (bf16)0.f; s.Tb[e] = (bf16)0.f; s.TbT[e] = (bf16)0.f;
+    }
+    for (int e = tid; e < C * LDA; e += NT) s.P2b[e] = 0.f;
+    if (tid < 16) s.ones[tid] = 1.f;
+    if (ord1) {
+        lds_barrier();
+        if (tid < C) s.LbT[tid * LDC + kperm(tid)] = (bf16)-1.f;
+    }
+}
+
 // PRO: the call has an input prologue; k is scaled per token by
 // (|k|^2 + eps)^{-1/2} (each token's row is one wavefront: 64 lanes x 2 channels),
 // beta and log a are transformed where they are loaded.
@@ -196,15 +453,7 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
     const int blk_b = o >> 1;     // 16-token block of the octet
 
     // upper blocks of the masked products are never written: zero them once
-    for (int e = tid; e < C * LDC; e += NT) {
-        s.LbT[e] = (bf16)0.f; s.P1[e] = (bf16)0.f; s.Tb[e] = (bf16)0.f; s.TbT[e] = (bf16)0.f;
-    }
-    for (int e = tid; e < C * LDA; e += NT) s.P2b[e] = 0.f;
-    if (tid < 16) s.ones[tid] = 1.f;
-    if (ORD1) {  // L diag(b) = -I for the whole walk
-        lds_barrier();
-        if (tid < C) s.LbT[tid * LDC + kperm(tid)] = (bf16)-1.f;
-    }
+    prep2_init_lds(s, tid, ORD1);
 
     auto next_item = [&](int it, int64_t& t0, int& Lc, int& h) {
         while (it < p.items && !prep2_locate(p, it, t0, Lc, h)) it += gridDim.x;
@@ -251,6 +500,7 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
                                    readlanef(ss[j], 48) + PROLOGUE_EPS);
         }
         f32x2 a[8], ai[8], E[8], Ei[8];
+        bool steep = false;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const bool valid = 8 * o + j < Lc;
@@ -260,6 +510,7 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
                 la2 = f32x2{prologue_log2_a(in.la[j][0], lo2), prologue_log2_a(in.la[j][1], lo2)};
             }
             if (!valid) la2 = f32x2{0.f, 0.f};
+            steep |= la2[0] < STEEP_LOG2 || la2[1] < STEEP_LOG2;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const float x = fmaxf(la2[e], LA_MIN);
@@ -288,6 +539,10 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
             P = E[7];
         }
         *reinterpret_cast<f32x2*>(&s.Pq[o * DK + 2 * c2]) = P;
+        {
+            const bool ws = wave_any(steep);
+            if (lane == 0) s.steep[wv] = ws;
+        }
         if (tid < C) s.beta[tid] = (PRO && p.pro.beta_logits && tid < Lc) ? prologue_beta(raw.b) : raw.b;
 
         f32x2 kr[8], qr[8], kce[8], kci[8];
@@ -322,7 +577,10 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
             const f32x2 ec = blk_b ? ec1 : F * ec1;
             if (o == 0) {
                 *reinterpret_cast<f32x2*>(&s.F[2 * c2]) = F;
-                *reinterpret_cast<f32x2*>(blk + WS::GAM + 8 * c2) = (em0 * F) * ec1;
+                // a steep chunk is marked for kda_prep2_exact_kernel instead
+                const bool steep_chunk = (s.steep[0] | s.steep[1] | s.steep[2] | s.steep[3]) != 0;
+                *reinterpret_cast<f32x2*>(blk + WS::GAM + 8 * c2) =
+                    steep_chunk ? f32x2{-1.f, -1.f} : (em0 * F) * ec1;
             }
             // KbT rows (channels), tokens at their permuted positions: tokens 8 o .. 8 o + 3
             // and 8 o + 4 .. 8 o + 7 land at two 4-element runs
@@ -422,107 +680,69 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
         }
         lds_barrier();
 
-        // ---- C: T = (I + A)^-1: diagonal blocks on wavefronts 0 and 1, then
-        //      T21 = -T22 A21 T11 on wavefront 0 ---------------------------------------------
-        if (wv < 2)
-            block_inverse<float, 16, LDA, LDA>(s.A + 16 * wv * LDA + 16 * wv, s.ones, s.u.v.X + wv * 512,
-                                               s.u.v.Tf + 16 * wv * LDA + 16 * wv, lane);
-        lds_barrier();
-        if (wv == 0) {
-            f32x4 x = zero4();
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int kk = 4 * ks + lg;
-                x = __builtin_amdgcn_mfma_f32_16x16x4f32(s.A[(16 + lr) * LDA + kk], s.u.v.Tf[kk * LDA + lr], x, 0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s.u.v.Xs[(4 * lg + r) * 17 + lr] = x[r];
-            wave_sync();
-            f32x4 t = zero4();
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int kk = 4 * ks + lg;
-                t = __builtin_amdgcn_mfma_f32_16x16x4f32(s.u.v.Tf[(16 + lr) * LDA + 16 + kk], s.u.v.Xs[kk * 17 + lr], t,
-                                                         0, 0, 0);
-            }
-            // T21 = -t: rows 16 + 4 lg + r, column lr.  Tb = T diag(b) at permuted
-            // columns; Tb^T rows are columns of T (four consecutive rows here)
-            const float bcol = s.beta[lr];
-            f32x4 tb;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                tb[r] = -t[r] * bcol;
-                s.Tb[(16 + 4 * lg + r) * LDC + kperm(lr)] = (bf16)tb[r];
-            }
-            store4(&s.TbT[lr * LDC + 16 + 4 * lg], tb);
-        } else {
-            // diagonal blocks on wavefronts 1-3: (block, row t, column run 4 u .. 4 u + 3)
-            for (int e = tid - 64; e < 128; e += 192) {
-                const int bb = e >> 6, t = (e >> 2) & 15, u = e & 3;
-                const int row = 16 * bb + t, col = 16 * bb + 4 * u;
-                const f32x4 x = *reinterpret_cast<const f32x4*>(&s.u.v.Tf[row * LDA + col]) *
-                                *reinterpret_cast<const f32x4*>(&s.beta[col]);
-                store4(&s.Tb[row * LDC + kperm(col)], x);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) s.TbT[(col + r) * LDC + row] = (bf16)x[r];
-            }
-        }
-        lds_barrier();
-
-        // ---- D: wavefront w: token tile tt = w & 1; channel pairs 2 (w >> 1) and
-        //      2 (w >> 1) + 1 of W and QP; M1 (w < 2) or M2 (w >= 2) --------------------------
-        {
-            const int tt = wv & 1, half = wv >> 1;
-            const int t = 16 * tt + lr;
-            // R = P1 Tb as a B-operand fragment: out[s][t] = sum_i TbT[s][i] P1[t][i]
-            const M::frag p1f = M::loadr(s.P1 + t * LDC, lane);
-            const f32x4 r0 = M::mma(M::loadr(s.TbT + lr * LDC, lane), p1f, zero4());
-            const f32x4 r1 = M::mma(M::loadr(s.TbT + (16 + lr) * LDC, lane), p1f, zero4());
-            M::frag rfr;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { rfr[i] = (bf16)r0[i]; rfr[4 + i] = (bf16)r1[i]; }
-            const M::frag tbf = M::loadr(s.Tb + t * LDC, lane);
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const int cp = 2 * half + cc;  // 32-channel block
-                const M::frag kb0 = M::loadr(s.KbT + (32 * cp + lr) * LDC, lane);
-                const M::frag kb1 = M::loadr(s.KbT + (32 * cp + 16 + lr) * LDC, lane);
-                const f32x4 w0 = M::mma(kb0, tbf, zero4()), w1 = M::mma(kb1, tbf, zero4());
-                const f32x4 x0 = M::mma(kb0, rfr, zero4()), x1 = M::mma(kb1, rfr, zero4());
-                const f32x4 q0 = load4(&s.Qb[t * LDK + 32 * cp + 4 * lg]);
-                const f32x4 q1 = load4(&s.Qb[t * LDK + 32 * cp + 16 + 4 * lg]);
-                bf16x8 wo, qo;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    wo[r] = (bf16)w0[r]; wo[4 + r] = (bf16)w1[r];
-                    qo[r] = (bf16)(q0[r] - x0[r]); qo[4 + r] = (bf16)(q1[r] - x1[r]);
-                }
-                *reinterpret_cast<bf16x8*>(blk + WS::W + swz<2 * DK>(kinv(t), 4 * cp + lg)) = wo;
-                *reinterpret_cast<bf16x8*>(blk + WS::QP + swz<2 * DK>(t, 4 * cp + lg)) = qo;
-            }
-            // rows i of (L diag(b))^T taken so that lane group lg ends with columns
-            // 8 lg .. 8 lg + 7 of M1 or M2 (tile 0: i = 8 lg + r, tile 1: 8 lg + 4 + r)
-            const int li = 8 * (lr >> 2) + (lr & 3);
-            const M::frag lb0 = M::loadr(s.LbT + li * LDC, lane);
-            const M::frag lb1 = M::loadr(s.LbT + (li + 4) * LDC, lane);
-            bf16x8 mo;
-            if (half == 0) {  // M1 = Tb (L diag(b)): out[i][t], row t of M1 at W's row for t
-                const f32x4 m0 = M::mma(lb0, tbf, zero4()), m1 = M::mma(lb1, tbf, zero4());
-#pragma unroll
-                for (int r = 0; r < 4; ++r) { mo[r] = (bf16)m0[r]; mo[4 + r] = (bf16)m1[r]; }
-                *reinterpret_cast<bf16x8*>(blk + WS::M1 + piece<C>(kinv(t), lg)) = mo;
-            } else {  // M2 = P2 diag(b) - R (L diag(b))
-                const f32x4 m0 = M::mma(lb0, rfr, zero4()), m1 = M::mma(lb1, rfr, zero4());
-                const f32x4 pa = *reinterpret_cast<const f32x4*>(&s.P2b[t * LDA + 8 * lg]);
-                const f32x4 pb = *reinterpret_cast<const f32x4*>(&s.P2b[t * LDA + 8 * lg + 4]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) { mo[r] = (bf16)(pa[r] - m0[r]); mo[4 + r] = (bf16)(pb[r] - m1[r]); }
-                *reinterpret_cast<bf16x8*>(blk + WS::M2 + piece<C>(t, lg)) = mo;
-            }
-        }
+        prep2_solve_store<ORD1>(s, blk, tid, lane, wv);
         lds_barrier();  // LDS of this chunk is reused by the next
 
         item = nitem; t0 = nt0; Lc = nLc; h = nh;
+    }
+}
+
+// Marked chunks of one segment, run after kda_prep2_kernel on the same items:
+// every non-empty item whose block carries the mark (GAM[0] == -1) is formed
+// again, all of it, with the decay factors of the chunk-referenced operands and
+// of the Gram products taken one exponential each (prep2_steep_operands,
+// exact_gram); phases C-D are those of kda_prep2_kernel.  Workgroup b checks its
+// items b, b + G, b + 2 G, ... (G = gridDim.x) NT at a time, one per thread, and
+// forms the marked ones of each round; unmarked blocks are not touched.
+template <bool SCALAR, bool ORD1, bool PRO>
+__global__ void __launch_bounds__(p2::NT, 2) kda_prep2_exact_kernel(Prep2Params p) {
+    using namespace p2;
+    typedef WsBlock<DK, C, ORD1> WS;
+    __shared__ Prep2Lds s;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    bool init = false;
+    for (int64_t base = 0; (int64_t)blockIdx.x + base * gridDim.x < p.items; base += NT) {
+        const int64_t it = (int64_t)blockIdx.x + (base + tid) * gridDim.x;
+        bool marked = false;
+        if (it < p.items) {
+            int64_t t0;
+            int Lc, h;
+            if (prep2_locate(p, (int)it, t0, Lc, h))
+                marked = *reinterpret_cast<const float*>(p.ws + (size_t)it * WS::BYTES + WS::GAM) == -1.f;
+        }
+        // marked items of this round, in order, to s.list
+        const uint64_t m = __ballot(marked);
+        if (lane == 0) s.steep[wv] = __popcll(m);
+        lds_barrier();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < NT / WAVE; ++w) {
+            const int c = s.steep[w];
+            before += w < wv ? c : 0;
+            total += c;
+        }
+        if (marked) s.list[before + __popcll(m & ((1ull << lane) - 1))] = (int)it;
+        lds_barrier();
+        if (total > 0 && !init) {
+            prep2_init_lds(s, tid, ORD1);
+            init = true;
+            lds_barrier();
+        }
+        for (int x = 0; x < total; ++x) {
+            const int item = __builtin_amdgcn_readfirstlane(s.list[x]);
+            int64_t t0;
+            int Lc, h;
+            prep2_locate(p, item, t0, Lc, h);
+            uint8_t* __restrict__ blk = p.ws + (size_t)item * WS::BYTES;
+            Prep2Raw raw;
+            prep2_load<SCALAR>(p, t0, Lc, h, tid, lane, wv, raw);
+            prep2_steep_operands<SCALAR, ORD1, PRO>(p, s, raw, blk, tid, lane, lane, wv, Lc);
+            prep2_steep_gram<ORD1>(s, wv, lane);
+            lds_barrier();
+            prep2_solve_store<ORD1>(s, blk, tid, lane, wv);
+            lds_barrier();
+        }
     }
 }
 
@@ -541,15 +761,21 @@ hipError_t launch_prep2(const PrepLaunch& a, hipStream_t stream) {
     if (blocks < 1) blocks = 1;
     // order 1 comes with per-channel decay only (the host maps scalar decay to order 0)
     const dim3 grid((unsigned)blocks), block(p2::NT);
+#define KDA_PREP2_LAUNCH(SC, O1, PR)                                                                  \
+    do {                                                                                              \
+        hipLaunchKernelGGL((kda_prep2_kernel<SC, O1, PR>), grid, block, 0, stream, p);                \
+        hipLaunchKernelGGL((kda_prep2_exact_kernel<SC, O1, PR>), grid, block, 0, stream, p);          \
+    } while (0)
     if (a.pro.any()) {
-        if (a.scalar) hipLaunchKernelGGL((kda_prep2_kernel<true, false, true>), grid, block, 0, stream, p);
-        else if (a.order) hipLaunchKernelGGL((kda_prep2_kernel<false, true, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((kda_prep2_kernel<false, false, true>), grid, block, 0, stream, p);
+        if (a.scalar) KDA_PREP2_LAUNCH(true, false, true);
+        else if (a.order) KDA_PREP2_LAUNCH(false, true, true);
+        else KDA_PREP2_LAUNCH(false, false, true);
     } else {
-        if (a.scalar) hipLaunchKernelGGL((kda_prep2_kernel<true, false, false>), grid, block, 0, stream, p);
-        else if (a.order) hipLaunchKernelGGL((kda_prep2_kernel<false, true, false>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((kda_prep2_kernel<false, false, false>), grid, block, 0, stream, p);
+        if (a.scalar) KDA_PREP2_LAUNCH(true, false, false);
+        else if (a.order) KDA_PREP2_LAUNCH(false, true, false);
+        else KDA_PREP2_LAUNCH(false, false, false);
     }
+#undef KDA_PREP2_LAUNCH
     return hipGetLastError();
 }
 

@@ -70,6 +70,19 @@ def _declare(lib) -> None:
                                        ctypes.c_int, P, P, P, P, P, P, P, P, ctypes.c_int]
 
 
+MAX_THREADS = 16  # the host CPU share that goes with one GPU
+
+
+def default_threads() -> int:
+    """Threads of the oracle's pool: the CPUs this process may run on, at most
+    MAX_THREADS (a machine shared by several GPUs grants each that many)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, MAX_THREADS))
+
+
 def _f64(x) -> np.ndarray:
     """Exact upcast to a contiguous float64 array (bf16/fp32 -> fp64 is exact)."""
     if hasattr(x, "detach"):  # torch tensor (possibly bf16, possibly on a device)
@@ -145,7 +158,7 @@ def kda_oracle(q, k, v, log_a, beta, S0=None, cu_seqlens=None, order: int = 0,
             raise ValueError("S0 must be [N,H,dk,dv]")
     o = np.zeros((T, H, dv), dtype=np.float64)
     ST = np.zeros((N, H, dk, dv), dtype=np.float64)
-    nt = threads if threads is not None else (os.cpu_count() or 1)
+    nt = threads if threads is not None else default_threads()
     L = lib if lib is not None else load_library()
     ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
     rc = L.kda_oracle_fwd(N, ptr(cu), H, dk, dv, ptr(q), ptr(k), ptr(v), ptr(log_a), scalar,
@@ -197,7 +210,7 @@ def kda_oracle_bwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, dO=None, dST=
     out = {"dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
            "dlog_a": np.zeros(log_a.shape), "dbeta": np.zeros((T, H)),
            "dS0": np.zeros((N, H, dk, dv))}
-    nt = threads if threads is not None else (os.cpu_count() or 1)
+    nt = threads if threads is not None else default_threads()
     L = lib if lib is not None else load_library()
     ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
     rc = L.kda_oracle_bwd(N, ptr(cu), H, dk, dv, ptr(q), ptr(k), ptr(v), ptr(log_a), scalar,

@@ -241,3 +241,77 @@ def chunk_forward_split(q, k, v, la, beta, S0=None, C=32, bf16=False):
         Oc, S = chunk_apply(ops, pad(v), S, bf16=bf16)
         O[s:e] = Oc[:n]
     return O, S
+
+
+def exact_chunk_step(q, k, v, la, beta, S, order=0, dtype=np.float32):
+    """One chunk by the path the kernels take for a chunk whose decay is too steep
+    for the factor split: every decay factor is 2^(a run of consecutive log2
+    decays, summed in order), evaluated in `dtype` (float32 as on the GPU); no
+    exponent is the difference of two large sums.
+      A  (t,i) = b_t sum_c k_t k_i 2^{la_i + .. + la_{t-1}}    (order 1: 2^{la_{i+1} + .. + la_t})
+      L  (t,i) =     sum_c k_t k_i 2^{la_{i+1} + .. + la_{t-1}}
+      P1 (t,i) =     sum_c q_t k_i 2^{la_i + .. + la_t}
+      P2 (t,i) =     sum_c q_t k_i 2^{la_{i+1} + .. + la_t}
+    with running sums over t for each key row i, and the chunk-referenced
+    operands from prefix (g_{t-1}, g_t) and suffix (g_C - g_{t-1}, g_C - g_t) sums.
+    Returns (O, S_C) in float64."""
+    C, dk = q.shape
+    f = lambda x: np.asarray(x, dtype=dtype)
+    l2 = f(la * np.log2(np.e))
+    kq, qq = f(k), f(q)
+    A = np.zeros((C, C)); Lm = np.zeros((C, C)); P1 = np.zeros((C, C)); P2 = np.zeros((C, C))
+    for i in range(C):
+        s = np.zeros(dk, dtype=dtype)  # la_{i+1} + ... + la_{t-1}
+        for t in range(i, C):
+            kk, qk = kq[t] * kq[i], qq[t] * kq[i]
+            if t == i:
+                P1[t, i] = np.sum(qk * np.exp2(l2[t]))
+                P2[t, i] = np.sum(qk)
+                continue
+            e2 = s + l2[t]
+            P2[t, i] = np.sum(qk * np.exp2(e2))
+            if order:
+                A[t, i] = beta[t] * np.sum(kk * np.exp2(e2))
+            else:
+                A[t, i] = beta[t] * np.sum(kk * np.exp2(s + l2[i]))
+                Lm[t, i] = np.sum(kk * np.exp2(s))
+                P1[t, i] = np.sum(qk * np.exp2(e2 + l2[i]))
+            s = s + l2[t]
+    pre = np.zeros((C, dk), dtype=dtype)   # g_{t-1}
+    suf = np.zeros((C, dk), dtype=dtype)   # g_C - g_t
+    run = np.zeros(dk, dtype=dtype)
+    for t in range(C):
+        pre[t] = run
+        run = run + l2[t]
+    gC = run
+    run = np.zeros(dk, dtype=dtype)
+    for t in range(C - 1, -1, -1):
+        suf[t] = run
+        run = run + l2[t]
+    g = pre + l2
+    T = np.linalg.inv(np.eye(C) + A)
+    bV = beta[:, None] * v
+    Qb = q * np.exp2(g)
+    gam = np.exp2(gC)[:, None]
+    if order:
+        Kd = k * np.exp2(g)
+        U = T @ (beta[:, None] * (v - Kd @ S))
+        O = Qb @ S + P2 @ U
+        S_C = gam * S + (k * np.exp2(suf)).T @ U
+        return O, S_C
+    Kb = k * np.exp2(pre)
+    E = -(T @ (beta[:, None] * (Kb @ S)) + T @ (beta[:, None] * (Lm @ bV)))
+    O = Qb @ S + P1 @ E + P2 @ bV
+    S_C = gam * S + (k * np.exp2(suf + l2)).T @ E + (k * np.exp2(suf)).T @ bV
+    return O, S_C
+
+
+def exact_chunk_forward(q, k, v, la, beta, S0=None, C=32, order=0, dtype=np.float32):
+    """exact_chunk_step over a whole sequence (the last chunk may be partial)."""
+    T, dk = q.shape
+    S = np.zeros((dk, v.shape[1])) if S0 is None else np.array(S0, dtype=np.float64)
+    O = np.zeros((T, v.shape[1]))
+    for c0 in range(0, T, C):
+        c1 = min(T, c0 + C)
+        O[c0:c1], S = exact_chunk_step(q[c0:c1], k[c0:c1], v[c0:c1], la[c0:c1], beta[c0:c1], S, order, dtype)
+    return O, S

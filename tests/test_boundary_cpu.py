@@ -299,3 +299,40 @@ def test_bwd_refuses_unsupported_shapes(lib):
     assert backward(lib, dims(order=1), ws_bytes=1 << 20) == UNSUPPORTED
     assert "erase-first" in lib.kda_last_error().decode()
     assert backward(lib, dims(dk=64, dv=128), ws_bytes=1 << 20) == UNSUPPORTED
+
+
+def _cpu_prefill_inputs(T=40, H=2, dk=32, dv=16, N=2):
+    import torch
+    q = torch.zeros(T, H, dk, dtype=torch.bfloat16)
+    return dict(q=q, k=q.clone(), v=torch.zeros(T, H, dv, dtype=torch.bfloat16),
+                log_a=torch.zeros(T, H, dk), beta=torch.zeros(T, H),
+                cu_seqlens=torch.tensor([0, 25, T], dtype=torch.int32)), (T, H, dk, dv, N)
+
+
+@pytest.mark.parametrize("which", ["out", "final_state"])
+def test_prefill_rejects_wrong_output_shapes(which):
+    """The library cannot see sizes: a too-small output tensor is refused by the
+    binding (ValueError) before any device check or call."""
+    import torch
+    inp, (T, H, dk, dv, N) = _cpu_prefill_inputs()
+    bad = {"out": torch.zeros(T - 1, H, dv, dtype=torch.bfloat16),
+           "final_state": torch.zeros(N, H, dk, dv - 1)}[which]
+    with pytest.raises(ValueError, match=which):
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], cu_seqlens=inp["cu_seqlens"],
+                      **{which: bad})
+    with pytest.raises(RuntimeError, match="no CPU path"):  # right shapes: refused for the device
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], cu_seqlens=inp["cu_seqlens"])
+
+
+@pytest.mark.parametrize("which", ["out", "S_out"])
+def test_decode_rejects_wrong_output_shapes(which):
+    import torch
+    N, H, dk, dv = 3, 2, 32, 16
+    q = torch.zeros(N, H, dk, dtype=torch.bfloat16)
+    args = (q, q.clone(), torch.zeros(N, H, dv, dtype=torch.bfloat16), torch.zeros(N, H, dk), torch.zeros(N, H),
+            torch.zeros(N, H, dk, dv))
+    bad = {"out": torch.zeros(N, H, dv + 1, dtype=torch.bfloat16), "S_out": torch.zeros(N - 1, H, dk, dv)}[which]
+    with pytest.raises(ValueError, match=which):
+        kda.decode_step(*args, **{which: bad})
+    with pytest.raises(RuntimeError, match="no CPU path"):
+        kda.decode_step(*args)

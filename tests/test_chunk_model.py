@@ -96,3 +96,36 @@ def test_factored_operators_in_bf16_meet_bf16_bar():
     ro, rS = oracle_one(q, k, v, la, beta, S0)
     o, S = chunk_forward_split(q, k, v, la, beta, S0=S0, C=32, bf16=True)
     assert rel(o, ro) < 2e-2 and rel(S, rS) < 2e-2
+
+
+@pytest.mark.parametrize("order", [0, 1])
+@pytest.mark.parametrize("steep", [-9.0, -12.0, -25.0, -80.0, -1000.0])
+def test_exact_path_equals_token_loop_for_steep_decay(steep, order):
+    """The steep-chunk path of the kernels (one exponential of a running sum of
+    consecutive log2 decays per term, float32) against the oracle, with a steep
+    stretch in the middle of the sequence on two channels in three: within 1e-6,
+    far inside the fp32 bar, for any decay."""
+    from tests.chunk_model import exact_chunk_forward
+    q, k, v, la, beta, S0 = draw(150, 24, 8, seed=int(-steep) + order, s0=0.3)
+    la = la.copy()
+    la[40:76, np.arange(24) % 3 != 0] = steep
+    o, S = exact_chunk_forward(q, k, v, la, beta, S0, C=32, order=order)
+    ro, rS = kda_oracle(q[:, None], k[:, None], v[:, None], la[:, None], beta[:, None], S0=S0[None, None],
+                        order=order)
+    assert rel(o, ro[:, 0]) < 1e-6 and rel(S, rS[0, 0]) < 1e-6
+
+
+def test_difference_of_prefix_sums_is_what_the_exact_path_avoids():
+    """Why the exponents are running sums: with a steep stretch the chunk's prefix
+    sums reach thousands (log2), and a factor formed as 2^(P_t - P_i) carries
+    float32 rounding of that size, far above the fp32 bar for a factor near 1."""
+    r = np.random.default_rng(0)
+    l2 = np.concatenate([np.full(24, -115.0), -r.random(8)]).astype(np.float32)
+    P = np.cumsum(l2, dtype=np.float32)
+    exact = float(np.sum(l2[27:31].astype(np.float64)))
+    diff = float(P[30] - P[26])
+    run = np.float32(0)
+    for x in l2[27:31]:
+        run = np.float32(run + x)
+    assert abs(float(run) - exact) < 1e-6
+    assert abs(diff - exact) > 1e-5

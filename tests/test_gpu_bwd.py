@@ -81,23 +81,24 @@ def test_bwd_scalar_gate_fp32():
     check(inp, gpu_grad(inp), TOL[torch.float32], "fp32 scalar gate")
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("steep", [-10.5, -25.0])
-def test_bwd_steep_decay_takes_exact_terms(dtype, steep):
-    # 16-token pieces spanning 168 or 400 nats, beyond the backward's factor split
-    # (160 nats), so they take one exponent per term.  The steep stretch lies in the
-    # first 64 tokens: their gradients start from S0 and need no state kept by the
-    # forward rerun, whose own factor split is accurate for log a >= -8 per token.
+@pytest.mark.parametrize("dtype,steep", [(torch.float32, -10.5), (torch.float32, -25.0), (torch.bfloat16, -10.5),
+                                         (torch.bfloat16, -25.0), (torch.bfloat16, -80.0)])
+def test_bwd_steep_decay_mid_sequence(dtype, steep):
+    # One 120-token sequence with log a = steep on tokens 30-55: 16-token pieces
+    # spanning up to 1280 nats, beyond the backward's factor split (160 nats), take
+    # one exponent per term, and the chunk states after the stretch come from the
+    # forward rerun, whose chunks with tokens below log2 a = -12 take their own
+    # exact path.
     base = "kda_t64_d16_fp32" if dtype == torch.float32 else "kda_b2_h32_t32768_d128_bf16"
     d = 32 if dtype == torch.float32 else 64
-    inp = draw(base, 6, [62, 40], dk=d, dv=d)
+    inp = draw(base, 6, [120], dk=d, dv=d)
     la = inp["log_a"].clone()
-    la[30:55] = steep
+    la[30:56] = steep
     inp["log_a"] = la
     got = gpu_grad(inp)
     for n in NAMES:
         assert torch.isfinite(got[n].float()).all(), n
-    check(inp, got, TOL[dtype], f"steep decay {dtype}")
+    check(inp, got, TOL[dtype], f"steep decay {dtype} mid-sequence")
 
 
 def test_bwd_without_optional_arguments():

@@ -44,21 +44,18 @@ def test_decode_chain_small(dtype, dk, dv, scalar):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
-def test_decode_full_size_sampled():
-    """256 sequences x 32 heads, dk = dv = 128, 100 chained steps; every state
-    and output is produced on the GPU, 48 (sequence, head) states are checked."""
-    log("decode full size: 256 x 32 heads, 100 steps")
+@pytest.mark.timeout(300)
+def test_decode_full_size():
+    """256 sequences x 32 heads, dk = dv = 128, 100 chained steps: every one of
+    the 8192 states and every output of every step against the oracle."""
+    log("decode full size: 256 x 32 heads, 100 steps, all states")
     w = WORKLOADS["kda_decode_b256_h32_d128"]
     inp = generate(w, seed=4, device=DEV)
     o, S = run_chain(inp)
-    rng = np.random.default_rng(0)
-    ns = rng.integers(0, w.n_seqs, 48)
-    hs = rng.integers(0, w.heads, 48)
-    sub = {key: val[:, ns, hs][:, :, None] for key, val in inp.items() if key != "S"}
-    sub["S"] = inp["S"][ns, hs][:, None]
-    seq, steps, N = decode_as_sequence({k: v.cpu() for k, v in sub.items()})
+    seq, steps, N = decode_as_sequence({k: v.cpu() for k, v in inp.items()})
+    del inp
     ro, rS = oracle_all(seq)
-    go = np64(o[:, ns, hs])[:, :, None].transpose(1, 0, 2, 3).reshape(ro.shape)
-    eo, es = max_rel_err(go, ro), max_rel_err(S[ns, hs], rS[:, 0])
-    log(f"  err o {eo:.2e} S {es:.2e}")
+    go = np64(o).transpose(1, 0, 2, 3).reshape(ro.shape)
+    eo, es = max_rel_err(go, ro), max_rel_err(S, rS)
+    log(f"  err o {eo:.2e} S {es:.2e} over {N * w.heads} states")
     assert eo <= 2e-2 and es <= 2e-2
