@@ -202,6 +202,28 @@ KDA_API int kda_chunk_fwd_ex(const kda_dims_t* dims, const kda_prologue_t* prolo
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_fwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The call allocates nothing; it takes the two-pass
+ * workspace from a fixed array of KDA_NOALLOC_SCRATCH_BYTES in device memory,
+ * one per GPU, held from the library's first use on that GPU until the process
+ * ends.  Arguments, layouts and results are those of kda_chunk_fwd (method,
+ * chunk and dv split from dims; no prologue, no snapshots).  When S_T is given
+ * it holds the running state, and the scratch holds only operator blocks: a
+ * call needs units x 37,376 bytes for one chunk per (sequence, head) at dk = 128
+ * (units x 20,736 at dk = 64), plus units x dk x dv x 4 when S_T is NULL, and
+ * fails with KDA_ERR_INVALID_ARGUMENT (nothing enqueued) when that exceeds the
+ * scratch; larger segments of chunks run when more fits.  Shapes without a
+ * two-pass kernel run single-pass and use no scratch.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+KDA_API int kda_chunk_fwd_noalloc(const kda_dims_t* dims, const void* q, const void* k, const void* v,
+                                  const float* log_a, const float* beta, const float* S0,
+                                  const int32_t* cu_seqlens, void* o, float* S_T, void* stream);
+
+/*
  * Workspace the two-pass prefill prefers for these dims (segments of up to
  * 4 GiB of operator blocks: about 1.2 KB per token and head at dk = 128, so a
  * whole 2 x 32-head x 32K-token batch runs as one segment), or 0 if the call

@@ -110,6 +110,8 @@ def load_library(build_if_missing: bool = True):
                 fn = getattr(lib, name)
                 fn.restype = ctypes.c_int
                 fn.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(ctypes.c_size_t)]
+            lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+            lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P]
             lib.kda_decode_step.restype = ctypes.c_int
             lib.kda_decode_step.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P]
             lib.kda_status_string.restype = ctypes.c_char_p
@@ -236,8 +238,20 @@ def chunk_fwd_snapshots(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, snaps
                     method, workspace, max_seqlen, int(snapshot_every), snapshots, order, prologue)
 
 
+def chunk_fwd_noalloc(q, k, v, log_a, beta, S0=None, cu_seqlens=None, *, chunk_size: int = 0,
+                      dv_split: int = 0, out=None, final_state=True, num_seqs: int | None = None,
+                      method: int = METHOD_AUTO, max_seqlen: int | None = None, order: int = ORDER_ERASE_FIRST):
+    """chunk_fwd through kda_chunk_fwd_noalloc: the library allocates nothing and
+    takes its two-pass workspace from a fixed device array (KDA_NOALLOC_SCRATCH_BYTES,
+    128 MiB per GPU).  Outputs are allocated here unless `out` / `final_state`
+    tensors are passed.  Calls that overlap on one GPU share that array and race."""
+    o, ST, _ = _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state, num_seqs,
+                        method, None, max_seqlen, 0, None, order, None, noalloc=True)
+    return o, ST
+
+
 def _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, final_state, num_seqs,
-             method, workspace, max_seqlen, snapshot_every, snapshots, order, prologue):
+             method, workspace, max_seqlen, snapshot_every, snapshots, order, prologue, noalloc=False):
     lib = load_library()
     _need(q, "q", ndim=3)
     T, H, dk = q.shape
@@ -288,6 +302,11 @@ def _prefill(q, k, v, log_a, beta, S0, cu_seqlens, chunk_size, dv_split, out, fi
             max_seqlen = 0
     d = _Dims(N, H, T, dk, dv, _dtype_code(q), scalar, int(chunk_size), int(dv_split), int(method), int(order),
               int(max_seqlen))
+    if noalloc:
+        st = lib.kda_chunk_fwd_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
+                                       _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(ST), _stream_handle(q.device))
+        _check(lib, st)
+        return o, ST, None
     if workspace is None and method != METHOD_SINGLE:
         need = ctypes.c_size_t(0)
         _check(lib, lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(need)))

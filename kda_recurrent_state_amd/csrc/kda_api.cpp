@@ -1,11 +1,13 @@
 // kda_api.cpp -- the extern "C" entry points declared in include/kda.h.
 //
 // Host-side argument validation, choice of kernel configuration, launch on the
-// caller's stream.  Nothing here allocates device memory or keeps state other
-// than the thread-local text of the last error.
+// caller's stream.  Nothing here allocates device memory.  State kept: the
+// thread-local text of the last error, and per device the address of the fixed
+// scratch array that kda_chunk_fwd_noalloc uses (looked up on its first call).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <mutex>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -13,6 +15,12 @@
 
 #include "../../include/kda.h"
 #include "kda_launch.hpp"
+
+// Scratch of kda_chunk_fwd_noalloc (the two-pass workspace of a caller that
+// cannot allocate): a fixed array in device memory, of which every GPU the
+// library runs on holds its own copy until the process ends.  Host code uses
+// only the per-device address from hipGetSymbolAddress, never this name.
+static __device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -226,10 +234,16 @@ int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, c
                             snapshot_every, workspace, workspace_bytes, stream);
 }
 
-int kda_chunk_fwd_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const void* q, const void* k,
-                     const void* v, const float* log_a, const float* beta, const float* S0,
-                     const int32_t* cu_seqlens, void* o, float* S_T, float* snapshots, int64_t snapshot_rows,
-                     int64_t snapshot_every, void* workspace, size_t workspace_bytes, void* stream) {
+// The prefill behind every kda_chunk_fwd* entry point.  Workspace layout: the
+// running states of all units (state_off bytes), then the operator blocks.  The
+// public entry points always reserve the states (their documented minimum);
+// kda_chunk_fwd_noalloc reserves them only when S_T is NULL (otherwise S_T holds
+// the running state), which leaves its fixed scratch to the blocks.
+static int chunk_fwd_impl(const kda_dims_t* d, const kda_prologue_t* prologue, const void* q, const void* k,
+                          const void* v, const float* log_a, const float* beta, const float* S0,
+                          const int32_t* cu_seqlens, void* o, float* S_T, float* snapshots, int64_t snapshot_rows,
+                          int64_t snapshot_every, void* workspace, size_t workspace_bytes, bool reserve_states,
+                          void* stream) {
     Plan pl;
     int st = plan_prefill(d, cu_seqlens != nullptr, &pl);
     if (st) return st;
@@ -279,11 +293,13 @@ int kda_chunk_fwd_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const 
 
     // method
     bool two_pass = false;
+    const size_t state_off = (reserve_states || !S_T) ? pl.state_bytes : 0;
     if (pl.two_pass_ok) {
-        const bool have_ws = workspace && workspace_bytes >= pl.min_bytes;
+        const size_t need = state_off + (size_t)pl.units * pl.block;
+        const bool have_ws = workspace && workspace_bytes >= need;
         if (d->method == KDA_METHOD_TWO_PASS && !have_ws)
             return fail(KDA_ERR_INVALID_ARGUMENT, "two-pass prefill needs a workspace of at least %zu bytes (got %zu)",
-                        pl.min_bytes, workspace ? workspace_bytes : (size_t)0);
+                        need, workspace ? workspace_bytes : (size_t)0);
         two_pass = have_ws;
     }
     if (pro.any() && !two_pass)
@@ -292,7 +308,7 @@ int kda_chunk_fwd_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const 
     if (two_pass) {
         if ((uintptr_t)workspace & 255u) return fail(KDA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
         const size_t per_chunk = (size_t)pl.units * pl.block;
-        int64_t m = (int64_t)((workspace_bytes - pl.state_bytes) / per_chunk);
+        int64_t m = (int64_t)((workspace_bytes - state_off) / per_chunk);
         if (m > pl.max_chunks) m = pl.max_chunks;
         if (m < 1) m = 1;
         if (pl.units * m > 0x7fffffff || pl.units * pl.split > 0x7fffffff)
@@ -300,7 +316,7 @@ int kda_chunk_fwd_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const 
         const int64_t nseg = pl.max_chunks > 0 ? (pl.max_chunks + m - 1) / m : 1;
         uint8_t* ws = static_cast<uint8_t*>(workspace);
         float* run = S_T ? S_T : reinterpret_cast<float*>(ws);
-        uint8_t* blocks = ws + pl.state_bytes;
+        uint8_t* blocks = ws + state_off;
         const int64_t eq_len = cu_seqlens ? 0 : d->total_tokens / d->num_seqs;
         for (int64_t sgi = 0; sgi < nseg; ++sgi) {
             const int64_t chunk0 = sgi * m;
@@ -352,6 +368,64 @@ int kda_chunk_fwd_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const 
     return ok();
 }
 
+
+int kda_chunk_fwd_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const void* q, const void* k,
+                     const void* v, const float* log_a, const float* beta, const float* S0,
+                     const int32_t* cu_seqlens, void* o, float* S_T, float* snapshots, int64_t snapshot_rows,
+                     int64_t snapshot_every, void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_fwd_impl(d, prologue, q, k, v, log_a, beta, S0, cu_seqlens, o, S_T, snapshots, snapshot_rows,
+                          snapshot_every, workspace, workspace_bytes, true, stream);
+}
+
+// Per-device address of `scratch`, looked up once per device with that device
+// current (each GPU holds its own copy of the array at its own address).
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64] = {};
+
+static int scratch_address(void* stream, void** out) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(KDA_ERR_HIP, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(KDA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
+int kda_chunk_fwd_noalloc(const kda_dims_t* d, const void* q, const void* k, const void* v, const float* log_a,
+                          const float* beta, const float* S0, const int32_t* cu_seqlens, void* o, float* S_T,
+                          void* stream) {
+    Plan pl;
+    int st = plan_prefill(d, cu_seqlens != nullptr, &pl);
+    if (st) return st;
+    if (!pl.two_pass_ok || d->num_seqs == 0)  // single-pass: no scratch at all
+        return chunk_fwd_impl(d, nullptr, q, k, v, log_a, beta, S0, cu_seqlens, o, S_T, nullptr, 0, 0, nullptr, 0,
+                              false, stream);
+    const size_t need = (S_T ? 0 : pl.state_bytes) + (size_t)pl.units * pl.block;
+    if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "the two-pass prefill of %lld (sequence, head) units needs %zu bytes of scratch%s; the fixed "
+                    "scratch holds %zu (use kda_chunk_fwd with a workspace, or the single-pass method)",
+                    (long long)pl.units, need, S_T ? "" : " (S_T is NULL: the running states too)",
+                    (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((st = scratch_address(stream, &ws))) return st;
+    return chunk_fwd_impl(d, nullptr, q, k, v, log_a, beta, S0, cu_seqlens, o, S_T, nullptr, 0, 0, ws,
+                          (size_t)KDA_NOALLOC_SCRATCH_BYTES, false, stream);
+}
+
 }  // extern "C"
 
 namespace {
@@ -363,6 +437,7 @@ struct BwdPlan {
     size_t fwd_ws = 0, o_bytes = 0, snap_bytes = 0, ops_bytes = 0, x_bytes = 0, scr_bytes = 0, total = 0;
     int64_t snap_rows = 0, maxlen = 0;
 };
+
 
 int plan_bwd(const kda_dims_t* d, bool have_cu, BwdPlan* bp) {
     int st = plan_prefill(d, have_cu, &bp->fwd);

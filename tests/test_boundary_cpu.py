@@ -336,3 +336,20 @@ def test_decode_rejects_wrong_output_shapes(which):
         kda.decode_step(*args, **{which: bad})
     with pytest.raises(RuntimeError, match="no CPU path"):
         kda.decode_step(*args)
+
+
+def test_noalloc_rejects_beyond_its_scratch(lib):
+    """kda_chunk_fwd_noalloc refuses, before touching a device, a two-pass call
+    whose one-chunk segment does not fit its fixed scratch (4096 units x 37,376
+    bytes > 128 MiB), and says so."""
+    P = lambda x: ctypes.c_void_p(x)
+    d = dims(num_seqs=1, num_heads=4096, total_tokens=64, method=2)
+    st = lib.kda_chunk_fwd_noalloc(ctypes.byref(d), P(GOOD), P(GOOD), P(GOOD), P(GOOD), P(GOOD), None, P(GOOD),
+                                   P(GOOD), P(GOOD), None)
+    assert st == INVALID
+    assert b"scratch" in lib.kda_last_error()
+    # without S_T the running states count too: 1400 units x (64 KiB + 37,376 bytes) > 128 MiB
+    d = dims(num_seqs=1, num_heads=1400, total_tokens=64, method=2)
+    st = lib.kda_chunk_fwd_noalloc(ctypes.byref(d), P(GOOD), P(GOOD), P(GOOD), P(GOOD), P(GOOD), None, P(GOOD),
+                                   P(GOOD), None, None)
+    assert st == INVALID and b"S_T is NULL" in lib.kda_last_error()

@@ -1,0 +1,59 @@
+"""The allocation-free prefill entry point (kda_chunk_fwd_noalloc) on the GPU:
+two calls in a row, the second on a smaller input, each against kda_chunk_fwd
+(the entry point with a caller-owned workspace) on the same inputs."""
+import pytest
+import torch
+
+import kda_recurrent_state_amd as kda
+from kda_recurrent_state_amd.workloads import WORKLOADS, generate, scaled
+from tests.parity import TOL, log, max_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def both(inp, **kw):
+    args = (inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"])
+    ref = kda.chunk_fwd(*args, S0=inp["S0"], cu_seqlens=inp["cu_seqlens"], **kw)
+    got = kda.chunk_fwd_noalloc(*args, S0=inp["S0"], cu_seqlens=inp["cu_seqlens"], **kw)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+def compare(ref, got, what):
+    eo = max_rel_err(got[0], ref[0])
+    es = 0.0 if ref[1] is None else max_rel_err(got[1], ref[1])
+    same = torch.equal(got[0], ref[0]) and (ref[1] is None or torch.equal(got[1], ref[1]))
+    log(f"  {what}: err o {eo:.2e} S {es:.2e} bit-identical {same}")
+    assert eo <= TOL[torch.bfloat16] and es <= TOL[torch.bfloat16]
+
+
+def test_noalloc_two_calls_second_smaller():
+    # 1st: 2 x 16 heads x 8192 tokens at d = 128 needs several segments of the
+    # 128 MiB scratch (32 units x 37,376 bytes per chunk: 112 chunks per segment)
+    log("noalloc call 1: 2 x 16 heads x 8192 tokens, d = 128")
+    w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seqlen=8192, heads=16)
+    big = generate(w, seed=61, device=DEV)
+    compare(*both(big), "call 1")
+    # 2nd, smaller and ragged, with a steep stretch (marked chunks re-formed in the scratch)
+    log("noalloc call 2: ragged [300, 7, 161] x 2 heads, steep stretch")
+    w2 = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=3, heads=2)
+    small = generate(w2, seed=62, device=DEV, lengths=[300, 7, 161])
+    la = small["log_a"].clone()
+    la[100:140, :, ::2] = -30.0
+    small["log_a"] = la.contiguous()
+    compare(*both(small), "call 2")
+    # 3rd: without S_T the running states live in the scratch too
+    log("noalloc call 3: no final state")
+    compare(*both(small, final_state=False), "call 3")
+
+
+def test_noalloc_dk64_and_single_pass_shapes():
+    log("noalloc dk = 64 (two-pass) and fp32 (single-pass, no scratch)")
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=2, heads=3, dk=64, dv=64)
+    inp = generate(w, seed=63, device=DEV, lengths=[500, 77])
+    compare(*both(inp), "dk 64")
+    w32 = scaled(WORKLOADS["kda_t64_d16_fp32"], n_seqs=2, heads=2, dk=32, dv=32)
+    inp32 = generate(w32, seed=64, device=DEV, lengths=[90, 33])
+    ref, got = both(inp32)
+    assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
