@@ -11,13 +11,19 @@ prefill batch is also timed with state snapshots every 1024 tokens, with the
 decay-first ordering, and from raw inputs through the input prologue (against
 torch transforming them first), and the decode leg with the decay-first
 ordering ("variants", "decode.decay_first").  The gradient of the same prefill
-(kda_chunk_bwd, for seeded upstream derivatives) is timed as "backward".
+(kda_chunk_bwd, for seeded upstream derivatives) is timed as "backward".  Two
+more prefill workloads get their own timing, roofline and parity under "legs":
+Gated DeltaNet (scalar decay, 16 heads x 4096 tokens) and 64 packed sequences
+of 512 to 16384 tokens x 32 heads.  The headline batch's every output and final
+state is checked against the fp64 oracle ("parity"), whose run is also the CPU
+baseline.
 
 Timing uses HIP events recorded on the stream the kernels are launched on
 (torch's current stream, which the library receives).  The fp64 CPU oracle is
 timed afterwards on a bounded sample of the same prefill workload.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-variants]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-variants] [--no-backward] [--no-legs]
+                    [--only prefill|decode|gdn|varlen]
     python bench.py --copy-calibration   # plain device copy of known size, for counters
     python bench.py --record-traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
         # writes profiles/traffic_counters.json from four rocprofv3 --pmc output
@@ -61,18 +67,27 @@ def source_hash(kind):
     return h.hexdigest()[:16]
 
 
-def prefill_algorithmic(w, chunk_alg=64):
+def prefill_algorithmic(w, chunk_alg=64, tokens=None):
     """Algorithmic bytes and flops of one prefill pass (what the method must move
     and compute, not what the kernel executes).  Bytes per token-head: q, k, v
-    in bf16, log_a fp32 per channel, beta fp32, o bf16; plus S0 read and S_T
-    written once per (sequence, head).  Flops per chunk of C tokens per head:
-    10 C^2 dk + 6 C^2 dv + 8 C dk dv + (2/3) C^3 (four C x C Gram products, W,
-    U, E, O, the two state products, and the triangular solve) at C = 64."""
-    th = w.n_seqs * w.seqlen * w.heads
-    per_th = 2 * (2 * w.dk + w.dv) + 4 * w.dk + 4 + 2 * w.dv
-    states = w.n_seqs * w.heads * 2 * 4 * w.dk * w.dv
+    in bf16, log_a fp32 per channel (GDN: one fp32 per token-head), beta fp32,
+    o bf16; plus S0 read (when the workload has one) and S_T written once per
+    (sequence, head).  Flops per chunk of C tokens per head:
+      KDA: 10 C^2 dk + 6 C^2 dv + 8 C dk dv + (2/3) C^3 (four C x C Gram products,
+           W, U, E, O, the two state products, the triangular solve);
+      GDN: 6 C^2 dk + 4 C^2 dv + 6 C dk dv + (2/3) C^3 (two Gram products with a
+           scalar decay mask, and one state-side product fewer).
+    `tokens`: total tokens when the lengths vary (default n_seqs * seqlen)."""
+    T = tokens if tokens is not None else w.n_seqs * w.seqlen
+    th = T * w.heads
+    la_bytes = 4 if w.scalar_decay else 4 * w.dk
+    per_th = 2 * (2 * w.dk + w.dv) + la_bytes + 4 + 2 * w.dv
+    states = w.n_seqs * w.heads * (2 if w.s0_std > 0 else 1) * 4 * w.dk * w.dv
     C, dk, dv = chunk_alg, w.dk, w.dv
-    per_chunk = 10 * C * C * dk + 6 * C * C * dv + 8 * C * dk * dv + (2.0 / 3.0) * C ** 3
+    if w.scalar_decay:
+        per_chunk = 6 * C * C * dk + 4 * C * C * dv + 6 * C * dk * dv + (2.0 / 3.0) * C ** 3
+    else:
+        per_chunk = 10 * C * C * dk + 6 * C * C * dv + 8 * C * dk * dv + (2.0 / 3.0) * C ** 3
     return th * per_th + states, th * per_chunk / C
 
 
@@ -111,6 +126,42 @@ def stored_traffic(kind, launch_bytes):
     return ent.get("hbm_bytes_per_launch")
 
 
+def max_rel(x, r):
+    """max |x - r| / max |r| over one whole output tensor (GPU tensor x, fp64 numpy r),
+    computed in slices so that host memory stays bounded."""
+    import numpy as np
+    num = den = 0.0
+    flat_x = x.reshape(x.shape[0], -1)
+    flat_r = r.reshape(r.shape[0], -1)
+    step = max(1, (1 << 26) // max(1, flat_r.shape[1]))
+    for a in range(0, flat_r.shape[0], step):
+        xs = flat_x[a:a + step].double().cpu().numpy()
+        rs = flat_r[a:a + step]
+        num = max(num, float(np.abs(xs - rs).max()))
+        den = max(den, float(np.abs(rs).max()))
+    return num / den if den > 0 else num
+
+
+def host_info(threads):
+    """The host the CPU baseline ran on: CPUs visible, CPUs this process may use,
+    the CPU model, and the oracle's thread count (at most 16: the host CPU share
+    that goes with one GPU on a shared machine)."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = None
+    return {"nproc": os.cpu_count(), "affinity_cpus": aff, "cpu_model": model, "oracle_threads": threads}
+
+
 def time_events(fn, iters, stream):
     import torch
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -136,7 +187,8 @@ def copy_calibration(steps):
 
 
 # kernels whose per-dispatch counters add up to one call of each measured entry point
-KERNEL_SYMBOLS = {"prefill": ["kda_prep2_kernel", "kda_scan_kernel"], "decode": ["kda_decode_kernel"]}
+KERNEL_SYMBOLS = {"prefill": ["kda_prep2_kernel", "kda_prep2_exact_kernel", "kda_scan_kernel"],
+                  "decode": ["kda_decode_kernel"]}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -188,6 +240,74 @@ def record_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
     print(json.dumps(out, indent=1))
 
 
+def prefill_leg(leg, args, kda, dev, stream):
+    """One more prefill workload, timed like the headline one (HIP events on the
+    launch stream, inputs resident, default method and workspace):
+      gdn    -- Gated DeltaNet (scalar log a per token and head), 1 x 16 heads x 4096
+                tokens, d = 128, bf16, S0 = 0: whole batch checked against the oracle;
+      varlen -- KDA, 64 packed sequences of U[512, 16384] tokens x 32 heads, d = 128,
+                per-sequence S0: two sequences (all heads) checked against the oracle
+                (every unit is checked by the GPU test suite)."""
+    import numpy as np
+    import torch
+    from kda_recurrent_state_amd.workloads import WORKLOADS, generate
+    from oracle import kda_oracle
+    name = {"gdn": "gdn_h16_t4096_d128_bf16", "varlen": "kda_varlen_64seq_h32_d128"}[leg]
+    w = WORKLOADS[name]
+    log(f"leg {leg}: generating {name}")
+    x = generate(w, seed=2 if leg == "gdn" else 5, device=dev)
+    T = int(x["q"].shape[0])
+    lens = np.asarray(x["lengths"], dtype=np.int64)
+    maxlen = int(lens.max())
+    o = torch.empty((T, w.heads, w.dv), dtype=w.dtype, device=dev)
+    ST = torch.empty((w.n_seqs, w.heads, w.dk, w.dv), dtype=torch.float32, device=dev)
+    wsb = kda.chunk_workspace_size(x["q"], x["v"], num_seqs=w.n_seqs, scalar_decay=w.scalar_decay,
+                                   max_seqlen=maxlen)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+
+    def step():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["log_a"], x["beta"], S0=x["S0"], cu_seqlens=x["cu_seqlens"],
+                      out=o, final_state=ST, workspace=ws, max_seqlen=maxlen)
+    for _ in range(max(args.warmup, 3)):
+        step()
+    torch.cuda.synchronize()
+    t = time_events(step, args.steps, stream) / args.steps
+    B, F64 = prefill_algorithmic(w, 64, tokens=T)
+    _, F32 = prefill_algorithmic(w, 32, tokens=T)
+    gbs = B / t / 1e9
+    res = {"workload": name, "tokens": T, "ms_per_step": t * 1e3, "tokens_per_s": T / t,
+           "method": "two-pass" if wsb else "single", "chunk": 32, "workspace_MiB": round(wsb / 2**20, 1),
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": gbs / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes_per_launch": B,
+                        "avg_launch_ms": t * 1e3},
+           "mfma": {"algorithmic_tflop_at_C64": F64 / 1e12, "pct_peak": 100.0 * F64 / t / 1e12 / PEAK_BF16_TFLOPS,
+                    "pct_peak_at_run_chunk": 100.0 * F32 / t / 1e12 / PEAK_BF16_TFLOPS}}
+    if leg == "gdn":
+        res["note"] = ("the workload names C = 64; at d = 128 the kernels run C = 32 (a 64-token operator block "
+                       "of 82 KB does not fit the state pass's LDS ring)")
+        seqs = list(range(w.n_seqs))
+    else:
+        seqs = [int(np.argmax(lens)), int(np.argmin(lens))]
+    # parity on the timed output
+    cu = x["cu_seqlens"].cpu().numpy().astype(np.int64)
+    eo = es = 0.0
+    for n in seqs:
+        a, b = int(cu[n]), int(cu[n + 1])
+        h = {k_: x[k_][a:b].cpu() for k_ in ("q", "k", "v", "log_a", "beta")}
+        S0 = None if x["S0"] is None else x["S0"][n:n + 1].cpu()
+        ro, rS = kda_oracle(h["q"], h["k"], h["v"], h["log_a"], h["beta"], S0=S0)
+        eo = max(eo, max_rel(o[a:b], ro))
+        es = max(es, max_rel(ST[n:n + 1], rS))
+    res["parity"] = {"o_max_rel_err": eo, "S_T_max_rel_err": es, "tol": 2e-2,
+                     "checked": "whole batch" if leg == "gdn" else
+                                f"sequences {seqs} (longest, shortest), all heads"}
+    log(f"leg {leg}: {t*1e3:.3f} ms/step, {T/t/1e6:.2f} Mtok/s, {gbs:.0f} GB/s ({100*gbs/PEAK_HBM_GBS:.1f}%), "
+        f"parity o {eo:.2e} S {es:.2e}")
+    del x, o, ST, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,7 +318,8 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="skip the snapshot and decay-first legs")
     ap.add_argument("--no-backward", action="store_true", help="skip the gradient leg")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "gdn", "varlen"], default=None)
+    ap.add_argument("--no-legs", action="store_true", help="skip the Gated DeltaNet and varlen prefill legs")
     ap.add_argument("--method", choices=["auto", "single", "two-pass"], default="auto")
     ap.add_argument("--workspace-mib", type=int, default=0, help="two-pass workspace size (default: preferred)")
     ap.add_argument("--record-traffic", nargs=4, metavar="DIR", default=None)
@@ -242,7 +363,8 @@ def main():
                       args.workspace_mib << 20)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
         used = "two-pass" if wsb else "single"
-        log(f"prefill method {used}, workspace {wsb / 2**20:.1f} MiB")
+        chunk_run = 32  # chunk_size 0: the library's default chunk (include/kda.h)
+        log(f"prefill method {used}, chunk {chunk_run}, workspace {wsb / 2**20:.1f} MiB")
 
         def step():
             kda.chunk_fwd(x["q"], x["k"], x["v"], x["log_a"], x["beta"], S0=x["S0"],
@@ -267,13 +389,14 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic: seeded tensors with the layer's shapes and value distributions (no dataset)",
             "config": {"workload": wp.name, "batch": wp.n_seqs, "heads": wp.heads, "seq_len": wp.seqlen,
-                       "dk": wp.dk, "dv": wp.dv, "state": "fp32", "chunk": 32, "dv_split": "auto",
+                       "dk": wp.dk, "dv": wp.dv, "state": "fp32", "chunk": chunk_run, "dv_split": "auto",
                        "method": used, "workspace_MiB": round(wsb / 2**20, 1)},
         })
         # One prefill call is the unit: with the two-pass method it is one launch of the
         # operator pass and one of the state pass (a single segment at the preferred
         # workspace); the bytes are the method's algorithmic bytes, not the workspace's.
-        kernels = "kda_prep2_kernel + kda_scan_kernel" if used == "two-pass" else "kda_chunk_kernel"
+        kernels = ("kda_prep2_kernel + kda_prep2_exact_kernel + kda_scan_kernel" if used == "two-pass"
+                   else "kda_chunk_kernel")
         out["roofline"] = {
             "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": gbs / PEAK_HBM_GBS,
@@ -281,19 +404,32 @@ def main():
             "kernel": kernels, "algorithmic_bytes_per_launch": B,
             "avg_launch_ms": per * 1e3,
         }
+        _, F_run = prefill_algorithmic(wp, chunk_run)
         out["mfma"] = {"algorithmic_tflop_per_launch": F / 1e12, "achieved_tflops": tflops,
                        "peak_tflops": PEAK_BF16_TFLOPS, "pct_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
-                       "note": "algorithmic flops at C=64; bf16 dense peak"}
-        # quick parity on the timed output: first 2048 tokens of (sequence 0, head 0)
-        from oracle import kda_oracle
-        sl = lambda t: t[:2048, 0:1].cpu()
-        ro, _ = kda_oracle(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_a"]), sl(x["beta"]),
-                           S0=x["S0"][0:1, 0:1].cpu())
-        go = o[:2048, 0].double().cpu().numpy()
-        perr = float(np.abs(go - ro[:, 0]).max() / np.abs(ro).max())
-        out["parity"] = {"prefill_o_max_rel_err": perr, "tol": 2e-2, "sample": "seq 0, head 0, tokens 0..2047"}
+                       "pct_peak_at_run_chunk": 100.0 * F_run / per / 1e12 / PEAK_BF16_TFLOPS,
+                       "algorithmic_tflop_at_run_chunk": F_run / 1e12, "run_chunk": chunk_run,
+                       "note": f"pct_peak counts the algorithmic flops at C=64 (the chunk the workload names); "
+                               f"pct_peak_at_run_chunk at the C={chunk_run} the kernels run; bf16 dense peak"}
+        # parity of the whole timed batch (o and S_T of every (sequence, head)) against the
+        # fp64 oracle, whose run is also the CPU baseline below
+        from oracle import default_threads, kda_oracle
+        ncpu = default_threads()
+        log(f"oracle on the whole prefill batch, {ncpu} threads")
+        hx = {k_: x[k_].cpu() for k_ in ("q", "k", "v", "log_a", "beta", "S0")}
+        t0 = time.perf_counter()
+        ro, rS = kda_oracle(hx["q"], hx["k"], hx["v"], hx["log_a"], hx["beta"], S0=hx["S0"],
+                            cu_seqlens=x["cu_seqlens"].cpu().numpy(), threads=ncpu)
+        dt_oracle = time.perf_counter() - t0
+        del hx
+        perr = max_rel(o, ro)
+        serr = max_rel(ST, rS)
+        del ro, rS
+        out["parity"] = {"prefill_o_max_rel_err": perr, "prefill_S_T_max_rel_err": serr, "tol": 2e-2,
+                         "checked": f"every output and final state of the timed batch "
+                                    f"({wp.n_seqs} x {wp.seqlen} tokens x {wp.heads} heads)"}
         log(f"prefill: {per*1e3:.3f} ms/step, {tokens/per/1e6:.2f} Mtok/s, {gbs:.0f} GB/s, "
-            f"{tflops:.1f} TFLOP/s, parity {perr:.2e}")
+            f"{tflops:.1f} TFLOP/s, parity o {perr:.2e} S_T {serr:.2e}")
 
         if not args.no_variants:
             # the same batch through the two other prefill entries: state snapshots every
@@ -327,6 +463,7 @@ def main():
                 d1_step()
             torch.cuda.synchronize()
             t1 = time_events(d1_step, vsteps, stream) / vsteps
+            sl = lambda t: t[:2048, 0:1].cpu()
             ro1, _ = kda_oracle(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_a"]), sl(x["beta"]),
                                 S0=x["S0"][0:1, 0:1].cpu(), order=1)
             perr1 = float(np.abs(o[:2048, 0].double().cpu().numpy() - ro1[:, 0]).max() / np.abs(ro1).max())
@@ -421,18 +558,13 @@ def main():
                 f"gradient kernels {(tb-tr)*1e3:.3f} ms")
 
         if not args.no_cpu_baseline:
-            ncpu = min(16, os.cpu_count() or 1)
-            log(f"cpu oracle on the whole prefill batch, {ncpu} threads")
-            hx = {k: x[k].cpu() for k in ("q", "k", "v", "log_a", "beta", "S0")}
-            t0 = time.perf_counter()
-            kda_oracle(hx["q"], hx["k"], hx["v"], hx["log_a"], hx["beta"], S0=hx["S0"],
-                       cu_seqlens=x["cu_seqlens"].cpu().numpy(), threads=ncpu)
-            dt = time.perf_counter() - t0
+            dt = dt_oracle
             out["cpu_baseline"] = {
                 "value": tokens / dt, "unit": "tokens/s", "cores": ncpu, "kind": "oracle",
                 "sample": f"the whole timed prefill batch ({wp.n_seqs} x {wp.seqlen} tokens x "
                           f"{wp.heads} heads), fp64 token-by-token, one pass, {dt:.1f} s",
                 "gpu_speedup": (tokens / per) / (tokens / dt),
+                "host": host_info(ncpu),
             }
             log(f"cpu oracle: {tokens/dt:.0f} tokens/s ({dt:.1f} s)")
             if not args.no_backward:
@@ -466,6 +598,14 @@ def main():
                 del dO, dST
         del x, o, ST
         torch.cuda.empty_cache()
+
+    # ---------------- other prefill workloads: each its own timing, roofline and parity ----------------
+    legs = [] if args.no_legs or args.only not in (None, "gdn", "varlen") else ["gdn", "varlen"]
+    if args.only in ("gdn", "varlen"):
+        legs = [args.only]
+    for leg in legs:
+        out.setdefault("legs", {})[leg] = prefill_leg(leg, args, kda, dev, stream)
+
 
     # ---------------- decode: 256 sequences x 32 heads, 100 chained steps ----------------
     if args.only in (None, "decode"):
