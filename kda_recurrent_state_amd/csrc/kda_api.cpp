@@ -395,7 +395,7 @@ static int scratch_address(void* stream, void** out) {
             return fail(KDA_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
         void* p = nullptr;
         e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-        if (cur != dev) hipSetDevice(cur);
+        if (cur != dev) (void)hipSetDevice(cur);
         if (e != hipSuccess || !p)
             return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
         g_scratch_ptr[dev] = p;
