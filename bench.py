@@ -283,8 +283,9 @@ def prefill_leg(leg, args, kda, dev, stream):
            "mfma": {"algorithmic_tflop_at_C64": F64 / 1e12, "pct_peak": 100.0 * F64 / t / 1e12 / PEAK_BF16_TFLOPS,
                     "pct_peak_at_run_chunk": 100.0 * F32 / t / 1e12 / PEAK_BF16_TFLOPS}}
     if leg == "gdn":
-        res["note"] = ("the workload names C = 64; at d = 128 the kernels run C = 32 (a 64-token operator block "
-                       "of 82 KB does not fit the state pass's LDS ring)")
+        res["note"] = ("the workload names C = 64; at d = 128 the kernels run C = 32: a 64-token operator block "
+                       "(65 KB in the decay-first form a scalar decay runs) leaves room for two slots of the state "
+                       "pass's LDS ring, which needs three to keep its copies ahead of the walk")
         seqs = list(range(w.n_seqs))
     else:
         seqs = [int(np.argmax(lens)), int(np.argmin(lens))]

@@ -705,14 +705,14 @@ int prep_block_bytes(int dk, int chunk, int order) {
     return 0;
 }
 
-// order 1 comes with per-channel decay only (the host maps scalar decay to order 0)
+// a scalar decay comes with the decay-first order (the host's choice for the two-pass method)
 template <int DK, int C>
 static hipError_t prep_dispatch(const PrepLaunch& a, hipStream_t stream) {
     if (a.pro.any()) {
-        if (a.scalar) return prep_cfg<DK, C, true, false, true>(a, stream);
+        if (a.scalar) return prep_cfg<DK, C, true, true, true>(a, stream);
         return a.order ? prep_cfg<DK, C, false, true, true>(a, stream) : prep_cfg<DK, C, false, false, true>(a, stream);
     }
-    if (a.scalar) return prep_cfg<DK, C, true, false, false>(a, stream);
+    if (a.scalar) return prep_cfg<DK, C, true, true, false>(a, stream);
     return a.order ? prep_cfg<DK, C, false, true, false>(a, stream) : prep_cfg<DK, C, false, false, false>(a, stream);
 }
 

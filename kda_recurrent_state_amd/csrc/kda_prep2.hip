@@ -81,6 +81,8 @@ struct Prep2Lds {
     alignas(16) float Pq[4 * p2::DK];        // product of a over each token octet (exact kernel:
                                              // sum of log2 a)
     int steep[4];                            // per wavefront: a token below STEEP_LOG2
+    float ltok[p2::C];                       // scalar decay: log2 a of each token
+    float gtok[p2::C];                       // scalar decay: running sum of log2 a to each token
     int list[p2::NT];                        // exact kernel: marked items of one round
     alignas(16) float beta[p2::C];
     alignas(16) float ones[16];
@@ -436,6 +438,118 @@ __device__ __forceinline__ void prep2_init_lds(Prep2Lds& s, int tid, bool ord1) 
     }
 }
 
+// A2 of a scalar-decay chunk (after A1 has put log2 a of every token in ltok):
+// running sums referenced to the chunk start (G_t = la_0 + .. + la_t) and end
+// (X_t = la_{t+1} + .. + la_{C-1}), each summed in token order, give per-token
+// factors, so every channel of a token takes the same two exponentials:
+// Kd = k 2^G (KbT), Qb = q 2^G, KC = (k 2^X)^T, GAM = 2^{G_{C-1}}; G goes to gtok
+// for the Gram masks.  A chunk with a token below STEEP_LOG2 is marked instead
+// (GAM[0] = -1), as in the per-channel path.
+template <bool ORD1>
+__device__ __forceinline__ void prep2_scalar_operands(Prep2Lds& s, uint8_t* __restrict__ blk, const Prep2In& in,
+                                                      const float (&kscale)[8], int lane, int c2, int o) {
+    using namespace p2;
+    typedef WsBlock<DK, C, ORD1> WS;
+    float pre = 0.f, suf = 0.f, tot = 0.f;
+    for (int t = 0; t < 8 * o; ++t) pre += s.ltok[t];
+    for (int t = C - 1; t >= 8 * o + 8; --t) suf += s.ltok[t];
+    for (int t = 0; t < C; ++t) tot += s.ltok[t];
+    float G[8], X[8];
+    {
+        float run = pre;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            run += s.ltok[8 * o + j];
+            G[j] = run;
+        }
+        run = suf;
+#pragma unroll
+        for (int j = 7; j >= 0; --j) {
+            X[j] = run;
+            run += s.ltok[8 * o + j];
+        }
+    }
+    float mine = G[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mine = lane == j ? G[j] : mine;
+    if (lane < 8) s.gtok[8 * o + lane] = mine;
+    if (o == 0) {
+        const bool steep_chunk = (s.steep[0] | s.steep[1] | s.steep[2] | s.steep[3]) != 0;
+        const float gam = steep_chunk ? -1.f : __builtin_amdgcn_exp2f(tot);
+        *reinterpret_cast<f32x2*>(blk + WS::GAM + 8 * c2) = f32x2{gam, gam};
+    }
+    float fg[8], fx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        fg[j] = __builtin_amdgcn_exp2f(G[j]);
+        fx[j] = __builtin_amdgcn_exp2f(X[j]);
+    }
+    const int pos0 = kperm(8 * o), pos1 = kperm(8 * o + 4);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        float k[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const Vec2<bf16>::type kv = __builtin_bit_cast(Vec2<bf16>::type, in.k[j]);
+            k[j] = (e ? Vec2<bf16>::hi(kv) : Vec2<bf16>::lo(kv)) * kscale[j];
+        }
+        const int c = 2 * c2 + e;
+        store4(&s.KbT[c * LDC + pos0], f32x4{k[0] * fg[0], k[1] * fg[1], k[2] * fg[2], k[3] * fg[3]});
+        store4(&s.KbT[c * LDC + pos1], f32x4{k[4] * fg[4], k[5] * fg[5], k[6] * fg[6], k[7] * fg[7]});
+        bf16x8 kc;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kc[j] = (bf16)(k[j] * fx[j]);
+        *reinterpret_cast<bf16x8*>(blk + WS::KC + piece<DK>(c, o)) = kc;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const Vec2<bf16>::type qv = __builtin_bit_cast(Vec2<bf16>::type, in.q[j]);
+        store2(&s.Qb[(8 * o + j) * LDK + 2 * c2], Vec2<bf16>::lo(qv) * fg[j], Vec2<bf16>::hi(qv) * fg[j]);
+    }
+}
+
+// Phase B of a scalar-decay chunk (decay-first form): wavefront 0 forms
+// A = strict_lower(diag(b) (K K^T) o [2^{G_t - G_i}]), wavefront 3
+// P2 = lower((Q K^T) o [2^{G_t - G_i}]) (in P1's slot), each from the raw rows with
+// the decay applied to the fp32 result: for i <= t the exponent is <= 0.
+__device__ __forceinline__ void prep2_scalar_gram(Prep2Lds& s, int wv, int lane) {
+    using namespace p2;
+    typedef Mma<bf16> M;
+    constexpr int NK = DK / M::K;
+    const int lr = lane & 15, lg = lane >> 4;
+    const bf16* rows = wv == 0 ? s.u.g.Kr : s.u.g.Qr;
+    const bf16* cols = s.u.g.Kr;
+    M::frag r0[NK], r1[NK], c0[NK], c1[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+        r0[kk] = M::loadr(rows + lr * LDK + kk * M::K, lane);
+        r1[kk] = M::loadr(rows + (16 + lr) * LDK + kk * M::K, lane);
+        c0[kk] = M::loadr(cols + lr * LDK + kk * M::K, lane);
+        c1[kk] = M::loadr(cols + (16 + lr) * LDK + kk * M::K, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int pr = 0; pr < 3; ++pr) {
+        const int bt = pr == 0 ? 0 : 1, bi = pr == 2 ? 1 : 0;
+        const M::frag* fr = bt == 0 ? r0 : r1;
+        const M::frag* fc = bi == 0 ? c0 : c1;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) acc = M::mma(fc[kk], fr[kk], acc);
+        // column t = 16 bt + lr, rows i = 16 bi + 4 lg + r
+        const int t = 16 * bt + lr, i0 = 16 * bi + 4 * lg;
+        const float gt = s.gtok[t];
+        f32x4 m;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool keep = wv == 0 ? i0 + r < t : i0 + r <= t;
+            m[r] = keep ? acc[r] * __builtin_amdgcn_exp2f(fminf(gt - s.gtok[i0 + r], 0.f)) : 0.f;
+        }
+        if (wv == 0) *reinterpret_cast<f32x4*>(&s.A[t * LDA + i0]) = s.beta[t] * m;
+        else store4(&s.P1[t * LDC + i0], m);
+    }
+}
+
 // PRO: the call has an input prologue; k is scaled per token by
 // (|k|^2 + eps)^{-1/2} (each token's row is one wavefront: 64 lanes x 2 channels),
 // beta and log a are transformed where they are loaded.
@@ -499,6 +613,37 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
                 kscale[j] = rsqrtf(readlanef(ss[j], 0) + readlanef(ss[j], 16) + readlanef(ss[j], 32) +
                                    readlanef(ss[j], 48) + PROLOGUE_EPS);
         }
+        if constexpr (SCALAR) {
+            // scalar decay (Gated DeltaNet): one log2 decay per token, the same in every
+            // lane; the Gram products take the raw rows and the decay as a scalar mask
+            static_assert(ORD1, "a scalar decay runs the decay-first form");
+            float l2[8];
+            bool steep = false;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float x = in.la[j][0] * LOG2E;
+                if (PRO && p.pro.log_a_raw) x = prologue_log2_a(in.la[j][0], p.pro.log_a_min * LOG2E);
+                if (8 * o + j >= Lc) x = 0.f;
+                steep |= x < STEEP_LOG2;
+                l2[j] = x;
+            }
+            float mine = l2[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) mine = lane == j ? l2[j] : mine;
+            if (lane < 8) s.ltok[8 * o + lane] = mine;
+            if (lane == 0) s.steep[wv] = steep;
+            if (tid < C) s.beta[tid] = (PRO && p.pro.beta_logits && tid < Lc) ? prologue_beta(raw.b) : raw.b;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = 8 * o + j;
+                const Vec2<bf16>::type kv = __builtin_bit_cast(Vec2<bf16>::type, in.k[j]);
+                const f32x2 k = f32x2{Vec2<bf16>::lo(kv), Vec2<bf16>::hi(kv)} * kscale[j];
+                store2(&s.u.g.Kr[t * LDK + 2 * c2], k[0], k[1]);
+                *reinterpret_cast<uint32_t*>(&s.u.g.Qr[t * LDK + 2 * c2]) = in.q[j];
+            }
+            lds_barrier();
+            prep2_scalar_operands<ORD1>(s, blk, in, kscale, lane, c2, o);
+        } else {
         f32x2 a[8], ai[8], E[8], Ei[8];
         bool steep = false;
 #pragma unroll
@@ -612,6 +757,7 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
                 store2(&s.Qb[(8 * o + j) * LDK + 2 * c2], qb[0], qb[1]);
             }
         }
+        }  // per-channel decay
         lds_barrier();
 
         // next chunk's inputs: in flight during phases B-D
@@ -630,7 +776,9 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
         //      the block pairs (0,0), (1,0) and (1,1) from 16 fragments read at once; rows
         //      of block 1 are scaled by F for the off-diagonal pair -------------------------
         //      ORD1: only A (wavefront 0, columns Kt) and P2 (wavefront 3, unscaled, into P1)
-        if (!ORD1 || wv == 0 || wv == 3) {
+        if (SCALAR) {
+            if (wv == 0 || wv == 3) prep2_scalar_gram(s, wv, lane);
+        } else if (!ORD1 || wv == 0 || wv == 3) {
             const int g = wv;
             constexpr int NK = DK / M::K;
             const bf16* rows = g < 2 ? s.u.g.Kr : s.u.g.Qr;
@@ -759,19 +907,19 @@ hipError_t launch_prep2(const PrepLaunch& a, hipStream_t stream) {
     int64_t blocks = (int64_t)cus * 2;
     if (blocks > p.items) blocks = p.items;
     if (blocks < 1) blocks = 1;
-    // order 1 comes with per-channel decay only (the host maps scalar decay to order 0)
     const dim3 grid((unsigned)blocks), block(p2::NT);
 #define KDA_PREP2_LAUNCH(SC, O1, PR)                                                                  \
     do {                                                                                              \
         hipLaunchKernelGGL((kda_prep2_kernel<SC, O1, PR>), grid, block, 0, stream, p);                \
         hipLaunchKernelGGL((kda_prep2_exact_kernel<SC, O1, PR>), grid, block, 0, stream, p);          \
     } while (0)
+    // a scalar decay comes with the decay-first order (the host's choice for the two-pass method)
     if (a.pro.any()) {
-        if (a.scalar) KDA_PREP2_LAUNCH(true, false, true);
+        if (a.scalar) KDA_PREP2_LAUNCH(true, true, true);
         else if (a.order) KDA_PREP2_LAUNCH(false, true, true);
         else KDA_PREP2_LAUNCH(false, false, true);
     } else {
-        if (a.scalar) KDA_PREP2_LAUNCH(true, false, false);
+        if (a.scalar) KDA_PREP2_LAUNCH(true, true, false);
         else if (a.order) KDA_PREP2_LAUNCH(false, true, false);
         else KDA_PREP2_LAUNCH(false, false, false);
     }
