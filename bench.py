@@ -543,7 +543,25 @@ def main():
                 rerun_step()
             torch.cuda.synchronize()
             tr = time_events(rerun_step, args.steps, stream) / args.steps
-            del snaps64, wsB
+            # the same gradient from the forward's kept states (kda_chunk_bwd_saved):
+            # a training step whose forward kept them runs no rerun
+            rerun_grads = {n_: t_.clone() for n_, t_ in bwd_step().items() if t_ is not None}
+            del wsB
+            wssb = kda.chunk_bwd_workspace_size(x["q"], x["v"], num_seqs=wp.n_seqs, method=method,
+                                                max_seqlen=wp.seqlen, saved=True)
+            wsS = torch.empty(wssb, dtype=torch.uint8, device=dev)
+
+            def saved_step():
+                return kda.chunk_bwd(x["q"], x["k"], x["v"], x["log_a"], x["beta"], dO, S0=x["S0"],
+                                     cu_seqlens=x["cu_seqlens"], dS_T=dST, workspace=wsS, max_seqlen=wp.seqlen,
+                                     states=snaps64)
+            same = all(torch.equal(t_, rerun_grads[n_]) for n_, t_ in saved_step().items() if t_ is not None)
+            del rerun_grads
+            for _ in range(max(args.warmup, 3)):
+                saved_step()
+            torch.cuda.synchronize()
+            tsv = time_events(saved_step, args.steps, stream) / args.steps
+            del snaps64, wsS
             Bb, Fb = backward_algorithmic(wp)
             out["backward"] = {
                 "ms_per_step": tb * 1e3, "tokens_per_s": tokens / tb,
@@ -554,9 +572,21 @@ def main():
                 "workspace_MiB": round(wsbb / 2**20, 1),
                 "kernels": "prefill rerun (kda_prep2_kernel + kda_scan_kernel, states every 64 tokens) + "
                            "kda_bwd_ops_kernel + kda_bwd_scan_kernel + kda_bwd_grad_kernel",
+                "saved_states": {
+                    "ms_per_step": tsv * 1e3, "tokens_per_s": tokens / tsv,
+                    "algorithmic_GBps": Bb / tsv / 1e9, "frac_hbm": Bb / tsv / 1e9 / PEAK_HBM_GBS,
+                    "pct_bf16_peak": 100.0 * Fb / tsv / 1e12 / PEAK_BF16_TFLOPS,
+                    "workspace_MiB": round(wssb / 2**20, 1),
+                    "bit_identical_to_rerun": same,
+                    "forward_keeping_states_ms": tr * 1e3,
+                    "training_step_ms": (tr + tsv) * 1e3,
+                    "training_step_with_rerun_ms": (per + tb) * 1e3,
+                    "note": "kda_chunk_bwd_saved with the states a forward call kept every 64 tokens; a training "
+                            "step is that forward plus this call, against the plain forward plus kda_chunk_bwd",
+                },
             }
             log(f"backward: {tb*1e3:.3f} ms/step ({tokens/tb/1e6:.2f} Mtok/s), prefill rerun {tr*1e3:.3f} ms, "
-                f"gradient kernels {(tb-tr)*1e3:.3f} ms")
+                f"gradient kernels {(tb-tr)*1e3:.3f} ms; from saved states {tsv*1e3:.3f} ms (identical: {same})")
 
         if not args.no_cpu_baseline:
             dt = dt_oracle

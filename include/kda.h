@@ -278,6 +278,37 @@ KDA_API int kda_chunk_bwd(const kda_dims_t* dims, const void* q, const void* k, 
 KDA_API int kda_chunk_bwd_workspace_size(const kda_dims_t* dims, size_t* bytes);
 
 /*
+ * kda_chunk_bwd for a training step whose forward call kept its states: the
+ * state at every 64th token of each sequence, as kda_chunk_fwd_snapshots
+ * writes it with snapshot_every = 64 (same dims and inputs; any method, chunk
+ * or dv split, which change the states only by rounding).  The backward then
+ * runs no prefill of its own: it is the three gradient kernels alone, with a
+ * smaller workspace (kda_chunk_bwd_saved_workspace_size).
+ *   states      [R, H, dk, dv] float32, 16-byte aligned, read only: row P_n + s
+ *               is the state of sequence n after its first 64 (s + 1) tokens,
+ *               P_n = sum over m < n of floor(len_m / 64).  May be NULL only
+ *               when total_tokens < 64 (no row is needed).
+ *   state_rows  R.  Without cu_seqlens the call checks R >= N floor(T / (64 N))
+ *               and returns KDA_ERR_INVALID_ARGUMENT otherwise; with cu_seqlens
+ *               the lengths are on the device, so the caller passes at least
+ *               P_N rows: a row at or past R is read as a zero state (wrong
+ *               gradients for that chunk, but no access outside the buffer).
+ * Every other argument, the supported shapes and the error behaviour are those
+ * of kda_chunk_bwd, whose gradients this returns (bit for bit when the forward
+ * ran with the same method, chunk and dv split as kda_chunk_bwd's rerun).
+ */
+KDA_API int kda_chunk_bwd_saved(const kda_dims_t* dims, const void* q, const void* k, const void* v,
+                                const float* log_a, const float* beta, const float* S0,
+                                const int32_t* cu_seqlens, const float* states, int64_t state_rows,
+                                const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                                float* dlog_a, float* dbeta, float* dS0, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Workspace kda_chunk_bwd_saved needs for these dims (about 4.6 KB per token and
+ * head at dk = dv = 128: the gradient kernels' share of kda_chunk_bwd's). */
+KDA_API int kda_chunk_bwd_saved_workspace_size(const kda_dims_t* dims, size_t* bytes);
+
+/*
  * One decode step: one token per sequence (T == N).
  *   q, k      [N, H, dk]   qkv_dtype
  *   v         [N, H, dv]   qkv_dtype

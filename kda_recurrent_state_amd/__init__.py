@@ -106,7 +106,11 @@ def load_library(build_if_missing: bool = True):
             lib.kda_chunk_bwd.restype = ctypes.c_int
             lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                           ctypes.c_size_t, P]
-            for name in ("kda_chunk_workspace_size", "kda_chunk_workspace_min", "kda_chunk_bwd_workspace_size"):
+            lib.kda_chunk_bwd_saved.restype = ctypes.c_int
+            lib.kda_chunk_bwd_saved.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, ctypes.c_int64, P,
+                                                P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+            for name in ("kda_chunk_workspace_size", "kda_chunk_workspace_min", "kda_chunk_bwd_workspace_size",
+                         "kda_chunk_bwd_saved_workspace_size"):
                 fn = getattr(lib, name)
                 fn.restype = ctypes.c_int
                 fn.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(ctypes.c_size_t)]
@@ -352,15 +356,19 @@ def chunk_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, 
 
 def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, chunk_size: int = 0,
               dv_split: int = 0, num_seqs: int | None = None, method: int = METHOD_AUTO, workspace=None,
-              max_seqlen: int | None = None, initial_state_grad=True):
+              max_seqlen: int | None = None, initial_state_grad=True, states=None):
     """Gradient of chunk_fwd (erase-first order) for upstream derivatives dO
     [T,H,dv] (and dS_T [N,H,dk,dv], None for zero).  Returns a dict with "dq",
     "dk" [T,H,dk] and "dv" [T,H,dv] in q's dtype, "dlog_a" (log_a's shape) and
     "dbeta" [T,H] in float32, and "dS0" [N,H,dk,dv] float32 (None when
-    initial_state_grad is False).  The forward inputs are passed again; the call
-    reruns the prefill to recover its states.  workspace: a uint8 tensor of at
-    least chunk_bwd_workspace_size bytes, or None to have one allocated for this
-    call.  chunk_size, dv_split and method choose the prefill rerun."""
+    initial_state_grad is False).  The forward inputs are passed again.
+
+    states: the forward's states at every 64th token, [R,H,dk,dv] float32 as
+    chunk_fwd_snapshots(..., snapshot_every=64) returns them; the call then
+    runs no prefill of its own (kda_chunk_bwd_saved).  None: the call reruns
+    the prefill to recover them, and chunk_size, dv_split and method choose that
+    rerun.  workspace: a uint8 tensor of at least chunk_bwd_workspace_size
+    (saved=states is not None) bytes, or None to have one allocated."""
     lib = load_library()
     _need(q, "q", ndim=3)
     T, H, dk = q.shape
@@ -394,8 +402,16 @@ def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, 
                 raise ValueError(f"{name} must be [{N},{H},{dk},{dv}] (got {tuple(x.shape)})")
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, 1)
+    saved = states is not None
+    if saved:
+        _need(states, "states", torch.float32, 4)
+        if states.shape[1:] != (H, dk, dv):
+            raise ValueError(f"states must be [R,{H},{dk},{dv}] (got {tuple(states.shape)})")
+        rows = snapshot_rows(cu_seqlens, 64, total_tokens=T, num_seqs=N)
+        if states.shape[0] < rows:
+            raise ValueError(f"states holds {states.shape[0]} rows, the sequences need {rows}")
     _same_device(q, k=k, v=v, log_a=log_a, beta=beta, dO=dO, S0=S0, dS_T=dS_T, cu_seqlens=cu_seqlens,
-                 workspace=workspace)
+                 workspace=workspace, states=states)
     if max_seqlen is None:
         if cu_seqlens is not None and N > 0:
             max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
@@ -405,28 +421,36 @@ def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, 
               ORDER_ERASE_FIRST, int(max_seqlen))
     if workspace is None:
         need = ctypes.c_size_t(0)
-        _check(lib, lib.kda_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(need)))
+        size_fn = lib.kda_chunk_bwd_saved_workspace_size if saved else lib.kda_chunk_bwd_workspace_size
+        _check(lib, size_fn(ctypes.byref(d), ctypes.byref(need)))
         workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=q.device)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
            "dlog_a": torch.empty_like(log_a), "dbeta": torch.empty_like(beta),
            "dS0": torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device) if initial_state_grad else None}
-    st = lib.kda_chunk_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta), _ptr(S0),
-                           _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]),
-                           _ptr(out["dv"]), _ptr(out["dlog_a"]), _ptr(out["dbeta"]), _ptr(out["dS0"]),
-                           _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream_handle(q.device))
+    grads = (_ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_a"]), _ptr(out["dbeta"]),
+             _ptr(out["dS0"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream_handle(q.device))
+    if saved:
+        st = lib.kda_chunk_bwd_saved(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
+                                     _ptr(S0), _ptr(cu_seqlens), _ptr(states), ctypes.c_int64(states.shape[0]),
+                                     _ptr(dO), _ptr(dS_T), *grads)
+    else:
+        st = lib.kda_chunk_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta), _ptr(S0),
+                               _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), *grads)
     _check(lib, st)
     return out
 
 
 def chunk_bwd_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, dv_split=0,
-                             method=METHOD_AUTO, max_seqlen=0):
-    """Bytes of workspace chunk_bwd needs for these shapes."""
+                             method=METHOD_AUTO, max_seqlen=0, saved=False):
+    """Bytes of workspace chunk_bwd needs for these shapes (saved=True: with the
+    forward's states passed in, so without the prefill rerun)."""
     lib = load_library()
     T, H, dk = q.shape
     d = _Dims(int(num_seqs), H, T, dk, v.shape[2], _dtype_code(q), int(bool(scalar_decay)), int(chunk_size),
               int(dv_split), int(method), ORDER_ERASE_FIRST, int(max_seqlen))
     need = ctypes.c_size_t(0)
-    _check(lib, lib.kda_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(need)))
+    fn = lib.kda_chunk_bwd_saved_workspace_size if saved else lib.kda_chunk_bwd_workspace_size
+    _check(lib, fn(ctypes.byref(d), ctypes.byref(need)))
     return need.value
 
 

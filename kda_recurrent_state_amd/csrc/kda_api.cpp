@@ -444,7 +444,9 @@ struct BwdPlan {
 };
 
 
-int plan_bwd(const kda_dims_t* d, bool have_cu, BwdPlan* bp) {
+// saved: the caller hands in the forward's states at every 64th token, so the
+// workspace holds no rerun (no prefill workspace, outputs or states of its own).
+int plan_bwd(const kda_dims_t* d, bool have_cu, bool saved, BwdPlan* bp) {
     int st = plan_prefill(d, have_cu, &bp->fwd);
     if (st) return st;
     if (d->order == KDA_ORDER_DECAY_FIRST && !d->scalar_decay)
@@ -453,10 +455,12 @@ int plan_bwd(const kda_dims_t* d, bool have_cu, BwdPlan* bp) {
         return fail(KDA_ERR_UNSUPPORTED, "no backward for dtype %d, dk %d, dv %d", d->qkv_dtype, d->dk, d->dv);
     const int64_t T = d->total_tokens, N = d->num_seqs, H = d->num_heads;
     const size_t state = (size_t)d->dk * d->dv * 4;
-    bp->fwd_ws = bp->fwd.two_pass_ok ? bp->fwd.pref_bytes : 0;
-    bp->o_bytes = round256((size_t)T * H * d->dv * (d->qkv_dtype == KDA_BF16 ? 2 : 4));
     bp->snap_rows = T / 64;
-    bp->snap_bytes = round256((size_t)bp->snap_rows * H * state);
+    if (!saved) {
+        bp->fwd_ws = bp->fwd.two_pass_ok ? bp->fwd.pref_bytes : 0;
+        bp->o_bytes = round256((size_t)T * H * d->dv * (d->qkv_dtype == KDA_BF16 ? 2 : 4));
+        bp->snap_bytes = round256((size_t)bp->snap_rows * H * state);
+    }
     bp->ops_bytes = round256((size_t)(T / 16 + N) * H * kda::bwd_block_bytes(d->qkv_dtype, d->dk));
     bp->x_bytes = round256((size_t)(T / 64 + N) * H * state);
     bp->scr_bytes = round256((size_t)(T / 64 + N) * H * (size_t)kda::bwd_scratch_bytes(d->qkv_dtype, d->dk, d->dv));
@@ -503,18 +507,33 @@ int kda_decode_step_ex(const kda_dims_t* d, const kda_prologue_t* prologue, cons
 int kda_chunk_bwd_workspace_size(const kda_dims_t* d, size_t* bytes) {
     if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
     BwdPlan bp;
-    int st = plan_bwd(d, true, &bp);
+    int st = plan_bwd(d, true, false, &bp);
     if (st) return st;
     *bytes = bp.total;
     return ok();
 }
 
-int kda_chunk_bwd(const kda_dims_t* d, const void* q, const void* k, const void* v, const float* log_a,
-                  const float* beta, const float* S0, const int32_t* cu_seqlens, const void* dO, const float* dS_T,
-                  void* dq, void* dk, void* dv, float* dlog_a, float* dbeta, float* dS0, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+int kda_chunk_bwd_saved_workspace_size(const kda_dims_t* d, size_t* bytes) {
+    if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
     BwdPlan bp;
-    int st = plan_bwd(d, cu_seqlens != nullptr, &bp);
+    int st = plan_bwd(d, true, true, &bp);
+    if (st) return st;
+    *bytes = bp.total;
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// The backward's four stages.  states == nullptr (saved false): the prefill is run
+// again for the states at every 64th token; otherwise they are the caller's rows.
+int chunk_bwd_impl(const kda_dims_t* d, const void* q, const void* k, const void* v, const float* log_a,
+                   const float* beta, const float* S0, const int32_t* cu_seqlens, bool saved, const float* states,
+                   int64_t state_rows, const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                   float* dlog_a, float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+    BwdPlan bp;
+    int st = plan_bwd(d, cu_seqlens != nullptr, saved, &bp);
     if (st) return st;
     if (d->num_seqs == 0) {
         if (d->total_tokens != 0)
@@ -541,6 +560,17 @@ int kda_chunk_bwd(const kda_dims_t* d, const void* q, const void* k, const void*
         return fail(KDA_ERR_INVALID_ARGUMENT, "the backward needs a workspace of at least %zu bytes (got %zu)",
                     bp.total, workspace ? workspace_bytes : (size_t)0);
     if ((uintptr_t)workspace & 255u) return fail(KDA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+    if (saved) {
+        // rows the kernels may read: one per whole 64 tokens of each sequence
+        // (known on the host only for equal lengths)
+        const int64_t need = cu_seqlens ? 0 : (int64_t)d->num_seqs * ((d->total_tokens / d->num_seqs) / 64);
+        if (state_rows < need)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "states holds %lld rows, the sequences need %lld",
+                        (long long)state_rows, (long long)need);
+        if (!states && d->total_tokens >= 64)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "states is NULL (the states at every 64th token are needed)");
+        if (states && !aligned16(states)) return fail(KDA_ERR_MISALIGNED, "states is not 16-byte aligned");
+    }
     const int64_t units = (int64_t)d->num_seqs * d->num_heads;
     const int64_t nsub_max = (bp.maxlen + 15) / 16, nch_max = (bp.maxlen + 63) / 64;
     if (units > 65535 || nsub_max > 0x7fffffff)
@@ -559,9 +589,13 @@ int kda_chunk_bwd(const kda_dims_t* d, const void* q, const void* k, const void*
     off += bp.x_bytes;
     void* scr = ws + off;
 
-    // the prefill again, keeping the state at every 64th token (nothing to keep
-    // when no sequence reaches 64 tokens)
-    if (bp.snap_rows > 0) {
+    int64_t snap_rows = bp.snap_rows;
+    if (saved) {
+        snap = const_cast<float*>(states);
+        snap_rows = states ? state_rows : 0;
+    } else if (bp.snap_rows > 0) {
+        // the prefill again, keeping the state at every 64th token (nothing to
+        // keep when no sequence reaches 64 tokens)
         kda_dims_t d2 = *d;
         d2.order = KDA_ORDER_ERASE_FIRST;
         st = kda_chunk_fwd_snapshots(&d2, q, k, v, log_a, beta, S0, cu_seqlens, o_scratch, nullptr, snap,
@@ -573,12 +607,33 @@ int kda_chunk_bwd(const kda_dims_t* d, const void* q, const void* k, const void*
     a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.beta = beta; a.S0 = S0;
     a.cu_seqlens = cu_seqlens; a.eq_len = cu_seqlens ? 0 : d->total_tokens / d->num_seqs;
     a.dO = dO; a.dST = dS_T; a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_a = dlog_a; a.dbeta = dbeta; a.dS0 = dS0;
-    a.snap = snap; a.ops = ops; a.xbuf = xbuf; a.scr = scr;
+    a.snap = snap; a.snap_rows = snap_rows; a.ops = ops; a.xbuf = xbuf; a.scr = scr;
     a.num_heads = d->num_heads; a.units = units; a.nsub_max = (int32_t)nsub_max; a.nch_max = (int32_t)nch_max;
     a.kdim = d->dk; a.vdim = d->dv; a.dtype = d->qkv_dtype; a.scalar = d->scalar_decay;
     hipError_t e = kda::launch_bwd(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_bwd(const kda_dims_t* d, const void* q, const void* k, const void* v, const float* log_a,
+                  const float* beta, const float* S0, const int32_t* cu_seqlens, const void* dO, const float* dS_T,
+                  void* dq, void* dk, void* dv, float* dlog_a, float* dbeta, float* dS0, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    return chunk_bwd_impl(d, q, k, v, log_a, beta, S0, cu_seqlens, false, nullptr, 0, dO, dS_T, dq, dk, dv, dlog_a,
+                          dbeta, dS0, workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_bwd_saved(const kda_dims_t* d, const void* q, const void* k, const void* v, const float* log_a,
+                        const float* beta, const float* S0, const int32_t* cu_seqlens, const float* states,
+                        int64_t state_rows, const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                        float* dlog_a, float* dbeta, float* dS0, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    return chunk_bwd_impl(d, q, k, v, log_a, beta, S0, cu_seqlens, true, states, state_rows, dO, dS_T, dq, dk, dv,
+                          dlog_a, dbeta, dS0, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

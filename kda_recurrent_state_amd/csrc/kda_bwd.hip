@@ -188,6 +188,7 @@ struct BwdParams {
     float* dbeta;
     float* dS0;
     const float* snap;       // forward states, row per 64 tokens of each sequence
+    int64_t snap_rows;       // rows snap holds (reads stay below it)
     uint8_t* ops;            // operator blocks
     float* xbuf;             // state derivatives at 64-token chunk ends
     void* scr;               // per chunk: start state, E and Y of its sub-chunks
@@ -745,7 +746,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         int64_t before;
         if (!p.cu) before = (int64_t)n * (p.eq_len / CHB);
         else before = snapshots_before(p.cu, p.eq_len, n, CHB);
-        s_start = p.snap + ((before + jc - 1) * p.H + h) * (int64_t)DK * DV;
+        if (before + jc - 1 < p.snap_rows) s_start = p.snap + ((before + jc - 1) * p.H + h) * (int64_t)DK * DV;
     }
     const MT* Kg = static_cast<const MT*>(p.k);
     const MT* Qg = static_cast<const MT*>(p.q);
@@ -1398,7 +1399,7 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t st) {
     p.q = a.q; p.k = a.k; p.v = a.v; p.log_a = a.log_a; p.beta = a.beta; p.S0 = a.S0;
     p.cu = a.cu_seqlens; p.eq_len = a.eq_len; p.dO = a.dO; p.dST = a.dST;
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dla = a.dlog_a; p.dbeta = a.dbeta; p.dS0 = a.dS0;
-    p.snap = a.snap; p.ops = static_cast<uint8_t*>(a.ops); p.xbuf = a.xbuf; p.scr = a.scr;
+    p.snap = a.snap; p.snap_rows = a.snap_rows; p.ops = static_cast<uint8_t*>(a.ops); p.xbuf = a.xbuf; p.scr = a.scr;
     p.H = a.num_heads; p.scalar = a.scalar; p.split = 0;
     if (a.dtype == 1) {
         if (a.kdim == 128 && a.vdim == 128) return run_all<bf16, 128, 128>(a, p, st);

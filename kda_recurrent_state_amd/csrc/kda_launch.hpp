@@ -109,6 +109,7 @@ struct BwdLaunch {
     float* dbeta;
     float* dS0;                 // may be null (not written)
     const float* snap;          // forward states, one row per 64 tokens of each sequence
+    int64_t snap_rows;          // rows snap holds; a row at or past it reads as a zero state
     void* ops;                  // operator blocks, bwd_block_bytes each
     float* xbuf;                // derivatives at chunk ends, [chunks][dk][dv]
     void* scr;                  // bwd_scratch_bytes per chunk

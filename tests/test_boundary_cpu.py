@@ -301,6 +301,56 @@ def test_bwd_refuses_unsupported_shapes(lib):
     assert backward(lib, dims(dk=64, dv=128), ws_bytes=1 << 20) == UNSUPPORTED
 
 
+def bwd_saved(lib, d, states=GOOD, rows=2, ws_bytes=None, **ptrs):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    vals = {n: GOOD for n in ["q", "k", "v", "la", "beta", "cu", "dO", "dq", "dk", "dv", "dla", "dbeta", "ws"]}
+    vals.update(S0=None, dST=None, dS0=None)
+    vals.update(ptrs)
+    if ws_bytes is None:
+        need = ctypes.c_size_t(0)
+        assert lib.kda_chunk_bwd_saved_workspace_size(ctypes.byref(d), ctypes.byref(need)) == OK
+        ws_bytes = need.value
+    g = lambda *ns: [P(vals[n]) for n in ns]
+    return lib.kda_chunk_bwd_saved(ctypes.byref(d), *g("q", "k", "v", "la", "beta", "S0", "cu"), P(states),
+                                   ctypes.c_int64(rows), *g("dO", "dST", "dq", "dk", "dv", "dla", "dbeta", "dS0",
+                                                            "ws"), ctypes.c_size_t(ws_bytes), None)
+
+
+def test_bwd_saved_workspace_is_the_gradient_share():
+    """With the forward's states passed in, the workspace drops the rerun's
+    prefill workspace, outputs and kept states."""
+    lib = kda.load_library(build_if_missing=False)
+    d = dims(total_tokens=65536, num_seqs=2, num_heads=32, max_seqlen=32768)
+    full, saved = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(full)) == OK
+    assert lib.kda_chunk_bwd_saved_workspace_size(ctypes.byref(d), ctypes.byref(saved)) == OK
+    pref = ctypes.c_size_t(0)
+    assert lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(pref)) == OK
+    rerun = pref.value + 65536 * 32 * 128 * 2 + (65536 // 64) * 32 * 128 * 128 * 4
+    assert abs(full.value - saved.value - rerun) < 4096
+    d1 = dims(order=1)
+    assert lib.kda_chunk_bwd_saved_workspace_size(ctypes.byref(d1), ctypes.byref(saved)) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(states=None), INVALID),                   # 128 tokens: rows are needed
+    (dict(cu=None, rows=1), INVALID),               # equal lengths 2 x 64: two rows
+    (dict(states=GOOD + 8), MISALIGNED),
+    (dict(ws_bytes=1024), INVALID),
+    (dict(dq=None), INVALID),
+])
+def test_bwd_saved_validation(lib, case, expect):
+    assert bwd_saved(lib, dims(), **case) == expect
+
+
+def test_bwd_saved_states_optional_below_64_tokens(lib):
+    """Fewer than 64 tokens: no state row can be read, so states may be NULL;
+    the call gets past every argument check (it then needs the GPU, and fails
+    here only at the launch)."""
+    st = bwd_saved(lib, dims(total_tokens=40, num_seqs=2), states=None, rows=0)
+    assert st not in (INVALID, MISALIGNED, UNSUPPORTED)
+
+
 def _cpu_prefill_inputs(T=40, H=2, dk=32, dv=16, N=2):
     import torch
     q = torch.zeros(T, H, dk, dtype=torch.bfloat16)

@@ -121,6 +121,42 @@ def test_bwd_two_pass_and_single_pass_reruns_agree():
         assert e <= 2e-2, n
 
 
+@pytest.mark.parametrize("dtype,d,lengths,scalar", [(torch.bfloat16, 128, [130, 64, 37], False),
+                                                    (torch.bfloat16, 64, [300, 63, 128], True),
+                                                    (torch.float32, 32, [150, 64], False)])
+def test_bwd_saved_states(dtype, d, lengths, scalar):
+    """The forward's states at every 64th token, passed in, give the gradients of
+    the call that reruns the prefill, bit for bit, and the oracle's."""
+    log(f"backward from saved states {dtype} d={d} lengths={lengths} scalar={scalar}")
+    inp = draw("kda_b2_h32_t32768_d128_bf16", 21 + d, lengths, dtype=dtype, dk=d, dv=d, scalar_decay=scalar)
+    _, _, states = kda.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], S0=inp["S0"],
+                                           cu_seqlens=inp["cu_seqlens"], snapshot_every=64)
+    assert states.shape[0] == sum(n // 64 for n in lengths)
+    saved = gpu_grad(inp, states=states)
+    rerun = gpu_grad(inp)
+    for n in NAMES:
+        assert torch.equal(saved[n], rerun[n]), n
+    check(inp, saved, TOL[dtype], "saved states")
+
+
+def test_bwd_saved_states_equal_lengths():
+    """Without cu_seqlens (two sequences of 192 tokens): the rows are checked on
+    the host, and the smaller workspace suffices."""
+    log("backward from saved states, equal lengths")
+    inp = draw("kda_b2_h32_t32768_d128_bf16", 33, [192, 192])
+    args = (inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"])
+    _, _, states = kda.chunk_fwd_snapshots(*args, S0=inp["S0"], num_seqs=2, snapshot_every=64)
+    assert states.shape[0] == 6
+    need = kda.chunk_bwd_workspace_size(inp["q"], inp["v"], num_seqs=2, max_seqlen=192, saved=True)
+    assert need < kda.chunk_bwd_workspace_size(inp["q"], inp["v"], num_seqs=2, max_seqlen=192)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    got = kda.chunk_bwd(*args, inp["dO"], S0=inp["S0"], dS_T=inp["dST"], num_seqs=2, states=states, workspace=ws)
+    torch.cuda.synchronize()
+    check(inp, got, TOL[torch.bfloat16], "saved states, equal lengths")
+    with pytest.raises(ValueError):
+        kda.chunk_bwd(*args, inp["dO"], S0=inp["S0"], num_seqs=2, states=states[:5])
+
+
 @pytest.mark.parametrize("d", [32, 128])
 def test_bwd_deterministic(d):
     # bit-identical results whatever the workspace held before the call
