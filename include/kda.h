@@ -263,8 +263,9 @@ KDA_API int kda_chunk_workspace_min(const kda_dims_t* dims, size_t* bytes);
  * pieces: operators per piece, the derivative with respect to the state
  * backwards through each sequence, and the gradients of each 64-token chunk.
  * Supported: the erase-first order (KDA_ORDER_DECAY_FIRST with a per-channel
- * decay returns KDA_ERR_UNSUPPORTED), dk == dv, bf16 with dk in {32, 64, 128},
- * fp32 with dk in {16, 32, 64}.  No input prologue.  Outputs must not alias
+ * decay returns KDA_ERR_UNSUPPORTED); bf16 with dk, dv in {32, 64, 128}, fp32
+ * with dk, dv in {16, 32, 64}, in both cases dk and dv equal or a factor 2
+ * apart.  No input prologue.  Outputs must not alias
  * inputs or each other.  Returns a kda_status_t.
  */
 KDA_API int kda_chunk_bwd(const kda_dims_t* dims, const void* q, const void* k, const void* v,

@@ -1388,9 +1388,12 @@ int64_t bwd_scratch_bytes(int dtype, int dk, int dv) {
     return (int64_t)(CHB / SC) * ((int64_t)dk * dv + 2 * 16 * dv) * s;
 }
 
+// Compiled (dk, dv): bf16 with dk, dv in {32, 64, 128} and dk, dv at most a
+// factor 2 apart; fp32 with dk, dv in {16, 32, 64}, likewise.
 bool bwd_supported(int dtype, int dk, int dv) {
-    if (dtype == 1) return (dk == 32 || dk == 64 || dk == 128) && (dv == 32 || dv == 64 || dv == 128) && dk == dv;
-    if (dtype == 0) return (dk == 16 || dk == 32 || dk == 64) && dk == dv;
+    const bool near = dk == dv || dk == 2 * dv || dv == 2 * dk;
+    if (dtype == 1) return (dk == 32 || dk == 64 || dk == 128) && (dv == 32 || dv == 64 || dv == 128) && near;
+    if (dtype == 0) return (dk == 16 || dk == 32 || dk == 64) && (dv == 16 || dv == 32 || dv == 64) && near;
     return false;
 }
 
@@ -1403,11 +1406,19 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t st) {
     p.H = a.num_heads; p.scalar = a.scalar; p.split = 0;
     if (a.dtype == 1) {
         if (a.kdim == 128 && a.vdim == 128) return run_all<bf16, 128, 128>(a, p, st);
+        if (a.kdim == 128 && a.vdim == 64) return run_all<bf16, 128, 64>(a, p, st);
+        if (a.kdim == 64 && a.vdim == 128) return run_all<bf16, 64, 128>(a, p, st);
         if (a.kdim == 64 && a.vdim == 64) return run_all<bf16, 64, 64>(a, p, st);
+        if (a.kdim == 64 && a.vdim == 32) return run_all<bf16, 64, 32>(a, p, st);
+        if (a.kdim == 32 && a.vdim == 64) return run_all<bf16, 32, 64>(a, p, st);
         if (a.kdim == 32 && a.vdim == 32) return run_all<bf16, 32, 32>(a, p, st);
     } else {
         if (a.kdim == 64 && a.vdim == 64) return run_all<float, 64, 64>(a, p, st);
+        if (a.kdim == 64 && a.vdim == 32) return run_all<float, 64, 32>(a, p, st);
+        if (a.kdim == 32 && a.vdim == 64) return run_all<float, 32, 64>(a, p, st);
         if (a.kdim == 32 && a.vdim == 32) return run_all<float, 32, 32>(a, p, st);
+        if (a.kdim == 32 && a.vdim == 16) return run_all<float, 32, 16>(a, p, st);
+        if (a.kdim == 16 && a.vdim == 32) return run_all<float, 16, 32>(a, p, st);
         if (a.kdim == 16 && a.vdim == 16) return run_all<float, 16, 16>(a, p, st);
     }
     return hipErrorInvalidValue;

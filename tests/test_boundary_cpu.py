@@ -272,9 +272,13 @@ def test_bwd_workspace_size(lib):
     assert st == OK and b256 > 1.9 * b128 - (1 << 30)
     assert bwd_ws(lib, dims(order=1))[0] == UNSUPPORTED               # decay-first, per-channel
     assert bwd_ws(lib, dims(order=1, scalar_decay=1))[0] == OK       # one map with a scalar gate
-    assert bwd_ws(lib, dims(dk=128, dv=64))[0] == UNSUPPORTED
+    assert bwd_ws(lib, dims(dk=128, dv=64))[0] == OK                   # dk, dv a factor 2 apart
+    assert bwd_ws(lib, dims(dk=32, dv=64))[0] == OK
+    assert bwd_ws(lib, dims(dk=128, dv=32))[0] == UNSUPPORTED          # a factor 4
     assert bwd_ws(lib, dims(dk=16, dv=16))[0] == UNSUPPORTED          # bf16 needs dk >= 32
     assert bwd_ws(lib, dims(dk=16, dv=16, qkv_dtype=0))[0] == OK
+    assert bwd_ws(lib, dims(dk=16, dv=32, qkv_dtype=0))[0] == OK
+    assert bwd_ws(lib, dims(dk=16, dv=64, qkv_dtype=0))[0] == UNSUPPORTED
     assert bwd_ws(lib, dims(dk=128, dv=128, qkv_dtype=0))[0] == UNSUPPORTED
 
 
@@ -298,7 +302,7 @@ def test_bwd_validation(lib, case, expect):
 def test_bwd_refuses_unsupported_shapes(lib):
     assert backward(lib, dims(order=1), ws_bytes=1 << 20) == UNSUPPORTED
     assert "erase-first" in lib.kda_last_error().decode()
-    assert backward(lib, dims(dk=64, dv=128), ws_bytes=1 << 20) == UNSUPPORTED
+    assert backward(lib, dims(dk=32, dv=128), ws_bytes=1 << 20) == UNSUPPORTED
 
 
 def bwd_saved(lib, d, states=GOOD, rows=2, ws_bytes=None, **ptrs):

@@ -71,6 +71,16 @@ def test_bwd_fp32(d, lengths):
     check(inp, gpu_grad(inp), TOL[torch.float32], f"fp32 d{d} lengths {lengths}")
 
 
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.bfloat16, 128, 64), (torch.bfloat16, 64, 128),
+                                         (torch.bfloat16, 64, 32), (torch.bfloat16, 32, 64),
+                                         (torch.float32, 64, 32), (torch.float32, 32, 64),
+                                         (torch.float32, 32, 16), (torch.float32, 16, 32)])
+def test_bwd_dk_ne_dv(dtype, dk, dv):
+    log(f"backward dk={dk} dv={dv} {dtype}")
+    inp = draw("kda_b2_h32_t32768_d128_bf16", 60 + dk + dv, [150, 64, 21], dtype=dtype, dk=dk, dv=dv)
+    check(inp, gpu_grad(inp), TOL[dtype], f"dk {dk} dv {dv}")
+
+
 def test_bwd_scalar_gate_bf16():
     inp = draw("gdn_h16_t4096_d128_bf16", 4, [190, 70])
     check(inp, gpu_grad(inp), TOL[torch.bfloat16], "bf16 scalar gate")
