@@ -190,10 +190,10 @@ typedef struct {
 
 /*
  * kda_chunk_fwd_snapshots with an input prologue (NULL, or all fields 0: none).
- * The prologue runs in the two-pass method's operator pass (bf16, dk = 64 or
- * 128); a call that would run single-pass (fp32 inputs, other shapes,
- * KDA_METHOD_SINGLE, or no workspace) returns KDA_ERR_UNSUPPORTED when any
- * transform is requested.  Everything else is as kda_chunk_fwd_snapshots.
+ * The prologue runs where the kernels load their inputs: in the two-pass
+ * method's operator pass, or in the single-pass kernel (fp32 inputs, the other
+ * shapes, KDA_METHOD_SINGLE, no workspace).  Everything else is as
+ * kda_chunk_fwd_snapshots.
  */
 KDA_API int kda_chunk_fwd_ex(const kda_dims_t* dims, const kda_prologue_t* prologue, const void* q,
                      const void* k, const void* v, const float* log_a, const float* beta,

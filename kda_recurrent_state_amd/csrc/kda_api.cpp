@@ -307,9 +307,6 @@ static int chunk_fwd_impl(const kda_dims_t* d, const kda_prologue_t* prologue, c
                         need, workspace ? workspace_bytes : (size_t)0);
         two_pass = have_ws;
     }
-    if (pro.any() && !two_pass)
-        return fail(KDA_ERR_UNSUPPORTED, "an input prologue needs the two-pass prefill (bf16, dk 64 or 128, method "
-                                         "AUTO or TWO_PASS, a workspace)");
     if (two_pass) {
         if ((uintptr_t)workspace & 255u) return fail(KDA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
         const size_t per_chunk = (size_t)pl.units * pl.block;
@@ -368,6 +365,7 @@ static int chunk_fwd_impl(const kda_dims_t* d, const kda_prologue_t* prologue, c
     a.dk = d->dk; a.dv = d->dv; a.dtype = d->qkv_dtype; a.scalar_decay = d->scalar_decay;
     a.chunk = chunk; a.split = split; a.order = kernel_order(d);
     a.snap = snapshots; a.snap_rows = snapshot_rows; a.snap_every = (int32_t)snapshot_every;
+    a.pro = pro;
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return ok();

@@ -131,6 +131,12 @@ struct ChunkParams {
     int snap_every;  // tokens between snapshots (a multiple of C)
 };
 
+// Input prologue switches (read by the PRO instances only) and its clip of log2 a.
+struct ChunkPro {
+    int nk, bl, la;
+    float lo2;
+};
+
 // Raw inputs of one 4-token x 2-channel unit, held in registers one chunk ahead.
 template <typename T>
 struct UnitIn {
@@ -192,6 +198,36 @@ __device__ __forceinline__ void load_chunk(const ChunkParams& p, const T* gq, co
     }
 }
 
+// Input prologue: the sum of x over the lanes that hold one token's key row
+// (32 lanes for dk >= 64, whose rows a half-wavefront covers in one or two
+// pieces; dk / 2 consecutive lanes below), in a fixed order.  Every lane of a
+// wavefront runs it.
+template <int NCP>
+__device__ __forceinline__ float key_row_sum(float x) {
+    constexpr int GS = NCP >= 32 ? 32 : NCP;
+#pragma unroll
+    for (int m = 1; m < GS; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+// log2 a of a unit's two channels as loaded (x: log a, or with the prologue's
+// log_a_raw the pre-activation of log a = max(-softplus(x), lo))
+// (used by the PRO instances; the others scale by log2 e in place)
+__device__ __forceinline__ f32x2 unit_log2_a(const ChunkPro& pr, f32x2 x) {
+    if (pr.la) return f32x2{prologue_log2_a(x[0], pr.lo2), prologue_log2_a(x[1], pr.lo2)};
+    return x * LOG2E;
+}
+
+// Prologue scale of token t's key, 1 / sqrt(|k_t|^2 + eps), from the squared
+// norms P1 left in knrm (two row pieces at dk = 128), or 1 without normalisation
+template <int C, int DK>
+__device__ __forceinline__ float key_scale(const ChunkPro& pr, const float* knrm, int t) {
+    if (!pr.nk) return 1.f;
+    float x = knrm[t];
+    if (DK >= 128) x += knrm[C + t];
+    return rsqrtf(x + PROLOGUE_EPS);
+}
+
 // P2 of a chunk with a token below STEEP_LOG2: the chunk-referenced operands
 // Kbar, Qbar, Kcc^T, Ktc^T with one exponential each, from running sums of log2 a
 // referenced to the chunk start (prefixes: group sums before the unit's group,
@@ -200,8 +236,9 @@ __device__ __forceinline__ void load_chunk(const ChunkParams& p, const T* gq, co
 // and Kci for exact_gram.  e^{g_C} comes from the block loop after it, as in the
 // factored path.  The unit's decays are read again from memory (rare path; the
 // walk does not keep them in registers).
-template <typename T, int DK, int DVS, int C, bool SCALAR, bool ORD1>
-__device__ __forceinline__ void chunk_steep_operands(const ChunkParams& p, ChunkLds<T, DK, DVS, C>& s, int64_t t0,
+template <typename T, int DK, int DVS, int C, bool SCALAR, bool ORD1, bool PRO>
+__device__ __forceinline__ void chunk_steep_operands(const ChunkParams& p, const ChunkPro& pr,
+                                                     ChunkLds<T, DK, DVS, C>& s, int64_t t0,
                                                      int Lc, int h, int tid,
                                                      const typename Vec2<T>::type (&qraw)[ChunkCfg<T, DK, DVS, C>::UPT][4],
                                                      const typename Vec2<T>::type (&kraw)[ChunkCfg<T, DK, DVS, C>::UPT][4]) {
@@ -222,7 +259,7 @@ __device__ __forceinline__ void chunk_steep_operands(const ChunkParams& p, Chunk
                 const int64_t row = (t0 + min(4 * tg + i, Lc - 1)) * p.H + h;
                 const f32x2 x = SCALAR ? f32x2{p.log_a[row], p.log_a[row]}
                                        : *reinterpret_cast<const f32x2*>(p.log_a + row * DK + c);
-                l2[i] = 4 * tg + i < Lc ? x * LOG2E : f32x2{0.f, 0.f};
+                l2[i] = 4 * tg + i < Lc ? (PRO ? unit_log2_a(pr, x) : x * LOG2E) : f32x2{0.f, 0.f};
             }
             f32x2 pre = {0.f, 0.f}, suf = {0.f, 0.f};
 #pragma unroll
@@ -245,7 +282,8 @@ __device__ __forceinline__ void chunk_steep_operands(const ChunkParams& p, Chunk
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 4 * tg + i;
-                const f32x2 k = f32x2{Vec2<T>::lo(kraw[u][i]), Vec2<T>::hi(kraw[u][i])};
+                f32x2 k = f32x2{Vec2<T>::lo(kraw[u][i]), Vec2<T>::hi(kraw[u][i])};
+                if constexpr (PRO) k = k * key_scale<C, DK>(pr, s.X, t);
                 const f32x2 q = f32x2{Vec2<T>::lo(qraw[u][i]), Vec2<T>::hi(qraw[u][i])};
                 const f32x2 g = gp + l2[i];
                 const f32x2 kb = k * ex2v(ORD1 ? g : gp), qb = q * ex2v(g);
@@ -269,9 +307,14 @@ __device__ __forceinline__ void chunk_steep_operands(const ChunkParams& p, Chunk
 }
 
 // SNAP: the call asks for state snapshots (a separate instantiation: the
-// snapshot stores would otherwise cost the plain walk registers).
-template <typename T, int DK, int DVS, int C, bool SCALAR, bool ORD1, bool SNAP>
-__global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
+// snapshot stores would otherwise cost the plain walk registers).  PRO: the
+// call has an input prologue (also separate; its switches are read at run time):
+// beta and log a are transformed as P1 takes them from the prefetch registers,
+// and each token's key row is scaled by 1 / sqrt(|k|^2 + eps) where P2 forms the
+// gated operands, the squared norm summed over the lanes of the row and, at
+// dk = 128, over the two wavefronts that share it (through LDS).
+template <typename T, int DK, int DVS, int C, bool SCALAR, bool ORD1, bool SNAP, bool PRO>
+__global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p, ChunkPro pr) {
     typedef ChunkCfg<T, DK, DVS, C> G;
     typedef Mma<T> M;
     constexpr int NT = G::NT, NW = G::NW, NB = G::NB, LDK = G::LDK, LDC = G::LDC, LDA = G::LDA;
@@ -373,7 +416,7 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 f32x2 run = f32x2{0.f, 0.f};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const f32x2 l2 = (4 * tg + i < Lc) ? ui[u].la[i] * LOG2E : f32x2{0.f, 0.f};
+                    const f32x2 l2 = (4 * tg + i < Lc) ? (PRO ? unit_log2_a(pr, ui[u].la[i]) : ui[u].la[i] * LOG2E) : f32x2{0.f, 0.f};
                     steep |= l2[0] < STEEP_LOG2 || l2[1] < STEEP_LOG2;
                     run += l2;
                     lam[u][i] = run;
@@ -381,6 +424,31 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                     kraw[u][i] = ui[u].k[i];
                 }
                 *reinterpret_cast<f32x2*>(&s.grp[tg * DK + c]) = run;
+            }
+        }
+        if (PRO && pr.nk) {
+            // squared key norms: per token, the sum over its row's lanes, stored
+            // by the row piece's first lane (a piece per wavefront half at dk = 128)
+            float* knrm = s.X;  // the solve's exchange buffer is free until P4
+#pragma unroll
+            for (int u = 0; u < G::UPT; ++u) {
+                const int uu = tid + NT * u;
+                int c = 0, tg = 0;
+                if (uu < G::NU) unit_of<G::NCP>(uu, c, tg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = 0.f;
+                    if (uu < G::NU) {
+                        const float k0 = Vec2<T>::lo(kraw[u][i]), k1 = Vec2<T>::hi(kraw[u][i]);
+                        x = k0 * k0 + k1 * k1;
+                    }
+                    x = key_row_sum<G::NCP>(x);
+                    constexpr int GS = G::NCP >= 32 ? 32 : G::NCP;
+                    if (uu < G::NU && (uu % GS) == 0) {
+                        const int half = G::NCP >= 32 ? (uu >> 6) % (G::NCP / 32) : 0;
+                        knrm[half * C + 4 * tg + i] = x;
+                    }
+                }
             }
         }
 #pragma unroll
@@ -391,7 +459,7 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                 f32x4 vals[4], bb;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    bb[i] = 4 * tg + i < Lc ? vi[u].b[i] : 0.f;
+                    bb[i] = 4 * tg + i < Lc ? (PRO && pr.bl ? prologue_beta(vi[u].b[i]) : vi[u].b[i]) : 0.f;
                     // (b V)^T; ORD1: V^T, padded rows zero
                     vals[i] = (ORD1 ? (4 * tg + i < Lc ? 1.f : 0.f) : bb[i]) * Vec4<T>::to_f32(vi[u].v[i]);
                 }
@@ -425,7 +493,7 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
         for (int w = 0; w < NW; ++w) steep_any |= s.steep[w];
         const bool steep_chunk = __builtin_amdgcn_readfirstlane(steep_any) != 0;
         if (steep_chunk) {
-            chunk_steep_operands<T, DK, DVS, C, SCALAR, ORD1>(p, s, t0, Lc, h, tid, qraw, kraw);
+            chunk_steep_operands<T, DK, DVS, C, SCALAR, ORD1, PRO>(p, pr, s, t0, Lc, h, tid, qraw, kraw);
         } else {
 #pragma unroll
         for (int u = 0; u < G::UPT; ++u) {
@@ -462,7 +530,8 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p) {
                             __builtin_amdgcn_fmed3f(off[e] + lam[u][i][e] - mid[e], -126.f, 126.f));
                         ci[e] = __builtin_amdgcn_rcpf(ri[e]);
                     }
-                    const f32x2 k = f32x2{Vec2<T>::lo(kraw[u][i]), Vec2<T>::hi(kraw[u][i])};
+                    f32x2 k = f32x2{Vec2<T>::lo(kraw[u][i]), Vec2<T>::hi(kraw[u][i])};
+                    if constexpr (PRO) k = k * key_scale<C, DK>(pr, s.X, t);
                     const f32x2 q = f32x2{Vec2<T>::lo(qraw[u][i]), Vec2<T>::hi(qraw[u][i])};
                     const f32x2 kr = ORD1 ? k * ri : k * prev, qr = q * ri, kce = k * prevc, kci = k * ci;
                     store2(&s.Kr[t * LDK + c], kr[0], kr[1]);
@@ -683,14 +752,17 @@ static hipError_t launch_cfg(const ChunkArgs& a, hipStream_t stream) {
     p.H = a.num_heads; p.DV = a.dv; p.split = a.split;
     p.eq_len = a.cu_seqlens ? 0 : a.total_tokens / (a.num_seqs > 0 ? a.num_seqs : 1);
     p.snap = a.snap; p.snap_rows = a.snap_rows; p.snap_every = a.snap_every;
+    const ChunkPro pr{a.pro.normalize_k, a.pro.beta_logits, a.pro.log_a_raw, a.pro.log_a_min * LOG2E};
     const int64_t blocks = (int64_t)a.num_seqs * a.num_heads * a.split;
     p.xcd_group = (blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
-    if (a.snap)
-        hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC, ORD1, true>), dim3((unsigned)blocks), dim3(NT), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC, ORD1, false>), dim3((unsigned)blocks), dim3(NT), 0,
-                           stream, p);
+    const dim3 grid((unsigned)blocks), block(NT);
+    if (a.pro.any()) {
+        if (a.snap) hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC, ORD1, true, true>), grid, block, 0, stream, p, pr);
+        else hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC, ORD1, false, true>), grid, block, 0, stream, p, pr);
+    } else {
+        if (a.snap) hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC, ORD1, true, false>), grid, block, 0, stream, p, pr);
+        else hipLaunchKernelGGL((kda_chunk_kernel<T, DK, DVS, C, SC, ORD1, false, false>), grid, block, 0, stream, p, pr);
+    }
     return hipGetLastError();
 }
 

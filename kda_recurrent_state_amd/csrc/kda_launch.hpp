@@ -36,6 +36,7 @@ struct ChunkArgs {
     float* snap;                // state snapshots [rows, H, dk, dv], or null
     int64_t snap_rows;
     int32_t snap_every;         // tokens between snapshots (a multiple of chunk), 0 = none
+    Prologue pro;               // input prologue (none by default)
 };
 
 bool decode_supported(int dtype, int dk, int dv);

@@ -98,12 +98,52 @@ def test_prologue_snapshots_and_segments():
     assert torch.equal(snaps[1], ST[0]) and torch.equal(snaps[3], ST[1])  # L divides both lengths
 
 
-def test_prologue_needs_two_pass():
-    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=2, heads=2, dk=32, dv=32, dtype=torch.float32)
-    inp = generate_raw(w, seed=123, device=DEV, lengths=[40, 8])
-    with pytest.raises(kda.KdaError) as e:
-        prefill(inp)
-    assert e.value.status == 2
+SINGLE_CASES = [
+    # dtype, dk, dv, scalar, order, chunk
+    (torch.float32, 32, 32, False, 0, 32), (torch.float32, 16, 16, False, 1, 32), (torch.float32, 64, 32, False, 0, 32),
+    (torch.float32, 32, 16, True, 0, 32), (torch.float32, 16, 16, False, 0, 64),
+    (torch.bfloat16, 32, 32, False, 0, 32), (torch.bfloat16, 128, 64, False, 0, 32),
+    (torch.bfloat16, 64, 64, True, 1, 32), (torch.bfloat16, 128, 128, False, 1, 32),
+]
+
+
+@pytest.mark.parametrize("dtype,dk,dv,scalar,order,chunk", SINGLE_CASES)
+def test_prologue_single_pass(dtype, dk, dv, scalar, order, chunk):
+    """The single-pass kernel (fp32 inputs, bf16 shapes without a two-pass kernel,
+    or method SINGLE) with the whole prologue, against the oracle: the key norm
+    reduced over the lanes of a row (and the two wavefronts of a row at dk = 128)."""
+    log(f"prologue single-pass {dtype} dk={dk} dv={dv} scalar={scalar} order={order} chunk={chunk}")
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=3, heads=2, dk=dk, dv=dv, dtype=dtype,
+               scalar_decay=scalar)
+    inp = generate_raw(w, seed=123 + dk + dv + order, device=DEV, lengths=[150, 7, 96])
+    o, ST = prefill(inp, order=order, method=kda.METHOD_SINGLE, chunk_size=chunk)
+    ro, rS = oracle_pro(inp, order=order)
+    eo, es = max_rel_err(o, ro), max_rel_err(ST, rS)
+    log(f"  err o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,dk", [(torch.float32, 32), (torch.bfloat16, 128)])
+def test_prologue_single_pass_steep_and_snapshots(dtype, dk):
+    """Pre-activations up to a few hundred (log a down to about -300: the steep
+    path reloads and transforms them) with snapshots, single-pass."""
+    log(f"prologue single-pass steep + snapshots {dtype} dk={dk}")
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=2, heads=2, dk=dk, dv=dk, dtype=dtype)
+    inp = generate_raw(w, seed=129 + dk, device=DEV, lengths=[140, 64])
+    x = inp["log_a"].clone()
+    x[30:90] = x[30:90].abs() * 60.0 + 20.0
+    inp["log_a"] = x.contiguous()
+    pro = dict(PRO, log_a_min=None)
+    o, ST, snaps = kda.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], S0=inp["S0"],
+                                           cu_seqlens=inp["cu_seqlens"], snapshot_every=32, prologue=pro,
+                                           method=kda.METHOD_SINGLE)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(ST).all()
+    ro, rS = oracle_pro(inp, pro=pro)
+    eo, es = max_rel_err(o, ro), max_rel_err(ST, rS)
+    log(f"  err o {eo:.2e} S {es:.2e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    assert torch.equal(snaps[-1], ST[1])  # 64 tokens: its last snapshot is its final state
 
 
 def test_prologue_kda_b2_h32_t32768_sampled():
