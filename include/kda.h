@@ -265,7 +265,7 @@ KDA_API int kda_chunk_workspace_min(const kda_dims_t* dims, size_t* bytes);
  * Supported: the erase-first order (KDA_ORDER_DECAY_FIRST with a per-channel
  * decay returns KDA_ERR_UNSUPPORTED); bf16 with dk, dv in {32, 64, 128}, fp32
  * with dk, dv in {16, 32, 64}, in both cases dk and dv equal or a factor 2
- * apart.  No input prologue.  Outputs must not alias
+ * apart.  No input prologue (kda_chunk_bwd_ex takes one).  Outputs must not alias
  * inputs or each other.  Returns a kda_status_t.
  */
 KDA_API int kda_chunk_bwd(const kda_dims_t* dims, const void* q, const void* k, const void* v,
@@ -304,6 +304,38 @@ KDA_API int kda_chunk_bwd_saved(const kda_dims_t* dims, const void* q, const voi
                                 const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
                                 float* dlog_a, float* dbeta, float* dS0, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_bwd for a forward call that ran an input prologue (kda_chunk_fwd_ex),
+ * optionally from the forward's kept states.  k, log_a and beta are the raw
+ * inputs the forward took, and dk, dlog_a, dbeta are the derivatives with
+ * respect to them: through k = x / sqrt(|x|^2 + 1e-6), beta = 1 / (1 + e^-z)
+ * and log a = max(-softplus(y), log_a_min), whose derivative is taken as 0
+ * where the clip is active (-softplus(y) < log_a_min).  The transformed inputs
+ * are formed in the workspace, the gradient runs on them, and the chain rule
+ * through the transforms is applied to dk, dlog_a and dbeta in place.
+ *   prologue    as for kda_chunk_fwd_ex (NULL or all fields 0: none)
+ *   states      NULL: the prefill is run again, as kda_chunk_bwd does; else the
+ *               forward's states at every 64th token, as for kda_chunk_bwd_saved
+ *   workspace   at least kda_chunk_bwd_ex_workspace_size bytes (saved = states
+ *               is not NULL), 256-byte aligned
+ * The other arguments, the supported shapes and the error behaviour are those of
+ * kda_chunk_bwd (with states: kda_chunk_bwd_saved); every argument is checked
+ * before anything is enqueued.
+ */
+KDA_API int kda_chunk_bwd_ex(const kda_dims_t* dims, const kda_prologue_t* prologue, const void* q,
+                             const void* k, const void* v, const float* log_a, const float* beta,
+                             const float* S0, const int32_t* cu_seqlens, const float* states,
+                             int64_t state_rows, const void* dO, const float* dS_T, void* dq, void* dk,
+                             void* dv, float* dlog_a, float* dbeta, float* dS0, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Workspace kda_chunk_bwd_ex needs: kda_chunk_bwd's (saved = 0) or
+ * kda_chunk_bwd_saved's (saved != 0), plus, with a prologue, the transformed
+ * keys, log a and beta (T H dk elements of qkv_dtype, T H dk or T H floats, and
+ * T H floats, each rounded up to 256 bytes). */
+KDA_API int kda_chunk_bwd_ex_workspace_size(const kda_dims_t* dims, const kda_prologue_t* prologue,
+                                            int saved, size_t* bytes);
 
 /* Workspace kda_chunk_bwd_saved needs for these dims (about 4.6 KB per token and
  * head at dk = dv = 128: the gradient kernels' share of kda_chunk_bwd's). */

@@ -106,6 +106,12 @@ def load_library(build_if_missing: bool = True):
             lib.kda_chunk_bwd.restype = ctypes.c_int
             lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                           ctypes.c_size_t, P]
+            lib.kda_chunk_bwd_ex.restype = ctypes.c_int
+            lib.kda_chunk_bwd_ex.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Prologue), P, P, P, P, P, P, P,
+                                             P, ctypes.c_int64, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+            lib.kda_chunk_bwd_ex_workspace_size.restype = ctypes.c_int
+            lib.kda_chunk_bwd_ex_workspace_size.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Prologue),
+                                                            ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
             lib.kda_chunk_bwd_saved.restype = ctypes.c_int
             lib.kda_chunk_bwd_saved.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, ctypes.c_int64, P,
                                                 P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -356,7 +362,7 @@ def chunk_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, 
 
 def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, chunk_size: int = 0,
               dv_split: int = 0, num_seqs: int | None = None, method: int = METHOD_AUTO, workspace=None,
-              max_seqlen: int | None = None, initial_state_grad=True, states=None):
+              max_seqlen: int | None = None, initial_state_grad=True, states=None, prologue: dict | None = None):
     """Gradient of chunk_fwd (erase-first order) for upstream derivatives dO
     [T,H,dv] (and dS_T [N,H,dk,dv], None for zero).  Returns a dict with "dq",
     "dk" [T,H,dk] and "dv" [T,H,dv] in q's dtype, "dlog_a" (log_a's shape) and
@@ -367,8 +373,11 @@ def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, 
     chunk_fwd_snapshots(..., snapshot_every=64) returns them; the call then
     runs no prefill of its own (kda_chunk_bwd_saved).  None: the call reruns
     the prefill to recover them, and chunk_size, dv_split and method choose that
-    rerun.  workspace: a uint8 tensor of at least chunk_bwd_workspace_size
-    (saved=states is not None) bytes, or None to have one allocated."""
+    rerun.  prologue: the input prologue the forward ran (chunk_fwd's
+    prologue); k, log_a and beta are then the raw inputs and dk, dlog_a, dbeta
+    the derivatives with respect to them (kda_chunk_bwd_ex).  workspace: a
+    uint8 tensor of at least chunk_bwd_workspace_size(saved=states is not None,
+    prologue=prologue) bytes, or None to have one allocated."""
     lib = load_library()
     _need(q, "q", ndim=3)
     T, H, dk = q.shape
@@ -419,17 +428,26 @@ def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, 
             max_seqlen = 0
     d = _Dims(N, H, T, dk, dv, _dtype_code(q), scalar, int(chunk_size), int(dv_split), int(method),
               ORDER_ERASE_FIRST, int(max_seqlen))
+    pro = _prologue(prologue)
     if workspace is None:
         need = ctypes.c_size_t(0)
-        size_fn = lib.kda_chunk_bwd_saved_workspace_size if saved else lib.kda_chunk_bwd_workspace_size
-        _check(lib, size_fn(ctypes.byref(d), ctypes.byref(need)))
+        if pro is not None:
+            _check(lib, lib.kda_chunk_bwd_ex_workspace_size(ctypes.byref(d), ctypes.byref(pro), int(saved),
+                                                            ctypes.byref(need)))
+        else:
+            size_fn = lib.kda_chunk_bwd_saved_workspace_size if saved else lib.kda_chunk_bwd_workspace_size
+            _check(lib, size_fn(ctypes.byref(d), ctypes.byref(need)))
         workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=q.device)
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
            "dlog_a": torch.empty_like(log_a), "dbeta": torch.empty_like(beta),
            "dS0": torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device) if initial_state_grad else None}
     grads = (_ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_a"]), _ptr(out["dbeta"]),
              _ptr(out["dS0"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream_handle(q.device))
-    if saved:
+    if pro is not None:
+        st = lib.kda_chunk_bwd_ex(ctypes.byref(d), ctypes.byref(pro), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a),
+                                  _ptr(beta), _ptr(S0), _ptr(cu_seqlens), _ptr(states),
+                                  ctypes.c_int64(states.shape[0] if saved else 0), _ptr(dO), _ptr(dS_T), *grads)
+    elif saved:
         st = lib.kda_chunk_bwd_saved(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(log_a), _ptr(beta),
                                      _ptr(S0), _ptr(cu_seqlens), _ptr(states), ctypes.c_int64(states.shape[0]),
                                      _ptr(dO), _ptr(dS_T), *grads)
@@ -441,16 +459,22 @@ def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, 
 
 
 def chunk_bwd_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, dv_split=0,
-                             method=METHOD_AUTO, max_seqlen=0, saved=False):
+                             method=METHOD_AUTO, max_seqlen=0, saved=False, prologue: dict | None = None):
     """Bytes of workspace chunk_bwd needs for these shapes (saved=True: with the
-    forward's states passed in, so without the prefill rerun)."""
+    forward's states passed in, so without the prefill rerun; prologue: the
+    input prologue the forward ran)."""
     lib = load_library()
     T, H, dk = q.shape
     d = _Dims(int(num_seqs), H, T, dk, v.shape[2], _dtype_code(q), int(bool(scalar_decay)), int(chunk_size),
               int(dv_split), int(method), ORDER_ERASE_FIRST, int(max_seqlen))
     need = ctypes.c_size_t(0)
-    fn = lib.kda_chunk_bwd_saved_workspace_size if saved else lib.kda_chunk_bwd_workspace_size
-    _check(lib, fn(ctypes.byref(d), ctypes.byref(need)))
+    pro = _prologue(prologue)
+    if pro is not None:
+        _check(lib, lib.kda_chunk_bwd_ex_workspace_size(ctypes.byref(d), ctypes.byref(pro), int(bool(saved)),
+                                                        ctypes.byref(need)))
+    else:
+        fn = lib.kda_chunk_bwd_saved_workspace_size if saved else lib.kda_chunk_bwd_workspace_size
+        _check(lib, fn(ctypes.byref(d), ctypes.byref(need)))
     return need.value
 
 

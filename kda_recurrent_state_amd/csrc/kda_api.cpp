@@ -442,6 +442,13 @@ struct BwdPlan {
 };
 
 
+// Transformed inputs of a backward with a prologue: keys, log a, beta.
+size_t prologue_bytes(const kda_dims_t* d) {
+    const size_t rows = (size_t)(d->total_tokens > 0 ? d->total_tokens : 0) * (size_t)d->num_heads;
+    const size_t esize = d->qkv_dtype == KDA_BF16 ? 2 : 4;
+    return round256(rows * d->dk * esize) + round256(rows * (d->scalar_decay ? 1 : d->dk) * 4) + round256(rows * 4);
+}
+
 // saved: the caller hands in the forward's states at every 64th token, so the
 // workspace holds no rerun (no prefill workspace, outputs or states of its own).
 int plan_bwd(const kda_dims_t* d, bool have_cu, bool saved, BwdPlan* bp) {
@@ -511,6 +518,17 @@ int kda_chunk_bwd_workspace_size(const kda_dims_t* d, size_t* bytes) {
     return ok();
 }
 
+int kda_chunk_bwd_ex_workspace_size(const kda_dims_t* d, const kda_prologue_t* prologue, int saved, size_t* bytes) {
+    if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    kda::Prologue pro;
+    int st = check_prologue(prologue, &pro);
+    if (st) return st;
+    BwdPlan bp;
+    if ((st = plan_bwd(d, true, saved != 0, &bp))) return st;
+    *bytes = bp.total + (pro.any() ? prologue_bytes(d) : 0);
+    return ok();
+}
+
 int kda_chunk_bwd_saved_workspace_size(const kda_dims_t* d, size_t* bytes) {
     if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
     BwdPlan bp;
@@ -529,7 +547,8 @@ namespace {
 int chunk_bwd_impl(const kda_dims_t* d, const void* q, const void* k, const void* v, const float* log_a,
                    const float* beta, const float* S0, const int32_t* cu_seqlens, bool saved, const float* states,
                    int64_t state_rows, const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
-                   float* dlog_a, float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+                   float* dlog_a, float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream,
+                   bool check_only = false) {
     BwdPlan bp;
     int st = plan_bwd(d, cu_seqlens != nullptr, saved, &bp);
     if (st) return st;
@@ -574,6 +593,7 @@ int chunk_bwd_impl(const kda_dims_t* d, const void* q, const void* k, const void
     if (units > 65535 || nsub_max > 0x7fffffff)
         return fail(KDA_ERR_INVALID_ARGUMENT, "too many (sequence, head) units for the backward: %lld",
                     (long long)units);
+    if (check_only) return ok();
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     uint8_t* fwd_ws = bp.fwd_ws ? ws : nullptr;
     size_t off = round256(bp.fwd_ws);
@@ -613,9 +633,77 @@ int chunk_bwd_impl(const kda_dims_t* d, const void* q, const void* k, const void
     return ok();
 }
 
+// The backward with an input prologue: the transformed inputs are formed in
+// the workspace past the gradient's own share, the gradient runs on them, and
+// the chain rule through the transforms is applied to dk, dlog_a and dbeta.
+int chunk_bwd_ex_impl(const kda_dims_t* d, const kda_prologue_t* prologue, const void* q, const void* k,
+                      const void* v, const float* log_a, const float* beta, const float* S0,
+                      const int32_t* cu_seqlens, const float* states, int64_t state_rows, const void* dO,
+                      const float* dS_T, void* dq, void* dk, void* dv, float* dlog_a, float* dbeta, float* dS0,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    kda::Prologue pro;
+    int st = check_prologue(prologue, &pro);
+    if (st) return st;
+    const bool saved = states != nullptr;
+    if (!pro.any())
+        return chunk_bwd_impl(d, q, k, v, log_a, beta, S0, cu_seqlens, saved, states, state_rows, dO, dS_T, dq, dk,
+                              dv, dlog_a, dbeta, dS0, workspace, workspace_bytes, stream);
+    BwdPlan bp;
+    if ((st = plan_bwd(d, cu_seqlens != nullptr, saved, &bp))) return st;
+    const size_t extra = prologue_bytes(d);
+    if (!workspace || workspace_bytes < bp.total + extra)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "the backward with a prologue needs a workspace of at least %zu bytes "
+                    "(got %zu)", bp.total + extra, workspace ? workspace_bytes : (size_t)0);
+    if ((uintptr_t)workspace & 255u) return fail(KDA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+    const int64_t rows = d->total_tokens * d->num_heads;
+    const size_t esize = d->qkv_dtype == KDA_BF16 ? 2 : 4;
+    uint8_t* px = static_cast<uint8_t*>(workspace) + bp.total;
+    void* k_t = px;
+    float* la_t = reinterpret_cast<float*>(px + round256((size_t)rows * d->dk * esize));
+    float* b_t = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(la_t) +
+                                          round256((size_t)rows * (d->scalar_decay ? 1 : d->dk) * 4));
+    const void* k_in = pro.normalize_k ? k_t : k;
+    const float* la_in = pro.log_a_raw ? la_t : log_a;
+    const float* b_in = pro.beta_logits ? b_t : beta;
+    // every argument is checked before anything is enqueued: the raw inputs
+    // here, the rest by the gradient's own checks (on the transformed inputs)
+    if (rows > 0) {
+        const void* ptrs[] = {k, log_a, beta};
+        const char* names[] = {"k", "log_a", "beta"};
+        const int align[] = {16, d->scalar_decay ? 4 : 16, 4};
+        if ((st = check_ptrs(ptrs, names, align, 3))) return st;
+    }
+    st = chunk_bwd_impl(d, q, k_in, v, la_in, b_in, S0, cu_seqlens, saved, states, state_rows, dO, dS_T, dq, dk, dv,
+                        dlog_a, dbeta, dS0, workspace, bp.total, stream, true);
+    if (st) return st;
+    if (rows > 0) {
+        hipError_t e = kda::launch_bwd_prologue(false, d->qkv_dtype, d->dk, d->scalar_decay, pro, rows, k, log_a,
+                                                beta, k_t, la_t, b_t, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(KDA_ERR_HIP, "prologue launch: %s", hipGetErrorString(e));
+    }
+    st = chunk_bwd_impl(d, q, k_in, v, la_in, b_in, S0, cu_seqlens, saved, states, state_rows, dO, dS_T, dq, dk, dv,
+                        dlog_a, dbeta, dS0, workspace, bp.total, stream);
+    if (st) return st;
+    if (rows > 0) {
+        hipError_t e = kda::launch_bwd_prologue(true, d->qkv_dtype, d->dk, d->scalar_decay, pro, rows, k, log_a, beta,
+                                                dk, dlog_a, dbeta, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(KDA_ERR_HIP, "prologue gradient launch: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+int kda_chunk_bwd_ex(const kda_dims_t* d, const kda_prologue_t* prologue, const void* q, const void* k,
+                     const void* v, const float* log_a, const float* beta, const float* S0,
+                     const int32_t* cu_seqlens, const float* states, int64_t state_rows, const void* dO,
+                     const float* dS_T, void* dq, void* dk, void* dv, float* dlog_a, float* dbeta, float* dS0,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_bwd_ex_impl(d, prologue, q, k, v, log_a, beta, S0, cu_seqlens, states, state_rows, dO, dS_T, dq,
+                             dk, dv, dlog_a, dbeta, dS0, workspace, workspace_bytes, stream);
+}
 
 int kda_chunk_bwd(const kda_dims_t* d, const void* q, const void* k, const void* v, const float* log_a,
                   const float* beta, const float* S0, const int32_t* cu_seqlens, const void* dO, const float* dS_T,

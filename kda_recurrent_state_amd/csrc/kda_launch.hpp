@@ -39,6 +39,15 @@ struct ChunkArgs {
     Prologue pro;               // input prologue (none by default)
 };
 
+// The input prologue around the prefill's gradient, over rows (token, head):
+// grad = false writes the transformed inputs (k_out, la_out, b_out) from the raw
+// ones; grad = true applies the chain rule through the transforms in place to
+// the gradient's dk (k_out), dlog_a (la_out) and dbeta (b_out).  Transforms that
+// pro does not request are skipped (their outputs are not touched).
+hipError_t launch_bwd_prologue(bool grad, int dtype, int dk, int scalar, const Prologue& pro, int64_t rows,
+                               const void* k, const float* log_a, const float* beta, void* k_out, float* la_out,
+                               float* b_out, hipStream_t st);
+
 bool decode_supported(int dtype, int dk, int dv);
 hipError_t launch_decode(int dtype, int dk, int dv, int scalar, int order, const Prologue& pro, int64_t heads,
                          const void* q,

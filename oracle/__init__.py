@@ -168,8 +168,35 @@ def kda_oracle(q, k, v, log_a, beta, S0=None, cu_seqlens=None, order: int = 0,
     return o, ST
 
 
+def prologue_bwd(k, log_a, beta, grads, normalize_k=False, beta_logits=False, log_a_raw=False, log_a_min=None):
+    """Chain rule through prologue(): given the raw inputs (k, log_a, beta) and
+    the derivatives "dk", "dlog_a", "dbeta" with respect to the transformed
+    ones, return a copy of grads with those three taken with respect to the raw
+    inputs (fp64):
+      normalize_k:  with n = sqrt(|x|^2 + eps) and u = x / n,  dx = (du - u (u . du)) / n
+      beta_logits:  with b = 1 / (1 + e^-z),                   dz = db b (1 - b)
+      log_a_raw:    with y the pre-activation,                 dy = dlog_a (-1 / (1 + e^-y)),
+                    and 0 where the clip at log_a_min is active (-softplus(y) < log_a_min)."""
+    k, log_a, beta = _f64(k), _f64(log_a), _f64(beta)
+    out = dict(grads)
+    if normalize_k:
+        n = np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + PROLOGUE_EPS)
+        u, du = k / n, np.asarray(grads["dk"], dtype=np.float64)
+        out["dk"] = (du - u * np.sum(u * du, axis=-1, keepdims=True)) / n
+    if beta_logits:
+        b = 1.0 / (1.0 + np.exp(-beta))
+        out["dbeta"] = np.asarray(grads["dbeta"], dtype=np.float64) * b * (1.0 - b)
+    if log_a_raw:
+        d = -np.asarray(grads["dlog_a"], dtype=np.float64) / (1.0 + np.exp(-log_a))
+        if log_a_min is not None:
+            y = -(np.maximum(log_a, 0.0) + np.log1p(np.exp(-np.abs(log_a))))
+            d = np.where(y >= float(log_a_min), d, 0.0)
+        out["dlog_a"] = d
+    return out
+
+
 def kda_oracle_bwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, dO=None, dST=None,
-                   order: int = 0, threads: int | None = None, lib=None):
+                   order: int = 0, threads: int | None = None, lib=None, pro: dict | None = None):
     """Gradient of kda_oracle in fp64.
 
     For a scalar loss whose derivatives with respect to kda_oracle's outputs are
@@ -178,7 +205,17 @@ def kda_oracle_bwd(q, k, v, log_a, beta, S0=None, cu_seqlens=None, dO=None, dST=
     "dlog_a" (the shape of log_a), "dbeta" [T, H] and "dS0" [N, H, dk, dv], as
     float64 arrays.  The walk is the chain rule applied to one token's update at a
     time, backwards from the last token (kda_oracle.c, kda_oracle_bwd).
+
+    pro: keyword arguments of prologue(): k, log_a and beta are then raw inputs,
+    transformed first, and their derivatives are taken through the transforms
+    (prologue_bwd).
     """
+    if pro:
+        raw = (_f64(k), _f64(log_a), _f64(beta))
+        k, log_a, beta = prologue(*raw, **pro)
+        g = kda_oracle_bwd(q, k, v, log_a, beta, S0=S0, cu_seqlens=cu_seqlens, dO=dO, dST=dST, order=order,
+                           threads=threads, lib=lib)
+        return prologue_bwd(*raw, g, **pro)
     q, k, v, log_a, beta = (_f64(x) for x in (q, k, v, log_a, beta))
     T, H, dk = q.shape
     dv = v.shape[2]

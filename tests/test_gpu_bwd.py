@@ -167,6 +167,59 @@ def test_bwd_saved_states_equal_lengths():
         kda.chunk_bwd(*args, inp["dO"], S0=inp["S0"], num_seqs=2, states=states[:5])
 
 
+PRO = dict(normalize_k=True, beta_logits=True, log_a_raw=True, log_a_min=-6.0)
+
+
+def raw_draw(dtype, d, lengths, seed, scalar=False):
+    from kda_recurrent_state_amd.workloads import generate_raw
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=len(lengths), heads=2, dk=d, dv=d, dtype=dtype,
+               scalar_decay=scalar, s0_std=0.3)
+    inp = generate_raw(w, seed, DEV, lengths=lengths)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed + 1000)
+    T = int(np.sum(lengths))
+    inp["dO"] = torch.randn((T, 2, d), generator=g, device=DEV).to(dtype)
+    inp["dST"] = torch.randn((len(lengths), 2, d, d), generator=g, device=DEV)
+    return inp
+
+
+def oracle_grad_pro(inp, pro):
+    c = lambda t: None if t is None else t.detach().cpu()
+    return kda_oracle_bwd(c(inp["q"]), c(inp["k"]), c(inp["v"]), c(inp["log_a"]), c(inp["beta"]), S0=c(inp["S0"]),
+                          cu_seqlens=inp["cu_seqlens"].cpu().numpy(), dO=c(inp["dO"]), dST=c(inp["dST"]), pro=pro)
+
+
+@pytest.mark.parametrize("dtype,d,scalar,saved", [(torch.bfloat16, 128, False, False), (torch.bfloat16, 64, True, False),
+                                                  (torch.float32, 32, False, False), (torch.bfloat16, 128, False, True),
+                                                  (torch.float32, 16, True, True)])
+def test_bwd_prologue(dtype, d, scalar, saved):
+    """Gradient with respect to the raw inputs of a forward that ran the input
+    prologue (kda_chunk_bwd_ex), from a rerun or from the forward's kept
+    states, against the oracle's gradient through the same prologue."""
+    log(f"backward with prologue {dtype} d={d} scalar={scalar} saved={saved}")
+    inp = raw_draw(dtype, d, [150, 64, 37], 70 + d + scalar, scalar)
+    states = None
+    if saved:
+        _, _, states = kda.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"],
+                                               S0=inp["S0"], cu_seqlens=inp["cu_seqlens"], snapshot_every=64,
+                                               prologue=PRO)
+    got = gpu_grad(inp, prologue=PRO, states=states)
+    ref = oracle_grad_pro(inp, PRO)
+    errs = {n: max_rel_err(got[n], ref[n]) for n in NAMES}
+    log("  " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= TOL[dtype]}
+    assert not bad, bad
+
+
+def test_bwd_prologue_off_is_plain():
+    """An all-zero prologue is the plain call, bit for bit."""
+    inp = draw("kda_b2_h32_t32768_d128_bf16", 77, [100, 30])
+    a = gpu_grad(inp)
+    b = gpu_grad(inp, prologue=dict())
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
+
+
 @pytest.mark.parametrize("d", [32, 128])
 def test_bwd_deterministic(d):
     # bit-identical results whatever the workspace held before the call

@@ -74,3 +74,98 @@ def test_prologue_feeds_the_recurrence(order):
     bb = np.exp(-np.logaddexp(0.0, -b))
     o2, s2 = kda_oracle(q, kn, v, la, bb, order=order)
     assert np.max(np.abs(o1 - o2)) < 1e-12 and np.max(np.abs(s1 - s2)) < 1e-12
+
+
+# ---- the gradient through the prologue (oracle.prologue_bwd) -----------------------
+PRO_ALL = dict(normalize_k=True, beta_logits=True, log_a_raw=True, log_a_min=-2.0)
+
+
+def _raw_case(seed, scalar=False, T=9, H=2, dk=4, dv=3):
+    rng = np.random.default_rng(seed)
+    q, v = rng.normal(size=(T, H, dk)), rng.normal(size=(T, H, dv))
+    k = rng.normal(size=(T, H, dk)) * 2.0
+    x = rng.normal(size=(T, H) if scalar else (T, H, dk)) * 2.0
+    # keep every pre-activation away from the clip's corner at -softplus(y) = -2
+    y = -np.logaddexp(0.0, x)
+    x = np.where(np.abs(y + 2.0) < 1e-3, x + 0.1, x)
+    z = rng.normal(size=(T, H))
+    S0 = rng.normal(size=(2, H, dk, dv)) * 0.3
+    dO, dST = rng.normal(size=(T, H, dv)), rng.normal(size=(2, H, dk, dv))
+    return q, k, v, x, z, S0, np.array([0, 4, T]), dO, dST
+
+
+def _grad_fd(case, pro, name, idx, h=1e-6):
+    q, k, v, x, z, S0, cu, dO, dST = case
+    args = dict(k=k, log_a=x, beta=z)
+
+    def loss(val):
+        a = {n: t.copy() for n, t in args.items()}
+        a[name][idx] = val
+        o, S = kda_oracle(q, a["k"], v, a["log_a"], a["beta"], S0=S0, cu_seqlens=cu, pro=pro)
+        return float(np.sum(o * dO) + np.sum(S * dST))
+    x0 = args[name][idx]
+    return (loss(x0 + h) - loss(x0 - h)) / (2 * h)
+
+
+def _check_against_fd(case, grads, pro):
+    """Every raw element of k, log_a and beta against a central difference of
+    the forward oracle with the prologue (its own pins are above)."""
+    worst = 0.0
+    for name, key in (("k", "dk"), ("log_a", "dlog_a"), ("beta", "dbeta")):
+        g = grads[key]
+        scale = max(np.max(np.abs(g)), 1e-3)
+        for idx in np.ndindex(g.shape):
+            worst = max(worst, abs(_grad_fd(case, pro, name, idx) - g[idx]) / scale)
+    return worst
+
+
+@pytest.mark.parametrize("scalar", [False, True])
+def test_prologue_gradient_matches_finite_differences(scalar):
+    from oracle import kda_oracle_bwd
+    case = _raw_case(11 + scalar, scalar)
+    q, k, v, x, z, S0, cu, dO, dST = case
+    g = kda_oracle_bwd(q, k, v, x, z, S0=S0, cu_seqlens=cu, dO=dO, dST=dST, pro=PRO_ALL)
+    y = -np.logaddexp(0.0, x)
+    assert np.any(y < -2.0) and np.any(y > -2.0)      # both sides of the clip are exercised
+    assert np.all(g["dlog_a"][y < -2.0] == 0.0)
+    assert _check_against_fd(case, g, PRO_ALL) < 1e-6
+
+
+def test_prologue_gradient_each_transform_alone():
+    from oracle import kda_oracle_bwd
+    case = _raw_case(13)
+    q, k, v, x, z, S0, cu, dO, dST = case
+    for pro in (dict(normalize_k=True), dict(beta_logits=True), dict(log_a_raw=True)):
+        xx = x if pro.get("log_a_raw") else -np.abs(x) * 0.3   # a valid log a when taken as given
+        zz = z if pro.get("beta_logits") else 1.0 / (1.0 + np.exp(-z))
+        c = (q, k, v, xx, zz, S0, cu, dO, dST)
+        g = kda_oracle_bwd(q, k, v, xx, zz, S0=S0, cu_seqlens=cu, dO=dO, dST=dST, pro=pro)
+        assert _check_against_fd(c, g, pro) < 1e-6, pro
+
+
+def _mutant_grads(case, which):
+    """The chain rule with one planted mistake, from the oracle's gradient on the
+    transformed inputs."""
+    from oracle import kda_oracle_bwd
+    q, k, v, x, z, S0, cu, dO, dST = case
+    kt, lat, bt = prologue(k, x, z, **PRO_ALL)
+    g = dict(kda_oracle_bwd(q, kt, v, lat, bt, S0=S0, cu_seqlens=cu, dO=dO, dST=dST))
+    n = np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + PROLOGUE_EPS)
+    u, du = k / n, g["dk"]
+    g["dk"] = (du - u * np.sum(u * du, axis=-1, keepdims=True)) / n
+    if which == "no projection":
+        g["dk"] = du / n
+    b = 1.0 / (1.0 + np.exp(-z))
+    g["dbeta"] = g["dbeta"] * (b if which == "beta slope" else b * (1.0 - b))
+    sig = 1.0 / (1.0 + np.exp(-x))
+    d = (1.0 if which == "log a sign" else -1.0) * g["dlog_a"] * sig
+    y = -np.logaddexp(0.0, x)
+    g["dlog_a"] = d if which == "no clip mask" else np.where(y >= -2.0, d, 0.0)
+    return g
+
+
+@pytest.mark.parametrize("which", ["no projection", "beta slope", "log a sign", "no clip mask"])
+def test_prologue_gradient_pins_catch_planted_mistakes(which):
+    case = _raw_case(17)
+    assert _check_against_fd(case, _mutant_grads(case, "none"), PRO_ALL) < 1e-6
+    assert _check_against_fd(case, _mutant_grads(case, which), PRO_ALL) > 1e-3

@@ -48,7 +48,8 @@ def test_oracle_under_asan_ubsan(outdir):
 def test_api_host_validation_under_asan_ubsan(outdir):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    kernels = ["kda_decode", "kda_chunk", "kda_prep", "kda_prep2", "kda_scan", "kda_bwd"]
+    from kda_recurrent_state_amd import _build as library_build
+    kernels = [os.path.splitext(f)[0] for f in library_build.SOURCES if f.endswith(".hip")]
     objs = [os.path.join(BUILD, k + ".o") for k in kernels]
     if not all(os.path.exists(o) for o in objs):
         from kda_recurrent_state_amd import _build
