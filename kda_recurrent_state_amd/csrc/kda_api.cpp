@@ -130,7 +130,10 @@ constexpr size_t kSegmentTarget = size_t(4) << 30;
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Smallest split with at least 256 workgroups among the two-pass shapes.
+// Smallest split with at least 256 workgroups among the two-pass shapes, and
+// with slices of at most 64 columns: the 128-column state pass holds two
+// column blocks of a 128-row state per wavefront and spills registers (on the
+// 64-sequence varlen batch split 2 runs 15.5 ms against 16.4 ms at split 1).
 int choose_split_two_pass(const kda_dims_t* d, int chunk) {
     const int64_t units = (int64_t)d->num_seqs * d->num_heads;
     int best = 0;
@@ -138,7 +141,7 @@ int choose_split_two_pass(const kda_dims_t* d, int chunk) {
         if (d->dv % split) break;
         if (!kda::two_pass_supported(d->qkv_dtype, d->dk, d->dv / split, chunk)) continue;
         best = split;
-        if (units * split >= 256) break;
+        if (units * split >= 256 && d->dv / split <= 64) break;
     }
     return best;
 }

@@ -76,6 +76,33 @@ struct ScanParams {
     int snap_every;       // tokens between snapshots (a multiple of C)
 };
 
+// Place of the value tile's 16-byte piece u of token row t (VPR pieces per
+// row) among the tile's pieces in LDS.  The copy puts each piece there (the
+// LDS-DMA lands lane l's 16 bytes at slot piece l, so the permutation is in
+// the choice of source), so that both LDS accesses of the tile are free of
+// bank conflicts at every slice width: the column reads of the value
+// fragment (16 lanes on 16 columns of a row, 4 row groups 8 rows apart) and
+// the output writes (16 rows, 8 bytes per lane).  Rows are XOR-permuted in
+// groups of four by bits 3-4 of t (an involution) and pieces within a row by
+// bits of t and t / 4.  Slices of 128 columns keep the plain row-major order:
+// there the lanes' extra read addresses would not fit in registers.
+template <int VPR>
+__device__ __forceinline__ int vpiece(int t, int u) {
+    if constexpr (VPR > 8) return VPR * t + u;
+    return VPR * (t ^ ((t >> 3) & 3)) + (u ^ ((t ^ (t >> 2)) & (VPR - 1)));
+}
+template <int VPR>
+__device__ __forceinline__ void vpiece_source(int q, int& t, int& u) {
+    const int r = q / VPR;
+    if constexpr (VPR > 8) {
+        t = r;
+        u = q % VPR;
+        return;
+    }
+    t = r ^ ((r >> 3) & 3);
+    u = (q % VPR) ^ ((t ^ (t >> 2)) & (VPR - 1));
+}
+
 // Ends a chunk: waits until at most N vector-memory operations of this
 // wavefront are outstanding and all its LDS reads have returned, then joins the
 // workgroup barrier.  A release fence is not used here: on LDS it would also
@@ -133,7 +160,6 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
     const uint32_t oM = piece<C>(lr, lg);                                   // M1, M2 fragments
     const uint32_t oK = piece<DK>(lr, lg);                                  // KC, KT fragments
     const uint32_t oG = WS::GAM + 16 * lg;                                  // GAM rows 4 lg .. 4 lg + 3
-    const uint32_t oV = G::NPB * 16 + 2 * (8 * lg * DVS + 16 * wv * CB + lr);  // value tile [token][column]
 
     // Copy chunk jj's operator block and value tile into slot sl: piece
     // r * NT + tid of the slot comes from the block (below NPB), from the value
@@ -152,7 +178,8 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
                 src = (blk + r * LT * 16) + (uint32_t)(16 * lt);
             } else {
                 const int pc = min(r * LT + lt, G::NPS - 1);
-                const int q = max(pc - G::NPB, 0), t = q / G::VPR, u = q % G::VPR;
+                int t, u;
+                vpiece_source<G::VPR>(max(pc - G::NPB, 0), t, u);
                 // rows past the chunk's end repeat its last row: they meet zero operator columns
                 const int64_t row = (t0 + min(t, Lc - 1)) * H + h;
                 const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(gv + row * DV + dv0 + 8 * u);
@@ -184,7 +211,8 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
         for (int r = 0; r < ROUNDS; ++r) {
             if ((r + 1) * LT <= G::NPB || r * LT >= G::NPS) continue;  // rounds without output pieces
             const int pc = r * LT + lt;
-            const int q = pc - G::NPB, t = q / G::VPR, u = q % G::VPR;
+            int t, u;
+            vpiece_source<G::VPR>(max(pc - G::NPB, 0), t, u);
             if (pc >= G::NPB && pc < G::NPS && t < Lc) {
                 const i32x4 x = *reinterpret_cast<const i32x4*>(slot + 16 * pc);
                 *reinterpret_cast<i32x4*>(go + ((t0 + t) * H + h) * DV + dv0 + 8 * u) = x;
@@ -265,7 +293,14 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
     // outputs of a chunk go (bf16) into the value tile of its slot, which the
     // value fragments have left by then; the copy wavefronts store them
     f32x4 ot[CB][NTT];
-    const uint32_t oO = G::NPB * 16 + 2 * (lr * DVS + 16 * wv * CB + 4 * lg);  // [token][column]
+    // this lane's output piece offsets (token 16 tt + lr, columns 16 (wv CB + cb) + 4 lg ..)
+    uint32_t oO[CB][NTT];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+            oO[cb][tt] = G::NPB * 16 + 16 * vpiece<G::VPR>(16 * tt + lr, 2 * (wv * CB + cb) + (lg >> 1)) +
+                         8 * (lg & 1);
 
     auto frag = [](const uint8_t* a) { return *reinterpret_cast<const bf16x8*>(a); };
     // Group 1 of a chunk: the E operands and the value fragment (column j of the
@@ -277,11 +312,14 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
     bf16x8 wf[NTT][NKS], m1f[NTT], vfr[CB];
     bf16 vraw[CB][8];  // value elements as read; packed into vfr where first used
     auto read_group1 = [&](const uint8_t* B) {
-        const bf16* bV = reinterpret_cast<const bf16*>(B + oV);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vraw[cb][e] = bV[e * DVS + 16 * cb];
+            for (int e = 0; e < 8; ++e) {
+                const int u = 2 * (wv * CB + cb) + (lr >> 3);
+                vraw[cb][e] = *reinterpret_cast<const bf16*>(
+                    B + G::NPB * 16 + 16 * vpiece<G::VPR>(8 * lg + e, u) + 2 * (lr & 7));
+            }
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
             m1f[tt] = frag(B + oM + WS::M1 + 16 * 16 * tt);
@@ -361,8 +399,7 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
             for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt)
-                    store4(reinterpret_cast<bf16*>(B + oO + 2 * (16 * tt * DVS + 16 * cb)),
-                           ot[cb][tt]);
+                    store4(reinterpret_cast<bf16*>(B + oO[cb][tt]), ot[cb][tt]);
             __builtin_amdgcn_sched_barrier(0);
 
             // This chunk's LDS reads and output writes are done; the barrier hands
