@@ -48,7 +48,11 @@ namespace kda {
 
 namespace p2 {
 constexpr int DK = 128, C = 32, NT = 256;
-constexpr int LDK = DK + 8;  // bf16 rows over channels
+// Row pitches.  Channel rows are 288 bytes: measured on gfx950 (one access
+// pattern at a time over the whole chip), the Gram fragment reads of phase B
+// (16 rows x 16 bytes per lane group) take 4 LDS cycles with this pitch and 8
+// with 272-byte rows.
+constexpr int LDK = DK + 16; // bf16 rows over channels
 constexpr int LDC = C + 8;   // bf16 rows over tokens
 constexpr int LDA = C + 4;   // fp32 rows over tokens
 constexpr float LA_MIN = -15.f;  // log2 clamp inside the factor split (never reached in its range)
