@@ -561,6 +561,20 @@ def main():
                 saved_step()
             torch.cuda.synchronize()
             tsv = time_events(saved_step, args.steps, stream) / args.steps
+            # the decay-first order's gradient from that order's kept states
+            kda.chunk_fwd_snapshots(x["q"], x["k"], x["v"], x["log_a"], x["beta"], S0=x["S0"],
+                                    cu_seqlens=x["cu_seqlens"], snapshot_every=64, snapshots=snaps64, out=o,
+                                    final_state=False, method=method, workspace=ws, max_seqlen=wp.seqlen,
+                                    order=kda.ORDER_DECAY_FIRST)
+
+            def saved_step_df():
+                return kda.chunk_bwd(x["q"], x["k"], x["v"], x["log_a"], x["beta"], dO, S0=x["S0"],
+                                     cu_seqlens=x["cu_seqlens"], dS_T=dST, workspace=wsS, max_seqlen=wp.seqlen,
+                                     states=snaps64, order=kda.ORDER_DECAY_FIRST)
+            for _ in range(max(args.warmup, 3)):
+                saved_step_df()
+            torch.cuda.synchronize()
+            tdf = time_events(saved_step_df, args.steps, stream) / args.steps
             del snaps64, wsS
             Bb, Fb = backward_algorithmic(wp)
             out["backward"] = {
@@ -584,6 +598,8 @@ def main():
                     "note": "kda_chunk_bwd_saved with the states a forward call kept every 64 tokens; a training "
                             "step is that forward plus this call, against the plain forward plus kda_chunk_bwd",
                 },
+                "decay_first_saved_states": {"ms_per_step": tdf * 1e3, "tokens_per_s": tokens / tdf,
+                                             "frac_hbm": Bb / tdf / 1e9 / PEAK_HBM_GBS},
             }
             log(f"backward: {tb*1e3:.3f} ms/step ({tokens/tb/1e6:.2f} Mtok/s), prefill rerun {tr*1e3:.3f} ms, "
                 f"gradient kernels {(tb-tr)*1e3:.3f} ms; from saved states {tsv*1e3:.3f} ms (identical: {same})")

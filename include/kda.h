@@ -262,8 +262,9 @@ KDA_API int kda_chunk_workspace_min(const kda_dims_t* dims, size_t* bytes);
  * keeping the state at every 64th token, then three kernels walk 16-token
  * pieces: operators per piece, the derivative with respect to the state
  * backwards through each sequence, and the gradients of each 64-token chunk.
- * Supported: the erase-first order (KDA_ORDER_DECAY_FIRST with a per-channel
- * decay returns KDA_ERR_UNSUPPORTED); bf16 with dk, dv in {32, 64, 128}, fp32
+ * Both orders (dims.order; the decay-first map's chunk form is the erase-first
+ * one with each token's decay applied before its own read, and differs only in
+ * the last step of dlog_a); bf16 with dk, dv in {32, 64, 128}, fp32
  * with dk, dv in {16, 32, 64}, in both cases dk and dv equal or a factor 2
  * apart.  No input prologue (kda_chunk_bwd_ex takes one).  Outputs must not alias
  * inputs or each other.  Returns a kda_status_t.

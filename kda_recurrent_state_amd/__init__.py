@@ -362,8 +362,9 @@ def chunk_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, 
 
 def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, chunk_size: int = 0,
               dv_split: int = 0, num_seqs: int | None = None, method: int = METHOD_AUTO, workspace=None,
-              max_seqlen: int | None = None, initial_state_grad=True, states=None, prologue: dict | None = None):
-    """Gradient of chunk_fwd (erase-first order) for upstream derivatives dO
+              max_seqlen: int | None = None, initial_state_grad=True, states=None, prologue: dict | None = None,
+              order: int = ORDER_ERASE_FIRST):
+    """Gradient of chunk_fwd (in the order `order`) for upstream derivatives dO
     [T,H,dv] (and dS_T [N,H,dk,dv], None for zero).  Returns a dict with "dq",
     "dk" [T,H,dk] and "dv" [T,H,dv] in q's dtype, "dlog_a" (log_a's shape) and
     "dbeta" [T,H] in float32, and "dS0" [N,H,dk,dv] float32 (None when
@@ -427,7 +428,7 @@ def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, 
         else:
             max_seqlen = 0
     d = _Dims(N, H, T, dk, dv, _dtype_code(q), scalar, int(chunk_size), int(dv_split), int(method),
-              ORDER_ERASE_FIRST, int(max_seqlen))
+              int(order), int(max_seqlen))
     pro = _prologue(prologue)
     if workspace is None:
         need = ctypes.c_size_t(0)
@@ -459,14 +460,15 @@ def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, 
 
 
 def chunk_bwd_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, dv_split=0,
-                             method=METHOD_AUTO, max_seqlen=0, saved=False, prologue: dict | None = None):
+                             method=METHOD_AUTO, max_seqlen=0, saved=False, prologue: dict | None = None,
+                             order: int = ORDER_ERASE_FIRST):
     """Bytes of workspace chunk_bwd needs for these shapes (saved=True: with the
     forward's states passed in, so without the prefill rerun; prologue: the
     input prologue the forward ran)."""
     lib = load_library()
     T, H, dk = q.shape
     d = _Dims(int(num_seqs), H, T, dk, v.shape[2], _dtype_code(q), int(bool(scalar_decay)), int(chunk_size),
-              int(dv_split), int(method), ORDER_ERASE_FIRST, int(max_seqlen))
+              int(dv_split), int(method), int(order), int(max_seqlen))
     need = ctypes.c_size_t(0)
     pro = _prologue(prologue)
     if pro is not None:

@@ -457,8 +457,6 @@ size_t prologue_bytes(const kda_dims_t* d) {
 int plan_bwd(const kda_dims_t* d, bool have_cu, bool saved, BwdPlan* bp) {
     int st = plan_prefill(d, have_cu, &bp->fwd);
     if (st) return st;
-    if (d->order == KDA_ORDER_DECAY_FIRST && !d->scalar_decay)
-        return fail(KDA_ERR_UNSUPPORTED, "the backward supports the erase-first order only");
     if (!kda::bwd_supported(d->qkv_dtype, d->dk, d->dv))
         return fail(KDA_ERR_UNSUPPORTED, "no backward for dtype %d, dk %d, dv %d", d->qkv_dtype, d->dk, d->dv);
     const int64_t T = d->total_tokens, N = d->num_seqs, H = d->num_heads;
@@ -617,9 +615,7 @@ int chunk_bwd_impl(const kda_dims_t* d, const void* q, const void* k, const void
     } else if (bp.snap_rows > 0) {
         // the prefill again, keeping the state at every 64th token (nothing to
         // keep when no sequence reaches 64 tokens)
-        kda_dims_t d2 = *d;
-        d2.order = KDA_ORDER_ERASE_FIRST;
-        st = kda_chunk_fwd_snapshots(&d2, q, k, v, log_a, beta, S0, cu_seqlens, o_scratch, nullptr, snap,
+        st = kda_chunk_fwd_snapshots(d, q, k, v, log_a, beta, S0, cu_seqlens, o_scratch, nullptr, snap,
                                      bp.snap_rows, 64, fwd_ws, bp.fwd_ws, stream);
         if (st) return st;
     }
@@ -631,6 +627,7 @@ int chunk_bwd_impl(const kda_dims_t* d, const void* q, const void* k, const void
     a.snap = snap; a.snap_rows = snap_rows; a.ops = ops; a.xbuf = xbuf; a.scr = scr;
     a.num_heads = d->num_heads; a.units = units; a.nsub_max = (int32_t)nsub_max; a.nch_max = (int32_t)nch_max;
     a.kdim = d->dk; a.vdim = d->dv; a.dtype = d->qkv_dtype; a.scalar = d->scalar_decay;
+    a.order = kernel_order(d);
     hipError_t e = kda::launch_bwd(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return ok();

@@ -1,6 +1,6 @@
 // kda_bwd.hip -- gradient of the prefill (the erase-then-decay ordering of the
-// table row "KDA" on page "The argument, in one page", in its chunkwise form, row
-// "Chunkwise / WY" of the same table).
+// table row "KDA" on page "The argument, in one page", and the decay-first one, in
+// their chunkwise form, row "Chunkwise / WY" of the same table).
 //
 // For a loss with derivatives dO (outputs) and dS_T (final states), the call
 // returns dq, dk, dv, dlog_a, dbeta and dS0.  Per (sequence, head) the tokens are
@@ -27,6 +27,15 @@
 // m = gC / 2 (Kc' = k e^{m-gm}, Kt' = k e^{m-g}, Qb' = q e^{g-m}, Kb' = k e^{gm-m}),
 // so every factor stays below e^{span/2}.  A sub-chunk whose span -gC exceeds 160
 // nats in some channel takes one exponent per term instead.
+//
+// The decay-first ordering, S_i = (I - b_i k_i^T k_i) Diag(a_i) S_{i-1} + b_i k_i^T v_i,
+// reads its token after the token's own decay and erases along the same key it
+// writes: its chunk form is every line above with gm replaced by g (then A0 = L,
+// P1 = P2, Kcc = Ktc), except the last step of dlog_a, which takes the step's own
+// telescoping terms off phi instead of b k vds:
+//   dlog_a_i = phi_i - (k dk + 2 b k gs)_i.
+// The kernels read gm from the decay-sum row of the token itself (gmo = 1) instead
+// of the row before it.
 //
 // Barriers inside the walks order LDS only (lds_barrier), so global loads fetched
 // for the next step stay in flight across them; every global value a walk reads
@@ -195,6 +204,7 @@ struct BwdParams {
     int32_t H;
     int32_t scalar;
     int32_t split;
+    int32_t gmo;             // 1: decay-first order, whose operators take g where erase-first takes gm
 };
 
 // A sub-chunk's inputs for one wavefront, in two halves: fetch issues every load
@@ -275,6 +285,7 @@ struct DecayFetch {
 // rows and the decays to the masked products and T once Kcc^T is formed.
 template <typename MT, int DK>
 __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
+    const int gmo = p.gmo;
     typedef OpBlock<MT, DK> OB;
     constexpr int P = 16 / (int)sizeof(MT);
     constexpr int LDK = DK + P, L16 = 16 + P;
@@ -334,7 +345,7 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
             for (int e = 0; e < 8; ++e) {
                 const int s2 = s0 + e;
                 out[e] = s2 < 16 ? to_f32(qr[s2 * LDK + c]) * ex2(G2[(s2 + 1) * G2L + c])
-                                 : to_f32(kr[(s2 - 16) * LDK + c]) * ex2(G2[(s2 - 16) * G2L + c]);
+                                 : to_f32(kr[(s2 - 16) * LDK + c]) * ex2(G2[(s2 - 16 + gmo) * G2L + c]);
             }
             store8<MT>(qk + c * 32 + s0, out);
         }
@@ -367,9 +378,9 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
             for (int e = 0; e < KPL; ++e) {
                 const int c = c0 + e;
                 const float m2 = 0.5f * G2[SC * G2L + c];
-                fk[e] = ex2(G2[r16 * G2L + c] - m2);          // e^{gm_t - m}
+                fk[e] = ex2(G2[(r16 + gmo) * G2L + c] - m2);  // e^{gm_t - m}
                 fq[e] = ex2(G2[(r16 + 1) * G2L + c] - m2);    // e^{g_t - m}
-                fm[e] = ex2(m2 - G2[r16 * G2L + c]);          // e^{m - gm_i}
+                fm[e] = ex2(m2 - G2[(r16 + gmo) * G2L + c]);  // e^{m - gm_i}
                 fg[e] = ex2(m2 - G2[(r16 + 1) * G2L + c]);    // e^{m - g_i}
             }
             const typename Mma<MT>::frag kx = Mma<MT>::loadr(kr + r16 * LDK + kb, lane);
@@ -391,8 +402,8 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
             if (i <= t) {
                 for (int c = 0; c < DK; ++c) {
                     const float kt = to_f32(kr[t * LDK + c]), qt = to_f32(qr[t * LDK + c]), ki = to_f32(kr[i * LDK + c]);
-                    const float gmt = G2[t * G2L + c], gt = G2[(t + 1) * G2L + c];
-                    const float gmi = G2[i * G2L + c], gi = G2[(i + 1) * G2L + c];
+                    const float gmt = G2[(t + gmo) * G2L + c], gt = G2[(t + 1) * G2L + c];
+                    const float gmi = G2[(i + gmo) * G2L + c], gi = G2[(i + 1) * G2L + c];
                     if (i < t) {
                         a0 += kt * ki * ex2(gmt - gmi);
                         l += kt * ki * ex2(gmt - gi);
@@ -409,7 +420,7 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     // Kcc^T [c][s] = k_s e^{gC - gm_s}
     for (int x = lane; x < DK * 16; x += 64) {
         const int c = x >> 4, s2 = x & 15;
-        KCT[c * 16 + s2] = from_f32<MT>(to_f32(kr[s2 * LDK + c]) * ex2(G2[SC * G2L + c] - G2[s2 * G2L + c]));
+        KCT[c * 16 + s2] = from_f32<MT>(to_f32(kr[s2 * LDK + c]) * ex2(G2[SC * G2L + c] - G2[(s2 + gmo) * G2L + c]));
     }
     __syncthreads();  // k's rows and the decays are dead
 
@@ -696,16 +707,16 @@ struct GradSmem {
 // for this lane's rows t = 4 g4 + r and channel c.  Masked-out pairs hold 0;
 // clamping their exponents at 0 keeps them finite.
 template <typename MT, int DK, typename SM>
-__device__ __attribute__((noinline)) void exact_terms(const SM& sm, int c, int g4, f32x4& mq, f32x4& mg, f32x4& mv,
-                                                      f32x4& my) {
+__device__ __attribute__((noinline)) void exact_terms(const SM& sm, int c, int g4, int gmo, f32x4& mq, f32x4& mg,
+                                                      f32x4& mv, f32x4& my) {
     constexpr int LDK = SM::LDK, L32 = SM::L32;
     for (int r = 0; r < 4; ++r) {
         const int t = 4 * g4 + r;
         float aq = 0.f, ag = 0.f, av = 0.f, ay = 0.f;
-        const float gmt = sm.G2[t * SM::G2L + c], gt = sm.G2[(t + 1) * SM::G2L + c];
+        const float gmt = sm.G2[(t + gmo) * SM::G2L + c], gt = sm.G2[(t + 1) * SM::G2L + c];
         for (int i = 0; i < 16; ++i) {
             const float ki = to_f32(sm.kr[i * LDK + c]), qi = to_f32(sm.qr[i * LDK + c]);
-            const float gmi = sm.G2[i * SM::G2L + c], gi = sm.G2[(i + 1) * SM::G2L + c];
+            const float gmi = sm.G2[(i + gmo) * SM::G2L + c], gi = sm.G2[(i + 1) * SM::G2L + c];
             aq += to_f32(sm.MQ[t * L32 + i]) * ki * ex2n(gt - gmi) + to_f32(sm.MQ[t * L32 + 16 + i]) * ki * ex2n(gt - gi);
             ag += to_f32(sm.MG[t * L32 + i]) * ki * ex2n(gmt - gmi) + to_f32(sm.MG[t * L32 + 16 + i]) * ki * ex2n(gmt - gi);
             av += to_f32(sm.MV[t * L32 + i]) * qi * ex2n(gi - gt) + to_f32(sm.MV[t * L32 + 16 + i]) * ki * ex2n(gmi - gt);
@@ -717,6 +728,7 @@ __device__ __attribute__((noinline)) void exact_terms(const SM& sm, int c, int g
 
 template <typename MT, int DK, int DV>
 __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
+    const int gmo = p.gmo;
     typedef GradSmem<MT, DK, DV> SM;
     typedef OpBlock<MT, DK> OB;
     constexpr int LDK = SM::LDK, LDV = SM::LDV, L16 = SM::L16, L32 = SM::L32;
@@ -914,7 +926,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             // ---- Kb rows, (bV)^T, [Kcc^T | Ktc^T]
             for (int x = tid; x < 16 * DK; x += NT) {
                 const int t = x / DK, c = x % DK;
-                sm.GA[t * LDK + c] = from_f32<MT>(to_f32(sm.kr[t * LDK + c]) * ex2(sm.G2[t * SM::G2L + c]));
+                sm.GA[t * LDK + c] = from_f32<MT>(to_f32(sm.kr[t * LDK + c]) * ex2(sm.G2[(t + gmo) * SM::G2L + c]));
             }
             for (int x = tid; x < 16 * DV; x += NT) {
                 const int i = x % 16, j = x / 16;
@@ -924,7 +936,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 for (int x = tid; x < 16 * DK; x += NT) {
                     const int s2 = x % 16, c = x / 16;
                     const float kv = to_f32(sm.kr[s2 * LDK + c]), gc = sm.G2[SC * SM::G2L + c];
-                    sm.CT[c * L32 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[s2 * SM::G2L + c]));
+                    sm.CT[c * L32 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[(s2 + gmo) * SM::G2L + c]));
                     sm.CT[c * L32 + 16 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[(s2 + 1) * SM::G2L + c]));
                 }
             }
@@ -1045,13 +1057,13 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         for (int x = tid; x < 16 * DK; x += NT) {
             const int t = x / DK, c = x % DK;
             const float kv = to_f32(sm.kr[t * LDK + c]), gc = sm.G2[SC * SM::G2L + c];
-            sm.GA[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[t * SM::G2L + c]));
+            sm.GA[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[(t + gmo) * SM::G2L + c]));
             sm.GB[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[(t + 1) * SM::G2L + c]));
         }
         for (int x = tid; x < 16 * DK; x += NT) {
             const int s2 = x % 16, c = x / 16;
             sm.CT[c * L32 + s2] = from_f32<MT>(to_f32(sm.qr[s2 * LDK + c]) * ex2(sm.G2[(s2 + 1) * SM::G2L + c]));
-            sm.CT[c * L32 + 16 + s2] = from_f32<MT>(to_f32(sm.kr[s2 * LDK + c]) * ex2(sm.G2[s2 * SM::G2L + c]));
+            sm.CT[c * L32 + 16 + s2] = from_f32<MT>(to_f32(sm.kr[s2 * LDK + c]) * ex2(sm.G2[(s2 + gmo) * SM::G2L + c]));
         }
         lds_barrier();
         // ---- dE = Kcc X + P1^T dO  (m = t, n = j) -> dE^T
@@ -1201,7 +1213,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         for (int x = tid; x < 16 * DK; x += NT) {
             const int i = x % 16, c = x / 16;
             const float kv = to_f32(sm.kr[i * LDK + c]), m2 = 0.5f * sm.G2[SC * SM::G2L + c];
-            sm.CT[c * L32 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[i * SM::G2L + c]));
+            sm.CT[c * L32 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[(i + gmo) * SM::G2L + c]));
             sm.CT[c * L32 + 16 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[(i + 1) * SM::G2L + c]));
         }
         lds_barrier();
@@ -1225,7 +1237,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             const int i = x % 16, c = x / 16;
             const float m2 = 0.5f * sm.G2[SC * SM::G2L + c];
             sm.CT[c * L32 + i] = from_f32<MT>(to_f32(sm.qr[i * LDK + c]) * ex2(sm.G2[(i + 1) * SM::G2L + c] - m2));
-            sm.CT[c * L32 + 16 + i] = from_f32<MT>(to_f32(sm.kr[i * LDK + c]) * ex2(sm.G2[i * SM::G2L + c] - m2));
+            sm.CT[c * L32 + 16 + i] = from_f32<MT>(to_f32(sm.kr[i * LDK + c]) * ex2(sm.G2[(i + gmo) * SM::G2L + c] - m2));
         }
         lds_barrier();
         // ---- masked products, combination, outputs  (m = t, n = c)
@@ -1242,14 +1254,14 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 mv[a] = mmak<MT, 32>(sm.MV + r16 * L32, sm.CT + c * L32, zero4(), lane);
                 my[a] = mmak<MT, 32>(sm.MY + r16 * L32, sm.CT + c * L32, zero4(), lane);
             } else {
-                exact_terms<MT, DK>(sm, c, g4, mq[a], mg[a], mv[a], my[a]);
+                exact_terms<MT, DK>(sm, c, g4, gmo, mq[a], mg[a], mv[a], my[a]);
             }
             const float gc = sm.G2[SC * SM::G2L + c], m2 = 0.5f * gc;
             float av[4], au[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * g4 + r;
-                const float gmt = sm.G2[t * SM::G2L + c], gt = sm.G2[(t + 1) * SM::G2L + c];
+                const float gmt = sm.G2[(t + gmo) * SM::G2L + c], gt = sm.G2[(t + 1) * SM::G2L + c];
                 const float fq = exact ? 1.f : ex2(gt - m2), fg = exact ? 1.f : ex2(gmt - m2);
                 const float fv = exact ? 1.f : ex2(m2 - gt), fy = exact ? 1.f : ex2(m2 - gmt);
                 const float dq = ex2(gt) * dqs[a][r] + fq * mq[a][r];
@@ -1261,7 +1273,9 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 const float dk = b * (vd - ay - gs);
                 av[r] = kt * dk + 2.f * b * kt * gs;
                 au[r] = qt * dq;
-                mv[a][r] = b * kt * vd;  // reuse: the b k vds term
+                // reuse: the term dlog a takes off phi (erase-first b k vds; decay-first the
+                // step's own k dk + 2 b k gs)
+                mv[a][r] = gmo ? av[r] : b * kt * vd;
                 oq[a][r] = dq;
                 ok[a][r] = dk;
             }
@@ -1403,7 +1417,7 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t st) {
     p.cu = a.cu_seqlens; p.eq_len = a.eq_len; p.dO = a.dO; p.dST = a.dST;
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dla = a.dlog_a; p.dbeta = a.dbeta; p.dS0 = a.dS0;
     p.snap = a.snap; p.snap_rows = a.snap_rows; p.ops = static_cast<uint8_t*>(a.ops); p.xbuf = a.xbuf; p.scr = a.scr;
-    p.H = a.num_heads; p.scalar = a.scalar; p.split = 0;
+    p.H = a.num_heads; p.scalar = a.scalar; p.split = 0; p.gmo = a.order ? 1 : 0;
     if (a.dtype == 1) {
         if (a.kdim == 128 && a.vdim == 128) return run_all<bf16, 128, 128>(a, p, st);
         if (a.kdim == 128 && a.vdim == 64) return run_all<bf16, 128, 64>(a, p, st);

@@ -127,6 +127,7 @@ struct BwdLaunch {
     int64_t units;
     int32_t nsub_max, nch_max;  // 16- and 64-token pieces of the longest sequence
     int32_t kdim, vdim, dtype, scalar;
+    int32_t order;              // 1: decay-first (per-channel decay), else erase-first
 };
 int bwd_block_bytes(int dtype, int dk);
 int64_t bwd_scratch_bytes(int dtype, int dk, int dv);  // per 64-token chunk

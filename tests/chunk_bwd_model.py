@@ -38,6 +38,17 @@ and so on, each factor at most e^{span/2}.  When a channel's span -gC exceeds
 SPAN_MAX the model (and the kernels) evaluate those products with one exponent
 per term instead.
 
+Decay-first order, S_i = (I - b_i k_i^T k_i) D_i S_{i-1} + b_i k_i^T v_i: the read of
+token i sees the state after its own decay, Y_i = k_i D_i S_{i-1}, and the erase and
+the write share the key.  Its chunk form is the lines above with every gm replaced
+by g (Kb = k e^{g}, A0 = L, P1 = P2, Kcc = Ktc), and so are the reverse walk and the
+products dq, gs, vds, ayds and dk, and the telescoping of phi.  Only the last step
+of dlog_a changes: with Lam_i = dL/dS_i and P_i = D_i S_{i-1},
+  dlog_a_i = rowsum(dL/dP_i * P_i) = phi_i - k_i * dk_i - 2 b_i k_i * gs_i,
+since dL/dP_i = (I - b k^T k) Lam_i, P_i = S_i + b_i k_i^T (Y_i - v_i),
+dk_i = b_i (Lam_i v_i^T - Lam_i Y_i^T - P_i (k_i Lam_i)^T) and gs_i = P_i (k_i Lam_i)^T:
+the sum of the telescoping step's own terms taken off phi_i.
+
 Levels, for a sequence of chunks of CH = 64 tokens split into sub-chunks of 16:
   1. forward states at every chunk start;
   2. the reverse walk X <- X_prev over all sub-chunks (X = dS_T at the end),
@@ -62,16 +73,19 @@ def _triu(M, d):
     return np.triu(M, d)
 
 
-def sub_ops(q, k, la, beta, exact=None):
-    """Per sub-chunk operators.  q, k [n, dk]; la [n, dk]; beta [n]."""
+def sub_ops(q, k, la, beta, exact=None, ord1=False):
+    """Per sub-chunk operators.  q, k [n, dk]; la [n, dk]; beta [n].  ord1: the
+    decay-first order (gm replaced by g)."""
     n, dk = k.shape
     G = np.vstack([np.zeros((1, dk)), np.cumsum(la, axis=0)])  # G[i] = g_{i-1}, G[n] = gC
     gm, g, gC = G[:-1], G[1:], G[-1]
+    if ord1:
+        gm = g
     span = float(np.max(-gC)) if n else 0.0
     if exact is None:
         exact = span > SPAN_MAX
     m = 0.5 * gC
-    o = dict(n=n, q=q, k=k, beta=beta, G=G, gm=gm, g=g, gC=gC, m=m, exact=exact)
+    o = dict(n=n, q=q, k=k, beta=beta, G=G, gm=gm, g=g, gC=gC, m=m, exact=exact, ord1=ord1)
     o["Kb"] = k * np.exp(gm)
     o["Qb"] = q * np.exp(g)
     o["Kcc"] = k * np.exp(gC - gm)
@@ -139,19 +153,20 @@ def sub_grads(o, v, dO, S, X):
     ayds = np.exp(gC - gm) * (Y @ X.T) + masked_rows(o, _triu(Y @ dO.T, 0), q, gm, g, -1) \
         + masked_rows(o, _triu(Y @ F.T, 1), k, gm, gm, -1)
     dk = b[:, None] * (vds - ayds - gs)
-    diff = k * dk + 2.0 * b[:, None] * k * gs
+    own = k * dk + 2.0 * b[:, None] * k * gs
+    diff = own.copy()
     diff[1:] -= q[:-1] * dq[:-1]
     phi = np.sum(X_prev * S, axis=1)[None, :] + np.cumsum(diff, axis=0)
-    dla = phi - b[:, None] * k * vds
+    dla = phi - own if o["ord1"] else phi - b[:, None] * k * vds
     return dict(dq=dq, dk=dk, dv=dv, dlog_a=dla, dbeta=dbeta), X_prev
 
 
-def chunk_backward(q, k, v, la, beta, S0, dO, dST, exact=None):
+def chunk_backward(q, k, v, la, beta, S0, dO, dST, exact=None, ord1=False):
     """One (sequence, head): returns the oracle's gradient dict (without batch axes)."""
     T, dk = q.shape
     dv = v.shape[1]
     subs = [(s, min(s + SUB, T)) for s in range(0, T, SUB)]
-    ops = [sub_ops(q[s:e], k[s:e], la[s:e], beta[s:e], exact) for s, e in subs]
+    ops = [sub_ops(q[s:e], k[s:e], la[s:e], beta[s:e], exact, ord1) for s, e in subs]
     per_chunk = CH // SUB
     # level 1: states at chunk starts
     S = S0.copy()

@@ -111,12 +111,31 @@ int main() {
            KDA_ERR_INVALID_ARGUMENT);
 
     // backward
-    d = dims(); d.order = KDA_ORDER_DECAY_FIRST;
-    expect("bwd decay-first",
+    d = dims(); d.dk = 32; d.dv = 128;
+    expect("bwd unsupported shape",
            kda_chunk_bwd(&d, P(GOOD), P(GOOD), P(GOOD), (const float*)GOOD, (const float*)GOOD, nullptr,
                          (const int32_t*)GOOD, P(GOOD), nullptr, (void*)GOOD, (void*)GOOD, (void*)GOOD, (float*)GOOD,
                          (float*)GOOD, nullptr, (void*)GOOD, size_t(1) << 40, nullptr),
            KDA_ERR_UNSUPPORTED);
+    d = dims();
+    expect("bwd saved without states",
+           kda_chunk_bwd_saved(&d, P(GOOD), P(GOOD), P(GOOD), (const float*)GOOD, (const float*)GOOD, nullptr,
+                               (const int32_t*)GOOD, nullptr, 0, P(GOOD), nullptr, (void*)GOOD, (void*)GOOD,
+                               (void*)GOOD, (float*)GOOD, (float*)GOOD, nullptr, (void*)GOOD, size_t(1) << 40,
+                               nullptr),
+           KDA_ERR_INVALID_ARGUMENT);
+    kda_prologue_t bad_pro = {2, 0, 0, 0.f};
+    expect("bwd_ex bad prologue",
+           kda_chunk_bwd_ex(&d, &bad_pro, P(GOOD), P(GOOD), P(GOOD), (const float*)GOOD, (const float*)GOOD, nullptr,
+                            (const int32_t*)GOOD, nullptr, 0, P(GOOD), nullptr, (void*)GOOD, (void*)GOOD, (void*)GOOD,
+                            (float*)GOOD, (float*)GOOD, nullptr, (void*)GOOD, size_t(1) << 40, nullptr),
+           KDA_ERR_INVALID_ARGUMENT);
+    kda_prologue_t all_pro = {1, 1, 1, -8.f};
+    expect("bwd_ex workspace too small",
+           kda_chunk_bwd_ex(&d, &all_pro, P(GOOD), P(GOOD), P(GOOD), (const float*)GOOD, (const float*)GOOD, nullptr,
+                            (const int32_t*)GOOD, nullptr, 0, P(GOOD), nullptr, (void*)GOOD, (void*)GOOD, (void*)GOOD,
+                            (float*)GOOD, (float*)GOOD, nullptr, (void*)GOOD, 4096, nullptr),
+           KDA_ERR_INVALID_ARGUMENT);
 
     for (int s = -1; s < 6; ++s)
         if (!kda_status_string(s) || !*kda_status_string(s)) ++failures;

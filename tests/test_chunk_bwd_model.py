@@ -23,9 +23,9 @@ def draw(T, dk, dv, seed, la_std=2.0, clip=-8.0, scalar=False):
     return q, k, v, la, beta, S0, dO, dST
 
 
-def oracle_one(q, k, v, la, beta, S0, dO, dST):
+def oracle_one(q, k, v, la, beta, S0, dO, dST, order=0):
     g = kda_oracle_bwd(q[:, None], k[:, None], v[:, None], la[:, None], beta[:, None], S0[None, None],
-                       dO=dO[:, None], dST=dST[None, None])
+                       dO=dO[:, None], dST=dST[None, None], order=order)
     return {n: (x[:, 0] if n != "dS0" else x[0, 0]) for n, x in g.items()}
 
 
@@ -70,3 +70,27 @@ def test_model_scalar_gate():
     got = chunk_backward(*x)
     for n in ref:
         assert rel(got[n], ref[n]) < 1e-10, n
+
+
+@pytest.mark.parametrize("T,dk,dv,seed", [(1, 4, 3, 10), (16, 8, 6, 11), (37, 8, 8, 12), (130, 16, 16, 13),
+                                          (200, 8, 4, 14)])
+def test_model_decay_first_matches_oracle(T, dk, dv, seed):
+    """The decay-first chunk form (gm replaced by g, the dlog_a rule of that
+    order) against the oracle's order-1 gradient."""
+    x = draw(T, dk, dv, seed)
+    ref = oracle_one(*x, order=1)
+    got = chunk_backward(*x, ord1=True)
+    for n in ref:
+        assert rel(got[n], ref[n]) < 1e-10, n
+    # and the erase-first rule on the same inputs is a different gradient
+    assert rel(chunk_backward(*x)["dlog_a"], ref["dlog_a"]) > 1e-3 or T == 1
+
+
+def test_model_decay_first_exact_path():
+    q, k, v, la, beta, S0, dO, dST = draw(80, 8, 8, 15)
+    la = la.copy()
+    la[20:40] = -25.0
+    ref = oracle_one(q, k, v, la, beta, S0, dO, dST, order=1)
+    got = chunk_backward(q, k, v, la, beta, S0, dO, dST, ord1=True)
+    for n in ref:
+        assert rel(got[n], ref[n]) < 1e-9, n

@@ -38,14 +38,15 @@ def gpu_grad(inp, **kw):
     return out
 
 
-def oracle_grad(inp):
+def oracle_grad(inp, order=0):
     c = lambda t: None if t is None else t.detach().cpu()
     return kda_oracle_bwd(c(inp["q"]), c(inp["k"]), c(inp["v"]), c(inp["log_a"]), c(inp["beta"]), S0=c(inp["S0"]),
-                          cu_seqlens=inp["cu_seqlens"].cpu().numpy(), dO=c(inp["dO"]), dST=c(inp["dST"]))
+                          cu_seqlens=inp["cu_seqlens"].cpu().numpy(), dO=c(inp["dO"]), dST=c(inp["dST"]),
+                          order=order)
 
 
-def check(inp, got, tol, what, names=NAMES):
-    ref = oracle_grad(inp)
+def check(inp, got, tol, what, names=NAMES, order=0):
+    ref = oracle_grad(inp, order)
     errs = {n: max_rel_err(got[n], ref[n]) for n in names if got.get(n) is not None}
     log(f"  {what}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
     bad = {n: e for n, e in errs.items() if not e <= tol}
@@ -165,6 +166,50 @@ def test_bwd_saved_states_equal_lengths():
     check(inp, got, TOL[torch.bfloat16], "saved states, equal lengths")
     with pytest.raises(ValueError):
         kda.chunk_bwd(*args, inp["dO"], S0=inp["S0"], num_seqs=2, states=states[:5])
+
+
+@pytest.mark.parametrize("dtype,dk,dv,lengths", [(torch.bfloat16, 128, 128, [130, 64, 37]),
+                                                 (torch.bfloat16, 64, 64, [300, 1, 0, 79]),
+                                                 (torch.bfloat16, 128, 64, [150, 20]),
+                                                 (torch.float32, 32, 32, [150, 64]),
+                                                 (torch.float32, 16, 16, [100, 3])])
+def test_bwd_decay_first(dtype, dk, dv, lengths):
+    """The decay-first order's gradient (the chunk form with each token's decay
+    before its own read) against the oracle's order-1 gradient."""
+    log(f"backward decay-first {dtype} dk={dk} dv={dv} lengths={lengths}")
+    inp = draw("kda_b2_h32_t32768_d128_bf16", 90 + dk + dv, lengths, dtype=dtype, dk=dk, dv=dv)
+    got = gpu_grad(inp, order=kda.ORDER_DECAY_FIRST)
+    check(inp, got, TOL[dtype], f"decay-first {dtype} dk {dk} dv {dv}", order=1)
+    # a different gradient from the erase-first one on the same inputs
+    other = gpu_grad(inp)
+    assert max_rel_err(other["dlog_a"], got["dlog_a"]) > 1e-3
+
+
+@pytest.mark.parametrize("dtype,steep", [(torch.float32, -25.0), (torch.bfloat16, -80.0)])
+def test_bwd_decay_first_steep_mid_sequence(dtype, steep):
+    """Steep decays in the middle of a sequence (sub-chunks past the factor split's
+    range take one exponent per term), decay-first order."""
+    log(f"backward decay-first steep {dtype} {steep}")
+    d = 32 if dtype == torch.float32 else 128
+    inp = draw("kda_b2_h32_t32768_d128_bf16", 97, [120], dtype=dtype, dk=d, dv=d)
+    la = inp["log_a"].clone()
+    la[30:56, :, ::2] = steep
+    inp["log_a"] = la.contiguous()
+    got = gpu_grad(inp, order=kda.ORDER_DECAY_FIRST)
+    check(inp, got, TOL[dtype], f"decay-first steep {dtype}", order=1)
+
+
+def test_bwd_decay_first_saved_states():
+    """From the decay-first forward's kept states: bit for bit the rerun's gradients."""
+    inp = draw("kda_b2_h32_t32768_d128_bf16", 98, [200, 64, 33])
+    _, _, states = kda.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], S0=inp["S0"],
+                                           cu_seqlens=inp["cu_seqlens"], snapshot_every=64,
+                                           order=kda.ORDER_DECAY_FIRST)
+    saved = gpu_grad(inp, states=states, order=kda.ORDER_DECAY_FIRST)
+    rerun = gpu_grad(inp, order=kda.ORDER_DECAY_FIRST)
+    for n in NAMES:
+        assert torch.equal(saved[n], rerun[n]), n
+    check(inp, saved, TOL[torch.bfloat16], "decay-first saved states", order=1)
 
 
 PRO = dict(normalize_k=True, beta_logits=True, log_a_raw=True, log_a_min=-6.0)
