@@ -679,9 +679,13 @@ __global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV, 
 template <typename MT, int DK, int DV>
 struct GradSmem {
     static constexpr int P = 16 / (int)sizeof(MT);
-    static constexpr int LDK = DK + P, LDV = DV + P, L16 = 16 + P, L32 = 32 + P;
+    // dk- and dv-long rows are padded by 32 bytes (288-byte rows at d = 128 bf16):
+    // with 16 bytes of pad, fragment reads of 16 such rows collide in pairs on
+    // gfx950's LDS banks (measured); the gradient kernels run 0.6 % faster
+    static constexpr int PR = 32 / (int)sizeof(MT);
+    static constexpr int LDK = DK + PR, LDV = DV + PR, L16 = 16 + P, L32 = 32 + P;
     static constexpr int DMX = DK > DV ? DK : DV;
-    static constexpr int LMX = (DK > DV ? DK : DV) + P;
+    static constexpr int LMX = (DK > DV ? DK : DV) + PR;
     MT kr[16 * LDK], qr[16 * LDK], vr[16 * LDV], dor[16 * LDV];
     MT mats[7][16 * L16];
     MT SB[DMX * LMX];         // S^T / X^T [j][c], or X / S row-major [c][j]
