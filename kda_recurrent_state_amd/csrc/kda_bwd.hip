@@ -43,13 +43,14 @@
 //
 // Three kernels follow the forward prefill, which leaves the state at every 64th
 // token: kda_bwd_ops (one wavefront per sub-chunk: the C x C products, the solve,
-// the operators of the reverse walk), kda_bwd_scan (one workgroup per (sequence,
-// head, value slice): the reverse walk X <- X_prev, keeping X at every 64-token
-// boundary) and kda_bwd_grad (one workgroup per 64-token chunk: its sub-chunks in
-// reverse, each start state recomputed from the chunk's kept state, all products
-// on matrix cores).
+// the operators of the reverse walk), the reverse walk X <- X_prev keeping X at
+// every 64-token boundary (one workgroup per (sequence, head, value slice):
+// kda_bwd_walk for bf16, kda_bwd_scan for fp32) and kda_bwd_grad (one workgroup
+// per 64-token chunk: its sub-chunks in reverse, each start state recomputed from
+// the chunk's kept state, all products on matrix cores).
 #include "kda_chunk_common.hpp"
 #include "kda_launch.hpp"
+#include "kda_ws.hpp"
 
 namespace kda {
 namespace {
@@ -164,6 +165,17 @@ __device__ __forceinline__ int64_t ceil_blocks_before(const int32_t* cu, int64_t
 //   gam  [DK]       e^{gC} (fp32)
 //   mats 7 x [16][16]: T diag(b), T^T, L, L^T, A0, P1^T, P2^T (row-major)
 //   flag int32: 1 if the sub-chunk needs one exponent per term
+// In bf16 blocks the walk's part (W, M, QK, gam) is stored as the LDS image
+// that kda_bwd_walk reads after a verbatim copy (WL below):
+//   W  rows of DK channels in kperm order (kda_ws.hpp), 16-byte pieces
+//      XOR-swizzled by the row (swz), so that X's accumulator tiles are its
+//      B operand and 16 lanes reading one piece of 16 rows meet no conflict;
+//   M  piece-major: columns 8q..8q+7 of row t at byte 16 (16 q + t);
+//   QK piece-major (piece g of channel row c at byte 16 (g DK + c)) with its
+//      32 columns interleaved: piece g holds Qb^T columns 4g..4g+3, then Kb^T
+//      columns 4g..4g+3, matching the operand [dO; F] that a lane group g
+//      holds as dO rows 4g..4g+3 and F's accumulator rows 4g..4g+3.
+// fp32 blocks keep the plain row-major matrices (kda_bwd_scan).
 template <typename MT, int DK>
 struct OpBlock {
     static constexpr int S = (int)sizeof(MT);
@@ -287,6 +299,7 @@ template <typename MT, int DK>
 __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     const int gmo = p.gmo;
     typedef OpBlock<MT, DK> OB;
+    constexpr bool WL = sizeof(MT) == 2;                      // the walk's operands in its LDS layout
     constexpr int P = 16 / (int)sizeof(MT);
     constexpr int LDK = DK + P, L16 = 16 + P;
     constexpr int ROWB = 16 * LDK * (int)sizeof(MT);          // bytes of 16 padded rows
@@ -339,15 +352,17 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     {
         MT* qk = reinterpret_cast<MT*>(blk + OB::QK);
         for (int pc = lane; pc < DK * 4; pc += 64) {
-            const int c = pc >> 2, s0 = (pc & 3) * 8;
+            const int c = pc >> 2, g = pc & 3, s0 = 8 * g;
             float out[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int s2 = s0 + e;
-                out[e] = s2 < 16 ? to_f32(qr[s2 * LDK + c]) * ex2(G2[(s2 + 1) * G2L + c])
-                                 : to_f32(kr[(s2 - 16) * LDK + c]) * ex2(G2[(s2 - 16 + gmo) * G2L + c]);
+                // WL: piece g holds the q terms of tokens 4g..4g+3, then their k terms
+                const bool qt = WL ? e < 4 : s0 + e < 16;
+                const int s2 = WL ? 4 * g + (e & 3) : (s0 + e) & 15;
+                out[e] = qt ? to_f32(qr[s2 * LDK + c]) * ex2(G2[(s2 + 1) * G2L + c])
+                            : to_f32(kr[s2 * LDK + c]) * ex2(G2[(s2 + gmo) * G2L + c]);
             }
-            store8<MT>(qk + c * 32 + s0, out);
+            store8<MT>(qk + (WL ? 8 * (g * DK + c) : c * 32 + s0), out);
         }
         float* gam = reinterpret_cast<float*>(blk + OB::GAM);
         for (int c = lane; c < DK; c += 64) gam[c] = ex2(G2[SC * G2L + c]);
@@ -493,15 +508,28 @@ __global__ __launch_bounds__(64) void kda_bwd_ops_kernel(BwdParams p) {
     }
 
     // W (m = c, n = t): W^T[c][t] = sum_s Kcc^T[c][s] (b_t T[s][t]); natural store gives W[t][c]
+    // (WL: lane row t = lane % 16, channels 16 cb + 4 g + r at positions
+    // kperm(...) = 32 (cb / 2) + 8 g + 4 (cb % 2) + r, four consecutive ones)
     MT* Wg = reinterpret_cast<MT*>(blk + OB::W);
     for (int cb = 0; cb < DK / 16; ++cb) {
         f32x4 a = mma16(KCT + (cb * 16 + (lane & 15)) * 16, bTT + (lane & 15) * L16, zero4(), lane);
-        store_nat<MT>(Wg + cb * 16, DK, a, lane);
+        if constexpr (WL) {
+            const int p0 = 32 * (cb >> 1) + 8 * (lane >> 4) + 4 * (cb & 1);
+            store4<MT>(reinterpret_cast<MT*>(blk + OB::W + swz_elem<2 * DK>(lane & 15, p0)), a);
+        } else {
+            store_nat<MT>(Wg + cb * 16, DK, a, lane);
+        }
     }
     // M (m = i, n = t): M^T[i][t] = sum_s P1[i][s] (b_t T[s][t]); natural store gives M[t][i]
+    // (WL: M[t][4g .. 4g+3] is half g % 2 of piece g / 2 of row t)
     {
         f32x4 a = mma16(P1rm + (lane & 15) * L16, bTT + (lane & 15) * L16, zero4(), lane);
-        store_nat<MT>(reinterpret_cast<MT*>(blk + OB::M), 16, a, lane);
+        if constexpr (WL) {
+            const int g = lane >> 4;
+            store4<MT>(reinterpret_cast<MT*>(blk + OB::M + 16 * (16 * (g >> 1) + (lane & 15)) + 8 * (g & 1)), a);
+        } else {
+            store_nat<MT>(reinterpret_cast<MT*>(blk + OB::M), 16, a, lane);
+        }
     }
 }
 
@@ -672,6 +700,262 @@ __global__ __launch_bounds__(256) void kda_bwd_scan_kernel(BwdParams p, int DV, 
                 const int cb = w + 4 * a;
                 if (cb < NCB) store_state_tile(p.dS0 + st_off + (int64_t)cb * 16 * DV + jb * 16, DV, lane, X[a][jb]);
             }
+    }
+}
+
+// ==================================================================== walk
+// The reverse walk for bf16 blocks, built like the prefill's state pass.  Each
+// compute wavefront owns one 16-column block of X for all DK channel rows, in
+// matrix-core accumulators for the whole walk, and needs no other wavefront's
+// data: X's accumulator tiles become the B operand of W X by a register move
+// (W's channels are stored in kperm order), and F's accumulator tile with the
+// step's dO rows becomes the B operand of the update (QK's columns are
+// interleaved to match).  Per step, with slot B holding the step's operators:
+//   F = -(M dO + W X)       (M dO as a 32-deep product whose upper half is zero)
+//   X <- Diag(gamma) X + QK [dO; F]
+// Two copy wavefronts bring each step's operators (the walk's part of the
+// block, stored by kda_bwd_ops as the LDS image read here) and dO rows into
+// one of NBUF LDS slots with the LDS-DMA form of the global load, AHEAD steps
+// ahead, and touch the block TOUCH steps further into L2 (the value slices of
+// a head share it there).  One barrier per step, between F and the update,
+// hands the slots over: after it the next step's operands are read while the
+// update runs.  The dO rows of a slot sit in the order 4 (t % 4) + t / 4, so
+// that the four rows 4g..4g+3 a lane group reads fall on distinct banks; rows
+// past a sub-chunk's end repeat its last row (they meet zero operator rows and
+// columns).  X at each 64-token chunk end is written by the compute
+// wavefronts into an LDS staging buffer and stored by the copy wavefronts
+// after the step's barrier, so that the compute wavefronts issue no global
+// memory operation in the walk.
+template <int DK>
+struct WalkCfg {
+    typedef OpBlock<bf16, DK> OB;
+    static constexpr int DVS = 32, NW = DVS / 16, NL = 2;  // compute and copy wavefronts
+    static constexpr int NT = 64 * (NW + NL), LT = 64 * NL;
+    static constexpr int NPB = OB::WALK / 16;            // 16-byte pieces of the operators
+    static constexpr int NPV = 16 * DVS * 2 / 16;        // and of the dO rows
+    static constexpr int NPS = NPB + NPV;
+    static constexpr int ROUNDS = (NPS + LT - 1) / LT;   // copy instructions per copy wavefront and step
+    static constexpr int TOFF = ROUNDS * LT * 16;        // where the touches land (never read)
+    static constexpr int SLOT = TOFF + 256 * NL;
+    static constexpr int NBUF = 6, AHEAD = NBUF - 1, TOUCH = 2;
+    // X at a 64-token chunk end: two staging buffers of DK rows x DVS fp32
+    // (rows XP floats apart, so that the quad-transposed writes of 16 lanes
+    // meet no conflict), stored to global memory by the copy wavefronts
+    static constexpr int XP = DVS + 16, STG = NBUF * SLOT, XB = DK * XP * 4;
+    static constexpr int XR = DK * (DVS / 4) / LT;       // 16-byte stores per copy lane
+    static constexpr int LDS = STG + 2 * XB;
+    static_assert(OB::WALK % 16 == 0 && DVS / 8 == 4, "pieces");
+    static_assert((AHEAD - 1) * (ROUNDS + 1) < 64, "vmcnt range");
+    static_assert(XR * LT == DK * (DVS / 4), "staging rounds");
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int DK>
+__global__ void __launch_bounds__(WalkCfg<DK>::NT, 1) kda_bwd_walk_kernel(BwdParams p, int DV, int nitems) {
+    typedef WalkCfg<DK> G;
+    typedef OpBlock<bf16, DK> OB;
+    constexpr int NR = DK / 16, NKS = DK / 32, ROUNDS = G::ROUNDS, LT = G::LT;
+    __shared__ alignas(16) uint8_t lds[G::LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    // the value slices of one (sequence, head) on one XCD (item = (bid % 8) per + bid / 8)
+    const int per = (nitems + 7) / 8;
+    const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (item >= nitems) return;
+    const int nsl = DV / G::DVS;
+    const int64_t unit = item / nsl;
+    const int slice = item % nsl;
+    const int n = (int)(unit / p.H), h = (int)(unit % p.H);
+    const SeqSpan sq = seq_span(p.cu, p.eq_len, n);
+    const int nsub = ceil_div(sq.len, SC), nch = ceil_div(sq.len, CHB);
+    const int j0 = slice * G::DVS;
+    const int64_t sbase = ceil_blocks_before(p.cu, p.eq_len, n, SC) * p.H + (int64_t)h * nsub;
+    const int64_t cbase = ceil_blocks_before(p.cu, p.eq_len, n, CHB) * p.H + (int64_t)h * nch;
+    const bf16* __restrict__ dO = static_cast<const bf16*>(p.dO);
+    // walk steps that end a 64-token chunk keep X (the derivative at that end),
+    // staged in buffer (chunk index) % 2: consecutive kept chunks alternate
+    auto keeps = [&](int jj) {
+        const int s = nsub - 1 - jj;
+        return s % (CHB / SC) == CHB / SC - 1 || s == nsub - 1;
+    };
+    auto staging = [&](int jj) { return lds + G::STG + ((nsub - 1 - jj) / (CHB / SC) & 1) * G::XB; };
+
+    if (wv >= G::NW) {
+        // ---- copy wavefronts: walk step jj is sub-chunk nsub - 1 - jj.  Step
+        // jj + AHEAD is copied during step jj and step jj + AHEAD + TOUCH touched;
+        // before the barrier of step jj the copies of step jj + 1 are waited for
+        // (younger: AHEAD - 1 steps of copies and touches; loads complete in order).
+        const int lt = tid - 64 * G::NW, lw = wv - G::NW;
+        auto copy = [&](int jj, int sl) {
+            const int s = nsub - 1 - jj;
+            const uint8_t* blk = p.ops + (sbase + s) * OB::BYTES;
+            const int64_t t0 = sq.t0 + (int64_t)s * SC;
+            const int nrow = min(SC, sq.len - s * SC);
+            uint8_t* slot = lds + sl * G::SLOT + lw * 1024;
+#pragma unroll
+            for (int r = 0; r < ROUNDS; ++r) {
+                const uint8_t* src;
+                if ((r + 1) * LT <= G::NPB) {
+                    src = blk + r * LT * 16 + 16 * lt;
+                } else {
+                    const int pc = min(r * LT + lt, G::NPS - 1);
+                    const int x = max(pc - G::NPB, 0), rp = x >> 2, u = x & 3;
+                    const int t = 4 * (rp & 3) + (rp >> 2);  // token held by row position rp
+                    const int64_t row = (t0 + min(t, nrow - 1)) * p.H + h;
+                    const uint8_t* dsrc = reinterpret_cast<const uint8_t*>(dO + row * DV + j0 + 8 * u);
+                    src = pc < G::NPB ? blk + 16 * pc : dsrc;
+                }
+                __builtin_amdgcn_global_load_lds(src, slot + r * LT * 16, 16, 0, 0);
+            }
+        };
+        // one dword per 128-byte line of the walk's operators, slice s taking
+        // lines s, s + nsl, ...; landing past the slot's pieces
+        auto touch = [&](int jj) {
+            constexpr int LINES = (OB::WALK + 127) / 128;
+            const int nb = (LINES - slice + nsl - 1) / nsl;
+            const int line = min(lt, nb - 1) * nsl + slice;
+            __builtin_amdgcn_global_load_lds(p.ops + (sbase + nsub - 1 - jj) * OB::BYTES + 128 * line,
+                                             lds + lw * G::SLOT + G::TOFF + 256 * lw, 4, 0, 0);
+        };
+        // X staged by the compute wavefronts at walk step jj (published by that
+        // step's barrier) goes to its 64-token chunk's row of xbuf
+        auto store_x = [&](int jj) {
+            const uint8_t* sx = staging(jj);
+            float* dst = p.xbuf + (cbase + (nsub - 1 - jj) / (CHB / SC)) * (int64_t)DK * DV + j0;
+#pragma unroll
+            for (int r = 0; r < G::XR; ++r) {
+                const int q = r * LT + lt, row = q / (G::DVS / 4), cp = q % (G::DVS / 4);
+                const i32x4 x = *reinterpret_cast<const i32x4*>(sx + (row * G::XP + 4 * cp) * 4);
+                *reinterpret_cast<i32x4*>(dst + (int64_t)row * DV + 4 * cp) = x;
+            }
+        };
+        if (nsub > 0) {
+#pragma unroll
+            for (int c = 0; c < G::AHEAD; ++c) {
+                copy(min(c, nsub - 1), c);
+                touch(min(c + G::TOUCH, nsub - 1));
+            }
+        }
+        // the vmcnt waits count copies and touches only: stores issued in between
+        // are older than the copies waited for or among the younger operations
+        slot_barrier<(G::AHEAD - 1) * (ROUNDS + 1)>();
+        for (int jj = 0; jj < nsub; ++jj) {
+            if (jj > 0 && keeps(jj - 1)) store_x(jj - 1);
+            copy(min(jj + G::AHEAD, nsub - 1), (jj + G::AHEAD) % G::NBUF);
+            touch(min(jj + G::AHEAD + G::TOUCH, nsub - 1));
+            slot_barrier<(G::AHEAD - 1) * (ROUNDS + 1)>();
+        }
+        if (nsub > 0 && keeps(nsub - 1)) store_x(nsub - 1);
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): no copy outlives the workgroup
+        return;
+    }
+
+    // ---- X: columns jw .. jw + 15 of the slice, tile r rows 16 r + 4 lg + i
+    const int jw = j0 + 16 * wv;
+    const int64_t xo = unit * (int64_t)DK * DV + jw;
+    f32x4 X[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+        X[r] = p.dST ? load_state_tile(p.dST + xo + (int64_t)16 * r * DV, DV, lane) : zero4();
+    bf16x8 xfr[NKS];
+    auto make_xfr = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xfr[ks][i] = (bf16)X[2 * ks][i];
+                xfr[ks][4 + i] = (bf16)X[2 * ks + 1][i];
+            }
+    };
+    make_xfr();
+
+    // lane parts of the operand addresses in a slot
+    uint32_t oW[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) oW[ks] = OB::W + swz<2 * DK>(lr, 4 * ks + lg);
+    const uint32_t oM = OB::M + 16 * (16 * (lg >> 1) + lr) + 8 * (lg & 1);
+    const uint32_t oQ = OB::QK + 16 * (lg * DK + lr);   // + 256 r: channel rows 16 r ..
+    const uint32_t oG = OB::GAM + 16 * lg;              // + 64 r
+    const uint32_t oD = G::NPB * 16 + 64 * lg + 2 * (16 * wv + lr);  // + 256 i: dO row 4 lg + i
+
+    // A step's operands, read right after the barrier that publishes its slot
+    // (while the previous step's update runs): W's fragments, M's half row and
+    // the four dO values of this lane, and the update's QK fragments and gamma.
+    // The loop is unrolled by two so that the QK / gamma registers of the step
+    // and of the next one are fixed sets.
+    bf16x8 wf[NKS];
+    bf16x4 mh;
+    bf16 dv4[4];
+    bf16x8 qf[2][NR];
+    f32x4 gm[2][NR];
+    auto read_ops = [&](const uint8_t* B, bf16x8 (&q)[NR], f32x4 (&g)[NR]) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) wf[ks] = *reinterpret_cast<const bf16x8*>(B + oW[ks]);
+        mh = *reinterpret_cast<const bf16x4*>(B + oM);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dv4[i] = *reinterpret_cast<const bf16*>(B + oD + 256 * i);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            q[r] = *reinterpret_cast<const bf16x8*>(B + oQ + 256 * r);
+            g[r] = *reinterpret_cast<const f32x4*>(B + oG + 64 * r);
+        }
+    };
+
+    // step jj with its update operands in (q, g); the next step's go to (qn, gn)
+    auto step = [&](int jj, bf16x8 (&q)[NR], f32x4 (&g)[NR], bf16x8 (&qn)[NR], f32x4 (&gn)[NR]) {
+        // derivative at the end of a 64-token chunk: staged rows, each lane four
+        // consecutive columns of one row (quad transpose), for the copy wavefronts
+        if (keeps(jj)) {
+            uint8_t* sx = staging(jj) + ((4 * lg + (lane & 3)) * G::XP + 16 * wv + 4 * ((lane & 15) >> 2)) * 4;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                *reinterpret_cast<i32x4*>(sx + 16 * r * G::XP * 4) =
+                    quad_transpose(__builtin_bit_cast(i32x4, X[r]), lane);
+        }
+        // F = -(M dO + W X): rows t = 4 lg + i of this lane, column jw + lr, as two
+        // independent accumulation chains
+        bf16x8 ma = {}, db = {};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ma[i] = mh[i];
+            db[i] = dv4[i];
+        }
+        constexpr int KH = (NKS + 1) / 2;
+        f32x4 fa = Mma<bf16>::mma(ma, db, zero4()), fb = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KH; ++ks) fa = Mma<bf16>::mma(wf[ks], xfr[ks], fa);
+#pragma unroll
+        for (int ks = KH; ks < NKS; ++ks) fb = Mma<bf16>::mma(wf[ks], xfr[ks], fb);
+        const f32x4 f = fa + fb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) db[4 + i] = (bf16)(-f[i]);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // this step's LDS reads are done: the barrier hands its slot to the copy
+        // wavefronts and publishes step jj + 1 (after the last step: a harmless
+        // read of a stale slot)
+        slot_barrier<63>();
+        read_ops(lds + ((jj + 1) % G::NBUF) * G::SLOT, qn, gn);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // X <- Diag(gamma) X + QK [dO; F]
+#pragma unroll
+        for (int r = 0; r < NR; ++r) X[r] = Mma<bf16>::mma(q[r], db, X[r] * g[r]);
+        __builtin_amdgcn_sched_barrier(0);
+        make_xfr();
+    };
+
+    slot_barrier<63>();
+    if (nsub > 0) read_ops(lds, qf[0], gm[0]);
+    for (int jj = 0; jj < nsub; jj += 2) {
+        step(jj, qf[0], gm[0], qf[1], gm[1]);
+        if (jj + 1 < nsub) step(jj + 1, qf[1], gm[1], qf[0], gm[0]);
+    }
+    if (p.dS0) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) store_state_tile(p.dS0 + xo + (int64_t)16 * r * DV, DV, lane, X[r]);
     }
 }
 
@@ -1363,6 +1647,14 @@ hipError_t scan_dispatch(const BwdParams& p, int64_t units, int dv, hipStream_t 
     hipLaunchKernelGGL((kda_bwd_scan_kernel<MT, DK, DVS>), dim3((unsigned)nblk), dim3(256), 0, st, p, dv, (int)nitems);
     return hipGetLastError();
 }
+template <int DK>
+hipError_t walk_dispatch(const BwdParams& p, int64_t units, int dv, hipStream_t st) {
+    const int64_t nitems = (int64_t)(dv / WalkCfg<DK>::DVS) * units;
+    const int64_t nblk = (nitems + 7) / 8 * 8;
+    hipLaunchKernelGGL((kda_bwd_walk_kernel<DK>), dim3((unsigned)nblk), dim3(WalkCfg<DK>::NT), 0, st, p, dv,
+                       (int)nitems);
+    return hipGetLastError();
+}
 template <typename MT, int DK, int DV>
 hipError_t grad_dispatch(const BwdParams& p, int64_t units, int nch_max, hipStream_t st) {
     const size_t sm = sizeof(GradSmem<MT, DK, DV>);
@@ -1380,8 +1672,14 @@ hipError_t run_all(const BwdLaunch& a, const BwdParams& p, hipStream_t st) {
     hipError_t e = hipSuccess;
     if (a.nsub_max > 0) e = ops_dispatch<MT, DK>(p, a.units, a.nsub_max, st);
     if (e != hipSuccess) return e;
-    constexpr int DVS = DV >= 32 ? 32 : DV;
-    e = scan_dispatch<MT, DK, DVS>(p, a.units, DV, st);  // also writes dS0 of empty sequences
+    // the reverse walk (also writes dS0 of empty sequences)
+    if constexpr (sizeof(MT) == 2) {
+        static_assert(DV % WalkCfg<DK>::DVS == 0, "bf16 value widths are multiples of 32");
+        e = walk_dispatch<DK>(p, a.units, DV, st);
+    } else {
+        constexpr int DVS = DV >= 32 ? 32 : DV;
+        e = scan_dispatch<MT, DK, DVS>(p, a.units, DV, st);
+    }
     if (e != hipSuccess || a.nch_max == 0) return e;
     return grad_dispatch<MT, DK, DV>(p, a.units, a.nch_max, st);
 }

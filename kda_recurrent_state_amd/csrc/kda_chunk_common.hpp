@@ -297,4 +297,19 @@ __device__ __forceinline__ void block_inverse(const float* A, const float* beta,
     }
 }
 
+// Ends a step of a walk fed through LDS slots: waits until at most N
+// vector-memory operations of this wavefront are outstanding and all its LDS
+// reads have returned, then joins the workgroup barrier.  A release fence is
+// not used here: on LDS it would also wait for the copies still in flight into
+// the other slots.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void slot_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // vmcnt(N) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace kda

@@ -103,20 +103,6 @@ __device__ __forceinline__ void vpiece_source(int q, int& t, int& u) {
     u = (q % VPR) ^ ((t ^ (t >> 2)) & (VPR - 1));
 }
 
-// Ends a chunk: waits until at most N vector-memory operations of this
-// wavefront are outstanding and all its LDS reads have returned, then joins the
-// workgroup barrier.  A release fence is not used here: on LDS it would also
-// wait for the copies still in flight into the other slots.  The empty asm
-// statements keep the compiler from moving memory accesses across the barrier.
-template <int N>
-__device__ __forceinline__ void slot_barrier() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // vmcnt(N) lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // SNAP: the call asks for state snapshots (a separate instantiation, so that
 // the plain walk carries no snapshot code).  ORD1: decay-first blocks (no KT V
 // term in the state update).
