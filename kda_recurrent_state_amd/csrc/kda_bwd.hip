@@ -994,10 +994,13 @@ struct GradSmem {
 // factor split, one exponent per term: out[t][c] = sum_i M[t][i] y_ic e^{+-(h_tc - h'_ic)}
 // for this lane's rows t = 4 g4 + r and channel c.  Masked-out pairs hold 0;
 // clamping their exponents at 0 keeps them finite.
+// (returned by value: the out-of-line call then keeps the caller's products in
+// registers instead of stack slots that every step would store and reload)
+struct ExactTerms { f32x4 q, g, v, y; };
 template <typename MT, int DK, typename SM>
-__device__ __attribute__((noinline)) void exact_terms(const SM& sm, int c, int g4, int gmo, f32x4& mq, f32x4& mg,
-                                                      f32x4& mv, f32x4& my) {
+__device__ __attribute__((noinline)) ExactTerms exact_terms(const SM& sm, int c, int g4, int gmo) {
     constexpr int LDK = SM::LDK, L32 = SM::L32;
+    f32x4 mq, mg, mv, my;
     for (int r = 0; r < 4; ++r) {
         const int t = 4 * g4 + r;
         float aq = 0.f, ag = 0.f, av = 0.f, ay = 0.f;
@@ -1012,6 +1015,7 @@ __device__ __attribute__((noinline)) void exact_terms(const SM& sm, int c, int g
         }
         mq[r] = aq; mg[r] = ag; mv[r] = av; my[r] = ay;
     }
+    return ExactTerms{mq, mg, mv, my};
 }
 
 template <typename MT, int DK, int DV>
@@ -1097,31 +1101,55 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
         if (pc < B5) return Piece{5, (pc - B4) / PM, ((pc - B4) % PM) * PER};
         return Piece{6, 0, 0};
     };
+    // A thread's pieces are the same at every step, so they are decoded once and
+    // packed, 16 bits per walk direction (kind << 11 | row << 6 | offset / 4), and
+    // unpacked where used behind an empty asm statement: the compiler then keeps
+    // one register per piece, and every address is a wave-uniform base of the step
+    // plus a small lane offset.  (Addresses hoisted per piece and tensor had spilled,
+    // and each reload waited for every load issued before it.)
+    uint32_t pdesc[NPF];
+#pragma unroll
+    for (int a = 0; a < NPF; ++a) {
+        const Piece f = decode(tid + NT * a, false), b = decode(tid + NT * a, true);
+        pdesc[a] = (uint32_t)(f.kind << 11 | f.i << 6 | f.e >> 2) | (uint32_t)(b.kind << 11 | b.i << 6 | b.e >> 2) << 16;
+    }
+    auto piece_of = [&](int a, bool bwd) -> Piece {
+        uint32_t d = pdesc[a];
+        asm volatile("" : "+v"(d));
+        d = bwd ? d >> 16 : d & 0xFFFFu;
+        return Piece{(int)(d >> 11), (int)((d >> 6) & 31), (int)((d & 63) << 2)};
+    };
     auto issue = [&](int s2, bool bwd) {
         const int64_t t0 = sq.t0 + (int64_t)jc * CHB + s2 * SC;
         const int nrow = min(SC, clen - s2 * SC);
+        const int64_t rb = t0 * p.H + h;  // the step's first row (wave-uniform)
+        const MT* kb = Kg + rb * DK;
+        const MT* vb = Vg + rb * DV;
+        const MT* qb = Qg + rb * DK;
+        const MT* ob = Og + rb * DV;
+        const float* lb = p.log_a + rb * (p.scalar ? 1 : DK);
         const MT* mats = reinterpret_cast<const MT*>(p.ops + (sbase + s2) * OB::BYTES + OB::MATS);
 #pragma unroll
         for (int a = 0; a < NPF; ++a) {
-            const Piece pc = decode(tid + NT * a, bwd);
+            const Piece pc = piece_of(a, bwd);
             VT x = {};
-            const int64_t row = (t0 + pc.i) * p.H + h;
+            const int ro = pc.i * p.H;  // the piece's row, counted from the step's first
             if (pc.kind <= 4 && pc.i >= nrow) {
             } else if (pc.kind == 0) {
-                x = *reinterpret_cast<const VT*>(Kg + row * DK + pc.e);
+                x = *reinterpret_cast<const VT*>(kb + (ro * DK + pc.e));
             } else if (pc.kind == 1) {
-                x = *reinterpret_cast<const VT*>(Vg + row * DV + pc.e);
+                x = *reinterpret_cast<const VT*>(vb + (ro * DV + pc.e));
             } else if (pc.kind == 2) {
-                x = *reinterpret_cast<const VT*>(Qg + row * DK + pc.e);
+                x = *reinterpret_cast<const VT*>(qb + (ro * DK + pc.e));
             } else if (pc.kind == 3) {
-                x = *reinterpret_cast<const VT*>(Og + row * DV + pc.e);
+                x = *reinterpret_cast<const VT*>(ob + (ro * DV + pc.e));
             } else if (pc.kind == 4) {
                 f32x4 d;
                 if (p.scalar) {
-                    const float a1 = p.log_a[row];
+                    const float a1 = lb[ro];
                     d = f32x4{a1, a1, a1, a1};
                 } else {
-                    d = *reinterpret_cast<const f32x4*>(p.log_a + row * DK + pc.e);
+                    d = *reinterpret_cast<const f32x4*>(lb + (ro * DK + pc.e));
                 }
                 x = __builtin_bit_cast(VT, d);
             } else if (pc.kind == 5) {
@@ -1135,7 +1163,7 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
     auto commit = [&](bool bwd) {
 #pragma unroll
         for (int a = 0; a < NPF; ++a) {
-            const Piece pc = decode(tid + NT * a, bwd);
+            const Piece pc = piece_of(a, bwd);
             if (pc.kind == 0) *reinterpret_cast<VT*>(sm.kr + pc.i * LDK + pc.e) = pf[a];
             else if (pc.kind == 1) *reinterpret_cast<VT*>(sm.vr + pc.i * LDV + pc.e) = pf[a];
             else if (pc.kind == 2) *reinterpret_cast<VT*>(sm.qr + pc.i * LDK + pc.e) = pf[a];
@@ -1542,7 +1570,8 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 mv[a] = mmak<MT, 32>(sm.MV + r16 * L32, sm.CT + c * L32, zero4(), lane);
                 my[a] = mmak<MT, 32>(sm.MY + r16 * L32, sm.CT + c * L32, zero4(), lane);
             } else {
-                exact_terms<MT, DK>(sm, c, g4, gmo, mq[a], mg[a], mv[a], my[a]);
+                const ExactTerms x = exact_terms<MT, DK>(sm, c, g4, gmo);
+                mq[a] = x.q; mg[a] = x.g; mv[a] = x.v; my[a] = x.y;
             }
             const float gc = sm.G2[SC * SM::G2L + c], m2 = 0.5f * gc;
             float av[4], au[4];
