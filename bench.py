@@ -585,7 +585,7 @@ def main():
                 "pct_bf16_peak": 100.0 * Fb / tb / 1e12 / PEAK_BF16_TFLOPS,
                 "workspace_MiB": round(wsbb / 2**20, 1),
                 "kernels": "prefill rerun (kda_prep2_kernel + kda_scan_kernel, states every 64 tokens) + "
-                           "kda_bwd_ops_kernel + kda_bwd_scan_kernel + kda_bwd_grad_kernel",
+                           "kda_bwd_ops_kernel + kda_bwd_walk_kernel (bf16; kda_bwd_scan_kernel for fp32) + kda_bwd_grad_kernel",
                 "saved_states": {
                     "ms_per_step": tsv * 1e3, "tokens_per_s": tokens / tsv,
                     "algorithmic_GBps": Bb / tsv / 1e9, "frac_hbm": Bb / tsv / 1e9 / PEAK_HBM_GBS,
