@@ -1201,6 +1201,41 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
     // that step no longer updates) and it is brought into tile order after the walk,
     // as load_state_tile does.
     f32x4 X[CBW][NJB];
+    // Elementwise fills of the step's operands.  A thread takes four consecutive
+    // channels (or value columns) of one token row, so that its LDS reads are
+    // vectors; the transposed fills (dst[c][off + i], rows L32 apart) give 16 lanes
+    // 16 consecutive rows i of one column, so that their 2- or 4-byte writes meet
+    // no bank conflict either.
+    typedef typename Vec4<MT>::type VX4;
+    auto rd4 = [&](const MT* src) { return Vec4<MT>::to_f32(*reinterpret_cast<const VX4*>(src)); };
+    auto gsum = [&](int row, int c0) { return *reinterpret_cast<const f32x4*>(sm.G2 + row * SM::G2L + c0); };
+    auto ex2v = [](f32x4 x) { return f32x4{ex2(x[0]), ex2(x[1]), ex2(x[2]), ex2(x[3])}; };
+    // row-major: f(t, c0) for t < 16, c0 = 0, 4, .. < N
+    auto fill_rows = [&](int N, auto&& f) {
+        for (int x = tid; x < 4 * N; x += NT) f(x / (N / 4), 4 * (x % (N / 4)));
+    };
+    // transposed: dst[(c0 + u) L32 + off + i] = f(i, c0)[u], and with a second part at off2
+    auto fill_cols = [&](MT* dst, int N, int off, auto&& f) {
+        for (int x = tid; x < 4 * N; x += NT) {
+            const int i = x & 15, c0 = 4 * (x >> 4);
+            const f32x4 v = f(i, c0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dst[(c0 + u) * L32 + off + i] = from_f32<MT>(v[u]);
+        }
+    };
+    auto fill_cols2 = [&](MT* dst, int N, auto&& f) {
+        for (int x = tid; x < 4 * N; x += NT) {
+            const int i = x & 15, c0 = 4 * (x >> 4);
+            f32x4 a, b;
+            f(i, c0, a, b);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                dst[(c0 + u) * L32 + i] = from_f32<MT>(a[u]);
+                dst[(c0 + u) * L32 + 16 + i] = from_f32<MT>(b[u]);
+            }
+        }
+    };
+
     // ================= forward walk: start state, E and Y of every sub-chunk
     {
         f32x4 S[CBW][NJB];
@@ -1240,21 +1275,16 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             prefix_decay();
             lds_barrier();
             // ---- Kb rows, (bV)^T, [Kcc^T | Ktc^T]
-            for (int x = tid; x < 16 * DK; x += NT) {
-                const int t = x / DK, c = x % DK;
-                sm.GA[t * LDK + c] = from_f32<MT>(to_f32(sm.kr[t * LDK + c]) * ex2(sm.G2[(t + gmo) * SM::G2L + c]));
-            }
-            for (int x = tid; x < 16 * DV; x += NT) {
-                const int i = x % 16, j = x / 16;
-                sm.EBVT[j * L32 + 16 + i] = from_f32<MT>(sm.bt[i] * to_f32(sm.vr[i * LDV + j]));
-            }
+            fill_rows(DK, [&](int t, int c0) {
+                store4<MT>(sm.GA + t * LDK + c0, rd4(sm.kr + t * LDK + c0) * ex2v(gsum(t + gmo, c0)));
+            });
+            fill_cols(sm.EBVT, DV, 16, [&](int i, int j0) { return sm.bt[i] * rd4(sm.vr + i * LDV + j0); });
             if constexpr (!last) {
-                for (int x = tid; x < 16 * DK; x += NT) {
-                    const int s2 = x % 16, c = x / 16;
-                    const float kv = to_f32(sm.kr[s2 * LDK + c]), gc = sm.G2[SC * SM::G2L + c];
-                    sm.CT[c * L32 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[(s2 + gmo) * SM::G2L + c]));
-                    sm.CT[c * L32 + 16 + s2] = from_f32<MT>(kv * ex2(gc - sm.G2[(s2 + 1) * SM::G2L + c]));
-                }
+                fill_cols2(sm.CT, DK, [&](int i, int c0, f32x4& a, f32x4& b) {
+                    const f32x4 kv = rd4(sm.kr + i * LDK + c0), gc = gsum(SC, c0);
+                    a = kv * ex2v(gc - gsum(i + gmo, c0));
+                    b = kv * ex2v(gc - gsum(i + 1, c0));
+                });
             }
             lds_barrier();
             // ---- Y0 = Kb S + L bV   (m = t, n = j)
@@ -1366,21 +1396,16 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 const int cb = w + GW * a;
                 if (cb < NCB) store_nat<MT>(sm.SB + jb * 16 * LDK + cb * 16, LDK, X[a][jb], lane);
             }
-        for (int x = tid; x < 16 * DV; x += NT) {
-            const int i = x % 16, j = x / 16;
-            sm.DFT[j * L32 + i] = sm.dor[i * LDV + j];
-        }
-        for (int x = tid; x < 16 * DK; x += NT) {
-            const int t = x / DK, c = x % DK;
-            const float kv = to_f32(sm.kr[t * LDK + c]), gc = sm.G2[SC * SM::G2L + c];
-            sm.GA[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[(t + gmo) * SM::G2L + c]));
-            sm.GB[t * LDK + c] = from_f32<MT>(kv * ex2(gc - sm.G2[(t + 1) * SM::G2L + c]));
-        }
-        for (int x = tid; x < 16 * DK; x += NT) {
-            const int s2 = x % 16, c = x / 16;
-            sm.CT[c * L32 + s2] = from_f32<MT>(to_f32(sm.qr[s2 * LDK + c]) * ex2(sm.G2[(s2 + 1) * SM::G2L + c]));
-            sm.CT[c * L32 + 16 + s2] = from_f32<MT>(to_f32(sm.kr[s2 * LDK + c]) * ex2(sm.G2[(s2 + gmo) * SM::G2L + c]));
-        }
+        fill_cols(sm.DFT, DV, 0, [&](int i, int j0) { return rd4(sm.dor + i * LDV + j0); });
+        fill_rows(DK, [&](int t, int c0) {
+            const f32x4 kv = rd4(sm.kr + t * LDK + c0), gc = gsum(SC, c0);
+            store4<MT>(sm.GA + t * LDK + c0, kv * ex2v(gc - gsum(t + gmo, c0)));
+            store4<MT>(sm.GB + t * LDK + c0, kv * ex2v(gc - gsum(t + 1, c0)));
+        });
+        fill_cols2(sm.CT, DK, [&](int i, int c0, f32x4& a, f32x4& b) {
+            a = rd4(sm.qr + i * LDK + c0) * ex2v(gsum(i + 1, c0));
+            b = rd4(sm.kr + i * LDK + c0) * ex2v(gsum(i + gmo, c0));
+        });
         lds_barrier();
         // ---- dE = Kcc X + P1^T dO  (m = t, n = j) -> dE^T
 #pragma unroll
@@ -1526,12 +1551,11 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 const int cb = w + GW * a;
                 if (cb < NCB) store_rm<MT>(sm.SB + cb * 16 * LDV + jb * 16, LDV, Vec4<MT>::to_f32(Sk[a][jb]), lane);
             }
-        for (int x = tid; x < 16 * DK; x += NT) {
-            const int i = x % 16, c = x / 16;
-            const float kv = to_f32(sm.kr[i * LDK + c]), m2 = 0.5f * sm.G2[SC * SM::G2L + c];
-            sm.CT[c * L32 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[(i + gmo) * SM::G2L + c]));
-            sm.CT[c * L32 + 16 + i] = from_f32<MT>(kv * ex2(m2 - sm.G2[(i + 1) * SM::G2L + c]));
-        }
+        fill_cols2(sm.CT, DK, [&](int i, int c0, f32x4& a, f32x4& b) {
+            const f32x4 kv = rd4(sm.kr + i * LDK + c0), m2 = 0.5f * gsum(SC, c0);
+            a = kv * ex2v(m2 - gsum(i + gmo, c0));
+            b = kv * ex2v(m2 - gsum(i + 1, c0));
+        });
         lds_barrier();
         const bool exact = sm.exact != 0;
         f32x4 mq[CBW], mg[CBW], mv[CBW], my[CBW];
@@ -1549,12 +1573,11 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             }
         }
         lds_barrier();
-        for (int x = tid; x < 16 * DK; x += NT) {
-            const int i = x % 16, c = x / 16;
-            const float m2 = 0.5f * sm.G2[SC * SM::G2L + c];
-            sm.CT[c * L32 + i] = from_f32<MT>(to_f32(sm.qr[i * LDK + c]) * ex2(sm.G2[(i + 1) * SM::G2L + c] - m2));
-            sm.CT[c * L32 + 16 + i] = from_f32<MT>(to_f32(sm.kr[i * LDK + c]) * ex2(sm.G2[(i + gmo) * SM::G2L + c] - m2));
-        }
+        fill_cols2(sm.CT, DK, [&](int i, int c0, f32x4& a, f32x4& b) {
+            const f32x4 m2 = 0.5f * gsum(SC, c0);
+            a = rd4(sm.qr + i * LDK + c0) * ex2v(gsum(i + 1, c0) - m2);
+            b = rd4(sm.kr + i * LDK + c0) * ex2v(gsum(i + gmo, c0) - m2);
+        });
         lds_barrier();
         // ---- masked products, combination, outputs  (m = t, n = c)
         MT* dqg = static_cast<MT*>(p.dq);
