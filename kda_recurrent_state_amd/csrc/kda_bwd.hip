@@ -1510,15 +1510,18 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
             f32x4 d = mmak<MT, DV>(A + r16 * LDV, B + r16 * LDV, zero4(), lane);
             MT* dst = mi < 2 ? sm.MQ : mi < 4 ? sm.MG : mi < 6 ? sm.MV : sm.MY;
             const int coff = (mi & 1) * 16;
+            // the lane's four rows i = 4 g4 .. 4 g4 + 3 of column t are consecutive in [t][i]
+            const f32x4 bq = *reinterpret_cast<const f32x4*>(sm.bt + 4 * g4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 4 * g4 + r, t = r16;
                 float x = d[r];
-                if (mi == 1 || mi == 3) x *= sm.bt[i];
-                if (mi == 5 || mi == 7) x *= -sm.bt[i];
+                if (mi == 1 || mi == 3) x *= bq[r];
+                if (mi == 5 || mi == 7) x *= -bq[r];
                 const bool keep = mi < 2 ? i <= t : mi < 4 ? i < t : (mi & 1) ? i > t : i >= t;
-                dst[t * L32 + coff + i] = from_f32<MT>(keep ? x : 0.f);
+                d[r] = keep ? x : 0.f;
             }
+            store4<MT>(dst + r16 * L32 + coff + 4 * g4, d);
         }
         // ---- X <- gamma X + [Qb^T | Kb^T] [dO; F]; phi_{-1} = rowsum(X_prev * S)
 #pragma unroll
