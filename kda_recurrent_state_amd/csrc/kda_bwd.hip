@@ -1599,18 +1599,28 @@ __global__ __launch_bounds__(64 * GW) void kda_bwd_grad_kernel(BwdParams p) {
                 const ExactTerms x = exact_terms<MT, DK>(sm, c, g4, gmo);
                 mq[a] = x.q; mg[a] = x.g; mv[a] = x.v; my[a] = x.y;
             }
-            const float gc = sm.G2[SC * SM::G2L + c], m2 = 0.5f * gc;
+            const float gc = sm.G2[SC * SM::G2L + c], m2 = 0.5f * gc, em = ex2(m2);
             float av[4], au[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * g4 + r;
                 const float gmt = sm.G2[(t + gmo) * SM::G2L + c], gt = sm.G2[(t + 1) * SM::G2L + c];
-                const float fq = exact ? 1.f : ex2(gt - m2), fg = exact ? 1.f : ex2(gmt - m2);
-                const float fv = exact ? 1.f : ex2(m2 - gt), fy = exact ? 1.f : ex2(m2 - gmt);
-                const float dq = ex2(gt) * dqs[a][r] + fq * mq[a][r];
-                const float gs = ex2(gmt) * gss[a][r] + fg * mg[a][r];
-                const float vd = ex2(gc - gt) * vds[a][r] + fv * mv[a][r];
-                const float ay = ex2(gc - gmt) * ayds[a][r] + fy * my[a][r];
+                // factored: the state parts' factors e^{g}, e^{gm}, e^{gC-g}, e^{gC-gm} are e^{m}
+                // times the masked parts' ones (each within e^{+-span/2}, no overflow); exact:
+                // one exponent each
+                float dq, gs, vd, ay;
+                if (!exact) {
+                    const float fq = ex2(gt - m2), fg = ex2(gmt - m2), fv = ex2(m2 - gt), fy = ex2(m2 - gmt);
+                    dq = (em * fq) * dqs[a][r] + fq * mq[a][r];
+                    gs = (em * fg) * gss[a][r] + fg * mg[a][r];
+                    vd = (em * fv) * vds[a][r] + fv * mv[a][r];
+                    ay = (em * fy) * ayds[a][r] + fy * my[a][r];
+                } else {
+                    dq = ex2(gt) * dqs[a][r] + mq[a][r];
+                    gs = ex2(gmt) * gss[a][r] + mg[a][r];
+                    vd = ex2(gc - gt) * vds[a][r] + mv[a][r];
+                    ay = ex2(gc - gmt) * ayds[a][r] + my[a][r];
+                }
                 const float b = sm.bt[t];
                 const float kt = to_f32(sm.kr[t * LDK + c]), qt = to_f32(sm.qr[t * LDK + c]);
                 const float dk = b * (vd - ay - gs);
