@@ -211,7 +211,9 @@ KDA_API int kda_chunk_fwd_ex(const kda_dims_t* dims, const kda_prologue_t* prolo
  * chunk and dv split from dims; no prologue, no snapshots).  When S_T is given
  * it holds the running state, and the scratch holds only operator blocks: a
  * call needs units x 37,376 bytes for one chunk per (sequence, head) at dk = 128
- * (units x 20,736 at dk = 64), plus units x dk x dv x 4 when S_T is NULL, and
+ * (units x 20,736 at dk = 64), plus units x dk x dv x 4 when S_T is NULL
+ * (and a 256-byte-rounded 4 bytes per sequence for packed batches of more than
+ * 256 state-pass workgroups, which the state pass takes longest first), and
  * fails with KDA_ERR_INVALID_ARGUMENT (nothing enqueued) when that exceeds the
  * scratch; larger segments of chunks run when more fits.  Shapes without a
  * two-pass kernel run single-pass and use no scratch.  Every call on one GPU
@@ -229,7 +231,11 @@ KDA_API int kda_chunk_fwd_noalloc(const kda_dims_t* dims, const void* q, const v
  * whole 2 x 32-head x 32K-token batch runs as one segment), or 0 if the call
  * would run single-pass (method SINGLE, or no two-pass kernel for the shape).
  * The minimum that still runs two-pass is what one chunk per (sequence, head)
- * needs: see kda_chunk_workspace_min.
+ * needs: see kda_chunk_workspace_min.  Both include, for packed batches
+ * (cu_seqlens) of 2 to 4096 sequences with more state-pass workgroups than the
+ * GPU's 256 compute units, 4 bytes per sequence (rounded to 256) for the
+ * order in which the state pass takes them: longest first, so that the long
+ * walks do not start last.
  */
 KDA_API int kda_chunk_workspace_size(const kda_dims_t* dims, size_t* bytes);
 KDA_API int kda_chunk_workspace_min(const kda_dims_t* dims, size_t* bytes);

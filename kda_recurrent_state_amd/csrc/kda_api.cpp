@@ -114,14 +114,20 @@ int kernel_order(const kda_dims_t* d) { return d->scalar_decay ? 0 : d->order; }
 int two_pass_order(const kda_dims_t* d) { return d->scalar_decay ? 1 : d->order; }
 
 // Plan of a prefill call: which method, chunk, split and, for the two-pass
-// method, the workspace layout [states of all units][operator blocks].
+// method, the workspace layout [sequence order][states of all units][operator
+// blocks].
 struct Plan {
     int method = KDA_METHOD_SINGLE;
     int chunk = 32, split = 0;
     int64_t units = 0, max_chunks = 0;
-    size_t block = 0, state_bytes = 0, min_bytes = 0, pref_bytes = 0;
+    size_t block = 0, state_bytes = 0, order_bytes = 0, min_bytes = 0, pref_bytes = 0;
     bool two_pass_ok = false;
 };
+
+// Sequences the state pass can take longest first: the rank kernel compares
+// every pair, so the order is formed up to this many sequences (a few
+// microseconds), and index order is kept beyond.
+constexpr int kMaxRankedSeqs = 4096;
 
 // Operator bytes per segment of the preferred workspace.  Each segment costs a
 // launch of both passes and a ramp of each; on the 288 GB parts a few GiB is
@@ -181,8 +187,15 @@ int plan_prefill(const kda_dims_t* d, bool have_cu, Plan* pl) {
         int64_t m = (int64_t)(kSegmentTarget / per_chunk);
         if (m > pl->max_chunks) m = pl->max_chunks;
         if (m < 1) m = 1;
-        pl->min_bytes = pl->state_bytes + per_chunk;
-        pl->pref_bytes = pl->state_bytes + per_chunk * (size_t)m;
+        // With more state-pass workgroups than compute units, sequences of
+        // different lengths finish unevenly in index order; the walk then takes
+        // them longest first (simulated on the 64-sequence varlen batch: 19-30 %
+        // above the even finish in index order, within 1 % longest first).
+        const int64_t groups = pl->units * split2;
+        if (have_cu && d->num_seqs >= 2 && d->num_seqs <= kMaxRankedSeqs && groups > 256)
+            pl->order_bytes = round256((size_t)d->num_seqs * 4);
+        pl->min_bytes = pl->order_bytes + pl->state_bytes + per_chunk;
+        pl->pref_bytes = pl->order_bytes + pl->state_bytes + per_chunk * (size_t)m;
         pl->split = split2;
     }
     return KDA_OK;
@@ -243,7 +256,9 @@ int kda_chunk_fwd_snapshots(const kda_dims_t* d, const void* q, const void* k, c
 }
 
 // The prefill behind every kda_chunk_fwd* entry point.  Workspace layout: the
-// running states of all units (state_off bytes), then the operator blocks.  The
+// longest-first sequence order (order_bytes, only for batches the state pass
+// takes in that order), the running states of all units, then the operator
+// blocks (at state_off).  The
 // public entry points always reserve the states (their documented minimum);
 // kda_chunk_fwd_noalloc reserves them only when S_T is NULL (otherwise S_T holds
 // the running state), which leaves its fixed scratch to the blocks.
@@ -301,7 +316,7 @@ static int chunk_fwd_impl(const kda_dims_t* d, const kda_prologue_t* prologue, c
 
     // method
     bool two_pass = false;
-    const size_t state_off = (reserve_states || !S_T) ? pl.state_bytes : 0;
+    const size_t state_off = pl.order_bytes + ((reserve_states || !S_T) ? pl.state_bytes : 0);
     if (pl.two_pass_ok) {
         const size_t need = state_off + (size_t)pl.units * pl.block;
         const bool have_ws = workspace && workspace_bytes >= need;
@@ -320,9 +335,14 @@ static int chunk_fwd_impl(const kda_dims_t* d, const kda_prologue_t* prologue, c
             return fail(KDA_ERR_INVALID_ARGUMENT, "too many (sequence, head) units: %lld", (long long)pl.units);
         const int64_t nseg = pl.max_chunks > 0 ? (pl.max_chunks + m - 1) / m : 1;
         uint8_t* ws = static_cast<uint8_t*>(workspace);
-        float* run = S_T ? S_T : reinterpret_cast<float*>(ws);
+        int32_t* ord = pl.order_bytes ? reinterpret_cast<int32_t*>(ws) : nullptr;
+        float* run = S_T ? S_T : reinterpret_cast<float*>(ws + pl.order_bytes);
         uint8_t* blocks = ws + state_off;
         const int64_t eq_len = cu_seqlens ? 0 : d->total_tokens / d->num_seqs;
+        if (ord) {
+            hipError_t e = kda::launch_seq_rank(cu_seqlens, d->num_seqs, ord, (hipStream_t)stream);
+            if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill sequence order launch: %s", hipGetErrorString(e));
+        }
         for (int64_t sgi = 0; sgi < nseg; ++sgi) {
             const int64_t chunk0 = sgi * m;
             hipError_t e = hipSuccess;
@@ -341,6 +361,7 @@ static int chunk_fwd_impl(const kda_dims_t* d, const kda_prologue_t* prologue, c
             sa.dk = d->dk; sa.dv = d->dv; sa.split = pl.split; sa.m = (int32_t)m; sa.chunk = chunk;
             sa.chunk0 = chunk0; sa.order = two_pass_order(d); sa.snap = snapshots; sa.snap_rows = snapshot_rows;
             sa.snap_every = (int32_t)snapshot_every;
+            sa.ord = ord;
             e = kda::launch_scan(sa, (hipStream_t)stream);
             if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill state pass launch: %s", hipGetErrorString(e));
         }
@@ -419,7 +440,7 @@ int kda_chunk_fwd_noalloc(const kda_dims_t* d, const void* q, const void* k, con
     if (!pl.two_pass_ok || d->num_seqs == 0)  // single-pass: no scratch at all
         return chunk_fwd_impl(d, nullptr, q, k, v, log_a, beta, S0, cu_seqlens, o, S_T, nullptr, 0, 0, nullptr, 0,
                               false, stream);
-    const size_t need = (S_T ? 0 : pl.state_bytes) + (size_t)pl.units * pl.block;
+    const size_t need = pl.order_bytes + (S_T ? 0 : pl.state_bytes) + (size_t)pl.units * pl.block;
     if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
         return fail(KDA_ERR_INVALID_ARGUMENT,
                     "the two-pass prefill of %lld (sequence, head) units needs %zu bytes of scratch%s; the fixed "

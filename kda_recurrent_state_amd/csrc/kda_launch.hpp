@@ -92,7 +92,10 @@ struct ScanLaunch {
     float* snap;                // as in ChunkArgs
     int64_t snap_rows;
     int32_t snap_every;
+    const int32_t* ord;         // sequences longest first (launch_seq_rank), or null: index order
 };
+// Longest-first order of the sequences of cu_seqlens: ord[r] = sequence of rank r.
+hipError_t launch_seq_rank(const int32_t* cu_seqlens, int num_seqs, int32_t* ord, hipStream_t stream);
 int prep_block_bytes(int dk, int chunk, int order);  // 0 if no prep kernel for (dk, chunk)
 hipError_t launch_prep(const PrepLaunch& a, hipStream_t stream);
 hipError_t launch_prep2(const PrepLaunch& a, hipStream_t stream);  // dk = 128, chunk 32

@@ -74,6 +74,7 @@ struct ScanParams {
     float* snap;          // state snapshots [rows][H][DK][DV], or null
     int64_t snap_rows;
     int snap_every;       // tokens between snapshots (a multiple of C)
+    const int32_t* ord;   // sequences longest first (kda_seq_rank_kernel), or null
 };
 
 // Place of the value tile's 16-byte piece u of token row t (VPR pieces per
@@ -119,12 +120,26 @@ __global__ void __launch_bounds__((ScanCfg<DK, DVS, CB, ORD1>::NT), 1) kda_scan_
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
     const int lr = lane & 15, lg = lane >> 4;
     const int H = p.H, DV = p.DV;
-    int item = blockIdx.x;
-    if (p.xcd_group) {
-        const int per = gridDim.x / 8;
-        item = (blockIdx.x % 8) * per + blockIdx.x / 8;
+    int unit, slice;
+    if (p.ord) {
+        // Longest sequences first.  Workgroups reach an XCD's compute units in
+        // the order of their index, and XCD x receives the indices x, x + 8, ...,
+        // so the units of rank x, x + 8, ... are dealt to it in that order, the
+        // slices of one unit next to each other (one L2 serves all of them).
+        const int b = blockIdx.x;
+        int rank;
+        if (p.xcd_group) { rank = (b / 8 / p.split) * 8 + b % 8; slice = (b / 8) % p.split; }
+        else { rank = b / p.split; slice = b % p.split; }
+        unit = p.ord[rank / H] * H + rank % H;
+    } else {
+        int item = blockIdx.x;
+        if (p.xcd_group) {
+            const int per = gridDim.x / 8;
+            item = (blockIdx.x % 8) * per + blockIdx.x / 8;
+        }
+        unit = item / p.split;
+        slice = item % p.split;
     }
-    const int unit = item / p.split, slice = item % p.split;
     const int n = unit / H, h = unit % H;
     const int dv0 = slice * DVS;
     int64_t tb, te;
@@ -441,8 +456,12 @@ static hipError_t scan_cfg(const ScanLaunch& a, hipStream_t stream) {
     p.ws = static_cast<const uint8_t*>(a.ws); p.S_in = a.S_in; p.S_out = a.S_out;
     p.H = a.num_heads; p.DV = a.dv; p.split = a.split; p.m = a.m; p.chunk0 = a.chunk0;
     p.snap = a.snap; p.snap_rows = a.snap_rows; p.snap_every = a.snap_every;
+    p.ord = a.ord;
     const int64_t blocks = (int64_t)a.units * a.split;
-    p.xcd_group = (a.split > 1 && blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
+    if (p.ord)  // the rank mapping deals whole units to the XCDs: it needs a multiple of 8 units
+        p.xcd_group = a.units % 8 == 0 ? 1 : 0;
+    else
+        p.xcd_group = (a.split > 1 && blocks % 8 == 0 && (blocks / 8) % a.split == 0) ? 1 : 0;
     constexpr int NT = ScanCfg<DK, DVS, CB, ORD1>::NT;
     if (a.snap)
         hipLaunchKernelGGL((kda_scan_kernel<DK, DVS, CB, true, ORD1>), dim3((unsigned)blocks), dim3(NT), 0, stream, p);
@@ -464,6 +483,35 @@ static bool scan_dispatch(int dk, int dvs, int chunk, const ScanLaunch* a, hipSt
     KDA_SCAN_CASE(128, 16, 1) KDA_SCAN_CASE(128, 32, 1) KDA_SCAN_CASE(128, 64, 2) KDA_SCAN_CASE(128, 128, 2)
     KDA_SCAN_CASE(64, 16, 1) KDA_SCAN_CASE(64, 32, 1) KDA_SCAN_CASE(64, 64, 2) KDA_SCAN_CASE(64, 128, 2)
     return false;
+}
+
+// ord[r] = the sequence of rank r when sequences are ordered by decreasing
+// length, equal lengths by index.  Thread i counts the sequences that come
+// before sequence i, reading the lengths through LDS in tiles.
+__global__ void __launch_bounds__(256) kda_seq_rank_kernel(const int32_t* __restrict__ cu, int N,
+                                                             int32_t* __restrict__ ord) {
+    constexpr int TILE = 1024;
+    __shared__ int32_t len_s[TILE];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int32_t li = i < N ? cu[i + 1] - cu[i] : 0;
+    int rank = 0;
+    for (int base = 0; base < N; base += TILE) {
+        const int cnt = min(TILE, N - base);
+        __syncthreads();
+        for (int t = threadIdx.x; t < cnt; t += 256) len_s[t] = cu[base + t + 1] - cu[base + t];
+        __syncthreads();
+        for (int t = 0; t < cnt; ++t) {
+            const int32_t lj = len_s[t];
+            rank += (lj > li) || (lj == li && base + t < i);
+        }
+    }
+    if (i < N) ord[rank] = i;
+}
+
+hipError_t launch_seq_rank(const int32_t* cu_seqlens, int num_seqs, int32_t* ord, hipStream_t stream) {
+    hipLaunchKernelGGL(kda_seq_rank_kernel, dim3((num_seqs + 255) / 256), dim3(256), 0, stream, cu_seqlens, num_seqs,
+                       ord);
+    return hipGetLastError();
 }
 
 bool two_pass_supported(int dtype, int dk, int dvs, int chunk) {

@@ -166,6 +166,23 @@ def test_workspace_sizes(lib):
     assert lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(size)) == OK and size.value == 0
 
 
+def test_workspace_holds_the_sequence_order(lib):
+    """Packed batches with more state-pass workgroups than the 256 compute
+    units reserve 4 bytes per sequence (rounded to 256) for the longest-first
+    order; smaller batches and batches beyond 4096 sequences do not."""
+    def least(**kw):
+        n = ctypes.c_size_t(0)
+        assert lib.kda_chunk_workspace_min(ctypes.byref(dims(**kw)), ctypes.byref(n)) == OK
+        return n.value
+    block, state = 37376, 128 * 128 * 4
+    # 300 units at split 2 (64-column slices): 600 workgroups, ordered
+    assert least(num_seqs=300, num_heads=1, total_tokens=30000) == 1280 + 300 * (state + block)
+    # 64 units at split 4: 256 workgroups, all resident at once, index order
+    assert least(num_seqs=2, num_heads=32, total_tokens=64) == 64 * (state + block)
+    # 5000 sequences: beyond the ranked maximum, index order
+    assert least(num_seqs=5000, num_heads=1, total_tokens=5000) == 5000 * (state + block)
+
+
 def test_status_strings(lib):
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(3) == b"KDA_ERR_MISALIGNED"

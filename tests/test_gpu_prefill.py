@@ -108,6 +108,33 @@ def test_two_pass_segments(dk, dv):
             assert torch.equal(o, ref[0]) and torch.equal(ST, ref[1])  # segmenting is exact
 
 
+@pytest.mark.parametrize("n_seqs", [300, 304])
+def test_prefill_many_sequences_longest_first(n_seqs):
+    """More state-pass workgroups than compute units: the state pass takes the
+    sequences longest first (300 units: rank order; 304: ranks dealt over the
+    eight XCDs).  Lengths repeat, include empty sequences and one long one, so
+    ties and empty units are ranked too; the preferred and the smallest
+    workspace (a segment per chunk) both match the oracle."""
+    log(f"prefill {n_seqs} sequences longest first")
+    rng = np.random.default_rng(n_seqs)
+    lengths = rng.integers(0, 120, n_seqs)
+    lengths[rng.integers(0, n_seqs, 20)] = 0
+    lengths[7] = 900
+    lengths[rng.integers(0, n_seqs, 30)] = 64
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=n_seqs, heads=1)
+    inp = generate(w, seed=40 + n_seqs, device=DEV, lengths=lengths.tolist())
+    q, v = inp["q"], inp["v"]
+    least = kda.chunk_workspace_size(q, v, num_seqs=n_seqs, method=TWO, max_seqlen=900, minimum=True)
+    ref = None
+    for ws in (None, torch.empty(least, dtype=torch.uint8, device=DEV)):
+        o, ST = run_method(inp, TWO, workspace=ws, max_seqlen=900)
+        if ref is None:
+            check_all(inp, o, ST, 2e-2, "preferred workspace")
+            ref = (o, ST)
+        else:
+            assert torch.equal(o, ref[0]) and torch.equal(ST, ref[1])  # segmenting is exact
+
+
 def test_two_pass_matches_single_pass():
     log("two-pass vs single-pass, d=128")
     w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seqlen=1000, heads=2)
