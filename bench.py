@@ -263,6 +263,9 @@ def prefill_leg(leg, args, kda, dev, stream):
     ST = torch.empty((w.n_seqs, w.heads, w.dk, w.dv), dtype=torch.float32, device=dev)
     wsb = kda.chunk_workspace_size(x["q"], x["v"], num_seqs=w.n_seqs, scalar_decay=w.scalar_decay,
                                    max_seqlen=maxlen)
+    if args.workspace_mib and wsb:
+        wsb = max(kda.chunk_workspace_size(x["q"], x["v"], num_seqs=w.n_seqs, scalar_decay=w.scalar_decay,
+                                           max_seqlen=maxlen, minimum=True), args.workspace_mib << 20)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
 
     def step():

@@ -227,7 +227,7 @@ KDA_API int kda_chunk_fwd_noalloc(const kda_dims_t* dims, const void* q, const v
 
 /*
  * Workspace the two-pass prefill prefers for these dims (segments of up to
- * 4 GiB of operator blocks: about 1.2 KB per token and head at dk = 128, so a
+ * 16 GiB of operator blocks: about 1.2 KB per token and head at dk = 128, so a
  * whole 2 x 32-head x 32K-token batch runs as one segment), or 0 if the call
  * would run single-pass (method SINGLE, or no two-pass kernel for the shape).
  * The minimum that still runs two-pass is what one chunk per (sequence, head)

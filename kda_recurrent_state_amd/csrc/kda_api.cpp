@@ -121,6 +121,7 @@ struct Plan {
     int chunk = 32, split = 0;
     int64_t units = 0, max_chunks = 0;
     size_t block = 0, state_bytes = 0, order_bytes = 0, min_bytes = 0, pref_bytes = 0;
+    size_t bwd_pref_bytes = 0;  // the preferred workspace of the backward's prefill rerun
     bool two_pass_ok = false;
 };
 
@@ -131,8 +132,13 @@ constexpr int kMaxRankedSeqs = 4096;
 
 // Operator bytes per segment of the preferred workspace.  Each segment costs a
 // launch of both passes and a ramp of each; on the 288 GB parts a few GiB is
-// cheap, and fewer, longer segments measured faster than cache-sized ones.
-constexpr size_t kSegmentTarget = size_t(4) << 30;
+// cheap, and fewer, longer segments measured faster than cache-sized ones (the
+// 64-sequence varlen batch: 14.5 ms in ten segments of 4 GiB, 13.9 ms in three
+// of 16 GiB; the 2 x 32K batch needs 2.4 GB, one segment either way).  The
+// backward's prefill rerun keeps 4 GiB segments: its workspace holds much
+// more besides.
+constexpr size_t kSegmentTarget = size_t(16) << 30;
+constexpr size_t kBwdSegmentTarget = size_t(4) << 30;
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -196,6 +202,10 @@ int plan_prefill(const kda_dims_t* d, bool have_cu, Plan* pl) {
             pl->order_bytes = round256((size_t)d->num_seqs * 4);
         pl->min_bytes = pl->order_bytes + pl->state_bytes + per_chunk;
         pl->pref_bytes = pl->order_bytes + pl->state_bytes + per_chunk * (size_t)m;
+        int64_t mb = (int64_t)(kBwdSegmentTarget / per_chunk);
+        if (mb > pl->max_chunks) mb = pl->max_chunks;
+        if (mb < 1) mb = 1;
+        pl->bwd_pref_bytes = pl->order_bytes + pl->state_bytes + per_chunk * (size_t)mb;
         pl->split = split2;
     }
     return KDA_OK;
@@ -484,7 +494,7 @@ int plan_bwd(const kda_dims_t* d, bool have_cu, bool saved, BwdPlan* bp) {
     const size_t state = (size_t)d->dk * d->dv * 4;
     bp->snap_rows = T / 64;
     if (!saved) {
-        bp->fwd_ws = bp->fwd.two_pass_ok ? bp->fwd.pref_bytes : 0;
+        bp->fwd_ws = bp->fwd.two_pass_ok ? bp->fwd.bwd_pref_bytes : 0;
         bp->o_bytes = round256((size_t)T * H * d->dv * (d->qkv_dtype == KDA_BF16 ? 2 : 4));
         bp->snap_bytes = round256((size_t)bp->snap_rows * H * state);
     }

@@ -156,7 +156,7 @@ def test_workspace_sizes(lib):
     assert least.value > state and (least.value - state) % units == 0
     block = (least.value - state) // units
     assert block % 256 == 0 and size.value >= least.value and (size.value - state) % (units * block) == 0
-    assert (size.value - state) <= (4 << 30)  # segments of at most 4 GiB of blocks
+    assert (size.value - state) <= (16 << 30)  # segments of at most 16 GiB of blocks
     d.max_seqlen = 32768  # with the longest sequence known, this batch fits one segment
     assert lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(size)) == OK
     assert size.value - state == units * block * (32768 // 32)
