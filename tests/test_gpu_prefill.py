@@ -135,6 +135,23 @@ def test_prefill_many_sequences_longest_first(n_seqs):
             assert torch.equal(o, ref[0]) and torch.equal(ST, ref[1])  # segmenting is exact
 
 
+@pytest.mark.parametrize("n_seqs", [2500, 4097])
+def test_prefill_thousands_of_short_sequences(n_seqs):
+    """2500 sequences: the rank kernel reads the lengths in three LDS tiles of
+    1024 and the last of its 10 workgroups is partly idle; 4097 sequences are
+    past the ranked maximum and run in index order.  Short lengths with many
+    ties and empty sequences; every unit against the oracle."""
+    log(f"prefill {n_seqs} short sequences")
+    rng = np.random.default_rng(n_seqs)
+    lengths = rng.integers(0, 24, n_seqs)
+    lengths[rng.integers(0, n_seqs, n_seqs // 10)] = 0
+    lengths[n_seqs // 2] = 200
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=n_seqs, heads=1)
+    inp = generate(w, seed=50 + n_seqs, device=DEV, lengths=lengths.tolist())
+    o, ST = run_method(inp, TWO, max_seqlen=200)
+    check_all(inp, o, ST, 2e-2, f"{n_seqs} sequences")
+
+
 def test_two_pass_matches_single_pass():
     log("two-pass vs single-pass, d=128")
     w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seqlen=1000, heads=2)

@@ -68,6 +68,21 @@ def test_snapshots_bf16_varlen(dk, dv, scalar, method):
     assert torch.equal(snaps[first[3] - 1], ST[2])
 
 
+def test_snapshots_longest_first():
+    """300 sequences (more state-pass workgroups than compute units, so the
+    walk takes them longest first): each sequence's rows still land at its own
+    place in the packed snapshot buffer."""
+    log("snapshots, 300 sequences longest first")
+    rng = np.random.default_rng(7)
+    lengths = rng.integers(0, 200, 300)
+    lengths[rng.integers(0, 300, 30)] = 64
+    lengths[11] = 0
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=300, heads=1)
+    inp = generate(w, seed=71, device=DEV, lengths=lengths.tolist())
+    o, ST, snaps = snap_call(inp, 64, method=TWO)
+    check_snapshots(inp, snaps, 64, 2e-2, "300 sequences")
+
+
 @pytest.mark.parametrize("dk,dv", [(32, 32), (64, 32)])
 def test_snapshots_fp32(dk, dv):
     log(f"snapshots fp32 dk={dk} dv={dv}")
