@@ -419,10 +419,24 @@ __global__ void __launch_bounds__(512, 2) kda_prep_kernel(PrepParams p) {
     // upper blocks of the masked products are never written: zero them once
     prep_init_lds<DK, C>(s, tid, ORD1);
 
-    // this workgroup's chunks: item = blockIdx.x + k gridDim.x, empty ones skipped
+    // this workgroup's chunks: item = blockIdx.x + k gridDim.x, empty ones skipped,
+    // 64 candidates at a time per wavefront (one per lane), as in kda_prep2.hip
     auto next_item = [&](int it, int64_t& t0, int& Lc, int& h) {
-        while (it < p.items && !prep_locate<DK, C, SCALAR>(p, it, t0, Lc, h)) it += gridDim.x;
-        return it;
+        const int64_t G = gridDim.x;
+        const int ln = tid & 63;
+        for (int64_t at = it; at < p.items; at += 64 * G) {
+            const int64_t cand = at + ln * G;
+            int64_t ct0;
+            int cLc, ch;
+            const bool live = cand < p.items && prep_locate<DK, C, SCALAR>(p, (int)cand, ct0, cLc, ch);
+            const uint64_t m = __ballot(live);
+            if (m) {
+                const int first = (int)(at + (__ffsll((unsigned long long)m) - 1) * G);
+                prep_locate<DK, C, SCALAR>(p, first, t0, Lc, h);
+                return first;
+            }
+        }
+        return p.items;
     };
     int64_t t0 = 0;
     int Lc = 0, h = 0;

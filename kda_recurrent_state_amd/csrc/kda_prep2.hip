@@ -573,9 +573,26 @@ __global__ void __launch_bounds__(p2::NT, 2) kda_prep2_kernel(Prep2Params p) {
     // upper blocks of the masked products are never written: zero them once
     prep2_init_lds(s, tid, ORD1);
 
+    // this workgroup's chunks: item = blockIdx.x + k gridDim.x, empty ones skipped.
+    // Packed batches leave many items past their sequence's end, so each
+    // wavefront tests 64 candidates at once (one per lane) and then locates the
+    // first non-empty one: one round trip to the sequence bounds per 64 items
+    // instead of one per item.
     auto next_item = [&](int it, int64_t& t0, int& Lc, int& h) {
-        while (it < p.items && !prep2_locate(p, it, t0, Lc, h)) it += gridDim.x;
-        return it;
+        const int64_t G = gridDim.x;
+        for (int64_t at = it; at < p.items; at += 64 * G) {
+            const int64_t cand = at + lane * G;
+            int64_t ct0;
+            int cLc, ch;
+            const bool live = cand < p.items && prep2_locate(p, (int)cand, ct0, cLc, ch);
+            const uint64_t m = __ballot(live);
+            if (m) {
+                const int first = (int)(at + (__ffsll((unsigned long long)m) - 1) * G);
+                prep2_locate(p, first, t0, Lc, h);
+                return first;
+            }
+        }
+        return p.items;
     };
     int64_t t0 = 0;
     int Lc = 0, h = 0;
