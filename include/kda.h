@@ -104,7 +104,8 @@ typedef struct {
     int32_t num_heads;    /* H */
     int64_t total_tokens; /* T: packed tokens over all sequences (decode: T == N) */
     int32_t dk;           /* key width: 16, 32, 64 or 128 (bf16 prefill: 32, 64 or 128;
-                             fp32 prefill: 16, 32 or 64) */
+                             fp32 prefill: 16, 32 or 64, and 128 with 16-column dv
+                             slices, i.e. dv_split = dv / 16) */
     int32_t dv;           /* value width: 16, 32, 64 or 128 */
     int32_t qkv_dtype;    /* kda_dtype_t of q, k, v and o */
     int32_t scalar_decay; /* 0: log_a is [T, H, dk] (KDA); 1: log_a is [T, H] (Gated DeltaNet) */

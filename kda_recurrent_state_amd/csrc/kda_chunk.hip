@@ -83,15 +83,36 @@ struct ChunkCfg {
     static constexpr int OTPWX = (NOT + NW - 2) / (NW - 1);  // per wavefront 1..NW-1
 };
 
+// LDS bytes of a configuration with Kbar and Qbar in rows of their own.
+template <typename T, int DK, int DVS, int C>
+constexpr size_t chunk_lds_full() {
+    typedef ChunkCfg<T, DK, DVS, C> G;
+    auto a16 = [](size_t n) { return (n + 15) / 16 * 16; };
+    return a16(6 * C * G::LDK * sizeof(T)) + a16(DVS * G::LDK * sizeof(T)) +
+           a16(2 * (size_t)prows<DK>() * G::LDC * sizeof(T)) + a16((size_t)prows<DVS>() * G::LDC * sizeof(T)) +
+           a16(2 * DVS * G::LDC * sizeof(T)) + a16(4 * C * G::LDC * sizeof(T)) + 4 * C * G::LDA + 4 * 2 * G::NB * 256 +
+           4 * (C / 4) * DK + 4 * (G::NPAIR > 0 ? G::NPAIR : 1) * DK + 4 * DK + 4 * C + 4 * G::NW;
+}
+// Configurations that would not fit a compute unit (fp32 at dk = 128) keep Kbar
+// and Qbar over the Gram columns Kce and Kci instead: they are formed with the
+// other gated operands but held in registers until the Gram products have read
+// the columns, and written there before the state products read them.
+template <typename T, int DK, int DVS, int C>
+constexpr bool chunk_alias_bar() { return chunk_lds_full<T, DK, DVS, C>() > 160 * 1024; }
+
 template <typename T, int DK, int DVS, int C>
 struct ChunkLds {
     typedef ChunkCfg<T, DK, DVS, C> G;
+    static constexpr bool AB = chunk_alias_bar<T, DK, DVS, C>();
+    static constexpr int NBAR = AB ? 16 / (int)sizeof(T) : C * G::LDK;  // own rows of Kbar, Qbar
     alignas(16) T Kr[C * G::LDK];    // K e^{g_{t-1} - mid}   Gram rows (A, L)
     alignas(16) T Qr[C * G::LDK];    // Q e^{g_t - mid}       Gram rows (P1, P2)
-    alignas(16) T Kce[C * G::LDK];   // K e^{mid - g_{t-1}}   Gram columns (A, P1)
-    alignas(16) T Kci[C * G::LDK];   // K e^{mid - g_t}       Gram columns (L, P2)
-    alignas(16) T Kbar[C * G::LDK];  // K e^{g_{t-1}}
-    alignas(16) T Qbar[C * G::LDK];  // Q e^{g_t}
+    alignas(16) T Kce[C * G::LDK];   // K e^{mid - g_{t-1}}   Gram columns (A, P1); Kbar when AB
+    alignas(16) T Kci[C * G::LDK];   // K e^{mid - g_t}       Gram columns (L, P2); Qbar when AB
+    alignas(16) T Kbar_own[NBAR];    // K e^{g_{t-1}}
+    alignas(16) T Qbar_own[NBAR];    // Q e^{g_t}
+    __device__ T* Kbar() { return AB ? Kce : Kbar_own; }
+    __device__ T* Qbar() { return AB ? Kci : Qbar_own; }
     alignas(16) T ST[DVS * G::LDK];  // state slice at the chunk start, [j][c]
     alignas(16) T KccT[prows<DK>() * G::LDC];  // (K e^{g_C - g_{t-1}})^T, plane rows
     alignas(16) T KtcT[prows<DK>() * G::LDC];  // (K e^{g_C - g_t})^T, plane rows
@@ -241,9 +262,12 @@ __device__ __forceinline__ void chunk_steep_operands(const ChunkParams& p, const
                                                      ChunkLds<T, DK, DVS, C>& s, int64_t t0,
                                                      int Lc, int h, int tid,
                                                      const typename Vec2<T>::type (&qraw)[ChunkCfg<T, DK, DVS, C>::UPT][4],
-                                                     const typename Vec2<T>::type (&kraw)[ChunkCfg<T, DK, DVS, C>::UPT][4]) {
+                                                     const typename Vec2<T>::type (&kraw)[ChunkCfg<T, DK, DVS, C>::UPT][4],
+                                                     f32x2 (&kbk)[ChunkCfg<T, DK, DVS, C>::UPT][4],
+                                                     f32x2 (&qbk)[ChunkCfg<T, DK, DVS, C>::UPT][4]) {
     typedef ChunkCfg<T, DK, DVS, C> G;
     constexpr int NT = G::NT, LDK = G::LDK, LDC = G::LDC;
+    constexpr bool AB = ChunkLds<T, DK, DVS, C>::AB;
     float* LA = reinterpret_cast<float*>(s.Kce);
     static_assert(sizeof(s.Kce) + sizeof(s.Kci) >= C * DK * sizeof(float), "log2 decays fit over Kce, Kci");
     auto ex2v = [](f32x2 x) { return f32x2{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1])}; };
@@ -289,8 +313,13 @@ __device__ __forceinline__ void chunk_steep_operands(const ChunkParams& p, const
                 const f32x2 kb = k * ex2v(ORD1 ? g : gp), qb = q * ex2v(g);
                 kc[i] = k * ex2v(sx[i] + l2[i]);
                 kt[i] = k * ex2v(sx[i]);
-                store2(&s.Kbar[t * LDK + c], kb[0], kb[1]);
-                store2(&s.Qbar[t * LDK + c], qb[0], qb[1]);
+                if (AB) {
+                    kbk[u][i] = kb;
+                    qbk[u][i] = qb;
+                } else {
+                    store2(&s.Kbar()[t * LDK + c], kb[0], kb[1]);
+                    store2(&s.Qbar()[t * LDK + c], qb[0], qb[1]);
+                }
                 store2(&s.Kr[t * LDK + c], k[0], k[1]);
                 store2(&s.Qr[t * LDK + c], q[0], q[1]);
                 *reinterpret_cast<f32x2*>(&LA[t * DK + c]) = l2[i];
@@ -318,7 +347,8 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p, ChunkPro 
     typedef ChunkCfg<T, DK, DVS, C> G;
     typedef Mma<T> M;
     constexpr int NT = G::NT, NW = G::NW, NB = G::NB, LDK = G::LDK, LDC = G::LDC, LDA = G::LDA;
-    __shared__ ChunkLds<T, DK, DVS, C> s;
+    typedef ChunkLds<T, DK, DVS, C> SL;
+    __shared__ SL s;
 
     const T* __restrict__ gq = static_cast<const T*>(p.q);
     const T* __restrict__ gk = static_cast<const T*>(p.k);
@@ -492,8 +522,10 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p, ChunkPro 
 #pragma unroll
         for (int w = 0; w < NW; ++w) steep_any |= s.steep[w];
         const bool steep_chunk = __builtin_amdgcn_readfirstlane(steep_any) != 0;
+        // Kbar, Qbar of this thread's units, when they wait for the Gram columns' rows
+        f32x2 kbk[SL::AB ? G::UPT : 1][4], qbk[SL::AB ? G::UPT : 1][4];
         if (steep_chunk) {
-            chunk_steep_operands<T, DK, DVS, C, SCALAR, ORD1, PRO>(p, pr, s, t0, Lc, h, tid, qraw, kraw);
+            chunk_steep_operands<T, DK, DVS, C, SCALAR, ORD1, PRO>(p, pr, s, t0, Lc, h, tid, qraw, kraw, kbk, qbk);
         } else {
 #pragma unroll
         for (int u = 0; u < G::UPT; ++u) {
@@ -538,8 +570,13 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p, ChunkPro 
                     store2(&s.Qr[t * LDK + c], qr[0], qr[1]);
                     if (!ORD1) store2(&s.Kce[t * LDK + c], kce[0], kce[1]);
                     store2(&s.Kci[t * LDK + c], kci[0], kci[1]);
-                    store2(&s.Kbar[t * LDK + c], kr[0] * em[0], kr[1] * em[1]);
-                    store2(&s.Qbar[t * LDK + c], qr[0] * em[0], qr[1] * em[1]);
+                    if (SL::AB) {
+                        kbk[u][i] = kr * em;
+                        qbk[u][i] = qr * em;
+                    } else {
+                        store2(&s.Kbar()[t * LDK + c], kr[0] * em[0], kr[1] * em[1]);
+                        store2(&s.Qbar()[t * LDK + c], qr[0] * em[0], qr[1] * em[1]);
+                    }
                     kc[i] = kce * ec;
                     kt[i] = kci * ec;
                     prev = ri;
@@ -616,6 +653,24 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p, ChunkPro 
             else store4(&(g == 1 ? s.L : (g == 2 ? s.P1 : s.P2))[t * LDC + i0], m);
         }
         lds_barrier();
+        if constexpr (SL::AB) {
+            // the Gram columns are read: Kbar and Qbar take their rows
+#pragma unroll
+            for (int u = 0; u < G::UPT; ++u) {
+                const int uu = tid + NT * u;
+                if (uu < G::NU) {
+                    int c, tg;
+                    unit_of<G::NCP>(uu, c, tg);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 4 * tg + i;
+                        store2(&s.Kbar()[t * LDK + c], kbk[u][i][0], kbk[u][i][1]);
+                        store2(&s.Qbar()[t * LDK + c], qbk[u][i][0], qbk[u][i][1]);
+                    }
+                }
+            }
+            lds_barrier();
+        }
 
         // ---- P4: wavefront 0 inverts (I + A); the others form Z = Kbar S + L (bV),
         //      O^T = S^T Qbar^T + (bV)^T P2^T and Gamma S + Kt^T bV for their tiles ---
@@ -629,7 +684,7 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p, ChunkPro 
                 oacc[i] = zero4();
                 if (w < G::NOT) {
                     const int mt = w / (DVS / 16), nj = w % (DVS / 16);
-                    f32x4 z = tile_mma<T, DK>(s.Kbar + 16 * mt * LDK, LDK, s.ST + 16 * nj * LDK, LDK, zero4(), lane);
+                    f32x4 z = tile_mma<T, DK>(s.Kbar() + 16 * mt * LDK, LDK, s.ST + 16 * nj * LDK, LDK, zero4(), lane);
                     if (ORD1)  // Z = Kbar S - V
                         z -= load4(&s.VT[prow<DVS>(16 * nj + lrow) * LDC + 16 * mt + 4 * lgrp]);
                     else
@@ -637,7 +692,7 @@ __global__ void __launch_bounds__(512) kda_chunk_kernel(ChunkParams p, ChunkPro 
                                              lane);
                     store4(&s.ZT[(16 * nj + lrow) * LDC + 16 * mt + 4 * lgrp], z);
                     const int mj = w / (C / 16), nt = w % (C / 16);
-                    f32x4 x = tile_mma<T, DK>(s.ST + 16 * mj * LDK, LDK, s.Qbar + 16 * nt * LDK, LDK, zero4(), lane);
+                    f32x4 x = tile_mma<T, DK>(s.ST + 16 * mj * LDK, LDK, s.Qbar() + 16 * nt * LDK, LDK, zero4(), lane);
                     oacc[i] = ORD1 ? x
                                    : tile_mma_r<T, C>(s.VT + prow<DVS>(16 * mj + lrow) * LDC,
                                                       s.P2 + (16 * nt + lrow) * LDC, x, lane);
@@ -792,7 +847,7 @@ static bool chunk_dispatch(int dtype, int dk, int dvs, int chunk, int scalar, bo
         KDA_CHUNK_CASE(bf16, 32, 32, 64) KDA_CHUNK_CASE(bf16, 64, 32, 64)
     } else if (dtype == 0) {
         KDA_CHUNK_CASE(float, 16, 16, 32) KDA_CHUNK_CASE(float, 32, 16, 32) KDA_CHUNK_CASE(float, 32, 32, 32)
-        KDA_CHUNK_CASE(float, 64, 16, 32) KDA_CHUNK_CASE(float, 64, 32, 32)
+        KDA_CHUNK_CASE(float, 64, 16, 32) KDA_CHUNK_CASE(float, 64, 32, 32) KDA_CHUNK_CASE(float, 128, 16, 32)
         KDA_CHUNK_CASE(float, 16, 16, 64) KDA_CHUNK_CASE(float, 32, 32, 64)
     }
     return false;

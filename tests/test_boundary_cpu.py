@@ -72,6 +72,7 @@ def decode(lib, d, q=GOOD, k=GOOD, v=GOOD, la=GOOD, beta=GOOD, Si=GOOD, So=GOOD,
     (dict(d=dims(chunk_size=48)), UNSUPPORTED),
     (dict(d=dims(dv_split=3)), INVALID),
     (dict(d=dims(qkv_dtype=1, dk=16, dv=16)), UNSUPPORTED),  # no bf16 kernel below dk=32
+    (dict(d=dims(qkv_dtype=0, dk=128, dv=128, dv_split=4)), UNSUPPORTED),  # fp32 at dk=128: 16-column slices only
     (dict(d=dims(), q=None), INVALID),
     (dict(d=dims(), beta=None), INVALID),
     (dict(d=dims(), o=None), INVALID),
@@ -234,6 +235,7 @@ def prefill_ex(lib, d, pro, ws=None, ws_bytes=0):
     # the single-pass kernel runs the prologue too: these pass every check and
     # fail here only at the launch (no GPU)
     ((1, 1, 1, -8.0), dims(qkv_dtype=0, dk=64, dv=64), "launch"),  # fp32 runs single-pass
+    ((1, 1, 1, -8.0), dims(qkv_dtype=0, dk=128, dv=128), "launch"),  # fp32 at dk = 128: 16-column slices
     ((1, 0, 0, 0.0), dims(method=1), "launch"),             # single-pass asked for
     ((0, 1, 0, 0.0), dims(), "launch"),                     # no workspace: single-pass
     ((0, 0, 0, 0.0), dims(num_seqs=0, total_tokens=0), OK),

@@ -75,7 +75,7 @@ def test_steep_bf16(dk, method, steep, order):
 
 @pytest.mark.parametrize("order", [0, 1])
 @pytest.mark.parametrize("steep", STEEP)
-@pytest.mark.parametrize("dk", [32, 64])
+@pytest.mark.parametrize("dk", [32, 64, 128])
 def test_steep_fp32(dk, steep, order):
     """fp32 inputs run the single-pass kernel (the two-pass one is bf16 only)."""
     log(f"steep fp32 dk={dk} log_a={steep} order={order}")

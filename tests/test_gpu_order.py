@@ -53,7 +53,7 @@ def test_decay_first_prefill_bf16(dk, dv, method):
         check(inp, *res, 2e-2, f"method {method}")
 
 
-@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (64, 32)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (64, 32), (128, 64)])
 def test_decay_first_prefill_fp32(dk, dv):
     log(f"decay-first prefill fp32 dk={dk} dv={dv}")
     w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=4, heads=2, dk=dk, dv=dv, dtype=torch.float32)

@@ -35,7 +35,7 @@ def test_prefill_kda_t64_d16_fp32():
     check_all(inp, o, ST, 1e-4, "C1")
 
 
-@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (64, 64), (32, 16), (64, 32)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (64, 64), (32, 16), (64, 32), (128, 128), (128, 16)])
 @pytest.mark.parametrize("scalar", [False, True])
 def test_prefill_fp32_varlen(dk, dv, scalar):
     log(f"prefill fp32 varlen dk={dk} dv={dv} scalar={scalar}")

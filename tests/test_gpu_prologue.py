@@ -101,7 +101,7 @@ def test_prologue_snapshots_and_segments():
 SINGLE_CASES = [
     # dtype, dk, dv, scalar, order, chunk
     (torch.float32, 32, 32, False, 0, 32), (torch.float32, 16, 16, False, 1, 32), (torch.float32, 64, 32, False, 0, 32),
-    (torch.float32, 32, 16, True, 0, 32), (torch.float32, 16, 16, False, 0, 64),
+    (torch.float32, 32, 16, True, 0, 32), (torch.float32, 16, 16, False, 0, 64), (torch.float32, 128, 128, False, 0, 32),
     (torch.bfloat16, 32, 32, False, 0, 32), (torch.bfloat16, 128, 64, False, 0, 32),
     (torch.bfloat16, 64, 64, True, 1, 32), (torch.bfloat16, 128, 128, False, 1, 32),
 ]

@@ -83,7 +83,7 @@ def test_snapshots_longest_first():
     check_snapshots(inp, snaps, 64, 2e-2, "300 sequences")
 
 
-@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 32)])
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 32), (128, 32)])
 def test_snapshots_fp32(dk, dv):
     log(f"snapshots fp32 dk={dk} dv={dv}")
     w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=3, heads=2, dk=dk, dv=dv, dtype=torch.float32)
