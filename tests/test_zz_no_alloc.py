@@ -57,3 +57,20 @@ def test_noalloc_dk64_and_single_pass_shapes():
     inp32 = generate(w32, seed=64, device=DEV, lengths=[90, 33])
     ref, got = both(inp32)
     assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+
+
+def test_noalloc_many_sequences_longest_first():
+    """300 packed sequences: more state-pass workgroups than compute units, so
+    the scratch also holds the longest-first order in front of the blocks; the
+    results equal those of kda_chunk_fwd, with and without S_T."""
+    import numpy as np
+    log("noalloc 300 sequences longest first")
+    rng = np.random.default_rng(65)
+    lengths = rng.integers(0, 150, 300)
+    lengths[5] = 600
+    w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=300, heads=1)
+    inp = generate(w, seed=65, device=DEV, lengths=lengths.tolist())
+    ref, got = both(inp)
+    compare(ref, got, "300 sequences")
+    assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+    compare(*both(inp, final_state=False), "300 sequences, no final state")
