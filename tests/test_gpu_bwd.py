@@ -326,3 +326,26 @@ def test_bwd_full_size_sampled():
     errs["dS0"] = max_rel_err(got["dS0"][n:n + 1, h:h + 1], ref["dS0"])
     log("  full size: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     assert all(v <= TOL[torch.bfloat16] for v in errs.values()), errs
+
+
+def test_bwd_gdn_h16_t4096_full():
+    """Gated DeltaNet at its full size (1 x 16 heads x 4096 tokens, d = 128,
+    bf16, scalar gate): every gradient element of the whole batch against the
+    oracle, both from a prefill rerun and from the forward's kept states."""
+    log("backward C2 full: GDN H=16 T=4096, whole batch")
+    inp = generate(WORKLOADS["gdn_h16_t4096_d128_bf16"], 2, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7)
+    T, H = inp["q"].shape[0], inp["q"].shape[1]
+    inp["dO"] = torch.randn((T, H, inp["v"].shape[2]), generator=g, device=DEV).to(inp["q"].dtype)
+    inp["dST"] = torch.randn((1, H, inp["q"].shape[2], inp["v"].shape[2]), generator=g, device=DEV)
+    if inp["cu_seqlens"] is None:
+        inp["cu_seqlens"] = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    got = gpu_grad(inp)
+    check(inp, got, TOL[torch.bfloat16], "C2 whole batch")
+    _, _, states = kda.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["log_a"], inp["beta"], S0=inp["S0"],
+                                           cu_seqlens=inp["cu_seqlens"], snapshot_every=64)
+    kept = gpu_grad(inp, states=states)
+    for n in NAMES:
+        if got.get(n) is not None:
+            assert torch.equal(got[n], kept[n]), n  # the rerun keeps the same states
