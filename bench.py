@@ -275,11 +275,14 @@ def prefill_leg(leg, args, kda, dev, stream):
         step()
     torch.cuda.synchronize()
     t = time_events(step, args.steps, stream) / args.steps
+    m_run, chunk_run, split_run = kda.chunk_plan(x["q"], x["v"], num_seqs=w.n_seqs, packed=True, workspace_bytes=wsb,
+                                                 scalar_decay=w.scalar_decay, max_seqlen=maxlen)
     B, F64 = prefill_algorithmic(w, 64, tokens=T)
-    _, F32 = prefill_algorithmic(w, 32, tokens=T)
+    _, F32 = prefill_algorithmic(w, chunk_run, tokens=T)
     gbs = B / t / 1e9
     res = {"workload": name, "tokens": T, "ms_per_step": t * 1e3, "tokens_per_s": T / t,
-           "method": "two-pass" if wsb else "single", "chunk": 32, "workspace_MiB": round(wsb / 2**20, 1),
+           "method": "two-pass" if m_run == kda.METHOD_TWO_PASS else "single", "chunk": chunk_run,
+           "dv_split": split_run, "workspace_MiB": round(wsb / 2**20, 1),
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": gbs / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes_per_launch": B,
                         "avg_launch_ms": t * 1e3},
@@ -366,9 +369,11 @@ def main():
                                                        max_seqlen=wp.seqlen, minimum=True),
                       args.workspace_mib << 20)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
-        used = "two-pass" if wsb else "single"
-        chunk_run = 32  # chunk_size 0: the library's default chunk (include/kda.h)
-        log(f"prefill method {used}, chunk {chunk_run}, workspace {wsb / 2**20:.1f} MiB")
+        # the configuration the library runs for this call (kda_chunk_plan)
+        m_run, chunk_run, split_run = kda.chunk_plan(x["q"], x["v"], num_seqs=wp.n_seqs, packed=False,
+                                                     workspace_bytes=wsb, method=method, max_seqlen=wp.seqlen)
+        used = "two-pass" if m_run == kda.METHOD_TWO_PASS else "single"
+        log(f"prefill method {used}, chunk {chunk_run}, dv split {split_run}, workspace {wsb / 2**20:.1f} MiB")
 
         def step():
             kda.chunk_fwd(x["q"], x["k"], x["v"], x["log_a"], x["beta"], S0=x["S0"],
@@ -393,7 +398,7 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic: seeded tensors with the layer's shapes and value distributions (no dataset)",
             "config": {"workload": wp.name, "batch": wp.n_seqs, "heads": wp.heads, "seq_len": wp.seqlen,
-                       "dk": wp.dk, "dv": wp.dv, "state": "fp32", "chunk": chunk_run, "dv_split": "auto",
+                       "dk": wp.dk, "dv": wp.dv, "state": "fp32", "chunk": chunk_run, "dv_split": split_run,
                        "method": used, "workspace_MiB": round(wsb / 2**20, 1)},
         })
         # One prefill call is the unit: with the two-pass method it is one launch of the

@@ -242,6 +242,23 @@ KDA_API int kda_chunk_workspace_size(const kda_dims_t* dims, size_t* bytes);
 KDA_API int kda_chunk_workspace_min(const kda_dims_t* dims, size_t* bytes);
 
 /*
+ * The kernel configuration a kda_chunk_fwd call with these dims would run,
+ * without running it (host only; no device is touched):
+ *   packed           1 if the call passes cu_seqlens, 0 if not
+ *   workspace_bytes  the workspace the call passes (0 for none)
+ *   method           out: KDA_METHOD_SINGLE or KDA_METHOD_TWO_PASS
+ *   chunk            out: the chunk size C
+ *   dv_split         out: workgroups per (sequence, head) along dv (0 when
+ *                    num_seqs is 0: nothing runs)
+ * Returns the status the call would return for these dims and workspace size
+ * (before its pointer checks): KDA_ERR_UNSUPPORTED for a shape not compiled,
+ * KDA_ERR_INVALID_ARGUMENT for a two-pass method asked for without enough
+ * workspace or a NULL output pointer.
+ */
+KDA_API int kda_chunk_plan(const kda_dims_t* dims, int packed, size_t workspace_bytes, int* method, int* chunk,
+                           int* dv_split);
+
+/*
  * Gradient of the prefill, for training.  On the pages the delta rule's cost is
  * a sequential dependency that blocks parallel training, and the chunkwise (WY)
  * form is what makes it parallel (page "The argument, in one page", section

@@ -24,7 +24,7 @@ import threading
 
 import torch  # loads the HIP runtime the library then shares
 
-__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "snapshot_rows", "chunk_workspace_size", "chunk_bwd",
+__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "snapshot_rows", "chunk_workspace_size", "chunk_plan", "chunk_bwd",
            "chunk_bwd_workspace_size", "decode_step", "KdaError", "library_path", "load_library",
            "METHOD_AUTO", "METHOD_SINGLE", "METHOD_TWO_PASS", "ORDER_ERASE_FIRST", "ORDER_DECAY_FIRST"]
 
@@ -120,6 +120,10 @@ def load_library(build_if_missing: bool = True):
                 fn = getattr(lib, name)
                 fn.restype = ctypes.c_int
                 fn.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(ctypes.c_size_t)]
+            lib.kda_chunk_plan.restype = ctypes.c_int
+            lib.kda_chunk_plan.argtypes = [ctypes.POINTER(_Dims), ctypes.c_int, ctypes.c_size_t,
+                                           ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                           ctypes.POINTER(ctypes.c_int)]
             lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
             lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P]
             lib.kda_decode_step.restype = ctypes.c_int
@@ -358,6 +362,20 @@ def chunk_workspace_size(q, v, *, num_seqs=1, scalar_decay=False, chunk_size=0, 
     fn = lib.kda_chunk_workspace_min if minimum else lib.kda_chunk_workspace_size
     _check(lib, fn(ctypes.byref(d), ctypes.byref(need)))
     return need.value
+
+
+def chunk_plan(q, v, *, num_seqs=1, packed=True, workspace_bytes=0, scalar_decay=False, chunk_size=0, dv_split=0,
+               method=METHOD_AUTO, max_seqlen=0, order=ORDER_ERASE_FIRST):
+    """The configuration chunk_fwd would run for these shapes and workspace size:
+    (method, chunk, dv_split), method METHOD_SINGLE or METHOD_TWO_PASS."""
+    lib = load_library()
+    T, H, dk = q.shape
+    d = _Dims(int(num_seqs), H, T, dk, v.shape[2], _dtype_code(q), int(bool(scalar_decay)), int(chunk_size),
+              int(dv_split), int(method), int(order), int(max_seqlen))
+    m, c, s = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib, lib.kda_chunk_plan(ctypes.byref(d), int(bool(packed)), ctypes.c_size_t(int(workspace_bytes)),
+                                   ctypes.byref(m), ctypes.byref(c), ctypes.byref(s)))
+    return m.value, c.value, s.value
 
 
 def chunk_bwd(q, k, v, log_a, beta, dO, S0=None, cu_seqlens=None, dS_T=None, *, chunk_size: int = 0,

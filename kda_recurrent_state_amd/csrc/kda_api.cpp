@@ -239,6 +239,42 @@ int kda_chunk_workspace_size(const kda_dims_t* d, size_t* bytes) {
     return ok();
 }
 
+int kda_chunk_plan(const kda_dims_t* d, int packed, size_t workspace_bytes, int* method, int* chunk,
+                   int* dv_split) {
+    if (!method || !chunk || !dv_split) return fail(KDA_ERR_INVALID_ARGUMENT, "method, chunk or dv_split is NULL");
+    Plan pl;
+    int st = plan_prefill(d, packed != 0, &pl);
+    if (st) return st;
+    *chunk = pl.chunk;
+    *method = KDA_METHOD_SINGLE;
+    *dv_split = 0;
+    if (d->num_seqs == 0) return ok();
+    // as chunk_fwd_impl decides (the public entry points reserve the running states)
+    if (pl.two_pass_ok) {
+        const size_t need = pl.order_bytes + pl.state_bytes + (size_t)pl.units * pl.block;
+        if (workspace_bytes >= need) {
+            *method = KDA_METHOD_TWO_PASS;
+            *dv_split = pl.split;
+            return ok();
+        }
+        if (d->method == KDA_METHOD_TWO_PASS)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "two-pass prefill needs a workspace of at least %zu bytes (got %zu)",
+                        need, workspace_bytes);
+    }
+    int split = d->dv_split;
+    if (split == 0) {
+        split = choose_split(d, pl.chunk);
+        if (split == 0)
+            return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, dk %d, dv %d, chunk %d", d->qkv_dtype,
+                        d->dk, d->dv, pl.chunk);
+    } else if (d->dv % split || !kda::chunk_supported(d->qkv_dtype, d->dk, d->dv / split, pl.chunk, d->scalar_decay)) {
+        return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, dk %d, dv %d / split %d, chunk %d",
+                    d->qkv_dtype, d->dk, d->dv, split, pl.chunk);
+    }
+    *dv_split = split;
+    return ok();
+}
+
 int kda_chunk_workspace_min(const kda_dims_t* d, size_t* bytes) {
     if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
     Plan pl;

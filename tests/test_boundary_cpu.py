@@ -429,3 +429,26 @@ def test_noalloc_rejects_beyond_its_scratch(lib):
     st = lib.kda_chunk_fwd_noalloc(ctypes.byref(d), P(GOOD), P(GOOD), P(GOOD), P(GOOD), P(GOOD), None, P(GOOD),
                                    P(GOOD), None, None)
     assert st == INVALID and b"S_T is NULL" in lib.kda_last_error()
+
+
+def test_chunk_plan(lib):
+    """kda_chunk_plan reports the configuration a prefill call would run, and
+    the status it would return, without touching a device."""
+    def plan(d, packed=1, ws=0):
+        m, c, s = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_int(-1)
+        st = lib.kda_chunk_plan(ctypes.byref(d), packed, ctypes.c_size_t(ws), ctypes.byref(m), ctypes.byref(c),
+                                ctypes.byref(s))
+        return st, m.value, c.value, s.value
+    d = dims(num_seqs=2, num_heads=32, total_tokens=2 * 32768, max_seqlen=32768)
+    need = ctypes.c_size_t(0)
+    assert lib.kda_chunk_workspace_size(ctypes.byref(d), ctypes.byref(need)) == OK
+    assert plan(d, 0, need.value) == (OK, 2, 32, 4)        # the benchmark's call: two-pass, C = 32, dv split 4
+    assert plan(d, 0, 0) == (OK, 1, 32, 4)                 # no workspace: single-pass
+    assert plan(dims(qkv_dtype=0, dk=128, dv=128, num_heads=1), 1, 0)[:2] == (OK, 1)
+    assert plan(dims(qkv_dtype=0, dk=128, dv=128, num_heads=1), 1, 0)[3] == 8   # fp32 at dk = 128: 16 columns
+    assert plan(dims(method=2), 1, 0)[0] == INVALID        # two-pass without a workspace
+    assert plan(dims(dk=48))[0] == UNSUPPORTED
+    assert plan(dims(qkv_dtype=0, dk=128, dv=128, dv_split=4))[0] == UNSUPPORTED
+    assert plan(dims(num_seqs=0, total_tokens=0)) == (OK, 1, 32, 0)
+    m = ctypes.c_int(0)
+    assert lib.kda_chunk_plan(ctypes.byref(dims()), 1, ctypes.c_size_t(0), ctypes.byref(m), None, None) == INVALID
