@@ -74,3 +74,46 @@ def test_noalloc_many_sequences_longest_first():
     compare(ref, got, "300 sequences")
     assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
     compare(*both(inp, final_state=False), "300 sequences, no final state")
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_noalloc_graph_replays(packed):
+    """The call the entry point is for: captured in a HIP graph and replayed three
+    times with eager work between, each replay bit-identical to the eager call."""
+    log(f"noalloc under graph capture, packed={packed}")
+    if packed:
+        w = scaled(WORKLOADS["kda_varlen_64seq_h32_d128"], n_seqs=3, heads=4)
+        x = generate(w, seed=66, device=DEV, lengths=[700, 33, 1290])
+    else:
+        w = scaled(WORKLOADS["kda_b2_h32_t32768_d128_bf16"], seqlen=2048, heads=4)
+        x = generate(w, seed=66, device=DEV)
+    T = x["q"].shape[0]
+    args = (x["q"], x["k"], x["v"], x["log_a"], x["beta"])
+    # max_seqlen given: the binding would otherwise read it from cu_seqlens on the host
+    maxlen = int(max(x["lengths"])) if "lengths" in x else w.seqlen
+    kw = dict(S0=x["S0"], cu_seqlens=x["cu_seqlens"], num_seqs=w.n_seqs, max_seqlen=maxlen)
+    o_ref = torch.empty((T, w.heads, w.dv), dtype=w.dtype, device=DEV)
+    S_ref = torch.empty((w.n_seqs, w.heads, w.dk, w.dv), dtype=torch.float32, device=DEV)
+    kda.chunk_fwd_noalloc(*args, out=o_ref, final_state=S_ref, **kw)  # eager, also the first-call set-up
+    torch.cuda.synchronize()
+    o = torch.zeros_like(o_ref)
+    S = torch.zeros_like(S_ref)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            kda.chunk_fwd_noalloc(*args, out=o, final_state=S, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    junk = torch.randn(1 << 20, device=DEV)
+    for r in range(3):
+        o.fill_(7.0)
+        S.fill_(-3.0)
+        junk.mul_(1.0001)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(o, o_ref) and torch.equal(S, S_ref)
+        log(f"  replay {r}: bit-identical {same}")
+        assert same, f"replay {r} differs from the eager call"
